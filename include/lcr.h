@@ -1,0 +1,175 @@
+/*
+ * lcr.h - route-layer attention with learned chunk routing, and bidirectional
+ * sliding-window attention, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the route layer of "Prefilling-dLLM v2: Learned Chunk Routing
+ * for Long-Context Diffusion Language Models" (Abstract; Figure 3 caption;
+ * Table 3) as also described in "The 172x Speedup Has an Evidence Budget"
+ * (section "How learned routing controls what the model can read").
+ *
+ * Sequence layout. A sequence of N chunks has L = 64*N slots. Chunk c holds 63
+ * content tokens in slots 64c..64c+62 and its routing mask in slot 64c+63.
+ * Content index i (0 <= i < T = 63*N) lives in slot 64*(i/63) + i%63.
+ * Query head h belongs to KV group g = h / G with G = Hq / Hkv.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *    library never allocates, frees or synchronises. Tensors are contiguous,
+ *    row-major, in the shapes given below.
+ *  - dtype LCR_BF16: q, k, v, x, A, Bm and o are bfloat16; LCR_F32: float32.
+ *    s, H, zsel and lse are always float32; idx is int32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and runs asynchronously. A call returns LCR_OK once its kernels are
+ *    enqueued.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    negative return nothing was enqueued and no output was touched.
+ *    LCR_ERR_HIP means a launch was rejected by the HIP runtime; earlier
+ *    kernels of the same call may already have been enqueued.
+ *  - Limits: d in {64, 128}; 1 <= G <= 8; 0 <= K <= 64; radius >= 0.
+ *  - The library keeps no state between calls and may be called from several
+ *    host threads on different streams.
+ */
+#ifndef LCR_H
+#define LCR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCR_CHUNK_SLOTS 64
+#define LCR_CHUNK_CONTENT 63
+#define LCR_MAX_GROUP 8
+#define LCR_MAX_TOPK 64
+
+typedef enum {
+  LCR_OK = 0,
+  LCR_ERR_ARG = -1,          /* a size, range or pointer is invalid */
+  LCR_ERR_DTYPE = -2,        /* dtype is not LCR_F32 or LCR_BF16 */
+  LCR_ERR_WORKSPACE = -3,    /* ws is NULL or smaller than lcr_workspace_bytes() */
+  LCR_ERR_HIP = -4,          /* the HIP runtime rejected a launch */
+  LCR_ERR_UNSUPPORTED = -5   /* valid, but outside this build's limits (d, G, K, LDS) */
+} lcr_status;
+
+typedef enum { LCR_F32 = 0, LCR_BF16 = 1 } lcr_dtype;
+
+/* Shape of a route layer: batch, query heads, KV heads, chunks, head dim, dtype. */
+typedef struct {
+  int B, Hq, Hkv, N, d;
+  int dtype; /* lcr_dtype */
+} lcr_dims;
+
+typedef enum {
+  LCR_OP_CHUNK_SUMMARY = 0,
+  LCR_OP_ROUTE_SCORE_TOPK = 1,
+  LCR_OP_ROUTED_ATTENTION = 2,
+  LCR_OP_SWA_ATTENTION = 3
+} lcr_op;
+
+/* Library version as 10000*major + 100*minor + patch. */
+int lcr_version(void);
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* lcr_status_string(int status);
+
+/*
+ * Bytes of device workspace `op` needs for these sizes (0 if none). D and r are
+ * used by LCR_OP_ROUTE_SCORE_TOPK only; K and nq by the two routing calls.
+ * Returns 0 for invalid sizes as well; the call itself reports those.
+ */
+size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, int nq);
+
+/*
+ * Summary keys and pooling entropies ("Prefilling-dLLM v2", Figure 3 caption:
+ * the routing mask's query pools its chunk's content keys with an intra-chunk
+ * softmax; the weighted sum is the summary key. "The 172x Speedup...": the
+ * entropy of these pooling weights is the second ranking signal).
+ *
+ *   alpha_j = softmax_j(scale * q[b,h,64c+63] . k[b,g,64c+j]),  j = 0..62
+ *   s[b,h,c] = sum_j alpha_j k[b,g,64c+j]
+ *   H[b,h,c] = -sum_j alpha_j ln alpha_j
+ *
+ * q [B,Hq,L,d]: only the mask-slot rows 64c+63 are read.
+ * k [B,Hkv,L,d]: only content rows are read.
+ * s [B,Hq,N,d] float32 (written), H [B,Hq,N] float32 (written).
+ * Arithmetic in float32.
+ */
+int lcr_chunk_summary(const lcr_dims* dims, const void* q, const void* k, float scale,
+                      float* s, float* H, void* stream);
+
+/*
+ * Residual-augmented scoring, GQA maximum and top-K selection ("Prefilling-dLLM
+ * v2", Figure 3 caption: a content query adds a low-rank residual and scores the
+ * summaries; scores are reduced by a maximum inside each GQA group; the top K
+ * chunks are shared by every head of the group. Table 3: the remote chunks lie
+ * beyond the local window).
+ *
+ * For content queries i = q0 .. q0+nq-1 (t = i - q0):
+ *   q~[b,h,t] = q[b,h,slot(i)] + (x[b,slot(i)] . A . Bm)[h*d .. h*d+d-1]
+ *   z[b,h,t,c] = scale * q~[b,h,t] . s[b,h,c] - beta * H[b,h,c]
+ *   zhat[b,g,t,c] = max over the G heads of group g of z[b,h,t,c]
+ *   candidates: chunks none of whose content indices 63c..63c+62 lies within
+ *               [i-radius, i+radius]
+ *   idx[b,g,t,:] = the min(K, #candidates) candidates with the largest zhat,
+ *                  ties to the smaller chunk index, in ascending chunk order,
+ *                  padded with -1
+ *   zsel[b,h,t,k] = z[b,h,t,idx[b,g,t,k]] (-INFINITY where idx is -1)
+ *
+ * q [B,Hq,L,d]; x [B,L,D] (rows at the query slots are read); A [D,r];
+ * Bm [r,Hq*d]; s [B,Hq,N,d]; H [B,Hq,N]. idx [B,Hkv,nq,K] int32 and
+ * zsel [B,Hq,nq,K] float32 are written; with K = 0 both may be NULL.
+ * Scores are computed to near-float32 accuracy (split-bfloat16 products with
+ * float32 accumulation). ws: lcr_workspace_bytes(LCR_OP_ROUTE_SCORE_TOPK, ...)
+ * bytes of device memory, contents need not be initialised.
+ * Limits: 1 <= r <= 128, D >= 1, 0 <= q0, q0 + nq <= T.
+ */
+int lcr_route_score_topk(const lcr_dims* dims, const void* q, const void* x, const void* A,
+                         const void* Bm, int D, int r, const float* s, const float* H,
+                         float beta, float scale, int K, int radius, int q0, int nq,
+                         int32_t* idx, float* zsel, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Routed attention ("Prefilling-dLLM v2", Figure 3 caption: the selected chunk
+ * scores and the local window's log-sum-exp share one softmax partition; a
+ * second softmax spreads each chunk's mass over its content tokens).
+ *
+ * For content query i (t = i - q0), head h, group g:
+ *   W = {u : |u - i| <= radius, 0 <= u < T}; a_u = scale * q[b,h,slot(i)] . k[b,g,slot(u)]
+ *   chunk logits z_k = zsel[b,h,t,k] for idx[b,g,t,k] >= 0
+ *   P = softmax over {a_u : u in W} joined with {z_k}
+ *   u_bar_k = sum_j softmax_j(scale * q . k[b,g,64c+j]) v[b,g,64c+j], j = 0..62, c = idx
+ *   o[b,h,slot(i)] = sum_u P_u v[b,g,slot(u)] + sum_k P_k u_bar_k
+ *   lse[b,h,t] = log of the partition's normaliser
+ *
+ * idx must list, for each row, chunks that are remote from i (as produced by
+ * lcr_route_score_topk), ascending, -1 padded. q, k, v as above;
+ * o [B,Hq,L,d]: only rows slot(i) for the queried i are written; lse
+ * [B,Hq,nq] float32 or NULL. ws: lcr_workspace_bytes(LCR_OP_ROUTED_ATTENTION,
+ * ...) bytes (may be 0 and ws NULL). Arithmetic: bf16 products with float32
+ * accumulation for bf16 inputs, split-bf16 (near float32) for float32 inputs.
+ */
+int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, const void* v,
+                         const int32_t* idx, const float* zsel, int K, int radius, float scale,
+                         int q0, int nq, void* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Bidirectional sliding-window attention for the layers that do not route
+ * ("Prefilling-dLLM v2", Abstract and Table 3: the other layers use a
+ * bidirectional sliding window, radius 1280). Every slot, content or mask, is
+ * an ordinary token:
+ *   o[b,h,t] = sum_u softmax_u(scale * q[b,h,t] . k[b,g,u]) v[b,g,u],
+ *   |u - t| <= radius, 0 <= u < L.
+ * q [B,Hq,L,d], k, v [B,Hkv,L,d], o [B,Hq,L,d]; lse [B,Hq,L] float32 or NULL.
+ */
+int lcr_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q,
+                      const void* k, const void* v, int radius, float scale, void* o,
+                      float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCR_H */

@@ -1,0 +1,19 @@
+"""Route-layer attention with learned chunk routing, and bidirectional sliding-window
+attention, on AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library liblcr.so (C ABI in include/lcr.h); the
+functions here marshal torch tensors into it. Import fails loudly only when a
+call is made without the library: build it with
+``python -m learned_chunk_routed_amd.build``.
+"""
+from ._lib import LIB_PATH, load  # noqa: F401
+from .ops import (  # noqa: F401
+    chunk_summary,
+    route_score_topk,
+    routed_attention,
+    swa_attention,
+    route_layer,
+    workspace_bytes,
+    make_dims,
+    default_scale,
+)

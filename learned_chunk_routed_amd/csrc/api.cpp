@@ -1,0 +1,101 @@
+// C ABI of the route-layer attention library (declared in include/lcr.h).
+// Each entry point validates its arguments on the host (validate.cpp), then
+// enqueues its kernels on the caller's stream. No allocation, no
+// synchronisation, no state kept between calls.
+#include <hip/hip_runtime.h>
+
+#include "../../include/lcr.h"
+#include "launch.h"
+#include "validate.h"
+
+using namespace lcr;
+
+static RouteDims to_route_dims(const lcr_dims* d) {
+  RouteDims r;
+  r.B = d->B;
+  r.Hq = d->Hq;
+  r.Hkv = d->Hkv;
+  r.N = d->N;
+  r.d = d->d;
+  r.dtype = d->dtype;
+  return r;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? LCR_OK : LCR_ERR_HIP; }
+
+extern "C" {
+
+int lcr_version(void) { return 10000; }
+
+const char* lcr_status_string(int status) {
+  switch (status) {
+    case LCR_OK: return "ok";
+    case LCR_ERR_ARG: return "invalid argument";
+    case LCR_ERR_DTYPE: return "invalid dtype";
+    case LCR_ERR_WORKSPACE: return "workspace missing or too small";
+    case LCR_ERR_HIP: return "HIP runtime error";
+    case LCR_ERR_UNSUPPORTED: return "outside this build's limits";
+    default: return "unknown status";
+  }
+}
+
+size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, int nq) {
+  (void)D;
+  (void)r;
+  if (check_dims(dims) != LCR_OK || K < 0 || nq < 0) return 0;
+  const RouteDims dm = to_route_dims(dims);
+  switch (op) {
+    case LCR_OP_ROUTE_SCORE_TOPK:
+      return (K > 0 && nq > 0) ? score_ws_bytes(dm, nq) : 0;
+    case LCR_OP_ROUTED_ATTENTION:
+      return nq > 0 ? plan_routed_attention(dm, K, nq).ws : 0;
+    default:
+      return 0;
+  }
+}
+
+int lcr_chunk_summary(const lcr_dims* dims, const void* q, const void* k, float scale, float* s, float* H,
+                      void* stream) {
+  const int st = check_chunk_summary(dims, q, k, scale, s, H);
+  if (st != LCR_OK) return st;
+  return hip_status(launch_chunk_summary(to_route_dims(dims), q, k, scale, s, H, (hipStream_t)stream));
+}
+
+int lcr_route_score_topk(const lcr_dims* dims, const void* q, const void* x, const void* A, const void* Bm,
+                         int D, int r, const float* s, const float* H, float beta, float scale, int K,
+                         int radius, int q0, int nq, int32_t* idx, float* zsel, void* ws, size_t ws_bytes,
+                         void* stream) {
+  const int st = check_route_score_topk(dims, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel);
+  if (st != LCR_OK) return st;
+  if (K == 0 || nq == 0) return LCR_OK;
+  const RouteDims dm = to_route_dims(dims);
+  const size_t need = score_ws_bytes(dm, nq);
+  if (ws == nullptr || ws_bytes < need) return LCR_ERR_WORKSPACE;
+  return hip_status(launch_route_score_topk(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx,
+                                            zsel, score_ws_carve(ws, dm, nq), (hipStream_t)stream));
+}
+
+int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, const void* v, const int32_t* idx,
+                         const float* zsel, int K, int radius, float scale, int q0, int nq, void* o, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_routed_attention(dims, q, k, v, idx, zsel, K, radius, scale, q0, nq, o);
+  if (st != LCR_OK) return st;
+  if (nq == 0) return LCR_OK;
+  const RouteDims dm = to_route_dims(dims);
+  const AttnPlan plan = plan_routed_attention(dm, K, nq);
+  if (plan.lds > routed_lds_limit()) return LCR_ERR_UNSUPPORTED;
+  if (plan.ws > 0 && (ws == nullptr || ws_bytes < plan.ws)) return LCR_ERR_WORKSPACE;
+  return hip_status(launch_routed_attention(dm, plan, q, k, v, K > 0 ? idx : nullptr, K > 0 ? zsel : nullptr, K,
+                                            radius, scale, q0, nq, o, lse, ws, (hipStream_t)stream));
+}
+
+int lcr_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, const void* k, const void* v,
+                      int radius, float scale, void* o, float* lse, void* stream) {
+  const int st = check_swa(B, Hq, Hkv, L, d, dtype, q, k, v, radius, scale, o);
+  if (st != LCR_OK) return st;
+  if (swa_lds_bytes(d, dtype) > routed_lds_limit()) return LCR_ERR_UNSUPPORTED;
+  return hip_status(
+      launch_swa_attention(B, Hq, Hkv, L, d, dtype, q, k, v, radius, scale, o, lse, (hipStream_t)stream));
+}
+
+}  // extern "C"

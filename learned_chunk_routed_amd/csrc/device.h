@@ -1,0 +1,147 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion and splitting,
+// 16x16x32 bf16 MFMA fragments, LDS transpose reads, wave reductions.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 operand layout (lane l of a 64-wide wave):
+//   A[m][k]: lane l holds m = l%16, k = 8*(l/16) + j (j = 0..7)
+//   B[k][n]: lane l holds n = l%16, k = 8*(l/16) + j
+//   D[m][n]: lane l holds n = l%16, m = 4*(l/16) + i (i = 0..3)
+// Only the M/N/D placement matters for correctness: A and B share the same
+// lane -> k assignment, so any consistent permutation of k is a valid product.
+//
+// ds_read_b64_tr_b16: within each 16-lane group, lane L supplies an 8-byte
+// address; lane L receives element (L%4) of the row addressed by lane
+// 4*j + L/4 as its j-th 16-bit value (j = 0..3). Supplying, from lane L, the
+// address of M[k0 + L/4][n0 + 4*(L%4)] gives lane L the column
+// M[k0 .. k0+3][n0 + L] of a row-major (n-contiguous) tile.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcr {
+
+typedef uint16_t bf16_t;
+typedef short s16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+constexpr int kSlots = 64;
+constexpr int kContent = 63;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): 16 significant bits in total.
+__device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float to_f(bf16_t v) { return bf2f(v); }
+  static __device__ __forceinline__ bf16_t from_f(float v) { return f2bf(v); }
+};
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// Pack 8 floats (bf16-rounded) into an operand fragment.
+__device__ __forceinline__ s16x8 pack8(const float* v) {
+  s16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (short)f2bf(v[j]);
+  return r;
+}
+__device__ __forceinline__ void pack8_split(const float* v, s16x8& hi, s16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bf16_t h, l;
+    split_bf16(v[j], h, l);
+    hi[j] = (short)h;
+    lo[j] = (short)l;
+  }
+}
+
+// 16-byte load of 8 bf16 values (any address space the compiler can see).
+__device__ __forceinline__ s16x8 load8(const bf16_t* p) { return *reinterpret_cast<const s16x8*>(p); }
+
+// ---------------------------------------------------------------- LDS transpose read
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ s16x4 ds_read_tr(const bf16_t* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr));
+}
+
+// Operand fragment for k-index slots (8*(l/16)+j) from a row-major LDS tile
+// M[k][n] (n contiguous, row stride `ld` elements, 8-byte aligned rows):
+// lane l receives M[k_lo + j][n0 + l%16] for j = 0..3 and M[k_hi + j][n0 + l%16]
+// for j = 4..7, where k_lo/k_hi are chosen by the caller per 16-lane group.
+__device__ __forceinline__ s16x8 lds_col_frag(const bf16_t* tile, int ld, int k_lo, int k_hi, int n0,
+                                              int lane) {
+  const int L = lane & 15;
+  const bf16_t* p0 = tile + (k_lo + (L >> 2)) * ld + n0 + 4 * (L & 3);
+  const bf16_t* p1 = tile + (k_hi + (L >> 2)) * ld + n0 + 4 * (L & 3);
+  s16x4 a = ds_read_tr(p0);
+  s16x4 b = ds_read_tr(p1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// Reduction over the four lanes {l%16 + 16*g}: they share one MFMA output column.
+__device__ __forceinline__ float col_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Order-preserving map float -> uint32 (larger float -> larger key); 0 is
+// reserved for "not a candidate" and never produced by a finite float.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return k == 0u ? 1u : k;
+}
+
+}  // namespace lcr

@@ -1,0 +1,53 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel files.
+// Every launcher assumes its arguments were validated by validate.cpp and
+// returns the HIP status of its launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lcr {
+
+struct RouteDims {
+  int B, Hq, Hkv, N, d, dtype;  // dtype: 0 = float32, 1 = bfloat16
+};
+
+// ---- chunk_summary (summary.hip)
+hipError_t launch_chunk_summary(const RouteDims& dm, const void* q, const void* k, float scale,
+                                float* s, float* H, hipStream_t st);
+
+// ---- route_score_topk (score.hip)
+struct ScoreWs {
+  float* qt;    // [B,Hq,nq,d]  routing queries q~ (float32)
+  float* zhat;  // [B,Hkv,nq,N] group maximum of the scores
+  float* z;     // [B,Hq,nq,N]  per-head scores
+};
+size_t score_ws_bytes(const RouteDims& dm, int nq);
+ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int nq);
+hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const void* x, const void* A,
+                                   const void* Bm, int D, int r, const float* s, const float* H,
+                                   float beta, float scale, int K, int radius, int q0, int nq,
+                                   int32_t* idx, float* zsel, const ScoreWs& ws, hipStream_t st);
+
+// ---- routed_attention and swa_attention (attention.hip)
+struct AttnPlan {
+  int waves;       // waves per block
+  int tiles;       // 16-row tiles per wave (a tile = 2 queries x 8 head rows)
+  int qblock;      // queries per block = 2 * waves * tiles
+  int nsplit;      // blocks sharing one query block's chunk list (partials combined after)
+  size_t lds;      // dynamic LDS bytes per block
+  size_t ws;       // workspace bytes for the split partials
+};
+AttnPlan plan_routed_attention(const RouteDims& dm, int K, int nq);
+size_t routed_lds_limit();
+hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& plan, const void* q,
+                                   const void* k, const void* v, const int32_t* idx,
+                                   const float* zsel, int K, int radius, float scale, int q0,
+                                   int nq, void* o, float* lse, void* ws, hipStream_t st);
+
+size_t swa_lds_bytes(int d, int dtype);
+hipError_t launch_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q,
+                                const void* k, const void* v, int radius, float scale, void* o,
+                                float* lse, hipStream_t st);
+
+}  // namespace lcr

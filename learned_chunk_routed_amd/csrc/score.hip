@@ -1,0 +1,409 @@
+// Residual-augmented summary scoring, GQA maximum and exact top-K selection.
+// "Prefilling-dLLM v2: Learned Chunk Routing for Long-Context Diffusion Language
+// Models", Figure 3 caption: a content query adds a low-rank residual and scores
+// the summaries; the scores are reduced by a maximum inside each GQA group and
+// the top K chunks are shared by every head of the group. Table 3: the remote
+// chunks are gathered beyond the local window. "The 172x Speedup Has an Evidence
+// Budget": rank-64 residual; similarity and pooling entropy rank the chunks.
+//
+// Three kernels:
+//  1. qtilde_kernel: u = x A (MFMA, bf16 products exact in float32), then
+//     q~ = q + u B per head with u split into bf16 hi + lo (B is exact in bf16),
+//     written as float32 rows.
+//  2. score_kernel: z = scale * q~ . s - beta * H per head on MFMA with both
+//     operands split into bf16 planes (hi + lo for bf16 inputs: hi.hi + hi.lo +
+//     lo.hi; hi + mid + lo for float32 inputs), float32 accumulation:
+//     near-float32 scores so the top-K set matches an exact computation
+//     wherever the K-th/(K+1)-th margin is not tiny, and the
+//     group maximum zhat. Summaries are the MFMA rows (M = chunks), queries
+//     the columns (N = 16 queries).
+//  3. topk_kernel: one wave per (batch, group, query): candidates are tested
+//     from their indices, the K-th largest score is found by bisection on an
+//     order-preserving integer key, and the chosen chunks are compacted in
+//     ascending order with ballots (ties go to the smaller index). zsel is
+//     gathered from the per-head scores.
+#include "device.h"
+#include "launch.h"
+
+namespace lcr {
+
+__device__ __forceinline__ long long slot_of(long long i) { return (i / kContent) * kSlots + (i % kContent); }
+
+// Load 8 consecutive elements [k, k+8) of a row of length n as floats (zero beyond n).
+template <typename T>
+__device__ __forceinline__ void load_row8(const T* row, long long k, long long n, float* out) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = (k + j < n) ? Elem<T>::to_f(row[k + j]) : 0.f;
+}
+template <>
+__device__ __forceinline__ void load_row8<bf16_t>(const bf16_t* row, long long k, long long n, float* out) {
+  if (k + 8 <= n && ((k & 7) == 0) && ((((uintptr_t)row) & 15) == 0)) {
+    s16x8 v = load8(row + k);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = bf2f((bf16_t)v[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = (k + j < n) ? bf2f(row[k + j]) : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------- 1. q~
+
+template <typename T, int D, int RP>
+__global__ __launch_bounds__(64) void qtilde_kernel(const T* __restrict__ q, const T* __restrict__ x,
+                                                    const T* __restrict__ A, const T* __restrict__ Bm,
+                                                    int Dh, int r, float* __restrict__ qt, int Hq,
+                                                    int N, int q0, int nq) {
+  constexpr bool kSplit = sizeof(T) == 4;       // float32 inputs: split both operands
+  constexpr int AS = RP + 16;                    // LDS row strides (bank-conflict-free tr reads)
+  constexpr int BS = D + 16;
+  __shared__ __align__(16) bf16_t a_hi[32 * AS];
+  __shared__ __align__(16) bf16_t a_lo[kSplit ? 32 * AS : 1];
+  __shared__ __align__(16) bf16_t b_hi[RP * BS];
+  __shared__ __align__(16) bf16_t b_lo[kSplit ? RP * BS : 1];
+  __shared__ float u_s[16][RP + 1];
+
+  const int lane = threadIdx.x, g16 = lane >> 4, L16 = lane & 15;
+  const int t0 = blockIdx.x * 16, b = blockIdx.y;
+  const long long L = (long long)N * kSlots;
+
+  // ---- u = x A, rows t0..t0+15
+  f32x4 acc_u[RP / 16];
+#pragma unroll
+  for (int nt = 0; nt < RP / 16; ++nt) acc_u[nt] = zero4();
+  const int my_t = t0 + L16;
+  const T* xrow = (my_t < nq) ? x + ((size_t)b * L + slot_of((long long)q0 + my_t)) * Dh : nullptr;
+  for (int k0 = 0; k0 < Dh; k0 += 32) {
+    for (int e = lane; e < 32 * RP; e += 64) {
+      const int kk = e / RP, n = e - kk * RP;
+      const float val = (k0 + kk < Dh && n < r) ? Elem<T>::to_f(A[(size_t)(k0 + kk) * r + n]) : 0.f;
+      if (kSplit) {
+        bf16_t h, l;
+        split_bf16(val, h, l);
+        a_hi[kk * AS + n] = h;
+        a_lo[kk * AS + n] = l;
+      } else {
+        a_hi[kk * AS + n] = f2bf(val);
+      }
+    }
+    __syncthreads();
+    float xv[8];
+    if (xrow) load_row8<T>(xrow, k0 + 8 * g16, Dh, xv);
+    else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = 0.f;
+    }
+    s16x8 xh, xl;
+    if (kSplit) pack8_split(xv, xh, xl);
+    else xh = pack8(xv);
+#pragma unroll
+    for (int nt = 0; nt < RP / 16; ++nt) {
+      const s16x8 bh = lds_col_frag(a_hi, AS, 8 * g16, 8 * g16 + 4, 16 * nt, lane);
+      acc_u[nt] = mfma16(xh, bh, acc_u[nt]);
+      if (kSplit) {
+        const s16x8 bl = lds_col_frag(a_lo, AS, 8 * g16, 8 * g16 + 4, 16 * nt, lane);
+        acc_u[nt] = mfma16(xh, bl, acc_u[nt]);
+        acc_u[nt] = mfma16(xl, bh, acc_u[nt]);
+      }
+    }
+    __syncthreads();
+  }
+  // D layout: lane holds u[row 4*g16 + i][col 16*nt + L16]
+#pragma unroll
+  for (int nt = 0; nt < RP / 16; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u_s[4 * g16 + i][16 * nt + L16] = acc_u[nt][i];
+  __syncthreads();
+
+  // ---- u fragments (A operand, k = rank index), split into hi + lo
+  s16x8 uh[RP / 32], ul[RP / 32];
+#pragma unroll
+  for (int ks = 0; ks < RP / 32; ++ks) {
+    float uv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) uv[j] = u_s[L16][32 * ks + 8 * g16 + j];
+    pack8_split(uv, uh[ks], ul[ks]);
+  }
+
+  // ---- q~ = q + u B_h for every head
+  for (int h = 0; h < Hq; ++h) {
+    for (int e = lane; e < RP * D; e += 64) {
+      const int kk = e / D, n = e - kk * D;
+      const float val = (kk < r) ? Elem<T>::to_f(Bm[(size_t)kk * Hq * D + (size_t)h * D + n]) : 0.f;
+      if (kSplit) {
+        bf16_t hh, ll;
+        split_bf16(val, hh, ll);
+        b_hi[kk * BS + n] = hh;
+        b_lo[kk * BS + n] = ll;
+      } else {
+        b_hi[kk * BS + n] = f2bf(val);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < RP / 32; ++ks) {
+        const s16x8 bh = lds_col_frag(b_hi, BS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+        acc = mfma16(ul[ks], bh, acc);
+        if (kSplit) {
+          const s16x8 bl = lds_col_frag(b_lo, BS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+          acc = mfma16(uh[ks], bl, acc);
+        }
+        acc = mfma16(uh[ks], bh, acc);
+      }
+      const int dd = 16 * nt + L16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * g16 + i;
+        if (t < nq) {
+          const long long sl = slot_of((long long)q0 + t);
+          const float qv = Elem<T>::to_f(q[((size_t)b * Hq + h) * L * D + (size_t)sl * D + dd]);
+          qt[(((size_t)b * Hq + h) * nq + t) * D + dd] = qv + acc[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------- 2. scores
+
+// Split a float into NS bf16 planes (2: 16 significant bits, 3: 24 bits).
+template <int NS>
+__device__ __forceinline__ void split_ns(const float* v, s16x8* out) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bf16_t h = f2bf(v[j]);
+    const float r = v[j] - bf2f(h);
+    out[0][j] = (short)h;
+    if constexpr (NS == 2) {
+      out[1][j] = (short)f2bf(r);
+    } else {
+      const bf16_t m = f2bf(r);
+      out[1][j] = (short)m;
+      out[2][j] = (short)f2bf(r - bf2f(m));
+    }
+  }
+}
+
+// NS = 2 for bf16 inputs (hi.hi + hi.lo + lo.hi), 3 for float32 inputs (six plane pairs).
+template <int D, int NS>
+__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qt, const float* __restrict__ s,
+                                                    const float* __restrict__ H, float beta, float scale,
+                                                    float* __restrict__ z, float* __restrict__ zhat,
+                                                    int Hq, int Hkv, int N, int nq) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const int c0 = blockIdx.x * 64 + 16 * w, t0 = blockIdx.y * 16;
+  const int bg = blockIdx.z, b = bg / Hkv, g = bg - b * Hkv;
+  const int G = Hq / Hkv;
+  const int ca = c0 + L16;   // A-operand row (chunk) of this lane
+  const int tb = t0 + L16;   // B-operand column (query) of this lane
+  float zmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    const float* srow = s + (((size_t)b * Hq + h) * N + (ca < N ? ca : 0)) * D;
+    const float* qrow = qt + (((size_t)b * Hq + h) * nq + (tb < nq ? tb : 0)) * D;
+    f32x4 acc_hi = zero4(), acc_x = zero4();
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      float av[8], bv[8];
+      const int kk = 32 * ks + 8 * g16;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(srow + kk);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(srow + kk + 4);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(qrow + kk);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(qrow + kk + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        av[j] = ca < N ? a0[j] : 0.f;
+        av[4 + j] = ca < N ? a1[j] : 0.f;
+        bv[j] = tb < nq ? b0[j] : 0.f;
+        bv[4 + j] = tb < nq ? b1[j] : 0.f;
+      }
+      s16x8 a[NS], bb[NS];
+      split_ns<NS>(av, a);
+      split_ns<NS>(bv, bb);
+      if constexpr (NS == 3) {
+        acc_x = mfma16(a[0], bb[2], acc_x);
+        acc_x = mfma16(a[2], bb[0], acc_x);
+        acc_x = mfma16(a[1], bb[1], acc_x);
+      }
+      acc_x = mfma16(a[0], bb[1], acc_x);
+      acc_x = mfma16(a[1], bb[0], acc_x);
+      acc_hi = mfma16(a[0], bb[0], acc_hi);
+    }
+    // D layout: lane holds chunk c0 + 4*g16 + i (rows), query t0 + L16 (column)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + 4 * g16 + i;
+      const int t = t0 + L16;
+      if (c < N && t < nq) {
+        const float zz = (acc_hi[i] + acc_x[i]) * scale - beta * H[((size_t)b * Hq + h) * N + c];
+        z[(((size_t)b * Hq + h) * nq + t) * N + c] = zz;
+        zmax[i] = fmaxf(zmax[i], zz);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = c0 + 4 * g16 + i;
+    const int t = t0 + L16;
+    if (c < N && t < nq) zhat[((size_t)bg * nq + t) * N + c] = zmax[i];
+  }
+}
+
+// ---------------------------------------------------------------------------- 3. top-K
+
+template <int P>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zhat, const float* __restrict__ z,
+                                                   int32_t* __restrict__ idx, float* __restrict__ zsel,
+                                                   int Hq, int Hkv, int N, int nq, int q0, int K, int R,
+                                                   long long nrows) {
+  __shared__ int chosen[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + w;
+  const bool live = row < nrows;
+  const long long rr = live ? row : 0;
+  const int t = (int)(rr % nq);
+  const long long bg = rr / nq;
+  const int b = (int)(bg / Hkv), g = (int)(bg % Hkv);
+  const int G = Hq / Hkv;
+  const long long i = (long long)q0 + t;
+  const float* zr = zhat + rr * N;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+
+  uint32_t key[P];
+  int nloc = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int c = 64 * j + lane;
+    const bool cand = c < N && ((63LL * c + 62 < i - R) || (63LL * c > i + R));
+    key[j] = cand ? order_key(zr[c]) : 0u;
+    nloc += key[j] != 0u;
+  }
+  const int ncand = wave_sum_i(nloc);
+  const bool take_all = ncand <= K;
+  uint32_t theta = 0u;
+  int need = 0;
+  if (!take_all) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t trial = theta | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < P; ++j) cnt += key[j] >= trial;
+      if (wave_sum_i(cnt) >= K) theta = trial;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) gt += key[j] > theta;
+    need = K - wave_sum_i(gt);
+  }
+  int base = 0, ties = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const bool nz = key[j] != 0u;
+    const bool gt = take_all ? nz : key[j] > theta;
+    const bool eq = !take_all && nz && key[j] == theta;
+    const unsigned long long em = __ballot(eq);
+    const bool take = gt || (eq && ties + __popcll(em & lt) < need);
+    const unsigned long long tm = __ballot(take);
+    if (take) chosen[w][base + __popcll(tm & lt)] = 64 * j + lane;
+    base += __popcll(tm);
+    ties += __popcll(em);
+  }
+  __syncthreads();
+  if (live && lane < K) {
+    const int c = lane < base ? chosen[w][lane] : -1;
+    idx[rr * K + lane] = c;
+    for (int hh = 0; hh < G; ++hh) {
+      const size_t hrow = ((size_t)b * Hq + g * G + hh) * nq + t;
+      zsel[hrow * K + lane] = c >= 0 ? z[hrow * N + c] : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- host side
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t score_ws_bytes(const RouteDims& dm, int nq) {
+  const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
+  return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4);
+}
+
+ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int nq) {
+  const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
+  char* p = (char*)ws;
+  ScoreWs out;
+  out.qt = (float*)p;
+  p += align256(rows_h * dm.d * 4);
+  out.zhat = (float*)p;
+  p += align256(rows_g * dm.N * 4);
+  out.z = (float*)p;
+  return out;
+}
+
+template <typename T, int D, int RP>
+static void launch_qtilde(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
+                          int Dh, int r, float* qt, int q0, int nq, hipStream_t st) {
+  dim3 grid((nq + 15) / 16, dm.B);
+  hipLaunchKernelGGL((qtilde_kernel<T, D, RP>), grid, dim3(64), 0, st, (const T*)q, (const T*)x,
+                     (const T*)A, (const T*)Bm, Dh, r, qt, dm.Hq, dm.N, q0, nq);
+}
+
+template <typename T, int D>
+static void launch_qtilde_r(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
+                            int Dh, int r, float* qt, int q0, int nq, hipStream_t st) {
+  if (r <= 32) launch_qtilde<T, D, 32>(dm, q, x, A, Bm, Dh, r, qt, q0, nq, st);
+  else if (r <= 64) launch_qtilde<T, D, 64>(dm, q, x, A, Bm, Dh, r, qt, q0, nq, st);
+  else launch_qtilde<T, D, 128>(dm, q, x, A, Bm, Dh, r, qt, q0, nq, st);
+}
+
+template <int P>
+static void launch_topk(const RouteDims& dm, const ScoreWs& ws, int32_t* idx, float* zsel, int q0, int nq,
+                        int K, int R, hipStream_t st) {
+  const long long nrows = (long long)dm.B * dm.Hkv * nq;
+  hipLaunchKernelGGL((topk_kernel<P>), dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, ws.zhat, ws.z, idx,
+                     zsel, dm.Hq, dm.Hkv, dm.N, nq, q0, K, R, nrows);
+}
+
+hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const void* x, const void* A,
+                                   const void* Bm, int D, int r, const float* s, const float* H,
+                                   float beta, float scale, int K, int radius, int q0, int nq,
+                                   int32_t* idx, float* zsel, const ScoreWs& ws, hipStream_t st) {
+  if (dm.dtype == 1) {
+    if (dm.d == 64) launch_qtilde_r<bf16_t, 64>(dm, q, x, A, Bm, D, r, ws.qt, q0, nq, st);
+    else launch_qtilde_r<bf16_t, 128>(dm, q, x, A, Bm, D, r, ws.qt, q0, nq, st);
+  } else {
+    if (dm.d == 64) launch_qtilde_r<float, 64>(dm, q, x, A, Bm, D, r, ws.qt, q0, nq, st);
+    else launch_qtilde_r<float, 128>(dm, q, x, A, Bm, D, r, ws.qt, q0, nq, st);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((dm.N + 63) / 64, (nq + 15) / 16, dm.B * dm.Hkv);
+#define LCR_SCORE(DD, NS)                                                                              \
+  hipLaunchKernelGGL((score_kernel<DD, NS>), grid, dim3(256), 0, st, ws.qt, s, H, beta, scale, ws.z, ws.zhat, \
+                     dm.Hq, dm.Hkv, dm.N, nq)
+  if (dm.d == 64) {
+    if (dm.dtype == 1) LCR_SCORE(64, 2);
+    else LCR_SCORE(64, 3);
+  } else {
+    if (dm.dtype == 1) LCR_SCORE(128, 2);
+    else LCR_SCORE(128, 3);
+  }
+#undef LCR_SCORE
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int P = (dm.N + 63) / 64;
+  if (P <= 1) launch_topk<1>(dm, ws, idx, zsel, q0, nq, K, radius, st);
+  else if (P <= 2) launch_topk<2>(dm, ws, idx, zsel, q0, nq, K, radius, st);
+  else if (P <= 4) launch_topk<4>(dm, ws, idx, zsel, q0, nq, K, radius, st);
+  else if (P <= 8) launch_topk<8>(dm, ws, idx, zsel, q0, nq, K, radius, st);
+  else if (P <= 16) launch_topk<16>(dm, ws, idx, zsel, q0, nq, K, radius, st);
+  else if (P <= 32) launch_topk<32>(dm, ws, idx, zsel, q0, nq, K, radius, st);
+  else launch_topk<64>(dm, ws, idx, zsel, q0, nq, K, radius, st);
+  return hipGetLastError();
+}
+
+}  // namespace lcr

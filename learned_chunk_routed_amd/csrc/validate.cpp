@@ -1,0 +1,89 @@
+// Host-side argument checks (see validate.h). No HIP dependency.
+#include "validate.h"
+
+#include <cmath>
+#include <limits>
+
+namespace lcr {
+
+static bool finite(float x) { return std::isfinite(x); }
+
+int check_dims(const lcr_dims* d) {
+  if (d == nullptr) return LCR_ERR_ARG;
+  if (d->dtype != LCR_F32 && d->dtype != LCR_BF16) return LCR_ERR_DTYPE;
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->N < 1 || d->d < 1) return LCR_ERR_ARG;
+  if (d->Hq % d->Hkv != 0) return LCR_ERR_ARG;
+  if (d->d != 64 && d->d != 128) return LCR_ERR_UNSUPPORTED;
+  if (d->Hq / d->Hkv > LCR_MAX_GROUP) return LCR_ERR_UNSUPPORTED;
+  // 64*N slots must be indexable and the grids must fit.
+  if ((long long)d->N * LCR_CHUNK_SLOTS > (long long)std::numeric_limits<int>::max()) return LCR_ERR_ARG;
+  if ((long long)d->B * d->Hkv > 65535) return LCR_ERR_UNSUPPORTED;
+  return LCR_OK;
+}
+
+int check_chunk_summary(const lcr_dims* d, const void* q, const void* k, float scale, const float* s,
+                        const float* H) {
+  int st = check_dims(d);
+  if (st != LCR_OK) return st;
+  if (!q || !k || !s || !H) return LCR_ERR_ARG;
+  if (!finite(scale)) return LCR_ERR_ARG;
+  return LCR_OK;
+}
+
+static int check_query_range(const lcr_dims* d, int q0, int nq) {
+  const long long T = (long long)d->N * LCR_CHUNK_CONTENT;
+  if (q0 < 0 || nq < 0) return LCR_ERR_ARG;
+  if ((long long)q0 + nq > T) return LCR_ERR_ARG;
+  return LCR_OK;
+}
+
+int check_route_score_topk(const lcr_dims* d, const void* q, const void* x, const void* A, const void* Bm,
+                           int D, int r, const float* s, const float* H, float beta, float scale, int K,
+                           int radius, int q0, int nq, const int32_t* idx, const float* zsel) {
+  int st = check_dims(d);
+  if (st != LCR_OK) return st;
+  if (D < 1 || r < 1) return LCR_ERR_ARG;
+  if (r > 128) return LCR_ERR_UNSUPPORTED;
+  if (K < 0 || radius < 0) return LCR_ERR_ARG;
+  if (K > LCR_MAX_TOPK) return LCR_ERR_UNSUPPORTED;
+  if (!finite(beta) || !finite(scale)) return LCR_ERR_ARG;
+  st = check_query_range(d, q0, nq);
+  if (st != LCR_OK) return st;
+  if (K > 0 && nq > 0) {
+    if (!q || !x || !A || !Bm || !s || !H || !idx || !zsel) return LCR_ERR_ARG;
+    if (d->N > kMaxChunksTopK) return LCR_ERR_UNSUPPORTED;
+  }
+  return LCR_OK;
+}
+
+int check_routed_attention(const lcr_dims* d, const void* q, const void* k, const void* v,
+                           const int32_t* idx, const float* zsel, int K, int radius, float scale, int q0,
+                           int nq, const void* o) {
+  int st = check_dims(d);
+  if (st != LCR_OK) return st;
+  if (K < 0 || radius < 0) return LCR_ERR_ARG;
+  if (K > LCR_MAX_TOPK) return LCR_ERR_UNSUPPORTED;
+  if (!finite(scale)) return LCR_ERR_ARG;
+  st = check_query_range(d, q0, nq);
+  if (st != LCR_OK) return st;
+  if (nq > 0) {
+    if (!q || !k || !v || !o) return LCR_ERR_ARG;
+    if (K > 0 && (!idx || !zsel)) return LCR_ERR_ARG;
+  }
+  return LCR_OK;
+}
+
+int check_swa(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, const void* k, const void* v,
+              int radius, float scale, const void* o) {
+  if (dtype != LCR_F32 && dtype != LCR_BF16) return LCR_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || d < 1 || radius < 0) return LCR_ERR_ARG;
+  if (Hq % Hkv != 0) return LCR_ERR_ARG;
+  if (d != 64 && d != 128) return LCR_ERR_UNSUPPORTED;
+  if (Hq / Hkv > LCR_MAX_GROUP) return LCR_ERR_UNSUPPORTED;
+  if ((long long)B * Hkv > 65535) return LCR_ERR_UNSUPPORTED;
+  if (!finite(scale)) return LCR_ERR_ARG;
+  if (!q || !k || !v || !o) return LCR_ERR_ARG;
+  return LCR_OK;
+}
+
+}  // namespace lcr

@@ -1,0 +1,195 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+Every step of the route layer runs in the HIP kernels of liblcr.so; this module
+checks tensors (device, dtype, contiguity, shapes), allocates outputs and
+workspace through PyTorch and passes raw device pointers plus the current HIP
+stream. There is no CPU or PyTorch fallback: a missing library raises.
+
+Shapes follow include/lcr.h: q [B,Hq,L,d], k and v [B,Hkv,L,d] with L = 64*N,
+x [B,L,D], A [D,r], Bm [r,Hq*d]; content query i lives in slot
+64*(i//63) + i%63.
+"""
+import math
+
+import torch
+
+from . import _lib
+from ._lib import Dims, check
+
+SLOTS, CONTENT = 64, 63
+
+_DTYPES = {torch.bfloat16: _lib.LCR_BF16, torch.float32: _lib.LCR_F32}
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check(t, name, device, dtype=None, shape=None):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.is_cuda and t.device == device, f"{name} must be on {device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def make_dims(B, Hq, Hkv, N, d, dtype) -> Dims:
+    _need(dtype in _DTYPES, f"unsupported dtype {dtype}")
+    return Dims(B, Hq, Hkv, N, d, _DTYPES[dtype])
+
+
+def _dims_from(q, Hkv):
+    _need(q.dim() == 4, "q must be [B,Hq,L,d]")
+    B, Hq, L, d = q.shape
+    _need(L % SLOTS == 0, f"L={L} must be a multiple of {SLOTS}")
+    return make_dims(B, Hq, Hkv, L // SLOTS, d, q.dtype)
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)
+
+
+def workspace_bytes(op, dims: Dims, D=0, r=0, K=0, nq=0) -> int:
+    return int(_lib.load().lcr_workspace_bytes(op, dims, D, r, K, nq))
+
+
+def _workspace(nbytes, device, ws=None):
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def chunk_summary(q, k, scale=None, s=None, H=None):
+    """Summary keys s [B,Hq,N,d] and pooling entropies H [B,Hq,N], float32."""
+    lib = _lib.load()
+    dev = q.device
+    dims = _dims_from(q, k.shape[1])
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (dims.B, dims.Hkv, dims.N * SLOTS, dims.d))
+    scale = default_scale(dims.d) if scale is None else float(scale)
+    if s is None:
+        s = torch.empty((dims.B, dims.Hq, dims.N, dims.d), dtype=torch.float32, device=dev)
+    if H is None:
+        H = torch.empty((dims.B, dims.Hq, dims.N), dtype=torch.float32, device=dev)
+    _check(s, "s", dev, torch.float32, (dims.B, dims.Hq, dims.N, dims.d))
+    _check(H, "H", dev, torch.float32, (dims.B, dims.Hq, dims.N))
+    check(lib.lcr_chunk_summary(dims, q.data_ptr(), k.data_ptr(), scale, s.data_ptr(), H.data_ptr(),
+                                _stream(dev)), "lcr_chunk_summary")
+    return s, H
+
+
+def route_score_topk(q, x, A, Bm, s, H, *, Hkv, K, radius, beta=0.0, scale=None, q0=0, nq=None,
+                     idx=None, zsel=None, ws=None):
+    """Chosen remote chunks idx [B,Hkv,nq,K] (int32, ascending, -1 padded) and the
+    per-head scores of the chosen chunks zsel [B,Hq,nq,K] (float32)."""
+    lib = _lib.load()
+    dev = q.device
+    dims = _dims_from(q, Hkv)
+    B, Hq, N, d = dims.B, dims.Hq, dims.N, dims.d
+    T = N * CONTENT
+    nq = T - q0 if nq is None else nq
+    _check(q, "q", dev)
+    _need(x.dim() == 3 and x.shape[:2] == (B, N * SLOTS), "x must be [B,L,D]")
+    D = x.shape[2]
+    _need(A.dim() == 2 and A.shape[0] == D, "A must be [D,r]")
+    r = A.shape[1]
+    _check(x, "x", dev, q.dtype)
+    _check(A, "A", dev, q.dtype)
+    _check(Bm, "Bm", dev, q.dtype, (r, Hq * d))
+    _check(s, "s", dev, torch.float32, (B, Hq, N, d))
+    _check(H, "H", dev, torch.float32, (B, Hq, N))
+    scale = default_scale(d) if scale is None else float(scale)
+    if idx is None:
+        idx = torch.empty((B, Hkv, nq, K), dtype=torch.int32, device=dev)
+    if zsel is None:
+        zsel = torch.empty((B, Hq, nq, K), dtype=torch.float32, device=dev)
+    _check(idx, "idx", dev, torch.int32, (B, Hkv, nq, K))
+    _check(zsel, "zsel", dev, torch.float32, (B, Hq, nq, K))
+    nbytes = workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims, D, r, K, nq)
+    w = _workspace(nbytes, dev, ws)
+    check(lib.lcr_route_score_topk(dims, q.data_ptr(), x.data_ptr(), A.data_ptr(), Bm.data_ptr(), D, r,
+                                   s.data_ptr(), H.data_ptr(), float(beta), scale, K, radius, q0, nq,
+                                   idx.data_ptr(), zsel.data_ptr(), None if w is None else w.data_ptr(),
+                                   nbytes, _stream(dev)), "lcr_route_score_topk")
+    return idx, zsel
+
+
+def routed_attention(q, k, v, idx, zsel, *, radius, scale=None, q0=0, nq=None, out=None, lse=None,
+                     want_lse=False, ws=None):
+    """Route-layer output o [B,Hq,L,d] (rows of the queried content positions written;
+    other rows of a freshly allocated `out` are zero) and optionally lse [B,Hq,nq]."""
+    lib = _lib.load()
+    dev = q.device
+    dims = _dims_from(q, k.shape[1])
+    B, Hq, Hkv, N, d = dims.B, dims.Hq, dims.Hkv, dims.N, dims.d
+    T = N * CONTENT
+    nq = T - q0 if nq is None else nq
+    K = idx.shape[-1]
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (B, Hkv, N * SLOTS, d))
+    _check(v, "v", dev, q.dtype, (B, Hkv, N * SLOTS, d))
+    _check(idx, "idx", dev, torch.int32, (B, Hkv, nq, K))
+    _check(zsel, "zsel", dev, torch.float32, (B, Hq, nq, K))
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.zeros_like(q)
+    _check(out, "out", dev, q.dtype, tuple(q.shape))
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, nq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", dev, torch.float32, (B, Hq, nq))
+    nbytes = workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims, 0, 0, K, nq)
+    w = _workspace(nbytes, dev, ws)
+    check(lib.lcr_routed_attention(dims, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+                                   zsel.data_ptr(), K, radius, scale, q0, nq, out.data_ptr(),
+                                   None if lse is None else lse.data_ptr(), None if w is None else w.data_ptr(),
+                                   nbytes, _stream(dev)), "lcr_routed_attention")
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def swa_attention(q, k, v, *, radius, scale=None, out=None, lse=None, want_lse=False):
+    """Bidirectional sliding-window attention over slots |u - t| <= radius: o [B,Hq,L,d]."""
+    lib = _lib.load()
+    dev = q.device
+    _need(q.dim() == 4 and k.dim() == 4, "q, k, v must be [B,H,L,d]")
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    _need(q.dtype in _DTYPES, f"unsupported dtype {q.dtype}")
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (B, Hkv, L, d))
+    _check(v, "v", dev, q.dtype, (B, Hkv, L, d))
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dev, q.dtype, tuple(q.shape))
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", dev, torch.float32, (B, Hq, L))
+    check(lib.lcr_swa_attention(B, Hq, Hkv, L, d, _DTYPES[q.dtype], q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                radius, scale, out.data_ptr(), None if lse is None else lse.data_ptr(),
+                                _stream(dev)), "lcr_swa_attention")
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def route_layer(q, k, v, x, A, Bm, *, K, radius, beta=0.0, scale=None, q0=0, nq=None, out=None,
+                want_lse=False, s=None, H=None):
+    """Whole route layer: summaries (unless s and H are given), scoring + top-K,
+    routed attention. Returns a dict with s, H, idx, zsel, o (and lse)."""
+    if s is None or H is None:
+        s, H = chunk_summary(q, k, scale)
+    idx, zsel = route_score_topk(q, x, A, Bm, s, H, Hkv=k.shape[1], K=K, radius=radius, beta=beta,
+                                 scale=scale, q0=q0, nq=nq)
+    res = routed_attention(q, k, v, idx, zsel, radius=radius, scale=scale, q0=q0, nq=nq, out=out,
+                           want_lse=want_lse)
+    o, lse = res if isinstance(res, tuple) else (res, None)
+    return dict(s=s, H=H, idx=idx, zsel=zsel, o=o, lse=lse)

@@ -1,0 +1,172 @@
+"""The C ABI on the host: the library loads, exports every declared entry point, and
+rejects invalid arguments with the documented status codes before any launch
+(CPU only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from learned_chunk_routed_amd import _lib
+from learned_chunk_routed_amd._lib import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcr.h")
+P = ctypes.c_void_p(4096)          # a non-null pointer that is never dereferenced on the host
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("liblcr.so is not built (run python -m learned_chunk_routed_amd.build)")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(lcr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ["lcr_chunk_summary", "lcr_route_score_topk", "lcr_routed_attention", "lcr_swa_attention",
+              "lcr_workspace_bytes", "lcr_status_string", "lcr_version"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (lcr_[a-z_]+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in declared_functions():
+        assert hasattr(lib, n)
+    assert set(_lib.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code in [0, -1, -2, -3, -4, -5]:
+        assert lib.lcr_status_string(code)
+    assert lib.lcr_status_string(0) == b"ok"
+    assert lib.lcr_version() >= 10000
+
+
+def dims(**kw):
+    base = dict(B=1, Hq=28, Hkv=4, N=256, d=128, dtype=1)
+    base.update(kw)
+    return Dims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _lib.LCR_ERR_DTYPE),
+    (dict(B=0), _lib.LCR_ERR_ARG),
+    (dict(Hq=27), _lib.LCR_ERR_ARG),
+    (dict(N=0), _lib.LCR_ERR_ARG),
+    (dict(d=96), _lib.LCR_ERR_UNSUPPORTED),
+    (dict(Hq=36, Hkv=4), _lib.LCR_ERR_UNSUPPORTED),
+    (dict(N=1 << 26), _lib.LCR_ERR_ARG),
+])
+def test_chunk_summary_rejects_bad_dims(lib, kw, code):
+    assert lib.lcr_chunk_summary(dims(**kw), P, P, 0.1, P, P, NULL) == code
+
+
+def test_chunk_summary_rejects_nulls_and_scale(lib):
+    assert lib.lcr_chunk_summary(None, P, P, 0.1, P, P, NULL) == _lib.LCR_ERR_ARG
+    for i in range(4):
+        ptrs = [P] * 4
+        ptrs[i] = NULL
+        assert lib.lcr_chunk_summary(dims(), ptrs[0], ptrs[1], 0.1, ptrs[2], ptrs[3], NULL) == _lib.LCR_ERR_ARG
+    assert lib.lcr_chunk_summary(dims(), P, P, float("nan"), P, P, NULL) == _lib.LCR_ERR_ARG
+
+
+def score_call(lib, dm=None, D=3584, r=64, beta=0.0, scale=0.1, K=32, R=256, q0=0, nq=100, ptrs=None,
+               ws=NULL, ws_bytes=0):
+    pt = ptrs or [P] * 8
+    return lib.lcr_route_score_topk(dm or dims(), pt[0], pt[1], pt[2], pt[3], D, r, pt[4], pt[5], beta, scale,
+                                    K, R, q0, nq, pt[6], pt[7], ws, ws_bytes, NULL)
+
+
+def test_route_score_topk_validation(lib):
+    T = 256 * 63
+    assert score_call(lib, K=-1) == _lib.LCR_ERR_ARG
+    assert score_call(lib, K=65) == _lib.LCR_ERR_UNSUPPORTED
+    assert score_call(lib, R=-1) == _lib.LCR_ERR_ARG
+    assert score_call(lib, r=0) == _lib.LCR_ERR_ARG
+    assert score_call(lib, r=129) == _lib.LCR_ERR_UNSUPPORTED
+    assert score_call(lib, D=0) == _lib.LCR_ERR_ARG
+    assert score_call(lib, q0=-1) == _lib.LCR_ERR_ARG
+    assert score_call(lib, q0=T - 10, nq=11) == _lib.LCR_ERR_ARG
+    assert score_call(lib, nq=-1) == _lib.LCR_ERR_ARG
+    assert score_call(lib, beta=float("inf")) == _lib.LCR_ERR_ARG
+    assert score_call(lib, dm=dims(N=5000)) == _lib.LCR_ERR_UNSUPPORTED
+    for i in range(8):
+        pt = [P] * 8
+        pt[i] = NULL
+        assert score_call(lib, ptrs=pt) == _lib.LCR_ERR_ARG
+    # valid arguments but no workspace: rejected before any launch
+    assert score_call(lib) == _lib.LCR_ERR_WORKSPACE
+    need = lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims(), 3584, 64, 32, 100)
+    assert score_call(lib, ws=P, ws_bytes=need - 1) == _lib.LCR_ERR_WORKSPACE
+    # nothing to do: K = 0 or nq = 0 succeed without touching the device, NULL outputs allowed
+    assert score_call(lib, K=0, ptrs=[P] * 6 + [NULL, NULL]) == _lib.LCR_OK
+    assert score_call(lib, nq=0) == _lib.LCR_OK
+
+
+def test_workspace_sizes(lib):
+    dm = dims()
+    nq = 1000
+    got = lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dm, 3584, 64, 32, nq)
+    al = lambda x: (x + 255) // 256 * 256
+    assert got == al(28 * nq * 128 * 4) + al(4 * nq * 256 * 4) + al(28 * nq * 256 * 4)
+    assert lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dm, 3584, 64, 0, nq) == 0
+    assert lib.lcr_workspace_bytes(_lib.OP_CHUNK_SUMMARY, dm, 0, 0, 0, 0) == 0
+    assert lib.lcr_workspace_bytes(_lib.OP_SWA_ATTENTION, dm, 0, 0, 0, 0) == 0
+    # prefill-sized routed attention needs no workspace; decode-sized splits need partials
+    assert lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dm, 0, 0, 32, 256 * 63) == 0
+    dec = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=2048), 0, 0, 32, 32)
+    assert dec > 0 and dec % 256 == 0
+    assert lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims(dtype=9), 1, 1, 1, 1) == 0
+
+
+def test_routed_attention_validation(lib):
+    def call(dm=None, K=32, R=256, scale=0.1, q0=0, nq=100, ptrs=None, ws=NULL, ws_bytes=0):
+        pt = ptrs or [P] * 6
+        return lib.lcr_routed_attention(dm or dims(), pt[0], pt[1], pt[2], pt[3], pt[4], K, R, scale, q0, nq,
+                                        pt[5], NULL, ws, ws_bytes, NULL)
+    assert call(K=-1) == _lib.LCR_ERR_ARG
+    assert call(K=65) == _lib.LCR_ERR_UNSUPPORTED
+    assert call(R=-5) == _lib.LCR_ERR_ARG
+    assert call(q0=256 * 63, nq=1) == _lib.LCR_ERR_ARG
+    assert call(scale=float("nan")) == _lib.LCR_ERR_ARG
+    for i in range(6):
+        pt = [P] * 6
+        pt[i] = NULL
+        assert call(ptrs=pt) == _lib.LCR_ERR_ARG
+    assert call(nq=0) == _lib.LCR_OK
+    # decode-sized problems need the partial-sum workspace
+    assert call(dm=dims(N=2048), q0=2048 * 63 - 32, nq=32) == _lib.LCR_ERR_WORKSPACE
+
+
+def test_swa_validation(lib):
+    def call(B=1, Hq=28, Hkv=4, L=4096, d=128, dtype=1, R=1280, scale=0.1, ptrs=None):
+        pt = ptrs or [P] * 4
+        return lib.lcr_swa_attention(B, Hq, Hkv, L, d, dtype, pt[0], pt[1], pt[2], R, scale, pt[3], NULL, NULL)
+    assert call(dtype=3) == _lib.LCR_ERR_DTYPE
+    assert call(L=0) == _lib.LCR_ERR_ARG
+    assert call(R=-1) == _lib.LCR_ERR_ARG
+    assert call(Hq=30) == _lib.LCR_ERR_ARG
+    assert call(d=32) == _lib.LCR_ERR_UNSUPPORTED
+    assert call(Hq=72, Hkv=4) == _lib.LCR_ERR_UNSUPPORTED
+    for i in range(4):
+        pt = [P] * 4
+        pt[i] = NULL
+        assert call(ptrs=pt) == _lib.LCR_ERR_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()
