@@ -40,13 +40,11 @@ const char* lcr_status_string(int status) {
 }
 
 size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, int nq) {
-  (void)D;
-  (void)r;
   if (check_dims(dims) != LCR_OK || K < 0 || nq < 0) return 0;
   const RouteDims dm = to_route_dims(dims);
   switch (op) {
     case LCR_OP_ROUTE_SCORE_TOPK:
-      return (K > 0 && nq > 0) ? score_ws_bytes(dm, nq) : 0;
+      return (K > 0 && nq > 0 && D > 0 && r > 0 && r <= 128) ? score_ws_bytes(dm, D, r, nq) : 0;
     case LCR_OP_ROUTED_ATTENTION:
       return nq > 0 ? plan_routed_attention(dm, K, nq).ws : 0;
     default:
@@ -69,10 +67,10 @@ int lcr_route_score_topk(const lcr_dims* dims, const void* q, const void* x, con
   if (st != LCR_OK) return st;
   if (K == 0 || nq == 0) return LCR_OK;
   const RouteDims dm = to_route_dims(dims);
-  const size_t need = score_ws_bytes(dm, nq);
+  const size_t need = score_ws_bytes(dm, D, r, nq);
   if (ws == nullptr || ws_bytes < need) return LCR_ERR_WORKSPACE;
   return hip_status(launch_route_score_topk(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx,
-                                            zsel, score_ws_carve(ws, dm, nq), (hipStream_t)stream));
+                                            zsel, score_ws_carve(ws, dm, D, r, nq), (hipStream_t)stream));
 }
 
 int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, const void* v, const int32_t* idx,

@@ -31,6 +31,8 @@
 //    kernel merges them.
 // Sliding-window attention uses the same tile machinery with 16 consecutive
 // slots of one head per tile and a band mask.
+#include <stdlib.h>
+
 #include "device.h"
 #include "launch.h"
 
@@ -147,6 +149,35 @@ struct KVStage {
   }
 };
 
+// ---------------------------------------------------------------- tile layouts in LDS
+// Padded layout (register-staged tiles): K rows of D+8 and V rows of D+16
+// elements. Swizzled layout (tiles written by direct-to-LDS loads, 1 KB of
+// consecutive LDS per wave instruction, so rows cannot be padded): rows of D
+// elements whose 16-byte blocks are permuted by an XOR of the row index, chosen
+// so that the K fragment reads (16 rows, one block each) and the V transpose
+// reads (8 rows, two blocks each, per 32 lanes) hit distinct banks.
+template <int D, bool SWZ> struct TileLayout;
+
+template <int D> struct TileLayout<D, false> {
+  static constexpr int KE = 64 * (D + 8);
+  static constexpr int VE = 64 * (D + 16);
+  static constexpr int PL = KE + VE;
+  __device__ static __forceinline__ int k_off(int row, int cb) { return row * (D + 8) + cb * 8; }
+  __device__ static __forceinline__ int v_off(int row, int col) { return row * (D + 16) + col; }
+};
+
+template <int D> struct TileLayout<D, true> {
+  static constexpr int KE = 64 * D;
+  static constexpr int VE = 64 * D;
+  static constexpr int PL = KE + VE;
+  __device__ static __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  __device__ static __forceinline__ int swz_v(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
+  __device__ static __forceinline__ int k_off(int row, int cb) { return row * D + ((cb ^ swz_k(row)) << 3); }
+  __device__ static __forceinline__ int v_off(int row, int col) {
+    return row * D + (((col >> 3) ^ swz_v(row)) << 3) + (col & 7);
+  }
+};
+
 // ---------------------------------------------------------------- per-tile fragments and products
 
 template <int D, int NP> struct QFrag {
@@ -180,27 +211,32 @@ __device__ __forceinline__ void load_qfrag(QFrag<D, NP>& q, const T* row, int la
 }
 
 // S^T for 64 key slots x 16 rows: acc[mt] holds keys 16*mt + 4*(l/16) + i, row l%16.
-template <int D, int NP>
+template <int D, int NP, bool SWZ>
 __device__ __forceinline__ void s_tile(const bf16_t* buf, const QFrag<D, NP>& q, f32x4 acc[4], int lane) {
+  typedef TileLayout<D, SWZ> TL;
   const int L16 = lane & 15, g16 = lane >> 4;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     acc[mt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      const int off = (16 * mt + L16) * KV<D>::KS + 32 * ks + 8 * g16;
+      const int off = TL::k_off(16 * mt + L16, 4 * ks + g16);
       s16x8 a[NP];
 #pragma unroll
-      for (int pl = 0; pl < NP; ++pl) a[pl] = load8(buf + pl * KV<D>::PL + off);
+      for (int pl = 0; pl < NP; ++pl) a[pl] = load8(buf + pl * TL::PL + off);
       acc[mt] = mfma_planes<NP>(a, q.f[ks], acc[mt]);
     }
   }
 }
 
 // O^T[d][row] += sum_key V[key][d] p[row][key] with p in the S^T output layout.
-template <int D, int NP>
+// The V^T operand is read with ds_read_b64_tr_b16: lane L of each 16-lane group
+// addresses row k0 + L/4, columns 16*dm + 4*(L%4) .. +3, and receives the column
+// 16*dm + L over rows k0 .. k0+3.
+template <int D, int NP, bool SWZ>
 __device__ __forceinline__ void pv_tile(const bf16_t* buf, const float p[4][4], f32x4 o[D / 16], int lane) {
-  const int g16 = lane >> 4;
+  typedef TileLayout<D, SWZ> TL;
+  const int g16 = lane >> 4, L16 = lane & 15;
   s16x8 pf[2][NP];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
@@ -216,14 +252,222 @@ __device__ __forceinline__ void pv_tile(const bf16_t* buf, const float p[4][4], 
   for (int dm = 0; dm < D / 16; ++dm) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      const int r0 = 32 * ks + 4 * g16 + (L16 >> 2);
+      const int col = 16 * dm + 4 * (L16 & 3);
+      const int o0 = TL::KE + TL::v_off(r0, col);
+      const int o1 = TL::KE + TL::v_off(r0 + 16, col);
       s16x8 a[NP];
 #pragma unroll
-      for (int pl = 0; pl < NP; ++pl)
-        a[pl] = lds_col_frag(buf + pl * KV<D>::PL + 64 * KV<D>::KS, KV<D>::VS, 32 * ks + 4 * g16,
-                             32 * ks + 16 + 4 * g16, 16 * dm, lane);
+      for (int pl = 0; pl < NP; ++pl) {
+        const s16x4 lo = ds_read_tr(buf + pl * TL::PL + o0);
+        const s16x4 hi = ds_read_tr(buf + pl * TL::PL + o1);
+        a[pl] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
       o[dm] = mfma_planes<NP>(a, pf[ks], o[dm]);
     }
   }
+}
+
+// Online-softmax update of one 16-row tile for one chunk (or band tile).
+// mode 1: window keys (logits of in-window content keys); mode 2: selected
+// chunk (its 63 content keys normalised inside the chunk, then weighted by
+// e^{zc}); mode 0: nothing. x holds the raw S^T scores on entry and the
+// probabilities to multiply with V on exit; returns the factor that rescales
+// the row's accumulator. Window membership of key j: lo <= j <= hi (chunk-local
+// key indices, slot 63 excluded by the caller through hi).
+__device__ __forceinline__ float tile_update(float x[4][4], int mode, int lo, int hi, float zc, float sl2,
+                                             int g16, float& m, float& l) {
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 16 * mt + 4 * g16 + i;
+      const bool ok = mode != 0 && key >= lo && key <= hi;
+      const float xv = ok ? x[mt][i] * sl2 : -INFINITY;
+      x[mt][i] = xv;
+      mloc = fmaxf(mloc, xv);
+    }
+  const float mb = col_max(mloc);
+  const float m_old = m;
+  const float pbase = mode == 1 ? fmaxf(m_old, mb) : (mode == 2 ? mb : 0.f);
+  float psum = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(x[mt][i] - pbase);
+      x[mt][i] = e;
+      psum += e;
+    }
+  const float rs = col_sum(psum);
+  float alpha = 1.f;
+  if (mode == 1) {
+    alpha = fast_exp2(m_old - pbase);
+    l = l * alpha + rs;
+    m = pbase;
+  } else if (mode == 2) {
+    const float m_new = fmaxf(m_old, zc);
+    alpha = fast_exp2(m_old - m_new);
+    const float wz = fast_exp2(zc - m_new);
+    const float ws = wz / rs;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[mt][i] *= ws;
+    l = l * alpha + wz;
+    m = m_new;
+  }
+  return alpha;
+}
+
+// Streamlined update for bf16 tiles (one operand plane). Same algebra as
+// tile_update with fewer vector instructions per tile:
+//  - without window rows in the wave (general = false) only the routing-mask
+//    key (chunk slot 63) is masked; rows in mode 0 get P = 0 at the end;
+//  - the row maximum is taken on raw scores, then scale and shift are fused
+//    into one FMA before exp2;
+//  - the running reference m moves only when the new maximum exceeds it by
+//    more than 2^8 (values stay below 256 in float32), so the accumulator is
+//    usually not rescaled (alpha == 1, the caller skips the multiply);
+//  - P is packed with v_cvt_pk_bf16_f32 straight into the PV operand.
+// Returns alpha; pf receives the two B-operand fragments of O^T += V^T P^T.
+__device__ __forceinline__ float tile_update_bf16(f32x4 sacc[4], bool general, int mode, int lo, int hi, float zc,
+                                                  float sl2, int g16, float& m, float& l, s16x8 pf[2]) {
+  float mx = -INFINITY;
+  if (general) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * mt + 4 * g16 + i;
+        const bool ok = key >= lo && key <= hi;
+        sacc[mt][i] = ok ? sacc[mt][i] : -INFINITY;
+      }
+  } else {
+    if (g16 == 3) sacc[3][3] = -INFINITY;   // chunk slot 63: the routing mask, never a key
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) mx = fmaxf(mx, fmaxf(fmaxf(sacc[mt][0], sacc[mt][1]), fmaxf(sacc[mt][2], sacc[mt][3])));
+  mx = col_max(mx);
+  const float mb = mx * sl2;                               // scaled row maximum of this tile
+  const float m_old = m;
+  const float m_cand = mode == 1 ? fmaxf(m_old, mb) : (mode == 2 ? fmaxf(m_old, zc) : m_old);
+  const float m_new = m_cand > m_old + 8.f ? m_cand : m_old;
+  const float base = mode == 2 ? mb : (mode == 1 ? m_new : 0.f);
+  float e[16];
+  float rs = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[4 * mt + i] = fast_exp2(fmaf(sacc[mt][i], sl2, -base));
+      rs += e[4 * mt + i];
+    }
+  rs = col_sum(rs);
+  const float alpha = mode == 0 ? 1.f : fast_exp2(m_old - m_new);
+  float scale;
+  if (mode == 2) {
+    const float wz = fast_exp2(zc - m_new);
+    l = l * alpha + wz;
+    scale = wz / rs;
+  } else if (mode == 1) {
+    l = l * alpha + rs;
+    scale = 1.f;
+  } else {
+    scale = 0.f;
+  }
+  m = mode == 0 ? m_old : m_new;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+    u32x4 w;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      // slots j = 2h, 2h+1 of k-step ks: keys of m-tiles 2ks (j < 4) and 2ks+1 (j >= 4)
+      const int mt = 2 * ks + (h >> 1), i0 = 2 * (h & 1);
+      w[h] = pack2_bf16(e[4 * mt + i0] * scale, e[4 * mt + i0 + 1] * scale);
+    }
+    pf[ks] = __builtin_bit_cast(s16x8, w);
+  }
+  return alpha;
+}
+
+// O^T += V^T P^T with P already packed (bf16, swizzled V tile).
+template <int D>
+__device__ __forceinline__ void pv_tile_packed(const bf16_t* buf, const s16x8 pf[2], f32x4 o[D / 16], int lane) {
+  typedef TileLayout<D, true> TL;
+  const int g16 = lane >> 4, L16 = lane & 15;
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r0 = 32 * ks + 4 * g16 + (L16 >> 2);
+      const int col = 16 * dm + 4 * (L16 & 3);
+      const s16x4 lo = ds_read_tr(buf + TL::KE + TL::v_off(r0, col));
+      const s16x4 hi = ds_read_tr(buf + TL::KE + TL::v_off(r0 + 16, col));
+      o[dm] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[dm]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- direct-to-LDS chunk loads (bf16)
+
+// One 16-byte-per-lane global_load_lds_dwordx4: lane i's 16 bytes land at LDS
+// address m0 + 16*i. Issued from inline asm so that the compiler does not
+// order later LDS reads behind it (it cannot tell the ring buffers apart);
+// completion is awaited explicitly with wait_vm + a barrier before any wave
+// reads the buffer. The asm has no output registers.
+__device__ __forceinline__ void dma16(const void* gsrc, const bf16_t* lds_dst) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(la)
+               : "memory", "m0");
+}
+
+// 64 rows x D of K and of V (16 KB each at D = 128) land in the swizzled layout;
+// each wave instruction moves 1 KB (64 lanes x 16 bytes). The 2 * D / 8
+// instructions of a chunk (K first, then V) are dealt round-robin to the
+// waves: wave w issues 2 * D / (8 * WAVES) of them.
+template <int D, int WAVES>
+__device__ __forceinline__ void dma_chunk(const bf16_t* kc, const bf16_t* vc, bf16_t* buf, int w, int lane) {
+  typedef TileLayout<D, true> TL;
+  constexpr int NI = D / 8;              // 1 KB instructions per tile
+  constexpr int RPI = 512 / D;           // rows per instruction
+  constexpr int BPR = D / 8;             // 16-byte blocks per row
+  static_assert((2 * NI) % WAVES == 0, "instructions must divide evenly among waves");
+#pragma unroll
+  for (int jj = w; jj < 2 * NI; jj += WAVES) {
+    const bool is_v = jj >= NI;
+    const int ii = is_v ? jj - NI : jj;
+    const int pr = ii * RPI + lane / BPR, pb = lane % BPR;
+    if (!is_v) dma16(kc + pr * D + ((pb ^ TL::swz_k(pr)) << 3), buf + ii * 512);
+    else dma16(vc + pr * D + ((pb ^ TL::swz_v(pr)) << 3), buf + TL::KE + ii * 512);
+  }
+}
+
+// Compiler-only fence: keeps LDS accesses on their side of a raw barrier or flag.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt lgkmcnt(0): every LDS (and scalar memory) operation of this wave has completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); }
+
+// Bounded wait until an LDS counter reaches target (wave-uniform). Returns false
+// after ~2^22 polls (a fraction of a second), so a logic error cannot hang the GPU.
+constexpr int kSpinLimit = 1 << 22;
+__device__ __forceinline__ bool spin_until_ge(int* ctr, int target) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
+// s_waitcnt that waits for vector-memory operations only: at most n outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Store 4 consecutive output values of a row.
@@ -253,31 +497,54 @@ struct RoutedParams {
   float sl2;  // scale * log2(e)
 };
 
-template <typename T, int D, int WAVES, int TPW>
+// Chunk-staging policy: bf16 inputs go straight from HBM into LDS (swizzled
+// layout, NBUF-deep ring, prefetch distance NBUF-1, one barrier per chunk);
+// float32 inputs are split into three bf16 planes on the way, so they are
+// staged through registers into the padded layout (double buffered when it
+// fits).
+template <typename T, int D> struct RoutedCfg {
+  static constexpr int NP = NPlanes<T>::value;
+  static constexpr bool SWZ = NP == 1;
+  static constexpr int PLE = TileLayout<D, SWZ>::PL;           // elements per plane
+  static constexpr int BUFE = NP * PLE;                         // elements per chunk buffer
+};
+
+template <typename T, int D, int WAVES, int TPW, int NBUF>
 __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedParams p) {
-  constexpr int NP = NPlanes<T>::value;
+  typedef RoutedCfg<T, D> C;
+  constexpr int NP = C::NP;
+  constexpr bool SWZ = C::SWZ;
   constexpr int NT = WAVES * 64;
   constexpr int QB = 2 * WAVES * TPW;
-  constexpr int KVB = kv_buf_elems<D, NP>();
-  constexpr int NBUF = kv_nbuf<D, NP>();
+  constexpr int PD = NBUF - 1;                                  // prefetch distance (DMA path)
+  constexpr int NINST = 2 * (D / 8) / WAVES;                     // DMA instructions per wave per chunk
+  static_assert(!SWZ || PD * NINST < 64, "in-flight loads must fit the vmcnt counter");
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* kvb = reinterpret_cast<bf16_t*>(smem);
-  int* sel = reinterpret_cast<int*>(smem + NBUF * KVB * sizeof(bf16_t));
-  int* list = sel + QB * p.K;
+  int* sel = reinterpret_cast<int*>(smem + (size_t)NBUF * C::BUFE * sizeof(bf16_t));
+  float* zs = reinterpret_cast<float*>(sel + QB * p.K);          // [QB][G][K] chunk logits
+  const int G = p.Hq / p.Hkv;
+  int* list = reinterpret_cast<int*>(zs + QB * G * p.K);
   unsigned char* flags = reinterpret_cast<unsigned char*>(list + p.N);
   __shared__ int s_nlist;
+  __shared__ int ctl_arr[NBUF];    // per ring slot: wave shares landed (monotonic)
+  __shared__ int ctl_done[NBUF];   // per ring slot: waves finished with it (monotonic)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
   const int bg = blockIdx.y, b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const int G = p.Hq / p.Hkv;
   const int tb0 = blockIdx.x * QB;
+  if (tid < NBUF) {
+    ctl_arr[tid] = 0;
+    ctl_done[tid] = 0;
+  }
   const int split = blockIdx.z;
   const long long L = (long long)p.N * kSlots;
   const long long Tcont = (long long)p.N * kContent;
   const T* kg = reinterpret_cast<const T*>(p.k) + (size_t)bg * L * D;
   const T* vg = reinterpret_cast<const T*>(p.v) + (size_t)bg * L * D;
 
-  // ---- the ascending union of chunks needed by this block's queries
+  // ---- the ascending union of chunks needed by this block's queries, their
+  //      selections and chunk logits (no global loads remain in the chunk loop)
   for (int c = tid; c < p.N; c += NT) flags[c] = 0;
   __syncthreads();
   for (int e = tid; e < QB * p.K; e += NT) {
@@ -286,6 +553,11 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
     if (c >= p.N) c = -1;
     sel[e] = c;
     if (c >= 0) flags[c] = 1;
+  }
+  for (int e = tid; e < QB * G * p.K; e += NT) {
+    const int qi = e / (G * p.K), rem = e - qi * G * p.K, hh2 = rem / p.K, kk = rem - hh2 * p.K;
+    const int t = tb0 + qi;
+    zs[e] = (t < p.nq) ? p.zsel[(((size_t)b * p.Hq + g * G + hh2) * p.nq + t) * p.K + kk] : 0.f;
   }
   {
     const int t_last = min(tb0 + QB, p.nq) - 1;
@@ -340,98 +612,148 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
     }
   }
 
+  // ---- chunk loop
+  // bf16 (SWZ): no block barrier. Every wave issues its share of each chunk's
+  // direct-to-LDS loads PD positions ahead, publishes its share once its own
+  // loads have landed (ctl_arr[slot] += 1), waits for all WAVES shares only when
+  // it has work on that chunk, and reports the slot free afterwards
+  // (ctl_done[slot] += 1). A slot is refilled only when every wave is done with
+  // the chunk it held; PD <= NBUF - 1 keeps this free of deadlock. Every wait is
+  // bounded: a wave that times out stops (its outputs are then wrong, but every
+  // wave of the block still terminates).
+  // float32 (register-staged planes): one block barrier per chunk.
   KVStage<T, D, NT> stg;
-  if (beg < end) {
-    const size_t off = (size_t)list[beg] * kSlots * D;
-    stg.load(kg + off, vg + off, tid, 64);
-  }
-  for (int j = beg; j < end; ++j) {
-    bf16_t* buf = kvb + (NBUF == 2 ? (j & 1) : 0) * KVB;
-    if (NBUF == 1 && j > beg) __syncthreads();   // single buffer: wait for every reader
-    stg.store(buf, tid);
-    __syncthreads();
-    if (j + 1 < end) {
-      const size_t off = (size_t)list[j + 1] * kSlots * D;
+  bool failed = false;
+  if constexpr (SWZ) {
+    // Every earlier vector-memory load (query fragments, selections) completes
+    // here, so the only ones in flight inside the loop are this wave's chunk
+    // loads, which the loop waits for itself.
+    wait_vm<0>();
+#pragma unroll
+    for (int jj = 0; jj < PD; ++jj)
+      if (beg + jj < end) {
+        const size_t off = (size_t)list[beg + jj] * kSlots * D;
+        dma_chunk<D, WAVES>(reinterpret_cast<const bf16_t*>(kg + off), reinterpret_cast<const bf16_t*>(vg + off),
+                            kvb + (jj % NBUF) * C::BUFE, w, lane);
+      }
+  } else {
+    if (beg < end) {
+      const size_t off = (size_t)list[beg] * kSlots * D;
       stg.load(kg + off, vg + off, tid, 64);
+    }
+  }
+  for (int j = beg; j < end && !failed; ++j) {
+    const int pos = j - beg;
+    const int slot_buf = pos % NBUF;
+    bf16_t* buf = kvb + slot_buf * C::BUFE;
+    if constexpr (SWZ) {
+      // (1) this wave's share of position pos + PD
+      if (j + PD < end) {
+        const int p2 = pos + PD, s2 = p2 % NBUF, use2 = p2 / NBUF;
+        if (use2 > 0 && !spin_until_ge(&ctl_done[s2], WAVES * use2)) {
+          failed = true;
+          break;
+        }
+        compiler_fence();
+        const size_t off = (size_t)list[j + PD] * kSlots * D;
+        dma_chunk<D, WAVES>(reinterpret_cast<const bf16_t*>(kg + off), reinterpret_cast<const bf16_t*>(vg + off),
+                            kvb + s2 * C::BUFE, w, lane);
+      }
+      // (2) publish this wave's share of position pos once it has landed
+      const int ahead = min(PD, end - 1 - j);   // positions issued after pos
+      if (ahead >= 2) wait_vm<(PD >= 2 ? 2 * NINST : 0)>();
+      else if (ahead == 1) wait_vm<NINST>();
+      else wait_vm<0>();
+      compiler_fence();
+      if (lane == 0) __hip_atomic_fetch_add(&ctl_arr[slot_buf], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      if (NBUF == 1 && j > beg) __syncthreads();   // single buffer: wait for every reader
+      stg.store(buf, tid);
+      __syncthreads();
+      if (j + 1 < end) {
+        const size_t off = (size_t)list[j + 1] * kSlots * D;
+        stg.load(kg + off, vg + off, tid, 64);
+      }
     }
     const int c = list[j];
     const long long cf = (long long)c * kContent, cl = cf + kContent - 1;
+    int mode[TPW], slot[TPW];
+    bool any = false;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
       const bool qv = tq[tt] < p.nq;
       const bool win = qv && cf <= iq[tt] + p.R && cl >= iq[tt] - p.R;
-      int slot = -1;
+      slot[tt] = -1;
       if (qv && ptr[tt] < p.K) {
         if (sel[(tq[tt] - tb0) * p.K + ptr[tt]] == c) {
-          slot = ptr[tt];
+          slot[tt] = ptr[tt];
           ++ptr[tt];
         }
       }
-      int mode = win ? 1 : (slot >= 0 ? 2 : 0);
-      if (!rv[tt]) mode = 0;
-      if (__ballot(mode != 0) == 0ull) continue;
-
-      f32x4 sacc[4];
-      s_tile<D, NP>(buf, qf[tt], sacc, lane);
-
-      float x[4][4];
-      float mloc = -INFINITY;
+      mode[tt] = win ? 1 : (slot[tt] >= 0 ? 2 : 0);
+      if (!rv[tt]) mode[tt] = 0;
+      any = any || (__ballot(mode[tt] != 0) != 0ull);
+    }
+    if (any) {
+      if constexpr (SWZ) {
+        if (!spin_until_ge(&ctl_arr[slot_buf], WAVES * (pos / NBUF + 1))) {
+          failed = true;
+          break;
+        }
+        compiler_fence();
+      }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * mt + 4 * g16 + i;
-          bool ok = mode != 0 && key < kContent;
-          if (mode == 1) {
-            const long long u = cf + key;
-            ok = ok && u >= iq[tt] - p.R && u <= iq[tt] + p.R;
+      for (int tt = 0; tt < TPW; ++tt) {
+        if (__ballot(mode[tt] != 0) == 0ull) continue;
+        f32x4 sacc[4];
+        s_tile<D, NP, SWZ>(buf, qf[tt], sacc, lane);
+        if constexpr (NP == 1) {
+          const bool general = __ballot(mode[tt] == 1) != 0ull;
+          int lo = 0, hi = kContent - 1;
+          if (mode[tt] == 1) {
+            lo = (int)max(0LL, iq[tt] - p.R - cf);
+            hi = (int)min((long long)kContent - 1, iq[tt] + p.R - cf);
           }
-          const float xv = ok ? sacc[mt][i] * p.sl2 : -INFINITY;
-          x[mt][i] = xv;
-          mloc = fmaxf(mloc, xv);
-        }
-      const float mb = col_max(mloc);
-      float zc = 0.f;
-      if (mode == 2) zc = p.zsel[(((size_t)b * p.Hq + h) * p.nq + tq[tt]) * p.K + slot] * kLog2e;
-      const float m_old = mrow[tt];
-      float pbase;
-      if (mode == 1) pbase = fmaxf(m_old, mb);
-      else if (mode == 2) pbase = mb;
-      else pbase = 0.f;
-      float psum = 0.f;
+          const float zc = mode[tt] == 2 ? zs[((tq[tt] - tb0) * G + hh) * p.K + slot[tt]] * kLog2e : 0.f;
+          s16x8 pf[2];
+          const float alpha = tile_update_bf16(sacc, general, mode[tt], lo, hi, zc, p.sl2, g16, mrow[tt], lrow[tt], pf);
+          if (__ballot(alpha != 1.f) != 0ull) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+            for (int dm = 0; dm < D / 16; ++dm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(x[mt][i] - pbase);
-          x[mt][i] = e;
-          psum += e;
+              for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+          }
+          pv_tile_packed<D>(buf, pf, acc[tt], lane);
+          continue;
         }
-      const float rs = col_sum(psum);
-      float alpha = 1.f;
-      if (mode == 1) {
-        alpha = fast_exp2(m_old - pbase);
-        lrow[tt] = lrow[tt] * alpha + rs;
-        mrow[tt] = pbase;
-      } else if (mode == 2) {
-        const float m_new = fmaxf(m_old, zc);
-        alpha = fast_exp2(m_old - m_new);
-        const float wz = fast_exp2(zc - m_new);
-        const float ws = wz / rs;
+        float x[4][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[mt][i] *= ws;
-        lrow[tt] = lrow[tt] * alpha + wz;
-        mrow[tt] = m_new;
+          for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
+        int lo = 0, hi = kContent - 1;
+        if (mode[tt] == 1) {
+          lo = (int)max(0LL, iq[tt] - p.R - cf);
+          hi = (int)min((long long)kContent - 1, iq[tt] + p.R - cf);
+        }
+        float zc = 0.f;
+        if (mode[tt] == 2) zc = zs[((tq[tt] - tb0) * G + hh) * p.K + slot[tt]] * kLog2e;
+        const float alpha = tile_update(x, mode[tt], lo, hi, zc, p.sl2, g16, mrow[tt], lrow[tt]);
+#pragma unroll
+        for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+        pv_tile<D, NP, SWZ>(buf, x, acc[tt], lane);
       }
-#pragma unroll
-      for (int dm = 0; dm < D / 16; ++dm)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
-      pv_tile<D, NP>(buf, x, acc[tt], lane);
+    }
+    if constexpr (SWZ) {
+      // every LDS read of this slot by this wave has returned (their values fed the MFMAs)
+      wait_lgkm0();
+      compiler_fence();
+      if (lane == 0) __hip_atomic_fetch_add(&ctl_done[slot_buf], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
+  if constexpr (SWZ) wait_vm<0>();   // no load of this wave outlives the block
 
   // ---- results
 #pragma unroll
@@ -572,39 +894,21 @@ __global__ __launch_bounds__(512) void swa_kernel(SwaParams p) {
       const long long ts = t0 + 16 * tt;
       if (kb > ts + 15 + p.R || kb + 63 < ts - p.R || ts >= L) continue;
       f32x4 sacc[4];
-      s_tile<D, NP>(buf, qf[tt], sacc, lane);
+      s_tile<D, NP, false>(buf, qf[tt], sacc, lane);
       float x[4][4];
-      float mloc = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long long u = kb + 16 * mt + 4 * g16 + i;
-          const bool ok = trow[tt] < L && u < L && u >= trow[tt] - p.R && u <= trow[tt] + p.R;
-          const float xv = ok ? sacc[mt][i] * p.sl2 : -INFINITY;
-          x[mt][i] = xv;
-          mloc = fmaxf(mloc, xv);
-        }
-      const float mb = col_max(mloc);
-      const float m_new = fmaxf(mrow[tt], mb);
-      float psum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(x[mt][i] - m_new);
-          x[mt][i] = e;
-          psum += e;
-        }
-      const float rs = col_sum(psum);
-      const float alpha = fast_exp2(mrow[tt] - m_new);
-      lrow[tt] = lrow[tt] * alpha + rs;
-      mrow[tt] = m_new;
+        for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
+      const int mode = trow[tt] < L ? 1 : 0;
+      const int lo = (int)max(0LL, trow[tt] - p.R - kb);
+      const int hi = (int)min(63LL, min(L - 1, trow[tt] + p.R) - kb);
+      const float alpha = tile_update(x, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt]);
 #pragma unroll
       for (int dm = 0; dm < D / 16; ++dm)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
-      pv_tile<D, NP>(buf, x, acc[tt], lane);
+      pv_tile<D, NP, false>(buf, x, acc[tt], lane);
     }
   }
 
@@ -637,16 +941,44 @@ static size_t kv_lds_bytes(int d, int dtype) {
   return nbuf * one;
 }
 
-size_t routed_lds_limit() { return 160 * 1024; }
+size_t routed_lds_limit() { return 160 * 1024 - 256; }  // room for the static LDS variables
+
+static int routed_nbuf(int d, int dtype, int waves) {
+  if (dtype == 1) return waves == 1 ? 2 : 3;        // direct-to-LDS ring, prefetch distance NBUF - 1
+  return (d == 128) ? 1 : 2;                        // three float32-derived planes
+}
+
+static size_t routed_buf_bytes(int d, int dtype) {
+  if (dtype == 1) return (size_t)2 * 64 * d * 2;    // swizzled K + V, one plane
+  return (size_t)3 * 64 * ((d + 8) + (d + 16)) * 2;  // padded K + V, three planes
+}
+
+static size_t routed_lds(const RouteDims& dm, int K, int qblock, int waves) {
+  const int G = dm.Hq / dm.Hkv;
+  size_t b = (size_t)routed_nbuf(dm.d, dm.dtype, waves) * routed_buf_bytes(dm.d, dm.dtype) + (size_t)qblock * K * 4 +
+             (size_t)qblock * G * K * 4 + (size_t)dm.N * 4 + (size_t)dm.N;
+  return (b + 15) & ~(size_t)15;
+}
 
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int nq) {
   AttnPlan pl;
-  const size_t kvb = kv_lds_bytes(dm.d, dm.dtype);
-  // Prefill-sized problems: 8 waves x 2 tiles = 32 queries per block, no split.
+  // Prefill-sized problems: 8 waves x 2 tiles = 32 queries per block, no split;
+  // 8 waves x 1 tile when the selections of 32 queries do not fit in LDS.
   pl.waves = 8;
   pl.tiles = 2;
+  if (const char* e = getenv("LCR_ROUTED_WAVES16")) {
+    if (e[0] == '1') {
+      pl.waves = 16;
+      pl.tiles = 1;
+    }
+  }
   pl.qblock = 2 * pl.waves * pl.tiles;
   pl.nsplit = 1;
+  if (routed_lds(dm, K, pl.qblock, pl.waves) > routed_lds_limit()) {
+    pl.waves = 8;
+    pl.tiles = 1;
+    pl.qblock = 2 * pl.waves * pl.tiles;
+  }
   const long long blocks_prefill = (long long)((nq + pl.qblock - 1) / pl.qblock) * dm.B * dm.Hkv;
   if (blocks_prefill < 256) {
     // Decode-sized: one wave per 2-query tile and the chunk list split across blocks.
@@ -657,16 +989,15 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int nq) {
     long long ns = (1024 + blocks - 1) / (blocks > 0 ? blocks : 1);
     pl.nsplit = (int)(ns < 1 ? 1 : (ns > 8 ? 8 : ns));
   }
-  pl.lds = kvb + (size_t)pl.qblock * K * 4 + (size_t)dm.N * 4 + (size_t)dm.N;
-  pl.lds = (pl.lds + 15) & ~(size_t)15;
+  pl.lds = routed_lds(dm, K, pl.qblock, pl.waves);
   pl.ws = pl.nsplit > 1 ? align256a((size_t)pl.nsplit * dm.B * dm.Hq * nq * (dm.d + 4) * 4) : 0;
   return pl;
 }
 
-template <typename T, int D, int WAVES, int TPW>
+template <typename T, int D, int WAVES, int TPW, int NBUF>
 static hipError_t launch_routed_t(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
   constexpr int QB = 2 * WAVES * TPW;
-  auto kern = routed_attention_kernel<T, D, WAVES, TPW>;
+  auto kern = routed_attention_kernel<T, D, WAVES, TPW, NBUF>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
   if (e != hipSuccess) return e;
   dim3 grid((prm.nq + QB - 1) / QB, dm.B * dm.Hkv, pl.nsplit);
@@ -681,8 +1012,12 @@ static hipError_t launch_routed_t(const RouteDims& dm, const AttnPlan& pl, const
 
 template <typename T, int D>
 static hipError_t launch_routed_d(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
-  if (pl.waves == 8) return launch_routed_t<T, D, 8, 2>(dm, pl, prm, st);
-  return launch_routed_t<T, D, 1, 1>(dm, pl, prm, st);
+  constexpr int NB = sizeof(T) == 2 ? 3 : (D == 128 ? 1 : 2);
+  constexpr int NB1 = sizeof(T) == 2 ? 2 : NB;
+  if (pl.waves == 8 && pl.tiles == 2) return launch_routed_t<T, D, 8, 2, NB>(dm, pl, prm, st);
+  if (pl.waves == 16) return launch_routed_t<T, D, 16, 1, NB>(dm, pl, prm, st);
+  if (pl.waves == 8) return launch_routed_t<T, D, 8, 1, NB>(dm, pl, prm, st);
+  return launch_routed_t<T, D, 1, 1, NB1>(dm, pl, prm, st);
 }
 
 hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, const void* q, const void* k,

@@ -82,6 +82,13 @@ __device__ __forceinline__ void pack8_split(const float* v, s16x8& hi, s16x8& lo
   }
 }
 
+// Two floats -> packed bf16x2 (v_cvt_pk_bf16_f32, round to nearest even).
+typedef __bf16 hbf16x2 __attribute__((ext_vector_type(2)));
+typedef float hf32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(hf32x2{a, b}, hbf16x2));
+}
+
 // 16-byte load of 8 bf16 values (any address space the compiler can see).
 __device__ __forceinline__ s16x8 load8(const bf16_t* p) { return *reinterpret_cast<const s16x8*>(p); }
 
@@ -125,14 +132,28 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 // Reduction over the four lanes {l%16 + 16*g}: they share one MFMA output column.
-__device__ __forceinline__ float col_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// v_permlane16_swap / v_permlane32_swap exchange 16-lane rows (resp. 32-lane
+// halves) between two registers; with both operands equal, element 0 and 1 of
+// the result hold, in every lane, the value of the lane itself and of its
+// partner l^16 (resp. l^32), in some order. Plain VALU, no LDS round trip.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float col_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float col_max(float v) { return xor32_max(xor16_max(v)); }
+__device__ __forceinline__ float col_sum(float v) { return xor32_sum(xor16_sum(v)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

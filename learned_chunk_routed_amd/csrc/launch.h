@@ -21,9 +21,10 @@ struct ScoreWs {
   float* qt;    // [B,Hq,nq,d]  routing queries q~ (float32)
   float* zhat;  // [B,Hkv,nq,N] group maximum of the scores
   float* z;     // [B,Hq,nq,N]  per-head scores
+  float* upart; // [splits,B,nq,rank padded to 32/64/128]  partial x A
 };
-size_t score_ws_bytes(const RouteDims& dm, int nq);
-ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int nq);
+size_t score_ws_bytes(const RouteDims& dm, int D, int r, int nq);
+ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int D, int r, int nq);
 hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const void* x, const void* A,
                                    const void* Bm, int D, int r, const float* s, const float* H,
                                    float beta, float scale, int K, int radius, int q0, int nq,

@@ -7,9 +7,9 @@
 // Budget": rank-64 residual; similarity and pooling entropy rank the chunks.
 //
 // Three kernels:
-//  1. qtilde_kernel: u = x A (MFMA, bf16 products exact in float32), then
-//     q~ = q + u B per head with u split into bf16 hi + lo (B is exact in bf16),
-//     written as float32 rows.
+//  1. u_kernel + q_kernel: u = x A (MFMA, bf16 products exact in float32),
+//     then q~ = q + u B per head with u split into bf16 hi + lo (B is exact in
+//     bf16), written as float32 rows.
 //  2. score_kernel: z = scale * q~ . s - beta * H per head on MFMA with both
 //     operands split into bf16 planes (hi + lo for bf16 inputs: hi.hi + hi.lo +
 //     lo.hi; hi + mid + lo for float32 inputs), float32 accumulation:
@@ -48,123 +48,181 @@ __device__ __forceinline__ void load_row8<bf16_t>(const bf16_t* row, long long k
 }
 
 // ---------------------------------------------------------------------------- 1. q~
+//
+// 1a. u_kernel: partial u = x[rows] A over a range of the hidden dimension.
+//     Block = 4 waves x 16 rows. A is staged through LDS in 64-row slices
+//     (bf16 planes; row stride RP+16 keeps the transpose reads conflict free)
+//     with the next slice prefetched into registers; x fragments come straight
+//     from HBM (16 bytes per lane). Small query counts split the hidden
+//     dimension over several blocks (grid.z); q_kernel sums the partials.
+// 1b. q_kernel: q~ = q + u B_h for one head per block. B's slice for the head
+//     is staged into LDS; u is split into bf16 hi + lo (B is exact for bf16
+//     inputs; float32 inputs also split B).
 
-template <typename T, int D, int RP>
-__global__ __launch_bounds__(64) void qtilde_kernel(const T* __restrict__ q, const T* __restrict__ x,
-                                                    const T* __restrict__ A, const T* __restrict__ Bm,
-                                                    int Dh, int r, float* __restrict__ qt, int Hq,
-                                                    int N, int q0, int nq) {
-  constexpr bool kSplit = sizeof(T) == 4;       // float32 inputs: split both operands
-  constexpr int AS = RP + 16;                    // LDS row strides (bank-conflict-free tr reads)
-  constexpr int BS = D + 16;
-  __shared__ __align__(16) bf16_t a_hi[32 * AS];
-  __shared__ __align__(16) bf16_t a_lo[kSplit ? 32 * AS : 1];
-  __shared__ __align__(16) bf16_t b_hi[RP * BS];
-  __shared__ __align__(16) bf16_t b_lo[kSplit ? RP * BS : 1];
-  __shared__ float u_s[16][RP + 1];
+constexpr int kUKc = 64;   // rows of A per LDS slice
 
-  const int lane = threadIdx.x, g16 = lane >> 4, L16 = lane & 15;
-  const int t0 = blockIdx.x * 16, b = blockIdx.y;
+template <typename T, int RP>
+__global__ __launch_bounds__(256) void u_kernel(const T* __restrict__ x, const T* __restrict__ A, int Dh, int r,
+                                                float* __restrict__ upart, int N, int q0, int nq, int kslices_per_split) {
+  constexpr bool kSplit = sizeof(T) == 4;
+  constexpr int NPL = kSplit ? 2 : 1;
+  constexpr int AS = RP + 16;
+  constexpr int kElems = kUKc * RP;                 // elements per slice
+  constexpr int kPer = (kElems + 255) / 256;        // elements per thread per slice
+  __shared__ __align__(16) bf16_t a_s[NPL][kUKc * AS];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const int b = blockIdx.y, split = blockIdx.z;
+  const int t0 = blockIdx.x * 64 + 16 * w;
   const long long L = (long long)N * kSlots;
+  const int nslices = (Dh + kUKc - 1) / kUKc;
+  const int sl_beg = split * kslices_per_split;
+  const int sl_end = min(nslices, sl_beg + kslices_per_split);
 
-  // ---- u = x A, rows t0..t0+15
-  f32x4 acc_u[RP / 16];
-#pragma unroll
-  for (int nt = 0; nt < RP / 16; ++nt) acc_u[nt] = zero4();
   const int my_t = t0 + L16;
   const T* xrow = (my_t < nq) ? x + ((size_t)b * L + slot_of((long long)q0 + my_t)) * Dh : nullptr;
-  for (int k0 = 0; k0 < Dh; k0 += 32) {
-    for (int e = lane; e < 32 * RP; e += 64) {
+
+  f32x4 acc[RP / 16];
+#pragma unroll
+  for (int nt = 0; nt < RP / 16; ++nt) acc[nt] = zero4();
+
+  float pre[kPer];
+  auto fetch = [&](int sl) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = tid + 256 * j;
       const int kk = e / RP, n = e - kk * RP;
-      const float val = (k0 + kk < Dh && n < r) ? Elem<T>::to_f(A[(size_t)(k0 + kk) * r + n]) : 0.f;
-      if (kSplit) {
-        bf16_t h, l;
-        split_bf16(val, h, l);
-        a_hi[kk * AS + n] = h;
-        a_lo[kk * AS + n] = l;
-      } else {
-        a_hi[kk * AS + n] = f2bf(val);
+      const int k = sl * kUKc + kk;
+      pre[j] = (e < kElems && k < Dh && n < r) ? Elem<T>::to_f(A[(size_t)k * r + n]) : 0.f;
+    }
+  };
+  if (sl_beg < sl_end) fetch(sl_beg);
+  for (int sl = sl_beg; sl < sl_end; ++sl) {
+    __syncthreads();   // previous slice fully consumed
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = tid + 256 * j;
+      if (e < kElems) {
+        const int kk = e / RP, n = e - kk * RP;
+        if (kSplit) {
+          bf16_t h, l;
+          split_bf16(pre[j], h, l);
+          a_s[0][kk * AS + n] = h;
+          a_s[NPL - 1][kk * AS + n] = l;
+        } else {
+          a_s[0][kk * AS + n] = f2bf(pre[j]);
+        }
       }
     }
     __syncthreads();
-    float xv[8];
-    if (xrow) load_row8<T>(xrow, k0 + 8 * g16, Dh, xv);
-    else {
+    if (sl + 1 < sl_end) fetch(sl + 1);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) xv[j] = 0.f;
-    }
-    s16x8 xh, xl;
-    if (kSplit) pack8_split(xv, xh, xl);
-    else xh = pack8(xv);
+    for (int ks = 0; ks < kUKc / 32; ++ks) {
+      const int k0 = sl * kUKc + 32 * ks;
+      float xv[8];
+      if (xrow) load_row8<T>(xrow, k0 + 8 * g16, Dh, xv);
+      else {
 #pragma unroll
-    for (int nt = 0; nt < RP / 16; ++nt) {
-      const s16x8 bh = lds_col_frag(a_hi, AS, 8 * g16, 8 * g16 + 4, 16 * nt, lane);
-      acc_u[nt] = mfma16(xh, bh, acc_u[nt]);
-      if (kSplit) {
-        const s16x8 bl = lds_col_frag(a_lo, AS, 8 * g16, 8 * g16 + 4, 16 * nt, lane);
-        acc_u[nt] = mfma16(xh, bl, acc_u[nt]);
-        acc_u[nt] = mfma16(xl, bh, acc_u[nt]);
+        for (int j = 0; j < 8; ++j) xv[j] = 0.f;
+      }
+      s16x8 xh, xl;
+      if (kSplit) pack8_split(xv, xh, xl);
+      else xh = pack8(xv);
+#pragma unroll
+      for (int nt = 0; nt < RP / 16; ++nt) {
+        const s16x8 bh = lds_col_frag(a_s[0], AS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+        if (kSplit) {
+          const s16x8 bl = lds_col_frag(a_s[NPL - 1], AS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+          acc[nt] = mfma16(xh, bl, acc[nt]);
+          acc[nt] = mfma16(xl, bh, acc[nt]);
+        }
+        acc[nt] = mfma16(xh, bh, acc[nt]);
       }
     }
-    __syncthreads();
   }
-  // D layout: lane holds u[row 4*g16 + i][col 16*nt + L16]
+  // D layout: lane holds u[row 4*g16 + i][col 16*nt + L16] of this wave's 16 rows
+  float* up = upart + ((size_t)split * gridDim.y + b) * (size_t)nq * RP;
 #pragma unroll
   for (int nt = 0; nt < RP / 16; ++nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u_s[4 * g16 + i][16 * nt + L16] = acc_u[nt][i];
-  __syncthreads();
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g16 + i;
+      if (t < nq) up[(size_t)t * RP + 16 * nt + L16] = acc[nt][i];
+    }
+}
 
-  // ---- u fragments (A operand, k = rank index), split into hi + lo
+template <typename T, int D, int RP>
+__global__ __launch_bounds__(256) void q_kernel(const T* __restrict__ q, const T* __restrict__ Bm, int r,
+                                                const float* __restrict__ upart, int nsplit,
+                                                float* __restrict__ qt, int Hq, int N, int q0, int nq) {
+  constexpr bool kSplit = sizeof(T) == 4;
+  constexpr int NPL = kSplit ? 2 : 1;
+  constexpr int BS = D + 16;
+  __shared__ __align__(16) bf16_t b_s[NPL][RP * BS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int t0 = blockIdx.x * 64 + 16 * w;
+  const long long L = (long long)N * kSlots;
+  const int B = gridDim.z;
+
+  for (int e = tid; e < RP * D; e += 256) {
+    const int kk = e / D, n = e - kk * D;
+    const float val = (kk < r) ? Elem<T>::to_f(Bm[(size_t)kk * Hq * D + (size_t)h * D + n]) : 0.f;
+    if (kSplit) {
+      bf16_t hh, ll;
+      split_bf16(val, hh, ll);
+      b_s[0][kk * BS + n] = hh;
+      b_s[NPL - 1][kk * BS + n] = ll;
+    } else {
+      b_s[0][kk * BS + n] = f2bf(val);
+    }
+  }
+  // u fragments (A operand: row L16 of this wave, k = rank index), partials summed
   s16x8 uh[RP / 32], ul[RP / 32];
+  const int my_t = t0 + L16;
 #pragma unroll
   for (int ks = 0; ks < RP / 32; ++ks) {
     float uv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) uv[j] = u_s[L16][32 * ks + 8 * g16 + j];
+    for (int j = 0; j < 8; ++j) uv[j] = 0.f;
+    if (my_t < nq) {
+      for (int sp = 0; sp < nsplit; ++sp) {
+        const float* up = upart + (((size_t)sp * B + b) * nq + my_t) * RP + 32 * ks + 8 * g16;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uv[j] += a0[j];
+          uv[4 + j] += a1[j];
+        }
+      }
+    }
     pack8_split(uv, uh[ks], ul[ks]);
   }
-
-  // ---- q~ = q + u B_h for every head
-  for (int h = 0; h < Hq; ++h) {
-    for (int e = lane; e < RP * D; e += 64) {
-      const int kk = e / D, n = e - kk * D;
-      const float val = (kk < r) ? Elem<T>::to_f(Bm[(size_t)kk * Hq * D + (size_t)h * D + n]) : 0.f;
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < RP / 32; ++ks) {
+      const s16x8 bh = lds_col_frag(b_s[0], BS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+      acc = mfma16(ul[ks], bh, acc);
       if (kSplit) {
-        bf16_t hh, ll;
-        split_bf16(val, hh, ll);
-        b_hi[kk * BS + n] = hh;
-        b_lo[kk * BS + n] = ll;
-      } else {
-        b_hi[kk * BS + n] = f2bf(val);
+        const s16x8 bl = lds_col_frag(b_s[NPL - 1], BS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+        acc = mfma16(uh[ks], bl, acc);
+      }
+      acc = mfma16(uh[ks], bh, acc);
+    }
+    const int dd = 16 * nt + L16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g16 + i;
+      if (t < nq) {
+        const long long sl = slot_of((long long)q0 + t);
+        const float qv = Elem<T>::to_f(q[((size_t)b * Hq + h) * L * D + (size_t)sl * D + dd]);
+        qt[(((size_t)b * Hq + h) * nq + t) * D + dd] = qv + acc[i];
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < RP / 32; ++ks) {
-        const s16x8 bh = lds_col_frag(b_hi, BS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
-        acc = mfma16(ul[ks], bh, acc);
-        if (kSplit) {
-          const s16x8 bl = lds_col_frag(b_lo, BS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
-          acc = mfma16(uh[ks], bl, acc);
-        }
-        acc = mfma16(uh[ks], bh, acc);
-      }
-      const int dd = 16 * nt + L16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * g16 + i;
-        if (t < nq) {
-          const long long sl = slot_of((long long)q0 + t);
-          const float qv = Elem<T>::to_f(q[((size_t)b * Hq + h) * L * D + (size_t)sl * D + dd]);
-          qt[(((size_t)b * Hq + h) * nq + t) * D + dd] = qv + acc[i];
-        }
-      }
-    }
-    __syncthreads();
   }
 }
 
@@ -327,12 +385,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zha
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t score_ws_bytes(const RouteDims& dm, int nq) {
-  const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
-  return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4);
+static int rank_pad(int r) { return r <= 32 ? 32 : (r <= 64 ? 64 : 128); }
+
+// Hidden-dimension split of u_kernel: enough blocks to spread small query counts.
+static int u_splits(const RouteDims& dm, int Dh, int nq) {
+  const int tiles = (nq + 63) / 64 * dm.B;
+  const int nslices = (Dh + kUKc - 1) / kUKc;
+  int s = (512 + tiles - 1) / tiles;
+  if (s > nslices) s = nslices;
+  if (s < 1) s = 1;
+  const int per = (nslices + s - 1) / s;
+  return (nslices + per - 1) / per;
 }
 
-ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int nq) {
+size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
+  const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
+  const size_t upart = (size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4;
+  return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4) + align256(upart);
+}
+
+ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
   char* p = (char*)ws;
   ScoreWs out;
@@ -341,23 +413,31 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int nq) {
   out.zhat = (float*)p;
   p += align256(rows_g * dm.N * 4);
   out.z = (float*)p;
+  p += align256(rows_h * dm.N * 4);
+  out.upart = (float*)p;
+  (void)Dh;
+  (void)r;
   return out;
 }
 
 template <typename T, int D, int RP>
 static void launch_qtilde(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
-                          int Dh, int r, float* qt, int q0, int nq, hipStream_t st) {
-  dim3 grid((nq + 15) / 16, dm.B);
-  hipLaunchKernelGGL((qtilde_kernel<T, D, RP>), grid, dim3(64), 0, st, (const T*)q, (const T*)x,
-                     (const T*)A, (const T*)Bm, Dh, r, qt, dm.Hq, dm.N, q0, nq);
+                          int Dh, int r, const ScoreWs& ws, int q0, int nq, hipStream_t st) {
+  const int nsplit = u_splits(dm, Dh, nq);
+  const int nslices = (Dh + kUKc - 1) / kUKc;
+  const int per = (nslices + nsplit - 1) / nsplit;
+  hipLaunchKernelGGL((u_kernel<T, RP>), dim3((nq + 63) / 64, dm.B, nsplit), dim3(256), 0, st, (const T*)x,
+                     (const T*)A, Dh, r, ws.upart, dm.N, q0, nq, per);
+  hipLaunchKernelGGL((q_kernel<T, D, RP>), dim3((nq + 63) / 64, dm.Hq, dm.B), dim3(256), 0, st, (const T*)q,
+                     (const T*)Bm, r, ws.upart, nsplit, ws.qt, dm.Hq, dm.N, q0, nq);
 }
 
 template <typename T, int D>
 static void launch_qtilde_r(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
-                            int Dh, int r, float* qt, int q0, int nq, hipStream_t st) {
-  if (r <= 32) launch_qtilde<T, D, 32>(dm, q, x, A, Bm, Dh, r, qt, q0, nq, st);
-  else if (r <= 64) launch_qtilde<T, D, 64>(dm, q, x, A, Bm, Dh, r, qt, q0, nq, st);
-  else launch_qtilde<T, D, 128>(dm, q, x, A, Bm, Dh, r, qt, q0, nq, st);
+                            int Dh, int r, const ScoreWs& ws, int q0, int nq, hipStream_t st) {
+  if (r <= 32) launch_qtilde<T, D, 32>(dm, q, x, A, Bm, Dh, r, ws, q0, nq, st);
+  else if (r <= 64) launch_qtilde<T, D, 64>(dm, q, x, A, Bm, Dh, r, ws, q0, nq, st);
+  else launch_qtilde<T, D, 128>(dm, q, x, A, Bm, Dh, r, ws, q0, nq, st);
 }
 
 template <int P>
@@ -373,11 +453,11 @@ hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const voi
                                    float beta, float scale, int K, int radius, int q0, int nq,
                                    int32_t* idx, float* zsel, const ScoreWs& ws, hipStream_t st) {
   if (dm.dtype == 1) {
-    if (dm.d == 64) launch_qtilde_r<bf16_t, 64>(dm, q, x, A, Bm, D, r, ws.qt, q0, nq, st);
-    else launch_qtilde_r<bf16_t, 128>(dm, q, x, A, Bm, D, r, ws.qt, q0, nq, st);
+    if (dm.d == 64) launch_qtilde_r<bf16_t, 64>(dm, q, x, A, Bm, D, r, ws, q0, nq, st);
+    else launch_qtilde_r<bf16_t, 128>(dm, q, x, A, Bm, D, r, ws, q0, nq, st);
   } else {
-    if (dm.d == 64) launch_qtilde_r<float, 64>(dm, q, x, A, Bm, D, r, ws.qt, q0, nq, st);
-    else launch_qtilde_r<float, 128>(dm, q, x, A, Bm, D, r, ws.qt, q0, nq, st);
+    if (dm.d == 64) launch_qtilde_r<float, 64>(dm, q, x, A, Bm, D, r, ws, q0, nq, st);
+    else launch_qtilde_r<float, 128>(dm, q, x, A, Bm, D, r, ws, q0, nq, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
