@@ -56,7 +56,7 @@ def src_hash(path):
 def stored_traffic(kernel_tag, workload):
     """HBM bytes per launch from the committed counter summary, if it was taken on
     the current kernel source (the summary records the source hash)."""
-    path = os.path.join(PROFILE_DIR, f"{kernel_tag}_{workload}_counters.md")
+    path = os.path.join(PROFILE_DIR, f"{kernel_tag}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
