@@ -233,7 +233,8 @@ def bench_decode(args, torch, lcr):
     dims = lcr.make_dims(B, Hq, Hkv, N, dd, torch.bfloat16)
     ws_s = torch.empty(max(1, lcr.workspace_bytes(1, dims, cfg.D, cfg.r, cfg.K, cfg.nq)), dtype=torch.uint8,
                        device=dev)
-    ws_a = torch.empty(max(1, lcr.workspace_bytes(2, dims, 0, 0, cfg.K, cfg.nq)), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, lcr.workspace_bytes(2, dims, 0, 0, cfg.K, cfg.nq, cfg.R)), dtype=torch.uint8,
+                       device=dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def run(j, timed):

@@ -76,10 +76,12 @@ const char* lcr_status_string(int status);
 
 /*
  * Bytes of device workspace `op` needs for these sizes (0 if none). D and r are
- * used by LCR_OP_ROUTE_SCORE_TOPK only; K and nq by the two routing calls.
- * Returns 0 for invalid sizes as well; the call itself reports those.
+ * used by LCR_OP_ROUTE_SCORE_TOPK only; K and nq by the two routing calls;
+ * radius by LCR_OP_ROUTED_ATTENTION (decode-sized problems keep one partial
+ * result per selected or window chunk). Returns 0 for invalid sizes as well;
+ * the call itself reports those.
  */
-size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, int nq);
+size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, int radius, int nq);
 
 /*
  * Summary keys and pooling entropies ("Prefilling-dLLM v2", Figure 3 caption:

@@ -39,14 +39,14 @@ const char* lcr_status_string(int status) {
   }
 }
 
-size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, int nq) {
-  if (check_dims(dims) != LCR_OK || K < 0 || nq < 0) return 0;
+size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, int radius, int nq) {
+  if (check_dims(dims) != LCR_OK || K < 0 || nq < 0 || radius < 0) return 0;
   const RouteDims dm = to_route_dims(dims);
   switch (op) {
     case LCR_OP_ROUTE_SCORE_TOPK:
       return (K > 0 && nq > 0 && D > 0 && r > 0 && r <= 128) ? score_ws_bytes(dm, D, r, nq) : 0;
     case LCR_OP_ROUTED_ATTENTION:
-      return nq > 0 ? plan_routed_attention(dm, K, nq).ws : 0;
+      return nq > 0 ? plan_routed_attention(dm, K, radius, nq).ws : 0;
     default:
       return 0;
   }
@@ -80,7 +80,7 @@ int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, con
   if (st != LCR_OK) return st;
   if (nq == 0) return LCR_OK;
   const RouteDims dm = to_route_dims(dims);
-  const AttnPlan plan = plan_routed_attention(dm, K, nq);
+  const AttnPlan plan = plan_routed_attention(dm, K, radius, nq);
   if (plan.lds > routed_lds_limit()) return LCR_ERR_UNSUPPORTED;
   if (plan.ws > 0 && (ws == nullptr || ws_bytes < plan.ws)) return LCR_ERR_WORKSPACE;
   return hip_status(launch_routed_attention(dm, plan, q, k, v, K > 0 ? idx : nullptr, K > 0 ? zsel : nullptr, K,

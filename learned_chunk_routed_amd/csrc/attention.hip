@@ -789,24 +789,75 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
   }
 }
 
-// Merge the split partials of every query row (one wave per row).
+// Merge the split partials of every query row (one wave per row). Partial s of
+// a row holds (O, m, l) at part[(s * rows + row) * (D + 4)]; a partial with
+// l = 0 saw no key of the row and its O is not read (it may not be written).
+constexpr int kCombineRegs = 4;                       // up to 64 * 4 partials per row
+constexpr int kMaxPartials = 64 * kCombineRegs;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int nsplit, size_t rows,
                                                       void* o, float* lse, int nq, int N, int q0) {
+  constexpr int DE = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const size_t row = (size_t)blockIdx.x * 4 + w;
   if (row >= rows) return;
+  const size_t rs = rows * (D + 4);                   // stride between partials
+  const float* pr = part + row * (D + 4);
+  float mv[kCombineRegs], lv[kCombineRegs], wv[kCombineRegs];
   float M = kNegBig;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[((size_t)s * rows + row) * (D + 4) + D]);
-  float lsum = 0.f, a[D / 64];
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) a[e] = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* pp = part + ((size_t)s * rows + row) * (D + 4);
-    const float wgt = fast_exp2(pp[D] - M);
-    lsum += pp[D + 1] * wgt;
+  for (int j = 0; j < kCombineRegs; ++j) {
+    const int s = lane + 64 * j;
+    const int sc = s < nsplit ? s : nsplit - 1;          // in bounds: loads need no branch
+    const float m_s = pr[(size_t)sc * rs + D], l_s = pr[(size_t)sc * rs + D + 1];
+    mv[j] = s < nsplit ? m_s : kNegBig;
+    lv[j] = s < nsplit ? l_s : 0.f;
+    if (lv[j] > 0.f) M = fmaxf(M, mv[j]);
+  }
+  M = wave_max(M);
+  float lsum = 0.f;
+  unsigned long long act[kCombineRegs];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) a[e] += pp[lane + 64 * e] * wgt;
+  for (int j = 0; j < kCombineRegs; ++j) {
+    wv[j] = lv[j] > 0.f ? fast_exp2(mv[j] - M) : 0.f;
+    lsum += lv[j] * wv[j];
+    act[j] = __ballot(lv[j] > 0.f);
+  }
+  lsum = wave_sum(lsum);
+  float a[DE];
+#pragma unroll
+  for (int e = 0; e < DE; ++e) a[e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kCombineRegs; ++j) {
+    unsigned long long m = act[j];
+    while (m != 0ull) {
+      // up to 8 active partials at once (their loads are in flight together);
+      // unused slots repeat the first one with weight 0
+      int sl[8];
+      float ww[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (m != 0ull) {
+          const int bit = __builtin_ctzll(m);
+          m &= m - 1ull;
+          sl[u] = 64 * j + bit;
+          ww[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv[j]), bit));
+        } else {
+          sl[u] = sl[0];
+          ww[u] = 0.f;
+        }
+      }
+      float v[8][DE];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < DE; ++e) v[u][e] = pr[(size_t)sl[u] * rs + lane + 64 * e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < DE; ++e) a[e] += v[u][e] * ww[u];
+    }
   }
   const int t = (int)(row % nq);
   const size_t bh = row / nq;
@@ -814,8 +865,145 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   T* orow = reinterpret_cast<T*>(o) + (bh * L + slot_of_i((long long)q0 + t)) * D;
   const float inv = 1.f / lsum;
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) orow[lane + 64 * e] = Elem<T>::from_f(a[e] * inv);
+  for (int e = 0; e < DE; ++e) orow[lane + 64 * e] = Elem<T>::from_f(a[e] * inv);
   if (lse != nullptr && lane == 0) lse[row] = (M + __log2f(lsum)) * kLn2;
+}
+
+// ---------------------------------------------------------------- routed attention, decode-sized problems
+//
+// Few queries: the work is spread as one single-wave block per (2-query tile,
+// entry). Entries 0..K-1 are the first query's selected chunks, K..2K-1 the
+// second query's, and 2K.. the chunks of the tile's window range. A chunk
+// that occurs in more than one place is handled once: a selected chunk inside
+// the window range belongs to its window entry, and a chunk chosen by both
+// queries belongs to the first query's entry. A block stages its one chunk,
+// runs one tile step for both queries (window keys, selected-chunk keys or
+// nothing, per query) and writes unnormalised partials (O, m, l) that
+// combine_kernel merges. There is no chunk list to build and no loop.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void routed_decode_kernel(RoutedParams p) {
+  typedef RoutedCfg<T, D> C;
+  constexpr int NP = C::NP;
+  constexpr bool SWZ = C::SWZ;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* buf = reinterpret_cast<bf16_t*>(smem);
+  const int lane = threadIdx.x, g16 = lane >> 4;
+  const int bg = blockIdx.y, b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const int tb0 = 2 * blockIdx.x;
+  const int e = blockIdx.z;
+  const long long L = (long long)p.N * kSlots;
+  const long long Tcont = (long long)p.N * kContent;
+
+  // selections of the two queries: lane k holds entry k
+  int s0 = -1, s1 = -1;
+  if (p.K > 0) {   // uniform; idx may be NULL when K = 0
+    const int kl = lane < p.K ? lane : p.K - 1, t1 = tb0 + 1 < p.nq ? tb0 + 1 : tb0;
+    s0 = p.idx[((size_t)bg * p.nq + tb0) * p.K + kl];        // in bounds for every lane: no branch
+    s1 = p.idx[((size_t)bg * p.nq + t1) * p.K + kl];
+    if (lane >= p.K || s0 >= p.N) s0 = -1;
+    if (lane >= p.K || tb0 + 1 >= p.nq || s1 >= p.N) s1 = -1;
+  }
+  const int t_last = min(tb0 + 2, p.nq) - 1;
+  const long long i_first = (long long)p.q0 + tb0, i_last = (long long)p.q0 + t_last;
+  const int cw0 = (int)(max(0LL, i_first - p.R) / kContent);
+  const int cw1 = (int)(min(Tcont - 1, i_last + p.R) / kContent);
+  int c;
+  if (e < p.K) {
+    c = __builtin_amdgcn_readlane(s0, e);
+    if (c >= cw0 && c <= cw1) c = -1;
+  } else if (e < 2 * p.K) {
+    c = __builtin_amdgcn_readlane(s1, e - p.K);
+    if (c >= 0 && ((c >= cw0 && c <= cw1) || __ballot(s0 == c) != 0ull)) c = -1;
+  } else {
+    c = cw0 + (e - 2 * p.K);
+    if (c > cw1) c = -1;
+  }
+
+  // this lane's row: query qq of the tile, head hh of the group
+  const int qq = (lane & 15) >> 3, hh = lane & 7;
+  const int h = g * G + hh;
+  const int t = tb0 + qq;
+  const bool rv = t < p.nq && hh < G;
+  const long long iq = (long long)p.q0 + t;
+  const size_t rows = (size_t)p.B * p.Hq * p.nq;
+  float* pp = p.part + ((size_t)e * rows + ((size_t)b * p.Hq + h) * p.nq + t) * (D + 4);
+  if (c < 0) {
+    if (rv && g16 == 0) {
+      pp[D] = kNegBig;
+      pp[D + 1] = 0.f;
+    }
+    return;
+  }
+  const long long cf = (long long)c * kContent, cl = cf + kContent - 1;
+  const bool win = cf <= iq + p.R && cl >= iq - p.R;
+  const unsigned long long m0 = __ballot(s0 == c), m1 = __ballot(s1 == c);
+  const unsigned long long mq = qq ? m1 : m0;
+  const int ksel = mq != 0ull ? __builtin_ctzll(mq) : -1;
+  int mode = win ? 1 : (ksel >= 0 ? 2 : 0);
+  if (!rv) mode = 0;
+  int lo = 0, hi = kContent - 1;
+  if (mode == 1) {
+    lo = (int)max(0LL, iq - p.R - cf);
+    hi = (int)min((long long)kContent - 1, iq + p.R - cf);
+  }
+  float zc = 0.f;
+  if (p.K > 0) {   // uniform; zsel may be NULL when K = 0
+    const float zraw =
+        p.zsel[(((size_t)b * p.Hq + (rv ? h : g * G)) * p.nq + (rv ? t : tb0)) * p.K + (ksel >= 0 ? ksel : 0)];
+    zc = mode == 2 ? zraw * kLog2e : 0.f;
+  }
+
+  const T* kg = reinterpret_cast<const T*>(p.k) + ((size_t)bg * L + (size_t)c * kSlots) * D;
+  const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)bg * L + (size_t)c * kSlots) * D;
+  QFrag<D, NP> qf;
+  const T* qrow = rv ? reinterpret_cast<const T*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D : nullptr;
+  if constexpr (SWZ) {
+    dma_chunk<D, 1>(reinterpret_cast<const bf16_t*>(kg), reinterpret_cast<const bf16_t*>(vg), buf, 0, lane);
+    load_qfrag<T, D, NP>(qf, qrow, lane);
+    wait_vm<0>();
+    compiler_fence();
+  } else {
+    KVStage<T, D, 64> stg;
+    stg.load(kg, vg, lane, 64);
+    load_qfrag<T, D, NP>(qf, qrow, lane);
+    stg.store(buf, lane);
+    __syncthreads();
+  }
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) acc[dm] = zero4();
+  float m = kNegBig, l = 0.f;
+  f32x4 sacc[4];
+  s_tile<D, NP, SWZ>(buf, qf, sacc, lane);
+  if constexpr (NP == 1) {
+    const bool general = __ballot(mode == 1) != 0ull;
+    s16x8 pf[2];
+    tile_update_bf16(sacc, general, mode, lo, hi, zc, p.sl2, g16, m, l, pf);
+    pv_tile_packed<D>(buf, pf, acc, lane);
+  } else {
+    float x[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
+    tile_update(x, mode, lo, hi, zc, p.sl2, g16, m, l);
+    pv_tile<D, NP, SWZ>(buf, x, acc, lane);
+  }
+  if (!rv) return;
+  if (l > 0.f) {
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) {
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = acc[dm][i];
+      store4<float>(pp + 16 * dm + 4 * g16, v4);
+    }
+  }
+  if (g16 == 0) {
+    pp[D] = m;
+    pp[D + 1] = l;
+  }
 }
 
 // ---------------------------------------------------------------- sliding-window attention
@@ -960,7 +1148,7 @@ static size_t routed_lds(const RouteDims& dm, int K, int qblock, int waves) {
   return (b + 15) & ~(size_t)15;
 }
 
-AttnPlan plan_routed_attention(const RouteDims& dm, int K, int nq) {
+AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   AttnPlan pl;
   // Prefill-sized problems: 8 waves x 2 tiles = 32 queries per block, no split;
   // 8 waves x 1 tile when the selections of 32 queries do not fit in LDS.
@@ -980,16 +1168,30 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int nq) {
     pl.qblock = 2 * pl.waves * pl.tiles;
   }
   const long long blocks_prefill = (long long)((nq + pl.qblock - 1) / pl.qblock) * dm.B * dm.Hkv;
+  pl.kind = 0;
   if (blocks_prefill < 256) {
-    // Decode-sized: one wave per 2-query tile and the chunk list split across blocks.
+    // Decode-sized. With a narrow window: one single-wave block per (2-query
+    // tile, entry), entries = 2K selected chunks + the tile's window chunks.
+    const long long wmax = (2LL * radius + 2) / kContent + 3;       // window chunks of a 2-query tile
+    const long long nent = 2LL * K + (wmax < dm.N ? wmax : dm.N);
     pl.waves = 1;
     pl.tiles = 1;
     pl.qblock = 2;
-    const long long blocks = (long long)((nq + 1) / 2) * dm.B * dm.Hkv;
-    long long ns = (1024 + blocks - 1) / (blocks > 0 ? blocks : 1);
-    pl.nsplit = (int)(ns < 1 ? 1 : (ns > 8 ? 8 : ns));
+    if (nent <= kMaxPartials) {
+      pl.kind = 1;
+      pl.nsplit = (int)nent;
+    } else {
+      // Wide window: the tile's chunk list is split across blocks instead.
+      const long long blocks = (long long)((nq + 1) / 2) * dm.B * dm.Hkv;
+      long long ns = (1024 + blocks - 1) / (blocks > 0 ? blocks : 1);
+      pl.nsplit = (int)(ns < 1 ? 1 : (ns > 8 ? 8 : ns));
+    }
   }
-  pl.lds = routed_lds(dm, K, pl.qblock, pl.waves);
+  if (pl.kind == 1) {
+    pl.lds = routed_buf_bytes(dm.d, dm.dtype);
+  } else {
+    pl.lds = routed_lds(dm, K, pl.qblock, pl.waves);
+  }
   pl.ws = pl.nsplit > 1 ? align256a((size_t)pl.nsplit * dm.B * dm.Hq * nq * (dm.d + 4) * 4) : 0;
   return pl;
 }
@@ -1020,6 +1222,21 @@ static hipError_t launch_routed_d(const RouteDims& dm, const AttnPlan& pl, const
   return launch_routed_t<T, D, 1, 1, NB1>(dm, pl, prm, st);
 }
 
+template <typename T, int D>
+static hipError_t launch_decode_t(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
+  auto kern = routed_decode_kernel<T, D>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
+  if (e != hipSuccess) return e;
+  dim3 grid((prm.nq + 1) / 2, dm.B * dm.Hkv, pl.nsplit);
+  hipLaunchKernelGGL(kern, grid, dim3(64), pl.lds, st, prm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t rows = (size_t)dm.B * dm.Hq * prm.nq;
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, prm.part,
+                     pl.nsplit, rows, prm.o, prm.lse, prm.nq, dm.N, prm.q0);
+  return hipGetLastError();
+}
+
 hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, const void* q, const void* k,
                                    const void* v, const int32_t* idx, const float* zsel, int K, int radius,
                                    float scale, int q0, int nq, void* o, float* lse, void* ws, hipStream_t st) {
@@ -1042,6 +1259,11 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, cons
   prm.nq = nq;
   prm.nsplit = pl.nsplit;
   prm.sl2 = scale * kLog2e;
+  if (pl.kind == 1) {
+    if (dm.dtype == 1) return dm.d == 64 ? launch_decode_t<bf16_t, 64>(dm, pl, prm, st)
+                                         : launch_decode_t<bf16_t, 128>(dm, pl, prm, st);
+    return dm.d == 64 ? launch_decode_t<float, 64>(dm, pl, prm, st) : launch_decode_t<float, 128>(dm, pl, prm, st);
+  }
   if (dm.dtype == 1) return dm.d == 64 ? launch_routed_d<bf16_t, 64>(dm, pl, prm, st)
                                        : launch_routed_d<bf16_t, 128>(dm, pl, prm, st);
   return dm.d == 64 ? launch_routed_d<float, 64>(dm, pl, prm, st) : launch_routed_d<float, 128>(dm, pl, prm, st);

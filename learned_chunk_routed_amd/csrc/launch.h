@@ -35,11 +35,12 @@ struct AttnPlan {
   int waves;       // waves per block
   int tiles;       // 16-row tiles per wave (a tile = 2 queries x 8 head rows)
   int qblock;      // queries per block = 2 * waves * tiles
-  int nsplit;      // blocks sharing one query block's chunk list (partials combined after)
+  int nsplit;      // partials per query row, merged by combine_kernel when > 1
+  int kind;        // 0: blocks walk a chunk list; 1: one block per (2-query tile, chunk entry)
   size_t lds;      // dynamic LDS bytes per block
   size_t ws;       // workspace bytes for the split partials
 };
-AttnPlan plan_routed_attention(const RouteDims& dm, int K, int nq);
+AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq);
 size_t routed_lds_limit();
 hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& plan, const void* q,
                                    const void* k, const void* v, const int32_t* idx,

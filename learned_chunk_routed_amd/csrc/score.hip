@@ -186,10 +186,28 @@ __global__ __launch_bounds__(256) void q_kernel(const T* __restrict__ q, const T
 #pragma unroll
     for (int j = 0; j < 8; ++j) uv[j] = 0.f;
     if (my_t < nq) {
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float* up = upart + (((size_t)sp * B + b) * nq + my_t) * RP + 32 * ks + 8 * g16;
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
+      // partials in groups of 8 so that 16 loads are in flight at once
+      const size_t sstride = (size_t)B * nq * RP;
+      const float* up0 = upart + ((size_t)b * nq + my_t) * RP + 32 * ks + 8 * g16;
+      int sp = 0;
+      for (; sp + 8 <= nsplit; sp += 8) {
+        f32x4 a[8][2];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[e][0] = *reinterpret_cast<const f32x4*>(up0 + (sp + e) * sstride);
+          a[e][1] = *reinterpret_cast<const f32x4*>(up0 + (sp + e) * sstride + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uv[j] += a[e][0][j];
+            uv[4 + j] += a[e][1][j];
+          }
+      }
+      for (; sp < nsplit; ++sp) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(up0 + sp * sstride);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(up0 + sp * sstride + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           uv[j] += a0[j];
@@ -226,6 +244,167 @@ __global__ __launch_bounds__(256) void q_kernel(const T* __restrict__ q, const T
   }
 }
 
+// 1c. qtilde_small_kernel (bf16, at most 32 queries, as in a decode step): one
+//     block per head computes u = x A for all the queries itself, then
+//     q~ = q + u B_h. Wave w takes every eighth 64-row slice of A (staged in
+//     its own LDS region, next slice prefetched into registers) and the eight
+//     partial u are summed through LDS. No split partials in HBM, one launch.
+constexpr int kSmallQ = 32;
+constexpr int kSmallW = 8;   // waves per block
+
+template <int D, int RP>
+__global__ __launch_bounds__(64 * kSmallW) void qtilde_small_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
+                                                           int Dh, int r, float* __restrict__ qt, int Hq, int N,
+                                                           int q0, int nq) {
+  constexpr int AS = RP + 16;                       // staged A slice row stride (elements)
+  constexpr int US = RP + 4;                        // u row stride (floats)
+  constexpr int BS = D + 16;
+  constexpr int kAPer = kUKc * RP / 8 / 64;         // 16-byte pieces of a slice per lane
+  static_assert(kUKc * AS * 2 >= kSmallQ * US * 4, "u partials alias the A staging area");
+  __shared__ __align__(16) unsigned char stage[kSmallW * kUKc * AS * 2];
+  __shared__ __align__(16) bf16_t b_s[RP * BS];
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const long long L = (long long)N * kSlots;
+  bf16_t* a_s = reinterpret_cast<bf16_t*>(stage) + w * kUKc * AS;
+  const bool vec = (r == RP) && (Dh % kUKc == 0);
+
+  // B_h slice [RP][D] into LDS (rows >= r are zero)
+  for (int e = tid; e < RP * D / 8; e += 64 * kSmallW) {
+    const int kk = (8 * e) / D, n = (8 * e) % D;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (kk < r) v = *reinterpret_cast<const u32x4*>(Bm + (size_t)kk * Hq * D + (size_t)h * D + n);
+    *reinterpret_cast<u32x4*>(b_s + kk * BS + n) = v;
+  }
+
+  // query rows of this lane's A-operand fragments (two 16-row tiles)
+  const bf16_t* xrow[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int t = 16 * mt + L16;
+    xrow[mt] = t < nq ? x + ((size_t)b * L + slot_of((long long)q0 + t)) * Dh : nullptr;
+  }
+  const bf16_t* x0 = x + ((size_t)b * L + slot_of((long long)q0)) * Dh;
+  const int nslices = (Dh + kUKc - 1) / kUKc;
+  u32x4 apre[kAPer];
+  s16x8 xpre[2][kUKc / 32];
+  auto fetch = [&](int sl) {
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+      const int e = 8 * (lane + 64 * j);            // element of the slice, row-major [64][RP]
+      const int kk = e / RP, n = e % RP;
+      const long long k = (long long)sl * kUKc + kk;
+      if (vec) {
+        apre[j] = *reinterpret_cast<const u32x4*>(A + (size_t)k * r + n);
+      } else {
+        s16x8 t;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) t[jj] = (k < Dh && n + jj < r) ? (short)A[(size_t)k * r + n + jj] : (short)0;
+        apre[j] = __builtin_bit_cast(u32x4, t);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < kUKc / 32; ++ks) {
+        const long long k0 = (long long)sl * kUKc + 32 * ks + 8 * g16;
+        if (vec) {
+          // rows past nq read row 0's data (always valid) and are zeroed after
+          const s16x8 v = load8((xrow[mt] ? xrow[mt] : x0) + k0);
+          xpre[mt][ks] = xrow[mt] ? v : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        } else {
+          float xv[8];
+          if (xrow[mt]) load_row8<bf16_t>(xrow[mt], k0, Dh, xv);
+          else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xv[j] = 0.f;
+          }
+          xpre[mt][ks] = pack8(xv);
+        }
+      }
+  };
+  f32x4 acc[2][RP / 16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < RP / 16; ++nt) acc[mt][nt] = zero4();
+  if (w < nslices) fetch(w);
+  for (int sl = w; sl < nslices; sl += kSmallW) {
+    // this wave's region only: its earlier LDS reads were consumed by MFMAs already
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+      const int e = 8 * (lane + 64 * j);
+      *reinterpret_cast<u32x4*>(a_s + (e / RP) * AS + (e % RP)) = apre[j];
+    }
+    s16x8 xf[2][kUKc / 32];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < kUKc / 32; ++ks) xf[mt][ks] = xpre[mt][ks];
+    if (sl + kSmallW < nslices) fetch(sl + kSmallW);
+#pragma unroll
+    for (int ks = 0; ks < kUKc / 32; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < RP / 16; ++nt) {
+        const s16x8 bf = lds_col_frag(a_s, AS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16(xf[mt][ks], bf, acc[mt][nt]);
+      }
+  }
+  __syncthreads();   // every wave is done with its A staging area
+  float* u_s = reinterpret_cast<float*>(stage);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < RP / 16; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u_s[(w * kSmallQ + 16 * mt + 4 * g16 + i) * US + 16 * nt + L16] = acc[mt][nt][i];
+  __syncthreads();
+  for (int e = tid; e < kSmallQ * RP; e += 64 * kSmallW) {
+    const int row = e / RP, col = e % RP;
+    float sum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kSmallW; ++ww) sum += u_s[(ww * kSmallQ + row) * US + col];
+    u_s[row * US + col] = sum;   // wave 0's partial is overwritten only by its own sum
+  }
+  __syncthreads();
+
+  // q~ = q + u B_h: wave w takes row tile w & 1 and a quarter of the D columns
+  const int mt = w & 1, nh = w >> 1;
+  s16x8 uh[RP / 32], ul[RP / 32];
+#pragma unroll
+  for (int ks = 0; ks < RP / 32; ++ks) {
+    float uv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) uv[j] = u_s[(16 * mt + L16) * US + 32 * ks + 8 * g16 + j];
+    pack8_split(uv, uh[ks], ul[ks]);
+  }
+#pragma unroll
+  for (int nn = 0; nn < D / 64; ++nn) {
+    const int nt = nh * (D / 64) + nn;
+    f32x4 c = zero4();
+#pragma unroll
+    for (int ks = 0; ks < RP / 32; ++ks) {
+      const s16x8 bh = lds_col_frag(b_s, BS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+      c = mfma16(ul[ks], bh, c);
+      c = mfma16(uh[ks], bh, c);
+    }
+    const int dd = 16 * nt + L16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * mt + 4 * g16 + i;
+      if (t < nq) {
+        const long long sl = slot_of((long long)q0 + t);
+        const float qv = bf2f(q[((size_t)b * Hq + h) * L * D + (size_t)sl * D + dd]);
+        qt[(((size_t)b * Hq + h) * nq + t) * D + dd] = qv + c[i];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------- 2. scores
 
 // Split a float into NS bf16 planes (2: 16 significant bits, 3: 24 bits).
@@ -247,7 +426,9 @@ __device__ __forceinline__ void split_ns(const float* v, s16x8* out) {
 }
 
 // NS = 2 for bf16 inputs (hi.hi + hi.lo + lo.hi), 3 for float32 inputs (six plane pairs).
-template <int D, int NS>
+// PIPE: load the next head's operands while the current head is multiplied
+// (few blocks, as in a decode step); without it fewer registers, more waves.
+template <int D, int NS, bool PIPE>
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qt, const float* __restrict__ s,
                                                     const float* __restrict__ H, float beta, float scale,
                                                     float* __restrict__ z, float* __restrict__ zhat,
@@ -259,37 +440,60 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qt
   const int ca = c0 + L16;   // A-operand row (chunk) of this lane
   const int tb = t0 + L16;   // B-operand column (query) of this lane
   float zmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  for (int hh = 0; hh < G; ++hh) {
+  // operands of head hh + 1 are loaded while head hh is multiplied
+  f32x4 sa[D / 32][2], qb[D / 32][2];
+  float hv[4];
+  auto fetch = [&](int hh) {
     const int h = g * G + hh;
     const float* srow = s + (((size_t)b * Hq + h) * N + (ca < N ? ca : 0)) * D;
     const float* qrow = qt + (((size_t)b * Hq + h) * nq + (tb < nq ? tb : 0)) * D;
-    f32x4 acc_hi = zero4(), acc_x = zero4();
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const int kk = 32 * ks + 8 * g16;
+      sa[ks][0] = *reinterpret_cast<const f32x4*>(srow + kk);
+      sa[ks][1] = *reinterpret_cast<const f32x4*>(srow + kk + 4);
+      qb[ks][0] = *reinterpret_cast<const f32x4*>(qrow + kk);
+      qb[ks][1] = *reinterpret_cast<const f32x4*>(qrow + kk + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + 4 * g16 + i;
+      hv[i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
+    }
+  };
+  if (PIPE) fetch(0);
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    if (!PIPE) fetch(hh);
+    s16x8 a[D / 32][NS], bb[D / 32][NS];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       float av[8], bv[8];
-      const int kk = 32 * ks + 8 * g16;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(srow + kk);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(srow + kk + 4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(qrow + kk);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(qrow + kk + 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        av[j] = ca < N ? a0[j] : 0.f;
-        av[4 + j] = ca < N ? a1[j] : 0.f;
-        bv[j] = tb < nq ? b0[j] : 0.f;
-        bv[4 + j] = tb < nq ? b1[j] : 0.f;
+        av[j] = ca < N ? sa[ks][0][j] : 0.f;
+        av[4 + j] = ca < N ? sa[ks][1][j] : 0.f;
+        bv[j] = tb < nq ? qb[ks][0][j] : 0.f;
+        bv[4 + j] = tb < nq ? qb[ks][1][j] : 0.f;
       }
-      s16x8 a[NS], bb[NS];
-      split_ns<NS>(av, a);
-      split_ns<NS>(bv, bb);
+      split_ns<NS>(av, a[ks]);
+      split_ns<NS>(bv, bb[ks]);
+    }
+    float hcur[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hcur[i] = hv[i];
+    if (PIPE && hh + 1 < G) fetch(hh + 1);
+    f32x4 acc_hi = zero4(), acc_x = zero4();
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
       if constexpr (NS == 3) {
-        acc_x = mfma16(a[0], bb[2], acc_x);
-        acc_x = mfma16(a[2], bb[0], acc_x);
-        acc_x = mfma16(a[1], bb[1], acc_x);
+        acc_x = mfma16(a[ks][0], bb[ks][2], acc_x);
+        acc_x = mfma16(a[ks][2], bb[ks][0], acc_x);
+        acc_x = mfma16(a[ks][1], bb[ks][1], acc_x);
       }
-      acc_x = mfma16(a[0], bb[1], acc_x);
-      acc_x = mfma16(a[1], bb[0], acc_x);
-      acc_hi = mfma16(a[0], bb[0], acc_hi);
+      acc_x = mfma16(a[ks][0], bb[ks][1], acc_x);
+      acc_x = mfma16(a[ks][1], bb[ks][0], acc_x);
+      acc_hi = mfma16(a[ks][0], bb[ks][0], acc_hi);
     }
     // D layout: lane holds chunk c0 + 4*g16 + i (rows), query t0 + L16 (column)
 #pragma unroll
@@ -297,7 +501,7 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qt
       const int c = c0 + 4 * g16 + i;
       const int t = t0 + L16;
       if (c < N && t < nq) {
-        const float zz = (acc_hi[i] + acc_x[i]) * scale - beta * H[((size_t)b * Hq + h) * N + c];
+        const float zz = (acc_hi[i] + acc_x[i]) * scale - beta * hcur[i];
         z[(((size_t)b * Hq + h) * nq + t) * N + c] = zz;
         zmax[i] = fmaxf(zmax[i], zz);
       }
@@ -331,16 +535,27 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zha
   const float* zr = zhat + rr * N;
   const unsigned long long lt = (1ull << lane) - 1ull;
 
-  uint32_t key[P];
-  int nloc = 0;
+  // All P loads are issued before any is used: the empty asm "redefines" each
+  // value, which keeps the compiler from sinking a load into the branch that
+  // tests its candidate (that would serialise P memory round trips).
+  float zv[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const int c = 64 * j + lane;
-    const bool cand = c < N && ((63LL * c + 62 < i - R) || (63LL * c > i + R));
-    key[j] = cand ? order_key(zr[c]) : 0u;
-    nloc += key[j] != 0u;
+    zv[j] = zr[c < N ? c : N - 1];   // always in bounds
   }
-  const int ncand = wave_sum_i(nloc);
+#pragma unroll
+  for (int j = 0; j < P; ++j) asm volatile("" : "+v"(zv[j]));
+  uint32_t key[P];
+  int ncand = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int c = 64 * j + lane;
+    const bool cand = (c < N) & ((63LL * c + 62 < i - R) | (63LL * c > i + R));
+    key[j] = cand ? order_key(zv[j]) : 0u;
+    ncand += __popcll(__ballot(key[j] != 0u));
+  }
+  // counts are taken with ballots (scalar popcounts), no cross-lane shuffles
   const bool take_all = ncand <= K;
   uint32_t theta = 0u;
   int need = 0;
@@ -349,13 +564,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zha
       const uint32_t trial = theta | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < P; ++j) cnt += key[j] >= trial;
-      if (wave_sum_i(cnt) >= K) theta = trial;
+      for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[j] >= trial));
+      if (cnt >= K) theta = trial;
     }
     int gt = 0;
 #pragma unroll
-    for (int j = 0; j < P; ++j) gt += key[j] > theta;
-    need = K - wave_sum_i(gt);
+    for (int j = 0; j < P; ++j) gt += __popcll(__ballot(key[j] > theta));
+    need = K - gt;
   }
   int base = 0, ties = 0;
 #pragma unroll
@@ -392,6 +607,7 @@ static int u_splits(const RouteDims& dm, int Dh, int nq) {
   const int tiles = (nq + 63) / 64 * dm.B;
   const int nslices = (Dh + kUKc - 1) / kUKc;
   int s = (512 + tiles - 1) / tiles;
+  if (s > 16) s = 16;   // q_kernel re-reads every partial once per head
   if (s > nslices) s = nslices;
   if (s < 1) s = 1;
   const int per = (nslices + s - 1) / s;
@@ -423,6 +639,13 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
 template <typename T, int D, int RP>
 static void launch_qtilde(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
                           int Dh, int r, const ScoreWs& ws, int q0, int nq, hipStream_t st) {
+  if constexpr (sizeof(T) == 2 && RP <= 64) {   // rank 128 would not fit the LDS staging
+    if (nq <= kSmallQ) {
+      hipLaunchKernelGGL((qtilde_small_kernel<D, RP>), dim3(dm.Hq, dm.B), dim3(64 * kSmallW), 0, st, (const bf16_t*)q,
+                         (const bf16_t*)x, (const bf16_t*)A, (const bf16_t*)Bm, Dh, r, ws.qt, dm.Hq, dm.N, q0, nq);
+      return;
+    }
+  }
   const int nsplit = u_splits(dm, Dh, nq);
   const int nslices = (Dh + kUKc - 1) / kUKc;
   const int per = (nslices + nsplit - 1) / nsplit;
@@ -462,9 +685,16 @@ hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const voi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((dm.N + 63) / 64, (nq + 15) / 16, dm.B * dm.Hkv);
-#define LCR_SCORE(DD, NS)                                                                              \
-  hipLaunchKernelGGL((score_kernel<DD, NS>), grid, dim3(256), 0, st, ws.qt, s, H, beta, scale, ws.z, ws.zhat, \
-                     dm.Hq, dm.Hkv, dm.N, nq)
+  const bool pipe = (long long)grid.x * grid.y * grid.z < 2048;
+#define LCR_SCORE(DD, NS)                                                                                   \
+  do {                                                                                                      \
+    if (pipe)                                                                                               \
+      hipLaunchKernelGGL((score_kernel<DD, NS, true>), grid, dim3(256), 0, st, ws.qt, s, H, beta, scale, ws.z, \
+                         ws.zhat, dm.Hq, dm.Hkv, dm.N, nq);                                                   \
+    else                                                                                                    \
+      hipLaunchKernelGGL((score_kernel<DD, NS, false>), grid, dim3(256), 0, st, ws.qt, s, H, beta, scale,     \
+                         ws.z, ws.zhat, dm.Hq, dm.Hkv, dm.N, nq);                                             \
+  } while (0)
   if (dm.d == 64) {
     if (dm.dtype == 1) LCR_SCORE(64, 2);
     else LCR_SCORE(64, 3);

@@ -56,8 +56,8 @@ def default_scale(d):
     return 1.0 / math.sqrt(d)
 
 
-def workspace_bytes(op, dims: Dims, D=0, r=0, K=0, nq=0) -> int:
-    return int(_lib.load().lcr_workspace_bytes(op, dims, D, r, K, nq))
+def workspace_bytes(op, dims: Dims, D=0, r=0, K=0, nq=0, radius=0) -> int:
+    return int(_lib.load().lcr_workspace_bytes(op, dims, D, r, K, radius, nq))
 
 
 def _workspace(nbytes, device, ws=None):
@@ -147,7 +147,7 @@ def routed_attention(q, k, v, idx, zsel, *, radius, scale=None, q0=0, nq=None, o
         lse = torch.empty((B, Hq, nq), dtype=torch.float32, device=dev)
     if lse is not None:
         _check(lse, "lse", dev, torch.float32, (B, Hq, nq))
-    nbytes = workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims, 0, 0, K, nq)
+    nbytes = workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims, 0, 0, K, nq, radius)
     w = _workspace(nbytes, dev, ws)
     check(lib.lcr_routed_attention(dims, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
                                    zsel.data_ptr(), K, radius, scale, q0, nq, out.data_ptr(),

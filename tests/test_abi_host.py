@@ -107,7 +107,7 @@ def test_route_score_topk_validation(lib):
         assert score_call(lib, ptrs=pt) == _lib.LCR_ERR_ARG
     # valid arguments but no workspace: rejected before any launch
     assert score_call(lib) == _lib.LCR_ERR_WORKSPACE
-    need = lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims(), 3584, 64, 32, 100)
+    need = lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims(), 3584, 64, 32, 256, 100)
     assert score_call(lib, ws=P, ws_bytes=need - 1) == _lib.LCR_ERR_WORKSPACE
     # nothing to do: K = 0 or nq = 0 succeed without touching the device, NULL outputs allowed
     assert score_call(lib, K=0, ptrs=[P] * 6 + [NULL, NULL]) == _lib.LCR_OK
@@ -117,19 +117,26 @@ def test_route_score_topk_validation(lib):
 def test_workspace_sizes(lib):
     dm = dims()
     nq = 1000
-    got = lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dm, 3584, 64, 32, nq)
+    got = lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dm, 3584, 64, 32, 256, nq)
     al = lambda x: (x + 255) // 256 * 256
     # q~ rows, group maxima and per-head scores, plus the partial x.A sums
     assert got >= al(28 * nq * 128 * 4) + al(4 * nq * 256 * 4) + al(28 * nq * 256 * 4) + al(nq * 64 * 4)
     assert got % 256 == 0
-    assert lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dm, 3584, 64, 0, nq) == 0
-    assert lib.lcr_workspace_bytes(_lib.OP_CHUNK_SUMMARY, dm, 0, 0, 0, 0) == 0
-    assert lib.lcr_workspace_bytes(_lib.OP_SWA_ATTENTION, dm, 0, 0, 0, 0) == 0
+    assert lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dm, 3584, 64, 0, 256, nq) == 0
+    assert lib.lcr_workspace_bytes(_lib.OP_CHUNK_SUMMARY, dm, 0, 0, 0, 0, 0) == 0
+    assert lib.lcr_workspace_bytes(_lib.OP_SWA_ATTENTION, dm, 0, 0, 0, 0, 0) == 0
     # prefill-sized routed attention needs no workspace; decode-sized splits need partials
-    assert lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dm, 0, 0, 32, 256 * 63) == 0
-    dec = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=2048), 0, 0, 32, 32)
+    assert lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dm, 0, 0, 32, 256, 256 * 63) == 0
+    dec = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=2048), 0, 0, 32, 256, 32)
     assert dec > 0 and dec % 256 == 0
-    assert lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims(dtype=9), 1, 1, 1, 1) == 0
+    # one partial (d + 4 floats) per query row and entry: 2K selected + the window chunks of a 2-query tile
+    entries = 2 * 32 + (2 * 256 + 2) // 63 + 3
+    assert dec >= entries * 28 * 32 * (128 + 4) * 4
+    # a window over the whole sequence makes too many entries: the chunk list is split instead
+    wide = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=2048), 0, 0, 32, 10 ** 6, 32)
+    assert 0 < wide < dec
+    assert lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=2048), 0, 0, 32, -1, 32) == 0
+    assert lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims(dtype=9), 1, 1, 1, 1, 1) == 0
 
 
 def test_routed_attention_validation(lib):

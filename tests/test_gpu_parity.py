@@ -148,6 +148,8 @@ EDGE = [
     ("radius zero", dict(R=0)),
     ("large K", dict(N=40, K=64, R=30)),
     ("entropy weight", dict(beta=0.8)),
+    ("32 queries, rank 64", dict(r=64, D=256), 700, 32),
+    ("5 queries at the end, ragged hidden", dict(), 1507, 5),
 ]
 
 
