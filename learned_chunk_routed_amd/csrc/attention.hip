@@ -33,6 +33,8 @@
 // slots of one head per tile and a band mask.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -789,6 +791,492 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
   }
 }
 
+// ---------------------------------------------------------------- routed attention, prefill (bf16)
+//
+// Same tiles and algebra as routed_attention_kernel, with the work of a block
+// split between one producer wave and kPfCons consumer waves so that no wave
+// waits for another one's progress except through the ring of chunk buffers:
+//  - setup (all waves): the ascending list of chunks the block's queries need,
+//    and per list position a mask of the block's queries active on it (window
+//    or selected), built with LDS atomics; each query's chunk logits.
+//  - producer: walks the list in order and moves each chunk into a free slot of
+//    an NBUF-slot pool with direct-to-LDS loads, K and V as separate halves so
+//    that a consumer can start S = K Q^T before V has landed; it publishes the
+//    slot of each position and the number of landed halves.
+//  - consumer w (2 tiles = 4 queries): visits only the positions where one of
+//    its queries is active (found from the masks with ballots, 64 positions at
+//    a time). A slot is free again once every consumer active on its position
+//    is done with it (a per-slot count), so a consumer that is behind holds only
+//    the slots of positions it still needs, not the whole ring.
+// A consumer whose two tiles are both active on a chunk reads each K and V
+// fragment once for both.
+constexpr int kPfCons = 7;                 // consumer waves
+constexpr int kPfWaves = kPfCons + 1;      // + the producer
+constexpr int kPfQB = 4 * kPfCons;         // queries per block
+
+__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
+// Softmax update of a bf16 tile (see tile_update_bf16); WINDOW selects at
+// compile time whether per-key window bounds are applied.
+template <bool WINDOW>
+__device__ __forceinline__ float tile_softmax(f32x4 sacc[4], int mode, int lo, int hi, float zc, float sl2, int g16,
+                                              float& m, float& l, s16x8 pf[2]) {
+  if constexpr (WINDOW) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * mt + 4 * g16 + i;
+        sacc[mt][i] = (key >= lo && key <= hi) ? sacc[mt][i] : -INFINITY;
+      }
+  } else {
+    if (g16 == 3) sacc[3][3] = -INFINITY;   // chunk slot 63: the routing mask, never a key
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+    mx = fmax_nc(mx, fmax_nc(fmax_nc(sacc[mt][0], sacc[mt][1]), fmax_nc(sacc[mt][2], sacc[mt][3])));
+  mx = col_max(mx);
+  const float mb = mx * sl2;
+  const float m_old = m;
+  const float m_cand = mode == 1 ? fmax_nc(m_old, mb) : (mode == 2 ? fmax_nc(m_old, zc) : m_old);
+  const float m_new = m_cand > m_old + 8.f ? m_cand : m_old;
+  const float base = mode == 2 ? mb : (mode == 1 ? m_new : 0.f);
+  float e[16];
+  float rs = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[4 * mt + i] = fast_exp2(fmaf(sacc[mt][i], sl2, -base));
+      rs += e[4 * mt + i];
+    }
+  rs = col_sum(rs);
+  const float alpha = mode == 0 ? 1.f : fast_exp2(m_old - m_new);
+  float scale;
+  if (mode == 2) {
+    const float wz = fast_exp2(zc - m_new);
+    l = l * alpha + wz;
+    scale = wz * __builtin_amdgcn_rcpf(rs);
+  } else {
+    l = mode == 1 ? l * alpha + rs : l;
+    scale = mode == 1 ? 1.f : 0.f;
+  }
+  m = mode == 0 ? m_old : m_new;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+    u32x4 wv;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int mt = 2 * ks + (h >> 1), i0 = 2 * (h & 1);
+      wv[h] = pack2_bf16(e[4 * mt + i0] * scale, e[4 * mt + i0 + 1] * scale);
+    }
+    pf[ks] = __builtin_bit_cast(s16x8, wv);
+  }
+  return alpha;
+}
+
+// S^T for NT tiles sharing every K fragment read.
+template <int D, int NT>
+__device__ __forceinline__ void s_tiles(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4], int lane) {
+  typedef TileLayout<D, true> TL;
+  const int L16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t][mt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const s16x8 a = load8(buf + TL::k_off(16 * mt + L16, 4 * ks + g16));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][mt] = mfma16(a, q[t].f[ks][0], acc[t][mt]);
+    }
+  }
+}
+
+// O^T += V^T P^T for NT tiles sharing every V^T fragment read.
+template <int D, int NT>
+__device__ __forceinline__ void pv_tiles(const bf16_t* buf, const s16x8 (*pf)[2], f32x4 (*o)[D / 16], int lane) {
+  typedef TileLayout<D, true> TL;
+  const int g16 = lane >> 4, L16 = lane & 15;
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r0 = 32 * ks + 4 * g16 + (L16 >> 2);
+      const int col = 16 * dm + 4 * (L16 & 3);
+      const s16x4 lo = ds_read_tr(buf + TL::KE + TL::v_off(r0, col));
+      const s16x4 hi = ds_read_tr(buf + TL::KE + TL::v_off(r0 + 16, col));
+      const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) o[t][dm] = mfma16(a, pf[t][ks], o[t][dm]);
+    }
+  }
+}
+
+// One half (K or V) of a chunk: NI = D / 8 direct-to-LDS instructions of 1 KB.
+template <int D>
+__device__ __forceinline__ void dma_half(const bf16_t* src, bf16_t* dst, bool is_v, int lane) {
+  typedef TileLayout<D, true> TL;
+  constexpr int NI = D / 8, RPI = 512 / D, BPR = D / 8;
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int pr = ii * RPI + lane / BPR, pb = lane % BPR;
+    const int sw = is_v ? TL::swz_v(pr) : TL::swz_k(pr);
+    dma16(src + pr * D + ((pb ^ sw) << 3), dst + ii * 512);
+  }
+}
+
+// The same half with the global address split into a uniform 64-bit base
+// (SGPRs) and per-lane 32-bit offsets that depend only on the lane and on the
+// instruction's position in a group of four (the swizzle repeats every 16 rows,
+// one group spans 4 KB). voff[u] is precomputed once; per instruction only M0
+// changes. No output registers: completion is awaited with wait_vm.
+template <int D>
+__device__ __forceinline__ int dma_voff(bool is_v, int u, int lane) {
+  typedef TileLayout<D, true> TL;
+  constexpr int RPI = 512 / D, BPR = D / 8;
+  const int pr = u * RPI + lane / BPR, pb = lane % BPR;
+  const int sw = is_v ? TL::swz_v(pr) : TL::swz_k(pr);
+  return pr * D * 2 + ((pb ^ sw) << 4);
+}
+
+template <int D>
+__device__ __forceinline__ void dma_half_fast(const bf16_t* src, uint32_t lds, const int* voff) {
+  constexpr int NI = D / 8;
+  static_assert(NI % 4 == 0, "groups of four instructions");
+#pragma unroll
+  for (int g = 0; g < NI / 4; ++g) {
+    const bf16_t* sg = src + g * 2048;   // 4 KB per group
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds + (4 * g + u) * 1024),
+                   "v"(voff[u]), "s"(sg)
+                   : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ void lds_store_rel(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int lds_load_rel(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <int D, int NBUF>
+__global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedParams p) {
+  typedef TileLayout<D, true> TL;
+  constexpr int BUFE = TL::PL;                 // elements per chunk buffer (K then V)
+  constexpr int NI = D / 8;                    // DMA instructions per half
+  constexpr int HF = (63 / NI) < 2 * NBUF ? (63 / NI) : 2 * NBUF;   // halves in flight
+  static_assert(HF >= 2 && (HF - 1) * NI < 64, "in-flight loads must fit the vmcnt counter");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int G = p.Hq / p.Hkv;
+  bf16_t* kvb = reinterpret_cast<bf16_t*>(smem);
+  float* zs = reinterpret_cast<float*>(smem + (size_t)NBUF * BUFE * sizeof(bf16_t));   // [QB][G][K]
+  int* pos_chunk = reinterpret_cast<int*>(zs + kPfQB * G * p.K);                      // [N]
+  unsigned* pos_mask = reinterpret_cast<unsigned*>(pos_chunk + p.N);                  // [N]
+  short* pos_of = reinterpret_cast<short*>(pos_mask + p.N);                           // [N]
+  __shared__ int s_n;
+  __shared__ int s_landed;           // halves landed: K of position j is half 2j, V half 2j + 1
+  __shared__ int s_rem[NBUF];        // consumers still to finish the position held by a slot
+  __shared__ int s_fail;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
+  const int bg = blockIdx.y, b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int tb0 = blockIdx.x * kPfQB;
+  const long long L = (long long)p.N * kSlots;
+  const long long Tcont = (long long)p.N * kContent;
+  const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (size_t)bg * L * D;
+  const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (size_t)bg * L * D;
+  constexpr int NT = 64 * kPfWaves;
+
+  // ---- setup: chunk list, per-position query masks, chunk logits
+  if (tid == 0) {
+    s_landed = 0;
+    s_fail = 0;
+  }
+  if (tid < NBUF) s_rem[tid] = 0;
+  for (int c = tid; c < p.N; c += NT) pos_of[c] = 0;
+  __syncthreads();
+  const int t_last = min(tb0 + kPfQB, p.nq) - 1;
+  {
+    const long long i_first = (long long)p.q0 + tb0, i_last = (long long)p.q0 + t_last;
+    const int cw0 = (int)(max(0LL, i_first - p.R) / kContent);
+    const int cw1 = (int)(min(Tcont - 1, i_last + p.R) / kContent);
+    for (int c = cw0 + tid; c <= cw1; c += NT) pos_of[c] = 1;
+  }
+  for (int e = tid; e < kPfQB * p.K; e += NT) {
+    const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
+    const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
+    if (c >= 0 && c < p.N) pos_of[c] = 1;
+  }
+  for (int e = tid; e < kPfQB * G * p.K; e += NT) {
+    const int qi = e / (G * p.K), rem = e - qi * G * p.K, hh2 = rem / p.K, kk = rem - hh2 * p.K;
+    const int t = tb0 + qi;
+    zs[e] = (t < p.nq) ? p.zsel[(((size_t)b * p.Hq + g * G + hh2) * p.nq + t) * p.K + kk] * kLog2e : 0.f;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 < p.N; c0 += 64) {
+      const int c = c0 + lane;
+      const bool f = c < p.N && pos_of[c] != 0;
+      const unsigned long long m = __ballot(f);
+      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (f) {
+        pos_chunk[pos] = c;
+        pos_mask[pos] = 0u;
+        pos_of[c] = (short)pos;
+      }
+      base += __popcll(m);
+    }
+    if (lane == 0) s_n = base;
+  }
+  __syncthreads();
+  const int n = s_n;
+  for (int e = tid; e < kPfQB * p.K; e += NT) {
+    const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
+    const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
+    if (c >= 0 && c < p.N) atomicOr(&pos_mask[pos_of[c]], 1u << qi);
+  }
+  for (int qi = w; qi < kPfQB; qi += kPfWaves) {
+    const int t = tb0 + qi;
+    if (t >= p.nq) continue;
+    const long long i = (long long)p.q0 + t;
+    const int c0 = (int)(max(0LL, i - p.R) / kContent), c1 = (int)(min(Tcont - 1, i + p.R) / kContent);
+    for (int c = c0 + lane; c <= c1; c += 64) atomicOr(&pos_mask[pos_of[c]], 1u << qi);
+  }
+  __syncthreads();
+
+  if (w == kPfCons) {
+    // ---------------- producer
+    int h = 0, told = 0;   // told: landed halves already published (monotonic)
+    int slot = 0;
+    bool ok = true;
+    int voffk[4], voffv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      voffk[u] = dma_voff<D>(false, u, lane);
+      voffv[u] = dma_voff<D>(true, u, lane);
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)kvb);
+    for (; h < 2 * n && ok; ++h) {
+      const int j = h >> 1;
+      if ((h & 1) == 0) {
+        // a free slot for position j
+        unsigned long long fr = __ballot(lane < NBUF && lds_load_rel(&s_rem[lane < NBUF ? lane : 0]) == 0);
+        if (fr == 0ull) {
+          wait_vm<0>();                     // publish what has landed before waiting
+          compiler_fence();
+          if (lane == 0) lds_store_rel(&s_landed, h);
+          told = h;
+          int it = 0;
+          for (; it < kSpinLimit && fr == 0ull; ++it) {
+            __builtin_amdgcn_s_sleep(1);
+            fr = __ballot(lane < NBUF && lds_load_rel(&s_rem[lane < NBUF ? lane : 0]) == 0);
+          }
+          if (fr == 0ull || lds_load_rel(&s_fail) != 0) {
+            ok = false;
+            break;
+          }
+        }
+        slot = __builtin_ctzll(fr);
+        // consumers active on position j: one bit per 4-query group of the mask
+        const unsigned pm = pos_mask[j];
+        int users = 0;
+#pragma unroll
+        for (int cw = 0; cw < kPfCons; ++cw) users += ((pm >> (4 * cw)) & 15u) != 0u ? 1 : 0;
+        if (lane == 0) {
+          lds_store_rel(&s_rem[slot], users);
+          pos_of[j] = (short)slot;          // published before the halves landed count
+        }
+        compiler_fence();
+      }
+      if (h >= HF && h - HF + 1 > told) {
+        wait_vm<(HF - 1) * NI>();           // halves up to h - HF have landed
+        compiler_fence();
+        if (lane == 0) lds_store_rel(&s_landed, h - HF + 1);
+        told = h - HF + 1;
+      }
+      const int c = __builtin_amdgcn_readfirstlane(pos_chunk[j]);
+      const size_t off = (size_t)c * kSlots * D;
+      const uint32_t lbuf = lds0 + (uint32_t)(slot * BUFE * 2);
+      if ((h & 1) == 0) dma_half_fast<D>(kg + off, lbuf, voffk);
+      else dma_half_fast<D>(vg + off, lbuf + TL::KE * 2, voffv);
+    }
+    wait_vm<0>();
+    compiler_fence();
+    if (lane == 0) {
+      if (ok) lds_store_rel(&s_landed, 2 * n);
+      else lds_store_rel(&s_fail, 1);
+    }
+    return;
+  }
+
+  // ---------------- consumer w: queries 4w .. 4w + 3 of the block
+  const int qq = (lane & 15) >> 3, hh = lane & 7;
+  const int h = g * G + hh;
+  QFrag<D, 1> qf[2];
+  f32x4 acc[2][D / 16];
+  float mrow[2], lrow[2];
+  int ptr[2], tq[2];
+  bool rv[2];
+  long long iq[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    tq[tt] = tb0 + 4 * w + 2 * tt + qq;
+    iq[tt] = (long long)p.q0 + tq[tt];
+    rv[tt] = tq[tt] < p.nq && hh < G;
+    const bf16_t* qrow = rv[tt] ? reinterpret_cast<const bf16_t*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq[tt])) * D
+                                : nullptr;
+    load_qfrag<bf16_t, D, 1>(qf[tt], qrow, lane);
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) acc[tt][dm] = zero4();
+    mrow[tt] = kNegBig;
+    lrow[tt] = 0.f;
+    ptr[tt] = 0;
+  }
+  const float* zrow[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) zrow[tt] = zs + ((4 * w + 2 * tt + qq) * G + (hh < G ? hh : 0)) * p.K;
+  bool failed = false;
+  for (int base = 0; base < n && !failed; base += 64) {
+    const int pl = base + lane < n ? base + lane : n - 1;
+    const unsigned pm = base + lane < n ? pos_mask[pl] : 0u;
+    const int pc = pos_chunk[pl];
+    unsigned long long mine = __ballot(((pm >> (4 * w)) & 15u) != 0u);
+    while (mine != 0ull) {
+      const int bit = __builtin_ctzll(mine);
+      mine &= mine - 1ull;
+      const int j = base + bit;
+      const int c = __builtin_amdgcn_readlane(pc, bit);
+      const unsigned bits = (unsigned)__builtin_amdgcn_readlane((int)pm, bit) >> (4 * w);
+      // per tile and lane: window keys, selected chunk, or nothing
+      const long long cf = (long long)c * kContent, cl = cf + kContent - 1;
+      int mode[2], lo[2], hi[2];
+      float zc[2];
+      bool act[2], anywin = false;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        act[tt] = ((bits >> (2 * tt)) & 3u) != 0u;
+        const bool qa = ((bits >> (2 * tt + qq)) & 1u) != 0u;
+        const bool win = cf <= iq[tt] + p.R && cl >= iq[tt] - p.R;
+        mode[tt] = (!qa || !rv[tt]) ? 0 : (win ? 1 : 2);
+        lo[tt] = mode[tt] == 1 ? (int)max(0LL, iq[tt] - p.R - cf) : 0;
+        hi[tt] = mode[tt] == 1 ? (int)min((long long)kContent - 1, iq[tt] + p.R - cf) : kContent - 1;
+        zc[tt] = 0.f;
+        if (p.K > 0) zc[tt] = zrow[tt][ptr[tt] < p.K ? ptr[tt] : p.K - 1];   // K uniform
+        if (qa && !win) ++ptr[tt];
+        anywin = anywin || (__ballot(mode[tt] == 1) != 0ull);
+      }
+      // K of position j landed?
+      {
+        int it = 0;
+        while (lds_load_rel(&s_landed) < 2 * j + 1 && it < kSpinLimit) {
+          __builtin_amdgcn_s_sleep(1);
+          ++it;
+        }
+        if (it == kSpinLimit || lds_load_rel(&s_fail) != 0) {
+          failed = true;
+          break;
+        }
+      }
+      compiler_fence();
+      const int slot = pos_of[j];   // written by the producer before the landed count
+      const bf16_t* buf = kvb + slot * BUFE;
+      if (act[0] && act[1]) {
+        f32x4 sacc[2][4];
+        s_tiles<D, 2>(buf, qf, sacc, lane);
+        s16x8 pf[2][2];
+        float alpha[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          alpha[tt] = anywin ? tile_softmax<true>(sacc[tt], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16, mrow[tt],
+                                                  lrow[tt], pf[tt])
+                             : tile_softmax<false>(sacc[tt], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16, mrow[tt],
+                                                   lrow[tt], pf[tt]);
+          if (__ballot(alpha[tt] != 1.f) != 0ull) {
+#pragma unroll
+            for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha[tt];
+          }
+        }
+        {
+          int it = 0;
+          while (lds_load_rel(&s_landed) < 2 * j + 2 && it < kSpinLimit) {
+            __builtin_amdgcn_s_sleep(1);
+            ++it;
+          }
+          if (it == kSpinLimit) {
+            failed = true;
+            break;
+          }
+        }
+        compiler_fence();
+        pv_tiles<D, 2>(buf, pf, acc, lane);
+      } else {
+        // one tile: the same code for tile 0 or tile 1, chosen by a uniform branch
+        auto single = [&](auto tile) -> bool {
+          constexpr int tt = decltype(tile)::value;
+          f32x4 sacc[1][4];
+          s_tiles<D, 1>(buf, &qf[tt], sacc, lane);
+          s16x8 pf[1][2];
+          const float alpha = anywin ? tile_softmax<true>(sacc[0], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16,
+                                                          mrow[tt], lrow[tt], pf[0])
+                                     : tile_softmax<false>(sacc[0], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16,
+                                                           mrow[tt], lrow[tt], pf[0]);
+          if (__ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+            for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+          }
+          int it = 0;
+          while (lds_load_rel(&s_landed) < 2 * j + 2 && it < kSpinLimit) {
+            __builtin_amdgcn_s_sleep(1);
+            ++it;
+          }
+          if (it == kSpinLimit) return false;
+          compiler_fence();
+          pv_tiles<D, 1>(buf, pf, &acc[tt], lane);
+          return true;
+        };
+        const bool done = act[0] ? single(std::integral_constant<int, 0>{}) : single(std::integral_constant<int, 1>{});
+        if (!done) {
+          failed = true;
+          break;
+        }
+      }
+      // every LDS read of the slot has returned: release it
+      wait_lgkm0();
+      compiler_fence();
+      if (lane == 0) __hip_atomic_fetch_add(&s_rem[slot], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  if (failed && lane == 0) lds_store_rel(&s_fail, 1);
+
+  // ---- results
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    if (!rv[tt]) continue;
+    const float inv = 1.f / lrow[tt];
+    bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq[tt])) * D;
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) {
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = acc[tt][dm][i] * inv;
+      store4<bf16_t>(orow + 16 * dm + 4 * g16, v4);
+    }
+    if (p.lse != nullptr && g16 == 0)
+      p.lse[((size_t)b * p.Hq + h) * p.nq + tq[tt]] = (mrow[tt] + __log2f(lrow[tt])) * kLn2;
+  }
+}
+
 // Merge the split partials of every query row (one wave per row). Partial s of
 // a row holds (O, m, l) at part[(s * rows + row) * (D + 4)]; a partial with
 // l = 0 saw no key of the row and its O is not read (it may not be written).
@@ -1148,6 +1636,14 @@ static size_t routed_lds(const RouteDims& dm, int K, int qblock, int waves) {
   return (b + 15) & ~(size_t)15;
 }
 
+// LDS of routed_prefill_kernel: the ring, the block's chunk logits and the
+// per-position tables (chunk, query mask, position of each chunk).
+static size_t prefill_lds(const RouteDims& dm, int K, int nbuf) {
+  const int G = dm.Hq / dm.Hkv;
+  const size_t b = (size_t)nbuf * 2 * 64 * dm.d * 2 + (size_t)kPfQB * G * K * 4 + (size_t)dm.N * (4 + 4 + 2);
+  return (b + 15) & ~(size_t)15;
+}
+
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   AttnPlan pl;
   // Prefill-sized problems: 8 waves x 2 tiles = 32 queries per block, no split;
@@ -1191,6 +1687,22 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
     pl.lds = routed_buf_bytes(dm.d, dm.dtype);
   } else {
     pl.lds = routed_lds(dm, K, pl.qblock, pl.waves);
+  }
+  pl.nbuf = 0;
+  if (pl.kind == 0 && pl.nsplit == 1 && dm.dtype == 1 && dm.N < 32768) {
+    // bf16 prefill: producer / consumer kernel with the deepest ring that fits
+    for (int nb = 4; nb >= 2; --nb) {
+      const size_t lds = prefill_lds(dm, K, nb);
+      if (lds <= routed_lds_limit()) {
+        pl.kind = 2;
+        pl.nbuf = nb;
+        pl.waves = kPfWaves;
+        pl.tiles = 2;
+        pl.qblock = kPfQB;
+        pl.lds = lds;
+        break;
+      }
+    }
   }
   pl.ws = pl.nsplit > 1 ? align256a((size_t)pl.nsplit * dm.B * dm.Hq * nq * (dm.d + 4) * 4) : 0;
   return pl;
@@ -1237,6 +1749,23 @@ static hipError_t launch_decode_t(const RouteDims& dm, const AttnPlan& pl, const
   return hipGetLastError();
 }
 
+template <int D, int NBUF>
+static hipError_t launch_prefill_t(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
+  auto kern = routed_prefill_kernel<D, NBUF>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
+  if (e != hipSuccess) return e;
+  dim3 grid((prm.nq + kPfQB - 1) / kPfQB, dm.B * dm.Hkv);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kPfWaves), pl.lds, st, prm);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
+  if (pl.nbuf >= 4) return launch_prefill_t<D, 4>(dm, pl, prm, st);
+  if (pl.nbuf == 3) return launch_prefill_t<D, 3>(dm, pl, prm, st);
+  return launch_prefill_t<D, 2>(dm, pl, prm, st);
+}
+
 hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, const void* q, const void* k,
                                    const void* v, const int32_t* idx, const float* zsel, int K, int radius,
                                    float scale, int q0, int nq, void* o, float* lse, void* ws, hipStream_t st) {
@@ -1259,6 +1788,7 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, cons
   prm.nq = nq;
   prm.nsplit = pl.nsplit;
   prm.sl2 = scale * kLog2e;
+  if (pl.kind == 2) return dm.d == 64 ? launch_prefill_d<64>(dm, pl, prm, st) : launch_prefill_d<128>(dm, pl, prm, st);
   if (pl.kind == 1) {
     if (dm.dtype == 1) return dm.d == 64 ? launch_decode_t<bf16_t, 64>(dm, pl, prm, st)
                                          : launch_decode_t<bf16_t, 128>(dm, pl, prm, st);

@@ -36,7 +36,9 @@ struct AttnPlan {
   int tiles;       // 16-row tiles per wave (a tile = 2 queries x 8 head rows)
   int qblock;      // queries per block = 2 * waves * tiles
   int nsplit;      // partials per query row, merged by combine_kernel when > 1
-  int kind;        // 0: blocks walk a chunk list; 1: one block per (2-query tile, chunk entry)
+  int kind;        // 0: blocks walk a chunk list; 1: one block per (2-query tile, chunk entry);
+                   // 2: producer / consumer waves over a chunk ring (bf16 prefill)
+  int nbuf;        // ring slots of kind 2
   size_t lds;      // dynamic LDS bytes per block
   size_t ws;       // workspace bytes for the split partials
 };

@@ -596,6 +596,300 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zha
   }
 }
 
+// ---------------------------------------------------------------------------- 4. fused scoring (bf16)
+//
+// route_score_kernel: for a tile of QT = 16 * NT consecutive queries and one
+// KV group, everything between the residual partials and the selection in one
+// block of 8 waves, without writing per-head scores or q~ to memory:
+//  A. for each head of the group: q~^T = q^T + B_h^T u^T on MFMA (u split into
+//     bf16 hi + lo, B exact), then z^T = s q~^T for every chunk on MFMA with
+//     both operands split into hi + lo (hi.hi + hi.lo + lo.hi), scaled, minus
+//     beta * H; the group maximum stays in registers. The q~^T output fragment
+//     is already the B operand of the scoring product (same lane -> k
+//     assignment on both sides), so it only passes through LDS to reach the
+//     waves that own other chunks.
+//  B. exact top-K per query from the group maxima in LDS (bisection on an
+//     order-preserving key with ballot counts, ties to the smaller chunk),
+//     written as idx; the rank of every chosen chunk is kept in LDS.
+//  C. the same products again (bit-identical), and each chosen (query, chunk)
+//     score of every head is written to zsel.
+// Wave w computes q~ for query tile w % NT over 8 / NT of the head dimension,
+// and owns the chunk row tiles w, w + 8, ... of the scores.
+constexpr int kRsWaves = 8;
+// MTW chunk row tiles per wave: N <= 16 * 8 * MTW (MTW * NT = 8 keeps the register use fixed)
+
+template <int D, int RP, int NT>
+struct RsCfg {
+  static constexpr int QT = 16 * NT;          // queries per block
+  static constexpr int KS = D / 32;           // k-steps over the head dimension
+  static constexpr int RK = RP / 32;          // k-steps over the residual rank
+  static constexpr int BS = D + 16;           // staged B_h row stride (bf16)
+  static constexpr int QFB = NT * KS * 2;     // q~ fragments (16 B per lane) in LDS
+};
+
+// LDS layout (bytes): B_h slice | q~ fragments | group maxima [QT][N+1] f32 | ranks [QT][N] u8 | chosen [8][64] i32
+__host__ __device__ inline size_t rs_off_q(int D, int RP) { return (size_t)RP * (D + 16) * 2; }
+__host__ __device__ inline size_t rs_off_z(int D, int RP, int NT) { return rs_off_q(D, RP) + (size_t)NT * (D / 32) * 2 * 1024; }
+__host__ __device__ inline size_t rs_off_r(int D, int RP, int NT, int N) { return rs_off_z(D, RP, NT) + (size_t)16 * NT * (N + 1) * 4; }
+__host__ __device__ inline size_t rs_off_c(int D, int RP, int NT, int N) { return (rs_off_r(D, RP, NT, N) + (size_t)16 * NT * N + 15) & ~(size_t)15; }
+__host__ __device__ inline size_t rs_lds(int D, int RP, int NT, int N) { return rs_off_c(D, RP, NT, N) + kRsWaves * 64 * 4; }
+
+template <int D, int RP, int NT, int MTW, typename Emit>
+__device__ __forceinline__ void rs_head_scores(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bm,
+                                               const float* __restrict__ s, const float* __restrict__ H,
+                                               unsigned char* smem, const s16x8 (&uh)[RP / 32],
+                                               const s16x8 (&ul)[RP / 32], int h, int b, int Hq, int N, int q0,
+                                               int t0, int nq, int r, float scale, float beta,
+                                               Emit&& emit) {
+  typedef RsCfg<D, RP, NT> C;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const long long L = (long long)N * kSlots;
+  bf16_t* b_s = reinterpret_cast<bf16_t*>(smem);
+  s16x8* qa = reinterpret_cast<s16x8*>(smem + rs_off_q(D, RP));
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  __syncthreads();   // previous head: every wave is done with b_s and the q~ fragments
+  for (int e = tid; e < RP * D / 8; e += 64 * kRsWaves) {
+    const int kk = (8 * e) / D, n = (8 * e) % D;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (kk < r) v = *reinterpret_cast<const u32x4*>(Bm + (size_t)kk * Hq * D + (size_t)h * D + n);
+    *reinterpret_cast<u32x4*>(b_s + kk * C::BS + n) = v;
+  }
+  __syncthreads();
+  // q~^T for query tile nt over k-steps [ks0, ks0 + KSW)
+  constexpr int PARTS = kRsWaves / NT;
+  constexpr int KSW = (C::KS + PARTS - 1) / PARTS;
+  const int nt = w % NT, ks0 = (w / NT) * KSW;
+  const int tq = t0 + 16 * nt + L16;
+  const bf16_t* qrow = q + ((size_t)b * Hq + h) * L * D + (size_t)slot_of((long long)q0 + (tq < nq ? tq : nq - 1)) * D;
+#pragma unroll
+  for (int kk = 0; kk < KSW; ++kk) {
+    const int ks = ks0 + kk;
+    if (ks >= C::KS) break;
+    float qv[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int dm = 2 * ks + half;           // d rows 16 dm .. 16 dm + 15 of q~^T
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int rk = 0; rk < C::RK; ++rk) {
+        const s16x8 bt = lds_col_frag(b_s, C::BS, 32 * rk + 8 * g16, 32 * rk + 8 * g16 + 4, 16 * dm, lane);
+        acc = mfma16(bt, ul[rk], acc);
+        acc = mfma16(bt, uh[rk], acc);
+      }
+      const s16x4 q4 = *reinterpret_cast<const s16x4*>(qrow + 16 * dm + 4 * g16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[4 * half + i] = acc[i] + bf2f((bf16_t)q4[i]);
+    }
+    s16x8 hi, lo;
+    pack8_split(qv, hi, lo);
+    qa[((nt * C::KS + ks) * 2 + 0) * 64 + lane] = hi;
+    qa[((nt * C::KS + ks) * 2 + 1) * 64 + lane] = lo;
+  }
+  __syncthreads();
+  // z^T = s q~^T for this wave's chunk row tiles (one row tile at a time keeps
+  // the q~ fragments out of registers: they are re-read from LDS per tile)
+  const int NMT = (N + 15) / 16;
+#pragma unroll 1
+  for (int m = 0; m < MTW; ++m) {
+    const int mt = w + kRsWaves * m;
+    if (mt >= NMT) break;
+    const int cr = 16 * mt + L16;
+    const float* srow = s + (((size_t)b * Hq + h) * N + (cr < N ? cr : N - 1)) * D;
+    f32x4 acc_hi[NT], acc_x[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      acc_hi[n] = zero4();
+      acc_x[n] = zero4();
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      // k order of this lane: d = 32 ks + 4 g16 + {0..3}, then 32 ks + 16 + 4 g16 + {0..3}
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(srow + 32 * ks + 4 * g16);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(srow + 32 * ks + 16 + 4 * g16);
+      float av[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = a0[i];
+        av[4 + i] = a1[i];
+      }
+      s16x8 ah, al;
+      pack8_split(av, ah, al);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const s16x8 bh = qa[((n * C::KS + ks) * 2 + 0) * 64 + lane];
+        const s16x8 bl = qa[((n * C::KS + ks) * 2 + 1) * 64 + lane];
+        acc_x[n] = mfma16(ah, bl, acc_x[n]);
+        acc_x[n] = mfma16(al, bh, acc_x[n]);
+        acc_hi[n] = mfma16(ah, bh, acc_hi[n]);
+      }
+    }
+    float hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * mt + 4 * g16 + i;
+      hv[i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      f32x4 zz;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zz[i] = (acc_hi[n][i] + acc_x[n][i]) * scale - beta * hv[i];
+      emit(m, mt, n, zz);
+    }
+  }
+}
+
+template <int D, int RP, int NT, int MTW, int P>
+__global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bm, const float* __restrict__ upart, int nsplit,
+    const float* __restrict__ s, const float* __restrict__ H, float beta, float scale, int32_t* __restrict__ idx,
+    float* __restrict__ zsel, int Hq, int Hkv, int N, int q0, int nq, int r, int K, int R) {
+  typedef RsCfg<D, RP, NT> C;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const int bg = blockIdx.y, b = bg / Hkv, g = bg - b * Hkv;
+  const int G = Hq / Hkv;
+  const int t0 = blockIdx.x * C::QT;
+  const int B = gridDim.y / Hkv;
+  float* zt = reinterpret_cast<float*>(smem + rs_off_z(D, RP, NT));
+  unsigned char* rk_s = smem + rs_off_r(D, RP, NT, N);
+  int* chosen = reinterpret_cast<int*>(smem + rs_off_c(D, RP, NT, N));
+  const int ZS = N + 1;
+  const int NMT = (N + 15) / 16;
+
+  // u^T operand (rank k-steps) of this wave's query tile, partials summed, split hi + lo
+  s16x8 uh[RP / 32], ul[RP / 32];
+  {
+    const int nt = w % NT;
+    const int tq = t0 + 16 * nt + L16;
+    const int tc = tq < nq ? tq : nq - 1;
+#pragma unroll
+    for (int rk = 0; rk < RP / 32; ++rk) {
+      float uv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) uv[j] = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) {
+        const float* up = upart + (((size_t)sp * B + b) * nq + tc) * RP + 32 * rk + 8 * g16;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uv[j] += a0[j];
+          uv[4 + j] += a1[j];
+        }
+      }
+      if (tq >= nq) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) uv[j] = 0.f;
+      }
+      pack8_split(uv, uh[rk], ul[rk]);
+    }
+  }
+
+  // ---- A: group maxima
+  f32x4 zmax[MTW][NT];
+#pragma unroll
+  for (int m = 0; m < MTW; ++m)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) zmax[m][n] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int hh = 0; hh < G; ++hh)
+    rs_head_scores<D, RP, NT, MTW>(q, Bm, s, H, smem, uh, ul, g * G + hh, b, Hq, N, q0, t0, nq, r, scale, beta,
+                                   [&](int m, int, int n, const f32x4& zz) {
+#pragma unroll
+                                     for (int i = 0; i < 4; ++i) zmax[m][n][i] = fmaxf(zmax[m][n][i], zz[i]);
+                                   });
+#pragma unroll
+  for (int m = 0; m < MTW; ++m) {
+    const int mt = w + kRsWaves * m;
+    if (mt >= NMT) break;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * mt + 4 * g16 + i;
+        if (c < N) zt[(16 * n + L16) * ZS + c] = zmax[m][n][i];
+      }
+  }
+  for (int e = tid; e < C::QT * N; e += 64 * kRsWaves) rk_s[e] = 0xFF;
+  __syncthreads();
+
+  // ---- B: top-K per query (wave w: queries w, w + 8, ...)
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int qi = w; qi < C::QT; qi += kRsWaves) {
+    const int t = t0 + qi;
+    if (t >= nq) break;
+    const long long i = (long long)q0 + t;
+    uint32_t key[P];
+    int ncand = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int c = 64 * j + lane;
+      const bool cand = (c < N) & ((63LL * c + 62 < i - R) | (63LL * c > i + R));
+      const float zv = zt[qi * ZS + (c < N ? c : N - 1)];
+      key[j] = cand ? order_key(zv) : 0u;
+      ncand += __popcll(__ballot(key[j] != 0u));
+    }
+    const bool take_all = ncand <= K;
+    uint32_t theta = 0u;
+    int need = 0;
+    if (!take_all) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t trial = theta | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[j] >= trial));
+        if (cnt >= K) theta = trial;
+      }
+      int gt = 0;
+#pragma unroll
+      for (int j = 0; j < P; ++j) gt += __popcll(__ballot(key[j] > theta));
+      need = K - gt;
+    }
+    int base = 0, ties = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const bool nz = key[j] != 0u;
+      const bool gt = take_all ? nz : key[j] > theta;
+      const bool eq = !take_all && nz && key[j] == theta;
+      const unsigned long long em = __ballot(eq);
+      const bool take = gt || (eq && ties + __popcll(em & lt) < need);
+      const unsigned long long tm = __ballot(take);
+      if (take) {
+        const int k = base + __popcll(tm & lt);
+        chosen[w * 64 + k] = 64 * j + lane;
+        rk_s[qi * N + 64 * j + lane] = (unsigned char)k;
+      }
+      base += __popcll(tm);
+      ties += __popcll(em);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane < K) {
+      const int c = lane < base ? chosen[w * 64 + lane] : -1;
+      idx[((size_t)bg * nq + t) * K + lane] = c;
+      if (c < 0)
+        for (int hh = 0; hh < G; ++hh) zsel[(((size_t)b * Hq + g * G + hh) * nq + t) * K + lane] = -INFINITY;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- C: every head's score of each chosen chunk
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    rs_head_scores<D, RP, NT, MTW>(q, Bm, s, H, smem, uh, ul, h, b, Hq, N, q0, t0, nq, r, scale, beta,
+                                   [&](int, int mt, int n, const f32x4& zz) {
+#pragma unroll
+                                     for (int i = 0; i < 4; ++i) {
+                                       const int c = 16 * mt + 4 * g16 + i, qi = 16 * n + L16, t = t0 + qi;
+                                       if (c < N && t < nq) {
+                                         const unsigned k = rk_s[qi * N + c];
+                                         if (k != 0xFFu) zsel[(((size_t)b * Hq + h) * nq + t) * K + k] = zz[i];
+                                       }
+                                     }
+                                   });
+  }
+}
+
 // ---------------------------------------------------------------------------- host side
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -614,9 +908,15 @@ static int u_splits(const RouteDims& dm, int Dh, int nq) {
   return (nslices + per - 1) / per;
 }
 
+// bf16 prefill-sized problems take the fused scoring kernel (no q~, z or zhat in memory).
+static bool fused_score_ok(const RouteDims& dm, int r, int nq) {
+  return dm.dtype == 1 && dm.N <= 512 && r <= 64 && nq > kSmallQ && dm.Hq / dm.Hkv <= 8;
+}
+
 size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
   const size_t upart = (size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4;
+  if (fused_score_ok(dm, r, nq)) return align256(upart);
   return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4) + align256(upart);
 }
 
@@ -624,6 +924,14 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
   char* p = (char*)ws;
   ScoreWs out;
+  (void)Dh;
+  if (fused_score_ok(dm, r, nq)) {
+    out.qt = nullptr;
+    out.zhat = nullptr;
+    out.z = nullptr;
+    out.upart = (float*)p;
+    return out;
+  }
   out.qt = (float*)p;
   p += align256(rows_h * dm.d * 4);
   out.zhat = (float*)p;
@@ -631,8 +939,6 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
   out.z = (float*)p;
   p += align256(rows_h * dm.N * 4);
   out.upart = (float*)p;
-  (void)Dh;
-  (void)r;
   return out;
 }
 
@@ -671,10 +977,46 @@ static void launch_topk(const RouteDims& dm, const ScoreWs& ws, int32_t* idx, fl
                      zsel, dm.Hq, dm.Hkv, dm.N, nq, q0, K, R, nrows);
 }
 
+template <int D, int RP>
+static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const void* x, const void* A,
+                                     const void* Bm, int Dh, int r, const float* s, const float* H, float beta,
+                                     float scale, int K, int radius, int q0, int nq, int32_t* idx, float* zsel,
+                                     const ScoreWs& ws, hipStream_t st) {
+  const int nsplit = u_splits(dm, Dh, nq);
+  const int nslices = (Dh + kUKc - 1) / kUKc;
+  const int per = (nslices + nsplit - 1) / nsplit;
+  hipLaunchKernelGGL((u_kernel<bf16_t, RP>), dim3((nq + 63) / 64, dm.B, nsplit), dim3(256), 0, st, (const bf16_t*)x,
+                     (const bf16_t*)A, Dh, r, ws.upart, dm.N, q0, nq, per);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool wide = dm.N > 256;
+  const int NT = wide ? 2 : 4;
+  const size_t lds = rs_lds(D, RP, NT, dm.N);
+  dim3 grid((nq + 16 * NT - 1) / (16 * NT), dm.B * dm.Hkv);
+#define LCR_RS(NTT, MTW, PP)                                                                                     \
+  do {                                                                                                           \
+    auto kern = route_score_kernel<D, RP, NTT, MTW, PP>;                                                        \
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
+    if (e != hipSuccess) return e;                                                                               \
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kRsWaves), lds, st, (const bf16_t*)q, (const bf16_t*)Bm, ws.upart, \
+                       nsplit, s, H, beta, scale, idx, zsel, dm.Hq, dm.Hkv, dm.N, q0, nq, r, K, radius);         \
+  } while (0)
+  if (wide) LCR_RS(2, 4, 8);
+  else LCR_RS(4, 2, 4);
+#undef LCR_RS
+  return hipGetLastError();
+}
+
 hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const void* x, const void* A,
                                    const void* Bm, int D, int r, const float* s, const float* H,
                                    float beta, float scale, int K, int radius, int q0, int nq,
                                    int32_t* idx, float* zsel, const ScoreWs& ws, hipStream_t st) {
+  if (fused_score_ok(dm, r, nq)) {
+    if (dm.d == 64) return r <= 32 ? launch_fused_score<64, 32>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st)
+                                   : launch_fused_score<64, 64>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st);
+    return r <= 32 ? launch_fused_score<128, 32>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st)
+                   : launch_fused_score<128, 64>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st);
+  }
   if (dm.dtype == 1) {
     if (dm.d == 64) launch_qtilde_r<bf16_t, 64>(dm, q, x, A, Bm, D, r, ws, q0, nq, st);
     else launch_qtilde_r<bf16_t, 128>(dm, q, x, A, Bm, D, r, ws, q0, nq, st);

@@ -165,6 +165,34 @@ def test_route_layer_edge(case, dtype):
     route_parity(cfg, q0=q0, nq=nq, label=f"{name} [{dtype}]")
 
 
+# Prefill-sized edge cases (enough query blocks for the prefill kernel), checked on
+# sampled query blocks: first, last and a middle block of the queried range.
+PREFILL_EDGE = [
+    ("window only (K=0)", dict(K=0)),
+    ("ragged query range", dict(), 1000, 5001),
+    ("eight-head groups", dict(Hq=16, Hkv=2)),
+    ("single-head groups", dict(Hq=4, Hkv=4)),
+    ("head dim 64", dict(d=64)),
+    ("K=64", dict(K=64, R=30)),
+    ("radius zero", dict(R=0)),
+    ("wide window", dict(R=3000)),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_EDGE, ids=[c[0] for c in PREFILL_EDGE])
+def test_route_layer_prefill_edge(case):
+    name, over = case[0], case[1]
+    q0, nq = (case[2], case[3]) if len(case) > 2 else (0, None)
+    base = dict(N=128, Hq=8, Hkv=2, d=128, r=16, D=96, K=8, R=128, beta=0.0, dtype="bf16")
+    base.update(over)
+    cfg = get_config("tiny_fp32", **base)
+    nq_eff = cfg.T - q0 if nq is None else nq
+    lo, hi = q0, q0 + nq_eff
+    mid = lo + (nq_eff // 2) // 64 * 64
+    queries = np.unique(np.concatenate([np.arange(lo, lo + 64), np.arange(mid, mid + 64), np.arange(hi - 64, hi)]))
+    route_parity(cfg, queries=queries, q0=q0, nq=nq, label=f"prefill {name}")
+
+
 def test_determinism_and_decode_split_matches_prefill():
     """Two runs are bitwise identical; the split (decode) plan equals the unsplit plan."""
     cfg = get_config("tiny_fp32", N=64, Hq=8, Hkv=2, d=128, r=32, D=256, K=8, R=128, dtype="bf16")
