@@ -89,6 +89,22 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(hf32x2{a, b}, hbf16x2));
 }
 
+// x = hi + lo as pack8_split, with the round-to-nearest-even conversions done by
+// v_cvt_pk_bf16_f32 (two values per instruction).
+__device__ __forceinline__ void pack8_split_hw(const float* v, s16x8& hi, s16x8& lo) {
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  u32x4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t hp = pack2_bf16(v[2 * j], v[2 * j + 1]);
+    h[j] = hp;
+    const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xFFFF0000u);
+    l[j] = pack2_bf16(v[2 * j] - h0, v[2 * j + 1] - h1);
+  }
+  hi = __builtin_bit_cast(s16x8, h);
+  lo = __builtin_bit_cast(s16x8, l);
+}
+
 // 16-byte load of 8 bf16 values (any address space the compiler can see).
 __device__ __forceinline__ s16x8 load8(const bf16_t* p) { return *reinterpret_cast<const s16x8*>(p); }
 

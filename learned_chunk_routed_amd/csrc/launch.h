@@ -8,6 +8,8 @@
 
 namespace lcr {
 
+typedef uint16_t bf16_t;
+
 struct RouteDims {
   int B, Hq, Hkv, N, d, dtype;  // dtype: 0 = float32, 1 = bfloat16
 };
@@ -22,6 +24,7 @@ struct ScoreWs {
   float* zhat;  // [B,Hkv,nq,N] group maximum of the scores
   float* z;     // [B,Hq,nq,N]  per-head scores
   float* upart; // [splits,B,nq,rank padded to 32/64/128]  partial x A
+  bf16_t* splanes; // [B,Hq,N,2d] summaries as bf16 hi then lo, k-permuted (fused path)
 };
 size_t score_ws_bytes(const RouteDims& dm, int D, int r, int nq);
 ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int D, int r, int nq);

@@ -616,6 +616,42 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zha
 // Wave w computes q~ for query tile w % NT over 8 / NT of the head dimension,
 // and owns the chunk row tiles w, w + 8, ... of the scores.
 constexpr int kRsWaves = 8;
+
+// Barrier for LDS hand-offs only: this wave's LDS accesses have completed, but
+// its global loads may still be in flight (a __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Summaries as the A operand of the scoring product: per (b, h, chunk) row, the
+// D values split into bf16 hi (first D) and lo (next D), each 32-wide k-step
+// stored as 4 groups of 8 with group g holding d = 32 ks + 4 g + {0..3} and
+// 32 ks + 16 + 4 g + {0..3} (the lane order of the MFMA fragments).
+template <int D>
+__global__ __launch_bounds__(256) void split_summary_kernel(const float* __restrict__ s, bf16_t* __restrict__ sp,
+                                                            long long rows) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;   // one group of 8 per thread
+  constexpr int GPR = D / 8;                                         // groups per row
+  if (e >= rows * GPR) return;
+  const long long row = e / GPR;
+  const int gi = (int)(e % GPR), ks = gi >> 2, gg = gi & 3;
+  const float* src = s + row * D + 32 * ks + 4 * gg;
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 16);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a0[i];
+    v[4 + i] = a1[i];
+  }
+  s16x8 hi, lo;
+  pack8_split_hw(v, hi, lo);
+  *reinterpret_cast<s16x8*>(sp + row * 2 * D + 8 * gi) = hi;
+  *reinterpret_cast<s16x8*>(sp + row * 2 * D + D + 8 * gi) = lo;
+}
 // MTW chunk row tiles per wave: N <= 16 * 8 * MTW (MTW * NT = 8 keeps the register use fixed)
 
 template <int D, int RP, int NT>
@@ -627,40 +663,97 @@ struct RsCfg {
   static constexpr int QFB = NT * KS * 2;     // q~ fragments (16 B per lane) in LDS
 };
 
-// LDS layout (bytes): B_h slice | q~ fragments | group maxima [QT][N+1] f32 | ranks [QT][N] u8 | chosen [8][64] i32
+// LDS layout (bytes): B_h slice | q~ fragments | group maxima, then one head's scores [QT][N+1] f32 |
+// chosen chunks [QT][64] i16 | per-wave compaction buffer [8][64] i32
 __host__ __device__ inline size_t rs_off_q(int D, int RP) { return (size_t)RP * (D + 16) * 2; }
 __host__ __device__ inline size_t rs_off_z(int D, int RP, int NT) { return rs_off_q(D, RP) + (size_t)NT * (D / 32) * 2 * 1024; }
 __host__ __device__ inline size_t rs_off_r(int D, int RP, int NT, int N) { return rs_off_z(D, RP, NT) + (size_t)16 * NT * (N + 1) * 4; }
-__host__ __device__ inline size_t rs_off_c(int D, int RP, int NT, int N) { return (rs_off_r(D, RP, NT, N) + (size_t)16 * NT * N + 15) & ~(size_t)15; }
+__host__ __device__ inline size_t rs_off_c(int D, int RP, int NT, int N) { return (rs_off_r(D, RP, NT, N) + (size_t)16 * NT * 64 * 2 + 15) & ~(size_t)15; }
 __host__ __device__ inline size_t rs_lds(int D, int RP, int NT, int N) { return rs_off_c(D, RP, NT, N) + kRsWaves * 64 * 4; }
+
+// Global loads are issued ahead of their use: the caller passes this head's
+// B_h pieces (loaded during the previous head) and receives the next head's;
+// the q rows are requested before the barriers; each chunk row tile's s
+// fragments are loaded while the previous tile is multiplied.
+template <int D, int RP>
+struct RsBh {
+  static constexpr int PER = (RP * D / 8 + 64 * kRsWaves - 1) / (64 * kRsWaves);   // 16-byte pieces per thread
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  u32x4 v[PER];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ Bm, int h, int Hq, int r) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid + 64 * kRsWaves * j;
+      const int kk = (8 * e) / D, n = (8 * e) % D;
+      const bool ok = e < RP * D / 8 && kk < r;
+      const u32x4 t = *reinterpret_cast<const u32x4*>(Bm + (size_t)(ok ? kk : 0) * Hq * D + (size_t)h * D + n);
+      v[j] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* b_s) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid + 64 * kRsWaves * j;
+      if (e < RP * D / 8) *reinterpret_cast<u32x4*>(b_s + ((8 * e) / D) * (D + 16) + (8 * e) % D) = v[j];
+    }
+  }
+};
 
 template <int D, int RP, int NT, int MTW, typename Emit>
 __device__ __forceinline__ void rs_head_scores(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bm,
-                                               const float* __restrict__ s, const float* __restrict__ H,
+                                               const bf16_t* __restrict__ sp, const float* __restrict__ H,
                                                unsigned char* smem, const s16x8 (&uh)[RP / 32],
-                                               const s16x8 (&ul)[RP / 32], int h, int b, int Hq, int N, int q0,
-                                               int t0, int nq, int r, float scale, float beta,
-                                               Emit&& emit) {
+                                               const s16x8 (&ul)[RP / 32], RsBh<D, RP>& bh_pre, int h, int h_next,
+                                               int b, int Hq, int N, int q0, int t0, int nq, int r, float scale,
+                                               float beta, Emit&& emit) {
   typedef RsCfg<D, RP, NT> C;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
   const long long L = (long long)N * kSlots;
   bf16_t* b_s = reinterpret_cast<bf16_t*>(smem);
   s16x8* qa = reinterpret_cast<s16x8*>(smem + rs_off_q(D, RP));
-  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
-  __syncthreads();   // previous head: every wave is done with b_s and the q~ fragments
-  for (int e = tid; e < RP * D / 8; e += 64 * kRsWaves) {
-    const int kk = (8 * e) / D, n = (8 * e) % D;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (kk < r) v = *reinterpret_cast<const u32x4*>(Bm + (size_t)kk * Hq * D + (size_t)h * D + n);
-    *reinterpret_cast<u32x4*>(b_s + kk * C::BS + n) = v;
-  }
-  __syncthreads();
-  // q~^T for query tile nt over k-steps [ks0, ks0 + KSW)
   constexpr int PARTS = kRsWaves / NT;
   constexpr int KSW = (C::KS + PARTS - 1) / PARTS;
   const int nt = w % NT, ks0 = (w / NT) * KSW;
   const int tq = t0 + 16 * nt + L16;
   const bf16_t* qrow = q + ((size_t)b * Hq + h) * L * D + (size_t)slot_of((long long)q0 + (tq < nq ? tq : nq - 1)) * D;
+  // q rows of this wave's part, requested before the barriers
+  s16x4 q4[KSW][2];
+#pragma unroll
+  for (int kk = 0; kk < KSW; ++kk)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int ks = ks0 + kk < C::KS ? ks0 + kk : C::KS - 1;
+      q4[kk][half] = *reinterpret_cast<const s16x4*>(qrow + 16 * (2 * ks + half) + 4 * g16);
+    }
+  // chunk row tiles of this wave, two at a time; the first pair's s fragments
+  // are requested before the barriers
+  const int NMT = (N + 15) / 16;
+  constexpr int MP = MTW < 2 ? MTW : 2;
+  auto load_s = [&](int m0, s16x8 (&f)[MP][D / 32][2]) {
+#pragma unroll
+    for (int mm = 0; mm < MP; ++mm) {
+      int mt = w + kRsWaves * (m0 + mm);
+      mt = mt < NMT ? mt : NMT - 1;
+      const int cr = 16 * mt + L16;
+      const bf16_t* srow = sp + (((size_t)b * Hq + h) * N + (cr < N ? cr : N - 1)) * 2 * D;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        // k order of this lane: d = 32 ks + 4 g16 + {0..3}, then 32 ks + 16 + 4 g16 + {0..3}
+        f[mm][ks][0] = load8(srow + 32 * ks + 8 * g16);
+        f[mm][ks][1] = load8(srow + D + 32 * ks + 8 * g16);
+      }
+    }
+  };
+  s16x8 scur[MP][D / 32][2];
+  load_s(0, scur);
+
+  lds_barrier();   // previous head: every wave is done with b_s and the q~ fragments
+  bh_pre.store(b_s);
+  if (h_next >= 0) bh_pre.load(Bm, h_next, Hq, r);
+  lds_barrier();
+  // q~^T for query tile nt over k-steps [ks0, ks0 + KSW)
 #pragma unroll
   for (int kk = 0; kk < KSW; ++kk) {
     const int ks = ks0 + kk;
@@ -676,65 +769,75 @@ __device__ __forceinline__ void rs_head_scores(const bf16_t* __restrict__ q, con
         acc = mfma16(bt, ul[rk], acc);
         acc = mfma16(bt, uh[rk], acc);
       }
-      const s16x4 q4 = *reinterpret_cast<const s16x4*>(qrow + 16 * dm + 4 * g16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qv[4 * half + i] = acc[i] + bf2f((bf16_t)q4[i]);
+      for (int i = 0; i < 4; ++i) qv[4 * half + i] = acc[i] + bf2f((bf16_t)q4[kk][half][i]);
     }
     s16x8 hi, lo;
-    pack8_split(qv, hi, lo);
+    pack8_split_hw(qv, hi, lo);
     qa[((nt * C::KS + ks) * 2 + 0) * 64 + lane] = hi;
     qa[((nt * C::KS + ks) * 2 + 1) * 64 + lane] = lo;
   }
-  __syncthreads();
-  // z^T = s q~^T for this wave's chunk row tiles (one row tile at a time keeps
-  // the q~ fragments out of registers: they are re-read from LDS per tile)
-  const int NMT = (N + 15) / 16;
+  lds_barrier();
+  // z^T = s q~^T: per k-step the q~ fragments of all query tiles are read once
+  // and feed both chunk row tiles of the pair
 #pragma unroll 1
-  for (int m = 0; m < MTW; ++m) {
-    const int mt = w + kRsWaves * m;
-    if (mt >= NMT) break;
-    const int cr = 16 * mt + L16;
-    const float* srow = s + (((size_t)b * Hq + h) * N + (cr < N ? cr : N - 1)) * D;
-    f32x4 acc_hi[NT], acc_x[NT];
+  for (int m0 = 0; m0 < MTW; m0 += MP) {
+    if (w + kRsWaves * m0 >= NMT) break;
+    s16x8 snext[MP][D / 32][2];
+    if (m0 + MP < MTW) load_s(m0 + MP, snext);
+    float hv[MP][4];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      acc_hi[n] = zero4();
-      acc_x[n] = zero4();
-    }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      // k order of this lane: d = 32 ks + 4 g16 + {0..3}, then 32 ks + 16 + 4 g16 + {0..3}
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(srow + 32 * ks + 4 * g16);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(srow + 32 * ks + 16 + 4 * g16);
-      float av[8];
+    for (int mm = 0; mm < MP; ++mm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        av[i] = a0[i];
-        av[4 + i] = a1[i];
+        const int c = 16 * (w + kRsWaves * (m0 + mm)) + 4 * g16 + i;
+        hv[mm][i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
       }
-      s16x8 ah, al;
-      pack8_split(av, ah, al);
+    f32x4 acc_hi[MP][NT], acc_x[MP][NT];
+#pragma unroll
+    for (int mm = 0; mm < MP; ++mm)
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const s16x8 bh = qa[((n * C::KS + ks) * 2 + 0) * 64 + lane];
-        const s16x8 bl = qa[((n * C::KS + ks) * 2 + 1) * 64 + lane];
-        acc_x[n] = mfma16(ah, bl, acc_x[n]);
-        acc_x[n] = mfma16(al, bh, acc_x[n]);
-        acc_hi[n] = mfma16(ah, bh, acc_hi[n]);
+        acc_hi[mm][n] = zero4();
+        acc_x[mm][n] = zero4();
+      }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      s16x8 bq[NT][2];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        bq[n][0] = qa[((n * C::KS + ks) * 2 + 0) * 64 + lane];
+        bq[n][1] = qa[((n * C::KS + ks) * 2 + 1) * 64 + lane];
+      }
+#pragma unroll
+      for (int mm = 0; mm < MP; ++mm)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          acc_x[mm][n] = mfma16(scur[mm][ks][0], bq[n][1], acc_x[mm][n]);
+          acc_x[mm][n] = mfma16(scur[mm][ks][1], bq[n][0], acc_x[mm][n]);
+          acc_hi[mm][n] = mfma16(scur[mm][ks][0], bq[n][0], acc_hi[mm][n]);
+        }
+    }
+#pragma unroll
+    for (int mm = 0; mm < MP; ++mm) {
+      const int m = m0 + mm, mt = w + kRsWaves * m;
+      if (mt >= NMT) break;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        f32x4 zz;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zz[i] = (acc_hi[mm][n][i] + acc_x[mm][n][i]) * scale - beta * hv[mm][i];
+        emit(m, mt, n, zz);
       }
     }
-    float hv[4];
+    if (m0 + MP < MTW) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * mt + 4 * g16 + i;
-      hv[i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
-    }
+      for (int mm = 0; mm < MP; ++mm)
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      f32x4 zz;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) zz[i] = (acc_hi[n][i] + acc_x[n][i]) * scale - beta * hv[i];
-      emit(m, mt, n, zz);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          scur[mm][ks][0] = snext[mm][ks][0];
+          scur[mm][ks][1] = snext[mm][ks][1];
+        }
     }
   }
 }
@@ -742,7 +845,7 @@ __device__ __forceinline__ void rs_head_scores(const bf16_t* __restrict__ q, con
 template <int D, int RP, int NT, int MTW, int P>
 __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bm, const float* __restrict__ upart, int nsplit,
-    const float* __restrict__ s, const float* __restrict__ H, float beta, float scale, int32_t* __restrict__ idx,
+    const bf16_t* __restrict__ s, const float* __restrict__ H, float beta, float scale, int32_t* __restrict__ idx,
     float* __restrict__ zsel, int Hq, int Hkv, int N, int q0, int nq, int r, int K, int R) {
   typedef RsCfg<D, RP, NT> C;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -752,7 +855,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
   const int t0 = blockIdx.x * C::QT;
   const int B = gridDim.y / Hkv;
   float* zt = reinterpret_cast<float*>(smem + rs_off_z(D, RP, NT));
-  unsigned char* rk_s = smem + rs_off_r(D, RP, NT, N);
+  short* sel_s = reinterpret_cast<short*>(smem + rs_off_r(D, RP, NT, N));   // [QT][K] chosen, -1 padded
   int* chosen = reinterpret_cast<int*>(smem + rs_off_c(D, RP, NT, N));
   const int ZS = N + 1;
   const int NMT = (N + 15) / 16;
@@ -782,7 +885,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) uv[j] = 0.f;
       }
-      pack8_split(uv, uh[rk], ul[rk]);
+      pack8_split_hw(uv, uh[rk], ul[rk]);
     }
   }
 
@@ -792,8 +895,11 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
   for (int m = 0; m < MTW; ++m)
 #pragma unroll
     for (int n = 0; n < NT; ++n) zmax[m][n] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  RsBh<D, RP> bh_pre;
+  bh_pre.load(Bm, g * G, Hq, r);
   for (int hh = 0; hh < G; ++hh)
-    rs_head_scores<D, RP, NT, MTW>(q, Bm, s, H, smem, uh, ul, g * G + hh, b, Hq, N, q0, t0, nq, r, scale, beta,
+    rs_head_scores<D, RP, NT, MTW>(q, Bm, s, H, smem, uh, ul, bh_pre, g * G + hh, g * G + (hh + 1 < G ? hh + 1 : 0),
+                                   b, Hq, N, q0, t0, nq, r, scale, beta,
                                    [&](int m, int, int n, const f32x4& zz) {
 #pragma unroll
                                      for (int i = 0; i < 4; ++i) zmax[m][n][i] = fmaxf(zmax[m][n][i], zz[i]);
@@ -810,7 +916,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
         if (c < N) zt[(16 * n + L16) * ZS + c] = zmax[m][n][i];
       }
   }
-  for (int e = tid; e < C::QT * N; e += 64 * kRsWaves) rk_s[e] = 0xFF;
+  for (int e = tid; e < C::QT * K; e += 64 * kRsWaves) sel_s[e] = -1;
   __syncthreads();
 
   // ---- B: top-K per query (wave w: queries w, w + 8, ...)
@@ -854,11 +960,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
       const unsigned long long em = __ballot(eq);
       const bool take = gt || (eq && ties + __popcll(em & lt) < need);
       const unsigned long long tm = __ballot(take);
-      if (take) {
-        const int k = base + __popcll(tm & lt);
-        chosen[w * 64 + k] = 64 * j + lane;
-        rk_s[qi * N + 64 * j + lane] = (unsigned char)k;
-      }
+      if (take) chosen[w * 64 + base + __popcll(tm & lt)] = 64 * j + lane;
       base += __popcll(tm);
       ties += __popcll(em);
     }
@@ -867,26 +969,31 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
     if (lane < K) {
       const int c = lane < base ? chosen[w * 64 + lane] : -1;
       idx[((size_t)bg * nq + t) * K + lane] = c;
+      sel_s[qi * K + lane] = (short)c;
       if (c < 0)
         for (int hh = 0; hh < G; ++hh) zsel[(((size_t)b * Hq + g * G + hh) * nq + t) * K + lane] = -INFINITY;
     }
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- C: every head's score of each chosen chunk
+  // ---- C: every head's score of each chosen chunk: the head's scores go to LDS
+  //      (where the group maxima were), then the chosen ones are gathered into zsel
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
-    rs_head_scores<D, RP, NT, MTW>(q, Bm, s, H, smem, uh, ul, h, b, Hq, N, q0, t0, nq, r, scale, beta,
-                                   [&](int, int mt, int n, const f32x4& zz) {
+    rs_head_scores<D, RP, NT, MTW>(q, Bm, s, H, smem, uh, ul, bh_pre, h, hh + 1 < G ? h + 1 : -1, b, Hq, N, q0, t0,
+                                   nq, r, scale, beta, [&](int, int mt, int n, const f32x4& zz) {
 #pragma unroll
                                      for (int i = 0; i < 4; ++i) {
-                                       const int c = 16 * mt + 4 * g16 + i, qi = 16 * n + L16, t = t0 + qi;
-                                       if (c < N && t < nq) {
-                                         const unsigned k = rk_s[qi * N + c];
-                                         if (k != 0xFFu) zsel[(((size_t)b * Hq + h) * nq + t) * K + k] = zz[i];
-                                       }
+                                       const int c = 16 * mt + 4 * g16 + i;
+                                       if (c < N) zt[(16 * n + L16) * ZS + c] = zz[i];
                                      }
                                    });
+    lds_barrier();   // the head's scores are complete (the next head's first barrier protects them)
+    for (int e = tid; e < C::QT * K; e += 64 * kRsWaves) {
+      const int qi = e / K, k = e - qi * K, t = t0 + qi;
+      const int c = sel_s[e];
+      if (t < nq && c >= 0) zsel[(((size_t)b * Hq + h) * nq + t) * K + k] = zt[qi * ZS + c];
+    }
   }
 }
 
@@ -916,7 +1023,7 @@ static bool fused_score_ok(const RouteDims& dm, int r, int nq) {
 size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
   const size_t upart = (size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4;
-  if (fused_score_ok(dm, r, nq)) return align256(upart);
+  if (fused_score_ok(dm, r, nq)) return align256(upart) + align256((size_t)dm.B * dm.Hq * dm.N * dm.d * 4);
   return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4) + align256(upart);
 }
 
@@ -925,11 +1032,14 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
   char* p = (char*)ws;
   ScoreWs out;
   (void)Dh;
+  out.splanes = nullptr;
   if (fused_score_ok(dm, r, nq)) {
     out.qt = nullptr;
     out.zhat = nullptr;
     out.z = nullptr;
     out.upart = (float*)p;
+    p += align256((size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4);
+    out.splanes = (bf16_t*)p;
     return out;
   }
   out.qt = (float*)p;
@@ -989,6 +1099,11 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
                      (const bf16_t*)A, Dh, r, ws.upart, dm.N, q0, nq, per);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const long long rows = (long long)dm.B * dm.Hq * dm.N;
+  hipLaunchKernelGGL((split_summary_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st, s,
+                     ws.splanes, rows);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const bool wide = dm.N > 256;
   const int NT = wide ? 2 : 4;
   const size_t lds = rs_lds(D, RP, NT, dm.N);
@@ -999,7 +1114,7 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
     if (e != hipSuccess) return e;                                                                               \
     hipLaunchKernelGGL(kern, grid, dim3(64 * kRsWaves), lds, st, (const bf16_t*)q, (const bf16_t*)Bm, ws.upart, \
-                       nsplit, s, H, beta, scale, idx, zsel, dm.Hq, dm.Hkv, dm.N, q0, nq, r, K, radius);         \
+                       nsplit, ws.splanes, H, beta, scale, idx, zsel, dm.Hq, dm.Hkv, dm.N, q0, nq, r, K, radius); \
   } while (0)
   if (wide) LCR_RS(2, 4, 8);
   else LCR_RS(4, 2, 4);

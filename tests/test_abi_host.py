@@ -122,9 +122,10 @@ def test_workspace_sizes(lib):
     # float32: q~ rows, group maxima and per-head scores, plus the partial x.A sums
     assert got >= al(28 * nq * 128 * 4) + al(4 * nq * 256 * 4) + al(28 * nq * 256 * 4) + al(nq * 64 * 4)
     assert got % 256 == 0
-    # bf16 at prefill size: the fused scoring kernel keeps only the partial x.A sums
+    # bf16 at prefill size: the fused scoring kernel keeps only the partial x.A sums and the
+    # summaries as bf16 planes; no per-head scores
     fused = lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims(), 3584, 64, 32, 256, nq)
-    assert al(nq * 64 * 4) <= fused < al(4 * nq * 256 * 4) and fused % 256 == 0
+    assert al(nq * 64 * 4) + al(28 * 256 * 128 * 4) <= fused < al(28 * nq * 256 * 4) and fused % 256 == 0
     dm = dims()
     assert lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dm, 3584, 64, 0, 256, nq) == 0
     assert lib.lcr_workspace_bytes(_lib.OP_CHUNK_SUMMARY, dm, 0, 0, 0, 0, 0) == 0
