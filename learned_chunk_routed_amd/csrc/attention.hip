@@ -451,9 +451,6 @@ __device__ __forceinline__ void dma_chunk(const bf16_t* kc, const bf16_t* vc, bf
 // Compiler-only fence: keeps LDS accesses on their side of a raw barrier or flag.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// s_waitcnt lgkmcnt(0): every LDS (and scalar memory) operation of this wave has completed.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); }
-
 // Bounded wait until an LDS counter reaches target (wave-uniform). Returns false
 // after ~2^22 polls (a fraction of a second), so a logic error cannot hang the GPU.
 constexpr int kSpinLimit = 1 << 22;
@@ -463,13 +460,6 @@ __device__ __forceinline__ bool spin_until_ge(int* ctr, int target) {
     __builtin_amdgcn_s_sleep(1);
   }
   return false;
-}
-
-// s_waitcnt that waits for vector-memory operations only: at most n outstanding.
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Store 4 consecutive output values of a row.
@@ -496,7 +486,8 @@ struct RoutedParams {
   float* lse;
   float* part;
   int B, Hq, Hkv, N, K, R, q0, nq, nsplit;
-  float sl2;  // scale * log2(e)
+  int nent, epb;  // decode-sized plan: entries per 2-query tile, entries per block
+  float sl2;      // scale * log2(e)
 };
 
 // Chunk-staging policy: bf16 inputs go straight from HBM into LDS (swizzled
@@ -984,8 +975,11 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   __shared__ int s_fail;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
-  const int bg = blockIdx.y, b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const int tb0 = blockIdx.x * kPfQB;
+  const int nqb = (p.nq + kPfQB - 1) / kPfQB;
+  const int tile = xcd_tile(nqb * p.B * p.Hkv);   // (batch-head, query block), batch-head major
+  if (tile < 0) return;
+  const int bg = tile / nqb, b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int tb0 = (tile - bg * nqb) * kPfQB;
   const long long L = (long long)p.N * kSlots;
   const long long Tcont = (long long)p.N * kContent;
   const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (size_t)bg * L * D;
@@ -1359,27 +1353,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------- routed attention, decode-sized problems
 //
-// Few queries: the work is spread as one single-wave block per (2-query tile,
-// entry). Entries 0..K-1 are the first query's selected chunks, K..2K-1 the
-// second query's, and 2K.. the chunks of the tile's window range. A chunk
-// that occurs in more than one place is handled once: a selected chunk inside
-// the window range belongs to its window entry, and a chunk chosen by both
-// queries belongs to the first query's entry. A block stages its one chunk,
-// runs one tile step for both queries (window keys, selected-chunk keys or
-// nothing, per query) and writes unnormalised partials (O, m, l) that
-// combine_kernel merges. There is no chunk list to build and no loop.
+// Few queries: the work of a 2-query tile is a list of entries. Entries 0..K-1
+// are the first query's selected chunks, K..2K-1 the second query's, and 2K..
+// the chunks of the tile's window range. A chunk that occurs in more than one
+// place is handled once: a selected chunk inside the window range belongs to
+// its window entry, and a chunk chosen by both queries belongs to the first
+// query's entry. The list is cut into runs of p.epb entries, one single-wave
+// block per (tile, run). A block walks the chunks of its run (bf16: the next
+// chunk is loaded into the second LDS buffer while the current one is
+// multiplied), keeps the online-softmax state of both queries across them and
+// writes one unnormalised partial (O, m, l) per row; combine_kernel merges the
+// runs of a row.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void routed_decode_kernel(RoutedParams p) {
   typedef RoutedCfg<T, D> C;
   constexpr int NP = C::NP;
   constexpr bool SWZ = C::SWZ;
+  constexpr int NI2 = 2 * (D / 8);   // direct-to-LDS loads per chunk (bf16)
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16_t* buf = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* bufs = reinterpret_cast<bf16_t*>(smem);
+  const int G = p.Hq / p.Hkv;
+  float* zs = reinterpret_cast<float*>(smem + (size_t)(SWZ ? 2 : 1) * C::BUFE * sizeof(bf16_t));   // [2][G][K]
   const int lane = threadIdx.x, g16 = lane >> 4;
   const int bg = blockIdx.y, b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const int G = p.Hq / p.Hkv;
   const int tb0 = 2 * blockIdx.x;
-  const int e = blockIdx.z;
   const long long L = (long long)p.N * kSlots;
   const long long Tcont = (long long)p.N * kContent;
 
@@ -1396,17 +1393,31 @@ __global__ __launch_bounds__(64) void routed_decode_kernel(RoutedParams p) {
   const long long i_first = (long long)p.q0 + tb0, i_last = (long long)p.q0 + t_last;
   const int cw0 = (int)(max(0LL, i_first - p.R) / kContent);
   const int cw1 = (int)(min(Tcont - 1, i_last + p.R) / kContent);
-  int c;
-  if (e < p.K) {
-    c = __builtin_amdgcn_readlane(s0, e);
-    if (c >= cw0 && c <= cw1) c = -1;
-  } else if (e < 2 * p.K) {
-    c = __builtin_amdgcn_readlane(s1, e - p.K);
-    if (c >= 0 && ((c >= cw0 && c <= cw1) || __ballot(s0 == c) != 0ull)) c = -1;
-  } else {
-    c = cw0 + (e - 2 * p.K);
-    if (c > cw1) c = -1;
-  }
+  const int e_end = min(p.nent, (int)blockIdx.z * p.epb + p.epb);
+  // chunk of entry e, or -1 (wave-uniform)
+  auto chunk_of = [&](int e) -> int {
+    int c;
+    if (e < p.K) {
+      c = __builtin_amdgcn_readlane(s0, e);
+      if (c >= cw0 && c <= cw1) c = -1;
+    } else if (e < 2 * p.K) {
+      c = __builtin_amdgcn_readlane(s1, e - p.K);
+      if (c >= 0 && ((c >= cw0 && c <= cw1) || __ballot(s0 == c) != 0ull)) c = -1;
+    } else {
+      c = cw0 + (e - 2 * p.K);
+      if (c > cw1) c = -1;
+    }
+    return c;
+  };
+  // first entry at or after e that has a chunk (e_end if none); its chunk in c
+  auto next_entry = [&](int e, int& c) -> int {
+    c = -1;
+    for (; e < e_end; ++e) {
+      c = chunk_of(e);
+      if (c >= 0) return e;
+    }
+    return e_end;
+  };
 
   // this lane's row: query qq of the tile, head hh of the group
   const int qq = (lane & 15) >> 3, hh = lane & 7;
@@ -1415,7 +1426,9 @@ __global__ __launch_bounds__(64) void routed_decode_kernel(RoutedParams p) {
   const bool rv = t < p.nq && hh < G;
   const long long iq = (long long)p.q0 + t;
   const size_t rows = (size_t)p.B * p.Hq * p.nq;
-  float* pp = p.part + ((size_t)e * rows + ((size_t)b * p.Hq + h) * p.nq + t) * (D + 4);
+  float* pp = p.part + ((size_t)blockIdx.z * rows + ((size_t)b * p.Hq + h) * p.nq + t) * (D + 4);
+  int c;
+  int e = next_entry((int)blockIdx.z * p.epb, c);
   if (c < 0) {
     if (rv && g16 == 0) {
       pp[D] = kNegBig;
@@ -1423,60 +1436,115 @@ __global__ __launch_bounds__(64) void routed_decode_kernel(RoutedParams p) {
     }
     return;
   }
-  const long long cf = (long long)c * kContent, cl = cf + kContent - 1;
-  const bool win = cf <= iq + p.R && cl >= iq - p.R;
-  const unsigned long long m0 = __ballot(s0 == c), m1 = __ballot(s1 == c);
-  const unsigned long long mq = qq ? m1 : m0;
-  const int ksel = mq != 0ull ? __builtin_ctzll(mq) : -1;
-  int mode = win ? 1 : (ksel >= 0 ? 2 : 0);
-  if (!rv) mode = 0;
-  int lo = 0, hi = kContent - 1;
-  if (mode == 1) {
-    lo = (int)max(0LL, iq - p.R - cf);
-    hi = (int)min((long long)kContent - 1, iq + p.R - cf);
-  }
-  float zc = 0.f;
-  if (p.K > 0) {   // uniform; zsel may be NULL when K = 0
-    const float zraw =
-        p.zsel[(((size_t)b * p.Hq + (rv ? h : g * G)) * p.nq + (rv ? t : tb0)) * p.K + (ksel >= 0 ? ksel : 0)];
-    zc = mode == 2 ? zraw * kLog2e : 0.f;
-  }
+  auto kv_of = [&](int cc, const T*& kc, const T*& vc) {
+    kc = reinterpret_cast<const T*>(p.k) + ((size_t)bg * L + (size_t)cc * kSlots) * D;
+    vc = reinterpret_cast<const T*>(p.v) + ((size_t)bg * L + (size_t)cc * kSlots) * D;
+  };
+  const T* kc;
+  const T* vc;
+  kv_of(c, kc, vc);
+  if constexpr (SWZ) dma_chunk<D, 1>(reinterpret_cast<const bf16_t*>(kc), reinterpret_cast<const bf16_t*>(vc), bufs, 0, lane);
 
-  const T* kg = reinterpret_cast<const T*>(p.k) + ((size_t)bg * L + (size_t)c * kSlots) * D;
-  const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)bg * L + (size_t)c * kSlots) * D;
+  // the two queries' chunk logits into LDS and the query fragments, all awaited
+  // before the next chunk load is issued (the compiler does not count those loads)
+  if (p.K > 0) {   // uniform; zsel may be NULL when K = 0
+    constexpr int kZPer = 16;   // 2 queries x G <= 8 heads x K <= 64 values over 64 lanes
+    const int nz = 2 * G * p.K;
+    float zv[kZPer];
+#pragma unroll
+    for (int j = 0; j < kZPer; ++j) {
+      if (64 * j < nz) {   // uniform
+        const int x = lane + 64 * j < nz ? lane + 64 * j : nz - 1;
+        const int xq = x / (G * p.K), rem = x - xq * G * p.K, xh = rem / p.K, xk = rem - xh * p.K;
+        const int tt = tb0 + xq < p.nq ? tb0 + xq : tb0;
+        zv[j] = p.zsel[(((size_t)b * p.Hq + g * G + xh) * p.nq + tt) * p.K + xk];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kZPer; ++j)
+      if (lane + 64 * j < nz) zs[lane + 64 * j] = zv[j] * kLog2e;
+  }
   QFrag<D, NP> qf;
   const T* qrow = rv ? reinterpret_cast<const T*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D : nullptr;
-  if constexpr (SWZ) {
-    dma_chunk<D, 1>(reinterpret_cast<const bf16_t*>(kg), reinterpret_cast<const bf16_t*>(vg), buf, 0, lane);
-    load_qfrag<T, D, NP>(qf, qrow, lane);
-    wait_vm<0>();
-    compiler_fence();
-  } else {
-    KVStage<T, D, 64> stg;
-    stg.load(kg, vg, lane, 64);
-    load_qfrag<T, D, NP>(qf, qrow, lane);
-    stg.store(buf, lane);
-    __syncthreads();
-  }
+  load_qfrag<T, D, NP>(qf, qrow, lane);
+  wait_vm<0>();
+  wait_lgkm0();
+  compiler_fence();
+
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dm = 0; dm < D / 16; ++dm) acc[dm] = zero4();
   float m = kNegBig, l = 0.f;
-  f32x4 sacc[4];
-  s_tile<D, NP, SWZ>(buf, qf, sacc, lane);
-  if constexpr (NP == 1) {
-    const bool general = __ballot(mode == 1) != 0ull;
-    s16x8 pf[2];
-    tile_update_bf16(sacc, general, mode, lo, hi, zc, p.sl2, g16, m, l, pf);
-    pv_tile_packed<D>(buf, pf, acc, lane);
-  } else {
-    float x[4][4];
+  int cur = 0;
+  for (;;) {
+    int cn;
+    const int en = next_entry(e + 1, cn);
+    bf16_t* buf = bufs + cur * C::BUFE;
+    if constexpr (SWZ) {
+      if (cn >= 0) {
+        kv_of(cn, kc, vc);
+        dma_chunk<D, 1>(reinterpret_cast<const bf16_t*>(kc), reinterpret_cast<const bf16_t*>(vc),
+                        bufs + (cur ^ 1) * C::BUFE, 0, lane);
+        wait_vm<NI2>();   // chunk c has landed; chunk cn stays in flight
+      } else {
+        wait_vm<0>();
+      }
+      compiler_fence();
+    } else {
+      KVStage<T, D, 64> stg;
+      stg.load(kc, vc, lane, 64);
+      __syncthreads();   // the previous chunk's reads are done
+      stg.store(buf, lane);
+      __syncthreads();
+      if (cn >= 0) kv_of(cn, kc, vc);
+    }
+    // per lane: window keys, selected-chunk keys or nothing
+    const long long cf = (long long)c * kContent, cl = cf + kContent - 1;
+    const bool win = cf <= iq + p.R && cl >= iq - p.R;
+    const unsigned long long m0 = __ballot(s0 == c), m1 = __ballot(s1 == c);   // full-wave ballots
+    const unsigned long long mq = qq ? m1 : m0;
+    const int ksel = mq != 0ull ? __builtin_ctzll(mq) : -1;
+    int mode = win ? 1 : (ksel >= 0 ? 2 : 0);
+    if (!rv) mode = 0;
+    int lo = 0, hi = kContent - 1;
+    if (mode == 1) {
+      lo = (int)max(0LL, iq - p.R - cf);
+      hi = (int)min((long long)kContent - 1, iq + p.R - cf);
+    }
+    const float zc = mode == 2 ? zs[(qq * G + hh) * p.K + ksel] : 0.f;
+    f32x4 sacc[4];
+    s_tile<D, NP, SWZ>(buf, qf, sacc, lane);
+    float alpha;
+    if constexpr (NP == 1) {
+      const bool general = __ballot(mode == 1) != 0ull;
+      s16x8 pf[2];
+      alpha = tile_update_bf16(sacc, general, mode, lo, hi, zc, p.sl2, g16, m, l, pf);
+      if (__ballot(alpha != 1.f) != 0ull) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int dm = 0; dm < D / 16; ++dm)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
-    tile_update(x, mode, lo, hi, zc, p.sl2, g16, m, l);
-    pv_tile<D, NP, SWZ>(buf, x, acc, lane);
+          for (int i = 0; i < 4; ++i) acc[dm][i] *= alpha;
+      }
+      pv_tile_packed<D>(buf, pf, acc, lane);
+    } else {
+      float x[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
+      alpha = tile_update(x, mode, lo, hi, zc, p.sl2, g16, m, l);
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[dm][i] *= alpha;
+      pv_tile<D, NP, SWZ>(buf, x, acc, lane);
+    }
+    if (cn < 0) break;
+    wait_lgkm0();   // every LDS read of this buffer has returned before it is loaded again
+    compiler_fence();
+    e = en;
+    c = cn;
+    if constexpr (SWZ) cur ^= 1;
   }
   if (!rv) return;
   if (l > 0.f) {
@@ -1646,6 +1714,8 @@ static size_t prefill_lds(const RouteDims& dm, int K, int nbuf) {
 
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   AttnPlan pl;
+  pl.nent = 0;
+  pl.epb = 0;
   // Prefill-sized problems: 8 waves x 2 tiles = 32 queries per block, no split;
   // 8 waves x 1 tile when the selections of 32 queries do not fit in LDS.
   pl.waves = 8;
@@ -1674,8 +1744,16 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
     pl.tiles = 1;
     pl.qblock = 2;
     if (nent <= kMaxPartials) {
+      // runs of epb entries per block: enough blocks to fill the chip (about two
+      // single-wave blocks per CU), at least two chunks per block
       pl.kind = 1;
-      pl.nsplit = (int)nent;
+      const long long tiles = (long long)((nq + 1) / 2) * dm.B * dm.Hkv;
+      long long runs = (512 + tiles - 1) / (tiles > 0 ? tiles : 1);
+      if (runs > nent / 2) runs = nent / 2;
+      if (runs < 1) runs = 1;
+      pl.epb = (int)((nent + runs - 1) / runs);
+      pl.nsplit = (int)((nent + pl.epb - 1) / pl.epb);
+      pl.nent = (int)nent;
     } else {
       // Wide window: the tile's chunk list is split across blocks instead.
       const long long blocks = (long long)((nq + 1) / 2) * dm.B * dm.Hkv;
@@ -1684,7 +1762,7 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
     }
   }
   if (pl.kind == 1) {
-    pl.lds = routed_buf_bytes(dm.d, dm.dtype);
+    pl.lds = (size_t)(dm.dtype == 1 ? 2 : 1) * routed_buf_bytes(dm.d, dm.dtype) + (size_t)2 * (dm.Hq / dm.Hkv) * K * 4;
   } else {
     pl.lds = routed_lds(dm, K, pl.qblock, pl.waves);
   }
@@ -1704,7 +1782,8 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
       }
     }
   }
-  pl.ws = pl.nsplit > 1 ? align256a((size_t)pl.nsplit * dm.B * dm.Hq * nq * (dm.d + 4) * 4) : 0;
+  // kind 1 always writes its partials (one per run, merged by combine_kernel), even for a single run
+  pl.ws = (pl.nsplit > 1 || pl.kind == 1) ? align256a((size_t)pl.nsplit * dm.B * dm.Hq * nq * (dm.d + 4) * 4) : 0;
   return pl;
 }
 
@@ -1754,8 +1833,8 @@ static hipError_t launch_prefill_t(const RouteDims& dm, const AttnPlan& pl, cons
   auto kern = routed_prefill_kernel<D, NBUF>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
   if (e != hipSuccess) return e;
-  dim3 grid((prm.nq + kPfQB - 1) / kPfQB, dm.B * dm.Hkv);
-  hipLaunchKernelGGL(kern, grid, dim3(64 * kPfWaves), pl.lds, st, prm);
+  const int tiles = (prm.nq + kPfQB - 1) / kPfQB * dm.B * dm.Hkv;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * kPfWaves), pl.lds, st, prm);
   return hipGetLastError();
 }
 
@@ -1787,6 +1866,8 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, cons
   prm.q0 = q0;
   prm.nq = nq;
   prm.nsplit = pl.nsplit;
+  prm.nent = pl.nent;
+  prm.epb = pl.epb;
   prm.sl2 = scale * kLog2e;
   if (pl.kind == 2) return dm.d == 64 ? launch_prefill_d<64>(dm, pl, prm, st) : launch_prefill_d<128>(dm, pl, prm, st);
   if (pl.kind == 1) {

@@ -30,6 +30,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
 
+// Workgroups are handed to the 8 XCDs of the chip round-robin by linear block
+// id, and each XCD has its own L2. xcd_tile maps a 1-D grid of xcd_grid(total)
+// blocks onto `total` tiles so that XCD x runs the contiguous tile range
+// [x * per, (x + 1) * per) in order: tiles enumerated batch-head-major then keep
+// one head's K and V in the L2 of one or two XCDs instead of all eight.
+constexpr int kXcds = 8;
+__host__ __device__ __forceinline__ int xcd_per(int total) { return (total + kXcds - 1) / kXcds; }
+__host__ __device__ __forceinline__ int xcd_grid(int total) { return xcd_per(total) * kXcds; }
+__device__ __forceinline__ int xcd_tile(int total) {   // tile of this block, or -1 (nothing to do)
+  const int bid = blockIdx.x;
+  const int l = (bid % kXcds) * xcd_per(total) + bid / kXcds;
+  return l < total ? l : -1;
+}
+
 // ---------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
@@ -172,6 +186,18 @@ __device__ __forceinline__ float col_max(float v) { return xor32_max(xor16_max(v
 __device__ __forceinline__ float col_sum(float v) { return xor32_sum(xor16_sum(v)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- wait counters
+
+// s_waitcnt lgkmcnt(0): every LDS (and scalar memory) operation of this wave has completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); }
+
+// s_waitcnt that waits for vector-memory operations only: at most n outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Order-preserving map float -> uint32 (larger float -> larger key); 0 is
 // reserved for "not a candidate" and never produced by a finite float.

@@ -25,6 +25,7 @@ struct ScoreWs {
   float* z;     // [B,Hq,nq,N]  per-head scores
   float* upart; // [splits,B,nq,rank padded to 32/64/128]  partial x A
   bf16_t* splanes; // [B,Hq,N,2d] summaries as bf16 hi then lo, k-permuted (fused path)
+  bf16_t* qplanes; // [B,Hq,32,2d] q~ as bf16 hi then lo (decode-sized path)
 };
 size_t score_ws_bytes(const RouteDims& dm, int D, int r, int nq);
 ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int D, int r, int nq);
@@ -42,6 +43,8 @@ struct AttnPlan {
   int kind;        // 0: blocks walk a chunk list; 1: one block per (2-query tile, chunk entry);
                    // 2: producer / consumer waves over a chunk ring (bf16 prefill)
   int nbuf;        // ring slots of kind 2
+  int nent;        // kind 1: entries per 2-query tile (2K selected + window chunks)
+  int epb;         // kind 1: entries per block (nsplit = ceil(nent / epb) runs)
   size_t lds;      // dynamic LDS bytes per block
   size_t ws;       // workspace bytes for the split partials
 };

@@ -997,6 +997,482 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------- 5. decode-sized scoring (bf16)
+//
+// A decode step routes at most 32 queries: the residual weights and the
+// summaries are the only large operands, so these kernels put every CU's loads
+// in flight at once instead of walking them from a few blocks.
+//  5a. u_small_kernel: partial u = x A over 256 rows of A per block. The block's
+//      rows of A go to LDS in one pass, each wave multiplies a quarter of the
+//      k-steps for all queries, and the four wave partials are summed in LDS.
+//  5b. qtilde_dec_kernel: one block per head sums the block partials and forms
+//      q~ = q + u B_h (u split into bf16 hi + lo, B exact), stored as bf16 hi
+//      and lo planes: the B operand of the scoring product.
+//  5c. score_small_kernel: one block per (batch, group, 32 chunks). The
+//      summaries of every head of the group are moved into LDS with
+//      direct-to-LDS loads in one burst (16-byte pieces XOR-swizzled by row so
+//      that the fragment reads are conflict free); wave w scores heads w,
+//      w + 4 for all 32 chunks x 32 queries with the split products of
+//      score_kernel, and the group maximum is taken through LDS.
+//  5d. topk_small_kernel: one block per (batch, group, query). Each wave finds
+//      the top K of its own range of chunks; every member of the overall top K
+//      is in the top K of its range, so one wave then selects the final K from
+//      the at most 4K survivors with the same bisection and tie rule.
+constexpr int kDecQ = 32;          // queries of the decode-sized path
+constexpr int kUSmallRows = 256;   // rows of A per u_small_kernel block
+
+template <int RP>
+__global__ __launch_bounds__(256) void u_small_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ A,
+                                                      int Dh, int r, float* __restrict__ upart, int N, int q0,
+                                                      int nq) {
+  constexpr int AS = RP + 16;                        // LDS row stride of A (elements)
+  constexpr int US = RP + 4;                         // LDS row stride of the wave partials (floats)
+  constexpr int kPer = kUSmallRows * RP / 8 / 256;   // 16-byte pieces of A per thread
+  constexpr int KSW = kUSmallRows / 32 / 4;          // 32-wide k-steps per wave
+  constexpr int kABytes = kUSmallRows * AS * 2, kRBytes = 4 * kDecQ * US * 4;
+  __shared__ __align__(16) unsigned char smem[kABytes > kRBytes ? kABytes : kRBytes];
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  bf16_t* a_s = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const int split = blockIdx.x, b = blockIdx.y;
+  const long long L = (long long)N * kSlots;
+  const int k0 = split * kUSmallRows;
+  const bool vec = (r == RP) && (Dh % 8 == 0);
+
+  // the block's rows of A (zero past Dh and past r) and this wave's x fragments;
+  // every load is issued before any is used
+  u32x4 av[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = 8 * (tid + 256 * j);
+    const int kk = e / RP, n = e % RP, k = k0 + kk;
+    if (vec) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(A + (size_t)(k < Dh ? k : Dh - 1) * r + n);
+      av[j] = k < Dh ? v : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      s16x8 t;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) t[jj] = (k < Dh && n + jj < r) ? (short)A[(size_t)k * r + n + jj] : (short)0;
+      av[j] = __builtin_bit_cast(u32x4, t);
+    }
+  }
+  s16x8 xf[KSW][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int t = 16 * mt + L16;
+    const bf16_t* row = x + ((size_t)b * L + slot_of((long long)q0 + (t < nq ? t : 0))) * Dh;
+#pragma unroll
+    for (int kk = 0; kk < KSW; ++kk) {
+      const int kg = k0 + 32 * (w + 4 * kk) + 8 * g16;
+      if (vec) {
+        const s16x8 v = load8(row + (kg < Dh ? kg : 0));
+        xf[kk][mt] = (t < nq && kg < Dh) ? v : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      } else {
+        float xv[8];
+        load_row8<bf16_t>(row, kg, Dh, xv);
+        xf[kk][mt] = t < nq ? pack8(xv) : s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = 8 * (tid + 256 * j);
+    *reinterpret_cast<u32x4*>(a_s + (e / RP) * AS + (e % RP)) = av[j];
+  }
+  __syncthreads();
+  f32x4 acc[2][RP / 16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < RP / 16; ++nt) acc[mt][nt] = zero4();
+#pragma unroll
+  for (int kk = 0; kk < KSW; ++kk) {
+    const int kl = 32 * (w + 4 * kk) + 8 * g16;   // row of A within the block
+#pragma unroll
+    for (int nt = 0; nt < RP / 16; ++nt) {
+      const s16x8 bf = lds_col_frag(a_s, AS, kl, kl + 4, 16 * nt, lane);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16(xf[kk][mt], bf, acc[mt][nt]);
+    }
+  }
+  __syncthreads();   // every wave is done reading A
+  float* red = reinterpret_cast<float*>(smem);
+  // D layout: lane holds u[query 16 mt + 4 g16 + i][rank 16 nt + L16]
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < RP / 16; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(w * kDecQ + 16 * mt + 4 * g16 + i) * US + 16 * nt + L16] = acc[mt][nt][i];
+  __syncthreads();
+  float* up = upart + ((size_t)split * gridDim.y + b) * (size_t)nq * RP;
+  for (int e = tid; e < nq * RP; e += 256) {
+    const int t = e / RP, n = e - t * RP;
+    up[e] = ((red[t * US + n] + red[(kDecQ + t) * US + n]) + red[(2 * kDecQ + t) * US + n]) +
+            red[(3 * kDecQ + t) * US + n];
+  }
+}
+
+template <int D, int RP>
+__global__ __launch_bounds__(256) void qtilde_dec_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bm,
+                                                         int r, const float* __restrict__ upart, int nsplit,
+                                                         bf16_t* __restrict__ qp, int Hq, int N, int q0, int nq) {
+  constexpr int BS = D + 16, US = RP + 4;
+  constexpr int NTW = D / 32;                       // 16-column tiles per wave (two waves per query tile)
+  constexpr int kBPer = RP * D / 8 / 256;           // 16-byte pieces of B_h per thread
+  constexpr int kUPer = kDecQ * RP / 4 / 256;       // float4 groups of u per thread
+  static_assert(kBPer >= 1 && kUPer >= 1, "tile sizes");
+  __shared__ __align__(16) bf16_t b_s[RP * BS];
+  __shared__ __align__(16) float u_s[kDecQ * US];
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const int h = blockIdx.x, b = blockIdx.y, B = gridDim.y;
+  const long long L = (long long)N * kSlots;
+  const int mt = w & 1, nh = w >> 1;
+
+  // loads first: B_h slice, q values of this lane's outputs, the u partials
+  u32x4 bv[kBPer];
+#pragma unroll
+  for (int j = 0; j < kBPer; ++j) {
+    const int e = tid + 256 * j, kk = (8 * e) / D, n = (8 * e) % D;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(Bm + (size_t)(kk < r ? kk : 0) * Hq * D + (size_t)h * D + n);
+    bv[j] = kk < r ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+  float qv[NTW][4];
+#pragma unroll
+  for (int nn = 0; nn < NTW; ++nn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * mt + 4 * g16 + i, dd = 16 * (nh * NTW + nn) + L16;
+      const long long sl = slot_of((long long)q0 + (t < nq ? t : 0));
+      qv[nn][i] = bf2f(q[((size_t)b * Hq + h) * L * D + (size_t)sl * D + dd]);
+    }
+  f32x4 us[kUPer];
+#pragma unroll
+  for (int j = 0; j < kUPer; ++j) us[j] = zero4();
+  constexpr int kSB = 16;   // partials loaded per round (all of them for a hidden size up to 4096)
+  for (int sp0 = 0; sp0 < nsplit; sp0 += kSB) {
+    f32x4 v[kSB][kUPer];
+#pragma unroll
+    for (int qq = 0; qq < kSB; ++qq) {
+      const int sp = sp0 + qq < nsplit ? sp0 + qq : nsplit - 1;
+#pragma unroll
+      for (int j = 0; j < kUPer; ++j) {
+        const int e = 4 * (tid + 256 * j), t = e / RP, n = e % RP;
+        v[qq][j] = *reinterpret_cast<const f32x4*>(upart + (((size_t)sp * B + b) * nq + (t < nq ? t : 0)) * RP + n);
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < kSB; ++qq)
+#pragma unroll
+      for (int j = 0; j < kUPer; ++j) {
+        const int t = 4 * (tid + 256 * j) / RP;
+        if (sp0 + qq < nsplit && t < nq) us[j] += v[qq][j];
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < kBPer; ++j) {
+    const int e = tid + 256 * j;
+    *reinterpret_cast<u32x4*>(b_s + ((8 * e) / D) * BS + (8 * e) % D) = bv[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kUPer; ++j) {
+    const int e = 4 * (tid + 256 * j);
+    *reinterpret_cast<f32x4*>(u_s + (e / RP) * US + e % RP) = us[j];
+  }
+  __syncthreads();
+
+  // q~ tile: wave w takes query rows 16 (w & 1) .. + 15 and half of the head dimension
+  s16x8 uh[RP / 32], ul[RP / 32];
+#pragma unroll
+  for (int ks = 0; ks < RP / 32; ++ks) {
+    float uv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) uv[j] = u_s[(16 * mt + L16) * US + 32 * ks + 8 * g16 + j];
+    pack8_split(uv, uh[ks], ul[ks]);
+  }
+#pragma unroll
+  for (int nn = 0; nn < NTW; ++nn) {
+    const int nt = nh * NTW + nn;
+    f32x4 c = zero4();
+#pragma unroll
+    for (int ks = 0; ks < RP / 32; ++ks) {
+      const s16x8 bh = lds_col_frag(b_s, BS, 32 * ks + 8 * g16, 32 * ks + 8 * g16 + 4, 16 * nt, lane);
+      c = mfma16(ul[ks], bh, c);
+      c = mfma16(uh[ks], bh, c);
+    }
+    const int dd = 16 * nt + L16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * mt + 4 * g16 + i;
+      bf16_t hi, lo;
+      split_bf16(t < nq ? qv[nn][i] + c[i] : 0.f, hi, lo);
+      bf16_t* dst = qp + (((size_t)b * Hq + h) * kDecQ + t) * 2 * D;
+      dst[dd] = hi;
+      dst[D + dd] = lo;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void score_small_kernel(const bf16_t* __restrict__ qp, const float* __restrict__ s,
+                                                          const float* __restrict__ H, float beta, float scale,
+                                                          float* __restrict__ z, float* __restrict__ zhat, int Hq,
+                                                          int Hkv, int N, int nq) {
+  extern __shared__ __align__(16) unsigned char smem[];   // summaries [G][32][D] f32, then wave maxima [4][16][64]
+  constexpr int PR = D / 4;          // 16-byte pieces per summary row
+  constexpr int RPI = 64 / PR;       // rows per 1 KB direct-to-LDS load
+  constexpr int IPH = 32 / RPI;      // loads per head
+  constexpr int KS = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, g16 = lane >> 4, L16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = blockIdx.x * 32, bg = blockIdx.y, b = bg / Hkv, g = bg - b * Hkv;
+  const int G = Hq / Hkv;
+  float* s_l = reinterpret_cast<float*>(smem);
+  float* zm = s_l + (size_t)G * 32 * D;
+
+  // 1. rows c0 .. c0 + 31 (clamped to N - 1) of every head's summaries into LDS:
+  //    LDS piece p of row `row` holds source piece p ^ (row & 15)
+  {
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)smem);
+    const int prow = lane / PR, pp = lane - prow * PR;
+    for (int ins = w; ins < G * IPH; ins += 4) {
+      const int hh = ins / IPH, r0 = (ins - hh * IPH) * RPI;
+      const int row = r0 + prow;
+      const int c = min(c0 + row, N - 1);
+      const float* sh = s + ((size_t)b * Hq + g * G + hh) * N * D;
+      const int voff = (c * D + ((pp ^ (row & 15)) << 2)) * 4;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
+                       lds0 + (uint32_t)((hh * 32 + r0) * D * 4)),
+                   "v"(voff), "s"(sh)
+                   : "memory", "m0");
+    }
+  }
+  // 2. meanwhile: this wave's heads (w, w + 4) as B operands, and their entropies
+  const int nhw = G > w ? (G - w + 3) / 4 : 0;   // 0, 1 or 2 heads
+  s16x8 qb[2][2][KS][2];                          // [head slot][query tile][k-step][plane]
+  float hv[2][2][4];                              // [head slot][chunk tile][i]
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    const int hh = min(w + 4 * hs, G - 1), h = g * G + hh;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const bf16_t* row = qp + (((size_t)b * Hq + h) * kDecQ + 16 * nt + L16) * 2 * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) qb[hs][nt][ks][pl] = load8(row + pl * D + 32 * ks + 8 * g16);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + 16 * mt + 4 * g16 + i;
+        hv[hs][mt][i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
+      }
+  }
+  wait_vm<0>();
+  __syncthreads();
+
+  // 3. scores of this wave's heads; the wave's maximum over them
+  float zmx[2][2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zmx[mt][nt][i] = -INFINITY;
+  const bool vec_out = (N & 3) == 0;
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    if (hs >= nhw) break;
+    const int hh = w + 4 * hs, h = g * G + hh;
+    f32x4 ahi[2][2], ax[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        ahi[mt][nt] = zero4();
+        ax[mt][nt] = zero4();
+      }
+      const int row = 16 * mt + L16;
+      const float* rp = s_l + ((size_t)hh * 32 + row) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int pc = 8 * ks + 2 * g16;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(rp + ((pc ^ (row & 15)) << 2));
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(rp + (((pc + 1) ^ (row & 15)) << 2));
+        const float av[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        s16x8 a[2];
+        split_ns<2>(av, a);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          ax[mt][nt] = mfma16(a[0], qb[hs][nt][ks][1], ax[mt][nt]);
+          ax[mt][nt] = mfma16(a[1], qb[hs][nt][ks][0], ax[mt][nt]);
+          ahi[mt][nt] = mfma16(a[0], qb[hs][nt][ks][0], ahi[mt][nt]);
+        }
+      }
+    }
+    // D layout: lane holds chunk c0 + 16 mt + 4 g16 + i (rows), query 16 nt + L16 (column)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int t = 16 * nt + L16, cb = c0 + 16 * mt + 4 * g16;
+        float zz[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          zz[i] = (ahi[mt][nt][i] + ax[mt][nt][i]) * scale - beta * hv[hs][mt][i];
+          zmx[mt][nt][i] = fmaxf(zmx[mt][nt][i], zz[i]);
+        }
+        if (t < nq) {
+          float* zr = z + (((size_t)b * Hq + h) * nq + t) * N + cb;
+          if (vec_out && cb + 3 < N) {
+            *reinterpret_cast<f32x4*>(zr) = f32x4{zz[0], zz[1], zz[2], zz[3]};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (cb + i < N) zr[i] = zz[i];
+          }
+        }
+      }
+  }
+  // 4. group maximum over the four waves; wave w writes (chunk tile w >> 1, query tile w & 1)
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zm[(w * 16 + (2 * mt + nt) * 4 + i) * 64 + lane] = zmx[mt][nt][i];
+  __syncthreads();
+  {
+    const int mt = w >> 1, nt = w & 1;
+    const int t = 16 * nt + L16, cb = c0 + 16 * mt + 4 * g16;
+    if (t < nq) {
+      float m4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) m = fmaxf(m, zm[(ww * 16 + (2 * mt + nt) * 4 + i) * 64 + lane]);
+        m4[i] = m;
+      }
+      float* zr = zhat + ((size_t)bg * nq + t) * N + cb;
+      if (vec_out && cb + 3 < N) {
+        *reinterpret_cast<f32x4*>(zr) = f32x4{m4[0], m4[1], m4[2], m4[3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (cb + i < N) zr[i] = m4[i];
+      }
+    }
+  }
+}
+
+// Top K of a wave's keys: lane l holds key[j] for element 64 j + l (elements in
+// their order); keys are order_key values, 0 = not a candidate. The K largest
+// keys are chosen, ties going to the smaller element; emit(slot, j) is called
+// by the owning lane for every chosen element, slots 0 .. count - 1 in element
+// order. Returns count = min(K, number of candidates) (wave-uniform).
+template <int P, typename Emit>
+__device__ __forceinline__ int wave_topk(const uint32_t* key, int K, int lane, Emit emit) {
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int ncand = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) ncand += __popcll(__ballot(key[j] != 0u));
+  const bool take_all = ncand <= K;
+  uint32_t theta = 0u;
+  int need = 0;
+  if (!take_all) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t trial = theta | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[j] >= trial));
+      if (cnt >= K) theta = trial;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) gt += __popcll(__ballot(key[j] > theta));
+    need = K - gt;
+  }
+  int base = 0, ties = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const bool nz = key[j] != 0u;
+    const bool gt = take_all ? nz : key[j] > theta;
+    const bool eq = !take_all && nz && key[j] == theta;
+    const unsigned long long em = __ballot(eq);
+    const bool take = gt || (eq && ties + __popcll(em & lt) < need);
+    const unsigned long long tm = __ballot(take);
+    if (take) emit(base + __popcll(tm & lt), j);
+    base += __popcll(tm);
+    ties += __popcll(em);
+  }
+  return base;
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict__ zhat, const float* __restrict__ z,
+                                                         int32_t* __restrict__ idx, float* __restrict__ zsel, int Hq,
+                                                         int Hkv, int N, int nq, int q0, int K, int R) {
+  __shared__ uint32_t ckey[4 * 64];   // per wave: its top K keys, in chunk order
+  __shared__ int cidx[4 * 64];        // ... and their chunks
+  __shared__ int ccount[4];
+  __shared__ int chosen[64];
+  __shared__ int s_count;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long long row = blockIdx.x;
+  const int t = (int)(row % nq);
+  const long long bg = row / nq;
+  const int b = (int)(bg / Hkv), g = (int)(bg % Hkv);
+  const int G = Hq / Hkv;
+  const long long i = (long long)q0 + t;
+  const float* zr = zhat + row * N;
+
+  // 1. wave w: chunks 64 P w + 64 j + lane
+  const int cw = 64 * P * w;
+  float zv[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int c = cw + 64 * j + lane;
+    zv[j] = zr[c < N ? c : N - 1];   // always in bounds
+  }
+#pragma unroll
+  for (int j = 0; j < P; ++j) asm volatile("" : "+v"(zv[j]));   // keep every load ahead of its first use
+  uint32_t key[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int c = cw + 64 * j + lane;
+    const bool cand = (c < N) & ((63LL * c + 62 < i - R) | (63LL * c > i + R));
+    key[j] = cand ? order_key(zv[j]) : 0u;
+  }
+  const int nw = wave_topk<P>(key, K, lane, [&](int slot, int j) {
+    ckey[64 * w + slot] = key[j];
+    cidx[64 * w + slot] = cw + 64 * j + lane;
+  });
+  if (lane == 0) ccount[w] = nw;
+  __syncthreads();
+  // 2. wave 0: the final K from the survivors (element 64 e + l = entry l of wave e's list: chunk order)
+  if (w == 0) {
+    uint32_t k2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k2[e] = lane < ccount[e] ? ckey[64 * e + lane] : 0u;
+    const int n = wave_topk<4>(k2, K, lane, [&](int slot, int e) { chosen[slot] = cidx[64 * e + lane]; });
+    if (lane == 0) s_count = n;
+  }
+  __syncthreads();
+  if (lane < K) {
+    const int c = lane < s_count ? chosen[lane] : -1;
+    if (w == 0) idx[row * K + lane] = c;
+    for (int hh = w; hh < G; hh += 4) {
+      const size_t hrow = ((size_t)b * Hq + g * G + hh) * nq + t;
+      zsel[hrow * K + lane] = c >= 0 ? z[hrow * N + c] : -INFINITY;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------- host side
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1020,8 +1496,18 @@ static bool fused_score_ok(const RouteDims& dm, int r, int nq) {
   return dm.dtype == 1 && dm.N <= 512 && r <= 64 && nq > kSmallQ && dm.Hq / dm.Hkv <= 8;
 }
 
+// bf16 decode-sized problems (at most 32 queries) take the kernels of section 5.
+static bool small_score_ok(const RouteDims& dm, int r, int nq) {
+  return dm.dtype == 1 && nq <= kDecQ && r <= 64 && dm.Hq / dm.Hkv <= 8 && dm.N <= 8192;
+}
+static int u_small_splits(int Dh) { return (Dh + kUSmallRows - 1) / kUSmallRows; }
+
 size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
+  if (small_score_ok(dm, r, nq))
+    return align256((size_t)u_small_splits(Dh) * dm.B * nq * rank_pad(r) * 4) +
+           align256((size_t)dm.B * dm.Hq * kDecQ * 2 * dm.d * 2) + align256(rows_g * dm.N * 4) +
+           align256(rows_h * dm.N * 4);
   const size_t upart = (size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4;
   if (fused_score_ok(dm, r, nq)) return align256(upart) + align256((size_t)dm.B * dm.Hq * dm.N * dm.d * 4);
   return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4) + align256(upart);
@@ -1031,8 +1517,19 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
   char* p = (char*)ws;
   ScoreWs out;
-  (void)Dh;
   out.splanes = nullptr;
+  out.qplanes = nullptr;
+  if (small_score_ok(dm, r, nq)) {
+    out.qt = nullptr;
+    out.upart = (float*)p;
+    p += align256((size_t)u_small_splits(Dh) * dm.B * nq * rank_pad(r) * 4);
+    out.qplanes = (bf16_t*)p;
+    p += align256((size_t)dm.B * dm.Hq * kDecQ * 2 * dm.d * 2);
+    out.zhat = (float*)p;
+    p += align256(rows_g * dm.N * 4);
+    out.z = (float*)p;
+    return out;
+  }
   if (fused_score_ok(dm, r, nq)) {
     out.qt = nullptr;
     out.zhat = nullptr;
@@ -1122,10 +1619,53 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
   return hipGetLastError();
 }
 
+template <int D, int RP>
+static hipError_t launch_small_score(const RouteDims& dm, const void* q, const void* x, const void* A,
+                                     const void* Bm, int Dh, int r, const float* s, const float* H, float beta,
+                                     float scale, int K, int radius, int q0, int nq, int32_t* idx, float* zsel,
+                                     const ScoreWs& ws, hipStream_t st) {
+  const int nsplit = u_small_splits(Dh);
+  hipLaunchKernelGGL((u_small_kernel<RP>), dim3(nsplit, dm.B), dim3(256), 0, st, (const bf16_t*)x,
+                     (const bf16_t*)A, Dh, r, ws.upart, dm.N, q0, nq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((qtilde_dec_kernel<D, RP>), dim3(dm.Hq, dm.B), dim3(256), 0, st, (const bf16_t*)q,
+                     (const bf16_t*)Bm, r, ws.upart, nsplit, ws.qplanes, dm.Hq, dm.N, q0, nq);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)(dm.Hq / dm.Hkv) * 32 * D * 4 + 4 * 16 * 64 * 4;
+  auto sk = score_small_kernel<D>;
+  e = hipFuncSetAttribute((const void*)sk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sk, dim3((dm.N + 31) / 32, dm.B * dm.Hkv), dim3(256), lds, st, ws.qplanes, s, H, beta, scale,
+                     ws.z, ws.zhat, dm.Hq, dm.Hkv, dm.N, nq);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned rows = (unsigned)(dm.B * dm.Hkv * nq);
+  const int P = (dm.N + 255) / 256;
+#define LCR_TK(PP)                                                                                           \
+  hipLaunchKernelGGL((topk_small_kernel<PP>), dim3(rows), dim3(256), 0, st, ws.zhat, ws.z, idx, zsel, dm.Hq, \
+                     dm.Hkv, dm.N, nq, q0, K, radius)
+  if (P <= 1) LCR_TK(1);
+  else if (P <= 2) LCR_TK(2);
+  else if (P <= 4) LCR_TK(4);
+  else if (P <= 8) LCR_TK(8);
+  else if (P <= 16) LCR_TK(16);
+  else LCR_TK(32);
+#undef LCR_TK
+  return hipGetLastError();
+}
+
 hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const void* x, const void* A,
                                    const void* Bm, int D, int r, const float* s, const float* H,
                                    float beta, float scale, int K, int radius, int q0, int nq,
                                    int32_t* idx, float* zsel, const ScoreWs& ws, hipStream_t st) {
+  if (small_score_ok(dm, r, nq)) {
+    if (dm.d == 64) return r <= 32 ? launch_small_score<64, 32>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st)
+                                   : launch_small_score<64, 64>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st);
+    return r <= 32 ? launch_small_score<128, 32>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st)
+                   : launch_small_score<128, 64>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st);
+  }
   if (fused_score_ok(dm, r, nq)) {
     if (dm.d == 64) return r <= 32 ? launch_fused_score<64, 32>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st)
                                    : launch_fused_score<64, 64>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st);

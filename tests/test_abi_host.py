@@ -134,13 +134,21 @@ def test_workspace_sizes(lib):
     assert lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dm, 0, 0, 32, 256, 256 * 63) == 0
     dec = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=2048), 0, 0, 32, 256, 32)
     assert dec > 0 and dec % 256 == 0
-    # one partial (d + 4 floats) per query row and entry: 2K selected + the window chunks of a 2-query tile
+    # one partial (d + 4 floats) per query row and run of entries: a 2-query tile has 2K selected
+    # + its window chunks as entries, cut into runs so that about 512 single-wave blocks fill the chip
     entries = 2 * 32 + (2 * 256 + 2) // 63 + 3
-    assert dec >= entries * 28 * 32 * (128 + 4) * 4
+    tiles = 16 * 4
+    runs = min(-(-512 // tiles), entries // 2)
+    epb = -(-entries // runs)
+    assert dec == al(-(-entries // epb) * 28 * 32 * (128 + 4) * 4)
     # a window over the whole sequence makes too many entries: the chunk list is split instead
     wide = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=2048), 0, 0, 32, 10 ** 6, 32)
-    assert 0 < wide < dec
+    assert wide == al(8 * 28 * 32 * (128 + 4) * 4)
     assert lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=2048), 0, 0, 32, -1, 32) == 0
+    # a decode-sized plan with a single run per tile still writes one partial per row
+    tiny = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, dims(N=24, Hq=4, Hkv=2, d=64, dtype=0), 0, 0, 0, 64,
+                                   24 * 63)
+    assert tiny == al(1 * 4 * 24 * 63 * (64 + 4) * 4)
     assert lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_TOPK, dims(dtype=9), 1, 1, 1, 1, 1) == 0
 
 
