@@ -805,7 +805,7 @@ constexpr int kPfCons = 7;                 // consumer waves
 constexpr int kPfWaves = kPfCons + 1;      // + the producer
 constexpr int kPfQB = 4 * kPfCons;         // queries per block
 
-__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
 
 // Softmax update of a bf16 tile (see tile_update_bf16); WINDOW selects at
 // compile time whether per-key window bounds are applied.
@@ -823,14 +823,13 @@ __device__ __forceinline__ float tile_softmax(f32x4 sacc[4], int mode, int lo, i
   } else {
     if (g16 == 3) sacc[3][3] = -INFINITY;   // chunk slot 63: the routing mask, never a key
   }
-  float mx = -INFINITY;
+  float mx = max3(sacc[0][0], sacc[0][1], max2(sacc[0][2], sacc[0][3]));
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-    mx = fmax_nc(mx, fmax_nc(fmax_nc(sacc[mt][0], sacc[mt][1]), fmax_nc(sacc[mt][2], sacc[mt][3])));
+  for (int mt = 1; mt < 4; ++mt) mx = max3(mx, max3(sacc[mt][0], sacc[mt][1], sacc[mt][2]), sacc[mt][3]);
   mx = col_max(mx);
   const float mb = mx * sl2;
   const float m_old = m;
-  const float m_cand = mode == 1 ? fmax_nc(m_old, mb) : (mode == 2 ? fmax_nc(m_old, zc) : m_old);
+  const float m_cand = mode == 1 ? max2(m_old, mb) : (mode == 2 ? max2(m_old, zc) : m_old);
   const float m_new = m_cand > m_old + 8.f ? m_cand : m_old;
   const float base = mode == 2 ? mb : (mode == 1 ? m_new : 0.f);
   float e[16];
@@ -973,6 +972,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   __shared__ int s_landed;           // halves landed: K of position j is half 2j, V half 2j + 1
   __shared__ int s_rem[NBUF];        // consumers still to finish the position held by a slot
   __shared__ int s_fail;
+  __shared__ int s_nlo[kPfQB];       // per query: selected chunks below the block's window range
+  __shared__ int s_nin[kPfQB];       // ... and inside it
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
   const int nqb = (p.nq + kPfQB - 1) / kPfQB;
@@ -992,19 +993,25 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
     s_fail = 0;
   }
   if (tid < NBUF) s_rem[tid] = 0;
+  if (tid < kPfQB) {
+    s_nlo[tid] = 0;
+    s_nin[tid] = 0;
+  }
   for (int c = tid; c < p.N; c += NT) pos_of[c] = 0;
   __syncthreads();
   const int t_last = min(tb0 + kPfQB, p.nq) - 1;
-  {
-    const long long i_first = (long long)p.q0 + tb0, i_last = (long long)p.q0 + t_last;
-    const int cw0 = (int)(max(0LL, i_first - p.R) / kContent);
-    const int cw1 = (int)(min(Tcont - 1, i_last + p.R) / kContent);
-    for (int c = cw0 + tid; c <= cw1; c += NT) pos_of[c] = 1;
-  }
+  // the block's window range: chunks in the window of any of its queries
+  const int cw0 = (int)(max(0LL, (long long)p.q0 + tb0 - p.R) / kContent);
+  const int cw1 = (int)(min(Tcont - 1, (long long)p.q0 + t_last + p.R) / kContent);
+  for (int c = cw0 + tid; c <= cw1; c += NT) pos_of[c] = 1;
   for (int e = tid; e < kPfQB * p.K; e += NT) {
     const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
     const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
-    if (c >= 0 && c < p.N) pos_of[c] = 1;
+    if (c >= 0 && c < p.N) {
+      pos_of[c] = 1;
+      if (c < cw0) atomicAdd(&s_nlo[qi], 1);
+      else if (c <= cw1) atomicAdd(&s_nin[qi], 1);
+    }
   }
   for (int e = tid; e < kPfQB * G * p.K; e += NT) {
     const int qi = e / (G * p.K), rem = e - qi * G * p.K, hh2 = rem / p.K, kk = rem - hh2 * p.K;
@@ -1013,10 +1020,11 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   }
   __syncthreads();
   if (w == 0) {
+    // list order: the window range first (every block's heavy positions up front), then
+    // the other chunks ascending, so that concurrently running blocks walk the remote
+    // chunks in step and share them in L2
     int base = 0;
-    for (int c0 = 0; c0 < p.N; c0 += 64) {
-      const int c = c0 + lane;
-      const bool f = c < p.N && pos_of[c] != 0;
+    auto append = [&](int c, bool f) {
       const unsigned long long m = __ballot(f);
       const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
       if (f) {
@@ -1025,6 +1033,14 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
         pos_of[c] = (short)pos;
       }
       base += __popcll(m);
+    };
+    for (int c0 = cw0; c0 <= cw1; c0 += 64) {
+      const int c = c0 + lane;
+      append(c, c <= cw1 && pos_of[c] != 0);
+    }
+    for (int c0 = 0; c0 < p.N; c0 += 64) {
+      const int c = c0 + lane;
+      append(c, c < p.N && (c < cw0 || c > cw1) && pos_of[c] != 0);
     }
     if (lane == 0) s_n = base;
   }
@@ -1118,11 +1134,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   float mrow[2], lrow[2];
   int ptr[2], tq[2];
   bool rv[2];
-  long long iq[2];
+  int iq[2];   // content indices fit in 32 bits (N < 32768 on this path)
+  const int R32 = (int)min((long long)p.R, Tcont);   // a wider radius selects the same keys
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     tq[tt] = tb0 + 4 * w + 2 * tt + qq;
-    iq[tt] = (long long)p.q0 + tq[tt];
+    iq[tt] = p.q0 + tq[tt];
     rv[tt] = tq[tt] < p.nq && hh < G;
     const bf16_t* qrow = rv[tt] ? reinterpret_cast<const bf16_t*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq[tt])) * D
                                 : nullptr;
@@ -1134,8 +1151,13 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
     ptr[tt] = 0;
   }
   const float* zrow[2];
+  int nlo[2], nin[2];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) zrow[tt] = zs + ((4 * w + 2 * tt + qq) * G + (hh < G ? hh : 0)) * p.K;
+  for (int tt = 0; tt < 2; ++tt) {
+    zrow[tt] = zs + ((4 * w + 2 * tt + qq) * G + (hh < G ? hh : 0)) * p.K;
+    nlo[tt] = s_nlo[4 * w + 2 * tt + qq];
+    nin[tt] = s_nin[4 * w + 2 * tt + qq];
+  }
   bool failed = false;
   for (int base = 0; base < n && !failed; base += 64) {
     const int pl = base + lane < n ? base + lane : n - 1;
@@ -1149,7 +1171,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
       const int c = __builtin_amdgcn_readlane(pc, bit);
       const unsigned bits = (unsigned)__builtin_amdgcn_readlane((int)pm, bit) >> (4 * w);
       // per tile and lane: window keys, selected chunk, or nothing
-      const long long cf = (long long)c * kContent, cl = cf + kContent - 1;
+      const int cf = c * kContent;
       int mode[2], lo[2], hi[2];
       float zc[2];
       bool act[2], anywin = false;
@@ -1157,12 +1179,19 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
       for (int tt = 0; tt < 2; ++tt) {
         act[tt] = ((bits >> (2 * tt)) & 3u) != 0u;
         const bool qa = ((bits >> (2 * tt + qq)) & 1u) != 0u;
-        const bool win = cf <= iq[tt] + p.R && cl >= iq[tt] - p.R;
+        const int rel = iq[tt] - cf;   // query index relative to the chunk's first key
+        const bool win = rel + R32 >= 0 && rel - R32 <= kContent - 1;
         mode[tt] = (!qa || !rv[tt]) ? 0 : (win ? 1 : 2);
-        lo[tt] = mode[tt] == 1 ? (int)max(0LL, iq[tt] - p.R - cf) : 0;
-        hi[tt] = mode[tt] == 1 ? (int)min((long long)kContent - 1, iq[tt] + p.R - cf) : kContent - 1;
+        lo[tt] = mode[tt] == 1 ? max(0, rel - R32) : 0;
+        hi[tt] = mode[tt] == 1 ? min(kContent - 1, rel + R32) : kContent - 1;
         zc[tt] = 0.f;
-        if (p.K > 0) zc[tt] = zrow[tt][ptr[tt] < p.K ? ptr[tt] : p.K - 1];   // K uniform
+        if (p.K > 0) {   // K uniform
+          // the v-th selected chunk visited: the list walks the window range, then the
+          // chunks below it, then those above, each ascending, while zsel is ascending
+          const int v = ptr[tt];
+          int ks = v < nin[tt] ? nlo[tt] + v : (v < nin[tt] + nlo[tt] ? v - nin[tt] : v);
+          zc[tt] = zrow[tt][ks < p.K ? ks : p.K - 1];
+        }
         if (qa && !win) ++ptr[tt];
         anywin = anywin || (__ballot(mode[tt] == 1) != 0ull);
       }

@@ -166,13 +166,18 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 // halves) between two registers; with both operands equal, element 0 and 1 of
 // the result hold, in every lane, the value of the lane itself and of its
 // partner l^16 (resp. l^32), in some order. Plain VALU, no LDS round trip.
+// Maxima use the NaN-propagating IEEE maximum (v_maximum3_f32 on gfx950): the
+// reductions here only see finite values and -inf masks, and unlike fmaxf it
+// needs no canonicalisation of MFMA results.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return max2(a, max2(b, c)); }
 __device__ __forceinline__ float xor16_max(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor16_sum(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -1013,7 +1013,8 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
 //      direct-to-LDS loads in one burst (16-byte pieces XOR-swizzled by row so
 //      that the fragment reads are conflict free); wave w scores heads w,
 //      w + 4 for all 32 chunks x 32 queries with the split products of
-//      score_kernel, and the group maximum is taken through LDS.
+//      score_kernel, and the group maximum is taken through LDS. (Every block
+//      reads its group's q~, so smaller chunk tiles would re-read more of it.)
 //  5d. topk_small_kernel: one block per (batch, group, query). Each wave finds
 //      the top K of its own range of chunks; every member of the overall top K
 //      is in the top K of its range, so one wave then selects the final K from
@@ -1385,12 +1386,17 @@ __device__ __forceinline__ int wave_topk(const uint32_t* key, int K, int lane, E
   uint32_t theta = 0u;
   int need = 0;
   if (!take_all) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t trial = theta | (1u << bit);
-      int cnt = 0;
+    // theta = the largest key with at least K keys >= theta, two bits per step
+    for (int bit = 30; bit >= 0; bit -= 2) {
+      const uint32_t t1 = theta | (1u << bit), t2 = theta | (2u << bit), t3 = theta | (3u << bit);
+      int c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
-      for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[j] >= trial));
-      if (cnt >= K) theta = trial;
+      for (int j = 0; j < P; ++j) {
+        c1 += __popcll(__ballot(key[j] >= t1));
+        c2 += __popcll(__ballot(key[j] >= t2));
+        c3 += __popcll(__ballot(key[j] >= t3));
+      }
+      theta = c3 >= K ? t3 : (c2 >= K ? t2 : (c1 >= K ? t1 : theta));
     }
     int gt = 0;
 #pragma unroll
