@@ -801,9 +801,17 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
 //    the slots of positions it still needs, not the whole ring.
 // A consumer whose two tiles are both active on a chunk reads each K and V
 // fragment once for both.
-constexpr int kPfCons = 7;                 // consumer waves
-constexpr int kPfWaves = kPfCons + 1;      // + the producer
-constexpr int kPfQB = 4 * kPfCons;         // queries per block
+// Block shape: TPC 16-row tiles (2 queries x 8 head rows) per consumer wave.
+// TPC = 1 keeps a consumer under 128 VGPRs, so 16 waves fit a CU (four per
+// SIMD to hide the S -> softmax -> PV chain of each wave); TPC = 2 shares every
+// K and V fragment read between two tiles but allows only 8 waves.
+template <int TPC> struct PfShape {
+  static constexpr int kCons = TPC == 2 ? 7 : 15;              // consumer waves
+  static constexpr int kWaves = kCons + 1;                     // + the producer
+  static constexpr int kQB = 2 * TPC * kCons;                  // queries per block
+  static constexpr unsigned kMask = (1u << (2 * TPC)) - 1u;    // a consumer's bits of a position mask
+};
+constexpr int kPfTPC = 1;   // the shape the planner launches
 
 
 
@@ -954,8 +962,10 @@ __device__ __forceinline__ int lds_load_rel(int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <int D, int NBUF>
-__global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedParams p) {
+template <int D, int NBUF, int TPC>
+__global__ __launch_bounds__(64 * PfShape<TPC>::kWaves) void routed_prefill_kernel(RoutedParams p) {
+  constexpr int kPfCons = PfShape<TPC>::kCons, kPfWaves = PfShape<TPC>::kWaves, kPfQB = PfShape<TPC>::kQB;
+  constexpr unsigned kCMask = PfShape<TPC>::kMask;
   typedef TileLayout<D, true> TL;
   constexpr int BUFE = TL::PL;                 // elements per chunk buffer (K then V)
   constexpr int NI = D / 8;                    // DMA instructions per half
@@ -1062,6 +1072,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
 
   if (w == kPfCons) {
     // ---------------- producer
+    // Its instructions go ahead of the consumers' on the shared SIMD: the whole block
+    // runs at the pace of its loads, so their issue must not wait behind softmax work.
+    __builtin_amdgcn_s_setprio(3);
     int h = 0, told = 0;   // told: landed halves already published (monotonic)
     int slot = 0;
     bool ok = true;
@@ -1073,49 +1086,65 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
     }
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)kvb);
-    for (; h < 2 * n && ok; ++h) {
-      const int j = h >> 1;
-      if ((h & 1) == 0) {
-        // a free slot for position j
-        unsigned long long fr = __ballot(lane < NBUF && lds_load_rel(&s_rem[lane < NBUF ? lane : 0]) == 0);
-        if (fr == 0ull) {
-          wait_vm<0>();                     // publish what has landed before waiting
-          compiler_fence();
-          if (lane == 0) lds_store_rel(&s_landed, h);
-          told = h;
-          int it = 0;
-          for (; it < kSpinLimit && fr == 0ull; ++it) {
-            __builtin_amdgcn_s_sleep(1);
-            fr = __ballot(lane < NBUF && lds_load_rel(&s_rem[lane < NBUF ? lane : 0]) == 0);
-          }
-          if (fr == 0ull || lds_load_rel(&s_fail) != 0) {
-            ok = false;
-            break;
-          }
-        }
-        slot = __builtin_ctzll(fr);
-        // consumers active on position j: one bit per 4-query group of the mask
-        const unsigned pm = pos_mask[j];
-        int users = 0;
+    // publish the halves below h - HF + 1 once at most HF - 1 of this wave's loads are in flight
+    auto publish_landed = [&](int hh2) {
+      if (hh2 >= HF && hh2 - HF + 1 > told) {
+        wait_vm<(HF - 1) * NI>();
+        compiler_fence();
+        if (lane == 0) lds_store_rel(&s_landed, hh2 - HF + 1);
+        told = hh2 - HF + 1;
+      }
+    };
+    // Chunks and consumer counts of 64 positions are read lane-parallel up front, and
+    // slots seen free stay known (only this wave allocates them), so that the LDS round
+    // trips between loads are few: a refresh of the slot counts when no slot is known free.
+    unsigned known_free = (1u << NBUF) - 1u;
+    for (int base = 0; base < n && ok; base += 64) {
+      const int pj = base + lane < n ? base + lane : n - 1;
+      const int pcl = pos_chunk[pj];
+      const unsigned pml = pos_mask[pj];
+      int ul = 0;
 #pragma unroll
-        for (int cw = 0; cw < kPfCons; ++cw) users += ((pm >> (4 * cw)) & 15u) != 0u ? 1 : 0;
+      for (int cw = 0; cw < kPfCons; ++cw) ul += ((pml >> (2 * TPC * cw)) & kCMask) != 0u ? 1 : 0;
+      const int cnt = min(64, n - base);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const int j = base + jj;
+        h = 2 * j;
+        if (known_free == 0u) {
+          unsigned long long fr = __ballot(lane < NBUF && lds_load_rel(&s_rem[lane < NBUF ? lane : 0]) == 0);
+          if (fr == 0ull) {
+            wait_vm<0>();                     // publish what has landed before waiting
+            compiler_fence();
+            if (lane == 0) lds_store_rel(&s_landed, h);
+            told = h;
+            int it = 0;
+            for (; it < kSpinLimit && fr == 0ull; ++it) {
+              __builtin_amdgcn_s_sleep(1);
+              fr = __ballot(lane < NBUF && lds_load_rel(&s_rem[lane < NBUF ? lane : 0]) == 0);
+            }
+            if (fr == 0ull || lds_load_rel(&s_fail) != 0) {
+              ok = false;
+              break;
+            }
+          }
+          known_free = (unsigned)fr;
+        }
+        slot = __builtin_ctz(known_free);
+        known_free &= known_free - 1u;
+        const int users = __builtin_amdgcn_readlane(ul, jj);
+        const int c = __builtin_amdgcn_readlane(pcl, jj);
         if (lane == 0) {
           lds_store_rel(&s_rem[slot], users);
           pos_of[j] = (short)slot;          // published before the halves landed count
         }
         compiler_fence();
+        const size_t off = (size_t)c * kSlots * D;
+        const uint32_t lbuf = lds0 + (uint32_t)(slot * BUFE * 2);
+        publish_landed(h);
+        dma_half_fast<D>(kg + off, lbuf, voffk);
+        publish_landed(h + 1);
+        dma_half_fast<D>(vg + off, lbuf + TL::KE * 2, voffv);
       }
-      if (h >= HF && h - HF + 1 > told) {
-        wait_vm<(HF - 1) * NI>();           // halves up to h - HF have landed
-        compiler_fence();
-        if (lane == 0) lds_store_rel(&s_landed, h - HF + 1);
-        told = h - HF + 1;
-      }
-      const int c = __builtin_amdgcn_readfirstlane(pos_chunk[j]);
-      const size_t off = (size_t)c * kSlots * D;
-      const uint32_t lbuf = lds0 + (uint32_t)(slot * BUFE * 2);
-      if ((h & 1) == 0) dma_half_fast<D>(kg + off, lbuf, voffk);
-      else dma_half_fast<D>(vg + off, lbuf + TL::KE * 2, voffv);
     }
     wait_vm<0>();
     compiler_fence();
@@ -1126,19 +1155,20 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
     return;
   }
 
-  // ---------------- consumer w: queries 4w .. 4w + 3 of the block
+  // ---------------- consumer w: queries 2 TPC w .. 2 TPC w + 2 TPC - 1 of the block
   const int qq = (lane & 15) >> 3, hh = lane & 7;
   const int h = g * G + hh;
-  QFrag<D, 1> qf[2];
-  f32x4 acc[2][D / 16];
-  float mrow[2], lrow[2];
-  int ptr[2], tq[2];
-  bool rv[2];
-  int iq[2];   // content indices fit in 32 bits (N < 32768 on this path)
+  const int qw = 2 * TPC * w;   // the wave's first query in the block
+  QFrag<D, 1> qf[TPC];
+  f32x4 acc[TPC][D / 16];
+  float mrow[TPC], lrow[TPC];
+  int ptr[TPC], tq[TPC];
+  bool rv[TPC];
+  int iq[TPC];   // content indices fit in 32 bits (N < 32768 on this path)
   const int R32 = (int)min((long long)p.R, Tcont);   // a wider radius selects the same keys
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    tq[tt] = tb0 + 4 * w + 2 * tt + qq;
+  for (int tt = 0; tt < TPC; ++tt) {
+    tq[tt] = tb0 + qw + 2 * tt + qq;
     iq[tt] = p.q0 + tq[tt];
     rv[tt] = tq[tt] < p.nq && hh < G;
     const bf16_t* qrow = rv[tt] ? reinterpret_cast<const bf16_t*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq[tt])) * D
@@ -1150,33 +1180,33 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
     lrow[tt] = 0.f;
     ptr[tt] = 0;
   }
-  const float* zrow[2];
-  int nlo[2], nin[2];
+  const float* zrow[TPC];
+  int nlo[TPC], nin[TPC];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    zrow[tt] = zs + ((4 * w + 2 * tt + qq) * G + (hh < G ? hh : 0)) * p.K;
-    nlo[tt] = s_nlo[4 * w + 2 * tt + qq];
-    nin[tt] = s_nin[4 * w + 2 * tt + qq];
+  for (int tt = 0; tt < TPC; ++tt) {
+    zrow[tt] = zs + ((qw + 2 * tt + qq) * G + (hh < G ? hh : 0)) * p.K;
+    nlo[tt] = s_nlo[qw + 2 * tt + qq];
+    nin[tt] = s_nin[qw + 2 * tt + qq];
   }
   bool failed = false;
   for (int base = 0; base < n && !failed; base += 64) {
     const int pl = base + lane < n ? base + lane : n - 1;
     const unsigned pm = base + lane < n ? pos_mask[pl] : 0u;
     const int pc = pos_chunk[pl];
-    unsigned long long mine = __ballot(((pm >> (4 * w)) & 15u) != 0u);
+    unsigned long long mine = __ballot(((pm >> qw) & kCMask) != 0u);
     while (mine != 0ull) {
       const int bit = __builtin_ctzll(mine);
       mine &= mine - 1ull;
       const int j = base + bit;
       const int c = __builtin_amdgcn_readlane(pc, bit);
-      const unsigned bits = (unsigned)__builtin_amdgcn_readlane((int)pm, bit) >> (4 * w);
+      const unsigned bits = (unsigned)__builtin_amdgcn_readlane((int)pm, bit) >> qw;
       // per tile and lane: window keys, selected chunk, or nothing
       const int cf = c * kContent;
-      int mode[2], lo[2], hi[2];
-      float zc[2];
-      bool act[2], anywin = false;
+      int mode[TPC], lo[TPC], hi[TPC];
+      float zc[TPC];
+      bool act[TPC], anywin = false;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < TPC; ++tt) {
         act[tt] = ((bits >> (2 * tt)) & 3u) != 0u;
         const bool qa = ((bits >> (2 * tt + qq)) & 1u) != 0u;
         const int rel = iq[tt] - cf;   // query index relative to the chunk's first key
@@ -1210,7 +1240,34 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
       compiler_fence();
       const int slot = pos_of[j];   // written by the producer before the landed count
       const bf16_t* buf = kvb + slot * BUFE;
-      if (act[0] && act[1]) {
+      // one tile: the same code for tile 0 or tile 1, chosen by a uniform branch
+      auto single = [&](auto tile) -> bool {
+        constexpr int tt = decltype(tile)::value;
+        f32x4 sacc[1][4];
+        s_tiles<D, 1>(buf, &qf[tt], sacc, lane);
+        s16x8 pf[1][2];
+        const float alpha = anywin ? tile_softmax<true>(sacc[0], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16,
+                                                        mrow[tt], lrow[tt], pf[0])
+                                   : tile_softmax<false>(sacc[0], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16,
+                                                         mrow[tt], lrow[tt], pf[0]);
+        if (__ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+          for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+        }
+        int it = 0;
+        while (lds_load_rel(&s_landed) < 2 * j + 2 && it < kSpinLimit) {
+          __builtin_amdgcn_s_sleep(1);
+          ++it;
+        }
+        if (it == kSpinLimit) return false;
+        compiler_fence();
+        pv_tiles<D, 1>(buf, pf, &acc[tt], lane);
+        return true;
+      };
+      // both tiles: every K and V fragment read serves the two of them
+      auto fused = [&](auto) -> bool {
         f32x4 sacc[2][4];
         s_tiles<D, 2>(buf, qf, sacc, lane);
         s16x8 pf[2][2];
@@ -1234,45 +1291,23 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
             __builtin_amdgcn_s_sleep(1);
             ++it;
           }
-          if (it == kSpinLimit) {
-            failed = true;
-            break;
-          }
+          if (it == kSpinLimit) return false;
         }
         compiler_fence();
         pv_tiles<D, 2>(buf, pf, acc, lane);
+        return true;
+      };
+      bool done;
+      if constexpr (TPC == 2) {
+        done = (act[0] && act[1]) ? fused(0)
+                                  : (act[0] ? single(std::integral_constant<int, 0>{})
+                                            : single(std::integral_constant<int, 1>{}));
       } else {
-        // one tile: the same code for tile 0 or tile 1, chosen by a uniform branch
-        auto single = [&](auto tile) -> bool {
-          constexpr int tt = decltype(tile)::value;
-          f32x4 sacc[1][4];
-          s_tiles<D, 1>(buf, &qf[tt], sacc, lane);
-          s16x8 pf[1][2];
-          const float alpha = anywin ? tile_softmax<true>(sacc[0], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16,
-                                                          mrow[tt], lrow[tt], pf[0])
-                                     : tile_softmax<false>(sacc[0], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16,
-                                                           mrow[tt], lrow[tt], pf[0]);
-          if (__ballot(alpha != 1.f) != 0ull) {
-#pragma unroll
-            for (int dm = 0; dm < D / 16; ++dm)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
-          }
-          int it = 0;
-          while (lds_load_rel(&s_landed) < 2 * j + 2 && it < kSpinLimit) {
-            __builtin_amdgcn_s_sleep(1);
-            ++it;
-          }
-          if (it == kSpinLimit) return false;
-          compiler_fence();
-          pv_tiles<D, 1>(buf, pf, &acc[tt], lane);
-          return true;
-        };
-        const bool done = act[0] ? single(std::integral_constant<int, 0>{}) : single(std::integral_constant<int, 1>{});
-        if (!done) {
-          failed = true;
-          break;
-        }
+        done = single(std::integral_constant<int, 0>{});
+      }
+      if (!done) {
+        failed = true;
+        break;
       }
       // every LDS read of the slot has returned: release it
       wait_lgkm0();
@@ -1284,7 +1319,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
 
   // ---- results
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < TPC; ++tt) {
     if (!rv[tt]) continue;
     const float inv = 1.f / lrow[tt];
     bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq[tt])) * D;
@@ -1714,7 +1749,7 @@ static size_t kv_lds_bytes(int d, int dtype) {
   return nbuf * one;
 }
 
-size_t routed_lds_limit() { return 160 * 1024 - 256; }  // room for the static LDS variables
+size_t routed_lds_limit() { return 160 * 1024 - 512; }  // room for the static LDS variables
 
 static int routed_nbuf(int d, int dtype, int waves) {
   if (dtype == 1) return waves == 1 ? 2 : 3;        // direct-to-LDS ring, prefetch distance NBUF - 1
@@ -1737,7 +1772,8 @@ static size_t routed_lds(const RouteDims& dm, int K, int qblock, int waves) {
 // per-position tables (chunk, query mask, position of each chunk).
 static size_t prefill_lds(const RouteDims& dm, int K, int nbuf) {
   const int G = dm.Hq / dm.Hkv;
-  const size_t b = (size_t)nbuf * 2 * 64 * dm.d * 2 + (size_t)kPfQB * G * K * 4 + (size_t)dm.N * (4 + 4 + 2);
+  const size_t b = (size_t)nbuf * 2 * 64 * dm.d * 2 + (size_t)PfShape<kPfTPC>::kQB * G * K * 4 +
+                   (size_t)dm.N * (4 + 4 + 2);
   return (b + 15) & ~(size_t)15;
 }
 
@@ -1803,9 +1839,9 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
       if (lds <= routed_lds_limit()) {
         pl.kind = 2;
         pl.nbuf = nb;
-        pl.waves = kPfWaves;
+        pl.waves = PfShape<kPfTPC>::kWaves;
         pl.tiles = 2;
-        pl.qblock = kPfQB;
+        pl.qblock = PfShape<kPfTPC>::kQB;
         pl.lds = lds;
         break;
       }
@@ -1859,11 +1895,11 @@ static hipError_t launch_decode_t(const RouteDims& dm, const AttnPlan& pl, const
 
 template <int D, int NBUF>
 static hipError_t launch_prefill_t(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
-  auto kern = routed_prefill_kernel<D, NBUF>;
+  auto kern = routed_prefill_kernel<D, NBUF, kPfTPC>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
   if (e != hipSuccess) return e;
-  const int tiles = (prm.nq + kPfQB - 1) / kPfQB * dm.B * dm.Hkv;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * kPfWaves), pl.lds, st, prm);
+  const int tiles = (prm.nq + PfShape<kPfTPC>::kQB - 1) / PfShape<kPfTPC>::kQB * dm.B * dm.Hkv;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * PfShape<kPfTPC>::kWaves), pl.lds, st, prm);
   return hipGetLastError();
 }
 
