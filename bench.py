@@ -201,7 +201,7 @@ def bench_prefill(args, torch, lcr):
         "ms_per_step": wall / args.steps * 1e3,
         "op_ms_median": {"chunk_summary": round(float(med[0]), 4), "route_score_topk": round(float(med[1]), 4),
                          "routed_attention": round(float(med[2]), 4)},
-        "roofline": {"bound": "mfma", "kernel": "routed_attention_kernel", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "routed_prefill_kernel", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
                      "algorithmic_gflop_per_launch": round((local + chunks) / 1e9, 2),

@@ -1386,17 +1386,13 @@ __device__ __forceinline__ int wave_topk(const uint32_t* key, int K, int lane, E
   uint32_t theta = 0u;
   int need = 0;
   if (!take_all) {
-    // theta = the largest key with at least K keys >= theta, two bits per step
-    for (int bit = 30; bit >= 0; bit -= 2) {
-      const uint32_t t1 = theta | (1u << bit), t2 = theta | (2u << bit), t3 = theta | (3u << bit);
-      int c1 = 0, c2 = 0, c3 = 0;
+    // theta = the largest key with at least K keys >= theta, one bit per step
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t trial = theta | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        c1 += __popcll(__ballot(key[j] >= t1));
-        c2 += __popcll(__ballot(key[j] >= t2));
-        c3 += __popcll(__ballot(key[j] >= t3));
-      }
-      theta = c3 >= K ? t3 : (c2 >= K ? t2 : (c1 >= K ? t1 : theta));
+      for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[j] >= trial));
+      if (cnt >= K) theta = trial;
     }
     int gt = 0;
 #pragma unroll
