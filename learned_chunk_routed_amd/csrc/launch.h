@@ -26,6 +26,7 @@ struct ScoreWs {
   float* upart; // [splits,B,nq,rank padded to 32/64/128]  partial x A
   bf16_t* splanes; // [B,Hq,N,2d] summaries as bf16 hi then lo, k-permuted (fused path)
   bf16_t* qplanes; // [B,Hq,32,2d] q~ as bf16 hi then lo (decode-sized path)
+  bf16_t* at;      // [rank padded, D padded to 32] A transposed (bf16 prefill path)
 };
 size_t score_ws_bytes(const RouteDims& dm, int D, int r, int nq);
 ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int D, int r, int nq);

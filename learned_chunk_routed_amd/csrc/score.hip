@@ -244,6 +244,97 @@ __global__ __launch_bounds__(256) void q_kernel(const T* __restrict__ q, const T
   }
 }
 
+// 1d. u_stream_kernel (bf16, prefill-sized): u = x A for 64 queries per block with
+//     the hidden dimension split over the 4 waves. x fragments stream from HBM
+//     straight into MFMA registers, and A comes transposed (rows = rank, padded with
+//     zeros to whole 32-wide k-steps), so both operands are plain 16-byte loads with
+//     kUsPD k-steps in flight per wave; the wave partials are summed through LDS and
+//     one partial set is written (no split of the hidden dimension in memory).
+constexpr int kUsPD = 4;   // k-steps of loads in flight per wave
+
+template <int RP>
+__global__ __launch_bounds__(256) void transpose_a_kernel(const bf16_t* __restrict__ A, int Dh, int r, int Dhp,
+                                                          bf16_t* __restrict__ At) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)RP * Dhp) return;
+  const int n = (int)(e / Dhp), k = (int)(e - (long long)n * Dhp);
+  At[e] = (n < r && k < Dh) ? A[(size_t)k * r + n] : (bf16_t)0;
+}
+
+template <int RP>
+__global__ __launch_bounds__(256) void u_stream_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ At,
+                                                       int Dh, int Dhp, float* __restrict__ upart, int N, int q0,
+                                                       int nq) {
+  constexpr int NTR = RP / 16;
+  constexpr int US = RP + 4;
+  extern __shared__ __align__(16) unsigned char smem[];   // wave partials [4][64][US] f32
+  float* red = reinterpret_cast<float*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+  const int b = blockIdx.y, t0 = blockIdx.x * 64;
+  const long long L = (long long)N * kSlots;
+  const int nks = Dhp / 32, kw = (nks + 3) / 4;
+  const int ks0 = min(w * kw, nks), n = min(nks, ks0 + kw) - ks0;   // this wave's k-steps
+  const bf16_t* xr[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int t = t0 + 16 * mt + L16;
+    xr[mt] = x + ((size_t)b * L + slot_of((long long)q0 + (t < nq ? t : 0))) * Dh;
+  }
+  f32x4 acc[4][NTR];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTR; ++nt) acc[mt][nt] = zero4();
+  s16x8 xf[kUsPD][4], af[kUsPD][NTR];
+  // k-step ks into register slot p; past the wave's range a valid step is loaded and not used.
+  // No value is masked (that would make every load wait at once): rows past nq read row
+  // q0's data and are never stored, and pieces past Dh (Dh % 8 == 0: a piece is wholly in
+  // or out) read the row's first piece, which meets the zero padding of the transposed A.
+  auto load = [&](int ks, int p) {
+    ks = min(ks, nks - 1);
+    const int kg = 32 * ks + 8 * g16;
+    const int kx = kg < Dh ? kg : 0;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) xf[p][mt] = load8(xr[mt] + kx);
+#pragma unroll
+    for (int nt = 0; nt < NTR; ++nt) af[p][nt] = load8(At + (size_t)(16 * nt + L16) * Dhp + kg);
+  };
+  auto mul = [&](int p) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTR; ++nt) acc[mt][nt] = mfma16(xf[p][mt], af[p][nt], acc[mt][nt]);
+  };
+#pragma unroll
+  for (int p = 0; p < kUsPD; ++p) load(ks0 + p, p);
+  int it = 0;
+  for (; it + kUsPD <= n; it += kUsPD) {
+#pragma unroll
+    for (int p = 0; p < kUsPD; ++p) {
+      mul(p);
+      load(ks0 + it + p + kUsPD, p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kUsPD; ++p)
+    if (it + p < n) mul(p);
+  // D layout: lane holds u[query 16 mt + 4 g16 + i][rank 16 nt + L16]
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTR; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(w * 64 + 16 * mt + 4 * g16 + i) * US + 16 * nt + L16] = acc[mt][nt][i];
+  __syncthreads();
+  for (int e = tid; e < 64 * RP; e += 256) {
+    const int t = e / RP, nn = e - t * RP;
+    if (t0 + t < nq)
+      upart[((size_t)b * nq + t0 + t) * RP + nn] =
+          ((red[t * US + nn] + red[(64 + t) * US + nn]) + red[(128 + t) * US + nn]) + red[(192 + t) * US + nn];
+  }
+}
+static size_t u_stream_lds(int RP) { return (size_t)4 * 64 * (RP + 4) * 4; }
+
 // 1c. qtilde_small_kernel (bf16, at most 32 queries, as in a decode step): one
 //     block per head computes u = x A for all the queries itself, then
 //     q~ = q + u B_h. Wave w takes every eighth 64-row slice of A (staged in
@@ -1503,6 +1594,8 @@ static bool small_score_ok(const RouteDims& dm, int r, int nq) {
   return dm.dtype == 1 && nq <= kDecQ && r <= 64 && dm.Hq / dm.Hkv <= 8 && dm.N <= 8192;
 }
 static int u_small_splits(int Dh) { return (Dh + kUSmallRows - 1) / kUSmallRows; }
+static int dh_pad(int Dh) { return (Dh + 31) / 32 * 32; }
+static size_t at_bytes(int Dh, int r) { return (size_t)rank_pad(r) * dh_pad(Dh) * 2; }   // A transposed
 
 size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
@@ -1511,7 +1604,8 @@ size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
            align256((size_t)dm.B * dm.Hq * kDecQ * 2 * dm.d * 2) + align256(rows_g * dm.N * 4) +
            align256(rows_h * dm.N * 4);
   const size_t upart = (size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4;
-  if (fused_score_ok(dm, r, nq)) return align256(upart) + align256((size_t)dm.B * dm.Hq * dm.N * dm.d * 4);
+  if (fused_score_ok(dm, r, nq))
+    return align256(upart) + align256((size_t)dm.B * dm.Hq * dm.N * dm.d * 4) + align256(at_bytes(Dh, r));
   return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4) + align256(upart);
 }
 
@@ -1521,6 +1615,7 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
   ScoreWs out;
   out.splanes = nullptr;
   out.qplanes = nullptr;
+  out.at = nullptr;
   if (small_score_ok(dm, r, nq)) {
     out.qt = nullptr;
     out.upart = (float*)p;
@@ -1539,6 +1634,8 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
     out.upart = (float*)p;
     p += align256((size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4);
     out.splanes = (bf16_t*)p;
+    p += align256((size_t)dm.B * dm.Hq * dm.N * dm.d * 4);
+    out.at = (bf16_t*)p;
     return out;
   }
   out.qt = (float*)p;
@@ -1591,12 +1688,29 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
                                      const void* Bm, int Dh, int r, const float* s, const float* H, float beta,
                                      float scale, int K, int radius, int q0, int nq, int32_t* idx, float* zsel,
                                      const ScoreWs& ws, hipStream_t st) {
-  const int nsplit = u_splits(dm, Dh, nq);
-  const int nslices = (Dh + kUKc - 1) / kUKc;
-  const int per = (nslices + nsplit - 1) / nsplit;
-  hipLaunchKernelGGL((u_kernel<bf16_t, RP>), dim3((nq + 63) / 64, dm.B, nsplit), dim3(256), 0, st, (const bf16_t*)x,
-                     (const bf16_t*)A, Dh, r, ws.upart, dm.N, q0, nq, per);
-  hipError_t e = hipGetLastError();
+  int nsplit;
+  hipError_t e;
+  if (Dh % 8 == 0) {
+    // x streamed once against A transposed: one partial set
+    nsplit = 1;
+    const int Dhp = dh_pad(Dh);
+    hipLaunchKernelGGL((transpose_a_kernel<RP>), dim3((unsigned)(((long long)RP * Dhp + 255) / 256)), dim3(256), 0, st,
+                       (const bf16_t*)A, Dh, r, Dhp, ws.at);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    auto uk = u_stream_kernel<RP>;
+    e = hipFuncSetAttribute((const void*)uk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)u_stream_lds(RP));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(uk, dim3((nq + 63) / 64, dm.B), dim3(256), u_stream_lds(RP), st, (const bf16_t*)x, ws.at, Dh,
+                       Dhp, ws.upart, dm.N, q0, nq);
+  } else {
+    nsplit = u_splits(dm, Dh, nq);
+    const int nslices = (Dh + kUKc - 1) / kUKc;
+    const int per = (nslices + nsplit - 1) / nsplit;
+    hipLaunchKernelGGL((u_kernel<bf16_t, RP>), dim3((nq + 63) / 64, dm.B, nsplit), dim3(256), 0, st,
+                       (const bf16_t*)x, (const bf16_t*)A, Dh, r, ws.upart, dm.N, q0, nq, per);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = (long long)dm.B * dm.Hq * dm.N;
   hipLaunchKernelGGL((split_summary_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st, s,
