@@ -5,46 +5,59 @@
 // Speedup Has an Evidence Budget", section "How learned routing controls what
 // the model can read": the entropy of the pooling weights ranks chunks too.
 //
-// One 64-lane wave per (batch, KV head, chunk): the chunk's keys are read from
-// HBM once into LDS (float32, padded rows so lane j reading row j is bank-
-// conflict free) and serve the G mask queries of the group. Lane j < 63 owns
-// content key j for the logits; for the weighted sum lanes own output columns.
-// Work is tiny next to the routed attention (4*63*d flops per head and chunk),
-// so plain float32 VALU arithmetic with exact expf/logf is used.
+// One block of four waves per (batch, KV head, chunk): the chunk's keys are read
+// from HBM once into LDS with 16-byte loads (float32, padded rows so that lane j
+// reading row j is bank-conflict free) and serve the G mask queries of the group,
+// wave w taking heads w, w + 4, ... Lane j < 63 owns content key j for the logits
+// (four independent partial sums over d); for the weighted sum lanes own output
+// columns. Work is tiny next to the routed attention (4*63*d flops per head and
+// chunk), so plain float32 VALU arithmetic with exact expf/logf is used.
 #include "device.h"
 #include "launch.h"
 
 namespace lcr {
 
+constexpr int kSumWaves = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void chunk_summary_kernel(const T* __restrict__ q,
-                                                           const T* __restrict__ k, float scale,
-                                                           float* __restrict__ s,
-                                                           float* __restrict__ Hout, int Hq,
-                                                           int Hkv, int N) {
+__global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(const T* __restrict__ q,
+                                                                       const T* __restrict__ k, float scale,
+                                                                       float* __restrict__ s,
+                                                                       float* __restrict__ Hout, int Hq, int Hkv,
+                                                                       int N) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = Hq / Hkv;
   const size_t L = (size_t)N * kSlots;
+  constexpr int VE = 16 / sizeof(T);   // elements per 16-byte load
   __shared__ float ks[kContent][D + 1];
-  __shared__ float qs[D];
-  __shared__ float al[64];
+  __shared__ float qs[kSumWaves][D];
+  __shared__ float al[kSumWaves][64];
 
   const T* kc = k + (((size_t)b * Hkv + g) * L + (size_t)c * kSlots) * D;
-  for (int e = lane; e < kContent * D; e += 64) ks[e / D][e % D] = Elem<T>::to_f(kc[e]);
+  for (int e = VE * tid; e < kContent * D; e += VE * 64 * kSumWaves) {
+    typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(kc + e);
+    const T* pv = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int j = 0; j < VE; ++j) ks[(e + j) / D][(e + j) % D] = Elem<T>::to_f(pv[j]);
+  }
   __syncthreads();
 
-  for (int hh = 0; hh < G; ++hh) {
+  for (int hh = w; hh < G; hh += kSumWaves) {
     const int h = g * G + hh;
     const T* qm = q + (((size_t)b * Hq + h) * L + (size_t)c * kSlots + (kSlots - 1)) * D;
-    for (int e = lane; e < D; e += 64) qs[e] = Elem<T>::to_f(qm[e]);
-    __syncthreads();
+    for (int e = lane; e < D; e += 64) qs[w][e] = Elem<T>::to_f(qm[e]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the row is in LDS for the whole wave
+    __builtin_amdgcn_wave_barrier();
     float logit = -INFINITY;
     if (lane < kContent) {
-      float acc = 0.f;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-      for (int e = 0; e < D; ++e) acc = fmaf(qs[e], ks[lane][e], acc);
-      logit = scale * acc;
+      for (int e = 0; e < D; e += 4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = fmaf(qs[w][e + u], ks[lane][e + u], acc[u]);
+      logit = scale * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
     }
     const float m = wave_max(logit);
     const float ex = lane < kContent ? expf(logit - m) : 0.f;
@@ -52,17 +65,20 @@ __global__ __launch_bounds__(64) void chunk_summary_kernel(const T* __restrict__
     const float a = ex / sum;
     // H = -sum a ln a = ln(sum) - sum a (logit - m), with ln a = logit - m - ln(sum)
     const float Hv = logf(sum) - wave_sum(lane < kContent ? a * (logit - m) : 0.f);
-    al[lane] = a;
-    __syncthreads();
+    al[w][lane] = a;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
     float* so = s + (((size_t)b * Hq + h) * N + c) * D;
     for (int e = lane; e < D; e += 64) {
-      float acc = 0.f;
-#pragma unroll 9
-      for (int j = 0; j < kContent; ++j) acc = fmaf(al[j], ks[j][e], acc);
-      so[e] = acc;
+      float acc[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kContent; j += 3)
+#pragma unroll
+        for (int u = 0; u < 3; ++u) acc[u] = fmaf(al[w][j + u], ks[j + u][e], acc[u]);
+      so[e] = (acc[0] + acc[1]) + acc[2];
     }
     if (lane == 0) Hout[((size_t)b * Hq + h) * N + c] = Hv;
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();   // this wave's rows of qs and al are reused by its next head
   }
 }
 
@@ -70,7 +86,7 @@ template <typename T, int D>
 static hipError_t launch_summary_t(const RouteDims& dm, const void* q, const void* k, float scale,
                                    float* s, float* H, hipStream_t st) {
   dim3 grid(dm.N, dm.Hkv, dm.B);
-  hipLaunchKernelGGL((chunk_summary_kernel<T, D>), grid, dim3(64), 0, st, (const T*)q,
+  hipLaunchKernelGGL((chunk_summary_kernel<T, D>), grid, dim3(64 * kSumWaves), 0, st, (const T*)q,
                      (const T*)k, scale, s, H, dm.Hq, dm.Hkv, dm.N);
   return hipGetLastError();
 }
