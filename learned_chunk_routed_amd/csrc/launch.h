@@ -27,6 +27,7 @@ struct ScoreWs {
   bf16_t* splanes; // [B,Hq,N,2d] summaries as bf16 hi then lo, k-permuted (fused path)
   bf16_t* qplanes; // [B,Hq,32,2d] q~ as bf16 hi then lo (decode-sized path)
   bf16_t* at;      // [rank padded, D padded to 32] A transposed (bf16 prefill path)
+  bf16_t* bt;      // [Hq*d, rank padded] B transposed (bf16 prefill path)
 };
 size_t score_ws_bytes(const RouteDims& dm, int D, int r, int nq);
 ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int D, int r, int nq);

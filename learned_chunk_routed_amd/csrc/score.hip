@@ -6,22 +6,19 @@
 // chunks are gathered beyond the local window. "The 172x Speedup Has an Evidence
 // Budget": rank-64 residual; similarity and pooling entropy rank the chunks.
 //
-// Three kernels:
-//  1. u_kernel + q_kernel: u = x A (MFMA, bf16 products exact in float32),
-//     then q~ = q + u B per head with u split into bf16 hi + lo (B is exact in
-//     bf16), written as float32 rows.
-//  2. score_kernel: z = scale * q~ . s - beta * H per head on MFMA with both
-//     operands split into bf16 planes (hi + lo for bf16 inputs: hi.hi + hi.lo +
-//     lo.hi; hi + mid + lo for float32 inputs), float32 accumulation:
-//     near-float32 scores so the top-K set matches an exact computation
-//     wherever the K-th/(K+1)-th margin is not tiny, and the
-//     group maximum zhat. Summaries are the MFMA rows (M = chunks), queries
-//     the columns (N = 16 queries).
-//  3. topk_kernel: one wave per (batch, group, query): candidates are tested
-//     from their indices, the K-th largest score is found by bisection on an
-//     order-preserving integer key, and the chosen chunks are compacted in
-//     ascending order with ballots (ties go to the smaller index). zsel is
-//     gathered from the per-head scores.
+// Paths, chosen by problem size and dtype:
+//  - general (float32 inputs, or bf16 beyond the fused path's limits):
+//    u_kernel + q_kernel (u = x A, then q~ = q + u B per head with u split into
+//    bf16 hi + lo), score_kernel (z = scale * q~ . s - beta * H per head on MFMA
+//    with both operands split into bf16 planes: hi.hi + hi.lo + lo.hi for bf16
+//    inputs, hi + mid + lo for float32; float32 accumulation, so the top-K set
+//    matches an exact computation wherever the K-th/(K+1)-th margin is not tiny;
+//    plus the group maximum), topk_kernel (one wave per (batch, group, query):
+//    bisection on an order-preserving key with ballot counts, ties to the
+//    smaller index; zsel gathered from the per-head scores);
+//  - bf16 prefill (section 1d and 4): u_stream_kernel, then route_score3_kernel
+//    from q~ to idx and zsel without per-head scores in memory;
+//  - bf16 decode-sized, at most 32 queries (section 5).
 #include "device.h"
 #include "launch.h"
 
@@ -259,6 +256,17 @@ __global__ __launch_bounds__(256) void transpose_a_kernel(const bf16_t* __restri
   if (e >= (long long)RP * Dhp) return;
   const int n = (int)(e / Dhp), k = (int)(e - (long long)n * Dhp);
   At[e] = (n < r && k < Dh) ? A[(size_t)k * r + n] : (bf16_t)0;
+}
+
+// B transposed for the fused scoring kernel: Bt[n][rr] = B[rr][n] for n < Hq * d,
+// rank rr < RP (zero past r), so each head's q~ product reads rank-contiguous rows.
+template <int D, int RP>
+__global__ __launch_bounds__(256) void transpose_b_kernel(const bf16_t* __restrict__ Bm, int r, int HD,
+                                                          bf16_t* __restrict__ Bt) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)HD * RP) return;
+  const int n = (int)(e / RP), rr = (int)(e - (long long)n * RP);
+  Bt[e] = rr < r ? Bm[(size_t)rr * HD + n] : (bf16_t)0;
 }
 
 template <int RP>
@@ -689,402 +697,278 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zha
 
 // ---------------------------------------------------------------------------- 4. fused scoring (bf16)
 //
-// route_score_kernel: for a tile of QT = 16 * NT consecutive queries and one
-// KV group, everything between the residual partials and the selection in one
-// block of 8 waves, without writing per-head scores or q~ to memory:
-//  A. for each head of the group: q~^T = q^T + B_h^T u^T on MFMA (u split into
-//     bf16 hi + lo, B exact), then z^T = s q~^T for every chunk on MFMA with
-//     both operands split into hi + lo (hi.hi + hi.lo + lo.hi), scaled, minus
-//     beta * H; the group maximum stays in registers. The q~^T output fragment
-//     is already the B operand of the scoring product (same lane -> k
-//     assignment on both sides), so it only passes through LDS to reach the
-//     waves that own other chunks.
-//  B. exact top-K per query from the group maxima in LDS (bisection on an
-//     order-preserving key with ballot counts, ties to the smaller chunk),
-//     written as idx; the rank of every chosen chunk is kept in LDS.
-//  C. the same products again (bit-identical), and each chosen (query, chunk)
-//     score of every head is written to zsel.
-// Wave w computes q~ for query tile w % NT over 8 / NT of the head dimension,
-// and owns the chunk row tiles w, w + 8, ... of the scores.
+// route_score3_kernel: for QT = 16 NT consecutive queries of one KV group,
+// everything between the residual partials and the selection in one block of 8
+// waves, without writing per-head scores or q~ to memory. Wave w < G owns head w:
+//  0. it forms q~ = q + u B_h of its head for the block's queries on MFMA (u split
+//     into bf16 hi + lo, B exact; B comes transposed per call so its fragments are
+//     plain loads) and keeps it in registers as the hi/lo B operand of the scoring
+//     product (the q~^T output fragment already has that lane -> k assignment);
+//  A. it computes z^T = s q~^T for every chunk row tile of its head with both
+//     operands split into hi + lo (hi.hi + hi.lo + lo.hi), scaled, minus beta * H
+//     (summaries as fragment-major split planes, 1 KB contiguous per load, the
+//     next tile in flight while the current one is multiplied), and folds the
+//     scores into the group maximum with LDS atomic max on order-preserving keys;
+//  B. exact top-K per query from those keys (all waves; bisection with ballot
+//     counts, ties to the smaller chunk), written as idx, with a [QT][N] rank table;
+//  C. the same products again (bit-identical); the scores of chosen (query,
+//     chunk) pairs go straight to zsel, each tile's ranks read with its planes.
 constexpr int kRsWaves = 8;
 
-// Barrier for LDS hand-offs only: this wave's LDS accesses have completed, but
-// its global loads may still be in flight (a __syncthreads would wait for them).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+__host__ __device__ inline size_t rs3_off_r(int NT, int N) { return (size_t)16 * NT * (N + 1) * 4; }
+__host__ __device__ inline size_t rs3_off_c(int NT, int N) { return (rs3_off_r(NT, N) + (size_t)16 * NT * N + 15) & ~(size_t)15; }
+__host__ __device__ inline size_t rs3_lds(int NT, int N) { return rs3_off_c(NT, N) + kRsWaves * 64 * 4; }
 
-// Summaries as the A operand of the scoring product: per (b, h, chunk) row, the
-// D values split into bf16 hi (first D) and lo (next D), each 32-wide k-step
-// stored as 4 groups of 8 with group g holding d = 32 ks + 4 g + {0..3} and
-// 32 ks + 16 + 4 g + {0..3} (the lane order of the MFMA fragments).
+// Summaries as the A operand of the scoring product, fragment-major: for each
+// (batch, head, 16-chunk row tile, k-step, plane) the 64 lanes' 16-byte fragments
+// are contiguous. Lane l holds chunk 16 mt + l % 16 and d = 32 ks + 4 (l / 16) +
+// {0..3}, 32 ks + 16 + 4 (l / 16) + {0..3}; plane 0 is bf16 hi, plane 1 lo. Rows
+// past N are zero.
 template <int D>
-__global__ __launch_bounds__(256) void split_summary_kernel(const float* __restrict__ s, bf16_t* __restrict__ sp,
-                                                            long long rows) {
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;   // one group of 8 per thread
-  constexpr int GPR = D / 8;                                         // groups per row
-  if (e >= rows * GPR) return;
-  const long long row = e / GPR;
-  const int gi = (int)(e % GPR), ks = gi >> 2, gg = gi & 3;
-  const float* src = s + row * D + 32 * ks + 4 * gg;
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
-  const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 16);
+__global__ __launch_bounds__(256) void split_frag_kernel(const float* __restrict__ s, bf16_t* __restrict__ sp, int N,
+                                                         long long heads) {
+  constexpr int KS = D / 32, GPR = D / 8;
+  const int NMT = (N + 15) / 16;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;   // one (head, row, group of 8) per thread
+  if (e >= heads * NMT * 16 * GPR) return;
+  const int gi = (int)(e % GPR);
+  const long long rowg = e / GPR;
+  const long long hd = rowg / (NMT * 16);
+  const int row = (int)(rowg - hd * NMT * 16);
+  const int mt = row >> 4, L16 = row & 15, ks = gi >> 2, gg = gi & 3;
   float v[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = a0[i];
-    v[4 + i] = a1[i];
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  if (row < N) {
+    const float* src = s + (hd * N + row) * D + 32 * ks + 4 * gg;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a0[i];
+      v[4 + i] = a1[i];
+    }
   }
   s16x8 hi, lo;
   pack8_split_hw(v, hi, lo);
-  *reinterpret_cast<s16x8*>(sp + row * 2 * D + 8 * gi) = hi;
-  *reinterpret_cast<s16x8*>(sp + row * 2 * D + D + 8 * gi) = lo;
+  bf16_t* dst = sp + ((((hd * NMT + mt) * KS + ks) * 2) * 64 + gg * 16 + L16) * 8;
+  *reinterpret_cast<s16x8*>(dst) = hi;
+  *reinterpret_cast<s16x8*>(dst + 64 * 8) = lo;
 }
-// MTW chunk row tiles per wave: N <= 16 * 8 * MTW (MTW * NT = 8 keeps the register use fixed)
 
-template <int D, int RP, int NT>
-struct RsCfg {
-  static constexpr int QT = 16 * NT;          // queries per block
-  static constexpr int KS = D / 32;           // k-steps over the head dimension
-  static constexpr int RK = RP / 32;          // k-steps over the residual rank
-  static constexpr int BS = D + 16;           // staged B_h row stride (bf16)
-  static constexpr int QFB = NT * KS * 2;     // q~ fragments (16 B per lane) in LDS
-};
-
-// LDS layout (bytes): B_h slice | q~ fragments | group maxima, then one head's scores [QT][N+1] f32 |
-// chosen chunks [QT][64] i16 | per-wave compaction buffer [8][64] i32
-__host__ __device__ inline size_t rs_off_q(int D, int RP) { return (size_t)RP * (D + 16) * 2; }
-__host__ __device__ inline size_t rs_off_z(int D, int RP, int NT) { return rs_off_q(D, RP) + (size_t)NT * (D / 32) * 2 * 1024; }
-__host__ __device__ inline size_t rs_off_r(int D, int RP, int NT, int N) { return rs_off_z(D, RP, NT) + (size_t)16 * NT * (N + 1) * 4; }
-__host__ __device__ inline size_t rs_off_c(int D, int RP, int NT, int N) { return (rs_off_r(D, RP, NT, N) + (size_t)16 * NT * 64 * 2 + 15) & ~(size_t)15; }
-__host__ __device__ inline size_t rs_lds(int D, int RP, int NT, int N) { return rs_off_c(D, RP, NT, N) + kRsWaves * 64 * 4; }
-
-// Global loads are issued ahead of their use: the caller passes this head's
-// B_h pieces (loaded during the previous head) and receives the next head's;
-// the q rows are requested before the barriers; each chunk row tile's s
-// fragments are loaded while the previous tile is multiplied.
-template <int D, int RP>
-struct RsBh {
-  static constexpr int PER = (RP * D / 8 + 64 * kRsWaves - 1) / (64 * kRsWaves);   // 16-byte pieces per thread
-  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
-  u32x4 v[PER];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ Bm, int h, int Hq, int r) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = tid + 64 * kRsWaves * j;
-      const int kk = (8 * e) / D, n = (8 * e) % D;
-      const bool ok = e < RP * D / 8 && kk < r;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(Bm + (size_t)(ok ? kk : 0) * Hq * D + (size_t)h * D + n);
-      v[j] = ok ? t : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* b_s) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = tid + 64 * kRsWaves * j;
-      if (e < RP * D / 8) *reinterpret_cast<u32x4*>(b_s + ((8 * e) / D) * (D + 16) + (8 * e) % D) = v[j];
-    }
-  }
-};
-
-template <int D, int RP, int NT, int MTW, typename Emit>
-__device__ __forceinline__ void rs_head_scores(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bm,
-                                               const bf16_t* __restrict__ sp, const float* __restrict__ H,
-                                               unsigned char* smem, const s16x8 (&uh)[RP / 32],
-                                               const s16x8 (&ul)[RP / 32], RsBh<D, RP>& bh_pre, int h, int h_next,
-                                               int b, int Hq, int N, int q0, int t0, int nq, int r, float scale,
-                                               float beta, Emit&& emit) {
-  typedef RsCfg<D, RP, NT> C;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
+template <int D, int RP, int NT, int P>
+__global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bt, const float* __restrict__ upart, int nsplit,
+    const bf16_t* __restrict__ sp, const float* __restrict__ H, float beta, float scale, int32_t* __restrict__ idx,
+    float* __restrict__ zsel, int B, int Hq, int Hkv, int N, int q0, int nq, int K, int R) {
+  constexpr int QT = 16 * NT, KS = D / 32, RK = RP / 32;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, g16 = lane >> 4, L16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nqb = (nq + QT - 1) / QT;
+  const int tile = xcd_tile(nqb * B * Hkv);   // (batch-group, query block), batch-group major
+  if (tile < 0) return;
+  const int bg = tile / nqb, b = bg / Hkv, g = bg - b * Hkv;
+  const int G = Hq / Hkv;
+  const int t0 = (tile - bg * nqb) * QT;
   const long long L = (long long)N * kSlots;
-  bf16_t* b_s = reinterpret_cast<bf16_t*>(smem);
-  s16x8* qa = reinterpret_cast<s16x8*>(smem + rs_off_q(D, RP));
-  constexpr int PARTS = kRsWaves / NT;
-  constexpr int KSW = (C::KS + PARTS - 1) / PARTS;
-  const int nt = w % NT, ks0 = (w / NT) * KSW;
-  const int tq = t0 + 16 * nt + L16;
-  const bf16_t* qrow = q + ((size_t)b * Hq + h) * L * D + (size_t)slot_of((long long)q0 + (tq < nq ? tq : nq - 1)) * D;
-  // q rows of this wave's part, requested before the barriers
-  s16x4 q4[KSW][2];
+  const int NMT = (N + 15) / 16, ZS = N + 1;
+  uint32_t* zk = reinterpret_cast<uint32_t*>(smem);             // [QT][ZS] group-maximum keys
+  uint8_t* rank_t = smem + rs3_off_r(NT, N);                   // [QT][N]: rank in zsel, 0xFF if not chosen
+  int* chosen = reinterpret_cast<int*>(smem + rs3_off_c(NT, N));
+  for (int e = tid; e < QT * ZS; e += 64 * kRsWaves) zk[e] = 0u;
+  for (int e = tid; e < QT * N / 4; e += 64 * kRsWaves) reinterpret_cast<uint32_t*>(rank_t)[e] = 0xFFFFFFFFu;
+
+  const bool hw = w < G;   // this wave owns head w (wave-uniform)
+  const int h = g * G + (hw ? w : 0);
+
+  // ---- 0. q~ of head h as the scoring B operand, in registers
+  s16x8 qh[NT][KS], ql[NT][KS];
+  if (hw) {
+    s16x8 bt[KS][2][RK];   // B_h^T: d rows 16 (2 ks + half) + L16, ranks 32 rk + 8 g16 + {0..7}
 #pragma unroll
-  for (int kk = 0; kk < KSW; ++kk)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int ks = ks0 + kk < C::KS ? ks0 + kk : C::KS - 1;
-      q4[kk][half] = *reinterpret_cast<const s16x4*>(qrow + 16 * (2 * ks + half) + 4 * g16);
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int rk = 0; rk < RK; ++rk)
+          bt[ks][half][rk] = load8(Bt + ((size_t)h * D + 16 * (2 * ks + half) + L16) * RP + 32 * rk + 8 * g16);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int tq = t0 + 16 * nt + L16;
+      const int tc = tq < nq ? tq : nq - 1;
+      const bf16_t* qrow = q + ((size_t)b * Hq + h) * L * D + (size_t)slot_of((long long)q0 + tc) * D;
+      s16x4 q4[KS][2];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          q4[ks][half] = *reinterpret_cast<const s16x4*>(qrow + 16 * (2 * ks + half) + 4 * g16);
+      s16x8 uh[RK], ul[RK];
+#pragma unroll
+      for (int rk = 0; rk < RK; ++rk) {
+        float uv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) uv[j] = 0.f;
+        for (int sp2 = 0; sp2 < nsplit; ++sp2) {
+          const float* up = upart + (((size_t)sp2 * B + b) * nq + tc) * RP + 32 * rk + 8 * g16;
+          const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uv[j] += a0[j];
+            uv[4 + j] += a1[j];
+          }
+        }
+        if (tq >= nq) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) uv[j] = 0.f;
+        }
+        pack8_split_hw(uv, uh[rk], ul[rk]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float qv[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int rk = 0; rk < RK; ++rk) {
+            acc = mfma16(bt[ks][half][rk], ul[rk], acc);
+            acc = mfma16(bt[ks][half][rk], uh[rk], acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qv[4 * half + i] = acc[i] + bf2f((bf16_t)q4[ks][half][i]);
+        }
+        pack8_split_hw(qv, qh[nt][ks], ql[nt][ks]);
+      }
     }
-  // chunk row tiles of this wave, two at a time; the first pair's s fragments
-  // are requested before the barriers
-  const int NMT = (N + 15) / 16;
-  constexpr int MP = MTW < 2 ? MTW : 2;
-  auto load_s = [&](int m0, s16x8 (&f)[MP][D / 32][2]) {
+  }
+  __syncthreads();   // keys and ranks initialised
+
+  struct TileBuf {
+    s16x8 sf[KS][2];
+    float hv[4];
+    uint32_t rk[NT];
+  };
+  const bf16_t* sph = sp + (size_t)(b * Hq + h) * NMT * KS * 2 * 64 * 8;
+  const bool rk4 = (N & 3) == 0;
+  auto load_tile = [&](int mt, TileBuf& t, bool ranks) {
+    const bf16_t* base = sph + (size_t)mt * KS * 2 * 64 * 8;
 #pragma unroll
-    for (int mm = 0; mm < MP; ++mm) {
-      int mt = w + kRsWaves * (m0 + mm);
-      mt = mt < NMT ? mt : NMT - 1;
-      const int cr = 16 * mt + L16;
-      const bf16_t* srow = sp + (((size_t)b * Hq + h) * N + (cr < N ? cr : N - 1)) * 2 * D;
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        // k order of this lane: d = 32 ks + 4 g16 + {0..3}, then 32 ks + 16 + 4 g16 + {0..3}
-        f[mm][ks][0] = load8(srow + 32 * ks + 8 * g16);
-        f[mm][ks][1] = load8(srow + D + 32 * ks + 8 * g16);
+      for (int pl = 0; pl < 2; ++pl) t.sf[ks][pl] = load8(base + ((ks * 2 + pl) * 64 + lane) * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * mt + 4 * g16 + i;
+      t.hv[i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
+    }
+    if (ranks) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int cb = 16 * mt + 4 * g16;
+        const uint8_t* rr = rank_t + (16 * nt + L16) * N + cb;
+        if (rk4 && cb + 3 < N) {
+          t.rk[nt] = *reinterpret_cast<const uint32_t*>(rr);
+        } else {
+          uint32_t v = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v |= (cb + i < N ? (uint32_t)rr[i] : 0xFFu) << (8 * i);
+          t.rk[nt] = v;
+        }
       }
     }
   };
-  s16x8 scur[MP][D / 32][2];
-  load_s(0, scur);
-
-  lds_barrier();   // previous head: every wave is done with b_s and the q~ fragments
-  bh_pre.store(b_s);
-  if (h_next >= 0) bh_pre.load(Bm, h_next, Hq, r);
-  lds_barrier();
-  // q~^T for query tile nt over k-steps [ks0, ks0 + KSW)
+  auto tile_scores = [&](const TileBuf& t, f32x4 (&zz)[NT]) {
+    f32x4 ahi[NT], ax[NT];
 #pragma unroll
-  for (int kk = 0; kk < KSW; ++kk) {
-    const int ks = ks0 + kk;
-    if (ks >= C::KS) break;
-    float qv[8];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int dm = 2 * ks + half;           // d rows 16 dm .. 16 dm + 15 of q~^T
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int rk = 0; rk < C::RK; ++rk) {
-        const s16x8 bt = lds_col_frag(b_s, C::BS, 32 * rk + 8 * g16, 32 * rk + 8 * g16 + 4, 16 * dm, lane);
-        acc = mfma16(bt, ul[rk], acc);
-        acc = mfma16(bt, uh[rk], acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qv[4 * half + i] = acc[i] + bf2f((bf16_t)q4[kk][half][i]);
+    for (int nt = 0; nt < NT; ++nt) {
+      ahi[nt] = zero4();
+      ax[nt] = zero4();
     }
-    s16x8 hi, lo;
-    pack8_split_hw(qv, hi, lo);
-    qa[((nt * C::KS + ks) * 2 + 0) * 64 + lane] = hi;
-    qa[((nt * C::KS + ks) * 2 + 1) * 64 + lane] = lo;
-  }
-  lds_barrier();
-  // z^T = s q~^T: per k-step the q~ fragments of all query tiles are read once
-  // and feed both chunk row tiles of the pair
-#pragma unroll 1
-  for (int m0 = 0; m0 < MTW; m0 += MP) {
-    if (w + kRsWaves * m0 >= NMT) break;
-    s16x8 snext[MP][D / 32][2];
-    if (m0 + MP < MTW) load_s(m0 + MP, snext);
-    float hv[MP][4];
 #pragma unroll
-    for (int mm = 0; mm < MP; ++mm)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * (w + kRsWaves * (m0 + mm)) + 4 * g16 + i;
-        hv[mm][i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
-      }
-    f32x4 acc_hi[MP][NT], acc_x[MP][NT];
-#pragma unroll
-    for (int mm = 0; mm < MP; ++mm)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        acc_hi[mm][n] = zero4();
-        acc_x[mm][n] = zero4();
+      for (int nt = 0; nt < NT; ++nt) {
+        ax[nt] = mfma16(t.sf[ks][0], ql[nt][ks], ax[nt]);
+        ax[nt] = mfma16(t.sf[ks][1], qh[nt][ks], ax[nt]);
+        ahi[nt] = mfma16(t.sf[ks][0], qh[nt][ks], ahi[nt]);
       }
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      s16x8 bq[NT][2];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        bq[n][0] = qa[((n * C::KS + ks) * 2 + 0) * 64 + lane];
-        bq[n][1] = qa[((n * C::KS + ks) * 2 + 1) * 64 + lane];
+      for (int i = 0; i < 4; ++i) zz[nt][i] = (ahi[nt][i] + ax[nt][i]) * scale - beta * t.hv[i];
+  };
+  // every chunk row tile of the head, the next tile's loads in flight
+  auto sweep = [&](bool ranks, auto&& emit) {
+    TileBuf ta, tb;
+    f32x4 zz[NT];
+    load_tile(0, ta, ranks);
+    for (int mt = 0; mt < NMT; mt += 2) {
+      if (mt + 1 < NMT) load_tile(mt + 1, tb, ranks);
+      tile_scores(ta, zz);
+      emit(mt, ta, zz);
+      if (mt + 1 < NMT) {
+        if (mt + 2 < NMT) load_tile(mt + 2, ta, ranks);
+        tile_scores(tb, zz);
+        emit(mt + 1, tb, zz);
       }
+    }
+  };
+
+  // ---- A: group maximum through LDS atomic max on order-preserving keys
+  if (hw)
+    sweep(false, [&](int mt, const TileBuf&, const f32x4 (&zz)[NT]) {
 #pragma unroll
-      for (int mm = 0; mm < MP; ++mm)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          acc_x[mm][n] = mfma16(scur[mm][ks][0], bq[n][1], acc_x[mm][n]);
-          acc_x[mm][n] = mfma16(scur[mm][ks][1], bq[n][0], acc_x[mm][n]);
-          acc_hi[mm][n] = mfma16(scur[mm][ks][0], bq[n][0], acc_hi[mm][n]);
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * mt + 4 * g16 + i;
+          if (c < N) atomicMax(&zk[(16 * nt + L16) * ZS + c], order_key(zz[nt][i]));
         }
-    }
-#pragma unroll
-    for (int mm = 0; mm < MP; ++mm) {
-      const int m = m0 + mm, mt = w + kRsWaves * m;
-      if (mt >= NMT) break;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        f32x4 zz;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zz[i] = (acc_hi[mm][n][i] + acc_x[mm][n][i]) * scale - beta * hv[mm][i];
-        emit(m, mt, n, zz);
-      }
-    }
-    if (m0 + MP < MTW) {
-#pragma unroll
-      for (int mm = 0; mm < MP; ++mm)
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          scur[mm][ks][0] = snext[mm][ks][0];
-          scur[mm][ks][1] = snext[mm][ks][1];
-        }
-    }
-  }
-}
-
-template <int D, int RP, int NT, int MTW, int P>
-__global__ __launch_bounds__(64 * kRsWaves) void route_score_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bm, const float* __restrict__ upart, int nsplit,
-    const bf16_t* __restrict__ s, const float* __restrict__ H, float beta, float scale, int32_t* __restrict__ idx,
-    float* __restrict__ zsel, int Hq, int Hkv, int N, int q0, int nq, int r, int K, int R) {
-  typedef RsCfg<D, RP, NT> C;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
-  const int bg = blockIdx.y, b = bg / Hkv, g = bg - b * Hkv;
-  const int G = Hq / Hkv;
-  const int t0 = blockIdx.x * C::QT;
-  const int B = gridDim.y / Hkv;
-  float* zt = reinterpret_cast<float*>(smem + rs_off_z(D, RP, NT));
-  short* sel_s = reinterpret_cast<short*>(smem + rs_off_r(D, RP, NT, N));   // [QT][K] chosen, -1 padded
-  int* chosen = reinterpret_cast<int*>(smem + rs_off_c(D, RP, NT, N));
-  const int ZS = N + 1;
-  const int NMT = (N + 15) / 16;
-
-  // u^T operand (rank k-steps) of this wave's query tile, partials summed, split hi + lo
-  s16x8 uh[RP / 32], ul[RP / 32];
-  {
-    const int nt = w % NT;
-    const int tq = t0 + 16 * nt + L16;
-    const int tc = tq < nq ? tq : nq - 1;
-#pragma unroll
-    for (int rk = 0; rk < RP / 32; ++rk) {
-      float uv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) uv[j] = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float* up = upart + (((size_t)sp * B + b) * nq + tc) * RP + 32 * rk + 8 * g16;
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uv[j] += a0[j];
-          uv[4 + j] += a1[j];
-        }
-      }
-      if (tq >= nq) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) uv[j] = 0.f;
-      }
-      pack8_split_hw(uv, uh[rk], ul[rk]);
-    }
-  }
-
-  // ---- A: group maxima
-  f32x4 zmax[MTW][NT];
-#pragma unroll
-  for (int m = 0; m < MTW; ++m)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) zmax[m][n] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  RsBh<D, RP> bh_pre;
-  bh_pre.load(Bm, g * G, Hq, r);
-  for (int hh = 0; hh < G; ++hh)
-    rs_head_scores<D, RP, NT, MTW>(q, Bm, s, H, smem, uh, ul, bh_pre, g * G + hh, g * G + (hh + 1 < G ? hh + 1 : 0),
-                                   b, Hq, N, q0, t0, nq, r, scale, beta,
-                                   [&](int m, int, int n, const f32x4& zz) {
-#pragma unroll
-                                     for (int i = 0; i < 4; ++i) zmax[m][n][i] = fmaxf(zmax[m][n][i], zz[i]);
-                                   });
-#pragma unroll
-  for (int m = 0; m < MTW; ++m) {
-    const int mt = w + kRsWaves * m;
-    if (mt >= NMT) break;
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * mt + 4 * g16 + i;
-        if (c < N) zt[(16 * n + L16) * ZS + c] = zmax[m][n][i];
-      }
-  }
-  for (int e = tid; e < C::QT * K; e += 64 * kRsWaves) sel_s[e] = -1;
+    });
   __syncthreads();
 
-  // ---- B: top-K per query (wave w: queries w, w + 8, ...)
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int qi = w; qi < C::QT; qi += kRsWaves) {
+  // ---- B: top-K per query (wave w: queries w, w + 8, ...) and the rank table
+  for (int qi = w; qi < QT; qi += kRsWaves) {
     const int t = t0 + qi;
     if (t >= nq) break;
     const long long i = (long long)q0 + t;
     uint32_t key[P];
-    int ncand = 0;
 #pragma unroll
     for (int j = 0; j < P; ++j) {
       const int c = 64 * j + lane;
       const bool cand = (c < N) & ((63LL * c + 62 < i - R) | (63LL * c > i + R));
-      const float zv = zt[qi * ZS + (c < N ? c : N - 1)];
-      key[j] = cand ? order_key(zv) : 0u;
-      ncand += __popcll(__ballot(key[j] != 0u));
+      const uint32_t kv = zk[qi * ZS + (c < N ? c : N - 1)];
+      key[j] = cand ? kv : 0u;
     }
-    const bool take_all = ncand <= K;
-    uint32_t theta = 0u;
-    int need = 0;
-    if (!take_all) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t trial = theta | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[j] >= trial));
-        if (cnt >= K) theta = trial;
-      }
-      int gt = 0;
-#pragma unroll
-      for (int j = 0; j < P; ++j) gt += __popcll(__ballot(key[j] > theta));
-      need = K - gt;
-    }
-    int base = 0, ties = 0;
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const bool nz = key[j] != 0u;
-      const bool gt = take_all ? nz : key[j] > theta;
-      const bool eq = !take_all && nz && key[j] == theta;
-      const unsigned long long em = __ballot(eq);
-      const bool take = gt || (eq && ties + __popcll(em & lt) < need);
-      const unsigned long long tm = __ballot(take);
-      if (take) chosen[w * 64 + base + __popcll(tm & lt)] = 64 * j + lane;
-      base += __popcll(tm);
-      ties += __popcll(em);
-    }
+    const int cnt = wave_topk<P>(key, K, lane, [&](int slot, int j) { chosen[w * 64 + slot] = 64 * j + lane; });
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane < K) {
-      const int c = lane < base ? chosen[w * 64 + lane] : -1;
+      const int c = lane < cnt ? chosen[w * 64 + lane] : -1;
       idx[((size_t)bg * nq + t) * K + lane] = c;
-      sel_s[qi * K + lane] = (short)c;
-      if (c < 0)
+      if (c >= 0) rank_t[qi * N + c] = (uint8_t)lane;
+      else
         for (int hh = 0; hh < G; ++hh) zsel[(((size_t)b * Hq + g * G + hh) * nq + t) * K + lane] = -INFINITY;
     }
     __builtin_amdgcn_wave_barrier();
   }
+  __syncthreads();
 
-  // ---- C: every head's score of each chosen chunk: the head's scores go to LDS
-  //      (where the group maxima were), then the chosen ones are gathered into zsel
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    rs_head_scores<D, RP, NT, MTW>(q, Bm, s, H, smem, uh, ul, bh_pre, h, hh + 1 < G ? h + 1 : -1, b, Hq, N, q0, t0,
-                                   nq, r, scale, beta, [&](int, int mt, int n, const f32x4& zz) {
+  // ---- C: the chosen scores of head h straight to zsel
+  if (hw) {
+    float* zrow = zsel + (((size_t)b * Hq + h) * nq + t0) * K;
+    sweep(true, [&](int, const TileBuf& tbuf, const f32x4 (&zz)[NT]) {
 #pragma unroll
-                                     for (int i = 0; i < 4; ++i) {
-                                       const int c = 16 * mt + 4 * g16 + i;
-                                       if (c < N) zt[(16 * n + L16) * ZS + c] = zz[i];
-                                     }
-                                   });
-    lds_barrier();   // the head's scores are complete (the next head's first barrier protects them)
-    for (int e = tid; e < C::QT * K; e += 64 * kRsWaves) {
-      const int qi = e / K, k = e - qi * K, t = t0 + qi;
-      const int c = sel_s[e];
-      if (t < nq && c >= 0) zsel[(((size_t)b * Hq + h) * nq + t) * K + k] = zt[qi * ZS + c];
-    }
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t r8 = (tbuf.rk[nt] >> (8 * i)) & 0xFFu;
+          if (r8 != 0xFFu) zrow[(size_t)(16 * nt + L16) * K + r8] = zz[nt][i];
+        }
+    });
   }
 }
 
@@ -1596,6 +1480,9 @@ static bool small_score_ok(const RouteDims& dm, int r, int nq) {
 static int u_small_splits(int Dh) { return (Dh + kUSmallRows - 1) / kUSmallRows; }
 static int dh_pad(int Dh) { return (Dh + 31) / 32 * 32; }
 static size_t at_bytes(int Dh, int r) { return (size_t)rank_pad(r) * dh_pad(Dh) * 2; }   // A transposed
+static size_t bt_bytes(const RouteDims& dm, int r) { return (size_t)dm.Hq * dm.d * rank_pad(r) * 2; }   // B transposed
+// summaries as fragment-major bf16 hi/lo planes, rows padded to whole 16-chunk tiles
+static size_t frag_bytes(const RouteDims& dm) { return (size_t)dm.B * dm.Hq * ((dm.N + 15) / 16 * 16) * 2 * dm.d * 2; }
 
 size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
@@ -1605,7 +1492,7 @@ size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
            align256(rows_h * dm.N * 4);
   const size_t upart = (size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4;
   if (fused_score_ok(dm, r, nq))
-    return align256(upart) + align256((size_t)dm.B * dm.Hq * dm.N * dm.d * 4) + align256(at_bytes(Dh, r));
+    return align256(upart) + align256(frag_bytes(dm)) + align256(at_bytes(Dh, r)) + align256(bt_bytes(dm, r));
   return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4) + align256(upart);
 }
 
@@ -1616,6 +1503,7 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
   out.splanes = nullptr;
   out.qplanes = nullptr;
   out.at = nullptr;
+  out.bt = nullptr;
   if (small_score_ok(dm, r, nq)) {
     out.qt = nullptr;
     out.upart = (float*)p;
@@ -1634,8 +1522,10 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
     out.upart = (float*)p;
     p += align256((size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4);
     out.splanes = (bf16_t*)p;
-    p += align256((size_t)dm.B * dm.Hq * dm.N * dm.d * 4);
+    p += align256(frag_bytes(dm));
     out.at = (bf16_t*)p;
+    p += align256(at_bytes(Dh, r));
+    out.bt = (bf16_t*)p;
     return out;
   }
   out.qt = (float*)p;
@@ -1712,25 +1602,32 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long rows = (long long)dm.B * dm.Hq * dm.N;
-  hipLaunchKernelGGL((split_summary_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st, s,
-                     ws.splanes, rows);
+  const long long heads = (long long)dm.B * dm.Hq;
+  const long long groups8 = heads * ((dm.N + 15) / 16 * 16) * (D / 8);
+  hipLaunchKernelGGL((split_frag_kernel<D>), dim3((unsigned)((groups8 + 255) / 256)), dim3(256), 0, st, s, ws.splanes,
+                     dm.N, heads);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool wide = dm.N > 256;
-  const int NT = wide ? 2 : 4;
-  const size_t lds = rs_lds(D, RP, NT, dm.N);
-  dim3 grid((nq + 16 * NT - 1) / (16 * NT), dm.B * dm.Hkv);
-#define LCR_RS(NTT, MTW, PP)                                                                                     \
+  const int HD = dm.Hq * D;
+  hipLaunchKernelGGL((transpose_b_kernel<D, RP>), dim3((unsigned)(((long long)HD * RP + 255) / 256)), dim3(256), 0, st,
+                     (const bf16_t*)Bm, r, HD, ws.bt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 32 queries per block: the q~ of the wave's head for them stays in registers
+  const int NT = 2;
+  const size_t lds = rs3_lds(NT, dm.N);
+  const int tiles = (nq + 16 * NT - 1) / (16 * NT) * dm.B * dm.Hkv;
+#define LCR_RS(NTT, PP)                                                                                          \
   do {                                                                                                           \
-    auto kern = route_score_kernel<D, RP, NTT, MTW, PP>;                                                        \
+    auto kern = route_score3_kernel<D, RP, NTT, PP>;                                                            \
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
     if (e != hipSuccess) return e;                                                                               \
-    hipLaunchKernelGGL(kern, grid, dim3(64 * kRsWaves), lds, st, (const bf16_t*)q, (const bf16_t*)Bm, ws.upart, \
-                       nsplit, ws.splanes, H, beta, scale, idx, zsel, dm.Hq, dm.Hkv, dm.N, q0, nq, r, K, radius); \
+    hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * kRsWaves), lds, st, (const bf16_t*)q, ws.bt,      \
+                       ws.upart, nsplit, ws.splanes, H, beta, scale, idx, zsel, dm.B, dm.Hq, dm.Hkv, dm.N, q0, nq, \
+                       K, radius);                                                                               \
   } while (0)
-  if (wide) LCR_RS(2, 4, 8);
-  else LCR_RS(4, 2, 4);
+  if (dm.N <= 256) LCR_RS(2, 4);
+  else LCR_RS(2, 8);
 #undef LCR_RS
   return hipGetLastError();
 }
