@@ -900,19 +900,21 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) zz[nt][i] = (ahi[nt][i] + ax[nt][i]) * scale - beta * t.hv[i];
   };
-  // every chunk row tile of the head, the next tile's loads in flight
+  // every chunk row tile of the head, the next tile's loads in flight; wave w starts
+  // at tile w so that the waves' atomic updates of the group maximum rarely meet
   auto sweep = [&](bool ranks, auto&& emit) {
     TileBuf ta, tb;
     f32x4 zz[NT];
-    load_tile(0, ta, ranks);
-    for (int mt = 0; mt < NMT; mt += 2) {
-      if (mt + 1 < NMT) load_tile(mt + 1, tb, ranks);
+    auto tile_at = [&](int it) { return (w + it) % NMT; };
+    load_tile(tile_at(0), ta, ranks);
+    for (int it = 0; it < NMT; it += 2) {
+      if (it + 1 < NMT) load_tile(tile_at(it + 1), tb, ranks);
       tile_scores(ta, zz);
-      emit(mt, ta, zz);
-      if (mt + 1 < NMT) {
-        if (mt + 2 < NMT) load_tile(mt + 2, ta, ranks);
+      emit(tile_at(it), ta, zz);
+      if (it + 1 < NMT) {
+        if (it + 2 < NMT) load_tile(tile_at(it + 2), ta, ranks);
         tile_scores(tb, zz);
-        emit(mt + 1, tb, zz);
+        emit(tile_at(it + 1), tb, zz);
       }
     }
   };
@@ -1361,13 +1363,15 @@ __device__ __forceinline__ int wave_topk(const uint32_t* key, int K, int lane, E
   uint32_t theta = 0u;
   int need = 0;
   if (!take_all) {
-    // theta = the largest key with at least K keys >= theta, one bit per step
+    // theta = the largest key with at least K keys >= theta, one bit per step; once
+    // exactly K keys reach the threshold, the chosen set (ties included) is fixed
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t trial = theta | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[j] >= trial));
       if (cnt >= K) theta = trial;
+      if (cnt == K) break;
     }
     int gt = 0;
 #pragma unroll
