@@ -786,32 +786,26 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
 //
 // Same tiles and algebra as routed_attention_kernel, with the work of a block
 // split between one producer wave and kPfCons consumer waves so that no wave
-// waits for another one's progress except through the ring of chunk buffers:
-//  - setup (all waves): the ascending list of chunks the block's queries need,
-//    and per list position a mask of the block's queries active on it (window
-//    or selected), built with LDS atomics; each query's chunk logits.
-//  - producer: walks the list in order and moves each chunk into a free slot of
-//    an NBUF-slot pool with direct-to-LDS loads, K and V as separate halves so
-//    that a consumer can start S = K Q^T before V has landed; it publishes the
-//    slot of each position and the number of landed halves.
-//  - consumer w (2 tiles = 4 queries): visits only the positions where one of
-//    its queries is active (found from the masks with ballots, 64 positions at
-//    a time). A slot is free again once every consumer active on its position
-//    is done with it (a per-slot count), so a consumer that is behind holds only
-//    the slots of positions it still needs, not the whole ring.
-// A consumer whose two tiles are both active on a chunk reads each K and V
-// fragment once for both.
-// Block shape: TPC 16-row tiles (2 queries x 8 head rows) per consumer wave.
-// TPC = 1 keeps a consumer under 128 VGPRs, so 16 waves fit a CU (four per
-// SIMD to hide the S -> softmax -> PV chain of each wave); TPC = 2 shares every
-// K and V fragment read between two tiles but allows only 8 waves.
-template <int TPC> struct PfShape {
-  static constexpr int kCons = TPC == 2 ? 7 : 15;              // consumer waves
-  static constexpr int kWaves = kCons + 1;                     // + the producer
-  static constexpr int kQB = 2 * TPC * kCons;                  // queries per block
-  static constexpr unsigned kMask = (1u << (2 * TPC)) - 1u;    // a consumer's bits of a position mask
-};
-constexpr int kPfTPC = 1;   // the shape the planner launches
+// waits for another one's progress except through a pool of chunk halves:
+//  - setup (all waves): the list of chunks the block's queries need (the window
+//    range first, then the rest ascending), per list position a mask of the
+//    block's queries active on it (window or selected), built with LDS atomics,
+//    and each query's chunk logits.
+//  - producer: walks the list in order and moves the K and then the V of each
+//    chunk into free entries of an NH-entry pool with direct-to-LDS loads (an
+//    entry is free once its count of consumers still reading it is zero); it
+//    publishes the entry of each half and the number of landed halves.
+//  - consumer w (one 16-row tile: 2 queries x 8 head rows): visits only the
+//    positions where one of its queries is active (found from the masks with
+//    ballots, 64 positions at a time), forms S = K Q^T once the K half has
+//    landed and releases that entry, then P V once V has landed and releases
+//    V's entry. A consumer that is behind holds only the entries of positions
+//    it still needs, and K is free again long before V.
+// A consumer stays under 128 VGPRs, so 16 waves fit a CU (four per SIMD to hide
+// the S -> softmax -> PV chain of each wave).
+constexpr int kPfCons = 15;             // consumer waves
+constexpr int kPfWaves = kPfCons + 1;   // + the producer
+constexpr int kPfQB = 2 * kPfCons;      // queries per block
 
 
 
@@ -893,19 +887,30 @@ __device__ __forceinline__ void s_tiles(const bf16_t* buf, const QFrag<D, 1>* q,
   }
 }
 
-// O^T += V^T P^T for NT tiles sharing every V^T fragment read.
+// O^T += V^T P^T for NT tiles sharing every V^T fragment read (vbuf: a V half).
+// The swizzle XORs an even key into the 16-byte block index, so the offset of
+// rows r0 + 32 ks + 16 u and columns col + 16 dm is the unswizzled offset of
+// (r0, col) plus (32 ks + 16 u) D plus 16 (dm ^ key): one XOR per column block,
+// the rest immediate offsets. The lane index is formed here by an asm mbcnt that
+// the compiler cannot merge with another, so that it derives the lane constants
+// and the eight column offsets in place instead of keeping them live across the
+// chunk loop, where registers are short.
 template <int D, int NT>
-__device__ __forceinline__ void pv_tiles(const bf16_t* buf, const s16x8 (*pf)[2], f32x4 (*o)[D / 16], int lane) {
+__device__ __forceinline__ void pv_tiles(const bf16_t* vbuf, const s16x8 (*pf)[2], f32x4 (*o)[D / 16]) {
   typedef TileLayout<D, true> TL;
-  const int g16 = lane >> 4, L16 = lane & 15;
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const int r0 = ln >> 2;   // 4 (l / 16) + (l % 16) / 4
+  const int lb0 = r0 * D + 4 * (ln & 3);
+  const int key16 = 8 * TL::swz_v(r0);
+  const bf16_t* base = vbuf + lb0;
 #pragma unroll
   for (int dm = 0; dm < D / 16; ++dm) {
+    const bf16_t* bd = base + (key16 ^ (16 * dm));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int r0 = 32 * ks + 4 * g16 + (L16 >> 2);
-      const int col = 16 * dm + 4 * (L16 & 3);
-      const s16x4 lo = ds_read_tr(buf + TL::KE + TL::v_off(r0, col));
-      const s16x4 hi = ds_read_tr(buf + TL::KE + TL::v_off(r0 + 16, col));
+      const s16x4 lo = ds_read_tr(bd + 32 * ks * D);
+      const s16x4 hi = ds_read_tr(bd + (32 * ks + 16) * D);
       const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int t = 0; t < NT; ++t) o[t][dm] = mfma16(a, pf[t][ks], o[t][dm]);
@@ -962,25 +967,27 @@ __device__ __forceinline__ int lds_load_rel(int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <int D, int NBUF, int TPC>
-__global__ __launch_bounds__(64 * PfShape<TPC>::kWaves) void routed_prefill_kernel(RoutedParams p) {
-  constexpr int kPfCons = PfShape<TPC>::kCons, kPfWaves = PfShape<TPC>::kWaves, kPfQB = PfShape<TPC>::kQB;
-  constexpr unsigned kCMask = PfShape<TPC>::kMask;
+template <int D, int NH>
+__global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedParams p) {
   typedef TileLayout<D, true> TL;
-  constexpr int BUFE = TL::PL;                 // elements per chunk buffer (K then V)
+  static_assert(TL::KE == TL::VE, "K and V halves share one pool");
+  constexpr int HE = TL::KE;                   // elements per half (the K or the V of a chunk)
   constexpr int NI = D / 8;                    // DMA instructions per half
-  constexpr int HF = (63 / NI) < 2 * NBUF ? (63 / NI) : 2 * NBUF;   // halves in flight
+  constexpr int HF = (63 / NI) < NH ? (63 / NI) : NH;   // halves in flight
   static_assert(HF >= 2 && (HF - 1) * NI < 64, "in-flight loads must fit the vmcnt counter");
+  static_assert(NH >= 2 && NH <= 32, "half pool size");
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = p.Hq / p.Hkv;
   bf16_t* kvb = reinterpret_cast<bf16_t*>(smem);
-  float* zs = reinterpret_cast<float*>(smem + (size_t)NBUF * BUFE * sizeof(bf16_t));   // [QB][G][K]
+  float* zs = reinterpret_cast<float*>(smem + (size_t)NH * HE * sizeof(bf16_t));   // [QB][G][K]
   int* pos_chunk = reinterpret_cast<int*>(zs + kPfQB * G * p.K);                      // [N]
   unsigned* pos_mask = reinterpret_cast<unsigned*>(pos_chunk + p.N);                  // [N]
   short* pos_of = reinterpret_cast<short*>(pos_mask + p.N);                           // [N]
+  // after setup, the same bytes hold per position the pool entries of its K (byte 2j) and V (2j + 1)
+  unsigned char* pos_half = reinterpret_cast<unsigned char*>(pos_of);
   __shared__ int s_n;
   __shared__ int s_landed;           // halves landed: K of position j is half 2j, V half 2j + 1
-  __shared__ int s_rem[NBUF];        // consumers still to finish the position held by a slot
+  __shared__ int s_rem[NH];          // consumers still to finish the half held by a pool entry
   __shared__ int s_fail;
   __shared__ int s_nlo[kPfQB];       // per query: selected chunks below the block's window range
   __shared__ int s_nin[kPfQB];       // ... and inside it
@@ -1002,7 +1009,7 @@ __global__ __launch_bounds__(64 * PfShape<TPC>::kWaves) void routed_prefill_kern
     s_landed = 0;
     s_fail = 0;
   }
-  if (tid < NBUF) s_rem[tid] = 0;
+  if (tid < NH) s_rem[tid] = 0;
   if (tid < kPfQB) {
     s_nlo[tid] = 0;
     s_nin[tid] = 0;
@@ -1075,8 +1082,7 @@ __global__ __launch_bounds__(64 * PfShape<TPC>::kWaves) void routed_prefill_kern
     // Its instructions go ahead of the consumers' on the shared SIMD: the whole block
     // runs at the pace of its loads, so their issue must not wait behind softmax work.
     __builtin_amdgcn_s_setprio(3);
-    int h = 0, told = 0;   // told: landed halves already published (monotonic)
-    int slot = 0;
+    int told = 0;   // landed halves already published (monotonic)
     bool ok = true;
     int voffk[4], voffv[4];
 #pragma unroll
@@ -1086,7 +1092,7 @@ __global__ __launch_bounds__(64 * PfShape<TPC>::kWaves) void routed_prefill_kern
     }
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)kvb);
-    // publish the halves below h - HF + 1 once at most HF - 1 of this wave's loads are in flight
+    // publish the halves below hh2 - HF + 1 once at most HF - 1 of this wave's loads are in flight
     auto publish_landed = [&](int hh2) {
       if (hh2 >= HF && hh2 - HF + 1 > told) {
         wait_vm<(HF - 1) * NI>();
@@ -1095,55 +1101,71 @@ __global__ __launch_bounds__(64 * PfShape<TPC>::kWaves) void routed_prefill_kern
         told = hh2 - HF + 1;
       }
     };
-    // Chunks and consumer counts of 64 positions are read lane-parallel up front, and
-    // slots seen free stay known (only this wave allocates them), so that the LDS round
-    // trips between loads are few: a refresh of the slot counts when no slot is known free.
-    unsigned known_free = (1u << NBUF) - 1u;
+    // Any free entry takes the next half. Entries seen free stay known (only this wave
+    // fills them), so the counts are read again only when none is known free. Before
+    // waiting for one, everything issued is awaited and published, so that the
+    // consumers that hold the pool can finish. Returns -1 when the wait gives up or
+    // another wave has failed.
+    unsigned known_free = NH == 32 ? ~0u : (1u << NH) - 1u;
+    auto acquire = [&](int hx) -> int {
+      if (known_free == 0u) {
+        known_free = (unsigned)__ballot(lane < NH && lds_load_rel(&s_rem[lane < NH ? lane : 0]) == 0);
+        if (known_free == 0u) {
+          wait_vm<0>();
+          compiler_fence();
+          if (lane == 0) lds_store_rel(&s_landed, hx);
+          told = hx;
+          int it = 0;
+          for (; it < kSpinLimit && known_free == 0u; ++it) {
+            __builtin_amdgcn_s_sleep(1);
+            known_free = (unsigned)__ballot(lane < NH && lds_load_rel(&s_rem[lane < NH ? lane : 0]) == 0);
+          }
+          if (known_free == 0u || lds_load_rel(&s_fail) != 0) return -1;
+        }
+      }
+      const int e = __builtin_ctz(known_free);
+      known_free &= known_free - 1u;
+      return e;
+    };
+    // Chunks and consumer counts of 64 positions are read lane-parallel up front.
     for (int base = 0; base < n && ok; base += 64) {
       const int pj = base + lane < n ? base + lane : n - 1;
       const int pcl = pos_chunk[pj];
       const unsigned pml = pos_mask[pj];
       int ul = 0;
 #pragma unroll
-      for (int cw = 0; cw < kPfCons; ++cw) ul += ((pml >> (2 * TPC * cw)) & kCMask) != 0u ? 1 : 0;
+      for (int cw = 0; cw < kPfCons; ++cw) ul += ((pml >> (2 * cw)) & 3u) != 0u ? 1 : 0;
       const int cnt = min(64, n - base);
       for (int jj = 0; jj < cnt; ++jj) {
-        const int j = base + jj;
-        h = 2 * j;
-        if (known_free == 0u) {
-          unsigned long long fr = __ballot(lane < NBUF && lds_load_rel(&s_rem[lane < NBUF ? lane : 0]) == 0);
-          if (fr == 0ull) {
-            wait_vm<0>();                     // publish what has landed before waiting
-            compiler_fence();
-            if (lane == 0) lds_store_rel(&s_landed, h);
-            told = h;
-            int it = 0;
-            for (; it < kSpinLimit && fr == 0ull; ++it) {
-              __builtin_amdgcn_s_sleep(1);
-              fr = __ballot(lane < NBUF && lds_load_rel(&s_rem[lane < NBUF ? lane : 0]) == 0);
-            }
-            if (fr == 0ull || lds_load_rel(&s_fail) != 0) {
-              ok = false;
-              break;
-            }
-          }
-          known_free = (unsigned)fr;
-        }
-        slot = __builtin_ctz(known_free);
-        known_free &= known_free - 1u;
+        const int hk = 2 * (base + jj);
         const int users = __builtin_amdgcn_readlane(ul, jj);
-        const int c = __builtin_amdgcn_readlane(pcl, jj);
-        if (lane == 0) {
-          lds_store_rel(&s_rem[slot], users);
-          pos_of[j] = (short)slot;          // published before the halves landed count
+        const size_t off = (size_t)__builtin_amdgcn_readlane(pcl, jj) * kSlots * D;
+        // K, then V, each into an entry of its own: K is released once its users have
+        // formed S, well before they are done with V
+        const int ek = acquire(hk);
+        if (ek < 0) {
+          ok = false;
+          break;
+        }
+        if (lane == 0) {   // both written before the landed count covers the half
+          lds_store_rel(&s_rem[ek], users);
+          pos_half[hk] = (unsigned char)ek;
         }
         compiler_fence();
-        const size_t off = (size_t)c * kSlots * D;
-        const uint32_t lbuf = lds0 + (uint32_t)(slot * BUFE * 2);
-        publish_landed(h);
-        dma_half_fast<D>(kg + off, lbuf, voffk);
-        publish_landed(h + 1);
-        dma_half_fast<D>(vg + off, lbuf + TL::KE * 2, voffv);
+        publish_landed(hk);
+        dma_half_fast<D>(kg + off, lds0 + (uint32_t)(ek * HE * 2), voffk);
+        const int ev = acquire(hk + 1);
+        if (ev < 0) {
+          ok = false;
+          break;
+        }
+        if (lane == 0) {
+          lds_store_rel(&s_rem[ev], users);
+          pos_half[hk + 1] = (unsigned char)ev;
+        }
+        compiler_fence();
+        publish_landed(hk + 1);
+        dma_half_fast<D>(vg + off, lds0 + (uint32_t)(ev * HE * 2), voffv);
       }
     }
     wait_vm<0>();
@@ -1155,183 +1177,112 @@ __global__ __launch_bounds__(64 * PfShape<TPC>::kWaves) void routed_prefill_kern
     return;
   }
 
-  // ---------------- consumer w: queries 2 TPC w .. 2 TPC w + 2 TPC - 1 of the block
+  // ---------------- consumer w: queries 2w and 2w + 1 of the block, one 16-row tile
   const int qq = (lane & 15) >> 3, hh = lane & 7;
   const int h = g * G + hh;
-  const int qw = 2 * TPC * w;   // the wave's first query in the block
-  QFrag<D, 1> qf[TPC];
-  f32x4 acc[TPC][D / 16];
-  float mrow[TPC], lrow[TPC];
-  int ptr[TPC], tq[TPC];
-  bool rv[TPC];
-  int iq[TPC];   // content indices fit in 32 bits (N < 32768 on this path)
+  const int qb = 2 * w + qq;                 // this lane's query in the block
+  const int tq = tb0 + qb;
+  const int iq = p.q0 + tq;                  // content indices fit in 32 bits (N < 32768 on this path)
+  const bool rv = tq < p.nq && hh < G;
   const int R32 = (int)min((long long)p.R, Tcont);   // a wider radius selects the same keys
+  QFrag<D, 1> qf;
+  load_qfrag<bf16_t, D, 1>(qf, rv ? reinterpret_cast<const bf16_t*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D
+                                  : nullptr, lane);
+  f32x4 acc[D / 16];
 #pragma unroll
-  for (int tt = 0; tt < TPC; ++tt) {
-    tq[tt] = tb0 + qw + 2 * tt + qq;
-    iq[tt] = p.q0 + tq[tt];
-    rv[tt] = tq[tt] < p.nq && hh < G;
-    const bf16_t* qrow = rv[tt] ? reinterpret_cast<const bf16_t*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq[tt])) * D
-                                : nullptr;
-    load_qfrag<bf16_t, D, 1>(qf[tt], qrow, lane);
-#pragma unroll
-    for (int dm = 0; dm < D / 16; ++dm) acc[tt][dm] = zero4();
-    mrow[tt] = kNegBig;
-    lrow[tt] = 0.f;
-    ptr[tt] = 0;
-  }
-  const float* zrow[TPC];
-  int nlo[TPC], nin[TPC];
-#pragma unroll
-  for (int tt = 0; tt < TPC; ++tt) {
-    zrow[tt] = zs + ((qw + 2 * tt + qq) * G + (hh < G ? hh : 0)) * p.K;
-    nlo[tt] = s_nlo[qw + 2 * tt + qq];
-    nin[tt] = s_nin[qw + 2 * tt + qq];
-  }
+  for (int dm = 0; dm < D / 16; ++dm) acc[dm] = zero4();
+  float mrow = kNegBig, lrow = 0.f;
+  int ptr = 0;   // selected chunks of this lane's query visited so far
+  const float* zrow = zs + (qb * G + (hh < G ? hh : 0)) * p.K;
+  const int nlo = s_nlo[qb], nin = s_nin[qb];
+  // landed halves known to this wave: the count is read again only when it falls short
+  int seen = 0;
+  auto await = [&](int need) -> bool {
+    int it = 0;
+    while (seen < need) {
+      seen = lds_load_rel(&s_landed);
+      if (seen >= need) break;
+      if (++it == kSpinLimit || lds_load_rel(&s_fail) != 0) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    compiler_fence();
+    return true;
+  };
+  // every LDS read of entry e has returned: release it
+  auto release = [&](int e) {
+    wait_lgkm0();
+    compiler_fence();
+    if (lane == 0) __hip_atomic_fetch_add(&s_rem[e], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
   bool failed = false;
   for (int base = 0; base < n && !failed; base += 64) {
     const int pl = base + lane < n ? base + lane : n - 1;
     const unsigned pm = base + lane < n ? pos_mask[pl] : 0u;
     const int pc = pos_chunk[pl];
-    unsigned long long mine = __ballot(((pm >> qw) & kCMask) != 0u);
+    unsigned long long mine = __ballot(((pm >> (2 * w)) & 3u) != 0u);
     while (mine != 0ull) {
       const int bit = __builtin_ctzll(mine);
       mine &= mine - 1ull;
       const int j = base + bit;
       const int c = __builtin_amdgcn_readlane(pc, bit);
-      const unsigned bits = (unsigned)__builtin_amdgcn_readlane((int)pm, bit) >> qw;
-      // per tile and lane: window keys, selected chunk, or nothing
-      const int cf = c * kContent;
-      int mode[TPC], lo[TPC], hi[TPC];
-      float zc[TPC];
-      bool act[TPC], anywin = false;
-#pragma unroll
-      for (int tt = 0; tt < TPC; ++tt) {
-        act[tt] = ((bits >> (2 * tt)) & 3u) != 0u;
-        const bool qa = ((bits >> (2 * tt + qq)) & 1u) != 0u;
-        const int rel = iq[tt] - cf;   // query index relative to the chunk's first key
-        const bool win = rel + R32 >= 0 && rel - R32 <= kContent - 1;
-        mode[tt] = (!qa || !rv[tt]) ? 0 : (win ? 1 : 2);
-        lo[tt] = mode[tt] == 1 ? max(0, rel - R32) : 0;
-        hi[tt] = mode[tt] == 1 ? min(kContent - 1, rel + R32) : kContent - 1;
-        zc[tt] = 0.f;
-        if (p.K > 0) {   // K uniform
-          // the v-th selected chunk visited: the list walks the window range, then the
-          // chunks below it, then those above, each ascending, while zsel is ascending
-          const int v = ptr[tt];
-          int ks = v < nin[tt] ? nlo[tt] + v : (v < nin[tt] + nlo[tt] ? v - nin[tt] : v);
-          zc[tt] = zrow[tt][ks < p.K ? ks : p.K - 1];
-        }
-        if (qa && !win) ++ptr[tt];
-        anywin = anywin || (__ballot(mode[tt] == 1) != 0ull);
+      const unsigned bits = (unsigned)__builtin_amdgcn_readlane((int)pm, bit) >> (2 * w);
+      // per lane: window keys, selected chunk, or nothing
+      const bool qa = ((bits >> qq) & 1u) != 0u;
+      const int rel = iq - c * kContent;   // query index relative to the chunk's first key
+      const bool win = rel + R32 >= 0 && rel - R32 <= kContent - 1;
+      const int mode = (!qa || !rv) ? 0 : (win ? 1 : 2);
+      const int lo = mode == 1 ? max(0, rel - R32) : 0;
+      const int hi = mode == 1 ? min(kContent - 1, rel + R32) : kContent - 1;
+      float zc = 0.f;
+      if (p.K > 0) {   // K uniform
+        // the v-th selected chunk visited: the list walks the window range, then the
+        // chunks below it, then those above, each ascending, while zsel is ascending
+        const int v = ptr;
+        const int ks = v < nin ? nlo + v : (v < nin + nlo ? v - nin : v);
+        zc = zrow[ks < p.K ? ks : p.K - 1];
       }
-      // K of position j landed?
-      {
-        int it = 0;
-        while (lds_load_rel(&s_landed) < 2 * j + 1 && it < kSpinLimit) {
-          __builtin_amdgcn_s_sleep(1);
-          ++it;
-        }
-        if (it == kSpinLimit || lds_load_rel(&s_fail) != 0) {
-          failed = true;
-          break;
-        }
-      }
-      compiler_fence();
-      const int slot = pos_of[j];   // written by the producer before the landed count
-      const bf16_t* buf = kvb + slot * BUFE;
-      // one tile: the same code for tile 0 or tile 1, chosen by a uniform branch
-      auto single = [&](auto tile) -> bool {
-        constexpr int tt = decltype(tile)::value;
-        f32x4 sacc[1][4];
-        s_tiles<D, 1>(buf, &qf[tt], sacc, lane);
-        s16x8 pf[1][2];
-        const float alpha = anywin ? tile_softmax<true>(sacc[0], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16,
-                                                        mrow[tt], lrow[tt], pf[0])
-                                   : tile_softmax<false>(sacc[0], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16,
-                                                         mrow[tt], lrow[tt], pf[0]);
-        if (__ballot(alpha != 1.f) != 0ull) {
-#pragma unroll
-          for (int dm = 0; dm < D / 16; ++dm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
-        }
-        int it = 0;
-        while (lds_load_rel(&s_landed) < 2 * j + 2 && it < kSpinLimit) {
-          __builtin_amdgcn_s_sleep(1);
-          ++it;
-        }
-        if (it == kSpinLimit) return false;
-        compiler_fence();
-        pv_tiles<D, 1>(buf, pf, &acc[tt], lane);
-        return true;
-      };
-      // both tiles: every K and V fragment read serves the two of them
-      auto fused = [&](auto) -> bool {
-        f32x4 sacc[2][4];
-        s_tiles<D, 2>(buf, qf, sacc, lane);
-        s16x8 pf[2][2];
-        float alpha[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          alpha[tt] = anywin ? tile_softmax<true>(sacc[tt], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16, mrow[tt],
-                                                  lrow[tt], pf[tt])
-                             : tile_softmax<false>(sacc[tt], mode[tt], lo[tt], hi[tt], zc[tt], p.sl2, g16, mrow[tt],
-                                                   lrow[tt], pf[tt]);
-          if (__ballot(alpha[tt] != 1.f) != 0ull) {
-#pragma unroll
-            for (int dm = 0; dm < D / 16; ++dm)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha[tt];
-          }
-        }
-        {
-          int it = 0;
-          while (lds_load_rel(&s_landed) < 2 * j + 2 && it < kSpinLimit) {
-            __builtin_amdgcn_s_sleep(1);
-            ++it;
-          }
-          if (it == kSpinLimit) return false;
-        }
-        compiler_fence();
-        pv_tiles<D, 2>(buf, pf, acc, lane);
-        return true;
-      };
-      bool done;
-      if constexpr (TPC == 2) {
-        done = (act[0] && act[1]) ? fused(0)
-                                  : (act[0] ? single(std::integral_constant<int, 0>{})
-                                            : single(std::integral_constant<int, 1>{}));
-      } else {
-        done = single(std::integral_constant<int, 0>{});
-      }
-      if (!done) {
+      if (qa && !win) ++ptr;
+      const bool anywin = __ballot(mode == 1) != 0ull;
+      if (!await(2 * j + 1)) {
         failed = true;
         break;
       }
-      // every LDS read of the slot has returned: release it
-      wait_lgkm0();
-      compiler_fence();
-      if (lane == 0) __hip_atomic_fetch_add(&s_rem[slot], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const int ek = pos_half[2 * j];   // written by the producer before the landed count covered it
+      f32x4 sacc[1][4];
+      s_tiles<D, 1>(kvb + ek * HE, &qf, sacc, lane);
+      release(ek);
+      s16x8 pf[1][2];
+      const float alpha = anywin ? tile_softmax<true>(sacc[0], mode, lo, hi, zc, p.sl2, g16, mrow, lrow, pf[0])
+                                 : tile_softmax<false>(sacc[0], mode, lo, hi, zc, p.sl2, g16, mrow, lrow, pf[0]);
+      if (__ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+        for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[dm][i] *= alpha;
+      }
+      if (!await(2 * j + 2)) {
+        failed = true;
+        break;
+      }
+      const int ev = pos_half[2 * j + 1];
+      pv_tiles<D, 1>(kvb + ev * HE, pf, &acc);
+      release(ev);
     }
   }
   if (failed && lane == 0) lds_store_rel(&s_fail, 1);
 
   // ---- results
-#pragma unroll
-  for (int tt = 0; tt < TPC; ++tt) {
-    if (!rv[tt]) continue;
-    const float inv = 1.f / lrow[tt];
-    bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq[tt])) * D;
+  if (rv) {
+    const float inv = 1.f / lrow;
+    bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D;
 #pragma unroll
     for (int dm = 0; dm < D / 16; ++dm) {
       float v4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v4[i] = acc[tt][dm][i] * inv;
+      for (int i = 0; i < 4; ++i) v4[i] = acc[dm][i] * inv;
       store4<bf16_t>(orow + 16 * dm + 4 * g16, v4);
     }
-    if (p.lse != nullptr && g16 == 0)
-      p.lse[((size_t)b * p.Hq + h) * p.nq + tq[tt]] = (mrow[tt] + __log2f(lrow[tt])) * kLn2;
+    if (p.lse != nullptr && g16 == 0) p.lse[((size_t)b * p.Hq + h) * p.nq + tq] = (mrow + __log2f(lrow)) * kLn2;
   }
 }
 
@@ -1768,11 +1719,11 @@ static size_t routed_lds(const RouteDims& dm, int K, int qblock, int waves) {
   return (b + 15) & ~(size_t)15;
 }
 
-// LDS of routed_prefill_kernel: the ring, the block's chunk logits and the
-// per-position tables (chunk, query mask, position of each chunk).
-static size_t prefill_lds(const RouteDims& dm, int K, int nbuf) {
+// LDS of routed_prefill_kernel: the pool of nh K-or-V halves, the block's chunk
+// logits and the per-position tables (chunk, query mask, position of each chunk).
+static size_t prefill_lds(const RouteDims& dm, int K, int nh) {
   const int G = dm.Hq / dm.Hkv;
-  const size_t b = (size_t)nbuf * 2 * 64 * dm.d * 2 + (size_t)PfShape<kPfTPC>::kQB * G * K * 4 +
+  const size_t b = (size_t)nh * 64 * dm.d * 2 + (size_t)kPfQB * G * K * 4 +
                    (size_t)dm.N * (4 + 4 + 2);
   return (b + 15) & ~(size_t)15;
 }
@@ -1833,15 +1784,15 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   }
   pl.nbuf = 0;
   if (pl.kind == 0 && pl.nsplit == 1 && dm.dtype == 1 && dm.N < 32768) {
-    // bf16 prefill: producer / consumer kernel with the deepest ring that fits
-    for (int nb = 4; nb >= 2; --nb) {
-      const size_t lds = prefill_lds(dm, K, nb);
+    // bf16 prefill: producer / consumer kernel with the largest pool of halves that fits
+    for (int nh = 8; nh >= 4; nh -= 2) {
+      const size_t lds = prefill_lds(dm, K, nh);
       if (lds <= routed_lds_limit()) {
         pl.kind = 2;
-        pl.nbuf = nb;
-        pl.waves = PfShape<kPfTPC>::kWaves;
+        pl.nbuf = nh;
+        pl.waves = kPfWaves;
         pl.tiles = 2;
-        pl.qblock = PfShape<kPfTPC>::kQB;
+        pl.qblock = kPfQB;
         pl.lds = lds;
         break;
       }
@@ -1893,21 +1844,21 @@ static hipError_t launch_decode_t(const RouteDims& dm, const AttnPlan& pl, const
   return hipGetLastError();
 }
 
-template <int D, int NBUF>
+template <int D, int NH>
 static hipError_t launch_prefill_t(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
-  auto kern = routed_prefill_kernel<D, NBUF, kPfTPC>;
+  auto kern = routed_prefill_kernel<D, NH>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
   if (e != hipSuccess) return e;
-  const int tiles = (prm.nq + PfShape<kPfTPC>::kQB - 1) / PfShape<kPfTPC>::kQB * dm.B * dm.Hkv;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * PfShape<kPfTPC>::kWaves), pl.lds, st, prm);
+  const int tiles = (prm.nq + kPfQB - 1) / kPfQB * dm.B * dm.Hkv;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * kPfWaves), pl.lds, st, prm);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_prefill_d(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
-  if (pl.nbuf >= 4) return launch_prefill_t<D, 4>(dm, pl, prm, st);
-  if (pl.nbuf == 3) return launch_prefill_t<D, 3>(dm, pl, prm, st);
-  return launch_prefill_t<D, 2>(dm, pl, prm, st);
+  if (pl.nbuf >= 8) return launch_prefill_t<D, 8>(dm, pl, prm, st);
+  if (pl.nbuf >= 6) return launch_prefill_t<D, 6>(dm, pl, prm, st);
+  return launch_prefill_t<D, 4>(dm, pl, prm, st);
 }
 
 hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, const void* q, const void* k,

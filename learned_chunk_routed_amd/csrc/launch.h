@@ -44,7 +44,7 @@ struct AttnPlan {
   int nsplit;      // partials per query row, merged by combine_kernel when > 1
   int kind;        // 0: blocks walk a chunk list; 1: one block per (2-query tile, chunk entry);
                    // 2: producer / consumer waves over a chunk ring (bf16 prefill)
-  int nbuf;        // ring slots of kind 2
+  int nbuf;        // kind 2: K-or-V halves in the LDS pool
   int nent;        // kind 1: entries per 2-query tile (2K selected + window chunks)
   int epb;         // kind 1: entries per block (nsplit = ceil(nent / epb) runs)
   size_t lds;      // dynamic LDS bytes per block
