@@ -789,8 +789,7 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
 // waits for another one's progress except through a pool of chunk halves:
 //  - setup (all waves): the list of chunks the block's queries need (the window
 //    range first, then the rest ascending), per list position a mask of the
-//    block's queries active on it (window or selected), built with LDS atomics,
-//    and each query's chunk logits.
+//    block's queries active on it (window or selected), built with LDS atomics.
 //  - producer: walks the list in order and moves the K and then the V of each
 //    chunk into free entries of an NH-entry pool with direct-to-LDS loads (an
 //    entry is free once its count of consumers still reading it is zero); it
@@ -800,7 +799,9 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
 //    ballots, 64 positions at a time), forms S = K Q^T once the K half has
 //    landed and releases that entry, then P V once V has landed and releases
 //    V's entry. A consumer that is behind holds only the entries of positions
-//    it still needs, and K is free again long before V.
+//    it still needs, and K is free again long before V. The chunk logit of a
+//    lane's next selected chunk is loaded from zsel one visit ahead, so LDS
+//    holds only the pool and the position tables.
 // A consumer stays under 128 VGPRs, so 16 waves fit a CU (four per SIMD to hide
 // the S -> softmax -> PV chain of each wave).
 constexpr int kPfCons = 15;             // consumer waves
@@ -979,8 +980,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = p.Hq / p.Hkv;
   bf16_t* kvb = reinterpret_cast<bf16_t*>(smem);
-  float* zs = reinterpret_cast<float*>(smem + (size_t)NH * HE * sizeof(bf16_t));   // [QB][G][K]
-  int* pos_chunk = reinterpret_cast<int*>(zs + kPfQB * G * p.K);                      // [N]
+  int* pos_chunk = reinterpret_cast<int*>(smem + (size_t)NH * HE * sizeof(bf16_t));   // [N]
   unsigned* pos_mask = reinterpret_cast<unsigned*>(pos_chunk + p.N);                  // [N]
   short* pos_of = reinterpret_cast<short*>(pos_mask + p.N);                           // [N]
   // after setup, the same bytes hold per position the pool entries of its K (byte 2j) and V (2j + 1)
@@ -1004,7 +1004,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (size_t)bg * L * D;
   constexpr int NT = 64 * kPfWaves;
 
-  // ---- setup: chunk list, per-position query masks, chunk logits
+  // ---- setup: chunk list and per-position query masks
   if (tid == 0) {
     s_landed = 0;
     s_fail = 0;
@@ -1029,11 +1029,6 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
       if (c < cw0) atomicAdd(&s_nlo[qi], 1);
       else if (c <= cw1) atomicAdd(&s_nin[qi], 1);
     }
-  }
-  for (int e = tid; e < kPfQB * G * p.K; e += NT) {
-    const int qi = e / (G * p.K), rem = e - qi * G * p.K, hh2 = rem / p.K, kk = rem - hh2 * p.K;
-    const int t = tb0 + qi;
-    zs[e] = (t < p.nq) ? p.zsel[(((size_t)b * p.Hq + g * G + hh2) * p.nq + t) * p.K + kk] * kLog2e : 0.f;
   }
   __syncthreads();
   if (w == 0) {
@@ -1193,8 +1188,17 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   for (int dm = 0; dm < D / 16; ++dm) acc[dm] = zero4();
   float mrow = kNegBig, lrow = 0.f;
   int ptr = 0;   // selected chunks of this lane's query visited so far
-  const float* zrow = zs + (qb * G + (hh < G ? hh : 0)) * p.K;
   const int nlo = s_nlo[qb], nin = s_nin[qb];
+  // the chunk logits of this lane's row stay in HBM / L2: the one for the next selected
+  // chunk is loaded a visit ahead (rows past the tile's queries or heads read a valid row)
+  const float* zrow = p.zsel + (((size_t)b * p.Hq + (hh < G ? h : g * G)) * p.nq + (tq < p.nq ? tq : p.nq - 1)) * p.K;
+  // the v-th selected chunk visited: the list walks the window range, then the chunks
+  // below it, then those above, each ascending, while zsel is ascending
+  auto zsel_slot = [&](int v) {
+    const int ks = v < nin ? nlo + v : (v < nin + nlo ? v - nin : v);
+    return ks < p.K ? ks : p.K - 1;
+  };
+  float znext = p.K > 0 ? zrow[zsel_slot(0)] : 0.f;
   // landed halves known to this wave: the count is read again only when it falls short
   int seen = 0;
   auto await = [&](int need) -> bool {
@@ -1233,15 +1237,11 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
       const int mode = (!qa || !rv) ? 0 : (win ? 1 : 2);
       const int lo = mode == 1 ? max(0, rel - R32) : 0;
       const int hi = mode == 1 ? min(kContent - 1, rel + R32) : kContent - 1;
-      float zc = 0.f;
-      if (p.K > 0) {   // K uniform
-        // the v-th selected chunk visited: the list walks the window range, then the
-        // chunks below it, then those above, each ascending, while zsel is ascending
-        const int v = ptr;
-        const int ks = v < nin ? nlo + v : (v < nin + nlo ? v - nin : v);
-        zc = zrow[ks < p.K ? ks : p.K - 1];
+      const float zc = znext * kLog2e;
+      if (qa && !win) {
+        ++ptr;
+        znext = zrow[zsel_slot(ptr)];   // lands while this chunk is processed
       }
-      if (qa && !win) ++ptr;
       const bool anywin = __ballot(mode == 1) != 0ull;
       if (!await(2 * j + 1)) {
         failed = true;
@@ -1719,12 +1719,10 @@ static size_t routed_lds(const RouteDims& dm, int K, int qblock, int waves) {
   return (b + 15) & ~(size_t)15;
 }
 
-// LDS of routed_prefill_kernel: the pool of nh K-or-V halves, the block's chunk
-// logits and the per-position tables (chunk, query mask, position of each chunk).
-static size_t prefill_lds(const RouteDims& dm, int K, int nh) {
-  const int G = dm.Hq / dm.Hkv;
-  const size_t b = (size_t)nh * 64 * dm.d * 2 + (size_t)kPfQB * G * K * 4 +
-                   (size_t)dm.N * (4 + 4 + 2);
+// LDS of routed_prefill_kernel: the pool of nh K-or-V halves and the per-position
+// tables (chunk, query mask, position of each chunk).
+static size_t prefill_lds(const RouteDims& dm, int nh) {
+  const size_t b = (size_t)nh * 64 * dm.d * 2 + (size_t)dm.N * (4 + 4 + 2);
   return (b + 15) & ~(size_t)15;
 }
 
@@ -1785,8 +1783,8 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   pl.nbuf = 0;
   if (pl.kind == 0 && pl.nsplit == 1 && dm.dtype == 1 && dm.N < 32768) {
     // bf16 prefill: producer / consumer kernel with the largest pool of halves that fits
-    for (int nh = 8; nh >= 4; nh -= 2) {
-      const size_t lds = prefill_lds(dm, K, nh);
+    for (int nh : {9, 8, 6, 4}) {
+      const size_t lds = prefill_lds(dm, nh);
       if (lds <= routed_lds_limit()) {
         pl.kind = 2;
         pl.nbuf = nh;
@@ -1856,6 +1854,7 @@ static hipError_t launch_prefill_t(const RouteDims& dm, const AttnPlan& pl, cons
 
 template <int D>
 static hipError_t launch_prefill_d(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
+  if (pl.nbuf >= 9) return launch_prefill_t<D, 9>(dm, pl, prm, st);
   if (pl.nbuf >= 8) return launch_prefill_t<D, 8>(dm, pl, prm, st);
   if (pl.nbuf >= 6) return launch_prefill_t<D, 6>(dm, pl, prm, st);
   return launch_prefill_t<D, 4>(dm, pl, prm, st);
