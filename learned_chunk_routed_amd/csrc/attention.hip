@@ -270,6 +270,25 @@ __device__ __forceinline__ void pv_tile(const bf16_t* buf, const float p[4][4], 
   }
 }
 
+// The same product for bf16 tiles with P already packed as the B operand (pf[ks]:
+// keys 32 ks + 4 (l / 16) + {0..3} and 32 ks + 16 + 4 (l / 16) + {0..3}).
+template <int D, bool SWZ>
+__device__ __forceinline__ void pv_tile_pf(const bf16_t* buf, const s16x8 pf[2], f32x4 o[D / 16], int lane) {
+  typedef TileLayout<D, SWZ> TL;
+  const int g16 = lane >> 4, L16 = lane & 15;
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r0 = 32 * ks + 4 * g16 + (L16 >> 2);
+      const int col = 16 * dm + 4 * (L16 & 3);
+      const s16x4 lo = ds_read_tr(buf + TL::KE + TL::v_off(r0, col));
+      const s16x4 hi = ds_read_tr(buf + TL::KE + TL::v_off(r0 + 16, col));
+      o[dm] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[dm]);
+    }
+  }
+}
+
 // Online-softmax update of one 16-row tile for one chunk (or band tile).
 // mode 1: window keys (logits of in-window content keys); mode 2: selected
 // chunk (its 63 content keys normalised inside the chunk, then weighted by
@@ -812,7 +831,7 @@ constexpr int kPfQB = 2 * kPfCons;      // queries per block
 
 // Softmax update of a bf16 tile (see tile_update_bf16); WINDOW selects at
 // compile time whether per-key window bounds are applied.
-template <bool WINDOW>
+template <bool WINDOW, bool MASK63 = true>
 __device__ __forceinline__ float tile_softmax(f32x4 sacc[4], int mode, int lo, int hi, float zc, float sl2, int g16,
                                               float& m, float& l, s16x8 pf[2]) {
   if constexpr (WINDOW) {
@@ -823,7 +842,7 @@ __device__ __forceinline__ float tile_softmax(f32x4 sacc[4], int mode, int lo, i
         const int key = 16 * mt + 4 * g16 + i;
         sacc[mt][i] = (key >= lo && key <= hi) ? sacc[mt][i] : -INFINITY;
       }
-  } else {
+  } else if constexpr (MASK63) {
     if (g16 == 3) sacc[3][3] = -INFINITY;   // chunk slot 63: the routing mask, never a key
   }
   float mx = max3(sacc[0][0], sacc[0][1], max2(sacc[0][2], sacc[0][3]));
@@ -1654,20 +1673,35 @@ __global__ __launch_bounds__(512) void swa_kernel(SwaParams p) {
       if (kb > ts + 15 + p.R || kb + 63 < ts - p.R || ts >= L) continue;
       f32x4 sacc[4];
       s_tile<D, NP, false>(buf, qf[tt], sacc, lane);
-      float x[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
       const int mode = trow[tt] < L ? 1 : 0;
       const int lo = (int)max(0LL, trow[tt] - p.R - kb);
       const int hi = (int)min(63LL, min(L - 1, trow[tt] + p.R) - kb);
-      const float alpha = tile_update(x, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt]);
+      if constexpr (NP == 1) {
+        // a tile inside the window of all 16 rows (and of the sequence) needs no mask
+        const bool inside = kb >= ts + 15 - p.R && kb + 63 <= ts + p.R && kb + 63 < L && ts + 15 < L;
+        s16x8 pf[2];
+        const float alpha = inside ? tile_softmax<false, false>(sacc, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf)
+                                   : tile_softmax<true, false>(sacc, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf);
+        if (__ballot(alpha != 1.f) != 0ull) {
 #pragma unroll
-      for (int dm = 0; dm < D / 16; ++dm)
+          for (int dm = 0; dm < D / 16; ++dm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
-      pv_tile<D, NP, false>(buf, x, acc[tt], lane);
+            for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+        }
+        pv_tile_pf<D, false>(buf, pf, acc[tt], lane);
+      } else {
+        float x[4][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
+        const float alpha = tile_update(x, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt]);
+#pragma unroll
+        for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+        pv_tile<D, NP, false>(buf, x, acc[tt], lane);
+      }
     }
   }
 
