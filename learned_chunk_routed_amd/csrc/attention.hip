@@ -270,25 +270,6 @@ __device__ __forceinline__ void pv_tile(const bf16_t* buf, const float p[4][4], 
   }
 }
 
-// The same product for bf16 tiles with P already packed as the B operand (pf[ks]:
-// keys 32 ks + 4 (l / 16) + {0..3} and 32 ks + 16 + 4 (l / 16) + {0..3}).
-template <int D, bool SWZ>
-__device__ __forceinline__ void pv_tile_pf(const bf16_t* buf, const s16x8 pf[2], f32x4 o[D / 16], int lane) {
-  typedef TileLayout<D, SWZ> TL;
-  const int g16 = lane >> 4, L16 = lane & 15;
-#pragma unroll
-  for (int dm = 0; dm < D / 16; ++dm) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int r0 = 32 * ks + 4 * g16 + (L16 >> 2);
-      const int col = 16 * dm + 4 * (L16 & 3);
-      const s16x4 lo = ds_read_tr(buf + TL::KE + TL::v_off(r0, col));
-      const s16x4 hi = ds_read_tr(buf + TL::KE + TL::v_off(r0 + 16, col));
-      o[dm] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[dm]);
-    }
-  }
-}
-
 // Online-softmax update of one 16-row tile for one chunk (or band tile).
 // mode 1: window keys (logits of in-window content keys); mode 2: selected
 // chunk (its 63 content keys normalised inside the chunk, then weighted by
@@ -835,13 +816,13 @@ template <bool WINDOW, bool MASK63 = true>
 __device__ __forceinline__ float tile_softmax(f32x4 sacc[4], int mode, int lo, int hi, float zc, float sl2, int g16,
                                               float& m, float& l, s16x8 pf[2]) {
   if constexpr (WINDOW) {
+    // key 16 mt + 4 g16 + i is kept when lo <= key <= hi: the constant 16 mt + i is
+    // compared with bounds shifted by the lane's 4 g16 (no per-key registers)
+    const int los = lo - 4 * g16, his = hi - 4 * g16;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * mt + 4 * g16 + i;
-        sacc[mt][i] = (key >= lo && key <= hi) ? sacc[mt][i] : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i) sacc[mt][i] = (16 * mt + i >= los && 16 * mt + i <= his) ? sacc[mt][i] : -INFINITY;
   } else if constexpr (MASK63) {
     if (g16 == 3) sacc[3][3] = -INFINITY;   // chunk slot 63: the routing mask, never a key
   }
@@ -1597,6 +1578,9 @@ __global__ __launch_bounds__(64) void routed_decode_kernel(RoutedParams p) {
 }
 
 // ---------------------------------------------------------------- sliding-window attention
+//
+// swa_kernel serves float32 inputs (three bf16 planes staged through registers);
+// swa_bf16_kernel below serves bf16 inputs.
 
 struct SwaParams {
   const void* q;
@@ -1676,32 +1660,17 @@ __global__ __launch_bounds__(512) void swa_kernel(SwaParams p) {
       const int mode = trow[tt] < L ? 1 : 0;
       const int lo = (int)max(0LL, trow[tt] - p.R - kb);
       const int hi = (int)min(63LL, min(L - 1, trow[tt] + p.R) - kb);
-      if constexpr (NP == 1) {
-        // a tile inside the window of all 16 rows (and of the sequence) needs no mask
-        const bool inside = kb >= ts + 15 - p.R && kb + 63 <= ts + p.R && kb + 63 < L && ts + 15 < L;
-        s16x8 pf[2];
-        const float alpha = inside ? tile_softmax<false, false>(sacc, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf)
-                                   : tile_softmax<true, false>(sacc, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf);
-        if (__ballot(alpha != 1.f) != 0ull) {
+      float x[4][4];
 #pragma unroll
-          for (int dm = 0; dm < D / 16; ++dm)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
-        }
-        pv_tile_pf<D, false>(buf, pf, acc[tt], lane);
-      } else {
-        float x[4][4];
+        for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
+      const float alpha = tile_update(x, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+      for (int dm = 0; dm < D / 16; ++dm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[mt][i] = sacc[mt][i];
-        const float alpha = tile_update(x, mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt]);
-#pragma unroll
-        for (int dm = 0; dm < D / 16; ++dm)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
-        pv_tile<D, NP, false>(buf, x, acc[tt], lane);
-      }
+        for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+      pv_tile<D, NP, false>(buf, x, acc[tt], lane);
     }
   }
 
@@ -1716,6 +1685,186 @@ __global__ __launch_bounds__(512) void swa_kernel(SwaParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) v4[i] = acc[tt][dm][i] * inv;
       store4<T>(orow + 16 * dm + 4 * g16, v4);
+    }
+    if (p.lse != nullptr && g16 == 0)
+      p.lse[((size_t)b * p.Hq + h) * L + trow[tt]] = (mrow[tt] + __log2f(lrow[tt])) * kLn2;
+  }
+}
+
+// Sliding-window attention, bf16 inputs. A block of G waves (one head each, the
+// heads of one KV group) covers 32 consecutive slots: two 16-row tiles per wave,
+// so every V^T fragment of O^T += V^T P^T read from LDS serves both tiles (S^T =
+// K Q^T is formed one tile at a time, which keeps the wave's registers in bounds). The 64-slot K/V tiles of the band come into a
+// RING-deep LDS ring with direct-to-LDS loads (swizzled layout), RING - 1 tiles
+// ahead, issued by the first DW waves; a raw s_barrier per tile, after each
+// issuing wave has seen its own loads of that tile land, makes the tile visible
+// and frees the slot of the previous one (no register staging, and no barrier
+// that would wait for the loads still in flight). Rows of a partial last tile
+// are read from the sequence's last row and masked out.
+template <int D, int DW, int RING>
+__global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
+  typedef TileLayout<D, true> TL;
+  constexpr int BUFE = TL::PL;              // K then V of one 64-slot tile
+  constexpr int NI = D / 8;                 // 1 KB instructions per half
+  constexpr int RPI = 512 / D, BPR = D / 8;
+  constexpr int PER = 2 * NI / DW;          // instructions per issuing wave per tile
+  constexpr int PD = RING - 1;              // tiles issued ahead
+  static_assert((2 * NI) % DW == 0 && PD * PER < 64, "in-flight loads must fit the vmcnt counter");
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* kvb = reinterpret_cast<bf16_t*>(smem);
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g16 = lane >> 4;
+  const int G = p.Hq / p.Hkv;
+  const int bg = blockIdx.y, b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int h = g * G + w;
+  const int t0 = blockIdx.x * 32;   // slot indices fit in 32 bits (L < 2^31 - 2^16)
+  const int L = p.L;
+  const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (size_t)bg * L * D;
+  const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (size_t)bg * L * D;
+
+  QFrag<D, 1> qf[2];
+  f32x4 acc[2][D / 16];
+  float mrow[2], lrow[2];
+  int trow[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    trow[tt] = t0 + 16 * tt + (lane & 15);
+    load_qfrag<bf16_t, D, 1>(
+        qf[tt], trow[tt] < L ? reinterpret_cast<const bf16_t*>(p.q) + (((size_t)b * p.Hq + h) * L + trow[tt]) * D : nullptr,
+        lane);
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) acc[tt][dm] = zero4();
+    mrow[tt] = kNegBig;
+    lrow[tt] = 0.f;
+  }
+  const int R = min(p.R, L);   // a wider radius covers the same slots
+  const int lo_all = max(0, t0 - R);
+  const int hi_all = min(L - 1, t0 + 31 + R);
+  const int kb0 = (lo_all / 64) * 64;
+  const int ntile = (hi_all - kb0) / 64 + 1;
+
+  // the query fragments have landed: from here on this wave's vector loads are its
+  // share of the ring, which the loop waits for itself
+  wait_vm<0>();
+  // Full tiles: groups of four 1 KB loads with a uniform base (SGPRs) and per-lane
+  // offsets that repeat every group (the swizzle period); the rare partial last
+  // tile reads its missing rows from the sequence's last row, with the lane index
+  // formed in place so that its addresses are not kept live across the loop.
+  static_assert(PER % 4 == 0, "whole groups of four loads per wave");
+  int voff[2][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    voff[0][u] = dma_voff<D>(false, u, lane);
+    voff[1][u] = dma_voff<D>(true, u, lane);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)kvb);
+  auto issue = [&](int j) {
+    if (w >= DW) return;
+    const int kb = kb0 + 64 * j;
+    const uint32_t lbuf = lds0 + (uint32_t)((j % RING) * BUFE * 2);
+    if (kb + 64 <= L) {
+#pragma unroll
+      for (int gi = 0; gi < PER / 4; ++gi) {
+        const int i0 = w * PER + 4 * gi;   // first load of the group (wave-uniform)
+        const bool is_v = i0 >= NI;
+        const int ii0 = is_v ? i0 - NI : i0;
+        const bf16_t* sg = (is_v ? vg : kg) + (size_t)kb * D + (size_t)ii0 * 512;
+        const uint32_t lg = lbuf + (uint32_t)((is_v ? TL::KE : 0) + ii0 * 512) * 2;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lg + u * 1024),
+                       "v"(is_v ? voff[1][u] : voff[0][u]), "s"(sg)
+                       : "memory", "m0");
+      }
+    } else {
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int rows_valid = L - kb;
+      bf16_t* buf = kvb + (j % RING) * BUFE;
+      for (int u = 0; u < PER; ++u) {
+        const int jj = w * PER + u;
+        const bool is_v = jj >= NI;
+        const int ii = is_v ? jj - NI : jj;
+        const int pr = ii * RPI + ln / BPR, pb = ln % BPR;
+        const int sr = pr < rows_valid ? pr : rows_valid - 1;
+        const int sw = is_v ? TL::swz_v(pr) : TL::swz_k(pr);
+        dma16((is_v ? vg : kg) + (size_t)(kb + sr) * D + ((pb ^ sw) << 3), buf + (is_v ? TL::KE : 0) + ii * 512);
+      }
+    }
+  };
+#pragma unroll
+  for (int jj = 0; jj < PD; ++jj)
+    if (jj < ntile) issue(jj);
+
+  for (int j = 0; j < ntile; ++j) {
+    const int kb = kb0 + 64 * j;
+    // this wave's share of tile j has landed (later tiles stay in flight) ...
+    if (w < DW) {
+      const int ahead = min(PD - 1, ntile - 1 - j);
+      if constexpr (PD >= 3) {
+        if (ahead >= 2) wait_vm<(PD >= 3 ? 2 : 0) * PER>();
+        else if (ahead == 1) wait_vm<PER>();
+        else wait_vm<0>();
+      } else if constexpr (PD == 2) {
+        if (ahead >= 1) wait_vm<PER>();
+        else wait_vm<0>();
+      } else {
+        wait_vm<0>();
+      }
+    }
+    // ... and every wave's LDS reads of tile j - 1 have returned
+    wait_lgkm0();
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    if (j + PD < ntile) issue(j + PD);   // into the slot of tile j - 1
+    const bf16_t* buf = kvb + (j % RING) * BUFE;
+    bool act[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int ts = t0 + 16 * tt;
+      act[tt] = ts < L && kb <= ts + 15 + R && kb + 63 >= ts - R;   // wave-uniform
+    }
+    s16x8 pf[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if (!act[tt]) continue;
+      // S one tile at a time (its scores are consumed right away); P V below shares
+      // every V^T fragment read between the two tiles
+      f32x4 sacc[1][4];
+      s_tiles<D, 1>(buf, &qf[tt], sacc, lane);
+      const int ts = t0 + 16 * tt;
+      const int mode = trow[tt] < L ? 1 : 0;
+      const int lo = max(0, trow[tt] - R - kb);
+      const int hi = min(63, min(L - 1, trow[tt] + R) - kb);
+      // a tile inside the window of all 16 rows (and of the sequence) needs no mask
+      const bool inside = kb >= ts + 15 - R && kb + 63 <= ts + R && kb + 63 < L && ts + 15 < L;
+      const float alpha =
+          inside ? tile_softmax<false, false>(sacc[0], mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt])
+                 : tile_softmax<true, false>(sacc[0], mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
+      if (__ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+        for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+      }
+    }
+    if (act[0] && act[1]) pv_tiles<D, 2>(buf + TL::KE, pf, acc);
+    else if (act[0]) pv_tiles<D, 1>(buf + TL::KE, &pf[0], &acc[0]);
+    else if (act[1]) pv_tiles<D, 1>(buf + TL::KE, &pf[1], &acc[1]);
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    if (trow[tt] >= L) continue;
+    const float inv = 1.f / lrow[tt];
+    bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (((size_t)b * p.Hq + h) * L + trow[tt]) * D;
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) {
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = acc[tt][dm][i] * inv;
+      store4<bf16_t>(orow + 16 * dm + 4 * g16, v4);
     }
     if (p.lse != nullptr && g16 == 0)
       p.lse[((size_t)b * p.Hq + h) * L + trow[tt]] = (mrow[tt] + __log2f(lrow[tt])) * kLn2;
@@ -1929,7 +2078,31 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, cons
   return dm.d == 64 ? launch_routed_d<float, 64>(dm, pl, prm, st) : launch_routed_d<float, 128>(dm, pl, prm, st);
 }
 
-size_t swa_lds_bytes(int d, int dtype) { return kv_lds_bytes(d, dtype); }
+// bf16: a ring of at most 4 swizzled 64-slot K/V tiles (2 for a one-wave block at
+// d = 128, where 32 loads per tile leave room for one tile in flight); float32: the
+// register-staged padded planes of swa_kernel.
+size_t swa_lds_bytes(int d, int dtype) {
+  return dtype == 1 ? (size_t)4 * 2 * 64 * d * 2 : kv_lds_bytes(d, dtype);
+}
+
+template <int D, int DW, int RING>
+static hipError_t launch_swa_bf16_t(const SwaParams& prm, int G, hipStream_t st) {
+  const size_t lds = (size_t)RING * 2 * 64 * D * 2;
+  auto kern = swa_bf16_kernel<D, DW, RING>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)((prm.L + 31) / 32), prm.B * prm.Hkv);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * G), lds, st, prm);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_swa_bf16(const SwaParams& prm, int G, hipStream_t st) {
+  if (G >= 4) return launch_swa_bf16_t<D, 4, 4>(prm, G, st);
+  if (G >= 2) return launch_swa_bf16_t<D, 2, 4>(prm, G, st);
+  if constexpr (D == 128) return launch_swa_bf16_t<D, 1, 2>(prm, G, st);
+  else return launch_swa_bf16_t<D, 1, 4>(prm, G, st);
+}
 
 template <typename T, int D>
 static hipError_t launch_swa_t(const SwaParams& prm, int G, hipStream_t st) {
@@ -1957,7 +2130,7 @@ hipError_t launch_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype,
   prm.R = radius;
   prm.sl2 = scale * kLog2e;
   const int G = Hq / Hkv;
-  if (dtype == 1) return d == 64 ? launch_swa_t<bf16_t, 64>(prm, G, st) : launch_swa_t<bf16_t, 128>(prm, G, st);
+  if (dtype == 1) return d == 64 ? launch_swa_bf16<64>(prm, G, st) : launch_swa_bf16<128>(prm, G, st);
   return d == 64 ? launch_swa_t<float, 64>(prm, G, st) : launch_swa_t<float, 128>(prm, G, st);
 }
 

@@ -223,6 +223,10 @@ SWA_CASES = [
     ("bf16 radius 1280", dict(B=1, Hq=28, Hkv=4, L=8192, d=128, R=1280, dtype="bf16")),
     ("bf16 dense", dict(B=1, Hq=8, Hkv=1, L=700, d=128, R=5000, dtype="bf16")),
     ("bf16 radius 0", dict(B=1, Hq=4, Hkv=4, L=256, d=128, R=0, dtype="bf16")),
+    # two loading waves (3 heads per group), d = 64, ragged last tile and block, batch 2
+    ("bf16 d64 ragged", dict(B=2, Hq=6, Hkv=2, L=333, d=64, R=100, dtype="bf16")),
+    # a sequence shorter than one 64-slot tile
+    ("bf16 short", dict(B=1, Hq=4, Hkv=2, L=40, d=128, R=10, dtype="bf16")),
 ]
 
 
