@@ -14,9 +14,11 @@ Printed JSON line (one, rank 0):
                extrapolated to the whole layer
   decode_128k  ms per decode step (32 tail queries, 2048 chunks), HBM roofline
   swa_64k      ms per sliding-window layer (65,536 slots, radius 1280)
+  dense_16k    ms per dense bidirectional attention layer (16,384 slots, every
+               slot attends to every slot: the sliding window with R >= L)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--no-decode] [--no-swa] [--only {prefill,decode,swa,copy}]
+       [--no-decode] [--no-swa] [--only {prefill,decode,swa,dense,copy}]
 (--only copy runs a plain 1 GiB device copy, used to calibrate byte counters.)
 """
 import argparse
@@ -318,6 +320,34 @@ def bench_swa(args, torch, lcr):
                                                      "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def bench_dense(args, torch, lcr):
+    """Dense bidirectional attention over 16,384 slots (28 query / 4 KV heads, d = 128,
+    bf16 ~ N(0,1), seeded): the swa entry point with a radius covering the sequence."""
+    B, Hq, Hkv, L, d = 1, 28, 4, 16384, 128
+    g = torch.Generator(device="cuda").manual_seed(16384)
+    q = torch.randn((B, Hq, L, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    scale = 1.0 / np.sqrt(d)
+    for _ in range(2):
+        lcr.swa_attention(q, k, v, radius=L, scale=scale, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 5
+    e0.record()
+    for _ in range(n):
+        lcr.swa_attention(q, k, v, radius=L, scale=scale, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 4.0 * d * Hq * B * float(L) * float(L)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_layer": round(ms, 4), "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,7 +356,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-swa", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "swa", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "swa", "dense", "copy"], default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -344,6 +374,9 @@ def main():
         return
     if args.only == "swa":
         print(json.dumps({"swa_64k": bench_swa(args, torch, lcr)}), flush=True)
+        return
+    if args.only == "dense":
+        print(json.dumps({"dense_16k": bench_dense(args, torch, lcr)}), flush=True)
         return
     if args.only == "copy":
         # Plain device copy of a known size: calibrates the HBM byte counters.
@@ -381,6 +414,7 @@ def main():
         line["decode_128k"] = bench_decode(args, torch, lcr)
     if args.only is None and not args.no_swa:
         line["swa_64k"] = bench_swa(args, torch, lcr)
+        line["dense_16k"] = bench_dense(args, torch, lcr)
     if args.only is None and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
