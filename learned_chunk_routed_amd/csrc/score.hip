@@ -695,6 +695,77 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ zha
   }
 }
 
+// Top K of a wave's keys: lane l holds key[j] for element 64 j + l (elements in
+// their order); keys are order_key values, 0 = not a candidate. The K largest
+// keys are chosen, ties going to the smaller element. Two parts:
+//  - wave_topk_thresholds: theta = the largest key with at least K keys >= theta,
+//    found one bit per step; once exactly K keys reach the threshold, the chosen
+//    set (ties included) is fixed and the search stops. It runs Q selections at
+//    once, interleaved, so that their ballot -> count chains overlap;
+//  - wave_topk_select: emit(slot, j) is called by the owning lane for every chosen
+//    element, slots 0 .. count - 1 in element order; returns count = min(K, number
+//    of candidates) (wave-uniform).
+template <int P, int Q>
+__device__ __forceinline__ void wave_topk_thresholds(const uint32_t (*key)[P], int K, uint32_t* theta, bool* take_all) {
+  unsigned done = 0u;   // selections whose threshold is final (wave-uniform)
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    int ncand = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) ncand += __popcll(__ballot(key[q][j] != 0u));
+    take_all[q] = ncand <= K;
+    theta[q] = 0u;
+    if (take_all[q]) done |= 1u << q;
+  }
+  for (int bit = 31; bit >= 0 && done != (1u << Q) - 1u; --bit) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      if ((done >> q) & 1u) continue;
+      const uint32_t trial = theta[q] | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[q][j] >= trial));
+      if (cnt >= K) theta[q] = trial;
+      if (cnt == K) done |= 1u << q;
+    }
+  }
+}
+
+template <int P, typename Emit>
+__device__ __forceinline__ int wave_topk_select(const uint32_t* key, int K, uint32_t theta, bool take_all, int lane,
+                                                Emit emit) {
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int need = 0;
+  if (!take_all) {
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) gt += __popcll(__ballot(key[j] > theta));
+    need = K - gt;
+  }
+  int base = 0, ties = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const bool nz = key[j] != 0u;
+    const bool gt = take_all ? nz : key[j] > theta;
+    const bool eq = !take_all && nz && key[j] == theta;
+    const unsigned long long em = __ballot(eq);
+    const bool take = gt || (eq && ties + __popcll(em & lt) < need);
+    const unsigned long long tm = __ballot(take);
+    if (take) emit(base + __popcll(tm & lt), j);
+    base += __popcll(tm);
+    ties += __popcll(em);
+  }
+  return base;
+}
+
+template <int P, typename Emit>
+__device__ __forceinline__ int wave_topk(const uint32_t* key, int K, int lane, Emit emit) {
+  uint32_t theta;
+  bool take_all;
+  wave_topk_thresholds<P, 1>(reinterpret_cast<const uint32_t(*)[P]>(key), K, &theta, &take_all);
+  return wave_topk_select<P>(key, K, theta, take_all, lane, emit);
+}
+
 // ---------------------------------------------------------------------------- 4. fused scoring (bf16)
 //
 // route_score3_kernel: for QT = 16 NT consecutive queries of one KV group,
@@ -717,7 +788,12 @@ constexpr int kRsWaves = 8;
 
 __host__ __device__ inline size_t rs3_off_r(int NT, int N) { return (size_t)16 * NT * (N + 1) * 4; }
 __host__ __device__ inline size_t rs3_off_c(int NT, int N) { return (rs3_off_r(NT, N) + (size_t)16 * NT * N + 15) & ~(size_t)15; }
-__host__ __device__ inline size_t rs3_lds(int NT, int N) { return rs3_off_c(NT, N) + kRsWaves * 64 * 4; }
+__host__ __device__ inline size_t rs3_off_z(int NT, int N) { return rs3_off_c(NT, N) + kRsWaves * 64 * 4; }
+// without / with the zsel staging area (per wave, [QT][K] floats)
+__host__ __device__ inline size_t rs3_lds(int NT, int N) { return rs3_off_z(NT, N); }
+__host__ __device__ inline size_t rs3_lds_staged(int NT, int N, int K) {
+  return rs3_off_z(NT, N) + (size_t)kRsWaves * 16 * NT * K * 4;
+}
 
 // Summaries as the A operand of the scoring product, fragment-major: for each
 // (batch, head, 16-chunk row tile, k-step, plane) the 64 lanes' 16-byte fragments
@@ -756,7 +832,7 @@ __global__ __launch_bounds__(256) void split_frag_kernel(const float* __restrict
   *reinterpret_cast<s16x8*>(dst + 64 * 8) = lo;
 }
 
-template <int D, int RP, int NT, int P>
+template <int D, int RP, int NT, int P, bool STAGE>
 __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bt, const float* __restrict__ upart, int nsplit,
     const bf16_t* __restrict__ sp, const float* __restrict__ H, float beta, float scale, int32_t* __restrict__ idx,
@@ -776,7 +852,10 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
   uint32_t* zk = reinterpret_cast<uint32_t*>(smem);             // [QT][ZS] group-maximum keys
   uint8_t* rank_t = smem + rs3_off_r(NT, N);                   // [QT][N]: rank in zsel, 0xFF if not chosen
   int* chosen = reinterpret_cast<int*>(smem + rs3_off_c(NT, N));
+  float* zst = reinterpret_cast<float*>(smem + rs3_off_z(NT, N));   // STAGE: per wave [QT][K] zsel rows
   for (int e = tid; e < QT * ZS; e += 64 * kRsWaves) zk[e] = 0u;
+  if constexpr (STAGE)
+    for (int e = tid; e < kRsWaves * QT * K; e += 64 * kRsWaves) zst[e] = -INFINITY;   // unfilled slots
   for (int e = tid; e < QT * N / 4; e += 64 * kRsWaves) reinterpret_cast<uint32_t*>(rank_t)[e] = 0xFFFFFFFFu;
 
   const bool hw = w < G;   // this wave owns head w (wave-uniform)
@@ -932,45 +1011,75 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
     });
   __syncthreads();
 
-  // ---- B: top-K per query (wave w: queries w, w + 8, ...) and the rank table
-  for (int qi = w; qi < QT; qi += kRsWaves) {
-    const int t = t0 + qi;
-    if (t >= nq) break;
-    const long long i = (long long)q0 + t;
-    uint32_t key[P];
+  // ---- B: top-K per query (wave w: queries w, w + 8, ..., their thresholds found
+  //      together) and the rank table
+  {
+    constexpr int QW = QT / kRsWaves;
+    static_assert(QT % kRsWaves == 0, "queries per wave");
+    uint32_t key[QW][P];
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int c = 64 * j + lane;
-      const bool cand = (c < N) & ((63LL * c + 62 < i - R) | (63LL * c > i + R));
-      const uint32_t kv = zk[qi * ZS + (c < N ? c : N - 1)];
-      key[j] = cand ? kv : 0u;
+    for (int qq = 0; qq < QW; ++qq) {
+      const int qi = w + kRsWaves * qq, t = t0 + qi;
+      const long long i = (long long)q0 + t;
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const int c = 64 * j + lane;
+        const bool cand = (t < nq) & (c < N) & ((63LL * c + 62 < i - R) | (63LL * c > i + R));
+        const uint32_t kv = zk[qi * ZS + (c < N ? c : N - 1)];
+        key[qq][j] = cand ? kv : 0u;
+      }
     }
-    const int cnt = wave_topk<P>(key, K, lane, [&](int slot, int j) { chosen[w * 64 + slot] = 64 * j + lane; });
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (lane < K) {
-      const int c = lane < cnt ? chosen[w * 64 + lane] : -1;
-      idx[((size_t)bg * nq + t) * K + lane] = c;
-      if (c >= 0) rank_t[qi * N + c] = (uint8_t)lane;
-      else
-        for (int hh = 0; hh < G; ++hh) zsel[(((size_t)b * Hq + g * G + hh) * nq + t) * K + lane] = -INFINITY;
+    uint32_t theta[QW];
+    bool take_all[QW];
+    wave_topk_thresholds<P, QW>(key, K, theta, take_all);
+#pragma unroll
+    for (int qq = 0; qq < QW; ++qq) {
+      const int qi = w + kRsWaves * qq, t = t0 + qi;
+      if (t >= nq) break;
+      const int cnt = wave_topk_select<P>(key[qq], K, theta[qq], take_all[qq], lane,
+                                          [&](int slot, int j) { chosen[w * 64 + slot] = 64 * j + lane; });
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane < K) {
+        const int c = lane < cnt ? chosen[w * 64 + lane] : -1;
+        idx[((size_t)bg * nq + t) * K + lane] = c;
+        if (c >= 0) rank_t[qi * N + c] = (uint8_t)lane;
+        else if constexpr (!STAGE)
+          for (int hh = 0; hh < G; ++hh) zsel[(((size_t)b * Hq + g * G + hh) * nq + t) * K + lane] = -INFINITY;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
 
-  // ---- C: the chosen scores of head h straight to zsel
+  // ---- C: the chosen scores of head h to zsel: through the wave's LDS rows and out
+  //      as whole contiguous rows (STAGE), or straight to zsel
   if (hw) {
     float* zrow = zsel + (((size_t)b * Hq + h) * nq + t0) * K;
+    float* zw = zst + (size_t)w * QT * K;
     sweep(true, [&](int, const TileBuf& tbuf, const f32x4 (&zz)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t r8 = (tbuf.rk[nt] >> (8 * i)) & 0xFFu;
-          if (r8 != 0xFFu) zrow[(size_t)(16 * nt + L16) * K + r8] = zz[nt][i];
+          if (r8 != 0xFFu) {
+            if constexpr (STAGE) zw[(16 * nt + L16) * K + r8] = zz[nt][i];
+            else zrow[(size_t)(16 * nt + L16) * K + r8] = zz[nt][i];
+          }
         }
     });
+    if constexpr (STAGE) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's rows are in LDS
+      __builtin_amdgcn_wave_barrier();
+      const int len = min(QT, nq - t0) * K;   // the block's rows of head h are contiguous in zsel
+      if ((K & 3) == 0) {
+        for (int e = 4 * lane; e < len; e += 256)
+          *reinterpret_cast<f32x4*>(zrow + e) = *reinterpret_cast<const f32x4*>(zw + e);
+      } else {
+        for (int e = lane; e < len; e += 64) zrow[e] = zw[e];
+      }
+    }
   }
 }
 
@@ -1348,52 +1457,6 @@ __global__ __launch_bounds__(256) void score_small_kernel(const bf16_t* __restri
   }
 }
 
-// Top K of a wave's keys: lane l holds key[j] for element 64 j + l (elements in
-// their order); keys are order_key values, 0 = not a candidate. The K largest
-// keys are chosen, ties going to the smaller element; emit(slot, j) is called
-// by the owning lane for every chosen element, slots 0 .. count - 1 in element
-// order. Returns count = min(K, number of candidates) (wave-uniform).
-template <int P, typename Emit>
-__device__ __forceinline__ int wave_topk(const uint32_t* key, int K, int lane, Emit emit) {
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  int ncand = 0;
-#pragma unroll
-  for (int j = 0; j < P; ++j) ncand += __popcll(__ballot(key[j] != 0u));
-  const bool take_all = ncand <= K;
-  uint32_t theta = 0u;
-  int need = 0;
-  if (!take_all) {
-    // theta = the largest key with at least K keys >= theta, one bit per step; once
-    // exactly K keys reach the threshold, the chosen set (ties included) is fixed
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t trial = theta | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < P; ++j) cnt += __popcll(__ballot(key[j] >= trial));
-      if (cnt >= K) theta = trial;
-      if (cnt == K) break;
-    }
-    int gt = 0;
-#pragma unroll
-    for (int j = 0; j < P; ++j) gt += __popcll(__ballot(key[j] > theta));
-    need = K - gt;
-  }
-  int base = 0, ties = 0;
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const bool nz = key[j] != 0u;
-    const bool gt = take_all ? nz : key[j] > theta;
-    const bool eq = !take_all && nz && key[j] == theta;
-    const unsigned long long em = __ballot(eq);
-    const bool take = gt || (eq && ties + __popcll(em & lt) < need);
-    const unsigned long long tm = __ballot(take);
-    if (take) emit(base + __popcll(tm & lt), j);
-    base += __popcll(tm);
-    ties += __popcll(em);
-  }
-  return base;
-}
-
 template <int P>
 __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict__ zhat, const float* __restrict__ z,
                                                          int32_t* __restrict__ idx, float* __restrict__ zsel, int Hq,
@@ -1617,21 +1680,24 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
                      (const bf16_t*)Bm, r, HD, ws.bt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 32 queries per block: the q~ of the wave's head for them stays in registers
-  const int NT = 2;
-  const size_t lds = rs3_lds(NT, dm.N);
+  // 48 queries per block: the q~ of the wave's head for them stays in registers
+  // (three 16-query tiles; two waves per SIMD either way)
+  const int NT = 3;
+  // zsel staged in LDS when the rows fit next to the keys and ranks
+  const bool stage = rs3_lds_staged(NT, dm.N, K) <= (size_t)(160 * 1024 - 512);
+  const size_t lds = stage ? rs3_lds_staged(NT, dm.N, K) : rs3_lds(NT, dm.N);
   const int tiles = (nq + 16 * NT - 1) / (16 * NT) * dm.B * dm.Hkv;
 #define LCR_RS(NTT, PP)                                                                                          \
   do {                                                                                                           \
-    auto kern = route_score3_kernel<D, RP, NTT, PP>;                                                            \
+    auto kern = stage ? route_score3_kernel<D, RP, NTT, PP, true> : route_score3_kernel<D, RP, NTT, PP, false>;                                                            \
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
     if (e != hipSuccess) return e;                                                                               \
     hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * kRsWaves), lds, st, (const bf16_t*)q, ws.bt,      \
                        ws.upart, nsplit, ws.splanes, H, beta, scale, idx, zsel, dm.B, dm.Hq, dm.Hkv, dm.N, q0, nq, \
                        K, radius);                                                                               \
   } while (0)
-  if (dm.N <= 256) LCR_RS(2, 4);
-  else LCR_RS(2, 8);
+  if (dm.N <= 256) LCR_RS(3, 4);
+  else LCR_RS(3, 8);
 #undef LCR_RS
   return hipGetLastError();
 }
