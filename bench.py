@@ -12,7 +12,9 @@ Printed JSON line (one, rank 0):
                timed live with HIP events on the stream it runs on
   cpu_baseline the fp64 oracle on a bounded sample of the same workload,
                extrapolated to the whole layer
-  decode_128k  ms per decode step (32 tail queries, 2048 chunks), HBM roofline
+  decode_128k  ms per decode step (32 tail queries, 2048 chunks), HBM roofline;
+               summary_ms: a whole summary pass against the refresh of the one
+               chunk whose keys a decode step rewrites
   swa_64k      ms per sliding-window layer (65,536 slots, radius 1280)
   dense_16k    ms per dense bidirectional attention layer (16,384 slots, every
                slot attends to every slot: the sliding window with R >= L)
@@ -226,6 +228,21 @@ def bench_decode(args, torch, lcr):
     i_tail = np.arange(cfg.q0, cfg.T)
     slots = torch.from_numpy((i_tail // 63) * 64 + i_tail % 63).to(dev)
     s, H = lcr.chunk_summary(q, k, cfg.scale)          # once per cache, untimed
+    # the summaries a decode loop keeps current: a whole pass against a refresh of the
+    # one chunk whose keys a step rewrites (the last one here)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    lcr.chunk_summary(q, k, cfg.scale, s=s, H=H, chunks=(N - 1, 1))
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(5):
+        lcr.chunk_summary(q, k, cfg.scale, s=s, H=H)
+    ev[1].record()
+    for _ in range(20):
+        lcr.chunk_summary(q, k, cfg.scale, s=s, H=H, chunks=(N - 1, 1))
+    ev[2].record()
+    torch.cuda.synchronize()
+    summary_ms = {"whole": round(ev[0].elapsed_time(ev[1]) / 5, 4),
+                  "one_chunk_refresh": round(ev[1].elapsed_time(ev[2]) / 20, 4)}
     steps_in = [decode_step(cfg, j) for j in range(cfg.steps)]
     q_tail = [to_dev(st["q_tail"], torch) for st in steps_in]
     x_tail = [to_dev(st["x_tail"], torch) for st in steps_in]
@@ -291,6 +308,7 @@ def bench_decode(args, torch, lcr):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "algorithmic_mb_per_step": round(float(np.median(nbytes)) / 1e6, 2)},
+            "summary_ms": summary_ms,
             "note": "route_score_topk + routed_attention per step on cached K/V, replayed from a HIP graph "
                     "(eager_ms_per_step_median: the same calls issued from Python); summaries precomputed"}
 

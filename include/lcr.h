@@ -102,6 +102,19 @@ int lcr_chunk_summary(const lcr_dims* dims, const void* q, const void* k, float 
                       float* s, float* H, void* stream);
 
 /*
+ * The same summaries for chunks c0 .. c0 + nc - 1 only: the refresh a decode
+ * loop needs after the keys of some chunks changed (the block being decoded),
+ * since a chunk's summary and entropy depend on that chunk's keys and mask
+ * query alone (same sources as lcr_chunk_summary). Rows of s and H outside the
+ * range are not touched; the refreshed rows equal those of a whole
+ * lcr_chunk_summary call on the same inputs bit for bit. nc = 0 does nothing.
+ * Errors: as lcr_chunk_summary, and LCR_ERR_ARG unless 0 <= c0, 0 <= nc and
+ * c0 + nc <= N.
+ */
+int lcr_chunk_summary_range(const lcr_dims* dims, const void* q, const void* k, float scale, int c0, int nc,
+                            float* s, float* H, void* stream);
+
+/*
  * Residual-augmented scoring, GQA maximum and top-K selection ("Prefilling-dLLM
  * v2", Figure 3 caption: a content query adds a low-rank residual and scores the
  * summaries; scores are reduced by a maximum inside each GQA group; the top K

@@ -56,7 +56,17 @@ int lcr_chunk_summary(const lcr_dims* dims, const void* q, const void* k, float 
                       void* stream) {
   const int st = check_chunk_summary(dims, q, k, scale, s, H);
   if (st != LCR_OK) return st;
-  return hip_status(launch_chunk_summary(to_route_dims(dims), q, k, scale, s, H, (hipStream_t)stream));
+  return hip_status(launch_chunk_summary(to_route_dims(dims), q, k, scale, s, H, 0, dims->N, (hipStream_t)stream));
+}
+
+int lcr_chunk_summary_range(const lcr_dims* dims, const void* q, const void* k, float scale, int c0, int nc,
+                            float* s, float* H, void* stream) {
+  int st = check_chunk_summary(dims, q, k, scale, s, H);
+  if (st != LCR_OK) return st;
+  st = check_chunk_range(dims, c0, nc);
+  if (st != LCR_OK) return st;
+  if (nc == 0) return LCR_OK;
+  return hip_status(launch_chunk_summary(to_route_dims(dims), q, k, scale, s, H, c0, nc, (hipStream_t)stream));
 }
 
 int lcr_route_score_topk(const lcr_dims* dims, const void* q, const void* x, const void* A, const void* Bm,

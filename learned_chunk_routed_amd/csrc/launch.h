@@ -15,8 +15,9 @@ struct RouteDims {
 };
 
 // ---- chunk_summary (summary.hip)
+// chunks c0 .. c0 + nc - 1 (nc >= 1)
 hipError_t launch_chunk_summary(const RouteDims& dm, const void* q, const void* k, float scale,
-                                float* s, float* H, hipStream_t st);
+                                float* s, float* H, int c0, int nc, hipStream_t st);
 
 // ---- route_score_topk (score.hip)
 struct ScoreWs {

@@ -5,7 +5,8 @@
 // Speedup Has an Evidence Budget", section "How learned routing controls what
 // the model can read": the entropy of the pooling weights ranks chunks too.
 //
-// One block of four waves per (batch, KV head, chunk): the chunk's keys are read
+// One block of four waves per (batch, KV head, chunk of the requested range c0 ..):
+// the chunk's keys are read
 // from HBM once into LDS with 16-byte loads (float32, padded rows so that lane j
 // reading row j is bank-conflict free) and serve the G mask queries of the group,
 // wave w taking heads w, w + 4, ... Lane j < 63 owns content key j for the logits
@@ -24,8 +25,8 @@ __global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(const T* 
                                                                        const T* __restrict__ k, float scale,
                                                                        float* __restrict__ s,
                                                                        float* __restrict__ Hout, int Hq, int Hkv,
-                                                                       int N) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+                                                                       int N, int c0) {
+  const int c = c0 + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = Hq / Hkv;
   const size_t L = (size_t)N * kSlots;
@@ -84,21 +85,21 @@ __global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(const T* 
 
 template <typename T, int D>
 static hipError_t launch_summary_t(const RouteDims& dm, const void* q, const void* k, float scale,
-                                   float* s, float* H, hipStream_t st) {
-  dim3 grid(dm.N, dm.Hkv, dm.B);
+                                   float* s, float* H, int c0, int nc, hipStream_t st) {
+  dim3 grid(nc, dm.Hkv, dm.B);
   hipLaunchKernelGGL((chunk_summary_kernel<T, D>), grid, dim3(64 * kSumWaves), 0, st, (const T*)q,
-                     (const T*)k, scale, s, H, dm.Hq, dm.Hkv, dm.N);
+                     (const T*)k, scale, s, H, dm.Hq, dm.Hkv, dm.N, c0);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_summary(const RouteDims& dm, const void* q, const void* k, float scale,
-                                float* s, float* H, hipStream_t st) {
+                                float* s, float* H, int c0, int nc, hipStream_t st) {
   if (dm.dtype == 1) {
-    return dm.d == 64 ? launch_summary_t<bf16_t, 64>(dm, q, k, scale, s, H, st)
-                      : launch_summary_t<bf16_t, 128>(dm, q, k, scale, s, H, st);
+    return dm.d == 64 ? launch_summary_t<bf16_t, 64>(dm, q, k, scale, s, H, c0, nc, st)
+                      : launch_summary_t<bf16_t, 128>(dm, q, k, scale, s, H, c0, nc, st);
   }
-  return dm.d == 64 ? launch_summary_t<float, 64>(dm, q, k, scale, s, H, st)
-                    : launch_summary_t<float, 128>(dm, q, k, scale, s, H, st);
+  return dm.d == 64 ? launch_summary_t<float, 64>(dm, q, k, scale, s, H, c0, nc, st)
+                    : launch_summary_t<float, 128>(dm, q, k, scale, s, H, c0, nc, st);
 }
 
 }  // namespace lcr

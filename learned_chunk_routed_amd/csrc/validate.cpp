@@ -30,6 +30,11 @@ int check_chunk_summary(const lcr_dims* d, const void* q, const void* k, float s
   return LCR_OK;
 }
 
+int check_chunk_range(const lcr_dims* d, int c0, int nc) {
+  if (c0 < 0 || nc < 0 || (long long)c0 + nc > d->N) return LCR_ERR_ARG;
+  return LCR_OK;
+}
+
 static int check_query_range(const lcr_dims* d, int q0, int nq) {
   const long long T = (long long)d->N * LCR_CHUNK_CONTENT;
   if (q0 < 0 || nq < 0) return LCR_ERR_ARG;

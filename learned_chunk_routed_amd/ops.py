@@ -68,22 +68,32 @@ def _workspace(nbytes, device, ws=None):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def chunk_summary(q, k, scale=None, s=None, H=None):
-    """Summary keys s [B,Hq,N,d] and pooling entropies H [B,Hq,N], float32."""
+def chunk_summary(q, k, scale=None, s=None, H=None, chunks=None):
+    """Summary keys s [B,Hq,N,d] and pooling entropies H [B,Hq,N], float32.
+
+    chunks=(c0, nc) refreshes only chunks c0 .. c0 + nc - 1 of the given s and H in
+    place (after their keys changed); the other rows are left as they are."""
     lib = _lib.load()
     dev = q.device
     dims = _dims_from(q, k.shape[1])
     _check(q, "q", dev)
     _check(k, "k", dev, q.dtype, (dims.B, dims.Hkv, dims.N * SLOTS, dims.d))
     scale = default_scale(dims.d) if scale is None else float(scale)
+    if chunks is not None and (s is None or H is None):
+        raise ValueError("a refresh of some chunks updates existing s and H: pass both")
     if s is None:
         s = torch.empty((dims.B, dims.Hq, dims.N, dims.d), dtype=torch.float32, device=dev)
     if H is None:
         H = torch.empty((dims.B, dims.Hq, dims.N), dtype=torch.float32, device=dev)
     _check(s, "s", dev, torch.float32, (dims.B, dims.Hq, dims.N, dims.d))
     _check(H, "H", dev, torch.float32, (dims.B, dims.Hq, dims.N))
-    check(lib.lcr_chunk_summary(dims, q.data_ptr(), k.data_ptr(), scale, s.data_ptr(), H.data_ptr(),
-                                _stream(dev)), "lcr_chunk_summary")
+    if chunks is None:
+        check(lib.lcr_chunk_summary(dims, q.data_ptr(), k.data_ptr(), scale, s.data_ptr(), H.data_ptr(),
+                                    _stream(dev)), "lcr_chunk_summary")
+    else:
+        c0, nc = (int(c) for c in chunks)
+        check(lib.lcr_chunk_summary_range(dims, q.data_ptr(), k.data_ptr(), scale, c0, nc, s.data_ptr(),
+                                          H.data_ptr(), _stream(dev)), "lcr_chunk_summary_range")
     return s, H
 
 

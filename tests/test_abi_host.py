@@ -72,6 +72,16 @@ def test_chunk_summary_rejects_bad_dims(lib, kw, code):
     assert lib.lcr_chunk_summary(dims(**kw), P, P, 0.1, P, P, NULL) == code
 
 
+@pytest.mark.parametrize("c0,nc,code", [
+    (-1, 1, _lib.LCR_ERR_ARG), (0, -1, _lib.LCR_ERR_ARG), (250, 7, _lib.LCR_ERR_ARG), (256, 1, _lib.LCR_ERR_ARG),
+    (256, 0, _lib.LCR_OK), (3, 0, _lib.LCR_OK),
+])
+def test_chunk_summary_range_checks(lib, c0, nc, code):
+    # an empty range is accepted and launches nothing, so it runs without a GPU
+    assert lib.lcr_chunk_summary_range(dims(), P, P, 0.1, c0, nc, P, P, NULL) == code
+    assert lib.lcr_chunk_summary_range(dims(B=0), P, P, 0.1, 0, 0, P, P, NULL) == _lib.LCR_ERR_ARG
+
+
 def test_chunk_summary_rejects_nulls_and_scale(lib):
     assert lib.lcr_chunk_summary(None, P, P, 0.1, P, P, NULL) == _lib.LCR_ERR_ARG
     for i in range(4):

@@ -86,6 +86,35 @@ def test_chunk_summary(name):
     assert max_err(f64(H), rH) < 1e-5
 
 
+def test_chunk_summary_refresh_after_keys_change():
+    """A decode step rewrites the keys of the block being decoded: refreshing only that
+    chunk's summaries must give what a whole recompute gives (bit for bit), and the
+    other rows must stay untouched."""
+    from lcr_inputs import bf16_round
+    cfg = get_config("tiny_fp32", N=32, Hq=8, Hkv=2, d=128, dtype="bf16")
+    print("[case] chunk_summary refresh of one chunk", flush=True)
+    inp = route_inputs(cfg)
+    q = to_dev(inp["q"])
+    s, H = lcr.chunk_summary(q, to_dev(inp["k"]), cfg.scale)
+    s_old, H_old = s.clone(), H.clone()
+    c = cfg.N - 2                                   # an interior chunk's keys change
+    k2 = inp["k"].copy()
+    rng = np.random.default_rng(99)
+    k2[:, :, 64 * c:64 * c + 63] = bf16_round(rng.standard_normal(k2[:, :, 64 * c:64 * c + 63].shape,
+                                                                  dtype=np.float32))
+    k = to_dev(k2)
+    lcr.chunk_summary(q, k, cfg.scale, s=s, H=H, chunks=(c, 1))
+    s_full, H_full = lcr.chunk_summary(q, k, cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(s, s_full) and torch.equal(H, H_full)
+    keep = [i for i in range(cfg.N) if i != c]
+    assert torch.equal(s[:, :, keep], s_old[:, :, keep]) and torch.equal(H[:, :, keep], H_old[:, :, keep])
+    assert not torch.equal(s[:, :, c], s_old[:, :, c])
+    rs, rH = O.chunk_summary(as_f64(inp["q"]), as_f64(k2), cfg.scale)
+    assert max_err(f64(s)[:, :, c], rs[:, :, c]) < 1e-5 * max(1.0, np.abs(rs).max())
+    assert max_err(f64(H)[:, :, c], rH[:, :, c]) < 1e-5
+
+
 # ----------------------------------------------------------------------------- full layers
 
 def test_route_layer_tiny_fp32_full():
