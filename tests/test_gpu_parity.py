@@ -259,6 +259,39 @@ SWA_CASES = [
 ]
 
 
+@pytest.mark.parametrize("L,R,label", [(65536, 1280, "64K radius 1280"), (16384, 16384, "16K dense")])
+def test_swa_full_size_sampled(L, R, label):
+    """The bench's SWA layer (65,536 slots, radius 1280) and dense layer (16,384 slots,
+    R >= L), 28/4 heads, d = 128, bf16, in the launch configuration the bench times;
+    the oracle computes 120 sampled rows (both ends and random interior slots)."""
+    from lcr_inputs import bf16_round
+    print(f"[case] swa full size {label}", flush=True)
+    B, Hq, Hkv, d = 1, 28, 4, 128
+    rng = np.random.default_rng([88, L, R])
+    q = bf16_round(rng.standard_normal((B, Hq, L, d), dtype=np.float32))
+    k = bf16_round(rng.standard_normal((B, Hkv, L, d), dtype=np.float32))
+    v = bf16_round(rng.standard_normal((B, Hkv, L, d), dtype=np.float32))
+    scale = 1.0 / np.sqrt(d)
+    o, lse = lcr.swa_attention(to_dev(q), to_dev(k), to_dev(v), radius=R, scale=scale, want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(L - 40, L), rng.choice(L, size=40, replace=False)]))
+    ro, rl = O.swa_attention(_RowView(q), as_f64(k), as_f64(v), R, scale, rows)
+    o_err = max_err(f64(o[:, :, torch.from_numpy(rows).cuda()]), ro)
+    l_err = max_err(f64(lse[:, :, torch.from_numpy(rows).cuda()]), rl)
+    print(f"    o_err={o_err:.2e} lse_err={l_err:.2e}", flush=True)
+    assert o_err < OUT_TOL["bf16"] and l_err < LSE_TOL["bf16"]
+
+
+class _RowView:
+    """q for the oracle without upcasting all of it: shape, and rows upcast on access."""
+
+    def __init__(self, q):
+        self.q, self.shape = q, q.shape
+
+    def __getitem__(self, ix):
+        return as_f64(self.q[ix])
+
+
 @pytest.mark.parametrize("case", SWA_CASES, ids=[c[0] for c in SWA_CASES])
 def test_swa(case):
     name, c = case
