@@ -229,20 +229,26 @@ def bench_decode(args, torch, lcr):
     slots = torch.from_numpy((i_tail // 63) * 64 + i_tail % 63).to(dev)
     s, H = lcr.chunk_summary(q, k, cfg.scale)          # once per cache, untimed
     # the summaries a decode loop keeps current: a whole pass against a refresh of the
-    # one chunk whose keys a step rewrites (the last one here)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    # one chunk whose keys a step rewrites (the last one here); and the pass of the
+    # mean-summary ablation
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     lcr.chunk_summary(q, k, cfg.scale, s=s, H=H, chunks=(N - 1, 1))
+    sm, Hm = lcr.chunk_summary_mean(k, Hq)
     torch.cuda.synchronize()
-    ev[0].record()
+    sev[0].record()
     for _ in range(5):
         lcr.chunk_summary(q, k, cfg.scale, s=s, H=H)
-    ev[1].record()
+    sev[1].record()
     for _ in range(20):
         lcr.chunk_summary(q, k, cfg.scale, s=s, H=H, chunks=(N - 1, 1))
-    ev[2].record()
+    sev[2].record()
+    for _ in range(5):
+        lcr.chunk_summary_mean(k, Hq, s=sm, H=Hm)
+    sev[3].record()
     torch.cuda.synchronize()
-    summary_ms = {"whole": round(ev[0].elapsed_time(ev[1]) / 5, 4),
-                  "one_chunk_refresh": round(ev[1].elapsed_time(ev[2]) / 20, 4)}
+    summary_ms = {"whole": round(sev[0].elapsed_time(sev[1]) / 5, 4),
+                  "one_chunk_refresh": round(sev[1].elapsed_time(sev[2]) / 20, 4),
+                  "mean_whole": round(sev[2].elapsed_time(sev[3]) / 5, 4)}
     steps_in = [decode_step(cfg, j) for j in range(cfg.steps)]
     q_tail = [to_dev(st["q_tail"], torch) for st in steps_in]
     x_tail = [to_dev(st["x_tail"], torch) for st in steps_in]

@@ -115,6 +115,20 @@ int lcr_chunk_summary_range(const lcr_dims* dims, const void* q, const void* k, 
                             float* s, float* H, void* stream);
 
 /*
+ * Mean summaries: the "Mean summary" ablation of "Prefilling-dLLM v2" (Table 6;
+ * Section "Discussion": attention-weighted summaries replaced by mean pooling).
+ * The pooling weights are uniform, so
+ *
+ *   s[b,h,c] = (1/63) sum_j k[b,g(h),64c+j]   (the same for every head of a group)
+ *   H[b,h,c] = ln 63
+ *
+ * which is lcr_chunk_summary with zero mask queries. k [B,Hkv,L,d]; s [B,Hq,N,d]
+ * and H [B,Hq,N] float32 (written); dims as lcr_chunk_summary. The result feeds
+ * lcr_route_score_topk unchanged. Errors: as lcr_chunk_summary (no q).
+ */
+int lcr_chunk_summary_mean(const lcr_dims* dims, const void* k, float* s, float* H, void* stream);
+
+/*
  * Residual-augmented scoring, GQA maximum and top-K selection ("Prefilling-dLLM
  * v2", Figure 3 caption: a content query adds a low-rank residual and scores the
  * summaries; scores are reduced by a maximum inside each GQA group; the top K

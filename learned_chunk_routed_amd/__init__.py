@@ -9,6 +9,7 @@ call is made without the library: build it with
 from ._lib import LIB_PATH, load  # noqa: F401
 from .ops import (  # noqa: F401
     chunk_summary,
+    chunk_summary_mean,
     route_score_topk,
     routed_attention,
     swa_attention,

@@ -27,6 +27,7 @@ SIGNATURES = {
     "lcr_workspace_bytes": (_sz, [_i, _pd, _i, _i, _i, _i, _i]),
     "lcr_chunk_summary": (_i, [_pd, _vp, _vp, _f, _vp, _vp, _vp]),
     "lcr_chunk_summary_range": (_i, [_pd, _vp, _vp, _f, _i, _i, _vp, _vp, _vp]),
+    "lcr_chunk_summary_mean": (_i, [_pd, _vp, _vp, _vp, _vp]),
     "lcr_route_score_topk": (_i, [_pd, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _f, _f, _i, _i, _i, _i,
                                   _vp, _vp, _vp, _sz, _vp]),
     "lcr_routed_attention": (_i, [_pd, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _i, _vp, _vp, _vp, _sz, _vp]),

@@ -59,6 +59,12 @@ int lcr_chunk_summary(const lcr_dims* dims, const void* q, const void* k, float 
   return hip_status(launch_chunk_summary(to_route_dims(dims), q, k, scale, s, H, 0, dims->N, (hipStream_t)stream));
 }
 
+int lcr_chunk_summary_mean(const lcr_dims* dims, const void* k, float* s, float* H, void* stream) {
+  const int st = check_chunk_summary_mean(dims, k, s, H);
+  if (st != LCR_OK) return st;
+  return hip_status(launch_chunk_summary_mean(to_route_dims(dims), k, s, H, (hipStream_t)stream));
+}
+
 int lcr_chunk_summary_range(const lcr_dims* dims, const void* q, const void* k, float scale, int c0, int nc,
                             float* s, float* H, void* stream) {
   int st = check_chunk_summary(dims, q, k, scale, s, H);

@@ -18,6 +18,8 @@ struct RouteDims {
 // chunks c0 .. c0 + nc - 1 (nc >= 1)
 hipError_t launch_chunk_summary(const RouteDims& dm, const void* q, const void* k, float scale,
                                 float* s, float* H, int c0, int nc, hipStream_t st);
+// uniform pooling weights (mean summaries), all chunks
+hipError_t launch_chunk_summary_mean(const RouteDims& dm, const void* k, float* s, float* H, hipStream_t st);
 
 // ---- route_score_topk (score.hip)
 struct ScoreWs {

@@ -20,7 +20,10 @@ namespace lcr {
 
 constexpr int kSumWaves = 4;
 
-template <typename T, int D>
+// MEAN: the mean-summary ablation ("Prefilling-dLLM v2", Table 6, row "Mean
+// summary"): every pooling logit is zero, so the weights are uniform (1/63), s is
+// the mean content key and H = ln 63; q is not read.
+template <typename T, int D, bool MEAN>
 __global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(const T* __restrict__ q,
                                                                        const T* __restrict__ k, float scale,
                                                                        float* __restrict__ s,
@@ -47,12 +50,16 @@ __global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(const T* 
 
   for (int hh = w; hh < G; hh += kSumWaves) {
     const int h = g * G + hh;
-    const T* qm = q + (((size_t)b * Hq + h) * L + (size_t)c * kSlots + (kSlots - 1)) * D;
-    for (int e = lane; e < D; e += 64) qs[w][e] = Elem<T>::to_f(qm[e]);
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the row is in LDS for the whole wave
-    __builtin_amdgcn_wave_barrier();
     float logit = -INFINITY;
-    if (lane < kContent) {
+    if constexpr (MEAN) {
+      if (lane < kContent) logit = 0.f;
+    } else {
+      const T* qm = q + (((size_t)b * Hq + h) * L + (size_t)c * kSlots + (kSlots - 1)) * D;
+      for (int e = lane; e < D; e += 64) qs[w][e] = Elem<T>::to_f(qm[e]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the row is in LDS for the whole wave
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (!MEAN && lane < kContent) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
       for (int e = 0; e < D; e += 4)
@@ -83,23 +90,33 @@ __global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(const T* 
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool MEAN>
 static hipError_t launch_summary_t(const RouteDims& dm, const void* q, const void* k, float scale,
                                    float* s, float* H, int c0, int nc, hipStream_t st) {
   dim3 grid(nc, dm.Hkv, dm.B);
-  hipLaunchKernelGGL((chunk_summary_kernel<T, D>), grid, dim3(64 * kSumWaves), 0, st, (const T*)q,
+  hipLaunchKernelGGL((chunk_summary_kernel<T, D, MEAN>), grid, dim3(64 * kSumWaves), 0, st, (const T*)q,
                      (const T*)k, scale, s, H, dm.Hq, dm.Hkv, dm.N, c0);
   return hipGetLastError();
 }
 
+template <bool MEAN>
+static hipError_t launch_summary_m(const RouteDims& dm, const void* q, const void* k, float scale,
+                                   float* s, float* H, int c0, int nc, hipStream_t st) {
+  if (dm.dtype == 1) {
+    return dm.d == 64 ? launch_summary_t<bf16_t, 64, MEAN>(dm, q, k, scale, s, H, c0, nc, st)
+                      : launch_summary_t<bf16_t, 128, MEAN>(dm, q, k, scale, s, H, c0, nc, st);
+  }
+  return dm.d == 64 ? launch_summary_t<float, 64, MEAN>(dm, q, k, scale, s, H, c0, nc, st)
+                    : launch_summary_t<float, 128, MEAN>(dm, q, k, scale, s, H, c0, nc, st);
+}
+
 hipError_t launch_chunk_summary(const RouteDims& dm, const void* q, const void* k, float scale,
                                 float* s, float* H, int c0, int nc, hipStream_t st) {
-  if (dm.dtype == 1) {
-    return dm.d == 64 ? launch_summary_t<bf16_t, 64>(dm, q, k, scale, s, H, c0, nc, st)
-                      : launch_summary_t<bf16_t, 128>(dm, q, k, scale, s, H, c0, nc, st);
-  }
-  return dm.d == 64 ? launch_summary_t<float, 64>(dm, q, k, scale, s, H, c0, nc, st)
-                    : launch_summary_t<float, 128>(dm, q, k, scale, s, H, c0, nc, st);
+  return launch_summary_m<false>(dm, q, k, scale, s, H, c0, nc, st);
+}
+
+hipError_t launch_chunk_summary_mean(const RouteDims& dm, const void* k, float* s, float* H, hipStream_t st) {
+  return launch_summary_m<true>(dm, nullptr, k, 0.f, s, H, 0, dm.N, st);
 }
 
 }  // namespace lcr

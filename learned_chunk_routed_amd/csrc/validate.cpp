@@ -30,6 +30,13 @@ int check_chunk_summary(const lcr_dims* d, const void* q, const void* k, float s
   return LCR_OK;
 }
 
+int check_chunk_summary_mean(const lcr_dims* d, const void* k, const float* s, const float* H) {
+  int st = check_dims(d);
+  if (st != LCR_OK) return st;
+  if (!k || !s || !H) return LCR_ERR_ARG;
+  return LCR_OK;
+}
+
 int check_chunk_range(const lcr_dims* d, int c0, int nc) {
   if (c0 < 0 || nc < 0 || (long long)c0 + nc > d->N) return LCR_ERR_ARG;
   return LCR_OK;

@@ -11,6 +11,7 @@ namespace lcr {
 
 int check_dims(const lcr_dims* d);
 int check_chunk_range(const lcr_dims* d, int c0, int nc);
+int check_chunk_summary_mean(const lcr_dims* d, const void* k, const float* s, const float* H);
 int check_chunk_summary(const lcr_dims* d, const void* q, const void* k, float scale, const float* s,
                         const float* H);
 int check_route_score_topk(const lcr_dims* d, const void* q, const void* x, const void* A, const void* Bm,

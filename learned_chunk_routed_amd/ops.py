@@ -97,6 +97,26 @@ def chunk_summary(q, k, scale=None, s=None, H=None, chunks=None):
     return s, H
 
 
+def chunk_summary_mean(k, Hq, s=None, H=None):
+    """Mean summaries (uniform pooling): s [B,Hq,N,d] = the mean content key of each chunk
+    for every head of its group, H [B,Hq,N] = ln 63; float32."""
+    lib = _lib.load()
+    dev = k.device
+    B, Hkv, L, d = k.shape
+    N = L // SLOTS
+    dims = make_dims(B, Hq, Hkv, N, d, k.dtype)
+    _check(k, "k", dev, k.dtype, (B, Hkv, N * SLOTS, d))
+    if s is None:
+        s = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    if H is None:
+        H = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    _check(s, "s", dev, torch.float32, (B, Hq, N, d))
+    _check(H, "H", dev, torch.float32, (B, Hq, N))
+    check(lib.lcr_chunk_summary_mean(dims, k.data_ptr(), s.data_ptr(), H.data_ptr(), _stream(dev)),
+          "lcr_chunk_summary_mean")
+    return s, H
+
+
 def route_score_topk(q, x, A, Bm, s, H, *, Hkv, K, radius, beta=0.0, scale=None, q0=0, nq=None,
                      idx=None, zsel=None, ws=None):
     """Chosen remote chunks idx [B,Hkv,nq,K] (int32, ascending, -1 padded) and the

@@ -105,6 +105,24 @@ def chunk_summary(q, k, scale):
     return chunk_summary_from_mask(q_mask, k, scale)
 
 
+def chunk_summary_mean(k, Hq):
+    """Mean summaries: "Prefilling-dLLM v2", Table 6 (row "Mean summary") and its
+    discussion, where attention-weighted summaries are replaced by mean pooling.
+
+    Readings: the 63 content keys are averaged (the mask slot's key is not); the
+    summary is repeated for every query head of the group; the pooling weights are
+    uniform, so the entropy is ln 63 for every chunk.
+
+    k [B,Hkv,L,d] -> s [B,Hq,N,d], H [B,Hq,N].
+    """
+    B, Hkv, L, d = k.shape
+    N, G = L // SLOTS, Hq // Hkv
+    kc = k.reshape(B, Hkv, N, SLOTS, d)[:, :, :, :CONTENT, :]
+    s = np.repeat(kc.mean(axis=3), G, axis=1)
+    H = np.full((B, Hq, N), np.log(CONTENT))
+    return s, H
+
+
 # ----------------------------------------------------------------------------- step 2: routing query
 
 def routing_query(q_rows, x_rows, A, Bm):

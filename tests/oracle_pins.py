@@ -90,6 +90,20 @@ def pin_pooling_uniform_when_mask_query_is_zero():
     close(H, np.full_like(H, math.log(CT)), 1e-12, "uniform entropy ln 63")
 
 
+def pin_mean_summary_is_pooling_with_zero_mask_queries():
+    """The mean-summary ablation equals mask-query pooling with every mask query zero
+    (the softmax of equal logits is uniform): two independent routes to one result."""
+    c = case(21, Hq=6, Hkv=2)
+    q = c["q"].copy()
+    q.reshape(c["B"], c["Hq"], c["N"], SL, c["d"])[:, :, :, SL - 1] = 0.0
+    s_pool, H_pool = O.chunk_summary(q, c["k"], c["scale"])
+    s_mean, H_mean = O.chunk_summary_mean(c["k"], c["Hq"])
+    close(s_mean, s_pool, 1e-12, "mean summary against uniform pooling")
+    close(H_mean, H_pool, 1e-12, "entropy of uniform pooling")
+    kc = c["k"].reshape(c["B"], c["Hkv"], c["N"], SL, c["d"])
+    assert not np.allclose(s_mean[:, 0], kc[:, 0, :, SL - 1]), "the mask slot's key is not averaged"
+
+
 def pin_pooling_concentrates_on_aligned_key():
     """Mask query = lambda * k_j* with a wide logit gap => the pooling is one-hot on j*."""
     c = case(3, d=32)

@@ -86,6 +86,24 @@ def test_chunk_summary(name):
     assert max_err(f64(H), rH) < 1e-5
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32", "prefill_16k"])
+def test_chunk_summary_mean(name):
+    """Mean summaries against the oracle, and bit for bit equal to mask-query pooling
+    with zero mask queries (the kernel's own special case)."""
+    cfg = get_config(name)
+    print(f"[case] chunk_summary_mean {name}", flush=True)
+    inp = route_inputs(cfg)
+    k = to_dev(inp["k"])
+    s, H = lcr.chunk_summary_mean(k, cfg.Hq)
+    q0 = torch.zeros(inp["q"].shape, dtype=k.dtype, device="cuda")
+    s0, H0 = lcr.chunk_summary(q0, k, cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(s, s0) and torch.equal(H, H0)
+    rs, rH = O.chunk_summary_mean(as_f64(inp["k"]), cfg.Hq)
+    assert max_err(f64(s), rs) < 1e-5 * max(1.0, np.abs(rs).max())
+    assert max_err(f64(H), rH) < 1e-5
+
+
 def test_chunk_summary_refresh_after_keys_change():
     """A decode step rewrites the keys of the block being decoded: refreshing only that
     chunk's summaries must give what a whole recompute gives (bit for bit), and the
