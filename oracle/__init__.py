@@ -12,6 +12,9 @@ Diffusion Language Models" (Abstract; Figure 2 and Figure 3 captions; Table 3)
 and "The 172x Speedup Has an Evidence Budget" (section "How learned routing
 controls what the model can read").
 
+Gradients (module ``backward``) hold the chosen chunks fixed and follow the
+chain rule through the forward's steps in reverse.
+
 Pins (all in tests/oracle_pins.py, run with ``-m "not gpu"``): every function
 here is pinned by closed forms, invariants, brute force or a library routine;
 none is "parity unpinned".
@@ -23,4 +26,8 @@ from .route import (  # noqa: F401
     routing_query, window_bounds, candidate_mask,
     route_scores, group_max, select_topk, gather_zsel,
     routed_attention, route_layer, route_layer_rows, swa_attention,
+)
+from .backward import (  # noqa: F401
+    routed_attention_backward, route_score_backward, chunk_summary_backward,
+    route_layer_backward,
 )

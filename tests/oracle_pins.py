@@ -20,6 +20,7 @@ import numpy as np
 import torch
 
 from oracle import route as O
+from oracle import backward as OB
 
 SL, CT = 64, 63
 
@@ -502,6 +503,214 @@ def pin_swa_against_library():
             close(lse[0, h], ref, 1e-12, "SWA log partition")
         if R == 0:
             close(o, np.repeat(v, 2, axis=1)[:, :, rows], 1e-12, "radius 0 returns v")
+
+
+# ----------------------------------------------------------------------------- backward (membership fixed)
+
+def _fd(f, args, name, w, eps=1e-6):
+    """Central difference of scalar f along direction w of argument `name`."""
+    up = dict(args)
+    dn = dict(args)
+    up[name] = args[name] + eps * w
+    dn[name] = args[name] - eps * w
+    return (f(**up) - f(**dn)) / (2 * eps)
+
+
+def _check_fd(f, args, grads, what, ndir=3, seed=0, tol=1e-6):
+    """Directional derivatives of f along random directions against <grad, w>."""
+    g = rng(100 + seed)
+    for name, gr in grads.items():
+        for _ in range(ndir):
+            w = g.standard_normal(args[name].shape)
+            num = _fd(f, args, name, w)
+            ana = float(np.sum(gr * w))
+            assert abs(num - ana) <= tol * max(1.0, abs(num)), \
+                f"{what}: d/d{name} finite difference {num:.9e} vs gradient {ana:.9e}"
+
+
+def _bwd_case(seed, K, R, queries, N=6):
+    c = case(seed, N=N, Hq=4, Hkv=2, d=8, K=K, R=R)
+    r = run_layer(c, queries)
+    g = rng(seed + 1)
+    zsel = np.where(r["idx"].repeat(c["G"], axis=1) >= 0, g.standard_normal(r["zsel"].shape), -np.inf)
+    dO = g.standard_normal(r["o"].shape)
+    return c, r, zsel, dO
+
+
+def pin_attention_backward_finite_differences():
+    for K, R in ((2, 12), (4, 100)):                       # R=100 leaves rows with fewer than K candidates
+        queries = np.array([0, 3, 64, 150, 290, 377])
+        c, r, zsel, dO = _bwd_case(40 + K, K, R, queries)
+        qr = c["q"][:, :, O.slot_of(queries)]
+        args = dict(qr=qr, k=c["k"], v=c["v"], zs=np.where(np.isfinite(zsel), zsel, 0.0))
+        fin = np.isfinite(zsel)
+
+        def f(qr, k, v, zs):
+            o, _ = O.routed_attention(qr, k, v, r["idx"], np.where(fin, zs, -np.inf), R, c["scale"], queries)
+            return float(np.sum(o * dO))
+
+        dq, dk, dv, dz = OB.routed_attention_backward(qr, c["k"], c["v"], r["idx"], zsel, R, c["scale"],
+                                                      queries, dO)
+        if K == 4:
+            assert not fin.all(), "case must hold padded selections"
+        assert np.all(dz[~fin] == 0), "no gradient for padded selections"
+        _check_fd(f, args, dict(qr=dq, k=dk, v=dv, zs=dz), f"routed attention backward K={K} R={R}", seed=K)
+
+
+def _torch_attention_grads(qrows, kc, vc, mask, dO, scale):
+    """float64 torch autograd of masked attention; qrows [n,d], kc, vc [T,d], mask [n,T]."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)).requires_grad_(True) for a in (qrows, kc, vc))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq[None, None], tk[None, None], tv[None, None], attn_mask=torch.from_numpy(mask)[None, None], scale=scale)
+    (o[0, 0] * torch.from_numpy(dO)).sum().backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_attention_backward_window_only_is_library_autograd():
+    c = case(44, N=7, Hq=4, Hkv=2, d=8, K=0, R=37)
+    queries = np.arange(0, c["T"], 11)
+    r = run_layer(c, queries)
+    dO = rng(45).standard_normal(r["o"].shape)
+    dq, dk, dv, _ = OB.routed_attention_backward(c["q"][:, :, O.slot_of(queries)], c["k"], c["v"], r["idx"],
+                                                 r["zsel"], c["R"], c["scale"], queries, dO)
+    cs = content_slots(c["T"])
+    mask = np.abs(queries[:, None] - np.arange(c["T"])[None, :]) <= c["R"]
+    wk, wv = np.zeros_like(dk), np.zeros_like(dv)
+    for h in range(c["Hq"]):
+        g = h // c["G"]
+        gq, gk, gv = _torch_attention_grads(c["q"][0, h, O.slot_of(queries)], c["k"][0, g, cs], c["v"][0, g, cs],
+                                            mask, dO[0, h], c["scale"])
+        close(dq[0, h], gq, 1e-12, "window-only dq")
+        wk[0, g, cs] += gk
+        wv[0, g, cs] += gv
+    close(dk, wk, 1e-12, "window-only dk")
+    close(dv, wv, 1e-12, "window-only dv")
+
+
+def pin_attention_backward_lse_chunk_logits_is_flat_autograd():
+    """With zsel = log-sum-exp of the chunk's own logits (a function of q), the total
+    gradient is that of flat attention over the window and the chosen chunks: the
+    attention backward plus dzsel times the gradient of log-sum-exp (scale * pi k
+    for q, scale * pi q for k)."""
+    c = case(46, N=9, Hq=4, Hkv=2, d=8, K=3, R=30)
+    queries = np.array([5, 70, 200, 311, 450, 566])
+    r = run_layer(c, queries)
+    sc = c["scale"]
+    cs = content_slots(c["T"])
+    qr = c["q"][:, :, O.slot_of(queries)]
+    zsel = r["zsel"].copy()
+    pis = {}
+    for t in range(len(queries)):
+        for h in range(c["Hq"]):
+            g = h // c["G"]
+            for kk, n in enumerate(r["idx"][0, g, t]):
+                if n >= 0:
+                    ell = sc * c["k"][0, g, cs[n * CT:(n + 1) * CT]] @ qr[0, h, t]
+                    zsel[0, h, t, kk] = np.log(np.sum(np.exp(ell - ell.max()))) + ell.max()
+                    pis[(h, t, kk)] = np.exp(ell - zsel[0, h, t, kk])
+    dO = rng(47).standard_normal(r["o"].shape)
+    dq, dk, dv, dz = OB.routed_attention_backward(qr, c["k"], c["v"], r["idx"], zsel, c["R"], sc, queries, dO)
+    for (h, t, kk), pi in pis.items():
+        g = h // c["G"]
+        rows = cs[r["idx"][0, g, t, kk] * CT + np.arange(CT)]
+        dq[0, h, t] += dz[0, h, t, kk] * sc * pi @ c["k"][0, g, rows]
+        dk[0, g, rows] += dz[0, h, t, kk] * sc * pi[:, None] * qr[0, h, t][None, :]
+    wk, wv = np.zeros_like(dk), np.zeros_like(dv)
+    for h in range(c["Hq"]):
+        g = h // c["G"]
+        mask = np.zeros((len(queries), c["T"]), dtype=bool)
+        for t, i in enumerate(queries):
+            lo, hi = O.window_bounds(i, c["R"], c["T"])
+            mask[t, lo: hi + 1] = True
+            for n in r["idx"][0, g, t]:
+                if n >= 0:
+                    mask[t, n * CT:(n + 1) * CT] = True
+        gq, gk, gv = _torch_attention_grads(qr[0, h], c["k"][0, g, cs], c["v"][0, g, cs], mask, dO[0, h], sc)
+        close(dq[0, h], gq, 1e-12, "flat-equivalent dq")
+        wk[0, g, cs] += gk
+        wv[0, g, cs] += gv
+    close(dk, wk, 1e-12, "flat-equivalent dk")
+    close(dv, wv, 1e-12, "flat-equivalent dv")
+
+
+def pin_score_backward_finite_differences():
+    queries = np.array([0, 40, 130, 260, 377])
+    c, r, _, _ = _bwd_case(48, 3, 20, queries)
+    g = rng(49)
+    s = g.standard_normal((1, c["Hq"], c["N"], c["d"]))
+    H = np.abs(g.standard_normal((1, c["Hq"], c["N"])))
+    sl = O.slot_of(queries)
+    fin = r["idx"].repeat(c["G"], axis=1) >= 0
+    dzsel = np.where(fin, g.standard_normal(r["zsel"].shape), 0.0)
+    args = dict(qr=c["q"][:, :, sl], xr=c["x"][:, sl], A=c["A"], Bm=c["Bm"], s=s, H=H)
+
+    def f(qr, xr, A, Bm, s, H):
+        z = O.route_scores(O.routing_query(qr, xr, A, Bm), s, H, c["beta"], c["scale"])
+        zs = O.gather_zsel(z, r["idx"], c["G"])
+        return float(np.sum(np.where(fin, zs, 0.0) * dzsel))
+
+    dq, dx, dA, dBm, ds, dH = OB.route_score_backward(args["qr"], args["xr"], c["A"], c["Bm"], s, H, r["idx"],
+                                                      dzsel, c["beta"], c["scale"])
+    _check_fd(f, args, dict(qr=dq, xr=dx, A=dA, Bm=dBm, s=ds, H=dH), "route score backward", seed=7)
+
+
+def pin_summary_backward_finite_differences():
+    c = case(50, N=5, Hq=4, Hkv=2, d=8)
+    g = rng(51)
+    qm = c["q"].reshape(1, c["Hq"], c["N"], SL, c["d"])[:, :, :, SL - 1]
+    ds = g.standard_normal((1, c["Hq"], c["N"], c["d"]))
+    dH = g.standard_normal((1, c["Hq"], c["N"]))
+    args = dict(qm=qm, k=c["k"])
+
+    def f(qm, k):
+        s, H = O.chunk_summary_from_mask(qm, k, c["scale"])
+        return float(np.sum(s * ds) + np.sum(H * dH))
+
+    dq, dk = OB.chunk_summary_backward(qm, c["k"], c["scale"], ds, dH)
+    _check_fd(f, args, dict(qm=dq, k=dk), "chunk summary backward", seed=8)
+    assert np.all(dk.reshape(1, c["Hkv"], c["N"], SL, c["d"])[:, :, :, SL - 1] == 0), "mask-slot keys get nothing"
+
+
+def pin_summary_backward_uniform_point():
+    """Zero mask query: uniform weights. Entropy is at its maximum (no gradient from dH);
+    the summary's gradient is scale * Cov(k) ds for the query and ds/63 for each key."""
+    c = case(52, N=4, Hq=2, Hkv=1, d=8)
+    g = rng(53)
+    qm = np.zeros((1, c["Hq"], c["N"], c["d"]))
+    ds = g.standard_normal((1, c["Hq"], c["N"], c["d"]))
+    dH = g.standard_normal((1, c["Hq"], c["N"]))
+    dq_h, dk_h = OB.chunk_summary_backward(qm, c["k"], c["scale"], np.zeros_like(ds), dH)
+    close(dq_h, 0.0, 1e-13, "entropy is stationary at uniform weights")
+    close(dk_h, 0.0, 1e-13, "entropy gradient on keys at a zero query")
+    dq, dk = OB.chunk_summary_backward(qm, c["k"], c["scale"], ds, np.zeros_like(dH))
+    kc = c["k"].reshape(1, 1, c["N"], SL, c["d"])[0, 0, :, :CT]
+    for n in range(c["N"]):
+        cov = np.cov(kc[n].T, bias=True)
+        for h in range(c["Hq"]):
+            close(dq[0, h, n], c["scale"] * cov @ ds[0, h, n], 1e-13, "covariance closed form")
+        close(dk.reshape(1, 1, c["N"], SL, c["d"])[0, 0, n, :CT],
+              np.repeat(ds[0, :, n].sum(0)[None] / CT, CT, axis=0), 1e-13, "uniform key gradient")
+
+
+def pin_layer_backward_finite_differences():
+    queries = np.array([2, 66, 190, 301, 377])
+    c, r, _, dO = _bwd_case(54, 3, 15, queries)
+    idx = r["idx"]
+    sl = O.slot_of(queries)
+    G, N, sc = c["G"], c["N"], c["scale"]
+
+    def f(q, k, v, x, A, Bm):
+        qm = q.reshape(1, c["Hq"], N, SL, c["d"])[:, :, :, SL - 1]
+        s, H = O.chunk_summary_from_mask(qm, k, sc)
+        z = O.route_scores(O.routing_query(q[:, :, sl], x[:, sl], A, Bm), s, H, c["beta"], sc)
+        o, _ = O.routed_attention(q[:, :, sl], k, v, idx, O.gather_zsel(z, idx, G), c["R"], sc, queries)
+        return float(np.sum(o * dO))
+
+    args = dict(q=c["q"], k=c["k"], v=c["v"], x=c["x"], A=c["A"], Bm=c["Bm"])
+    gr = OB.route_layer_backward(c["q"], c["k"], c["v"], c["x"], c["A"], c["Bm"], idx, dO, R=c["R"],
+                                 beta=c["beta"], scale=sc, queries=queries)
+    _check_fd(f, args, dict(q=gr["dq"], k=gr["dk"], v=gr["dv"], x=gr["dx"], A=gr["dA"], Bm=gr["dBm"]),
+              "route layer backward", seed=9)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -9,10 +9,12 @@ import numpy as np
 import pytest
 
 import oracle_pins
+from oracle import backward as OB
 from oracle import route as O
 
 SL, CT = 64, 63
 _orig = {name: getattr(O, name) for name in dir(O) if not name.startswith("__")}
+_orig_b = {name: getattr(OB, name) for name in dir(OB) if not name.startswith("__")}
 
 
 def _scores_entropy_plus(qt, s, H, beta, scale):
@@ -179,6 +181,66 @@ def test_mutation_is_caught(name, monkeypatch):
         try:
             pin()
         except Exception as e:  # an assertion or a crash both count as detection
+            caught.append(f"{pin.__name__}: {type(e).__name__}")
+            break
+    assert caught, f"no pin detects the planted mistake: {name}"
+
+
+# ----------------------------------------------------------------------------- backward mutations (module OB)
+
+def _softmax_bwd_no_mean(p, g, axis=-1):
+    return p * g
+
+
+def _summary_bwd_entropy_sign(q_mask, k, scale, ds, dH):
+    return _orig_b["chunk_summary_backward"](q_mask, k, scale, ds, -dH)
+
+
+def _summary_bwd_no_key_pooling_term(q_mask, k, scale, ds, dH):
+    dq, dk = _orig_b["chunk_summary_backward"](q_mask, k, scale, ds, dH)
+    dq0, dk0 = _orig_b["chunk_summary_backward"](q_mask, k, scale, ds * 0, dH)
+    return dq, dk0 + 0.5 * (dk - dk0)
+
+
+def _score_bwd_residual_dropped(*a):
+    dqt, dx, dA, dBm, ds, dH = _orig_b["route_score_backward"](*a)
+    return dqt, dx * 0, dA * 0, dBm * 0, ds, dH
+
+
+def _score_bwd_entropy_sign(*a):
+    dqt, dx, dA, dBm, ds, dH = _orig_b["route_score_backward"](*a)
+    return dqt, dx, dA, dBm, ds, -dH
+
+
+def _attn_bwd_no_dzsel(*a):
+    dq, dk, dv, dz = _orig_b["routed_attention_backward"](*a)
+    return dq, dk, dv, dz * 0
+
+
+def _attn_bwd_chunk_softmax_uniform(qh, kc, vc, scale):
+    return np.broadcast_to(vc.mean(axis=1)[None], (qh.shape[0],) + vc.mean(axis=1).shape).copy()
+
+
+BWD_MUTATIONS = {
+    "softmax backward without its mean term": ("_softmax_backward", _softmax_bwd_no_mean),
+    "pooling entropy gradient sign flipped": ("chunk_summary_backward", _summary_bwd_entropy_sign),
+    "pooling key gradient halved": ("chunk_summary_backward", _summary_bwd_no_key_pooling_term),
+    "no gradient into the low-rank residual": ("route_score_backward", _score_bwd_residual_dropped),
+    "scoring entropy gradient sign flipped": ("route_score_backward", _score_bwd_entropy_sign),
+    "no gradient into the chunk logits": ("routed_attention_backward", _attn_bwd_no_dzsel),
+    "backward recomputes a uniform intra-chunk softmax": ("chunk_attention", _attn_bwd_chunk_softmax_uniform),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_backward_mutation_is_caught(name, monkeypatch):
+    attr, fn = BWD_MUTATIONS[name]
+    monkeypatch.setattr(OB, attr, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:
             caught.append(f"{pin.__name__}: {type(e).__name__}")
             break
     assert caught, f"no pin detects the planted mistake: {name}"
