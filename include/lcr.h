@@ -65,7 +65,8 @@ typedef enum {
   LCR_OP_CHUNK_SUMMARY = 0,
   LCR_OP_ROUTE_SCORE_TOPK = 1,
   LCR_OP_ROUTED_ATTENTION = 2,
-  LCR_OP_SWA_ATTENTION = 3
+  LCR_OP_SWA_ATTENTION = 3,
+  LCR_OP_ROUTED_ATTENTION_BACKWARD = 4
 } lcr_op;
 
 /* Library version as 10000*major + 100*minor + patch. */
@@ -183,6 +184,39 @@ int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, con
                          const int32_t* idx, const float* zsel, int K, int radius, float scale,
                          int q0, int nq, void* o, float* lse, void* ws, size_t ws_bytes,
                          void* stream);
+
+/*
+ * Gradients of lcr_routed_attention with the chosen chunks held fixed ("The 172x
+ * Speedup Has an Evidence Budget", section "How learned routing controls what
+ * the model can read": chunk membership is not differentiable; the router is
+ * trained through the masses of the selected chunks, i.e. through zsel).
+ *
+ * With P, pi and u_bar as in lcr_routed_attention, dO the upstream gradient on
+ * o and D = dO . o per (head, query):
+ *   dzsel[b,h,t,k] = P_k (dO . u_bar_k - D)          (0 where idx is -1)
+ *   dq, dk, dv     = the gradients of o through every window key and every
+ *                    content key of the selected chunks (chain rule through the
+ *                    joint partition and the intra-chunk softmax)
+ *
+ * Inputs exactly as passed to (and produced by) the forward call: q, k, v, idx,
+ * zsel, K, radius, scale, q0, nq; o [B,Hq,L,d] and lse [B,Hq,nq] (both
+ * required); dO [B,Hq,L,d] (rows slot(i) read). dtype must be LCR_BF16.
+ * Outputs, float32: dq [B,Hq,L,d] (only rows slot(i) of the queried i are
+ * written); dk, dv [B,Hkv,L,d] (every row written: rows no queried row reads,
+ * mask slots included, are zero); dzsel [B,Hq,nq,K] (may be NULL when K = 0).
+ * Only the nq queried rows contribute. ws: lcr_workspace_bytes(
+ * LCR_OP_ROUTED_ATTENTION_BACKWARD, dims, 0, 0, K, radius, nq) bytes, contents
+ * need not be initialised. Arithmetic: bf16 products (probabilities and their
+ * gradients rounded to bf16 for the products), float32 accumulation. The
+ * summation order of dk and dv over the rows that selected a chunk depends on
+ * scheduling, so those two outputs agree between runs to float32 rounding.
+ * Errors: as lcr_routed_attention; LCR_ERR_UNSUPPORTED for LCR_F32 inputs.
+ */
+int lcr_routed_attention_backward(const lcr_dims* dims, const void* q, const void* k, const void* v,
+                                  const int32_t* idx, const float* zsel, int K, int radius, float scale,
+                                  int q0, int nq, const void* o, const float* lse, const void* dO,
+                                  float* dq, float* dk, float* dv, float* dzsel, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /*
  * Bidirectional sliding-window attention for the layers that do not route

@@ -15,10 +15,11 @@ from .gen import (
     decode_step,
     stack_layer_torch,
     sample_query_blocks,
+    backward_draws,
 )
 
 __all__ = [
     "CONFIGS", "Config", "get_config", "bf16_round", "bf16_to_f64", "as_f64",
     "route_inputs", "decode_cache", "decode_step", "stack_layer_torch",
-    "sample_query_blocks",
+    "sample_query_blocks", "backward_draws",
 ]

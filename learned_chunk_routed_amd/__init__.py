@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     chunk_summary_mean,
     route_score_topk,
     routed_attention,
+    routed_attention_backward,
     swa_attention,
     route_layer,
     workspace_bytes,

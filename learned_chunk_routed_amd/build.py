@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "liblcr.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["summary.hip", "score.hip", "attention.hip", "api.cpp"]
+HIP_SOURCES = ["summary.hip", "score.hip", "attention.hip", "backward.hip", "api.cpp"]
 HOST_SOURCES = ["validate.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

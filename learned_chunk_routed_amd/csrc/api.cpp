@@ -47,6 +47,8 @@ size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, in
       return (K > 0 && nq > 0 && D > 0 && r > 0 && r <= 128) ? score_ws_bytes(dm, D, r, nq) : 0;
     case LCR_OP_ROUTED_ATTENTION:
       return nq > 0 ? plan_routed_attention(dm, K, radius, nq).ws : 0;
+    case LCR_OP_ROUTED_ATTENTION_BACKWARD:
+      return routed_bwd_ws_bytes(dm, K, nq);
     default:
       return 0;
   }
@@ -101,6 +103,21 @@ int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, con
   if (plan.ws > 0 && (ws == nullptr || ws_bytes < plan.ws)) return LCR_ERR_WORKSPACE;
   return hip_status(launch_routed_attention(dm, plan, q, k, v, K > 0 ? idx : nullptr, K > 0 ? zsel : nullptr, K,
                                             radius, scale, q0, nq, o, lse, ws, (hipStream_t)stream));
+}
+
+int lcr_routed_attention_backward(const lcr_dims* dims, const void* q, const void* k, const void* v,
+                                  const int32_t* idx, const float* zsel, int K, int radius, float scale, int q0,
+                                  int nq, const void* o, const float* lse, const void* dO, float* dq, float* dk,
+                                  float* dv, float* dzsel, void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_routed_attention_backward(dims, q, k, v, idx, zsel, K, radius, scale, q0, nq, o, lse, dO,
+                                                 dq, dk, dv, dzsel);
+  if (st != LCR_OK) return st;
+  const RouteDims dm = to_route_dims(dims);
+  const size_t need = routed_bwd_ws_bytes(dm, K, nq);
+  if (ws == nullptr || ws_bytes < need) return LCR_ERR_WORKSPACE;
+  return hip_status(launch_routed_attention_backward(dm, q, k, v, K > 0 ? idx : nullptr, K > 0 ? zsel : nullptr, K,
+                                                     radius, scale, q0, nq, o, lse, dO, dq, dk, dv,
+                                                     K > 0 ? dzsel : nullptr, ws, (hipStream_t)stream));
 }
 
 int lcr_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, const void* k, const void* v,

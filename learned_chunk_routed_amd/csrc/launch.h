@@ -60,6 +60,15 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& plan, co
                                    const float* zsel, int K, int radius, float scale, int q0,
                                    int nq, void* o, float* lse, void* ws, hipStream_t st);
 
+// ---- routed attention backward (backward.hip), bf16 only
+size_t routed_bwd_ws_bytes(const RouteDims& dm, int K, int nq);
+size_t routed_bwd_lds_bytes(int d);
+hipError_t launch_routed_attention_backward(const RouteDims& dm, const void* q, const void* k, const void* v,
+                                            const int32_t* idx, const float* zsel, int K, int radius,
+                                            float scale, int q0, int nq, const void* o, const float* lse,
+                                            const void* dO, float* dq, float* dk, float* dv, float* dzsel,
+                                            void* ws, hipStream_t st);
+
 size_t swa_lds_bytes(int d, int dtype);
 hipError_t launch_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q,
                                 const void* k, const void* v, int radius, float scale, void* o,

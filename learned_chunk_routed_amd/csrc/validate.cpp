@@ -85,6 +85,23 @@ int check_routed_attention(const lcr_dims* d, const void* q, const void* k, cons
   return LCR_OK;
 }
 
+int check_routed_attention_backward(const lcr_dims* d, const void* q, const void* k, const void* v,
+                                    const int32_t* idx, const float* zsel, int K, int radius, float scale,
+                                    int q0, int nq, const void* o, const float* lse, const void* dO,
+                                    const float* dq, const float* dk, const float* dv, const float* dzsel) {
+  int st = check_routed_attention(d, q, k, v, idx, zsel, K, radius, scale, q0, nq, o);
+  if (st != LCR_OK) return st;
+  if (d->dtype != LCR_BF16) return LCR_ERR_UNSUPPORTED;
+  if (!dk || !dv) return LCR_ERR_ARG;
+  if (nq > 0) {
+    if (!lse || !dO || !dq) return LCR_ERR_ARG;
+    if (K > 0 && !dzsel) return LCR_ERR_ARG;
+  }
+  // entry lists index nq*K entries per (batch, group) with int32
+  if ((long long)nq * K > (long long)std::numeric_limits<int>::max()) return LCR_ERR_UNSUPPORTED;
+  return LCR_OK;
+}
+
 int check_swa(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, const void* k, const void* v,
               int radius, float scale, const void* o) {
   if (dtype != LCR_F32 && dtype != LCR_BF16) return LCR_ERR_DTYPE;

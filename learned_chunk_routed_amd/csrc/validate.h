@@ -20,6 +20,10 @@ int check_route_score_topk(const lcr_dims* d, const void* q, const void* x, cons
 int check_routed_attention(const lcr_dims* d, const void* q, const void* k, const void* v,
                            const int32_t* idx, const float* zsel, int K, int radius, float scale, int q0,
                            int nq, const void* o);
+int check_routed_attention_backward(const lcr_dims* d, const void* q, const void* k, const void* v,
+                                    const int32_t* idx, const float* zsel, int K, int radius, float scale,
+                                    int q0, int nq, const void* o, const float* lse, const void* dO,
+                                    const float* dq, const float* dk, const float* dv, const float* dzsel);
 int check_swa(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, const void* k, const void* v,
               int radius, float scale, const void* o);
 

@@ -186,6 +186,44 @@ def routed_attention(q, k, v, idx, zsel, *, radius, scale=None, q0=0, nq=None, o
     return (out, lse) if (want_lse or lse is not None) else out
 
 
+def routed_attention_backward(q, k, v, idx, zsel, o, lse, dO, *, radius, scale=None, q0=0, nq=None, ws=None):
+    """Gradients of routed_attention with the chosen chunks fixed (bf16 inputs).
+
+    o and lse are the forward's outputs; dO [B,Hq,L,d] bf16 (rows of the queried
+    positions are read). Returns dq [B,Hq,L,d] (queried rows written, other rows
+    zero), dk, dv [B,Hkv,L,d] and dzsel [B,Hq,nq,K], all float32."""
+    lib = _lib.load()
+    dev = q.device
+    dims = _dims_from(q, k.shape[1])
+    B, Hq, Hkv, N, d = dims.B, dims.Hq, dims.Hkv, dims.N, dims.d
+    T = N * CONTENT
+    nq = T - q0 if nq is None else nq
+    K = idx.shape[-1]
+    _need(q.dtype == torch.bfloat16, "routed_attention_backward takes bfloat16 q, k, v, o, dO")
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (B, Hkv, N * SLOTS, d))
+    _check(v, "v", dev, q.dtype, (B, Hkv, N * SLOTS, d))
+    _check(o, "o", dev, q.dtype, tuple(q.shape))
+    _check(dO, "dO", dev, q.dtype, tuple(q.shape))
+    _check(idx, "idx", dev, torch.int32, (B, Hkv, nq, K))
+    _check(zsel, "zsel", dev, torch.float32, (B, Hq, nq, K))
+    _check(lse, "lse", dev, torch.float32, (B, Hq, nq))
+    scale = default_scale(d) if scale is None else float(scale)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    dz = torch.empty((B, Hq, nq, K), dtype=torch.float32, device=dev)
+    nbytes = workspace_bytes(_lib.OP_ROUTED_ATTENTION_BACKWARD, dims, 0, 0, K, nq, radius)
+    w = _workspace(nbytes, dev, ws)
+    check(lib.lcr_routed_attention_backward(dims, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+                                            zsel.data_ptr(), K, radius, scale, q0, nq, o.data_ptr(),
+                                            lse.data_ptr(), dO.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                            dv.data_ptr(), dz.data_ptr() if K > 0 else None,
+                                            None if w is None else w.data_ptr(), nbytes, _stream(dev)),
+          "lcr_routed_attention_backward")
+    return dq, dk, dv, dz
+
+
 def swa_attention(q, k, v, *, radius, scale=None, out=None, lse=None, want_lse=False):
     """Bidirectional sliding-window attention over slots |u - t| <= radius: o [B,Hq,L,d]."""
     lib = _lib.load()

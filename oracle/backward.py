@@ -20,7 +20,7 @@ float64 attention autograd.
 """
 import numpy as np
 
-from .route import SLOTS, CONTENT, slot_of, softmax, window_bounds, partition, chunk_attention
+from .route import SLOTS, CONTENT, slot_of, softmax, window_bounds, partition
 
 
 def _softmax_backward(p, g, axis=-1):
@@ -66,16 +66,16 @@ def routed_attention_backward(q_rows, k, v, idx, zsel, R, scale, queries, do_row
                 m = len(sel)
                 cs = sel[:, None] * SLOTS + jj[None, :]                 # [m,63]
                 kc, vc = k[b, g, cs], v[b, g, cs]                       # [m,63,d]
-                # forward, kept for the backward
+                # forward, kept for the backward (chunk-major arrays [m,G,...])
                 a = scale * qh @ kw.T                                   # [G,W]
                 zc = zsel[b, hs, t, :m]                                 # [G,m]
                 Pu, Pc, _ = partition(a, zc)
-                pi = softmax(scale * np.einsum("hd,cjd->hcj", qh, kc), axis=-1)   # [G,m,63]
-                ubar = chunk_attention(qh, kc, vc, scale)              # [G,m,d]
+                pi = softmax(scale * (qh @ kc.transpose(0, 2, 1)), axis=-1)   # [m,G,63]
+                ubar = pi @ vc                                          # [m,G,d]
                 # o = Pu vw + sum_c Pc ubar_c
                 gPu = dO @ vw.T                                         # dL/dPu  [G,W]
-                gPc = np.einsum("hd,hcd->hc", dO, ubar)                 # dL/dPc  [G,m]
-                gubar = Pc[:, :, None] * dO[:, None, :]                 # dL/dubar [G,m,d]
+                gPc = np.sum(dO[None] * ubar, axis=-1).T                # dL/dPc  [G,m]
+                gubar = Pc.T[:, :, None] * dO[None]                     # dL/dubar [m,G,d]
                 dv[b, g, ws] += Pu.T @ dO
                 # partition: one softmax over [a, zc]
                 gx = _softmax_backward(np.concatenate([Pu, Pc], axis=1),
@@ -85,11 +85,11 @@ def routed_attention_backward(q_rows, k, v, idx, zsel, R, scale, queries, do_row
                 dq[b, hs, t] += scale * da @ kw
                 dk[b, g, ws] += scale * da.T @ qh
                 # chunk attention: ubar = pi vc, pi = softmax(scale q kc^T)
-                dv[b, g, cs] += np.einsum("hcj,hcd->cjd", pi, gubar)
-                gpi = np.einsum("hcd,cjd->hcj", gubar, vc)
-                dl = _softmax_backward(pi, gpi)                         # [G,m,63]
-                dq[b, hs, t] += scale * np.einsum("hcj,cjd->hd", dl, kc)
-                dk[b, g, cs] += scale * np.einsum("hcj,hd->cjd", dl, qh)
+                dv[b, g, cs] += pi.transpose(0, 2, 1) @ gubar
+                gpi = gubar @ vc.transpose(0, 2, 1)                     # [m,G,63]
+                dl = _softmax_backward(pi, gpi)
+                dq[b, hs, t] += scale * np.sum(dl @ kc, axis=0)
+                dk[b, g, cs] += scale * dl.transpose(0, 2, 1) @ qh
     return dq, dk, dv, dz
 
 

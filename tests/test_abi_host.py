@@ -181,6 +181,36 @@ def test_routed_attention_validation(lib):
     assert call(dm=dims(N=2048), q0=2048 * 63 - 32, nq=32) == _lib.LCR_ERR_WORKSPACE
 
 
+def test_routed_attention_backward_validation(lib):
+    def call(dm=None, K=32, R=256, scale=0.1, q0=0, nq=100, ptrs=None, ws=P, ws_bytes=1 << 40):
+        pt = ptrs or [P] * 13
+        return lib.lcr_routed_attention_backward(dm or dims(), pt[0], pt[1], pt[2], pt[3], pt[4], K, R, scale, q0,
+                                                 nq, pt[5], pt[6], pt[7], pt[8], pt[9], pt[10], pt[11], ws,
+                                                 ws_bytes, NULL)
+    assert call(dm=dims(dtype=0)) == _lib.LCR_ERR_UNSUPPORTED          # float32 inputs: not in this build
+    assert call(K=-1) == _lib.LCR_ERR_ARG
+    assert call(K=65) == _lib.LCR_ERR_UNSUPPORTED
+    assert call(R=-5) == _lib.LCR_ERR_ARG
+    assert call(q0=256 * 63, nq=1) == _lib.LCR_ERR_ARG
+    assert call(scale=float("inf")) == _lib.LCR_ERR_ARG
+    for i in range(12):          # q k v idx zsel o lse dO dq dk dv dzsel: every one is required
+        pt = [P] * 13
+        pt[i] = NULL
+        assert call(ptrs=pt) == _lib.LCR_ERR_ARG, i
+    # K = 0: idx, zsel and dzsel may be NULL
+    pt = [P] * 13
+    pt[3] = pt[4] = pt[11] = NULL
+    need0 = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION_BACKWARD, dims(), 0, 0, 0, 256, 100)
+    assert need0 > 0
+    assert call(K=0, ptrs=pt, ws=NULL) == _lib.LCR_ERR_WORKSPACE
+    need = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION_BACKWARD, dims(), 0, 0, 32, 256, 100)
+    assert call(ws_bytes=need - 1) == _lib.LCR_ERR_WORKSPACE
+    al = lambda x: (x + 255) // 256 * 256
+    rows, bgn = 28 * 100, 4 * 256
+    # D per row; bias and U per (row, selected chunk); counts, cursors and offsets per chunk; the entry lists
+    assert need == al(rows * 4) + 2 * al(rows * 32 * 4) + 2 * al(bgn * 4) + al(4 * 257 * 4) + al(4 * 100 * 32 * 4)
+
+
 def test_swa_validation(lib):
     def call(B=1, Hq=28, Hkv=4, L=4096, d=128, dtype=1, R=1280, scale=0.1, ptrs=None):
         pt = ptrs or [P] * 4

@@ -1,0 +1,167 @@
+"""Backward of routed attention: HIP path against the fp64 oracle, through the C ABI.
+
+Selections: random chunk scores ranked over each query's remote chunks by the
+oracle's own candidate and top-K functions (any valid selection is a valid
+input to the backward), or, in one case, the oracle route layer's selection.
+Chunk logits are seeded normals. Both sides receive identical bits.
+
+Tolerance: bf16 products with the probabilities and their gradients rounded to
+bf16 (relative 2^-9 each) and float32 sums, so every gradient must lie within
+2e-2 of the oracle's in max-abs error relative to max(1, max |oracle|).
+
+Tiny cases are checked in full. The 16K prefill layer runs at full size in the
+launch configuration the benchmark times; dq and dzsel are checked on sampled
+query blocks, dk and dv on sampled chunks against the oracle run over every
+query that reaches those chunks (its window queries and every query that
+selected it).
+"""
+import numpy as np
+import pytest
+import torch
+
+import learned_chunk_routed_amd as lcr
+from lcr_inputs import as_f64, backward_draws, get_config, route_inputs, sample_query_blocks
+from oracle import backward as OB
+from oracle import route as O
+from gpu_util import to_dev, f64
+
+pytestmark = pytest.mark.gpu
+
+BWD_TOL = 2e-2
+SL, CT = 64, 63
+
+
+def rel_err(a, b):
+    b = np.asarray(b)
+    if b.size == 0:
+        return 0.0
+    return float(np.max(np.abs(np.asarray(a) - b))) / max(1.0, float(np.max(np.abs(b))))
+
+
+def selection(cfg, draws, q0, nq):
+    """idx [B,Hkv,nq,K] int64 and zsel [B,Hq,nq,K] (float32 values, -inf padding)."""
+    queries = np.arange(q0, q0 + nq)
+    cand = O.candidate_mask(queries, cfg.R, cfg.N)
+    idx, _ = O.select_topk(draws["score"].astype(np.float64), cand, cfg.K)
+    fin = np.repeat(idx, cfg.G, axis=1) >= 0
+    zsel = np.where(fin, draws["zsel"], -np.inf).astype(np.float32)
+    return idx, zsel
+
+
+def run_gpu(cfg, inp, dO_bits, idx, zsel, q0, nq):
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    idx_t = torch.from_numpy(idx.astype(np.int32)).cuda()
+    z_t = torch.from_numpy(np.ascontiguousarray(zsel)).cuda()
+    o, lse = lcr.routed_attention(q, k, v, idx_t, z_t, radius=cfg.R, scale=cfg.scale, q0=q0, nq=nq,
+                                  want_lse=True)
+    dq, dk, dv, dz = lcr.routed_attention_backward(q, k, v, idx_t, z_t, o, lse, to_dev(dO_bits), radius=cfg.R,
+                                                   scale=cfg.scale, q0=q0, nq=nq)
+    torch.cuda.synchronize()
+    return f64(dq), f64(dk), f64(dv), f64(dz)
+
+
+TINY = {
+    "d128 G4": dict(N=12, Hq=8, Hkv=2, d=128, K=3, R=40),
+    "d64 G1 ragged partial range": dict(N=10, Hq=2, Hkv=2, d=64, K=2, R=20, q0=37, nq=301),
+    "G8 fewer candidates than K": dict(N=8, Hq=8, Hkv=1, d=128, K=6, R=150),
+    "window only K=0": dict(N=8, Hq=4, Hkv=1, d=64, K=0, R=70),
+    "B2 G7": dict(B=2, N=9, Hq=14, Hkv=2, d=128, K=4, R=30),
+    "radius 0": dict(N=6, Hq=4, Hkv=1, d=128, K=2, R=0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TINY))
+def test_backward_tiny(name):
+    kw = dict(TINY[name])
+    q0 = kw.pop("q0", 0)
+    nq = kw.pop("nq", None)
+    cfg = get_config("prefill_16k", dtype="bf16", **kw)
+    nq = cfg.T - q0 if nq is None else nq
+    print(f"[case] backward {name}: B={cfg.B} N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} K={cfg.K} R={cfg.R} "
+          f"q0={q0} nq={nq}", flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, q0, nq)
+    idx, zsel = selection(cfg, dr, q0, nq)
+    gq, gk, gv, gz = run_gpu(cfg, inp, dr["dO"], idx, zsel, q0, nq)
+    queries = np.arange(q0, q0 + nq)
+    sl = O.slot_of(queries)
+    q, k, v = as_f64(inp["q"]), as_f64(inp["k"]), as_f64(inp["v"])
+    dO = as_f64(dr["dO"])
+    rq, rk, rv, rz = OB.routed_attention_backward(q[:, :, sl], k, v, idx, zsel.astype(np.float64), cfg.R,
+                                                  cfg.scale, queries, dO[:, :, sl])
+    errs = dict(dq=rel_err(gq[:, :, sl], rq), dk=rel_err(gk, rk), dv=rel_err(gv, rv),
+                dzsel=rel_err(np.where(np.isfinite(zsel), gz, 0.0), rz))
+    print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e < BWD_TOL, f"{name}: {n} error {e:.3e}"
+    # rows outside the queried set stay zero in the binding's dq; mask-slot rows of dk, dv are zero
+    other = np.setdiff1d(np.arange(cfg.L), sl)
+    assert np.all(gq[:, :, other] == 0)
+    assert np.all(gk[:, :, SL - 1::SL] == 0) and np.all(gv[:, :, SL - 1::SL] == 0)
+    if cfg.K:
+        assert np.all(gz[~np.isfinite(zsel)] == 0), "padded selections get no gradient"
+
+
+def test_backward_layer_selection():
+    """The selection and chunk logits of the oracle route layer itself (a real top-K)."""
+    cfg = get_config("prefill_16k", N=10, Hq=8, Hkv=2, d=128, K=3, R=30, beta=0.2)
+    print("[case] backward with the oracle layer's own selection", flush=True)
+    inp = route_inputs(cfg)
+    f = {n: as_f64(inp[n]) for n in ("q", "k", "v", "x", "A", "Bm")}
+    queries = np.arange(cfg.T)
+    ref = O.route_layer(f["q"], f["k"], f["v"], f["x"], f["A"], f["Bm"], K=cfg.K, R=cfg.R, beta=cfg.beta,
+                        scale=cfg.scale, queries=queries)
+    zsel = ref["zsel"].astype(np.float32)
+    dr = backward_draws(cfg, 0, cfg.T)
+    gq, gk, gv, gz = run_gpu(cfg, inp, dr["dO"], ref["idx"], zsel, 0, cfg.T)
+    sl = O.slot_of(queries)
+    rq, rk, rv, rz = OB.routed_attention_backward(f["q"][:, :, sl], f["k"], f["v"], ref["idx"],
+                                                  zsel.astype(np.float64), cfg.R, cfg.scale, queries,
+                                                  as_f64(dr["dO"])[:, :, sl])
+    errs = dict(dq=rel_err(gq[:, :, sl], rq), dk=rel_err(gk, rk), dv=rel_err(gv, rv),
+                dzsel=rel_err(np.where(np.isfinite(zsel), gz, 0.0), rz))
+    print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e < BWD_TOL, f"{n} error {e:.3e}"
+
+
+@pytest.mark.timeout(300)
+def test_backward_prefill_16k_sampled():
+    cfg = get_config("prefill_16k")
+    q0, nq = 0, cfg.T
+    print(f"[case] backward prefill_16k full size: N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} K={cfg.K} R={cfg.R}",
+          flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, q0, nq)
+    idx, zsel = selection(cfg, dr, q0, nq)
+    gq, gk, gv, gz = run_gpu(cfg, inp, dr["dO"], idx, zsel, q0, nq)
+    k, v = as_f64(inp["k"]), as_f64(inp["v"])
+    G = cfg.G
+    # dq and dzsel on sampled query blocks (all heads)
+    queries = sample_query_blocks(cfg.T, n_blocks=4, block=32, seed=5)
+    sl = O.slot_of(queries)
+    qrows = as_f64(inp["q"][:, :, sl])
+    dOrows = as_f64(dr["dO"][:, :, sl])
+    rq, _, _, rz = OB.routed_attention_backward(qrows, k, v, idx[:, :, queries], zsel[:, :, queries].astype(
+        np.float64), cfg.R, cfg.scale, queries, dOrows)
+    e_q = rel_err(gq[:, :, sl], rq)
+    zs = zsel[:, :, queries]
+    e_z = rel_err(np.where(np.isfinite(zs), gz[:, :, queries], 0.0), rz)
+    print(f"    sampled rows={len(queries)} dq={e_q:.2e} dzsel={e_z:.2e}", flush=True)
+    assert e_q < BWD_TOL and e_z < BWD_TOL
+    # dk and dv on sampled chunks: every query that reaches the chunk, one KV group at a time
+    for g, c in ((0, 0), (2, cfg.N // 2 + 3)):
+        lo, hi = max(0, c * CT - cfg.R), min(cfg.T - 1, c * CT + CT - 1 + cfg.R)
+        sel_t = np.nonzero(np.any(idx[0, g] == c, axis=-1))[0]
+        qs = np.union1d(np.arange(lo, hi + 1), sel_t)
+        hs = slice(g * G, (g + 1) * G)
+        slq = O.slot_of(qs)
+        _, rk, rv, _ = OB.routed_attention_backward(
+            as_f64(inp["q"][:, hs][:, :, slq]), k[:, g:g + 1], v[:, g:g + 1], idx[:, g:g + 1][:, :, qs],
+            zsel[:, hs][:, :, qs].astype(np.float64), cfg.R, cfg.scale, qs, as_f64(dr["dO"][:, hs][:, :, slq]))
+        rows = slice(c * SL, c * SL + SL)
+        e_k = rel_err(gk[:, g, rows], rk[:, 0, rows])
+        e_v = rel_err(gv[:, g, rows], rv[:, 0, rows])
+        print(f"    group {g} chunk {c}: {len(qs)} queries ({len(sel_t)} selecting) dk={e_k:.2e} dv={e_v:.2e}",
+              flush=True)
+        assert e_k < BWD_TOL and e_v < BWD_TOL

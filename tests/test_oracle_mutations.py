@@ -217,8 +217,8 @@ def _attn_bwd_no_dzsel(*a):
     return dq, dk, dv, dz * 0
 
 
-def _attn_bwd_chunk_softmax_uniform(qh, kc, vc, scale):
-    return np.broadcast_to(vc.mean(axis=1)[None], (qh.shape[0],) + vc.mean(axis=1).shape).copy()
+def _bwd_softmax_wrong_axis(x, axis=-1):
+    return _orig["softmax"](x, axis=0 if x.ndim > 1 and x.shape[0] > 1 else axis)
 
 
 BWD_MUTATIONS = {
@@ -228,7 +228,7 @@ BWD_MUTATIONS = {
     "no gradient into the low-rank residual": ("route_score_backward", _score_bwd_residual_dropped),
     "scoring entropy gradient sign flipped": ("route_score_backward", _score_bwd_entropy_sign),
     "no gradient into the chunk logits": ("routed_attention_backward", _attn_bwd_no_dzsel),
-    "backward recomputes a uniform intra-chunk softmax": ("chunk_attention", _attn_bwd_chunk_softmax_uniform),
+    "backward recomputes the intra-chunk softmax over the wrong axis": ("softmax", _bwd_softmax_wrong_axis),
 }
 
 
