@@ -18,9 +18,11 @@ Printed JSON line (one, rank 0):
   swa_64k      ms per sliding-window layer (65,536 slots, radius 1280)
   dense_16k    ms per dense bidirectional attention layer (16,384 slots, every
                slot attends to every slot: the sliding window with R >= L)
+  backward_16k ms per backward call of the routed attention on the 16K-prefill
+               workload (dq, dk, dv, dzsel), with its MFMA roofline
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--no-decode] [--no-swa] [--only {prefill,decode,swa,dense,copy}]
+       [--no-decode] [--no-swa] [--only {prefill,decode,swa,dense,backward,copy}]
 (--only copy runs a plain 1 GiB device copy, used to calibrate byte counters.)
 """
 import argparse
@@ -372,6 +374,44 @@ def bench_dense(args, torch, lcr):
                                                      "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def bench_backward(args, torch, lcr):
+    """Backward of the routed attention over the 16K-prefill workload: the forward's own
+    selection, chunk logits, output and log-normaliser (computed once, untimed) and a
+    seeded N(0,1) bf16 upstream gradient. Times the whole backward call."""
+    from lcr_inputs import get_config, route_inputs
+    cfg = get_config("prefill_16k")
+    inp = route_inputs(cfg)
+    d = {k: to_dev(v, torch) for k, v in inp.items()}
+    res = lcr.route_layer(d["q"], d["k"], d["v"], d["x"], d["A"], d["Bm"], K=cfg.K, radius=cfg.R, beta=cfg.beta,
+                          scale=cfg.scale, want_lse=True)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dO = torch.randn(d["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    dims = lcr.make_dims(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d, torch.bfloat16)
+    ws = torch.empty(lcr.workspace_bytes(4, dims, 0, 0, cfg.K, cfg.T, cfg.R), dtype=torch.uint8, device="cuda")
+
+    def call():
+        return lcr.routed_attention_backward(d["q"], d["k"], d["v"], res["idx"], res["zsel"], res["o"], res["lse"],
+                                             dO, radius=cfg.R, scale=cfg.scale, ws=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 5
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    local, chunks = prefill_flops(cfg, int((res["idx"] >= 0).sum().item()))
+    # per (head, query, key): S, dP and dQ on the query side (6d), S, dP, dV and dK on the key side (8d)
+    flops = (local + chunks) * 14.0 / 4.0
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_call": round(ms, 4), "algorithmic_gflop": round(flops / 1e9, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,7 +420,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-swa", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "swa", "dense", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "swa", "dense", "backward", "copy"], default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -401,6 +441,9 @@ def main():
         return
     if args.only == "dense":
         print(json.dumps({"dense_16k": bench_dense(args, torch, lcr)}), flush=True)
+        return
+    if args.only == "backward":
+        print(json.dumps({"backward_16k": bench_backward(args, torch, lcr)}), flush=True)
         return
     if args.only == "copy":
         # Plain device copy of a known size: calibrates the HBM byte counters.
@@ -439,6 +482,8 @@ def main():
     if args.only is None and not args.no_swa:
         line["swa_64k"] = bench_swa(args, torch, lcr)
         line["dense_16k"] = bench_dense(args, torch, lcr)
+    if args.only is None:
+        line["backward_16k"] = bench_backward(args, torch, lcr)
     if args.only is None and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg, inp)

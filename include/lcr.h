@@ -207,10 +207,10 @@ int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, con
  * Only the nq queried rows contribute. ws: lcr_workspace_bytes(
  * LCR_OP_ROUTED_ATTENTION_BACKWARD, dims, 0, 0, K, radius, nq) bytes, contents
  * need not be initialised. Arithmetic: bf16 products (probabilities and their
- * gradients rounded to bf16 for the products), float32 accumulation. The
- * summation order of dk and dv over the rows that selected a chunk depends on
- * scheduling, so those two outputs agree between runs to float32 rounding.
- * Errors: as lcr_routed_attention; LCR_ERR_UNSUPPORTED for LCR_F32 inputs.
+ * gradients rounded to bf16 for the products), float32 accumulation in a
+ * fixed order: results are reproducible bit for bit.
+ * Errors: as lcr_routed_attention; LCR_ERR_UNSUPPORTED for LCR_F32 inputs or
+ * N > 32768.
  */
 int lcr_routed_attention_backward(const lcr_dims* dims, const void* q, const void* k, const void* v,
                                   const int32_t* idx, const float* zsel, int K, int radius, float scale,

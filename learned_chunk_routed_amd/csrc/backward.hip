@@ -27,7 +27,8 @@
 //     dQ^T += K^T dS^T (K^T read from LDS with the transposing read). Writes dq,
 //     dzsel, D and, per (row, selected chunk), the bias and U_c.
 //  2. inverse index: per (batch, KV group, chunk) the list of (query, slot)
-//     entries that selected it (counts, exclusive scan, placement).
+//     entries that selected it, in ascending query order (per-tile counts,
+//     a scan over chunks and tiles, placement row by row).
 //  3. bwd_key_kernel: one block per (batch, KV group, chunk), wave w owning keys
 //     16w .. 16w+15. Rows (query, head) are staged 32 at a time in LDS: first
 //     the queries whose window reaches the chunk, then the chunk's entries from
@@ -61,7 +62,7 @@ struct BwdParams {
   float* cbias;         // ws [B,Hq,nq,K]
   float* cu;            // ws [B,Hq,nq,K]
   int* cnt;             // ws [B*Hkv*N]
-  int* cur;             // ws [B*Hkv*N]
+  int* th;              // ws [B*Hkv*ntile*N]  per-tile chunk counts, then first positions
   int* off;             // ws [B*Hkv*(N+1)]
   int* list;            // ws [B*Hkv*nq*K]  entries t*K + slot
   int B, Hq, Hkv, N, G, K, R, q0, nq;
@@ -77,7 +78,7 @@ __device__ __forceinline__ s16x8 zero8() { return s16x8{0, 0, 0, 0, 0, 0, 0, 0};
 // ---------------------------------------------------------------- 1. query side
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_query_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
   constexpr int LDK = D + 8;   // padded K rows in LDS
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -263,31 +264,54 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdParams p) {
   }
 }
 
+__global__ __launch_bounds__(256) void bwd_zero_kernel(int* a, size_t n) {
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) a[x] = 0;
+}
+
 // ---------------------------------------------------------------- 2. inverse index
+// Rows t of one (batch, KV group) are cut into tiles of kIdxTile. The list of
+// chunk c holds its entries (t, slot) in ascending t: tile by tile, and inside
+// a tile row by row. Per tile an LDS histogram of the chunks it selects; a scan
+// over (chunk, tile) gives every tile its first position in each chunk's list;
+// one wave per tile then walks its rows in order. The result does not depend on
+// scheduling, so dk and dv are reproducible bit for bit.
+constexpr int kIdxTile = 256;
 
-__global__ __launch_bounds__(256) void bwd_zero_kernel(int* a, int* b2, size_t n) {
-  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
-    a[x] = 0;
-    b2[x] = 0;
+__global__ __launch_bounds__(256) void bwd_hist_kernel(BwdParams p) {
+  extern __shared__ int hist[];   // [N]
+  const int tile = blockIdx.x, bg = blockIdx.y, ntile = gridDim.x;
+  for (int c = threadIdx.x; c < p.N; c += 256) hist[c] = 0;
+  __syncthreads();
+  const int t0 = tile * kIdxTile, t1 = min(p.nq, t0 + kIdxTile);
+  const int32_t* id = p.idx + ((size_t)bg * p.nq + t0) * p.K;
+  const int n = (t1 - t0) * p.K;
+  for (int x = threadIdx.x; x < n; x += 256) {
+    const int c = id[x];
+    if (c >= 0) atomicAdd(&hist[c], 1);
   }
+  __syncthreads();
+  int* th = p.th + ((size_t)bg * ntile + tile) * p.N;
+  for (int c = threadIdx.x; c < p.N; c += 256) th[c] = hist[c];
 }
 
-__global__ __launch_bounds__(256) void bwd_count_kernel(BwdParams p) {
-  const size_t n = (size_t)p.B * p.Hkv * p.nq * p.K;
-  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
-    const int c = p.idx[x];
-    if (c >= 0) {
-      const size_t bg = x / ((size_t)p.nq * p.K);
-      atomicAdd(&p.cnt[bg * p.N + c], 1);
-    }
-  }
-}
-
-// One block per (batch, KV group): off[c] = sum of cnt[c'] for c' < c, off[N] = total.
-__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
+// One block per (batch, KV group): th[tile][c] becomes the number of entries of
+// chunk c in earlier tiles; cnt[c] the chunk's total; off[c] the exclusive
+// prefix of cnt (off[N] = all entries of the group).
+__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p, int ntile) {
   __shared__ int part[256];
   const int bg = blockIdx.x, tid = threadIdx.x;
-  const int* cnt = p.cnt + (size_t)bg * p.N;
+  int* th = p.th + (size_t)bg * ntile * p.N;
+  int* cnt = p.cnt + (size_t)bg * p.N;
+  for (int c = tid; c < p.N; c += 256) {
+    int run = 0;
+    for (int tl = 0; tl < ntile; ++tl) {
+      const int v = th[(size_t)tl * p.N + c];
+      th[(size_t)tl * p.N + c] = run;
+      run += v;
+    }
+    cnt[c] = run;
+  }
+  __syncthreads();
   int* off = p.off + (size_t)bg * (p.N + 1);
   int base = 0;
   for (int c0 = 0; c0 < p.N; c0 += 256) {
@@ -307,16 +331,27 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   if (tid == 0) off[p.N] = base;
 }
 
-__global__ __launch_bounds__(256) void bwd_fill_kernel(BwdParams p) {
+// One wave per (tile, batch and KV group): rows in order, lane k places entry (t, k).
+// Chunks within a row are distinct, so the LDS cursors see no two lanes of one row
+// on the same chunk; the atomic keeps positions distinct even if they were not.
+__global__ __launch_bounds__(64) void bwd_fill_kernel(BwdParams p) {
+  extern __shared__ int curs[];   // [N]
+  const int tile = blockIdx.x, bg = blockIdx.y, ntile = gridDim.x, lane = threadIdx.x;
+  const int* th = p.th + ((size_t)bg * ntile + tile) * p.N;
+  const int* off = p.off + (size_t)bg * (p.N + 1);
+  for (int c = lane; c < p.N; c += 64) curs[c] = off[c] + th[c];
+  __syncthreads();
+  const int t0 = tile * kIdxTile, t1 = min(p.nq, t0 + kIdxTile);
   const size_t per = (size_t)p.nq * p.K;
-  const size_t n = (size_t)p.B * p.Hkv * per;
-  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
-    const int c = p.idx[x];
-    if (c >= 0) {
-      const size_t bg = x / per;
-      const int e = (int)(x % per);   // t * K + slot
-      const int pos = atomicAdd(&p.cur[bg * p.N + c], 1);
-      p.list[bg * per + p.off[bg * (p.N + 1) + c] + pos] = e;
+  int* list = p.list + (size_t)bg * per;
+  for (int t = t0; t < t1; ++t) {
+    for (int k0 = 0; k0 < p.K; k0 += 64) {
+      const int k = k0 + lane;
+      const int c = k < p.K ? p.idx[((size_t)bg * p.nq + t) * p.K + k] : -1;
+      if (c >= 0) {
+        const int pos = atomicAdd(&curs[c], 1);
+        list[pos] = t * p.K + k;
+      }
     }
   }
 }
@@ -336,6 +371,19 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
   const int c = blockIdx.x % p.N, bg = blockIdx.x / p.N, b = bg / p.Hkv, g = bg % p.Hkv;
   const size_t L = (size_t)p.N * kSlots;
   const int key = 16 * w + L16;                 // this lane's key (chunk-local slot) in S = Q K^T
+  const int iw_lo = max(p.q0, c * kContent - p.R);
+  const int iw_hi = min(p.q0 + p.nq - 1, c * kContent + kContent - 1 + p.R);
+  const int nwq = max(0, iw_hi - iw_lo + 1);
+  const int ncnt = p.cnt[(size_t)bg * p.N + c];
+  if (nwq == 0 && ncnt == 0) {   // no queried row reaches this chunk: zero gradients (block-uniform exit)
+    float* dkb = p.dk + ((size_t)bg * L + (size_t)c * kSlots) * D;
+    float* dvb = p.dv + ((size_t)bg * L + (size_t)c * kSlots) * D;
+    for (int x = tid; x < kSlots * D; x += 256) {
+      dkb[x] = 0.f;
+      dvb[x] = 0.f;
+    }
+    return;
+  }
   const bf16_t* krow = p.k + ((size_t)bg * L + (size_t)c * kSlots + key) * D;
   const bf16_t* vrow = p.v + ((size_t)bg * L + (size_t)c * kSlots + key) * D;
   s16x8 kf[D / 32], vf[D / 32];
@@ -352,10 +400,6 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
   }
   const float sc = p.scale;
   const int u_key = c * kContent + key;         // content index of this lane's key (key < 63)
-  const int iw_lo = max(p.q0, c * kContent - p.R);
-  const int iw_hi = min(p.q0 + p.nq - 1, c * kContent + kContent - 1 + p.R);
-  const int nwq = max(0, iw_hi - iw_lo + 1);
-  const int ncnt = p.cnt[(size_t)bg * p.N + c];
   const size_t per = (size_t)p.nq * p.K;
   const int* lst = p.list + (size_t)bg * per + p.off[(size_t)bg * (p.N + 1) + c];
 
@@ -482,31 +526,45 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+static int bwd_ntile(int nq) { return (nq + kIdxTile - 1) / kIdxTile; }
+
 size_t routed_bwd_ws_bytes(const RouteDims& dm, int K, int nq) {
   const size_t rows = (size_t)dm.B * dm.Hq * nq;
-  const size_t bgn = (size_t)dm.B * dm.Hkv * dm.N;
-  return al256(rows * 4) + 2 * al256(rows * K * 4) + 2 * al256(bgn * 4) +
-         al256(((size_t)dm.B * dm.Hkv * (dm.N + 1)) * 4) + al256((size_t)dm.B * dm.Hkv * nq * K * 4);
+  const size_t bg = (size_t)dm.B * dm.Hkv;
+  return al256(rows * 4) + 2 * al256(rows * K * 4) + al256(bg * dm.N * 4) + al256(bg * (dm.N + 1) * 4) +
+         al256(bg * bwd_ntile(nq) * dm.N * 4) + al256(bg * nq * K * 4);
 }
 
 size_t routed_bwd_lds_bytes(int d) { return (size_t)4 * 64 * (d + 8) * 2; }
 
 template <int D>
 static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t st) {
-  const size_t ents = (size_t)prm.B * prm.Hkv * prm.nq * prm.K;
   const size_t bgn = (size_t)prm.B * prm.Hkv * prm.N;
-  const int egrid = (int)std::min<size_t>((ents + 255) / 256, 65535);
-  hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)std::min<size_t>((bgn + 255) / 256, 65535)), dim3(256), 0, st,
-                     prm.cnt, prm.cur, bgn);
-  if (ents > 0) hipLaunchKernelGGL(bwd_count_kernel, dim3(egrid), dim3(256), 0, st, prm);
-  hipLaunchKernelGGL(bwd_scan_kernel, dim3(prm.B * prm.Hkv), dim3(256), 0, st, prm);
-  if (ents > 0) hipLaunchKernelGGL(bwd_fill_kernel, dim3(egrid), dim3(256), 0, st, prm);
+  const int ntile = bwd_ntile(prm.nq);
+  const size_t idx_lds = (size_t)prm.N * 4;
+  hipError_t e = hipFuncSetAttribute((const void*)bwd_hist_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)idx_lds);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)bwd_fill_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)idx_lds);
+  if (e != hipSuccess) return e;
+  if (prm.nq > 0) {
+    hipLaunchKernelGGL(bwd_hist_kernel, dim3(ntile, prm.B * prm.Hkv), dim3(256), idx_lds, st, prm);
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(prm.B * prm.Hkv), dim3(256), 0, st, prm, ntile);
+    if (prm.K > 0) hipLaunchKernelGGL(bwd_fill_kernel, dim3(ntile, prm.B * prm.Hkv), dim3(64), idx_lds, st, prm);
+  } else {
+    // nothing selects anything: zero counts and offsets, the key side then writes zero gradients
+    const size_t no = (size_t)prm.B * prm.Hkv * (prm.N + 1);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)std::min<size_t>((bgn + 255) / 256, 65535)), dim3(256), 0,
+                       st, prm.cnt, bgn);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)std::min<size_t>((no + 255) / 256, 65535)), dim3(256), 0,
+                       st, prm.off, no);
+  }
   const int tiles = prm.B * prm.Hkv * ((prm.nq + 1) / 2);
   const size_t lds = routed_bwd_lds_bytes(D);
-  hipError_t e = hipFuncSetAttribute((const void*)bwd_query_kernel<D>,
+  e = hipFuncSetAttribute((const void*)bwd_query_kernel<D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_query_kernel<D>, dim3((tiles + 3) / 4), dim3(256), lds, st, prm);
+  if (tiles > 0) hipLaunchKernelGGL(bwd_query_kernel<D>, dim3((tiles + 3) / 4), dim3(256), lds, st, prm);
   hipLaunchKernelGGL(bwd_key_kernel<D>, dim3((unsigned)bgn), dim3(256), 0, st, prm);
   return hipGetLastError();
 }
@@ -540,10 +598,10 @@ hipError_t launch_routed_attention_backward(const RouteDims& dm, const void* q, 
   w += al256(rows * K * 4);
   prm.cnt = (int*)w;
   w += al256(bgn * 4);
-  prm.cur = (int*)w;
-  w += al256(bgn * 4);
   prm.off = (int*)w;
   w += al256(((size_t)dm.B * dm.Hkv * (dm.N + 1)) * 4);
+  prm.th = (int*)w;
+  w += al256((size_t)dm.B * dm.Hkv * bwd_ntile(nq) * dm.N * 4);
   prm.list = (int*)w;
   prm.B = dm.B;
   prm.Hq = dm.Hq;

@@ -97,8 +97,9 @@ int check_routed_attention_backward(const lcr_dims* d, const void* q, const void
     if (!lse || !dO || !dq) return LCR_ERR_ARG;
     if (K > 0 && !dzsel) return LCR_ERR_ARG;
   }
-  // entry lists index nq*K entries per (batch, group) with int32
+  // entry lists index nq*K entries per (batch, group) with int32; per-tile chunk counts live in LDS
   if ((long long)nq * K > (long long)std::numeric_limits<int>::max()) return LCR_ERR_UNSUPPORTED;
+  if (d->N > kMaxChunksBackward) return LCR_ERR_UNSUPPORTED;
   return LCR_OK;
 }
 

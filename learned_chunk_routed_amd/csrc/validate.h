@@ -30,4 +30,7 @@ int check_swa(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, co
 // Largest N the top-K kernel handles (64 chunks per lane step, 64 steps).
 constexpr int kMaxChunksTopK = 4096;
 
+// Largest N the backward's inverse index handles (one int per chunk in LDS).
+constexpr int kMaxChunksBackward = 32768;
+
 }  // namespace lcr

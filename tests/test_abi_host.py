@@ -207,8 +207,11 @@ def test_routed_attention_backward_validation(lib):
     assert call(ws_bytes=need - 1) == _lib.LCR_ERR_WORKSPACE
     al = lambda x: (x + 255) // 256 * 256
     rows, bgn = 28 * 100, 4 * 256
-    # D per row; bias and U per (row, selected chunk); counts, cursors and offsets per chunk; the entry lists
-    assert need == al(rows * 4) + 2 * al(rows * 32 * 4) + 2 * al(bgn * 4) + al(4 * 257 * 4) + al(4 * 100 * 32 * 4)
+    # D per row; bias and U per (row, selected chunk); counts and offsets per chunk; per-tile counts of
+    # 256-row tiles; the entry lists
+    assert need == al(rows * 4) + 2 * al(rows * 32 * 4) + al(bgn * 4) + al(4 * 257 * 4) + al(4 * 1 * 256 * 4) \
+        + al(4 * 100 * 32 * 4)
+    assert call(dm=dims(N=32769)) == _lib.LCR_ERR_UNSUPPORTED
 
 
 def test_swa_validation(lib):

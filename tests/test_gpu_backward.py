@@ -165,3 +165,46 @@ def test_backward_prefill_16k_sampled():
         print(f"    group {g} chunk {c}: {len(qs)} queries ({len(sel_t)} selecting) dk={e_k:.2e} dv={e_v:.2e}",
               flush=True)
         assert e_k < BWD_TOL and e_v < BWD_TOL
+
+
+def test_backward_decode_sized_tail():
+    """32 tail queries of a 64-chunk sequence (the decode shape): one index tile, most
+    chunks reached only through selections."""
+    cfg = get_config("prefill_16k", N=64, K=8, R=256)
+    q0, nq = cfg.T - 32, 32
+    print(f"[case] backward decode-sized tail: N={cfg.N} K={cfg.K} q0={q0} nq={nq}", flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, q0, nq)
+    idx, zsel = selection(cfg, dr, q0, nq)
+    gq, gk, gv, gz = run_gpu(cfg, inp, dr["dO"], idx, zsel, q0, nq)
+    queries = np.arange(q0, q0 + nq)
+    sl = O.slot_of(queries)
+    rq, rk, rv, rz = OB.routed_attention_backward(as_f64(inp["q"])[:, :, sl], as_f64(inp["k"]), as_f64(inp["v"]),
+                                                  idx, zsel.astype(np.float64), cfg.R, cfg.scale, queries,
+                                                  as_f64(dr["dO"])[:, :, sl])
+    errs = dict(dq=rel_err(gq[:, :, sl], rq), dk=rel_err(gk, rk), dv=rel_err(gv, rv),
+                dzsel=rel_err(np.where(np.isfinite(zsel), gz, 0.0), rz))
+    print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e < BWD_TOL, f"{n} error {e:.3e}"
+
+
+def test_backward_reproducible_and_empty_range():
+    """Two calls give identical bits (fixed summation order); nq = 0 writes zero dk, dv."""
+    cfg = get_config("prefill_16k", N=40, Hq=8, Hkv=2, K=6, R=64)
+    print("[case] backward reproducibility and nq = 0", flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, 0, cfg.T)
+    idx, zsel = selection(cfg, dr, 0, cfg.T)
+    a = run_gpu(cfg, inp, dr["dO"], idx, zsel, 0, cfg.T)
+    b = run_gpu(cfg, inp, dr["dO"], idx, zsel, 0, cfg.T)
+    for x, y, n in zip(a, b, ("dq", "dk", "dv", "dzsel")):
+        assert np.array_equal(x, y), f"{n} differs between two identical calls"
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    e_idx = torch.zeros((1, cfg.Hkv, 0, cfg.K), dtype=torch.int32, device="cuda")
+    e_z = torch.zeros((1, cfg.Hq, 0, cfg.K), dtype=torch.float32, device="cuda")
+    e_l = torch.zeros((1, cfg.Hq, 0), dtype=torch.float32, device="cuda")
+    dq, dk, dv, dz = lcr.routed_attention_backward(q, k, v, e_idx, e_z, torch.zeros_like(q), e_l,
+                                                   torch.zeros_like(q), radius=cfg.R, scale=cfg.scale, q0=5, nq=0)
+    torch.cuda.synchronize()
+    assert dz.numel() == 0 and not dq.any() and not dk.any() and not dv.any()
