@@ -66,7 +66,8 @@ typedef enum {
   LCR_OP_ROUTE_SCORE_TOPK = 1,
   LCR_OP_ROUTED_ATTENTION = 2,
   LCR_OP_SWA_ATTENTION = 3,
-  LCR_OP_ROUTED_ATTENTION_BACKWARD = 4
+  LCR_OP_ROUTED_ATTENTION_BACKWARD = 4,
+  LCR_OP_ROUTE_SCORE_BACKWARD = 5
 } lcr_op;
 
 /* Library version as 10000*major + 100*minor + patch. */
@@ -217,6 +218,50 @@ int lcr_routed_attention_backward(const lcr_dims* dims, const void* q, const voi
                                   int q0, int nq, const void* o, const float* lse, const void* dO,
                                   float* dq, float* dk, float* dv, float* dzsel, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/*
+ * Gradients of the scoring with the chosen chunks fixed ("Prefilling-dLLM v2",
+ * Figure 3 caption: the residual-augmented query scores the summaries; "The
+ * 172x Speedup...": similarity minus beta times the pooling entropy). For
+ * zsel[b,h,t,k] = scale q~[b,h,t] . s[b,h,c] - beta H[b,h,c], c = idx[b,g,t,k],
+ * q~ = q + (x A Bm)[h*d .. h*d+d-1] and an upstream dzsel (e.g. from
+ * lcr_routed_attention_backward):
+ *   dq~ = scale sum_k dzsel s[c_k]; dq[b,h,slot(i)] += dq~          (added)
+ *   ds[b,h,c] = scale sum over (t,k) with idx = c of dzsel q~[b,h,t] (written)
+ *   dH[b,h,c] = -beta sum over the same entries of dzsel             (written)
+ *   with U = x A per row: dBm = U^T dq~, dA = x^T (dq~ Bm^T),
+ *   dx[b,slot(i)] = (dq~ Bm^T) A^T                                   (written)
+ * The group maximum and the top-K choice only decide idx and get no gradient.
+ * q, x, A, Bm, s as in lcr_route_score_topk (dims->dtype); idx [B,Hkv,nq,K];
+ * dzsel [B,Hq,nq,K] float32. Outputs, float32: dq [B,Hq,L,d] (rows slot(i)
+ * accumulated into), dx [B,L,D] (rows slot(i) written), dA [D,r] and
+ * dBm [r,Hq*d] (written; sums over the nq rows and the batch), ds [B,Hq,N,d],
+ * dH [B,Hq,N] (written; zero for chunks no row selected). ws:
+ * lcr_workspace_bytes(LCR_OP_ROUTE_SCORE_BACKWARD, dims, D, r, K, 0, nq)
+ * bytes. Arithmetic in float32, in a fixed order (reproducible bit for bit).
+ * Errors: as lcr_route_score_topk; N > 32768 is LCR_ERR_UNSUPPORTED.
+ */
+int lcr_route_score_backward(const lcr_dims* dims, const void* q, const void* x, const void* A, const void* Bm,
+                             int D, int r, const float* s, float beta, float scale, int K, int q0, int nq,
+                             const int32_t* idx, const float* dzsel, float* dq, float* dx, float* dA, float* dBm,
+                             float* ds, float* dH, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gradients of lcr_chunk_summary ("Prefilling-dLLM v2", Figure 3 caption: mask-
+ * query pooling; "The 172x Speedup...": the pooling entropy) for upstream
+ * gradients ds [B,Hq,N,d] and dH [B,Hq,N] (float32), e.g. from the scoring's
+ * backward. With alpha, s and H as in lcr_chunk_summary:
+ *   g_j = ds . k_j - (ln alpha_j + 1) dH,  dlam_j = alpha_j (g_j - sum_i alpha_i g_i)
+ *   dq[b,h,64c+63] = scale sum_j dlam_j k_j                        (written)
+ *   dk[b,g,64c+j] += sum over the group's heads of alpha_j ds + scale dlam_j q_m
+ *                                                              (j < 63, added)
+ * q, k as in lcr_chunk_summary (dims->dtype); dq [B,Hq,L,d] float32: only the
+ * mask-slot rows are written; dk [B,Hkv,L,d] float32: content rows are
+ * accumulated into, mask rows untouched, so the call adds the pooling's share to
+ * the gradient lcr_routed_attention_backward wrote. Arithmetic in float32.
+ */
+int lcr_chunk_summary_backward(const lcr_dims* dims, const void* q, const void* k, float scale, const float* ds,
+                               const float* dH, float* dq, float* dk, void* stream);
 
 /*
  * Bidirectional sliding-window attention for the layers that do not route

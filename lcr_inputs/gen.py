@@ -11,7 +11,7 @@ import numpy as np
 from .configs import Config, SLOTS, CONTENT
 
 TAG_Q, TAG_K, TAG_V, TAG_X, TAG_A, TAG_B, TAG_NEEDLE, TAG_OFFSET = 1, 2, 3, 4, 5, 6, 7, 8
-TAG_DO, TAG_SCORE, TAG_ZSEL = 9, 10, 11
+TAG_DO, TAG_SCORE, TAG_ZSEL, TAG_DS, TAG_DH = 9, 10, 11, 12, 13
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -156,12 +156,15 @@ def backward_draws(cfg: Config, q0: int, nq: int, layer: int = 0) -> dict:
     dO [B,Hq,L,d] (upstream gradient on the route-layer output, stored like q);
     score [B,Hkv,nq,N] float32 (random chunk scores: ranking them over the
     remote chunks gives a synthetic selection); zsel [B,Hq,nq,K] float32
-    (chunk logits for the selected entries)."""
+    (chunk logits for the selected entries); ds [B,Hq,N,d] and dH [B,Hq,N]
+    float32 (upstream gradients on the summaries and entropies)."""
     B, Hq, Hkv, L, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d
     out = {}
     out["dO"] = _store(_normal(_rng(cfg, TAG_DO, layer), (B, Hq, L, d)), cfg.dtype)
     out["score"] = _normal(_rng(cfg, TAG_SCORE, layer), (B, Hkv, nq, cfg.N))
     out["zsel"] = _normal(_rng(cfg, TAG_ZSEL, layer), (B, Hq, nq, cfg.K))
+    out["ds"] = _normal(_rng(cfg, TAG_DS, layer), (B, Hq, cfg.N, d))
+    out["dH"] = _normal(_rng(cfg, TAG_DH, layer), (B, Hq, cfg.N))
     return out
 
 

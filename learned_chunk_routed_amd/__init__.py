@@ -10,6 +10,8 @@ from ._lib import LIB_PATH, load  # noqa: F401
 from .ops import (  # noqa: F401
     chunk_summary,
     chunk_summary_mean,
+    chunk_summary_backward,
+    route_score_backward,
     route_score_topk,
     routed_attention,
     routed_attention_backward,

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(_HERE, "liblcr.so")
 LCR_OK, LCR_ERR_ARG, LCR_ERR_DTYPE, LCR_ERR_WORKSPACE, LCR_ERR_HIP, LCR_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 LCR_F32, LCR_BF16 = 0, 1
 OP_CHUNK_SUMMARY, OP_ROUTE_SCORE_TOPK, OP_ROUTED_ATTENTION, OP_SWA_ATTENTION = 0, 1, 2, 3
-OP_ROUTED_ATTENTION_BACKWARD = 4
+OP_ROUTED_ATTENTION_BACKWARD, OP_ROUTE_SCORE_BACKWARD = 4, 5
 
 
 class Dims(ctypes.Structure):
@@ -34,6 +34,9 @@ SIGNATURES = {
     "lcr_routed_attention": (_i, [_pd, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "lcr_routed_attention_backward": (_i, [_pd, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _i, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lcr_route_score_backward": (_i, [_pd, _vp, _vp, _vp, _vp, _i, _i, _vp, _f, _f, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lcr_chunk_summary_backward": (_i, [_pd, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp]),
     "lcr_swa_attention": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _f, _vp, _vp, _vp]),
 }
 

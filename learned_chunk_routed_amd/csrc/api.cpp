@@ -49,6 +49,8 @@ size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, in
       return nq > 0 ? plan_routed_attention(dm, K, radius, nq).ws : 0;
     case LCR_OP_ROUTED_ATTENTION_BACKWARD:
       return routed_bwd_ws_bytes(dm, K, nq);
+    case LCR_OP_ROUTE_SCORE_BACKWARD:
+      return (D > 0 && r > 0 && r <= 128) ? score_bwd_ws_bytes(dm, D, r, K, nq) : 0;
     default:
       return 0;
   }
@@ -118,6 +120,29 @@ int lcr_routed_attention_backward(const lcr_dims* dims, const void* q, const voi
   return hip_status(launch_routed_attention_backward(dm, q, k, v, K > 0 ? idx : nullptr, K > 0 ? zsel : nullptr, K,
                                                      radius, scale, q0, nq, o, lse, dO, dq, dk, dv,
                                                      K > 0 ? dzsel : nullptr, ws, (hipStream_t)stream));
+}
+
+int lcr_route_score_backward(const lcr_dims* dims, const void* q, const void* x, const void* A, const void* Bm, int D,
+                             int r, const float* s, float beta, float scale, int K, int q0, int nq, const int32_t* idx,
+                             const float* dzsel, float* dq, float* dx, float* dA, float* dBm, float* ds, float* dH,
+                             void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_route_score_backward(dims, q, x, A, Bm, D, r, s, beta, scale, K, q0, nq, idx, dzsel, dq, dx,
+                                            dA, dBm, ds, dH);
+  if (st != LCR_OK) return st;
+  const RouteDims dm = to_route_dims(dims);
+  if (ws == nullptr || ws_bytes < score_bwd_ws_bytes(dm, D, r, K, nq)) return LCR_ERR_WORKSPACE;
+  return hip_status(launch_route_score_backward(dm, q, x, A, Bm, D, r, s, beta, scale, K, q0, nq,
+                                                K > 0 ? idx : nullptr, K > 0 ? dzsel : nullptr, dq, dx, dA, dBm, ds,
+                                                dH, ws, (hipStream_t)stream));
+}
+
+int lcr_chunk_summary_backward(const lcr_dims* dims, const void* q, const void* k, float scale, const float* ds,
+                               const float* dH, float* dq, float* dk, void* stream) {
+  int st = check_chunk_summary(dims, q, k, scale, ds, dH);
+  if (st != LCR_OK) return st;
+  if (!dq || !dk) return LCR_ERR_ARG;
+  return hip_status(
+      launch_chunk_summary_backward(to_route_dims(dims), q, k, scale, ds, dH, dq, dk, (hipStream_t)stream));
 }
 
 int lcr_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, const void* k, const void* v,

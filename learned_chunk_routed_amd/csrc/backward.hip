@@ -522,6 +522,109 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
     }
 }
 
+
+// ---------------------------------------------------------------- 4. summary pooling backward
+// "Prefilling-dLLM v2", Figure 3 caption: alpha = softmax_j(scale q_m . k_j) over the
+// chunk's 63 content keys, s = sum_j alpha_j k_j; "The 172x Speedup...": entropy
+// H = -sum_j alpha_j ln alpha_j. For upstream gradients ds, dH:
+//   g_j = ds . k_j - (ln alpha_j + 1) dH,  dlam_j = alpha_j (g_j - sum_i alpha_i g_i)
+//   dq_m = scale sum_j dlam_j k_j,  dk_j += alpha_j ds + scale dlam_j q_m.
+// One wave per (batch, KV group, chunk) walks the group's heads; K (float32, padded
+// rows) and the key gradient live in LDS; lanes own keys for the logits and
+// columns for the d-vectors.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void summary_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         float scale, const float* __restrict__ ds,
+                                                         const float* __restrict__ dH, float* __restrict__ dq,
+                                                         float* __restrict__ dk, int Hq, int Hkv, int N) {
+  constexpr int LK = D + 1;
+  extern __shared__ float sbw[];            // kt [63][D+1], gk [63][D], vq [D], vds [D], wal [64], wdl [64]
+  float* kt = sbw;
+  float* gk = kt + kContent * LK;
+  float* vq = gk + kContent * D;
+  float* vds = vq + D;
+  float* wal = vds + D;
+  float* wdl = wal + 64;
+  const int lane = threadIdx.x;
+  const int c = blockIdx.x % N, bg = blockIdx.x / N, b = bg / Hkv, g = bg % Hkv, G = Hq / Hkv;
+  const size_t L = (size_t)N * kSlots;
+  const T* kc = k + ((size_t)bg * L + (size_t)c * kSlots) * D;
+  for (int x = lane; x < kContent * D; x += 64) {
+    kt[(x / D) * LK + x % D] = Elem<T>::to_f(kc[x]);
+    gk[x] = 0.f;
+  }
+  __syncthreads();
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    const size_t hn = ((size_t)b * Hq + h) * N + c;
+    const T* qm = q + (((size_t)b * Hq + h) * L + (size_t)c * kSlots + kSlots - 1) * D;
+    for (int e = lane; e < D; e += 64) {
+      vq[e] = Elem<T>::to_f(qm[e]);
+      vds[e] = ds[hn * D + e];
+    }
+    __syncthreads();
+    // lane j < 63: logit and ds . k_j
+    float lam = -INFINITY, gdk = 0.f;
+    if (lane < kContent) {
+      float a = 0.f;
+      for (int e = 0; e < D; ++e) {
+        const float kv = kt[lane * LK + e];
+        a += vq[e] * kv;
+        gdk += vds[e] * kv;
+      }
+      lam = scale * a;
+    }
+    const float m = wave_max(lam);
+    const float ex = lane < kContent ? __expf(lam - m) : 0.f;
+    const float z = wave_sum(ex);
+    const float al = ex / z;
+    const float lnal = lam - m - __logf(z);
+    const float gj = lane < kContent ? gdk - (lnal + 1.f) * dH[hn] : 0.f;
+    const float ag = wave_sum(al * gj);
+    const float dl = lane < kContent ? al * (gj - ag) : 0.f;
+    wal[lane] = al;
+    wdl[lane] = dl;
+    __syncthreads();
+    // columns e: dq_m[e] and this head's share of dk[j][e]
+    float* dqm = dq + (((size_t)b * Hq + h) * L + (size_t)c * kSlots + kSlots - 1) * D;
+    for (int e = lane; e < D; e += 64) {
+      float acc = 0.f;
+      const float dse = vds[e], qe = scale * vq[e];
+      for (int j = 0; j < kContent; ++j) {
+        acc += wdl[j] * kt[j * LK + e];
+        gk[j * D + e] += wal[j] * dse + wdl[j] * qe;
+      }
+      dqm[e] = scale * acc;
+    }
+    __syncthreads();
+  }
+  float* dkc = dk + ((size_t)bg * L + (size_t)c * kSlots) * D;
+  for (int x = lane; x < kContent * D; x += 64) dkc[x] += gk[x];
+}
+
+template <typename T>
+static hipError_t launch_summary_bwd_t(const RouteDims& dm, const void* q, const void* k, float scale,
+                                       const float* ds, const float* dH, float* dq, float* dk, hipStream_t st) {
+  const dim3 grid((unsigned)((size_t)dm.B * dm.Hkv * dm.N));
+  const size_t lds = ((size_t)kContent * (dm.d + 1) + (size_t)kContent * dm.d + 2 * dm.d + 128) * 4;
+  const void* fn = dm.d == 128 ? (const void*)summary_bwd_kernel<T, 128> : (const void*)summary_bwd_kernel<T, 64>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  if (dm.d == 128)
+    hipLaunchKernelGGL((summary_bwd_kernel<T, 128>), grid, dim3(64), lds, st, (const T*)q, (const T*)k, scale, ds,
+                       dH, dq, dk, dm.Hq, dm.Hkv, dm.N);
+  else
+    hipLaunchKernelGGL((summary_bwd_kernel<T, 64>), grid, dim3(64), lds, st, (const T*)q, (const T*)k, scale, ds,
+                       dH, dq, dk, dm.Hq, dm.Hkv, dm.N);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_summary_backward(const RouteDims& dm, const void* q, const void* k, float scale,
+                                         const float* ds, const float* dH, float* dq, float* dk, hipStream_t st) {
+  return dm.dtype == 1 ? launch_summary_bwd_t<bf16_t>(dm, q, k, scale, ds, dH, dq, dk, st)
+                       : launch_summary_bwd_t<float>(dm, q, k, scale, ds, dH, dq, dk, st);
+}
+
 // ---------------------------------------------------------------- host side
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -536,6 +639,389 @@ size_t routed_bwd_ws_bytes(const RouteDims& dm, int K, int nq) {
 }
 
 size_t routed_bwd_lds_bytes(int d) { return (size_t)4 * 64 * (d + 8) * 2; }
+
+
+// ---------------------------------------------------------------- 5. scoring backward
+// "Prefilling-dLLM v2", Figure 3 caption: the residual-augmented query
+// q~ = q + (x A) B_h scores the summaries; "The 172x Speedup...": similarity minus
+// beta times the pooling entropy. zsel[b,h,t,k] = scale q~ . s[b,h,c] - beta H[b,h,c]
+// with c = idx[b,g,t,k] fixed, so for an upstream dzsel:
+//   dq~[b,h,t] = scale sum_k dzsel s[c_k]            (added to dq at slot(i))
+//   ds[b,h,c]  = scale sum over entries (t,k) of c of dzsel q~[b,h,t]
+//   dH[b,h,c]  = -beta sum over the same entries of dzsel
+//   dU = dq~ B^T (per row, over all heads), dB = U^T dq~, dA = x^T dU, dx = dU A^T
+// All in float32. The sums over rows for dA and dB are split into fixed row ranges
+// whose partials are added in order (no atomics).
+
+template <int D>
+__global__ __launch_bounds__(256) void sbwd_dqt_kernel(const int32_t* __restrict__ idx, const float* __restrict__ dzsel,
+                                                       const float* __restrict__ s, float* __restrict__ dqt,
+                                                       float* __restrict__ dq, float scale, int Hq, int Hkv, int N,
+                                                       int K, int q0, int nq) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int bh = blockIdx.y, b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+  const int t = blockIdx.x * 4 + w;
+  if (t >= nq) return;
+  const int32_t* id = idx + (((size_t)b * Hkv + g) * nq + t) * K;
+  const float* dz = dzsel + ((size_t)bh * nq + t) * K;
+  float acc[D / 64];
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
+  for (int kk = 0; kk < K; ++kk) {
+    const int c = id[kk];
+    if (c < 0) continue;
+    const float wz = dz[kk];
+    const float* sr = s + ((size_t)bh * N + c) * D;
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) acc[u] += wz * sr[lane + 64 * u];
+  }
+  const size_t L = (size_t)N * kSlots;
+  float* dqr = dq + ((size_t)bh * L + slot_of_c(q0 + t)) * D;
+  float* dtr = dqt + ((size_t)bh * nq + t) * D;
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) {
+    dtr[lane + 64 * u] = scale * acc[u];
+    dqr[lane + 64 * u] += scale * acc[u];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void sbwd_ds_kernel(BwdParams p, const float* __restrict__ qt, float* __restrict__ ds,
+                                                      float* __restrict__ dH, float beta) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x % p.N, bg = blockIdx.x / p.N, b = bg / p.Hkv, g = bg % p.Hkv;
+  const int ncnt = p.cnt[(size_t)bg * p.N + c];
+  const int* lst = p.list + (size_t)bg * p.nq * p.K + p.off[(size_t)bg * (p.N + 1) + c];
+  for (int hh = w; hh < p.G; hh += 4) {
+    const int h = g * p.G + hh;
+    const size_t bh = (size_t)b * p.Hq + h;
+    float acc[D / 64];
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
+    float hs = 0.f;
+    for (int e = 0; e < ncnt; ++e) {
+      const int ent = lst[e];
+      const int t = ent / p.K, kk = ent % p.K;
+      const float wz = p.dzsel[(bh * p.nq + t) * p.K + kk];
+      const float* qr = qt + (bh * p.nq + t) * D;
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) acc[u] += wz * qr[lane + 64 * u];
+      hs += wz;
+    }
+    float* dsr = ds + (bh * p.N + c) * D;
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) dsr[lane + 64 * u] = p.scale * acc[u];
+    if (lane == 0) dH[bh * p.N + c] = -beta * hs;
+  }
+}
+
+// U[b,t,j] = sum of the u_kernel partials over the hidden-dimension splits
+__global__ __launch_bounds__(256) void sbwd_usum_kernel(const float* __restrict__ upart, int nsplit, size_t n,
+                                                        float* __restrict__ U) {
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
+    float a = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) a += upart[(size_t)sp * n + x];
+    U[x] = a;
+  }
+}
+
+// dU[b,t,j] = sum_h sum_e dq~[b,h,t,e] Bm[j][h*D + e]: 16 rows x RP columns per block,
+// Bm staged 64 columns of one head at a time
+template <typename T, int D, int RP>
+__global__ __launch_bounds__(256) void sbwd_du_kernel(const float* __restrict__ dqt, const T* __restrict__ Bm, int r,
+                                                      float* __restrict__ dU, int Hq, int nq) {
+  constexpr int EC = 64;
+  __shared__ float bs[RP * (EC + 1)];
+  __shared__ float qs[16 * EC];
+  const int tid = threadIdx.x, b = blockIdx.y;
+  const int tl = tid >> 4, jg = tid & 15;
+  const int t0 = blockIdx.x * 16;
+  float acc[RP / 16];
+#pragma unroll
+  for (int m = 0; m < RP / 16; ++m) acc[m] = 0.f;
+  for (int h = 0; h < Hq; ++h)
+    for (int e0 = 0; e0 < D; e0 += EC) {
+      __syncthreads();
+      for (int x = tid; x < RP * EC; x += 256) {
+        const int j = x / EC, e = x % EC;
+        bs[j * (EC + 1) + e] = j < r ? Elem<T>::to_f(Bm[(size_t)j * Hq * D + (size_t)h * D + e0 + e]) : 0.f;
+      }
+      for (int x = tid; x < 16 * EC; x += 256) {
+        const int tt = t0 + x / EC;
+        qs[x] = tt < nq ? dqt[(((size_t)b * Hq + h) * nq + tt) * D + e0 + x % EC] : 0.f;
+      }
+      __syncthreads();
+      for (int e = 0; e < EC; ++e) {
+        const float a = qs[tl * EC + e];
+#pragma unroll
+        for (int m = 0; m < RP / 16; ++m) acc[m] += a * bs[(jg + 16 * m) * (EC + 1) + e];
+      }
+    }
+  const int t = t0 + tl;
+  if (t < nq) {
+#pragma unroll
+    for (int m = 0; m < RP / 16; ++m) dU[((size_t)b * nq + t) * RP + jg + 16 * m] = acc[m];
+  }
+}
+
+// dx[b, slot(q0+t), m] = sum_j dU[b,t,j] A[m][j]: 16 rows x 256 hidden columns per block
+template <typename T, int RP>
+__global__ __launch_bounds__(256) void sbwd_dx_kernel(const float* __restrict__ dU, const T* __restrict__ A, int Dh,
+                                                      int r, float* __restrict__ dx, int N, int q0, int nq) {
+  __shared__ float us[16 * RP];
+  const int tid = threadIdx.x, b = blockIdx.z;
+  const int t0 = blockIdx.x * 16, m = blockIdx.y * 256 + tid;
+  for (int x = tid; x < 16 * RP; x += 256) {
+    const int tt = t0 + x / RP;
+    us[x] = tt < nq ? dU[((size_t)b * nq + tt) * RP + x % RP] : 0.f;
+  }
+  __syncthreads();
+  if (m >= Dh) return;
+  float a[RP];
+#pragma unroll
+  for (int j = 0; j < RP; ++j) a[j] = j < r ? Elem<T>::to_f(A[(size_t)m * r + j]) : 0.f;
+  const size_t L = (size_t)N * kSlots;
+  for (int tl = 0; tl < 16; ++tl) {
+    const int t = t0 + tl;
+    if (t >= nq) break;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < RP; ++j) acc += us[tl * RP + j] * a[j];
+    dx[((size_t)b * L + slot_of_c(q0 + t)) * Dh + m] = acc;
+  }
+}
+
+// Partial dB over one range of rows: part[sp][j][col] = sum_rows U[row][j] dq~[b,h,t,e], col = h*D + e
+template <int D, int RP>
+__global__ __launch_bounds__(256) void sbwd_db_kernel(const float* __restrict__ U, const float* __restrict__ dqt,
+                                                      float* __restrict__ part, int Hq, int nq, int rows_total,
+                                                      int rows_per) {
+  __shared__ float us[16 * RP];
+  const int tid = threadIdx.x, sp = blockIdx.y;
+  const int col = blockIdx.x * 256 + tid;
+  const int HD = Hq * D;
+  const int r0 = sp * rows_per, r1 = min(rows_total, r0 + rows_per);
+  const int h = min(col, HD - 1) / D, e = min(col, HD - 1) % D;
+  float acc[RP];
+#pragma unroll
+  for (int j = 0; j < RP; ++j) acc[j] = 0.f;
+  for (int rb = r0; rb < r1; rb += 16) {
+    __syncthreads();
+    for (int x = tid; x < 16 * RP; x += 256) {
+      const int row = rb + x / RP;
+      us[x] = row < r1 ? U[(size_t)row * RP + x % RP] : 0.f;
+    }
+    __syncthreads();
+    for (int tl = 0; tl < 16 && rb + tl < r1; ++tl) {
+      const int row = rb + tl, b = row / nq, t = row % nq;
+      const float v = dqt[(((size_t)b * Hq + h) * nq + t) * D + e];
+#pragma unroll
+      for (int j = 0; j < RP; ++j) acc[j] += us[tl * RP + j] * v;
+    }
+  }
+  if (col < HD) {
+#pragma unroll
+    for (int j = 0; j < RP; ++j) part[((size_t)sp * RP + j) * HD + col] = acc[j];
+  }
+}
+
+// Partial dA over one range of rows: part[sp][m][j] = sum_rows x[b, slot(q0+t), m] dU[row][j]
+template <typename T, int RP>
+__global__ __launch_bounds__(256) void sbwd_da_kernel(const T* __restrict__ x, const float* __restrict__ dU,
+                                                      float* __restrict__ part, int Dh, int N, int q0, int nq,
+                                                      int rows_total, int rows_per) {
+  __shared__ float us[16 * RP];
+  const int tid = threadIdx.x, sp = blockIdx.y;
+  const int m = blockIdx.x * 256 + tid;
+  const int r0 = sp * rows_per, r1 = min(rows_total, r0 + rows_per);
+  const size_t L = (size_t)N * kSlots;
+  float acc[RP];
+#pragma unroll
+  for (int j = 0; j < RP; ++j) acc[j] = 0.f;
+  for (int rb = r0; rb < r1; rb += 16) {
+    __syncthreads();
+    for (int y = tid; y < 16 * RP; y += 256) {
+      const int row = rb + y / RP;
+      us[y] = row < r1 ? dU[(size_t)row * RP + y % RP] : 0.f;
+    }
+    __syncthreads();
+    if (m < Dh) {
+      for (int tl = 0; tl < 16 && rb + tl < r1; ++tl) {
+        const int row = rb + tl, b = row / nq, t = row % nq;
+        const float v = Elem<T>::to_f(x[((size_t)b * L + slot_of_c(q0 + t)) * Dh + m]);
+#pragma unroll
+        for (int j = 0; j < RP; ++j) acc[j] += us[tl * RP + j] * v;
+      }
+    }
+  }
+  if (m < Dh) {
+#pragma unroll
+    for (int j = 0; j < RP; ++j) part[((size_t)sp * Dh + m) * RP + j] = acc[j];
+  }
+}
+
+// dA[m][j] (j < r) and dB[j][col] (j < r) from the partials, added in split order
+__global__ __launch_bounds__(256) void sbwd_reduce_kernel(const float* __restrict__ pa, const float* __restrict__ pb,
+                                                          float* __restrict__ dA, float* __restrict__ dB, int nsp,
+                                                          int Dh, int r, int RP, int HD) {
+  const size_t na = (size_t)Dh * r, nb = (size_t)r * HD;
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < na + nb; x += (size_t)gridDim.x * 256) {
+    float a = 0.f;
+    if (x < na) {
+      const size_t m = x / r, j = x % r;
+      for (int sp = 0; sp < nsp; ++sp) a += pa[((size_t)sp * Dh + m) * RP + j];
+      dA[x] = a;
+    } else {
+      const size_t y = x - na, j = y / HD, col = y % HD;
+      for (int sp = 0; sp < nsp; ++sp) a += pb[((size_t)sp * RP + j) * HD + col];
+      dB[y] = a;
+    }
+  }
+}
+
+struct ScoreBwdWs {
+  float *qt, *upart, *U, *dqt, *dU, *pa, *pb;
+  int *cnt, *off, *th, *list;
+  int nsplit, RP, nsp, rows_per;
+};
+
+static int sbwd_nsp(int rows) { return std::max(1, std::min(64, (rows + 127) / 128)); }
+
+static ScoreBwdWs sbwd_carve(void* ws, const RouteDims& dm, int Dh, int r, int K, int nq) {
+  ScoreBwdWs o;
+  o.nsplit = qtilde_u_splits(dm, Dh, nq);
+  o.RP = qtilde_rank_pad(r);
+  const int rows = dm.B * nq;
+  o.nsp = sbwd_nsp(rows);
+  o.rows_per = (rows + o.nsp - 1) / o.nsp;
+  const size_t rh = (size_t)dm.B * dm.Hq * nq, bg = (size_t)dm.B * dm.Hkv;
+  char* w = (char*)ws;
+  auto take = [&](size_t bytes) { char* p = w; w += al256(bytes); return p; };
+  o.qt = (float*)take(rh * dm.d * 4);
+  o.dqt = (float*)take(rh * dm.d * 4);
+  o.upart = (float*)take((size_t)o.nsplit * rows * o.RP * 4);
+  o.U = (float*)take((size_t)rows * o.RP * 4);
+  o.dU = (float*)take((size_t)rows * o.RP * 4);
+  o.pa = (float*)take((size_t)o.nsp * Dh * o.RP * 4);
+  o.pb = (float*)take((size_t)o.nsp * o.RP * dm.Hq * dm.d * 4);
+  o.cnt = (int*)take(bg * dm.N * 4);
+  o.off = (int*)take(bg * (dm.N + 1) * 4);
+  o.th = (int*)take(bg * bwd_ntile(nq) * dm.N * 4);
+  o.list = (int*)take(bg * nq * K * 4);
+  return o;
+}
+
+size_t score_bwd_ws_bytes(const RouteDims& dm, int Dh, int r, int K, int nq) {
+  const int nsplit = qtilde_u_splits(dm, Dh, nq), RP = qtilde_rank_pad(r), rows = dm.B * nq, nsp = sbwd_nsp(rows);
+  const size_t rh = (size_t)dm.B * dm.Hq * nq, bg = (size_t)dm.B * dm.Hkv;
+  return 2 * al256(rh * dm.d * 4) + al256((size_t)nsplit * rows * RP * 4) + 2 * al256((size_t)rows * RP * 4) +
+         al256((size_t)nsp * Dh * RP * 4) + al256((size_t)nsp * RP * dm.Hq * dm.d * 4) + al256(bg * dm.N * 4) +
+         al256(bg * (dm.N + 1) * 4) + al256(bg * bwd_ntile(nq) * dm.N * 4) + al256(bg * nq * K * 4);
+}
+
+template <typename T, int D, int RP>
+static hipError_t launch_score_bwd_t(const RouteDims& dm, const void* x, const void* A, const void* Bm, int Dh, int r,
+                                     const float* s, float beta, float scale, int K, int q0, int nq,
+                                     const int32_t* idx, const float* dzsel, float* dq, float* dx, float* dA,
+                                     float* dBm, float* ds, float* dH, const ScoreBwdWs& w, hipStream_t st) {
+  const int rows = dm.B * nq;
+  // inverse index of the selections (as the attention backward builds it)
+  BwdParams ip;
+  ip.idx = idx;
+  ip.zsel = nullptr;
+  ip.dzsel = const_cast<float*>(dzsel);
+  ip.cnt = w.cnt;
+  ip.off = w.off;
+  ip.th = w.th;
+  ip.list = w.list;
+  ip.B = dm.B;
+  ip.Hq = dm.Hq;
+  ip.Hkv = dm.Hkv;
+  ip.N = dm.N;
+  ip.G = dm.Hq / dm.Hkv;
+  ip.K = K;
+  ip.q0 = q0;
+  ip.nq = nq;
+  ip.scale = scale;
+  const size_t bgn = (size_t)dm.B * dm.Hkv * dm.N;
+  const int ntile = bwd_ntile(nq);
+  const size_t idx_lds = (size_t)dm.N * 4;
+  hipError_t e = hipFuncSetAttribute((const void*)bwd_hist_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)idx_lds);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)bwd_fill_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)idx_lds);
+  if (e != hipSuccess) return e;
+  if (nq > 0 && K > 0) {
+    hipLaunchKernelGGL(bwd_hist_kernel, dim3(ntile, dm.B * dm.Hkv), dim3(256), idx_lds, st, ip);
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(dm.B * dm.Hkv), dim3(256), 0, st, ip, ntile);
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3(ntile, dm.B * dm.Hkv), dim3(64), idx_lds, st, ip);
+  } else {
+    const size_t no = (size_t)dm.B * dm.Hkv * (dm.N + 1);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)std::min<size_t>((bgn + 255) / 256, 65535)), dim3(256), 0,
+                       st, w.cnt, bgn);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)std::min<size_t>((no + 255) / 256, 65535)), dim3(256), 0,
+                       st, w.off, no);
+  }
+  if (nq > 0) {
+    hipLaunchKernelGGL((sbwd_dqt_kernel<D>), dim3((nq + 3) / 4, dm.B * dm.Hq), dim3(256), 0, st, idx, dzsel, s,
+                       w.dqt, dq, scale, dm.Hq, dm.Hkv, dm.N, K, q0, nq);
+  }
+  hipLaunchKernelGGL((sbwd_ds_kernel<D>), dim3((unsigned)bgn), dim3(256), 0, st, ip, (const float*)w.qt, ds, dH,
+                     beta);
+  if (nq > 0) {
+    const size_t nu = (size_t)rows * RP;
+    hipLaunchKernelGGL(sbwd_usum_kernel, dim3((unsigned)std::min<size_t>((nu + 255) / 256, 65535)), dim3(256), 0,
+                       st, (const float*)w.upart, w.nsplit, nu, w.U);
+    hipLaunchKernelGGL((sbwd_du_kernel<T, D, RP>), dim3((nq + 15) / 16, dm.B), dim3(256), 0, st,
+                       (const float*)w.dqt, (const T*)Bm, r, w.dU, dm.Hq, nq);
+    hipLaunchKernelGGL((sbwd_dx_kernel<T, RP>), dim3((nq + 15) / 16, (Dh + 255) / 256, dm.B), dim3(256), 0, st,
+                       (const float*)w.dU, (const T*)A, Dh, r, dx, dm.N, q0, nq);
+  }
+  const int HD = dm.Hq * D;
+  hipLaunchKernelGGL((sbwd_db_kernel<D, RP>), dim3((HD + 255) / 256, w.nsp), dim3(256), 0, st, (const float*)w.U,
+                     (const float*)w.dqt, w.pb, dm.Hq, nq, rows, w.rows_per);
+  hipLaunchKernelGGL((sbwd_da_kernel<T, RP>), dim3((Dh + 255) / 256, w.nsp), dim3(256), 0, st, (const T*)x,
+                     (const float*)w.dU, w.pa, Dh, dm.N, q0, nq, rows, w.rows_per);
+  const size_t nred = (size_t)Dh * r + (size_t)r * HD;
+  hipLaunchKernelGGL(sbwd_reduce_kernel, dim3((unsigned)std::min<size_t>((nred + 255) / 256, 65535)), dim3(256), 0,
+                     st, (const float*)w.pa, (const float*)w.pb, dA, dBm, w.nsp, Dh, r, RP, HD);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_score_bwd_r(const RouteDims& dm, const void* x, const void* A, const void* Bm, int Dh, int r,
+                                     const float* s, float beta, float scale, int K, int q0, int nq,
+                                     const int32_t* idx, const float* dzsel, float* dq, float* dx, float* dA,
+                                     float* dBm, float* ds, float* dH, const ScoreBwdWs& w, hipStream_t st) {
+  if (w.RP == 32)
+    return launch_score_bwd_t<T, D, 32>(dm, x, A, Bm, Dh, r, s, beta, scale, K, q0, nq, idx, dzsel, dq, dx, dA, dBm,
+                                        ds, dH, w, st);
+  if (w.RP == 64)
+    return launch_score_bwd_t<T, D, 64>(dm, x, A, Bm, Dh, r, s, beta, scale, K, q0, nq, idx, dzsel, dq, dx, dA, dBm,
+                                        ds, dH, w, st);
+  return launch_score_bwd_t<T, D, 128>(dm, x, A, Bm, Dh, r, s, beta, scale, K, q0, nq, idx, dzsel, dq, dx, dA, dBm,
+                                       ds, dH, w, st);
+}
+
+hipError_t launch_route_score_backward(const RouteDims& dm, const void* q, const void* x, const void* A,
+                                       const void* Bm, int Dh, int r, const float* s, float beta, float scale, int K,
+                                       int q0, int nq, const int32_t* idx, const float* dzsel, float* dq, float* dx,
+                                       float* dA, float* dBm, float* ds, float* dH, void* ws, hipStream_t st) {
+  const ScoreBwdWs w = sbwd_carve(ws, dm, Dh, r, K, nq);
+  if (nq > 0) {
+    hipError_t e = launch_qtilde_with_u(dm, q, x, A, Bm, Dh, r, w.qt, w.upart, q0, nq, st);
+    if (e != hipSuccess) return e;
+  }
+  if (dm.dtype == 1)
+    return dm.d == 128 ? launch_score_bwd_r<bf16_t, 128>(dm, x, A, Bm, Dh, r, s, beta, scale, K, q0, nq, idx, dzsel,
+                                                         dq, dx, dA, dBm, ds, dH, w, st)
+                       : launch_score_bwd_r<bf16_t, 64>(dm, x, A, Bm, Dh, r, s, beta, scale, K, q0, nq, idx, dzsel,
+                                                        dq, dx, dA, dBm, ds, dH, w, st);
+  return dm.d == 128 ? launch_score_bwd_r<float, 128>(dm, x, A, Bm, Dh, r, s, beta, scale, K, q0, nq, idx, dzsel, dq,
+                                                      dx, dA, dBm, ds, dH, w, st)
+                     : launch_score_bwd_r<float, 64>(dm, x, A, Bm, Dh, r, s, beta, scale, K, q0, nq, idx, dzsel, dq,
+                                                     dx, dA, dBm, ds, dH, w, st);
+}
 
 template <int D>
 static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t st) {

@@ -39,6 +39,12 @@ hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const voi
                                    float beta, float scale, int K, int radius, int q0, int nq,
                                    int32_t* idx, float* zsel, const ScoreWs& ws, hipStream_t st);
 
+// q~ and the partial sums of u = x A (general path) for the scoring's backward
+int qtilde_u_splits(const RouteDims& dm, int Dh, int nq);
+int qtilde_rank_pad(int r);
+hipError_t launch_qtilde_with_u(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
+                                int Dh, int r, float* qt, float* upart, int q0, int nq, hipStream_t st);
+
 // ---- routed_attention and swa_attention (attention.hip)
 struct AttnPlan {
   int waves;       // waves per block
@@ -68,6 +74,14 @@ hipError_t launch_routed_attention_backward(const RouteDims& dm, const void* q, 
                                             float scale, int q0, int nq, const void* o, const float* lse,
                                             const void* dO, float* dq, float* dk, float* dv, float* dzsel,
                                             void* ws, hipStream_t st);
+
+size_t score_bwd_ws_bytes(const RouteDims& dm, int Dh, int r, int K, int nq);
+hipError_t launch_route_score_backward(const RouteDims& dm, const void* q, const void* x, const void* A,
+                                       const void* Bm, int Dh, int r, const float* s, float beta, float scale, int K,
+                                       int q0, int nq, const int32_t* idx, const float* dzsel, float* dq, float* dx,
+                                       float* dA, float* dBm, float* ds, float* dH, void* ws, hipStream_t st);
+hipError_t launch_chunk_summary_backward(const RouteDims& dm, const void* q, const void* k, float scale,
+                                         const float* ds, const float* dH, float* dq, float* dk, hipStream_t st);
 
 size_t swa_lds_bytes(int d, int dtype);
 hipError_t launch_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q,

@@ -1739,6 +1739,43 @@ static hipError_t launch_small_score(const RouteDims& dm, const void* q, const v
   return hipGetLastError();
 }
 
+// q~ (float32 [B,Hq,nq,d]) and the partial sums of u = x A ([nsplit,B,nq,RP]) through
+// the general two-kernel path, for the backward of the scoring.
+template <typename T, int D, int RP>
+static void launch_qtilde_uq(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
+                             int Dh, int r, float* qt, float* upart, int q0, int nq, hipStream_t st) {
+  const int nsplit = u_splits(dm, Dh, nq);
+  const int nslices = (Dh + kUKc - 1) / kUKc;
+  const int per = (nslices + nsplit - 1) / nsplit;
+  hipLaunchKernelGGL((u_kernel<T, RP>), dim3((nq + 63) / 64, dm.B, nsplit), dim3(256), 0, st, (const T*)x,
+                     (const T*)A, Dh, r, upart, dm.N, q0, nq, per);
+  hipLaunchKernelGGL((q_kernel<T, D, RP>), dim3((nq + 63) / 64, dm.Hq, dm.B), dim3(256), 0, st, (const T*)q,
+                     (const T*)Bm, r, upart, nsplit, qt, dm.Hq, dm.N, q0, nq);
+}
+
+template <typename T, int D>
+static void launch_qtilde_uq_r(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
+                               int Dh, int r, float* qt, float* upart, int q0, int nq, hipStream_t st) {
+  if (r <= 32) launch_qtilde_uq<T, D, 32>(dm, q, x, A, Bm, Dh, r, qt, upart, q0, nq, st);
+  else if (r <= 64) launch_qtilde_uq<T, D, 64>(dm, q, x, A, Bm, Dh, r, qt, upart, q0, nq, st);
+  else launch_qtilde_uq<T, D, 128>(dm, q, x, A, Bm, Dh, r, qt, upart, q0, nq, st);
+}
+
+int qtilde_u_splits(const RouteDims& dm, int Dh, int nq) { return nq > 0 ? u_splits(dm, Dh, nq) : 1; }
+int qtilde_rank_pad(int r) { return rank_pad(r); }
+
+hipError_t launch_qtilde_with_u(const RouteDims& dm, const void* q, const void* x, const void* A, const void* Bm,
+                                int Dh, int r, float* qt, float* upart, int q0, int nq, hipStream_t st) {
+  if (dm.dtype == 1) {
+    if (dm.d == 64) launch_qtilde_uq_r<bf16_t, 64>(dm, q, x, A, Bm, Dh, r, qt, upart, q0, nq, st);
+    else launch_qtilde_uq_r<bf16_t, 128>(dm, q, x, A, Bm, Dh, r, qt, upart, q0, nq, st);
+  } else {
+    if (dm.d == 64) launch_qtilde_uq_r<float, 64>(dm, q, x, A, Bm, Dh, r, qt, upart, q0, nq, st);
+    else launch_qtilde_uq_r<float, 128>(dm, q, x, A, Bm, Dh, r, qt, upart, q0, nq, st);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const void* x, const void* A,
                                    const void* Bm, int D, int r, const float* s, const float* H,
                                    float beta, float scale, int K, int radius, int q0, int nq,

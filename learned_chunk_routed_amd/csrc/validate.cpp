@@ -103,6 +103,29 @@ int check_routed_attention_backward(const lcr_dims* d, const void* q, const void
   return LCR_OK;
 }
 
+int check_route_score_backward(const lcr_dims* d, const void* q, const void* x, const void* A, const void* Bm,
+                               int D, int r, const float* s, float beta, float scale, int K, int q0, int nq,
+                               const int32_t* idx, const float* dzsel, const float* dq, const float* dx,
+                               const float* dA, const float* dBm, const float* ds, const float* dH) {
+  int st = check_dims(d);
+  if (st != LCR_OK) return st;
+  if (D < 1 || r < 1 || K < 0) return LCR_ERR_ARG;
+  if (r > 128) return LCR_ERR_UNSUPPORTED;
+  if (K > LCR_MAX_TOPK) return LCR_ERR_UNSUPPORTED;
+  if (!finite(beta) || !finite(scale)) return LCR_ERR_ARG;
+  st = check_query_range(d, q0, nq);
+  if (st != LCR_OK) return st;
+  if (!A || !Bm || !dA || !dBm || !ds || !dH) return LCR_ERR_ARG;
+  if (nq > 0) {
+    if (!q || !x || !s || !dq || !dx) return LCR_ERR_ARG;
+    if (K > 0 && (!idx || !dzsel)) return LCR_ERR_ARG;
+  }
+  if ((long long)nq * K > (long long)std::numeric_limits<int>::max()) return LCR_ERR_UNSUPPORTED;
+  if ((long long)d->B * nq > (long long)std::numeric_limits<int>::max() / 2) return LCR_ERR_UNSUPPORTED;
+  if (d->N > kMaxChunksBackward) return LCR_ERR_UNSUPPORTED;
+  return LCR_OK;
+}
+
 int check_swa(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, const void* k, const void* v,
               int radius, float scale, const void* o) {
   if (dtype != LCR_F32 && dtype != LCR_BF16) return LCR_ERR_DTYPE;

@@ -24,6 +24,10 @@ int check_routed_attention_backward(const lcr_dims* d, const void* q, const void
                                     const int32_t* idx, const float* zsel, int K, int radius, float scale,
                                     int q0, int nq, const void* o, const float* lse, const void* dO,
                                     const float* dq, const float* dk, const float* dv, const float* dzsel);
+int check_route_score_backward(const lcr_dims* d, const void* q, const void* x, const void* A, const void* Bm,
+                               int D, int r, const float* s, float beta, float scale, int K, int q0, int nq,
+                               const int32_t* idx, const float* dzsel, const float* dq, const float* dx,
+                               const float* dA, const float* dBm, const float* ds, const float* dH);
 int check_swa(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q, const void* k, const void* v,
               int radius, float scale, const void* o);
 

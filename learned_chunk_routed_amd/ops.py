@@ -224,6 +224,75 @@ def routed_attention_backward(q, k, v, idx, zsel, o, lse, dO, *, radius, scale=N
     return dq, dk, dv, dz
 
 
+def route_score_backward(q, x, A, Bm, s, idx, dzsel, *, beta=0.0, scale=None, q0=0, nq=None, dq=None, ws=None):
+    """Gradients of route_score_topk's chunk logits with the selection idx fixed.
+
+    dzsel [B,Hq,nq,K] float32 is the upstream gradient (e.g. from
+    routed_attention_backward). dq [B,Hq,L,d] float32 is accumulated into at the
+    queried rows (allocated as zeros when not given). Returns a dict with dq,
+    dx [B,L,D] (queried rows), dA [D,r], dBm [r,Hq*d], ds [B,Hq,N,d], dH [B,Hq,N],
+    all float32."""
+    lib = _lib.load()
+    dev = q.device
+    Hkv = idx.shape[1]
+    dims = _dims_from(q, Hkv)
+    B, Hq, N, d = dims.B, dims.Hq, dims.N, dims.d
+    T = N * CONTENT
+    nq = T - q0 if nq is None else nq
+    K = idx.shape[-1]
+    D, r = A.shape
+    _check(q, "q", dev)
+    _check(x, "x", dev, q.dtype, (B, N * SLOTS, D))
+    _check(A, "A", dev, q.dtype, (D, r))
+    _check(Bm, "Bm", dev, q.dtype, (r, Hq * d))
+    _check(s, "s", dev, torch.float32, (B, Hq, N, d))
+    _check(idx, "idx", dev, torch.int32, (B, Hkv, nq, K))
+    _check(dzsel, "dzsel", dev, torch.float32, (B, Hq, nq, K))
+    scale = default_scale(d) if scale is None else float(scale)
+    if dq is None:
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+    _check(dq, "dq", dev, torch.float32, tuple(q.shape))
+    out = dict(dq=dq, dx=torch.zeros((B, N * SLOTS, D), dtype=torch.float32, device=dev),
+               dA=torch.empty((D, r), dtype=torch.float32, device=dev),
+               dBm=torch.empty((r, Hq * d), dtype=torch.float32, device=dev),
+               ds=torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev),
+               dH=torch.empty((B, Hq, N), dtype=torch.float32, device=dev))
+    nbytes = workspace_bytes(_lib.OP_ROUTE_SCORE_BACKWARD, dims, D, r, K, nq, 0)
+    w = _workspace(nbytes, dev, ws)
+    check(lib.lcr_route_score_backward(dims, q.data_ptr(), x.data_ptr(), A.data_ptr(), Bm.data_ptr(), D, r,
+                                       s.data_ptr(), float(beta), scale, K, q0, nq,
+                                       idx.data_ptr() if K > 0 else None, dzsel.data_ptr() if K > 0 else None,
+                                       dq.data_ptr(), out["dx"].data_ptr(), out["dA"].data_ptr(),
+                                       out["dBm"].data_ptr(), out["ds"].data_ptr(), out["dH"].data_ptr(),
+                                       None if w is None else w.data_ptr(), nbytes, _stream(dev)),
+          "lcr_route_score_backward")
+    return out
+
+
+def chunk_summary_backward(q, k, ds, dH, scale=None, dq=None, dk=None):
+    """Gradients of chunk_summary for upstream ds [B,Hq,N,d], dH [B,Hq,N] (float32).
+    Writes the mask-slot rows of dq and adds into the content rows of dk (both float32,
+    allocated as zeros when not given); returns (dq, dk)."""
+    lib = _lib.load()
+    dev = q.device
+    dims = _dims_from(q, k.shape[1])
+    B, Hq, Hkv, N, d = dims.B, dims.Hq, dims.Hkv, dims.N, dims.d
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (B, Hkv, N * SLOTS, d))
+    _check(ds, "ds", dev, torch.float32, (B, Hq, N, d))
+    _check(dH, "dH", dev, torch.float32, (B, Hq, N))
+    scale = default_scale(d) if scale is None else float(scale)
+    if dq is None:
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=dev)
+    _check(dq, "dq", dev, torch.float32, tuple(q.shape))
+    _check(dk, "dk", dev, torch.float32, tuple(k.shape))
+    check(lib.lcr_chunk_summary_backward(dims, q.data_ptr(), k.data_ptr(), scale, ds.data_ptr(), dH.data_ptr(),
+                                         dq.data_ptr(), dk.data_ptr(), _stream(dev)), "lcr_chunk_summary_backward")
+    return dq, dk
+
+
 def swa_attention(q, k, v, *, radius, scale=None, out=None, lse=None, want_lse=False):
     """Bidirectional sliding-window attention over slots |u - t| <= radius: o [B,Hq,L,d]."""
     lib = _lib.load()

@@ -114,24 +114,21 @@ def route_score_backward(q_rows, x_rows, A, Bm, s, H, idx, dzsel, beta, scale):
     N = s.shape[2]
     u = x_rows @ A                                                      # [B,n,r]
     qt = q_rows + (u @ Bm).reshape(B, n, Hq, d).transpose(0, 2, 1, 3)
-    # scatter dzsel onto the full score grid dz [B,Hq,n,N]; idx entries are distinct per row
+    # scatter dzsel onto the full score grid dz [B,Hq,n,N] (entries with idx -1 are dropped)
     dzfull = np.zeros((B, Hq, n, N))
     idx_h = np.repeat(idx, G, axis=1)
-    for b in range(B):
-        for h in range(Hq):
-            for t in range(n):
-                for kk, c in enumerate(idx_h[b, h, t]):
-                    if c >= 0:
-                        dzfull[b, h, t, c] += dzsel[b, h, t, kk]
+    bb, hh, tt, kk = np.nonzero(idx_h >= 0)
+    np.add.at(dzfull, (bb, hh, tt, idx_h[bb, hh, tt, kk]), dzsel[bb, hh, tt, kk])
     # z = scale q~ . s - beta H
-    dqt = scale * np.einsum("bhnc,bhcd->bhnd", dzfull, s)
-    ds = scale * np.einsum("bhnc,bhnd->bhcd", dzfull, qt)
+    dqt = scale * (dzfull @ s)                                          # [B,Hq,n,d]
+    ds = scale * (np.swapaxes(dzfull, -1, -2) @ qt)                     # [B,Hq,N,d]
     dH = -beta * dzfull.sum(axis=2)
     # q~ = q + u Bm (head h takes columns h*d .. h*d+d-1)
     dres = dqt.transpose(0, 2, 1, 3).reshape(B, n, Hq * d)            # [B,n,Hq*d]
-    dBm = np.einsum("bnr,bnc->rc", u, dres)
+    r = A.shape[1]
+    dBm = u.reshape(B * n, r).T @ dres.reshape(B * n, Hq * d)
     du = dres @ Bm.T                                                    # [B,n,r]
-    dA = np.einsum("bnD,bnr->Dr", x_rows, du)
+    dA = x_rows.reshape(B * n, -1).T @ du.reshape(B * n, r)
     dx = du @ A.T
     return dqt, dx, dA, dBm, ds, dH
 

@@ -214,6 +214,41 @@ def test_routed_attention_backward_validation(lib):
     assert call(dm=dims(N=32769)) == _lib.LCR_ERR_UNSUPPORTED
 
 
+def test_chunk_summary_backward_validation(lib):
+    def call(dm=None, scale=0.1, ptrs=None):
+        pt = ptrs or [P] * 6
+        return lib.lcr_chunk_summary_backward(dm or dims(), pt[0], pt[1], scale, pt[2], pt[3], pt[4], pt[5], NULL)
+    assert call(dm=dims(dtype=4)) == _lib.LCR_ERR_DTYPE
+    assert call(dm=dims(d=96)) == _lib.LCR_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == _lib.LCR_ERR_ARG
+    for i in range(6):
+        pt = [P] * 6
+        pt[i] = NULL
+        assert call(ptrs=pt) == _lib.LCR_ERR_ARG, i
+
+
+def test_route_score_backward_validation(lib):
+    def call(dm=None, D=3584, r=64, K=32, q0=0, nq=100, beta=0.0, scale=0.1, ptrs=None, ws=P, ws_bytes=1 << 40):
+        pt = ptrs or [P] * 13
+        return lib.lcr_route_score_backward(dm or dims(), pt[0], pt[1], pt[2], pt[3], D, r, pt[4], beta, scale, K, q0,
+                                            nq, pt[5], pt[6], pt[7], pt[8], pt[9], pt[10], pt[11], pt[12], ws,
+                                            ws_bytes, NULL)
+    assert call(r=129) == _lib.LCR_ERR_UNSUPPORTED
+    assert call(r=0) == _lib.LCR_ERR_ARG
+    assert call(K=-1) == _lib.LCR_ERR_ARG
+    assert call(beta=float("nan")) == _lib.LCR_ERR_ARG
+    assert call(q0=10, nq=256 * 63) == _lib.LCR_ERR_ARG
+    for i in range(13):
+        pt = [P] * 13
+        pt[i] = NULL
+        assert call(ptrs=pt) == _lib.LCR_ERR_ARG, i
+    need = lib.lcr_workspace_bytes(_lib.OP_ROUTE_SCORE_BACKWARD, dims(), 3584, 64, 32, 0, 100)
+    assert need > 0 and need % 256 == 0
+    assert call(ws_bytes=need - 1) == _lib.LCR_ERR_WORKSPACE
+    assert call(ws=NULL) == _lib.LCR_ERR_WORKSPACE
+    assert call(dm=dims(N=40000)) == _lib.LCR_ERR_UNSUPPORTED
+
+
 def test_swa_validation(lib):
     def call(B=1, Hq=28, Hkv=4, L=4096, d=128, dtype=1, R=1280, scale=0.1, ptrs=None):
         pt = ptrs or [P] * 4

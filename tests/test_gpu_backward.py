@@ -208,3 +208,111 @@ def test_backward_reproducible_and_empty_range():
                                                    torch.zeros_like(q), radius=cfg.R, scale=cfg.scale, q0=5, nq=0)
     torch.cuda.synchronize()
     assert dz.numel() == 0 and not dq.any() and not dk.any() and not dv.any()
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "prefill_16k"])
+def test_chunk_summary_backward(name):
+    """Pooling backward: mask-slot rows of dq written, content rows of dk accumulated
+    onto what is there (here a seeded non-zero start), against the oracle."""
+    cfg = get_config(name)
+    print(f"[case] chunk_summary_backward {name}", flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, 0, 1)
+    q, k = to_dev(inp["q"]), to_dev(inp["k"])
+    dk0 = np.random.default_rng(3).standard_normal(inp["k"].shape).astype(np.float32)
+    dq, dk = lcr.chunk_summary_backward(q, k, to_dev(dr["ds"]), to_dev(dr["dH"]), scale=cfg.scale,
+                                        dk=torch.from_numpy(dk0).cuda())
+    torch.cuda.synchronize()
+    f_q, f_k = as_f64(inp["q"]), as_f64(inp["k"])
+    qm = f_q.reshape(cfg.B, cfg.Hq, cfg.N, SL, cfg.d)[:, :, :, SL - 1]
+    rq, rk = OB.chunk_summary_backward(qm, f_k, cfg.scale, dr["ds"].astype(np.float64),
+                                       dr["dH"].astype(np.float64))
+    gq = f64(dq).reshape(cfg.B, cfg.Hq, cfg.N, SL, cfg.d)
+    e_q = rel_err(gq[:, :, :, SL - 1], rq)
+    e_k = rel_err(f64(dk) - dk0, rk)
+    print(f"    dq={e_q:.2e} dk={e_k:.2e}", flush=True)
+    assert e_q < 1e-5 and e_k < 1e-5
+    assert not gq[:, :, :, :SL - 1].any(), "content rows of dq are not written"
+    assert np.array_equal(f64(dk).reshape(cfg.B, cfg.Hkv, cfg.N, SL, cfg.d)[:, :, :, SL - 1],
+                          dk0.reshape(cfg.B, cfg.Hkv, cfg.N, SL, cfg.d)[:, :, :, SL - 1]), "mask rows of dk untouched"
+
+
+SCORE_CASES = {
+    "tiny_fp32": ("tiny_fp32", {}, 0, None),
+    "bf16 G7 ragged range": ("prefill_16k", dict(N=12, Hq=14, Hkv=2, d=64, r=16, D=96, K=3, R=20, beta=0.4), 50, 333),
+    "bf16 B2 rank 128 entropy": ("prefill_32k_entropy", dict(N=10, Hq=8, Hkv=2, r=128, D=160, K=4, R=30), 0, None),
+    "prefill_16k": ("prefill_16k", {}, 0, None),
+}
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", list(SCORE_CASES))
+def test_route_score_backward(name):
+    """Scoring backward against the oracle: dq accumulated onto a seeded start at the
+    queried rows only, dx at the queried rows, dA, dBm, ds, dH in full."""
+    base, over, q0, nq = SCORE_CASES[name]
+    cfg = get_config(base, **over)
+    nq = cfg.T - q0 if nq is None else nq
+    print(f"[case] route_score_backward {name}: B={cfg.B} N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} r={cfg.r} "
+          f"D={cfg.D} K={cfg.K} beta={cfg.beta} q0={q0} nq={nq} dtype={cfg.dtype}", flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, q0, nq)
+    idx, zsel = selection(cfg, dr, q0, nq)
+    dz = np.where(np.isfinite(zsel), dr["zsel"], 0.0).astype(np.float32)
+    s_ref, _ = O.chunk_summary(as_f64(inp["q"]), as_f64(inp["k"]), cfg.scale)
+    s32 = s_ref.astype(np.float32)
+    dq0 = np.random.default_rng(11).standard_normal(inp["q"].shape).astype(np.float32)
+    out = lcr.route_score_backward(to_dev(inp["q"]), to_dev(inp["x"]), to_dev(inp["A"]), to_dev(inp["Bm"]),
+                                   torch.from_numpy(s32).cuda(), torch.from_numpy(idx.astype(np.int32)).cuda(),
+                                   torch.from_numpy(dz).cuda(), beta=cfg.beta, scale=cfg.scale, q0=q0, nq=nq,
+                                   dq=torch.from_numpy(dq0).cuda())
+    torch.cuda.synchronize()
+    queries = np.arange(q0, q0 + nq)
+    sl = O.slot_of(queries)
+    rq, rx, rA, rB, rs, rH = OB.route_score_backward(as_f64(inp["q"])[:, :, sl], as_f64(inp["x"])[:, sl],
+                                                     as_f64(inp["A"]), as_f64(inp["Bm"]), s32.astype(np.float64),
+                                                     None, idx, dz.astype(np.float64), cfg.beta, cfg.scale)
+    gq = f64(out["dq"])
+    gx = f64(out["dx"])
+    errs = dict(dq=rel_err(gq[:, :, sl] - dq0[:, :, sl], rq), dx=rel_err(gx[:, sl], rx), dA=rel_err(f64(out["dA"]), rA),
+                dBm=rel_err(f64(out["dBm"]), rB), ds=rel_err(f64(out["ds"]), rs), dH=rel_err(f64(out["dH"]), rH))
+    print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e < 1e-4, f"{name}: {n} error {e:.3e}"
+    other = np.setdiff1d(np.arange(cfg.L), sl)
+    assert np.array_equal(gq[:, :, other], dq0[:, :, other]), "dq rows outside the queried set are untouched"
+    assert not gx[:, other].any(), "dx rows outside the queried set stay zero"
+
+
+def test_route_layer_backward_end_to_end():
+    """The three backward calls chained (attention, scoring, pooling) give the whole
+    layer's gradients with the oracle's selection held fixed."""
+    cfg = get_config("prefill_16k", N=10, Hq=8, Hkv=2, d=128, r=16, D=96, K=3, R=30, beta=0.3)
+    print("[case] route layer backward end to end", flush=True)
+    inp = route_inputs(cfg)
+    f = {n: as_f64(inp[n]) for n in ("q", "k", "v", "x", "A", "Bm")}
+    queries = np.arange(cfg.T)
+    ref = O.route_layer(f["q"], f["k"], f["v"], f["x"], f["A"], f["Bm"], K=cfg.K, R=cfg.R, beta=cfg.beta,
+                        scale=cfg.scale, queries=queries)
+    dr = backward_draws(cfg, 0, cfg.T)
+    dO_rows = as_f64(dr["dO"])[:, :, O.slot_of(queries)]
+    want = OB.route_layer_backward(f["q"], f["k"], f["v"], f["x"], f["A"], f["Bm"], ref["idx"], dO_rows, R=cfg.R,
+                                   beta=cfg.beta, scale=cfg.scale, queries=queries)
+    d = {n: to_dev(inp[n]) for n in ("q", "k", "v", "x", "A", "Bm")}
+    res = lcr.route_layer(d["q"], d["k"], d["v"], d["x"], d["A"], d["Bm"], K=cfg.K, radius=cfg.R, beta=cfg.beta,
+                          scale=cfg.scale, want_lse=True)
+    idx_t = torch.from_numpy(ref["idx"].astype(np.int32)).cuda()     # the oracle's selection, as in `want`
+    zsel = torch.from_numpy(ref["zsel"].astype(np.float32)).cuda()
+    o, lse = lcr.routed_attention(d["q"], d["k"], d["v"], idx_t, zsel, radius=cfg.R, scale=cfg.scale, want_lse=True)
+    dq, dk, dv, dz = lcr.routed_attention_backward(d["q"], d["k"], d["v"], idx_t, zsel, o, lse, to_dev(dr["dO"]),
+                                                   radius=cfg.R, scale=cfg.scale)
+    sc = lcr.route_score_backward(d["q"], d["x"], d["A"], d["Bm"], res["s"], idx_t, dz, beta=cfg.beta,
+                                  scale=cfg.scale, dq=dq)
+    lcr.chunk_summary_backward(d["q"], d["k"], sc["ds"], sc["dH"], scale=cfg.scale, dq=dq, dk=dk)
+    torch.cuda.synchronize()
+    errs = dict(dq=rel_err(f64(dq), want["dq"]), dk=rel_err(f64(dk), want["dk"]), dv=rel_err(f64(dv), want["dv"]),
+                dx=rel_err(f64(sc["dx"]), want["dx"]), dA=rel_err(f64(sc["dA"]), want["dA"]),
+                dBm=rel_err(f64(sc["dBm"]), want["dBm"]))
+    print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e < BWD_TOL, f"{n} error {e:.3e}"
