@@ -18,8 +18,9 @@ Printed JSON line (one, rank 0):
   swa_64k      ms per sliding-window layer (65,536 slots, radius 1280)
   dense_16k    ms per dense bidirectional attention layer (16,384 slots, every
                slot attends to every slot: the sliding window with R >= L)
-  backward_16k ms per backward call of the routed attention on the 16K-prefill
-               workload (dq, dk, dv, dzsel), with its MFMA roofline
+  backward_16k ms of the route layer's backward on the 16K-prefill workload:
+               attention (dq, dk, dv, dzsel, with its MFMA roofline), scoring
+               (dq, dx, dA, dBm, ds, dH) and pooling (dq mask rows, dk)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--no-decode] [--no-swa] [--only {prefill,decode,swa,dense,backward,copy}]
@@ -375,9 +376,11 @@ def bench_dense(args, torch, lcr):
 
 
 def bench_backward(args, torch, lcr):
-    """Backward of the routed attention over the 16K-prefill workload: the forward's own
-    selection, chunk logits, output and log-normaliser (computed once, untimed) and a
-    seeded N(0,1) bf16 upstream gradient. Times the whole backward call."""
+    """Backward of the route layer over the 16K-prefill workload: the forward's own
+    selection, chunk logits, summaries, output and log-normaliser (computed once,
+    untimed) and a seeded N(0,1) bf16 upstream gradient. Times the attention backward
+    (dq, dk, dv, dzsel), the scoring backward (dq, dx, dA, dBm, ds, dH) and the pooling
+    backward (dq at the mask rows, dk) separately, each averaged over 5 calls."""
     from lcr_inputs import get_config, route_inputs
     cfg = get_config("prefill_16k")
     inp = route_inputs(cfg)
@@ -387,30 +390,43 @@ def bench_backward(args, torch, lcr):
     g = torch.Generator(device="cuda").manual_seed(7)
     dO = torch.randn(d["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
     dims = lcr.make_dims(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d, torch.bfloat16)
-    ws = torch.empty(lcr.workspace_bytes(4, dims, 0, 0, cfg.K, cfg.T, cfg.R), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(lcr.workspace_bytes(4, dims, 0, 0, cfg.K, cfg.T, cfg.R), dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(lcr.workspace_bytes(5, dims, cfg.D, cfg.r, cfg.K, cfg.T, 0), dtype=torch.uint8, device="cuda")
+    st = {}
 
-    def call():
-        return lcr.routed_attention_backward(d["q"], d["k"], d["v"], res["idx"], res["zsel"], res["o"], res["lse"],
-                                             dO, radius=cfg.R, scale=cfg.scale, ws=ws)
-    for _ in range(2):
-        call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 5
-    e0.record()
-    for _ in range(n):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
+    def attn():
+        st["a"] = lcr.routed_attention_backward(d["q"], d["k"], d["v"], res["idx"], res["zsel"], res["o"],
+                                                res["lse"], dO, radius=cfg.R, scale=cfg.scale, ws=ws_a)
+
+    def score():
+        st["s"] = lcr.route_score_backward(d["q"], d["x"], d["A"], d["Bm"], res["s"], res["idx"], st["a"][3],
+                                           beta=cfg.beta, scale=cfg.scale, dq=st["a"][0], ws=ws_s)
+
+    def pool():
+        lcr.chunk_summary_backward(d["q"], d["k"], st["s"]["ds"], st["s"]["dH"], scale=cfg.scale, dq=st["a"][0],
+                                   dk=st["a"][1])
+
+    ms = {}
+    for name, fn in (("attention", attn), ("scoring", score), ("pooling", pool)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / 5
     local, chunks = prefill_flops(cfg, int((res["idx"] >= 0).sum().item()))
     # per (head, query, key): S, dP and dQ on the query side (6d), S, dP, dV and dK on the key side (8d)
     flops = (local + chunks) * 14.0 / 4.0
-    tf = flops / (ms * 1e-3) / 1e12
-    return {"ms_per_call": round(ms, 4), "algorithmic_gflop": round(flops / 1e9, 1),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
-
+    tf = flops / (ms["attention"] * 1e-3) / 1e12
+    return {"ms_attention": round(ms["attention"], 4), "ms_scoring": round(ms["scoring"], 4),
+            "ms_pooling": round(ms["pooling"], 4), "ms_layer": round(sum(ms.values()), 4),
+            "attention_algorithmic_gflop": round(flops / 1e9, 1),
+            "roofline": {"bound": "mfma", "kernels": "attention backward call", "achieved": round(tf, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 def main():
     ap = argparse.ArgumentParser()

@@ -276,6 +276,7 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(int* a, size_t n) {
 // one wave per tile then walks its rows in order. The result does not depend on
 // scheduling, so dk and dv are reproducible bit for bit.
 constexpr int kIdxTile = 256;
+constexpr int kMaxGroup = 8;   // largest GQA group (query heads per KV head)
 
 __global__ __launch_bounds__(256) void bwd_hist_kernel(BwdParams p) {
   extern __shared__ int hist[];   // [N]
@@ -667,13 +668,19 @@ __global__ __launch_bounds__(256) void sbwd_dqt_kernel(const int32_t* __restrict
   float acc[D / 64];
 #pragma unroll
   for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
-  for (int kk = 0; kk < K; ++kk) {
-    const int c = id[kk];
-    if (c < 0) continue;
-    const float wz = dz[kk];
-    const float* sr = s + ((size_t)bh * N + c) * D;
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const int cl = k0 + lane < K ? id[k0 + lane] : -1;
+    const float wl = k0 + lane < K ? dz[k0 + lane] : 0.f;
+    const int n = min(64, K - k0);
+    for (int i = 0; i < n; ++i) {
+      const int c = __shfl(cl, i);
+      const float wz = __shfl(wl, i);
+      if (c >= 0) {
+        const float* sr = s + ((size_t)bh * N + c) * D;
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) acc[u] += wz * sr[lane + 64 * u];
+        for (int u = 0; u < D / 64; ++u) acc[u] += wz * sr[lane + 64 * u];
+      }
+    }
   }
   const size_t L = (size_t)N * kSlots;
   float* dqr = dq + ((size_t)bh * L + slot_of_c(q0 + t)) * D;
@@ -685,33 +692,62 @@ __global__ __launch_bounds__(256) void sbwd_dqt_kernel(const int32_t* __restrict
   }
 }
 
+// ds, dH of one chunk: wave w takes entries w, w+4, ... of the chunk's list for all G
+// heads of the group (lanes over d); the four waves' sums are added in LDS in wave
+// order. Entry words are read 64 at a time, one per lane, and broadcast.
 template <int D>
 __global__ __launch_bounds__(256) void sbwd_ds_kernel(BwdParams p, const float* __restrict__ qt, float* __restrict__ ds,
                                                       float* __restrict__ dH, float beta) {
+  constexpr int PL = D / 64;
+  __shared__ float red[4][kMaxGroup][D + 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = blockIdx.x % p.N, bg = blockIdx.x / p.N, b = bg / p.Hkv, g = bg % p.Hkv;
+  const int G = p.G;
   const int ncnt = p.cnt[(size_t)bg * p.N + c];
   const int* lst = p.list + (size_t)bg * p.nq * p.K + p.off[(size_t)bg * (p.N + 1) + c];
-  for (int hh = w; hh < p.G; hh += 4) {
-    const int h = g * p.G + hh;
-    const size_t bh = (size_t)b * p.Hq + h;
-    float acc[D / 64];
+  const size_t bh0 = (size_t)b * p.Hq + (size_t)g * G;
+  float acc[kMaxGroup][PL], hs[kMaxGroup];
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
-    float hs = 0.f;
-    for (int e = 0; e < ncnt; ++e) {
-      const int ent = lst[e];
-      const int t = ent / p.K, kk = ent % p.K;
-      const float wz = p.dzsel[(bh * p.nq + t) * p.K + kk];
-      const float* qr = qt + (bh * p.nq + t) * D;
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    hs[hh] = 0.f;
 #pragma unroll
-      for (int u = 0; u < D / 64; ++u) acc[u] += wz * qr[lane + 64 * u];
-      hs += wz;
+    for (int u = 0; u < PL; ++u) acc[hh][u] = 0.f;
+  }
+  for (int e0 = 0; e0 < ncnt; e0 += 256) {
+    const int mine = e0 + 4 * lane + w;           // this lane's entry word for the wave
+    const int ent = mine < ncnt ? lst[mine] : -1;
+    const int n = min(64, (ncnt - e0 - w + 3) / 4);
+    for (int i = 0; i < n; ++i) {
+      const int en = __shfl(ent, i);
+      const int t = en / p.K, kk = en % p.K;
+#pragma unroll
+      for (int hh = 0; hh < kMaxGroup; ++hh) {
+        if (hh < G) {
+          const size_t bh = bh0 + hh;
+          const float wz = p.dzsel[(bh * p.nq + t) * p.K + kk];
+          const float* qr = qt + (bh * p.nq + t) * D;
+#pragma unroll
+          for (int u = 0; u < PL; ++u) acc[hh][u] += wz * qr[lane + 64 * u];
+          hs[hh] += wz;
+        }
+      }
     }
-    float* dsr = ds + (bh * p.N + c) * D;
+  }
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) dsr[lane + 64 * u] = p.scale * acc[u];
-    if (lane == 0) dH[bh * p.N + c] = -beta * hs;
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    if (hh < G) {
+#pragma unroll
+      for (int u = 0; u < PL; ++u) red[w][hh][lane + 64 * u] = acc[hh][u];
+      if (lane == 0) red[w][hh][D] = hs[hh];
+    }
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < G * (D + 1); x += 256) {
+    const int hh = x / (D + 1), e = x % (D + 1);
+    const float v = ((red[0][hh][e] + red[1][hh][e]) + red[2][hh][e]) + red[3][hh][e];
+    const size_t bh = bh0 + hh;
+    if (e < D) ds[(bh * p.N + c) * D + e] = p.scale * v;
+    else dH[bh * p.N + c] = -beta * v;
   }
 }
 
@@ -725,20 +761,23 @@ __global__ __launch_bounds__(256) void sbwd_usum_kernel(const float* __restrict_
   }
 }
 
-// dU[b,t,j] = sum_h sum_e dq~[b,h,t,e] Bm[j][h*D + e]: 16 rows x RP columns per block,
-// Bm staged 64 columns of one head at a time
+// dU[b,t,j] = sum_h sum_e dq~[b,h,t,e] Bm[j][h*D + e]: 64 rows x RP columns per block,
+// 64 columns of one head staged at a time; thread (ty, tx) owns rows 4 ty .. 4 ty + 3 and
+// columns tx + 16 m.
 template <typename T, int D, int RP>
 __global__ __launch_bounds__(256) void sbwd_du_kernel(const float* __restrict__ dqt, const T* __restrict__ Bm, int r,
                                                       float* __restrict__ dU, int Hq, int nq) {
-  constexpr int EC = 64;
+  constexpr int EC = 64, TR = 64, NM = RP / 16;
   __shared__ float bs[RP * (EC + 1)];
-  __shared__ float qs[16 * EC];
+  __shared__ float qs[TR * (EC + 1)];
   const int tid = threadIdx.x, b = blockIdx.y;
-  const int tl = tid >> 4, jg = tid & 15;
-  const int t0 = blockIdx.x * 16;
-  float acc[RP / 16];
+  const int ty = tid >> 4, tx = tid & 15;
+  const int t0 = blockIdx.x * TR;
+  float acc[4][NM];
 #pragma unroll
-  for (int m = 0; m < RP / 16; ++m) acc[m] = 0.f;
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[i][m] = 0.f;
   for (int h = 0; h < Hq; ++h)
     for (int e0 = 0; e0 < D; e0 += EC) {
       __syncthreads();
@@ -746,32 +785,42 @@ __global__ __launch_bounds__(256) void sbwd_du_kernel(const float* __restrict__ 
         const int j = x / EC, e = x % EC;
         bs[j * (EC + 1) + e] = j < r ? Elem<T>::to_f(Bm[(size_t)j * Hq * D + (size_t)h * D + e0 + e]) : 0.f;
       }
-      for (int x = tid; x < 16 * EC; x += 256) {
+      for (int x = tid; x < TR * EC; x += 256) {
         const int tt = t0 + x / EC;
-        qs[x] = tt < nq ? dqt[(((size_t)b * Hq + h) * nq + tt) * D + e0 + x % EC] : 0.f;
+        qs[(x / EC) * (EC + 1) + x % EC] = tt < nq ? dqt[(((size_t)b * Hq + h) * nq + tt) * D + e0 + x % EC] : 0.f;
       }
       __syncthreads();
       for (int e = 0; e < EC; ++e) {
-        const float a = qs[tl * EC + e];
+        float a[4], bb[NM];
 #pragma unroll
-        for (int m = 0; m < RP / 16; ++m) acc[m] += a * bs[(jg + 16 * m) * (EC + 1) + e];
+        for (int i = 0; i < 4; ++i) a[i] = qs[(4 * ty + i) * (EC + 1) + e];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) bb[m] = bs[(tx + 16 * m) * (EC + 1) + e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) acc[i][m] += a[i] * bb[m];
       }
     }
-  const int t = t0 + tl;
-  if (t < nq) {
 #pragma unroll
-    for (int m = 0; m < RP / 16; ++m) dU[((size_t)b * nq + t) * RP + jg + 16 * m] = acc[m];
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * ty + i;
+    if (t < nq) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) dU[((size_t)b * nq + t) * RP + tx + 16 * m] = acc[i][m];
+    }
   }
 }
 
-// dx[b, slot(q0+t), m] = sum_j dU[b,t,j] A[m][j]: 16 rows x 256 hidden columns per block
+// dx[b, slot(q0+t), m] = sum_j dU[b,t,j] A[m][j]: 64 rows x 256 hidden columns per block
 template <typename T, int RP>
 __global__ __launch_bounds__(256) void sbwd_dx_kernel(const float* __restrict__ dU, const T* __restrict__ A, int Dh,
                                                       int r, float* __restrict__ dx, int N, int q0, int nq) {
-  __shared__ float us[16 * RP];
+  constexpr int TR = 64;
+  __shared__ float us[TR * RP];
   const int tid = threadIdx.x, b = blockIdx.z;
-  const int t0 = blockIdx.x * 16, m = blockIdx.y * 256 + tid;
-  for (int x = tid; x < 16 * RP; x += 256) {
+  const int t0 = blockIdx.x * TR, m = blockIdx.y * 256 + tid;
+  for (int x = tid; x < TR * RP; x += 256) {
     const int tt = t0 + x / RP;
     us[x] = tt < nq ? dU[((size_t)b * nq + tt) * RP + x % RP] : 0.f;
   }
@@ -781,7 +830,7 @@ __global__ __launch_bounds__(256) void sbwd_dx_kernel(const float* __restrict__ 
 #pragma unroll
   for (int j = 0; j < RP; ++j) a[j] = j < r ? Elem<T>::to_f(A[(size_t)m * r + j]) : 0.f;
   const size_t L = (size_t)N * kSlots;
-  for (int tl = 0; tl < 16; ++tl) {
+  for (int tl = 0; tl < TR; ++tl) {
     const int t = t0 + tl;
     if (t >= nq) break;
     float acc = 0.f;
@@ -972,9 +1021,9 @@ static hipError_t launch_score_bwd_t(const RouteDims& dm, const void* x, const v
     const size_t nu = (size_t)rows * RP;
     hipLaunchKernelGGL(sbwd_usum_kernel, dim3((unsigned)std::min<size_t>((nu + 255) / 256, 65535)), dim3(256), 0,
                        st, (const float*)w.upart, w.nsplit, nu, w.U);
-    hipLaunchKernelGGL((sbwd_du_kernel<T, D, RP>), dim3((nq + 15) / 16, dm.B), dim3(256), 0, st,
+    hipLaunchKernelGGL((sbwd_du_kernel<T, D, RP>), dim3((nq + 63) / 64, dm.B), dim3(256), 0, st,
                        (const float*)w.dqt, (const T*)Bm, r, w.dU, dm.Hq, nq);
-    hipLaunchKernelGGL((sbwd_dx_kernel<T, RP>), dim3((nq + 15) / 16, (Dh + 255) / 256, dm.B), dim3(256), 0, st,
+    hipLaunchKernelGGL((sbwd_dx_kernel<T, RP>), dim3((nq + 63) / 64, (Dh + 255) / 256, dm.B), dim3(256), 0, st,
                        (const float*)w.dU, (const T*)A, Dh, r, dx, dm.N, q0, nq);
   }
   const int HD = dm.Hq * D;
