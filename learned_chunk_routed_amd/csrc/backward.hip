@@ -30,7 +30,7 @@
 //     entries that selected it, in ascending query order (per-tile counts,
 //     a scan over chunks and tiles, placement row by row).
 //  3. bwd_key_kernel: one block per (batch, KV group, chunk), wave w owning keys
-//     16w .. 16w+15. Rows (query, head) are staged 32 at a time in LDS: first
+//     16w .. 16w+15. Rows (query, head) are staged 64 at a time in LDS: first
 //     the queries whose window reaches the chunk, then the chunk's entries from
 //     the inverse index. Per step S = Q K^T and dP = dO V^T (K, V fragments in
 //     registers), then dV += P^T dO and dK += dS^T Q with P and dS straight from
@@ -277,6 +277,7 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(int* a, size_t n) {
 // scheduling, so dk and dv are reproducible bit for bit.
 constexpr int kIdxTile = 256;
 constexpr int kMaxGroup = 8;   // largest GQA group (query heads per KV head)
+constexpr int kKeyRows = 64;   // (query, head) rows the key-side kernel stages per step
 
 __global__ __launch_bounds__(256) void bwd_hist_kernel(BwdParams p) {
   extern __shared__ int hist[];   // [N]
@@ -360,13 +361,15 @@ __global__ __launch_bounds__(64) void bwd_fill_kernel(BwdParams p) {
 // ---------------------------------------------------------------- 3. key side
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_key_kernel(BwdParams p) {
   constexpr int LDR = D + 8;
-  constexpr int PPT = D / 64;   // 16-byte pieces per thread per staged tensor (32 rows x D/8 pieces / 256)
-  __shared__ __align__(16) bf16_t qs[32 * LDR];
-  __shared__ __align__(16) bf16_t dos[32 * LDR];
-  __shared__ float sbias[32], ssub[32];
-  __shared__ int squery[32];
+  constexpr int RS = kKeyRows;   // rows staged per step
+  constexpr int TPR = 256 / RS;  // staging threads per row
+  constexpr int PPT = D / 8 / TPR;   // 16-byte pieces per thread per staged tensor
+  __shared__ __align__(16) bf16_t qs[RS * LDR];
+  __shared__ __align__(16) bf16_t dos[RS * LDR];
+  __shared__ float sbias[RS], ssub[RS];
+  __shared__ int squery[RS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int L16 = lane & 15, g16 = lane >> 4;
   const int c = blockIdx.x % p.N, bg = blockIdx.x / p.N, b = bg / p.Hkv, g = bg % p.Hkv;
@@ -404,25 +407,30 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
   const size_t per = (size_t)p.nq * p.K;
   const int* lst = p.list + (size_t)bg * per + p.off[(size_t)bg * (p.N + 1) + c];
 
-  // staging role of this thread: row sr of the 32, pieces sp*PPT .. +PPT-1 of D/8
-  const int sr = tid >> 3, sp = tid & 7;
+  // staging role of this thread: row sr of the RS, pieces sp*PPT .. +PPT-1 of D/8
+  const int sr = tid / TPR, sp = tid % TPR;
 
   for (int pass = 0; pass < 2; ++pass) {
     const int nrows = (pass == 0 ? nwq : ncnt) * p.G;
-    const int nsteps = (nrows + 31) / 32;
+    const int nsteps = (nrows + RS - 1) / RS;
     s16x8 rq[PPT], rd[PPT];
     float rb = -INFINITY, ru = 0.f;
     int rqi = INT_MIN / 2;
-    auto fetch = [&](int step) {
-      const int r = step * 32 + sr;
+    // entry word of this thread's row in a step (pass 1), read two steps ahead of its use
+    auto entry = [&](int step) -> int {
+      const int r = step * RS + sr;
+      if (pass == 0 || r >= nrows) return 0;
+      return lst[r / p.G];
+    };
+    auto fetch = [&](int step, int ent) {
+      const int r = step * RS + sr;
       const int e = r / p.G, h = r % p.G;
-      bool ok = r < nrows;
+      const bool ok = r < nrows;
       int t = 0, slotk = 0;
       if (ok) {
         if (pass == 0) {
           t = iw_lo + e - p.q0;
         } else {
-          const int ent = lst[e];
           t = ent / p.K;
           slotk = ent % p.K;
         }
@@ -436,12 +444,15 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
         rd[u] = ok ? load8(p.dO + base + (sp * PPT + u) * 8) : zero8();
       }
       if (sp == 0) {
+        // bias: lse (pass 0, used negated) or the chunk bias (pass 1); rows past the end
+        // get a bias that makes their probability exactly 0. Loaded values are stored as
+        // they are, so no wait on them is needed before the next step.
         if (!ok) {
-          rb = -INFINITY;
+          rb = pass == 0 ? INFINITY : -INFINITY;
           ru = 0.f;
           rqi = INT_MIN / 2;
         } else if (pass == 0) {
-          rb = -p.lse[rowq];
+          rb = p.lse[rowq];
           ru = p.dsum[rowq];
           rqi = p.q0 + t;
         } else {
@@ -451,7 +462,11 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
         }
       }
     };
-    if (nsteps > 0) fetch(0);
+    int ent_next = 0;
+    if (nsteps > 0) {
+      fetch(0, entry(0));
+      ent_next = entry(1);
+    }
     for (int step = 0; step < nsteps; ++step) {
       __syncthreads();   // the previous step's readers are done with qs / dos
 #pragma unroll
@@ -465,12 +480,16 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
         squery[sr] = rqi;
       }
       __syncthreads();
-      if (step + 1 < nsteps) fetch(step + 1);
+      if (step + 1 < nsteps) {
+        fetch(step + 1, ent_next);
+        ent_next = entry(step + 2);
+      }
 
       // S = Q K^T, dP = dO V^T: rows 16 mt + 4 g16 + e, key column L16 of this wave
-      f32x4 sacc[2], pacc[2];
+      constexpr int MT = RS / 16;
+      f32x4 sacc[MT], pacc[MT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         sacc[mt] = zero4();
         pacc[mt] = zero4();
 #pragma unroll
@@ -481,31 +500,36 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdParams p) {
           pacc[mt] = mfma16(ad, vf[ks], pacc[mt]);
         }
       }
-      float pv[2][4], dsv[2][4];
+      float pv[MT][4], dsv[MT][4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * mt + 4 * g16 + e;
           bool ok = key < kContent;
           if (pass == 0) ok = ok && abs(u_key - squery[r]) <= p.R;
-          const float pr = ok ? __expf(sc * sacc[mt][e] + sbias[r]) : 0.f;
+          const float bias = pass == 0 ? -sbias[r] : sbias[r];
+          const float pr = ok ? __expf(sc * sacc[mt][e] + bias) : 0.f;
           pv[mt][e] = pr;
           dsv[mt][e] = pr * (pacc[mt][e] - ssub[r]);
         }
-      s16x8 pa, da;
+      // dV += P^T dO, dK += dS^T Q: M = this wave's 16 keys, k = the RS rows in 32-row
+      // steps (rows 32 kq + 4 g16 + j and 32 kq + 16 + 4 g16 + j, as the S output holds them)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pa[j] = (short)f2bf(j < 4 ? pv[0][j] : pv[1][j - 4]);
-        da[j] = (short)f2bf(j < 4 ? dsv[0][j] : dsv[1][j - 4]);
-      }
-      // dV += P^T dO, dK += dS^T Q: M = this wave's 16 keys, k = the 32 rows (same permutation)
+      for (int kq = 0; kq < RS / 32; ++kq) {
+        s16x8 pa, da;
 #pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) {
-        const s16x8 bo = lds_col_frag(dos, LDR, 4 * g16, 16 + 4 * g16, 16 * nt, lane);
-        dva[nt] = mfma16(pa, bo, dva[nt]);
-        const s16x8 bq = lds_col_frag(qs, LDR, 4 * g16, 16 + 4 * g16, 16 * nt, lane);
-        dka[nt] = mfma16(da, bq, dka[nt]);
+        for (int j = 0; j < 8; ++j) {
+          pa[j] = (short)f2bf(j < 4 ? pv[2 * kq][j] : pv[2 * kq + 1][j - 4]);
+          da[j] = (short)f2bf(j < 4 ? dsv[2 * kq][j] : dsv[2 * kq + 1][j - 4]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) {
+          const s16x8 bo = lds_col_frag(dos, LDR, 32 * kq + 4 * g16, 32 * kq + 16 + 4 * g16, 16 * nt, lane);
+          dva[nt] = mfma16(pa, bo, dva[nt]);
+          const s16x8 bq = lds_col_frag(qs, LDR, 32 * kq + 4 * g16, 32 * kq + 16 + 4 * g16, 16 * nt, lane);
+          dka[nt] = mfma16(da, bq, dka[nt]);
+        }
       }
     }
   }
@@ -651,8 +675,9 @@ size_t routed_bwd_lds_bytes(int d) { return (size_t)4 * 64 * (d + 8) * 2; }
 //   ds[b,h,c]  = scale sum over entries (t,k) of c of dzsel q~[b,h,t]
 //   dH[b,h,c]  = -beta sum over the same entries of dzsel
 //   dU = dq~ B^T (per row, over all heads), dB = U^T dq~, dA = x^T dU, dx = dU A^T
-// All in float32. The sums over rows for dA and dB are split into fixed row ranges
-// whose partials are added in order (no atomics).
+// All in float32 (ds as split-bf16 MFMA products, near float32). The sums over rows
+// for ds, dA and dB are split into fixed row ranges whose partials are added in order
+// (no atomics).
 
 template <int D>
 __global__ __launch_bounds__(256) void sbwd_dqt_kernel(const int32_t* __restrict__ idx, const float* __restrict__ dzsel,
@@ -692,62 +717,106 @@ __global__ __launch_bounds__(256) void sbwd_dqt_kernel(const int32_t* __restrict
   }
 }
 
-// ds, dH of one chunk: wave w takes entries w, w+4, ... of the chunk's list for all G
-// heads of the group (lanes over d); the four waves' sums are added in LDS in wave
-// order. Entry words are read 64 at a time, one per lane, and broadcast.
+// ds and dH as a dense product: ds[b,h,c,:] = sum_t Z[t][c] q~[b,h,t,:] with Z the chosen
+// chunk logits' gradients scattered on a [32 rows x 64 chunks] LDS tile per step (zero where
+// row t did not choose c). One block per (64 chunks, batch and head, row range); q~ is read
+// once per block. Products in split bf16 (hi and lo planes, three MFMAs: near float32);
+// dH takes the tile's column sums in row order. Each row range writes a partial; the
+// partials are added in range order.
+constexpr int kDsC = 64, kDsT = 32, kDsSplit = 8;
+
 template <int D>
-__global__ __launch_bounds__(256) void sbwd_ds_kernel(BwdParams p, const float* __restrict__ qt, float* __restrict__ ds,
-                                                      float* __restrict__ dH, float beta) {
-  constexpr int PL = D / 64;
-  __shared__ float red[4][kMaxGroup][D + 1];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c = blockIdx.x % p.N, bg = blockIdx.x / p.N, b = bg / p.Hkv, g = bg % p.Hkv;
-  const int G = p.G;
-  const int ncnt = p.cnt[(size_t)bg * p.N + c];
-  const int* lst = p.list + (size_t)bg * p.nq * p.K + p.off[(size_t)bg * (p.N + 1) + c];
-  const size_t bh0 = (size_t)b * p.Hq + (size_t)g * G;
-  float acc[kMaxGroup][PL], hs[kMaxGroup];
+__global__ __launch_bounds__(256) void sbwd_ds_dense_kernel(const int32_t* __restrict__ idx,
+                                                            const float* __restrict__ dzsel,
+                                                            const float* __restrict__ qt, float* __restrict__ dspart,
+                                                            float* __restrict__ dhpart, int BHq, int Hq, int Hkv,
+                                                            int N, int K, int nq, int rows_per) {
+  constexpr int ZS = kDsT + 8, QS = D + 16, FS = kDsT + 1;
+  __shared__ __align__(16) bf16_t zt[2][kDsC * ZS];
+  __shared__ __align__(16) bf16_t qp[2][kDsT * QS];
+  __shared__ float zf[kDsC * FS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, L16 = lane & 15, g16 = lane >> 4;
+  const int c0 = blockIdx.x * kDsC, bh = blockIdx.y, sp = blockIdx.z;
+  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+  const int tbeg = sp * rows_per, tend = min(nq, tbeg + rows_per);
+  f32x4 acc[D / 16];
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    hs[hh] = 0.f;
-#pragma unroll
-    for (int u = 0; u < PL; ++u) acc[hh][u] = 0.f;
-  }
-  for (int e0 = 0; e0 < ncnt; e0 += 256) {
-    const int mine = e0 + 4 * lane + w;           // this lane's entry word for the wave
-    const int ent = mine < ncnt ? lst[mine] : -1;
-    const int n = min(64, (ncnt - e0 - w + 3) / 4);
-    for (int i = 0; i < n; ++i) {
-      const int en = __shfl(ent, i);
-      const int t = en / p.K, kk = en % p.K;
-#pragma unroll
-      for (int hh = 0; hh < kMaxGroup; ++hh) {
-        if (hh < G) {
-          const size_t bh = bh0 + hh;
-          const float wz = p.dzsel[(bh * p.nq + t) * p.K + kk];
-          const float* qr = qt + (bh * p.nq + t) * D;
-#pragma unroll
-          for (int u = 0; u < PL; ++u) acc[hh][u] += wz * qr[lane + 64 * u];
-          hs[hh] += wz;
-        }
+  for (int nt = 0; nt < D / 16; ++nt) acc[nt] = zero4();
+  float hs = 0.f;
+  for (int t0 = tbeg; t0 < tend; t0 += kDsT) {
+    __syncthreads();
+    for (int x = tid; x < kDsC * FS; x += 256) zf[x] = 0.f;
+    __syncthreads();
+    for (int x = tid; x < kDsT * K; x += 256) {
+      const int tl = x / K, k = x % K, row = t0 + tl;
+      if (row < tend) {
+        const int c = idx[(((size_t)b * Hkv + g) * nq + row) * K + k] - c0;
+        if (c >= 0 && c < kDsC) zf[c * FS + tl] = dzsel[((size_t)bh * nq + row) * K + k];
       }
     }
-  }
+    for (int x = tid; x < kDsT * D / 4; x += 256) {
+      const int tl = x / (D / 4), e = 4 * (x % (D / 4)), row = t0 + tl;
+      f32x4 v = zero4();
+      if (row < tend) v = *reinterpret_cast<const f32x4*>(qt + ((size_t)bh * nq + row) * D + e);
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    if (hh < G) {
+      for (int j = 0; j < 4; ++j) {
+        bf16_t hi, lo;
+        split_bf16(v[j], hi, lo);
+        qp[0][tl * QS + e + j] = hi;
+        qp[1][tl * QS + e + j] = lo;
+      }
+    }
+    __syncthreads();
+    for (int x = tid; x < kDsC * kDsT; x += 256) {
+      const int c = x / kDsT, tl = x % kDsT;
+      bf16_t hi, lo;
+      split_bf16(zf[c * FS + tl], hi, lo);
+      zt[0][c * ZS + tl] = hi;
+      zt[1][c * ZS + tl] = lo;
+    }
+    if (tid < kDsC) {
+      float cs = 0.f;
+      for (int tl = 0; tl < kDsT; ++tl) cs += zf[tid * FS + tl];
+      hs += cs;
+    }
+    __syncthreads();
+    // wave w: chunks 16 w .. 16 w + 15 (M) x all of d (N), k = the 32 rows
+    const s16x8 ah = load8(zt[0] + (16 * w + L16) * ZS + 8 * g16);
+    const s16x8 al = load8(zt[1] + (16 * w + L16) * ZS + 8 * g16);
 #pragma unroll
-      for (int u = 0; u < PL; ++u) red[w][hh][lane + 64 * u] = acc[hh][u];
-      if (lane == 0) red[w][hh][D] = hs[hh];
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const s16x8 bhi = lds_col_frag(qp[0], QS, 8 * g16, 8 * g16 + 4, 16 * nt, lane);
+      const s16x8 blo = lds_col_frag(qp[1], QS, 8 * g16, 8 * g16 + 4, 16 * nt, lane);
+      acc[nt] = mfma16(ah, blo, acc[nt]);
+      acc[nt] = mfma16(al, bhi, acc[nt]);
+      acc[nt] = mfma16(ah, bhi, acc[nt]);
     }
   }
-  __syncthreads();
-  for (int x = threadIdx.x; x < G * (D + 1); x += 256) {
-    const int hh = x / (D + 1), e = x % (D + 1);
-    const float v = ((red[0][hh][e] + red[1][hh][e]) + red[2][hh][e]) + red[3][hh][e];
-    const size_t bh = bh0 + hh;
-    if (e < D) ds[(bh * p.N + c) * D + e] = p.scale * v;
-    else dH[bh * p.N + c] = -beta * v;
+  float* dst = dspart + ((size_t)sp * BHq + bh) * N * D;
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + 16 * w + 4 * g16 + i;
+      if (c < N) dst[(size_t)c * D + 16 * nt + L16] = acc[nt][i];
+    }
+  if (tid < kDsC && c0 + tid < N) dhpart[((size_t)sp * BHq + bh) * N + c0 + tid] = hs;
+}
+
+__global__ __launch_bounds__(256) void sbwd_ds_reduce_kernel(const float* __restrict__ dspart,
+                                                             const float* __restrict__ dhpart, float* __restrict__ ds,
+                                                             float* __restrict__ dH, size_t nds, size_t ndh, float scale,
+                                                             float beta) {
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < nds + ndh; x += (size_t)gridDim.x * 256) {
+    float a = 0.f;
+    if (x < nds) {
+      for (int sp = 0; sp < kDsSplit; ++sp) a += dspart[(size_t)sp * nds + x];
+      ds[x] = scale * a;
+    } else {
+      const size_t y = x - nds;
+      for (int sp = 0; sp < kDsSplit; ++sp) a += dhpart[(size_t)sp * ndh + y];
+      dH[y] = -beta * a;
+    }
   }
 }
 
@@ -929,8 +998,7 @@ __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const float* __restric
 }
 
 struct ScoreBwdWs {
-  float *qt, *upart, *U, *dqt, *dU, *pa, *pb;
-  int *cnt, *off, *th, *list;
+  float *qt, *upart, *U, *dqt, *dU, *pa, *pb, *dsp, *dhp;
   int nsplit, RP, nsp, rows_per;
 };
 
@@ -953,19 +1021,23 @@ static ScoreBwdWs sbwd_carve(void* ws, const RouteDims& dm, int Dh, int r, int K
   o.dU = (float*)take((size_t)rows * o.RP * 4);
   o.pa = (float*)take((size_t)o.nsp * Dh * o.RP * 4);
   o.pb = (float*)take((size_t)o.nsp * o.RP * dm.Hq * dm.d * 4);
-  o.cnt = (int*)take(bg * dm.N * 4);
-  o.off = (int*)take(bg * (dm.N + 1) * 4);
-  o.th = (int*)take(bg * bwd_ntile(nq) * dm.N * 4);
-  o.list = (int*)take(bg * nq * K * 4);
+  const size_t bhq = (size_t)dm.B * dm.Hq;
+  o.dsp = (float*)take((size_t)kDsSplit * bhq * dm.N * dm.d * 4);
+  o.dhp = (float*)take((size_t)kDsSplit * bhq * dm.N * 4);
+  (void)bg;
+  (void)K;
   return o;
 }
 
 size_t score_bwd_ws_bytes(const RouteDims& dm, int Dh, int r, int K, int nq) {
   const int nsplit = qtilde_u_splits(dm, Dh, nq), RP = qtilde_rank_pad(r), rows = dm.B * nq, nsp = sbwd_nsp(rows);
   const size_t rh = (size_t)dm.B * dm.Hq * nq, bg = (size_t)dm.B * dm.Hkv;
+  const size_t bhq = (size_t)dm.B * dm.Hq;
+  (void)bg;
+  (void)K;
   return 2 * al256(rh * dm.d * 4) + al256((size_t)nsplit * rows * RP * 4) + 2 * al256((size_t)rows * RP * 4) +
-         al256((size_t)nsp * Dh * RP * 4) + al256((size_t)nsp * RP * dm.Hq * dm.d * 4) + al256(bg * dm.N * 4) +
-         al256(bg * (dm.N + 1) * 4) + al256(bg * bwd_ntile(nq) * dm.N * 4) + al256(bg * nq * K * 4);
+         al256((size_t)nsp * Dh * RP * 4) + al256((size_t)nsp * RP * dm.Hq * dm.d * 4) +
+         al256((size_t)kDsSplit * bhq * dm.N * dm.d * 4) + al256((size_t)kDsSplit * bhq * dm.N * 4);
 }
 
 template <typename T, int D, int RP>
@@ -974,49 +1046,19 @@ static hipError_t launch_score_bwd_t(const RouteDims& dm, const void* x, const v
                                      const int32_t* idx, const float* dzsel, float* dq, float* dx, float* dA,
                                      float* dBm, float* ds, float* dH, const ScoreBwdWs& w, hipStream_t st) {
   const int rows = dm.B * nq;
-  // inverse index of the selections (as the attention backward builds it)
-  BwdParams ip;
-  ip.idx = idx;
-  ip.zsel = nullptr;
-  ip.dzsel = const_cast<float*>(dzsel);
-  ip.cnt = w.cnt;
-  ip.off = w.off;
-  ip.th = w.th;
-  ip.list = w.list;
-  ip.B = dm.B;
-  ip.Hq = dm.Hq;
-  ip.Hkv = dm.Hkv;
-  ip.N = dm.N;
-  ip.G = dm.Hq / dm.Hkv;
-  ip.K = K;
-  ip.q0 = q0;
-  ip.nq = nq;
-  ip.scale = scale;
-  const size_t bgn = (size_t)dm.B * dm.Hkv * dm.N;
-  const int ntile = bwd_ntile(nq);
-  const size_t idx_lds = (size_t)dm.N * 4;
-  hipError_t e = hipFuncSetAttribute((const void*)bwd_hist_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)idx_lds);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)bwd_fill_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)idx_lds);
-  if (e != hipSuccess) return e;
-  if (nq > 0 && K > 0) {
-    hipLaunchKernelGGL(bwd_hist_kernel, dim3(ntile, dm.B * dm.Hkv), dim3(256), idx_lds, st, ip);
-    hipLaunchKernelGGL(bwd_scan_kernel, dim3(dm.B * dm.Hkv), dim3(256), 0, st, ip, ntile);
-    hipLaunchKernelGGL(bwd_fill_kernel, dim3(ntile, dm.B * dm.Hkv), dim3(64), idx_lds, st, ip);
-  } else {
-    const size_t no = (size_t)dm.B * dm.Hkv * (dm.N + 1);
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)std::min<size_t>((bgn + 255) / 256, 65535)), dim3(256), 0,
-                       st, w.cnt, bgn);
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)std::min<size_t>((no + 255) / 256, 65535)), dim3(256), 0,
-                       st, w.off, no);
-  }
   if (nq > 0) {
     hipLaunchKernelGGL((sbwd_dqt_kernel<D>), dim3((nq + 3) / 4, dm.B * dm.Hq), dim3(256), 0, st, idx, dzsel, s,
                        w.dqt, dq, scale, dm.Hq, dm.Hkv, dm.N, K, q0, nq);
   }
-  hipLaunchKernelGGL((sbwd_ds_kernel<D>), dim3((unsigned)bgn), dim3(256), 0, st, ip, (const float*)w.qt, ds, dH,
-                     beta);
+  {
+    const int bhq = dm.B * dm.Hq;
+    const int rows_per = ((nq + kDsSplit - 1) / kDsSplit + kDsT - 1) / kDsT * kDsT;
+    hipLaunchKernelGGL((sbwd_ds_dense_kernel<D>), dim3((dm.N + kDsC - 1) / kDsC, bhq, kDsSplit), dim3(256), 0, st,
+                       idx, dzsel, (const float*)w.qt, w.dsp, w.dhp, bhq, dm.Hq, dm.Hkv, dm.N, K, nq, rows_per);
+    const size_t nds = (size_t)bhq * dm.N * D, ndh = (size_t)bhq * dm.N;
+    hipLaunchKernelGGL(sbwd_ds_reduce_kernel, dim3((unsigned)std::min<size_t>((nds + ndh + 255) / 256, 65535)),
+                       dim3(256), 0, st, (const float*)w.dsp, (const float*)w.dhp, ds, dH, nds, ndh, scale, beta);
+  }
   if (nq > 0) {
     const size_t nu = (size_t)rows * RP;
     hipLaunchKernelGGL(sbwd_usum_kernel, dim3((unsigned)std::min<size_t>((nu + 255) / 256, 65535)), dim3(256), 0,
