@@ -830,55 +830,61 @@ __global__ __launch_bounds__(256) void sbwd_usum_kernel(const float* __restrict_
   }
 }
 
-// dU[b,t,j] = sum_h sum_e dq~[b,h,t,e] Bm[j][h*D + e]: 64 rows x RP columns per block,
-// 64 columns of one head staged at a time; thread (ty, tx) owns rows 4 ty .. 4 ty + 3 and
-// columns tx + 16 m.
+// Eight consecutive values of a row as split-bf16 MFMA operands (hi + lo); `n` of them valid.
+template <typename T>
+__device__ __forceinline__ void load8_split(const T* p, int n, s16x8& hi, s16x8& lo) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = j < n ? Elem<T>::to_f(p[j]) : 0.f;
+  pack8_split(v, hi, lo);
+}
+
+// dU[b,t,j] = sum_h sum_e dq~[b,h,t,e] Bm[j][h*D + e] on MFMA: one wave per 16 rows x RP
+// columns, k over (head, e) in steps of 32. A = dq~ rows split into bf16 hi + lo; B = Bm
+// rows (bf16 inputs: exact, two products; float32 inputs: split, three products).
 template <typename T, int D, int RP>
 __global__ __launch_bounds__(256) void sbwd_du_kernel(const float* __restrict__ dqt, const T* __restrict__ Bm, int r,
-                                                      float* __restrict__ dU, int Hq, int nq) {
-  constexpr int EC = 64, TR = 64, NM = RP / 16;
-  __shared__ float bs[RP * (EC + 1)];
-  __shared__ float qs[TR * (EC + 1)];
-  const int tid = threadIdx.x, b = blockIdx.y;
-  const int ty = tid >> 4, tx = tid & 15;
-  const int t0 = blockIdx.x * TR;
-  float acc[4][NM];
+                                                      float* __restrict__ dU, int Hq, int nq, int ntiles) {
+  const int lane = threadIdx.x & 63, L16 = lane & 15, g16 = lane >> 4;
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= ntiles) return;
+  const int ntb = (nq + 15) / 16, b = tile / ntb, t0 = (tile % ntb) * 16;
+  const int t = min(t0 + L16, nq - 1);
+  const bool tv = t0 + L16 < nq;
+  f32x4 acc[RP / 16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int nt = 0; nt < RP / 16; ++nt) acc[nt] = zero4();
+  for (int h = 0; h < Hq; ++h) {
+    const float* arow = dqt + (((size_t)b * Hq + h) * nq + t) * D;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) acc[i][m] = 0.f;
-  for (int h = 0; h < Hq; ++h)
-    for (int e0 = 0; e0 < D; e0 += EC) {
-      __syncthreads();
-      for (int x = tid; x < RP * EC; x += 256) {
-        const int j = x / EC, e = x % EC;
-        bs[j * (EC + 1) + e] = j < r ? Elem<T>::to_f(Bm[(size_t)j * Hq * D + (size_t)h * D + e0 + e]) : 0.f;
+    for (int ks = 0; ks < D / 32; ++ks) {
+      s16x8 ah, al;
+      load8_split<float>(arow + 32 * ks + 8 * g16, tv ? 8 : 0, ah, al);
+#pragma unroll
+      for (int nt = 0; nt < RP / 16; ++nt) {
+        const int j = 16 * nt + L16;
+        const T* brow = Bm + (size_t)min(j, r - 1) * Hq * D + (size_t)h * D + 32 * ks + 8 * g16;
+        if constexpr (sizeof(T) == 2) {
+          const s16x8 bv = j < r ? load8(brow) : zero8();
+          acc[nt] = mfma16(ah, bv, acc[nt]);
+          acc[nt] = mfma16(al, bv, acc[nt]);
+        } else {
+          s16x8 bh, bl;
+          load8_split<T>(brow, j < r ? 8 : 0, bh, bl);
+          acc[nt] = mfma16(ah, bl, acc[nt]);
+          acc[nt] = mfma16(al, bh, acc[nt]);
+          acc[nt] = mfma16(ah, bh, acc[nt]);
+        }
       }
-      for (int x = tid; x < TR * EC; x += 256) {
-        const int tt = t0 + x / EC;
-        qs[(x / EC) * (EC + 1) + x % EC] = tt < nq ? dqt[(((size_t)b * Hq + h) * nq + tt) * D + e0 + x % EC] : 0.f;
-      }
-      __syncthreads();
-      for (int e = 0; e < EC; ++e) {
-        float a[4], bb[NM];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = qs[(4 * ty + i) * (EC + 1) + e];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) bb[m] = bs[(tx + 16 * m) * (EC + 1) + e];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int m = 0; m < NM; ++m) acc[i][m] += a[i] * bb[m];
-      }
-    }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 4 * ty + i;
-    if (t < nq) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m) dU[((size_t)b * nq + t) * RP + tx + 16 * m] = acc[i][m];
     }
   }
+#pragma unroll
+  for (int nt = 0; nt < RP / 16; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = t0 + 4 * g16 + i;
+      if (row < nq) dU[((size_t)b * nq + row) * RP + 16 * nt + L16] = acc[nt][i];
+    }
 }
 
 // dx[b, slot(q0+t), m] = sum_j dU[b,t,j] A[m][j]: 64 rows x 256 hidden columns per block
@@ -1063,8 +1069,9 @@ static hipError_t launch_score_bwd_t(const RouteDims& dm, const void* x, const v
     const size_t nu = (size_t)rows * RP;
     hipLaunchKernelGGL(sbwd_usum_kernel, dim3((unsigned)std::min<size_t>((nu + 255) / 256, 65535)), dim3(256), 0,
                        st, (const float*)w.upart, w.nsplit, nu, w.U);
-    hipLaunchKernelGGL((sbwd_du_kernel<T, D, RP>), dim3((nq + 63) / 64, dm.B), dim3(256), 0, st,
-                       (const float*)w.dqt, (const T*)Bm, r, w.dU, dm.Hq, nq);
+    const int ntu = dm.B * ((nq + 15) / 16);
+    hipLaunchKernelGGL((sbwd_du_kernel<T, D, RP>), dim3((ntu + 3) / 4), dim3(256), 0, st, (const float*)w.dqt,
+                       (const T*)Bm, r, w.dU, dm.Hq, nq, ntu);
     hipLaunchKernelGGL((sbwd_dx_kernel<T, RP>), dim3((nq + 63) / 64, (Dh + 255) / 256, dm.B), dim3(256), 0, st,
                        (const float*)w.dU, (const T*)A, Dh, r, dx, dm.N, q0, nq);
   }
