@@ -1286,6 +1286,442 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   }
 }
 
+// ---------------------------------------------------------------- routed attention backward, query side
+// The forward's producer / consumer pool with a backward consumer: the block's 14
+// queries (7 consumer waves, one 16-column tile each) share one ascending stream of
+// the chunks any of them needs, so each chunk's K and V are fetched once per block.
+// Per visit a consumer forms S^T = K Q^T and dP^T = V dO^T, the intra-chunk softmax
+// statistics, ds, and dQ^T += K^T dS^T (K^T by transposing reads of the K half, which
+// it holds until then). It writes dq, dzsel, D = dO . o and, per (row, selected chunk),
+// the probability bias and U_c that the key-side kernel needs.
+constexpr int kBqCons = 11;
+constexpr int kBqWaves = kBqCons + 1;
+constexpr int kBqQB = 2 * kBqCons;
+
+struct BwdQueryParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const int32_t* idx;
+  const float* zsel;
+  const float* lse;
+  float* dq;
+  float* dzsel;
+  float* dsum;
+  float* cbias;
+  float* cu;
+  int B, Hq, Hkv, N, K, R, q0, nq;
+  float scale;
+};
+
+template <int D, int NH>
+__global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryParams p) {
+  typedef TileLayout<D, true> TL;
+  static_assert(TL::KE == TL::VE, "K and V halves share one pool");
+  constexpr int HE = TL::KE;                   // elements per half (the K or the V of a chunk)
+  constexpr int NI = D / 8;                    // DMA instructions per half
+  constexpr int HF = (63 / NI) < NH ? (63 / NI) : NH;   // halves in flight
+  static_assert(HF >= 2 && (HF - 1) * NI < 64, "in-flight loads must fit the vmcnt counter");
+  static_assert(NH >= 2 && NH <= 32, "half pool size");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int G = p.Hq / p.Hkv;
+  bf16_t* kvb = reinterpret_cast<bf16_t*>(smem);
+  int* pos_chunk = reinterpret_cast<int*>(smem + (size_t)NH * HE * sizeof(bf16_t));   // [N]
+  unsigned* pos_mask = reinterpret_cast<unsigned*>(pos_chunk + p.N);                  // [N]
+  short* pos_of = reinterpret_cast<short*>(pos_mask + p.N);                           // [N]
+  // after setup, the same bytes hold per position the pool entries of its K (byte 2j) and V (2j + 1)
+  unsigned char* pos_half = reinterpret_cast<unsigned char*>(pos_of);
+  __shared__ int s_n;
+  __shared__ int s_landed;           // halves landed: K of position j is half 2j, V half 2j + 1
+  __shared__ int s_rem[NH];          // consumers still to finish the half held by a pool entry
+  __shared__ int s_fail;
+  __shared__ int s_nlo[kBqQB];       // per query: selected chunks below the block's window range
+  __shared__ int s_nin[kBqQB];       // ... and inside it
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
+  const int nqb = (p.nq + kBqQB - 1) / kBqQB;
+  const int tile = xcd_tile(nqb * p.B * p.Hkv);   // (batch-head, query block), batch-head major
+  if (tile < 0) return;
+  const int bg = tile / nqb, b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int tb0 = (tile - bg * nqb) * kBqQB;
+  const long long L = (long long)p.N * kSlots;
+  const long long Tcont = (long long)p.N * kContent;
+  const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (size_t)bg * L * D;
+  const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (size_t)bg * L * D;
+  constexpr int NT = 64 * kBqWaves;
+
+  // ---- setup: chunk list and per-position query masks
+  if (tid == 0) {
+    s_landed = 0;
+    s_fail = 0;
+  }
+  if (tid < NH) s_rem[tid] = 0;
+  if (tid < kBqQB) {
+    s_nlo[tid] = 0;
+    s_nin[tid] = 0;
+  }
+  for (int c = tid; c < p.N; c += NT) pos_of[c] = 0;
+  __syncthreads();
+  const int t_last = min(tb0 + kBqQB, p.nq) - 1;
+  // the block's window range: chunks in the window of any of its queries
+  const int cw0 = (int)(max(0LL, (long long)p.q0 + tb0 - p.R) / kContent);
+  const int cw1 = (int)(min(Tcont - 1, (long long)p.q0 + t_last + p.R) / kContent);
+  for (int c = cw0 + tid; c <= cw1; c += NT) pos_of[c] = 1;
+  for (int e = tid; e < kBqQB * p.K; e += NT) {
+    const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
+    const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
+    if (c >= 0 && c < p.N) {
+      pos_of[c] = 1;
+      if (c < cw0) atomicAdd(&s_nlo[qi], 1);
+      else if (c <= cw1) atomicAdd(&s_nin[qi], 1);
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    // list order: the window range first (every block's heavy positions up front), then
+    // the other chunks ascending, so that concurrently running blocks walk the remote
+    // chunks in step and share them in L2
+    int base = 0;
+    auto append = [&](int c, bool f) {
+      const unsigned long long m = __ballot(f);
+      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (f) {
+        pos_chunk[pos] = c;
+        pos_mask[pos] = 0u;
+        pos_of[c] = (short)pos;
+      }
+      base += __popcll(m);
+    };
+    for (int c0 = cw0; c0 <= cw1; c0 += 64) {
+      const int c = c0 + lane;
+      append(c, c <= cw1 && pos_of[c] != 0);
+    }
+    for (int c0 = 0; c0 < p.N; c0 += 64) {
+      const int c = c0 + lane;
+      append(c, c < p.N && (c < cw0 || c > cw1) && pos_of[c] != 0);
+    }
+    if (lane == 0) s_n = base;
+  }
+  __syncthreads();
+  const int n = s_n;
+  for (int e = tid; e < kBqQB * p.K; e += NT) {
+    const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
+    const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
+    if (c >= 0 && c < p.N) atomicOr(&pos_mask[pos_of[c]], 1u << qi);
+  }
+  for (int qi = w; qi < kBqQB; qi += kBqWaves) {
+    const int t = tb0 + qi;
+    if (t >= p.nq) continue;
+    const long long i = (long long)p.q0 + t;
+    const int c0 = (int)(max(0LL, i - p.R) / kContent), c1 = (int)(min(Tcont - 1, i + p.R) / kContent);
+    for (int c = c0 + lane; c <= c1; c += 64) atomicOr(&pos_mask[pos_of[c]], 1u << qi);
+  }
+  __syncthreads();
+
+  if (w == kBqCons) {
+    // ---------------- producer
+    // Its instructions go ahead of the consumers' on the shared SIMD: the whole block
+    // runs at the pace of its loads, so their issue must not wait behind softmax work.
+    __builtin_amdgcn_s_setprio(3);
+    int told = 0;   // landed halves already published (monotonic)
+    bool ok = true;
+    int voffk[4], voffv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      voffk[u] = dma_voff<D>(false, u, lane);
+      voffv[u] = dma_voff<D>(true, u, lane);
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)kvb);
+    // publish the halves below hh2 - HF + 1 once at most HF - 1 of this wave's loads are in flight
+    auto publish_landed = [&](int hh2) {
+      if (hh2 >= HF && hh2 - HF + 1 > told) {
+        wait_vm<(HF - 1) * NI>();
+        compiler_fence();
+        if (lane == 0) lds_store_rel(&s_landed, hh2 - HF + 1);
+        told = hh2 - HF + 1;
+      }
+    };
+    // Any free entry takes the next half. Entries seen free stay known (only this wave
+    // fills them), so the counts are read again only when none is known free. Before
+    // waiting for one, everything issued is awaited and published, so that the
+    // consumers that hold the pool can finish. Returns -1 when the wait gives up or
+    // another wave has failed.
+    unsigned known_free = NH == 32 ? ~0u : (1u << NH) - 1u;
+    auto acquire = [&](int hx) -> int {
+      if (known_free == 0u) {
+        known_free = (unsigned)__ballot(lane < NH && lds_load_rel(&s_rem[lane < NH ? lane : 0]) == 0);
+        if (known_free == 0u) {
+          wait_vm<0>();
+          compiler_fence();
+          if (lane == 0) lds_store_rel(&s_landed, hx);
+          told = hx;
+          int it = 0;
+          for (; it < kSpinLimit && known_free == 0u; ++it) {
+            __builtin_amdgcn_s_sleep(1);
+            known_free = (unsigned)__ballot(lane < NH && lds_load_rel(&s_rem[lane < NH ? lane : 0]) == 0);
+          }
+          if (known_free == 0u || lds_load_rel(&s_fail) != 0) return -1;
+        }
+      }
+      const int e = __builtin_ctz(known_free);
+      known_free &= known_free - 1u;
+      return e;
+    };
+    // Chunks and consumer counts of 64 positions are read lane-parallel up front.
+    for (int base = 0; base < n && ok; base += 64) {
+      const int pj = base + lane < n ? base + lane : n - 1;
+      const int pcl = pos_chunk[pj];
+      const unsigned pml = pos_mask[pj];
+      int ul = 0;
+#pragma unroll
+      for (int cw = 0; cw < kBqCons; ++cw) ul += ((pml >> (2 * cw)) & 3u) != 0u ? 1 : 0;
+      const int cnt = min(64, n - base);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const int hk = 2 * (base + jj);
+        const int users = __builtin_amdgcn_readlane(ul, jj);
+        const size_t off = (size_t)__builtin_amdgcn_readlane(pcl, jj) * kSlots * D;
+        // K, then V, each into an entry of its own: K is released once its users have
+        // formed S, well before they are done with V
+        const int ek = acquire(hk);
+        if (ek < 0) {
+          ok = false;
+          break;
+        }
+        if (lane == 0) {   // both written before the landed count covers the half
+          lds_store_rel(&s_rem[ek], users);
+          pos_half[hk] = (unsigned char)ek;
+        }
+        compiler_fence();
+        publish_landed(hk);
+        dma_half_fast<D>(kg + off, lds0 + (uint32_t)(ek * HE * 2), voffk);
+        const int ev = acquire(hk + 1);
+        if (ev < 0) {
+          ok = false;
+          break;
+        }
+        if (lane == 0) {
+          lds_store_rel(&s_rem[ev], users);
+          pos_half[hk + 1] = (unsigned char)ev;
+        }
+        compiler_fence();
+        publish_landed(hk + 1);
+        dma_half_fast<D>(vg + off, lds0 + (uint32_t)(ev * HE * 2), voffv);
+      }
+    }
+    wait_vm<0>();
+    compiler_fence();
+    if (lane == 0) {
+      if (ok) lds_store_rel(&s_landed, 2 * n);
+      else lds_store_rel(&s_fail, 1);
+    }
+    return;
+  }
+
+  // ---------------- consumer w: queries 2w and 2w + 1 of the block, one 16-row tile
+  const int qq = (lane & 15) >> 3, hh = lane & 7, L16 = lane & 15;
+  const int h = g * G + (hh < G ? hh : 0);
+  const int qb = 2 * w + qq;                 // this lane's query in the block
+  const int tq = tb0 + qb;
+  const int iq = p.q0 + (tq < p.nq ? tq : p.nq - 1);
+  const bool rv = tq < p.nq && hh < G;
+  const int R32 = (int)min((long long)p.R, Tcont);
+  const size_t row = (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D;
+  const size_t rq = ((size_t)b * p.Hq + h) * p.nq + (tq < p.nq ? tq : p.nq - 1);
+  // per-row offsets into zsel, dzsel, cbias and cu as 32-bit indices (fewer live registers
+  // than 64-bit row pointers; the host checks that B*Hq*nq*K fits)
+  const int rqk = (int)(rq * (size_t)p.K);
+  // B operands of this lane's column: q and dO (d = 32 ks + 8 g16 + j); D = dO . o
+  s16x8 qf2[D / 32], dof[D / 32];
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    if (rv) {
+      qf2[ks] = load8(reinterpret_cast<const bf16_t*>(p.q) + row + 32 * ks + 8 * g16);
+      dof[ks] = load8(reinterpret_cast<const bf16_t*>(p.dO) + row + 32 * ks + 8 * g16);
+      const s16x8 of = load8(reinterpret_cast<const bf16_t*>(p.o) + row + 32 * ks + 8 * g16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dsum += bf2f((bf16_t)dof[ks][j]) * bf2f((bf16_t)of[j]);
+    } else {
+      qf2[ks] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      dof[ks] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  QFrag<D, 1> qf;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) qf.f[ks][0] = qf2[ks];
+  dsum = col_sum(dsum);
+  const float lse = rv ? p.lse[rq] : 0.f;
+  if (rv && g16 == 0) {
+    p.dsum[rq] = dsum;
+    for (int kk = 0; kk < p.K; ++kk) p.dzsel[rqk + kk] = 0.f;
+  }
+  const float sc = p.scale;
+  f32x4 dqa[D / 16];
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) dqa[dm] = zero4();
+  int ptr = 0;   // selected chunks of this lane's query visited so far
+  const int nlo = s_nlo[qb], nin = s_nin[qb];
+
+  // the v-th selected chunk visited: the list walks the window range, then the chunks
+  // below it, then those above, each ascending, while zsel is ascending
+  auto zsel_slot = [&](int v) {
+    const int ks = v < nin ? nlo + v : (v < nin + nlo ? v - nin : v);
+    return ks < p.K ? ks : p.K - 1;
+  };
+  float znext = p.K > 0 ? p.zsel[rqk + zsel_slot(0)] : 0.f;
+  int seen = 0;
+  auto await = [&](int need) -> bool {
+    int it = 0;
+    while (seen < need) {
+      seen = lds_load_rel(&s_landed);
+      if (seen >= need) break;
+      if (++it == kSpinLimit || lds_load_rel(&s_fail) != 0) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    compiler_fence();
+    return true;
+  };
+  auto release = [&](int e) {
+    wait_lgkm0();
+    compiler_fence();
+    if (lane == 0) __hip_atomic_fetch_add(&s_rem[e], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  typedef TileLayout<D, true> TL;
+  bool failed = false;
+  for (int base = 0; base < n && !failed; base += 64) {
+    const int pl = base + lane < n ? base + lane : n - 1;
+    const unsigned pm = base + lane < n ? pos_mask[pl] : 0u;
+    const int pc = pos_chunk[pl];
+    unsigned long long mine = __ballot(((pm >> (2 * w)) & 3u) != 0u);
+    while (mine != 0ull) {
+      const int bit = __builtin_ctzll(mine);
+      mine &= mine - 1ull;
+      const int j = base + bit;
+      const int c = __builtin_amdgcn_readlane(pc, bit);
+      const unsigned bits = (unsigned)__builtin_amdgcn_readlane((int)pm, bit) >> (2 * w);
+      const bool qa = ((bits >> qq) & 1u) != 0u;
+      const int rel = iq - c * kContent;
+      const bool win = rel + R32 >= 0 && rel - R32 <= kContent - 1;
+      const int mode = (!qa || !rv) ? 0 : (win ? 1 : 2);
+      const int lo = mode == 1 ? max(0, rel - R32) : 0;
+      const int hi = mode == 1 ? min(kContent - 1, rel + R32) : kContent - 1;
+      int slot = 0;
+      float z = 0.f;
+      if (qa && !win) {
+        slot = zsel_slot(ptr);
+        z = znext;
+        ++ptr;
+        znext = p.zsel[rqk + zsel_slot(ptr)];
+      }
+      if (!await(2 * j + 1)) {
+        failed = true;
+        break;
+      }
+      const int ek = pos_half[2 * j];
+      const bf16_t* kb = kvb + ek * HE;
+      f32x4 sacc[1][4];
+      s_tiles<D, 1>(kb, &qf, sacc, lane);
+      if (!await(2 * j + 2)) {
+        failed = true;
+        break;
+      }
+      const int ev = pos_half[2 * j + 1];
+      const bf16_t* vb = kvb + ev * HE;
+      // dP^T = V dO^T: V rows (swizzled V layout) as the A operand
+      f32x4 pacc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        pacc[mt] = zero4();
+        const int vr = 16 * mt + L16;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+          pacc[mt] = mfma16(load8(vb + vr * D + (((4 * ks + g16) ^ TL::swz_v(vr)) << 3)), dof[ks], pacc[mt]);
+      }
+      release(ev);
+      // intra-chunk softmax statistics of every column (used where the chunk is selected)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (16 * mt + 4 * g16 + e < kContent) mx = fmaxf(mx, sc * sacc[0][mt][e]);
+      mx = col_max(mx);
+      float l = 0.f, tu = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 16 * mt + 4 * g16 + e;
+          const float ex = jj < kContent ? __expf(sc * sacc[0][mt][e] - mx) : 0.f;
+          l += ex;
+          tu += ex * pacc[mt][e];
+        }
+      l = col_sum(l);
+      tu = col_sum(tu);
+      const float il = 1.f / l, U = tu * il;
+      float Pc = 0.f;
+      if (mode == 2) {
+        Pc = __expf(z - lse);
+        if (g16 == 0) {
+          p.dzsel[rqk + slot] = Pc * (U - dsum);
+          p.cbias[rqk + slot] = z - lse - (mx + __logf(l));
+          p.cu[rqk + slot] = U;
+        }
+      }
+      float ds[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 16 * mt + 4 * g16 + e;
+          float v = 0.f;
+          if (mode == 1) {
+            const float pw = (jj >= lo && jj <= hi) ? __expf(sc * sacc[0][mt][e] - lse) : 0.f;
+            v = pw * (pacc[mt][e] - dsum);
+          } else if (mode == 2) {
+            const float ex = jj < kContent ? __expf(sc * sacc[0][mt][e] - mx) : 0.f;   // recomputed: saves registers
+            v = Pc * ex * il * (pacc[mt][e] - U);
+          }
+          ds[mt][e] = v;
+        }
+      s16x8 pf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int jq = 0; jq < 8; ++jq) pf[ks][jq] = (short)f2bf(jq < 4 ? ds[2 * ks][jq] : ds[2 * ks + 1][jq - 4]);
+      // dQ^T += K^T dS^T: K^T read transposed from the swizzled K half. Rows r0 + 32 ks + 16 u
+      // share the swizzle of r0 (period 16), so each column block is one XOR per lane.
+      {
+        const int r0 = lane >> 2;
+        const int sw = TL::swz_k(r0);
+        const int ab = (lane & 3) >> 1, b4 = 4 * (lane & 1);
+#pragma unroll
+        for (int dm = 0; dm < D / 16; ++dm) {
+          const int off = (((2 * dm + ab) ^ sw) << 3) + b4;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const s16x4 lo4 = ds_read_tr(kb + (r0 + 32 * ks) * D + off);
+            const s16x4 hi4 = ds_read_tr(kb + (r0 + 32 * ks + 16) * D + off);
+            dqa[dm] = mfma16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], dqa[dm]);
+          }
+        }
+      }
+      release(ek);
+    }
+  }
+  if (failed && lane == 0) lds_store_rel(&s_fail, 1);
+
+  // ---- results
+  if (rv) {
+    float* dqr = p.dq + row;
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) *reinterpret_cast<f32x4*>(dqr + 16 * dm + 4 * g16) = dqa[dm] * sc;
+  }
+}
+
 // Merge the split partials of every query row (one wave per row). Partial s of
 // a row holds (O, m, l) at part[(s * rows + row) * (D + 4)]; a partial with
 // l = 0 saw no key of the row and its O is not read (it may not be written).
@@ -2081,6 +2517,51 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, cons
 // bf16: a ring of at most 4 swizzled 64-slot K/V tiles (2 for a one-wave block at
 // d = 128, where 32 loads per tile leave room for one tile in flight); float32: the
 // register-staged padded planes of swa_kernel.
+
+size_t bwd_query_pool_lds(int d, int N) { return (size_t)9 * 64 * d * 2 + (size_t)N * 10; }
+
+template <int D>
+static hipError_t launch_bwd_query_pool_d(const BwdQueryParams& prm, hipStream_t st) {
+  const size_t lds = bwd_query_pool_lds(D, prm.N);
+  hipError_t e = hipFuncSetAttribute((const void*)bwd_query_pool_kernel<D, 9>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int nqb = (prm.nq + kBqQB - 1) / kBqQB;
+  hipLaunchKernelGGL((bwd_query_pool_kernel<D, 9>), dim3(xcd_grid(nqb * prm.B * prm.Hkv)), dim3(64 * kBqWaves), lds,
+                     st, prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_query_pool(const RouteDims& dm, const void* q, const void* k, const void* v, const void* o,
+                                 const void* dO, const int32_t* idx, const float* zsel, const float* lse, int K,
+                                 int radius, float scale, int q0, int nq, float* dq, float* dzsel, float* dsum,
+                                 float* cbias, float* cu, hipStream_t st) {
+  BwdQueryParams prm;
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.o = o;
+  prm.dO = dO;
+  prm.idx = idx;
+  prm.zsel = zsel;
+  prm.lse = lse;
+  prm.dq = dq;
+  prm.dzsel = dzsel;
+  prm.dsum = dsum;
+  prm.cbias = cbias;
+  prm.cu = cu;
+  prm.B = dm.B;
+  prm.Hq = dm.Hq;
+  prm.Hkv = dm.Hkv;
+  prm.N = dm.N;
+  prm.K = K;
+  prm.R = radius;
+  prm.q0 = q0;
+  prm.nq = nq;
+  prm.scale = scale;
+  return dm.d == 128 ? launch_bwd_query_pool_d<128>(prm, st) : launch_bwd_query_pool_d<64>(prm, st);
+}
+
 size_t swa_lds_bytes(int d, int dtype) {
   return dtype == 1 ? (size_t)4 * 2 * 64 * d * 2 : kv_lds_bytes(d, dtype);
 }

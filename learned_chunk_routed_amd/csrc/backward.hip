@@ -1148,7 +1148,18 @@ static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t st) {
   e = hipFuncSetAttribute((const void*)bwd_query_kernel<D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  if (tiles > 0) hipLaunchKernelGGL(bwd_query_kernel<D>, dim3((tiles + 3) / 4), dim3(256), lds, st, prm);
+  if (tiles > 0) {
+    if (bwd_query_pool_lds(D, prm.N) <= routed_lds_limit() &&
+        (long long)prm.B * prm.Hq * prm.nq * prm.K < (1LL << 31)) {
+      // consecutive queries share one chunk stream (the forward's pool)
+      e = launch_bwd_query_pool(RouteDims{prm.B, prm.Hq, prm.Hkv, prm.N, D, 1}, prm.q, prm.k, prm.v, prm.o, prm.dO,
+                                prm.idx, prm.zsel, prm.lse, prm.K, prm.R, prm.scale, prm.q0, prm.nq, prm.dq,
+                                prm.dzsel, prm.dsum, prm.cbias, prm.cu, st);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(bwd_query_kernel<D>, dim3((tiles + 3) / 4), dim3(256), lds, st, prm);
+    }
+  }
   hipLaunchKernelGGL(bwd_key_kernel<D>, dim3((unsigned)bgn), dim3(256), 0, st, prm);
   return hipGetLastError();
 }

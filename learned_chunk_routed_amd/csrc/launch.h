@@ -83,6 +83,13 @@ hipError_t launch_route_score_backward(const RouteDims& dm, const void* q, const
 hipError_t launch_chunk_summary_backward(const RouteDims& dm, const void* q, const void* k, float scale,
                                          const float* ds, const float* dH, float* dq, float* dk, hipStream_t st);
 
+// query side of the routed attention backward through the forward's chunk pool (bf16)
+size_t bwd_query_pool_lds(int d, int N);
+hipError_t launch_bwd_query_pool(const RouteDims& dm, const void* q, const void* k, const void* v, const void* o,
+                                 const void* dO, const int32_t* idx, const float* zsel, const float* lse, int K,
+                                 int radius, float scale, int q0, int nq, float* dq, float* dzsel, float* dsum,
+                                 float* cbias, float* cu, hipStream_t st);
+
 size_t swa_lds_bytes(int d, int dtype);
 hipError_t launch_swa_attention(int B, int Hq, int Hkv, int L, int d, int dtype, const void* q,
                                 const void* k, const void* v, int radius, float scale, void* o,
