@@ -316,3 +316,27 @@ def test_route_layer_backward_end_to_end():
     print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
         assert e < BWD_TOL, f"{n} error {e:.3e}"
+
+
+@pytest.mark.timeout(300)
+def test_backward_decode_128k_tail():
+    """The 128K decode shape (2,048 chunks, 32 tail queries): the chunk pool does not fit in
+    LDS at this N, so the query side takes the per-wave chunk walk."""
+    cfg = get_config("decode_128k")
+    q0, nq = cfg.T - 32, 32
+    print(f"[case] backward decode_128k tail: N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} K={cfg.K} q0={q0} nq={nq}",
+          flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, q0, nq)
+    idx, zsel = selection(cfg, dr, q0, nq)
+    gq, gk, gv, gz = run_gpu(cfg, inp, dr["dO"], idx, zsel, q0, nq)
+    queries = np.arange(q0, q0 + nq)
+    sl = O.slot_of(queries)
+    rq, rk, rv, rz = OB.routed_attention_backward(as_f64(inp["q"][:, :, sl]), as_f64(inp["k"]), as_f64(inp["v"]),
+                                                  idx, zsel.astype(np.float64), cfg.R, cfg.scale, queries,
+                                                  as_f64(dr["dO"][:, :, sl]))
+    errs = dict(dq=rel_err(gq[:, :, sl], rq), dk=rel_err(gk, rk), dv=rel_err(gv, rv),
+                dzsel=rel_err(np.where(np.isfinite(zsel), gz, 0.0), rz))
+    print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e < BWD_TOL, f"{n} error {e:.3e}"
