@@ -277,6 +277,7 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(int* a, size_t n) {
 // scheduling, so dk and dv are reproducible bit for bit.
 constexpr int kIdxTile = 256;
 constexpr int kMaxGroup = 8;   // largest GQA group (query heads per KV head)
+constexpr int kMaxTopK = 64;   // largest K
 constexpr int kKeyRows = 64;   // (query, head) rows the key-side kernel stages per step
 
 __global__ __launch_bounds__(256) void bwd_hist_kernel(BwdParams p) {
@@ -679,41 +680,90 @@ size_t routed_bwd_lds_bytes(int d) { return (size_t)4 * 64 * (d + 8) * 2; }
 // for ds, dA and dB are split into fixed row ranges whose partials are added in order
 // (no atomics).
 
+// dq~ as a dense product: dq~[b,h,t,:] = scale sum_c Z[t][c] s[b,h,c,:], Z the rows' dzsel
+// scattered over chunks. One block per (64 rows, batch and head); the rows' entries are
+// staged in LDS once; chunks go 32 at a time (a [64 x 32] Z tile and the 32 summaries
+// as bf16 hi and lo planes); split-bf16 MFMA (three products, near float32). Writes dq~
+// and adds it to dq at the rows' slots.
+constexpr int kDqR = 64, kDqC = 32;
+
 template <int D>
-__global__ __launch_bounds__(256) void sbwd_dqt_kernel(const int32_t* __restrict__ idx, const float* __restrict__ dzsel,
-                                                       const float* __restrict__ s, float* __restrict__ dqt,
-                                                       float* __restrict__ dq, float scale, int Hq, int Hkv, int N,
-                                                       int K, int q0, int nq) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) void sbwd_dqt_dense_kernel(const int32_t* __restrict__ idx,
+                                                             const float* __restrict__ dzsel,
+                                                             const float* __restrict__ s, float* __restrict__ dqt,
+                                                             float* __restrict__ dq, float scale, int Hq, int Hkv,
+                                                             int N, int K, int q0, int nq) {
+  constexpr int ZS = kDqC + 8, SS = D + 16;
+  __shared__ short ei[kDqR * kMaxTopK];   // chunk indices (N <= 32768 on this path), -1 for none
+  __shared__ float ew[kDqR * kMaxTopK];
+  __shared__ float zf[kDqR * (kDqC + 1)];
+  __shared__ __align__(16) bf16_t zp[2][kDqR * ZS];
+  __shared__ __align__(16) bf16_t sp[2][kDqC * SS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, L16 = lane & 15, g16 = lane >> 4;
   const int bh = blockIdx.y, b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
-  const int t = blockIdx.x * 4 + w;
-  if (t >= nq) return;
-  const int32_t* id = idx + (((size_t)b * Hkv + g) * nq + t) * K;
-  const float* dz = dzsel + ((size_t)bh * nq + t) * K;
-  float acc[D / 64];
+  const int t0 = blockIdx.x * kDqR;
+  for (int x = tid; x < kDqR * K; x += 256) {
+    const int tl = x / K, k = x % K, t = t0 + tl;
+    ei[x] = (short)(t < nq ? idx[(((size_t)b * Hkv + g) * nq + t) * K + k] : -1);
+    ew[x] = t < nq ? dzsel[((size_t)bh * nq + t) * K + k] : 0.f;
+  }
+  f32x4 acc[D / 16];
 #pragma unroll
-  for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    const int cl = k0 + lane < K ? id[k0 + lane] : -1;
-    const float wl = k0 + lane < K ? dz[k0 + lane] : 0.f;
-    const int n = min(64, K - k0);
-    for (int i = 0; i < n; ++i) {
-      const int c = __shfl(cl, i);
-      const float wz = __shfl(wl, i);
-      if (c >= 0) {
-        const float* sr = s + ((size_t)bh * N + c) * D;
+  for (int nt = 0; nt < D / 16; ++nt) acc[nt] = zero4();
+  for (int c0 = 0; c0 < N; c0 += kDqC) {
+    __syncthreads();
+    for (int x = tid; x < kDqR * (kDqC + 1); x += 256) zf[x] = 0.f;
+    for (int x = tid; x < kDqC * D / 4; x += 256) {
+      const int cl = x / (D / 4), e = 4 * (x % (D / 4)), c = c0 + cl;
+      f32x4 v = zero4();
+      if (c < N) v = *reinterpret_cast<const f32x4*>(s + ((size_t)bh * N + c) * D + e);
 #pragma unroll
-        for (int u = 0; u < D / 64; ++u) acc[u] += wz * sr[lane + 64 * u];
+      for (int j = 0; j < 4; ++j) {
+        bf16_t hi, lo;
+        split_bf16(v[j], hi, lo);
+        sp[0][cl * SS + e + j] = hi;
+        sp[1][cl * SS + e + j] = lo;
       }
+    }
+    __syncthreads();
+    for (int x = tid; x < kDqR * K; x += 256) {
+      const int c = ei[x] - c0;
+      if (c >= 0 && c < kDqC) zf[(x / K) * (kDqC + 1) + c] = ew[x];
+    }
+    __syncthreads();
+    for (int x = tid; x < kDqR * kDqC; x += 256) {
+      const int tl = x / kDqC, cl = x % kDqC;
+      bf16_t hi, lo;
+      split_bf16(zf[tl * (kDqC + 1) + cl], hi, lo);
+      zp[0][tl * ZS + cl] = hi;
+      zp[1][tl * ZS + cl] = lo;
+    }
+    __syncthreads();
+    // wave w: rows 16 w .. 16 w + 15 (M) x all of d (N), k = the 32 chunks
+    const s16x8 ah = load8(zp[0] + (16 * w + L16) * ZS + 8 * g16);
+    const s16x8 al = load8(zp[1] + (16 * w + L16) * ZS + 8 * g16);
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const s16x8 bhi = lds_col_frag(sp[0], SS, 8 * g16, 8 * g16 + 4, 16 * nt, lane);
+      const s16x8 blo = lds_col_frag(sp[1], SS, 8 * g16, 8 * g16 + 4, 16 * nt, lane);
+      acc[nt] = mfma16(ah, blo, acc[nt]);
+      acc[nt] = mfma16(al, bhi, acc[nt]);
+      acc[nt] = mfma16(ah, bhi, acc[nt]);
     }
   }
   const size_t L = (size_t)N * kSlots;
-  float* dqr = dq + ((size_t)bh * L + slot_of_c(q0 + t)) * D;
-  float* dtr = dqt + ((size_t)bh * nq + t) * D;
 #pragma unroll
-  for (int u = 0; u < D / 64; ++u) {
-    dtr[lane + 64 * u] = scale * acc[u];
-    dqr[lane + 64 * u] += scale * acc[u];
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 16 * w + 4 * g16 + i;
+    if (t >= nq) continue;
+    float* dtr = dqt + ((size_t)bh * nq + t) * D;
+    float* dqr = dq + ((size_t)bh * L + slot_of_c(q0 + t)) * D;
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const float v = scale * acc[nt][i];
+      dtr[16 * nt + L16] = v;
+      dqr[16 * nt + L16] += v;
+    }
   }
 }
 
@@ -1053,8 +1103,8 @@ static hipError_t launch_score_bwd_t(const RouteDims& dm, const void* x, const v
                                      float* dBm, float* ds, float* dH, const ScoreBwdWs& w, hipStream_t st) {
   const int rows = dm.B * nq;
   if (nq > 0) {
-    hipLaunchKernelGGL((sbwd_dqt_kernel<D>), dim3((nq + 3) / 4, dm.B * dm.Hq), dim3(256), 0, st, idx, dzsel, s,
-                       w.dqt, dq, scale, dm.Hq, dm.Hkv, dm.N, K, q0, nq);
+    hipLaunchKernelGGL((sbwd_dqt_dense_kernel<D>), dim3((nq + kDqR - 1) / kDqR, dm.B * dm.Hq), dim3(256), 0, st,
+                       idx, dzsel, s, w.dqt, dq, scale, dm.Hq, dm.Hkv, dm.N, K, q0, nq);
   }
   {
     const int bhq = dm.B * dm.Hq;
