@@ -20,12 +20,13 @@
 // (row, selected chunk), written by the query-side pass.
 //
 // Kernels (one call, in stream order):
-//  1. bwd_query_kernel: one wave per 2 consecutive queries x 8 head rows (the
-//     16 MFMA columns of a tile, as in the forward). The wave walks the union of
-//     its window chunks and selected chunks in ascending order; per chunk it
-//     recomputes S^T = K Q^T and dP^T = V dO^T, forms ds, and accumulates
-//     dQ^T += K^T dS^T (K^T read from LDS with the transposing read). Writes dq,
-//     dzsel, D and, per (row, selected chunk), the bias and U_c.
+//  1. query side: bwd_query_pool_kernel (attention.hip, beside the forward whose
+//     chunk pool it shares) walks one ascending stream of the chunks any of a
+//     block's 22 queries needs; where that pool does not fit in LDS,
+//     bwd_query_kernel here gives each wave of 2 queries its own walk. Per
+//     (tile, chunk) both recompute S^T = K Q^T and dP^T = V dO^T, form ds, and
+//     accumulate dQ^T += K^T dS^T (K^T read from LDS with the transposing read).
+//     They write dq, dzsel, D and, per (row, selected chunk), the bias and U_c.
 //  2. inverse index: per (batch, KV group, chunk) the list of (query, slot)
 //     entries that selected it, in ascending query order (per-tile counts,
 //     a scan over chunks and tiles, placement row by row).
