@@ -17,6 +17,7 @@ from .ops import (  # noqa: F401
     routed_attention_backward,
     swa_attention,
     route_layer,
+    route_layer_backward,
     workspace_bytes,
     make_dims,
     default_scale,

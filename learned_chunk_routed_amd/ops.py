@@ -293,6 +293,22 @@ def chunk_summary_backward(q, k, ds, dH, scale=None, dq=None, dk=None):
     return dq, dk
 
 
+def route_layer_backward(q, k, v, x, A, Bm, fwd, dO, *, radius, beta=0.0, scale=None, q0=0, nq=None):
+    """Gradients of the whole route layer with the forward's selection held fixed.
+
+    fwd is the dict route_layer returned (with want_lse=True: s, idx, zsel, o, lse);
+    dO [B,Hq,L,d] bf16 is the upstream gradient on o. Chains the attention, scoring
+    and pooling backward calls; returns a dict with dq [B,Hq,L,d] (query rows from
+    attention and scoring, mask rows from the pooling), dk, dv, dx, dA, dBm, and the
+    intermediates dzsel, ds, dH (all float32)."""
+    _need(fwd.get("lse") is not None, "route_layer_backward needs the forward's lse (route_layer(..., want_lse=True))")
+    dq, dk, dv, dz = routed_attention_backward(q, k, v, fwd["idx"], fwd["zsel"], fwd["o"], fwd["lse"], dO,
+                                               radius=radius, scale=scale, q0=q0, nq=nq)
+    sc = route_score_backward(q, x, A, Bm, fwd["s"], fwd["idx"], dz, beta=beta, scale=scale, q0=q0, nq=nq, dq=dq)
+    chunk_summary_backward(q, k, sc["ds"], sc["dH"], scale=scale, dq=dq, dk=dk)
+    return dict(dq=dq, dk=dk, dv=dv, dx=sc["dx"], dA=sc["dA"], dBm=sc["dBm"], dzsel=dz, ds=sc["ds"], dH=sc["dH"])
+
+
 def swa_attention(q, k, v, *, radius, scale=None, out=None, lse=None, want_lse=False):
     """Bidirectional sliding-window attention over slots |u - t| <= radius: o [B,Hq,L,d]."""
     lib = _lib.load()

@@ -340,3 +340,42 @@ def test_backward_decode_128k_tail():
     print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
         assert e < BWD_TOL, f"{n} error {e:.3e}"
+
+
+@pytest.mark.timeout(300)
+def test_route_layer_backward_binding_entropy_32k_sampled():
+    """route_layer_backward (the three calls chained) on the 32K entropy workload (batch 2,
+    beta = 0.5, shared per-chunk key offsets). Inputs of the backward that the forward would
+    provide come from the oracle (summaries; a selection ranked by the oracle over seeded
+    scores; seeded chunk logits); o and lse come from the GPU forward on those inputs and are
+    used on the GPU side only. Checked on sampled query blocks: dzsel, and the dq rows
+    (attention part plus scoring part, the oracle's per-row sums)."""
+    cfg = get_config("prefill_32k_entropy")
+    print(f"[case] route_layer_backward prefill_32k_entropy: B={cfg.B} N={cfg.N} beta={cfg.beta}", flush=True)
+    inp = route_inputs(cfg)
+    d = {n: to_dev(inp[n]) for n in ("q", "k", "v", "x", "A", "Bm")}
+    s_ref, _ = O.chunk_summary(as_f64(inp["q"]), as_f64(inp["k"]), cfg.scale)
+    s32 = s_ref.astype(np.float32)
+    dr = backward_draws(cfg, 0, cfg.T)
+    idx, zsel = selection(cfg, dr, 0, cfg.T)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).cuda()
+    z_t = torch.from_numpy(np.ascontiguousarray(zsel)).cuda()
+    o, lse = lcr.routed_attention(d["q"], d["k"], d["v"], idx_t, z_t, radius=cfg.R, scale=cfg.scale, want_lse=True)
+    fwd = dict(s=torch.from_numpy(s32).cuda(), idx=idx_t, zsel=z_t, o=o, lse=lse)
+    g = lcr.route_layer_backward(d["q"], d["k"], d["v"], d["x"], d["A"], d["Bm"], fwd, to_dev(dr["dO"]),
+                                 radius=cfg.R, beta=cfg.beta, scale=cfg.scale)
+    torch.cuda.synchronize()
+    queries = sample_query_blocks(cfg.T, n_blocks=3, block=16, seed=9)
+    sl = O.slot_of(queries)
+    qrows = as_f64(inp["q"][:, :, sl])
+    rq_a, _, _, rz = OB.routed_attention_backward(qrows, as_f64(inp["k"]), as_f64(inp["v"]), idx[:, :, queries],
+                                                  zsel[:, :, queries].astype(np.float64), cfg.R, cfg.scale,
+                                                  queries, as_f64(dr["dO"][:, :, sl]))
+    rq_s = OB.route_score_backward(qrows, as_f64(inp["x"][:, sl]), as_f64(inp["A"]), as_f64(inp["Bm"]),
+                                   s32.astype(np.float64), None, idx[:, :, queries], rz, cfg.beta, cfg.scale)[0]
+    fin = np.isfinite(zsel[:, :, queries])
+    errs = dict(dzsel=rel_err(np.where(fin, f64(g["dzsel"])[:, :, queries], 0.0), rz),
+                dq=rel_err(f64(g["dq"])[:, :, sl], rq_a + rq_s))
+    print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e < BWD_TOL, f"{n} error {e:.3e}"
