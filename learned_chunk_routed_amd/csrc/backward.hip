@@ -277,7 +277,6 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(int* a, size_t n) {
 // one wave per tile then walks its rows in order. The result does not depend on
 // scheduling, so dk and dv are reproducible bit for bit.
 constexpr int kIdxTile = 256;
-constexpr int kMaxGroup = 8;   // largest GQA group (query heads per KV head)
 constexpr int kMaxTopK = 64;   // largest K
 constexpr int kKeyRows = 64;   // (query, head) rows the key-side kernel stages per step
 
