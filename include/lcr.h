@@ -50,7 +50,7 @@ typedef enum {
   LCR_ERR_DTYPE = -2,        /* dtype is not LCR_F32 or LCR_BF16 */
   LCR_ERR_WORKSPACE = -3,    /* ws is NULL or smaller than lcr_workspace_bytes() */
   LCR_ERR_HIP = -4,          /* the HIP runtime rejected a launch */
-  LCR_ERR_UNSUPPORTED = -5   /* valid, but outside this build's limits (d, G, K, LDS) */
+  LCR_ERR_UNSUPPORTED = -5   /* valid, but outside this library's limits (d, G, K, LDS) */
 } lcr_status;
 
 typedef enum { LCR_F32 = 0, LCR_BF16 = 1 } lcr_dtype;

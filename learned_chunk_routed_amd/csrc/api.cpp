@@ -34,7 +34,7 @@ const char* lcr_status_string(int status) {
     case LCR_ERR_DTYPE: return "invalid dtype";
     case LCR_ERR_WORKSPACE: return "workspace missing or too small";
     case LCR_ERR_HIP: return "HIP runtime error";
-    case LCR_ERR_UNSUPPORTED: return "outside this build's limits";
+    case LCR_ERR_UNSUPPORTED: return "outside this library's limits";
     default: return "unknown status";
   }
 }

@@ -187,7 +187,7 @@ def test_routed_attention_backward_validation(lib):
         return lib.lcr_routed_attention_backward(dm or dims(), pt[0], pt[1], pt[2], pt[3], pt[4], K, R, scale, q0,
                                                  nq, pt[5], pt[6], pt[7], pt[8], pt[9], pt[10], pt[11], ws,
                                                  ws_bytes, NULL)
-    assert call(dm=dims(dtype=0)) == _lib.LCR_ERR_UNSUPPORTED          # float32 inputs: not in this build
+    assert call(dm=dims(dtype=0)) == _lib.LCR_ERR_UNSUPPORTED          # float32 inputs: not supported by the backward
     assert call(K=-1) == _lib.LCR_ERR_ARG
     assert call(K=65) == _lib.LCR_ERR_UNSUPPORTED
     assert call(R=-5) == _lib.LCR_ERR_ARG
