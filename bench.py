@@ -18,12 +18,14 @@ Printed JSON line (one, rank 0):
   swa_64k      ms per sliding-window layer (65,536 slots, radius 1280)
   dense_16k    ms per dense bidirectional attention layer (16,384 slots, every
                slot attends to every slot: the sliding window with R >= L)
+  prefill_32k_entropy  ms per 32K route layer with the entropy term (batch 2, beta 0.5)
+  stack_64k    ms per 28-layer attention forward at 64K (7 route layers, 21 SWA layers)
   backward_16k ms of the route layer's backward on the 16K-prefill workload:
                attention (dq, dk, dv, dzsel, with its MFMA roofline), scoring
                (dq, dx, dA, dBm, ds, dH) and pooling (dq mask rows, dk)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--no-decode] [--no-swa] [--only {prefill,decode,swa,dense,backward,copy}]
+       [--no-decode] [--no-swa] [--only {prefill,decode,swa,dense,backward,entropy,stack,copy}]
 (--only copy runs a plain 1 GiB device copy, used to calibrate byte counters.)
 """
 import argparse
@@ -308,18 +310,34 @@ def bench_decode(args, torch, lcr):
         ms.append(ev0.elapsed_time(ev1))
         b, _ = decode_bytes(cfg, idx.cpu().numpy())
         nbytes.append(b)
+    # cold: the Infinity Cache is scrubbed before each step by writing a 512 MB buffer (untimed)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for j in range(16):
+        q[:, :, slots] = q_tail[j]
+        x[:, slots] = x_tail[j]
+        scrub.fill_(j & 255)
+        torch.cuda.synchronize()
+        ev0.record()
+        graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        cold.append(ev0.elapsed_time(ev1))
+    del scrub
     ms, eager_ms = np.array(ms), np.array(eager_ms)
     med = float(np.median(ms))
     gbs = float(np.median(np.array(nbytes))) / (med * 1e-3) / 1e9
     return {"ms_per_step_median": round(med, 4), "ms_min": round(float(ms.min()), 4),
             "ms_max": round(float(ms.max()), 4), "steps": int(cfg.steps),
             "eager_ms_per_step_median": round(float(np.median(eager_ms)), 4),
+            "cold_ms_per_step_median": round(float(np.median(np.array(cold))), 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "algorithmic_mb_per_step": round(float(np.median(nbytes)) / 1e6, 2)},
             "summary_ms": summary_ms,
             "note": "route_score_topk + routed_attention per step on cached K/V, replayed from a HIP graph "
-                    "(eager_ms_per_step_median: the same calls issued from Python); summaries precomputed"}
+                    "(eager_ms_per_step_median: the same calls issued from Python; cold_ms_per_step_median: 16 "
+                    "steps each after a 512 MB write that scrubs the Infinity Cache); summaries precomputed"}
 
 
 def bench_swa(args, torch, lcr):
@@ -373,6 +391,138 @@ def bench_dense(args, torch, lcr):
     return {"ms_per_layer": round(ms, 4), "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                                                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                                      "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
+def _route_layer_runner(cfg, d, torch, lcr, bufs=None):
+    """Preallocated buffers and one call sequence for a whole route layer (summaries,
+    scoring + top-K, routed attention); returns (step, idx, bufs): step(ev) records ev[0]
+    before and ev[1] after the routed attention when ev is given. Pass the bufs of an
+    earlier runner of the same shape to share them (layers that run one after another)."""
+    B, Hq, Hkv, N, dd = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d
+    dev = "cuda"
+    if bufs is None:
+        dims = lcr.make_dims(B, Hq, Hkv, N, dd, torch.bfloat16)
+        bufs = dict(
+            s=torch.empty((B, Hq, N, dd), dtype=torch.float32, device=dev),
+            H=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+            idx=torch.empty((B, Hkv, cfg.T, cfg.K), dtype=torch.int32, device=dev),
+            zsel=torch.empty((B, Hq, cfg.T, cfg.K), dtype=torch.float32, device=dev),
+            out=torch.zeros_like(d["q"]),
+            ws_s=torch.empty(max(1, lcr.workspace_bytes(1, dims, cfg.D, cfg.r, cfg.K, cfg.T)), dtype=torch.uint8,
+                             device=dev),
+            ws_a=torch.empty(max(1, lcr.workspace_bytes(2, dims, 0, 0, cfg.K, cfg.T, cfg.R)), dtype=torch.uint8,
+                             device=dev))
+    b = bufs
+
+    def step(ev=None):
+        lcr.chunk_summary(d["q"], d["k"], cfg.scale, s=b["s"], H=b["H"])
+        lcr.route_score_topk(d["q"], d["x"], d["A"], d["Bm"], b["s"], b["H"], Hkv=Hkv, K=cfg.K, radius=cfg.R,
+                             beta=cfg.beta, scale=cfg.scale, idx=b["idx"], zsel=b["zsel"], ws=b["ws_s"])
+        if ev is not None:
+            ev[0].record()
+        lcr.routed_attention(d["q"], d["k"], d["v"], b["idx"], b["zsel"], radius=cfg.R, scale=cfg.scale,
+                             out=b["out"], ws=b["ws_a"])
+        if ev is not None:
+            ev[1].record()
+    return step, b["idx"], bufs
+
+
+def bench_entropy(args, torch, lcr):
+    """The 32K route layer with the entropy term: batch 2, N = 512 chunks, beta = 0.5, keys
+    with a shared per-chunk offset N(0, 0.3). Whole layers timed with HIP events (2 warmup,
+    5 timed); the routed attention's own launches timed beside them for its roofline."""
+    from lcr_inputs import get_config, route_inputs
+    cfg = get_config("prefill_32k_entropy")
+    log("[bench] prefill_32k_entropy: generating inputs")
+    d = {k: to_dev(v, torch) for k, v in route_inputs(cfg).items()}
+    step, idx, _ = _route_layer_runner(cfg, d, torch, lcr)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n = 5
+    e[0].record()
+    for _ in range(n):
+        step()
+    e[1].record()
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / n
+    ra = []
+    for _ in range(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        step(ev)
+        torch.cuda.synchronize()
+        ra.append(ev[0].elapsed_time(ev[1]))
+    attn_ms = float(np.mean(ra))
+    local, chunks = prefill_flops(cfg, int((idx >= 0).sum().item()))
+    tf = (local + chunks) / (attn_ms * 1e-3) / 1e12
+    return {"ms_per_layer": round(ms, 4), "queries_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+            "routed_attention_ms": round(attn_ms, 4),
+            "roofline": {"bound": "mfma", "kernel": "routed_prefill_kernel", "achieved": round(tf, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
+def bench_stack(args, torch, lcr):
+    """The 28-layer attention forward at 64K: route layers at l % 4 == 3 (7 of them), bidirectional
+    SWA with radius 1280 over all 65,536 slots in the other 21, each layer with its own inputs
+    (drawn on the device beforehand, about 20 GB). One warmup forward, then 2 timed; per-kind
+    layer times from HIP events in a further forward."""
+    from lcr_inputs import get_config, stack_layer_torch
+    cfg = get_config("stack_64k")
+    log("[bench] stack_64k: generating 28 layers of inputs on the device")
+    layers = [stack_layer_torch(cfg, l, "cuda", route=(l % cfg.route_every == cfg.route_every - 1))
+              for l in range(cfg.layers)]
+    runners = []
+    swa_out = torch.empty_like(layers[0]["q"])
+    bufs = None   # the route layers run one after another: one set of buffers and workspaces
+    for l, t in enumerate(layers):
+        if "x" in t:
+            step, idx, bufs = _route_layer_runner(cfg, t, torch, lcr, bufs)
+            runners.append(("route", step))
+        else:
+            runners.append(("swa", t))
+
+    def forward(evs=None):
+        for l, (kind, r) in enumerate(runners):
+            if evs is not None:
+                evs[l][0].record()
+            if kind == "route":
+                r()
+            else:
+                lcr.swa_attention(r["q"], r["k"], r["v"], radius=cfg.swa_radius, scale=cfg.scale, out=swa_out)
+            if evs is not None:
+                evs[l][1].record()
+    forward()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for _ in range(2):
+        forward()
+    e[1].record()
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / 2
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in runners]
+    forward(evs)
+    torch.cuda.synchronize()
+    lm = [ev[0].elapsed_time(ev[1]) for ev in evs]
+    route_ms = [m for m, (k, _) in zip(lm, runners) if k == "route"]
+    swa_ms = [m for m, (k, _) in zip(lm, runners) if k == "swa"]
+    # algorithmic attention flops: routed window + chunks per route layer (the chosen-chunk count of
+    # the last route layer, whose selection the shared buffers hold; every row chooses K chunks
+    # except at the sequence ends), 4 d per (head, slot, key) for SWA
+    lo, ch = prefill_flops(cfg, int((bufs["idx"] >= 0).sum().item()))
+    flops = len(route_ms) * (lo + ch)
+    u = np.arange(cfg.L)
+    keys = float((np.minimum(cfg.L - 1, u + cfg.swa_radius) - np.maximum(0, u - cfg.swa_radius) + 1).sum())
+    flops += len(swa_ms) * 4.0 * cfg.d * cfg.Hq * keys
+    tf = flops / (ms * 1e-3) / 1e12
+    del layers, runners, bufs
+    return {"ms_per_forward": round(ms, 3), "route_layer_ms_mean": round(float(np.mean(route_ms)), 3),
+            "swa_layer_ms_mean": round(float(np.mean(swa_ms)), 3), "route_layers": len(route_ms),
+            "swa_layers": len(swa_ms),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_tflop_per_forward": round(flops / 1e12, 2)}}
 
 
 def bench_backward(args, torch, lcr):
@@ -436,7 +586,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-swa", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "swa", "dense", "backward", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "swa", "dense", "backward", "entropy", "stack", "copy"],
+                    default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -457,6 +608,12 @@ def main():
         return
     if args.only == "dense":
         print(json.dumps({"dense_16k": bench_dense(args, torch, lcr)}), flush=True)
+        return
+    if args.only == "entropy":
+        print(json.dumps({"prefill_32k_entropy": bench_entropy(args, torch, lcr)}), flush=True)
+        return
+    if args.only == "stack":
+        print(json.dumps({"stack_64k": bench_stack(args, torch, lcr)}), flush=True)
         return
     if args.only == "backward":
         print(json.dumps({"backward_16k": bench_backward(args, torch, lcr)}), flush=True)
@@ -500,6 +657,8 @@ def main():
         line["dense_16k"] = bench_dense(args, torch, lcr)
     if args.only is None:
         line["backward_16k"] = bench_backward(args, torch, lcr)
+        line["prefill_32k_entropy"] = bench_entropy(args, torch, lcr)
+        line["stack_64k"] = bench_stack(args, torch, lcr)
     if args.only is None and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg, inp)

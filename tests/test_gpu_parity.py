@@ -331,3 +331,41 @@ def test_swa(case):
     l_err = max_err(f64(lse)[:, :, rows], rl)
     print(f"    o_err={o_err:.2e} lse_err={l_err:.2e}", flush=True)
     assert o_err < OUT_TOL[c["dtype"]] and l_err < LSE_TOL[c["dtype"]]
+
+
+@pytest.mark.timeout(600)
+def test_stack_64k_route_layer_sampled():
+    """A route layer of the 64K stack (N = 1,024 chunks: scoring takes the general path, the
+    routed kernel its chunk pool with 1,024 positions), inputs drawn on the device; the
+    oracle gets the same bits copied back (mask-query rows, sampled query and x rows, K, V)."""
+    from lcr_inputs import stack_layer_torch
+    cfg = get_config("stack_64k")
+    print(f"[case] stack_64k route layer 3: N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} K={cfg.K} R={cfg.R}", flush=True)
+    t = stack_layer_torch(cfg, 3, "cuda", route=True)
+    res = lcr.route_layer(t["q"], t["k"], t["v"], t["x"], t["A"], t["Bm"], K=cfg.K, radius=cfg.R, beta=cfg.beta,
+                          scale=cfg.scale, want_lse=True)
+    torch.cuda.synchronize()
+    queries = sample_query_blocks(cfg.T, n_blocks=4, block=32, seed=11)
+    slots = torch.from_numpy(O.slot_of(queries)).cuda()
+    q_rows = f64(t["q"][:, :, slots])
+    q_mask = f64(t["q"].view(cfg.B, cfg.Hq, cfg.N, 64, cfg.d)[:, :, :, 63])
+    x_rows = f64(t["x"][:, slots])
+    k, v, A, Bm = f64(t["k"]), f64(t["v"]), f64(t["A"]), f64(t["Bm"])
+    ref = O.route_layer_rows(q_rows, q_mask, k, v, x_rows, A, Bm, K=cfg.K, R=cfg.R, beta=cfg.beta, scale=cfg.scale,
+                             queries=queries)
+    tq = queries
+    idx_gpu = res["idx"][:, :, torch.from_numpy(tq).cuda()].cpu().numpy().astype(np.int64)
+    same = check_selection(idx_gpu, ref, cfg.K, "stack_64k")
+    fin = np.isfinite(ref["zsel"])
+    zg = f64(res["zsel"][:, :, torch.from_numpy(tq).cuda()])
+    sm = np.broadcast_to(np.repeat(same, cfg.G, axis=1)[..., None], fin.shape) & fin
+    z_err = max_err(zg[sm], ref["zsel"][sm])
+    rows_same = same.all(axis=(0, 1))
+    o_gpu = f64(res["o"][:, :, slots])
+    o_err = max_err(o_gpu[:, :, rows_same], ref["o"][:, :, rows_same])
+    l_err = max_err(f64(res["lse"][:, :, torch.from_numpy(tq).cuda()])[:, :, rows_same], ref["lse"][:, :, rows_same])
+    print(f"    rows={len(tq)} same={int(rows_same.sum())} o_err={o_err:.2e} lse_err={l_err:.2e} z_err={z_err:.2e}",
+          flush=True)
+    assert rows_same.sum() >= len(tq) // 2, "too few rows with the oracle's own selection to compare"
+    assert o_err < OUT_TOL["bf16"] and l_err < LSE_TOL["bf16"]
+    assert z_err < Z_TOL["bf16"] * max(1.0, np.abs(ref["zsel"][sm]).max())
