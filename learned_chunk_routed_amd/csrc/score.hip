@@ -784,15 +784,22 @@ __device__ __forceinline__ int wave_topk(const uint32_t* key, int K, int lane, E
 //     counts, ties to the smaller chunk), written as idx, with a [QT][N] rank table;
 //  C. the same products again (bit-identical); the scores of chosen (query,
 //     chunk) pairs go straight to zsel, each tile's ranks read with its planes.
+// The keys are dead once every wave holds its queries' keys in registers, so the
+// rank table and the zsel staging rows of phases B and C overlay them: the block's
+// LDS is the key table plus the chosen lists, which admits 32 queries per block at
+// N = 1024 within the 160 KB of a CU.
 constexpr int kRsWaves = 8;
 
-__host__ __device__ inline size_t rs3_off_r(int NT, int N) { return (size_t)16 * NT * (N + 1) * 4; }
-__host__ __device__ inline size_t rs3_off_c(int NT, int N) { return (rs3_off_r(NT, N) + (size_t)16 * NT * N + 15) & ~(size_t)15; }
-__host__ __device__ inline size_t rs3_off_z(int NT, int N) { return rs3_off_c(NT, N) + kRsWaves * 64 * 4; }
-// without / with the zsel staging area (per wave, [QT][K] floats)
-__host__ __device__ inline size_t rs3_lds(int NT, int N) { return rs3_off_z(NT, N); }
-__host__ __device__ inline size_t rs3_lds_staged(int NT, int N, int K) {
-  return rs3_off_z(NT, N) + (size_t)kRsWaves * 16 * NT * K * 4;
+__host__ __device__ inline size_t rs3_keys(int NT, int N) { return (size_t)16 * NT * (N + 1) * 4; }
+__host__ __device__ inline size_t rs3_off_z(int NT, int N) { return ((size_t)16 * NT * N + 15) & ~(size_t)15; }
+__host__ __device__ inline size_t rs3_stage(int NT, int K) { return (size_t)kRsWaves * 16 * NT * K * 4; }
+// offset of the chosen lists: past the keys, or past ranks + staging rows if longer
+__host__ __device__ inline size_t rs3_off_c(int NT, int N, int K, bool stage) {
+  const size_t over = rs3_off_z(NT, N) + (stage ? rs3_stage(NT, K) : 0);
+  return ((rs3_keys(NT, N) > over ? rs3_keys(NT, N) : over) + 15) & ~(size_t)15;
+}
+__host__ __device__ inline size_t rs3_lds(int NT, int N, int K, bool stage) {
+  return rs3_off_c(NT, N, K, stage) + kRsWaves * 64 * 4;
 }
 
 // Summaries as the A operand of the scoring product, fragment-major: for each
@@ -849,14 +856,11 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
   const int t0 = (tile - bg * nqb) * QT;
   const long long L = (long long)N * kSlots;
   const int NMT = (N + 15) / 16, ZS = N + 1;
-  uint32_t* zk = reinterpret_cast<uint32_t*>(smem);             // [QT][ZS] group-maximum keys
-  uint8_t* rank_t = smem + rs3_off_r(NT, N);                   // [QT][N]: rank in zsel, 0xFF if not chosen
-  int* chosen = reinterpret_cast<int*>(smem + rs3_off_c(NT, N));
-  float* zst = reinterpret_cast<float*>(smem + rs3_off_z(NT, N));   // STAGE: per wave [QT][K] zsel rows
+  uint32_t* zk = reinterpret_cast<uint32_t*>(smem);             // A, B: [QT][ZS] group-maximum keys
+  uint8_t* rank_t = smem;                                       // B, C: [QT][N] rank in zsel, 0xFF if not chosen
+  float* zst = reinterpret_cast<float*>(smem + rs3_off_z(NT, N));   // C (STAGE): per wave [QT][K] zsel rows
+  int* chosen = reinterpret_cast<int*>(smem + rs3_off_c(NT, N, K, STAGE));
   for (int e = tid; e < QT * ZS; e += 64 * kRsWaves) zk[e] = 0u;
-  if constexpr (STAGE)
-    for (int e = tid; e < kRsWaves * QT * K; e += 64 * kRsWaves) zst[e] = -INFINITY;   // unfilled slots
-  for (int e = tid; e < QT * N / 4; e += 64 * kRsWaves) reinterpret_cast<uint32_t*>(rank_t)[e] = 0xFFFFFFFFu;
 
   const bool hw = w < G;   // this wave owns head w (wave-uniform)
   const int h = g * G + (hw ? w : 0);
@@ -923,7 +927,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
       }
     }
   }
-  __syncthreads();   // keys and ranks initialised
+  __syncthreads();   // keys initialised
 
   struct TileBuf {
     s16x8 sf[KS][2];
@@ -1029,6 +1033,11 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
         key[qq][j] = cand ? kv : 0u;
       }
     }
+    __syncthreads();   // every wave holds its keys: the table becomes ranks and staging rows
+    for (int e = tid; e < QT * N / 4; e += 64 * kRsWaves) reinterpret_cast<uint32_t*>(rank_t)[e] = 0xFFFFFFFFu;
+    if constexpr (STAGE)
+      for (int e = tid; e < kRsWaves * QT * K; e += 64 * kRsWaves) zst[e] = -INFINITY;   // unfilled slots
+    __syncthreads();
     uint32_t theta[QW];
     bool take_all[QW];
     wave_topk_thresholds<P, QW>(key, K, theta, take_all);
@@ -1537,7 +1546,7 @@ static int u_splits(const RouteDims& dm, int Dh, int nq) {
 
 // bf16 prefill-sized problems take the fused scoring kernel (no q~, z or zhat in memory).
 static bool fused_score_ok(const RouteDims& dm, int r, int nq) {
-  return dm.dtype == 1 && dm.N <= 512 && r <= 64 && nq > kSmallQ && dm.Hq / dm.Hkv <= 8;
+  return dm.dtype == 1 && dm.N <= 1024 && r <= 64 && nq > kSmallQ && dm.Hq / dm.Hkv <= 8;
 }
 
 // bf16 decode-sized problems (at most 32 queries) take the kernels of section 5.
@@ -1680,12 +1689,13 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
                      (const bf16_t*)Bm, r, HD, ws.bt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 48 queries per block: the q~ of the wave's head for them stays in registers
-  // (three 16-query tiles; two waves per SIMD either way)
-  const int NT = 3;
-  // zsel staged in LDS when the rows fit next to the keys and ranks
-  const bool stage = rs3_lds_staged(NT, dm.N, K) <= (size_t)(160 * 1024 - 512);
-  const size_t lds = stage ? rs3_lds_staged(NT, dm.N, K) : rs3_lds(NT, dm.N);
+  // 48 queries per block up to N = 512 (the q~ of the wave's head for them stays in
+  // registers as three 16-query tiles), 32 beyond, where 48 rows of keys would pass
+  // the 160 KB of LDS
+  const int NT = dm.N <= 512 ? 3 : 2;
+  // zsel staged in LDS when the rows fit
+  const bool stage = rs3_lds(NT, dm.N, K, true) <= (size_t)(160 * 1024 - 512);
+  const size_t lds = rs3_lds(NT, dm.N, K, stage);
   const int tiles = (nq + 16 * NT - 1) / (16 * NT) * dm.B * dm.Hkv;
 #define LCR_RS(NTT, PP)                                                                                          \
   do {                                                                                                           \
@@ -1697,7 +1707,8 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
                        K, radius);                                                                               \
   } while (0)
   if (dm.N <= 256) LCR_RS(3, 4);
-  else LCR_RS(3, 8);
+  else if (dm.N <= 512) LCR_RS(3, 8);
+  else LCR_RS(2, 16);
 #undef LCR_RS
   return hipGetLastError();
 }
