@@ -17,7 +17,8 @@ Printed JSON line (one, rank 0):
                chunk whose keys a decode step rewrites
   swa_64k      ms per sliding-window layer (65,536 slots, radius 1280)
   dense_16k    ms per dense bidirectional attention layer (16,384 slots, every
-               slot attends to every slot: the sliding window with R >= L)
+               slot attends to every slot: the sliding window with R >= L);
+               dense_64k and dense_128k the same at 65,536 and 131,072 slots
   prefill_32k_entropy  ms per 32K route layer with the entropy term (batch 2, beta 0.5)
   stack_64k    ms per 28-layer attention forward at 64K (7 route layers, 21 SWA layers)
   backward_16k ms of the route layer's backward on the 16K-prefill workload:
@@ -365,11 +366,11 @@ def bench_swa(args, torch, lcr):
                                                      "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
-def bench_dense(args, torch, lcr):
-    """Dense bidirectional attention over 16,384 slots (28 query / 4 KV heads, d = 128,
+def bench_dense(args, torch, lcr, L=16384):
+    """Dense bidirectional attention over L slots (28 query / 4 KV heads, d = 128,
     bf16 ~ N(0,1), seeded): the swa entry point with a radius covering the sequence."""
-    B, Hq, Hkv, L, d = 1, 28, 4, 16384, 128
-    g = torch.Generator(device="cuda").manual_seed(16384)
+    B, Hq, Hkv, d = 1, 28, 4, 128
+    g = torch.Generator(device="cuda").manual_seed(L)
     q = torch.randn((B, Hq, L, d), generator=g, device="cuda").to(torch.bfloat16)
     k = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16)
     v = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16)
@@ -379,7 +380,7 @@ def bench_dense(args, torch, lcr):
         lcr.swa_attention(q, k, v, radius=L, scale=scale, out=out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 5
+    n = 5 if L <= 16384 else 2
     e0.record()
     for _ in range(n):
         lcr.swa_attention(q, k, v, radius=L, scale=scale, out=out)
@@ -607,7 +608,8 @@ def main():
         print(json.dumps({"swa_64k": bench_swa(args, torch, lcr)}), flush=True)
         return
     if args.only == "dense":
-        print(json.dumps({"dense_16k": bench_dense(args, torch, lcr)}), flush=True)
+        print(json.dumps({f"dense_{L // 1024}k": bench_dense(args, torch, lcr, L) for L in (16384, 65536, 131072)}),
+              flush=True)
         return
     if args.only == "entropy":
         print(json.dumps({"prefill_32k_entropy": bench_entropy(args, torch, lcr)}), flush=True)
@@ -654,7 +656,8 @@ def main():
         line["decode_128k"] = bench_decode(args, torch, lcr)
     if args.only is None and not args.no_swa:
         line["swa_64k"] = bench_swa(args, torch, lcr)
-        line["dense_16k"] = bench_dense(args, torch, lcr)
+        for L in (16384, 65536, 131072):
+            line[f"dense_{L // 1024}k"] = bench_dense(args, torch, lcr, L)
     if args.only is None:
         line["backward_16k"] = bench_backward(args, torch, lcr)
         line["prefill_32k_entropy"] = bench_entropy(args, torch, lcr)

@@ -280,11 +280,14 @@ SWA_CASES = [
 ]
 
 
-@pytest.mark.parametrize("L,R,label", [(65536, 1280, "64K radius 1280"), (16384, 16384, "16K dense")])
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("L,R,label", [(65536, 1280, "64K radius 1280"), (16384, 16384, "16K dense"),
+                                       (131072, 131072, "128K dense")])
 def test_swa_full_size_sampled(L, R, label):
-    """The bench's SWA layer (65,536 slots, radius 1280) and dense layer (16,384 slots,
-    R >= L), 28/4 heads, d = 128, bf16, in the launch configuration the bench times;
-    the oracle computes 120 sampled rows (both ends and random interior slots)."""
+    """The bench's SWA layer (65,536 slots, radius 1280) and dense layers (16,384 and
+    131,072 slots, R >= L), 28/4 heads, d = 128, bf16, in the launch configuration the
+    bench times; the oracle computes 120 sampled rows (both ends and random interior
+    slots)."""
     from lcr_inputs import bf16_round
     print(f"[case] swa full size {label}", flush=True)
     B, Hq, Hkv, d = 1, 28, 4, 128
