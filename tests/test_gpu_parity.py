@@ -229,6 +229,17 @@ PREFILL_EDGE = [
 ]
 
 
+@pytest.mark.parametrize("beta", [-0.5, 0.25, 1.0, 2.0])
+def test_route_layer_beta_sweep(beta):
+    """Entropy weights around and beyond the published one, on keys with per-chunk
+    offsets so that the pooling entropies spread; a negative weight prefers the
+    chunks whose summaries are least peaked."""
+    cfg = get_config("tiny_fp32", N=128, Hq=8, Hkv=2, d=128, r=16, D=96, K=8, R=128, beta=beta, dtype="bf16",
+                     key_offset_std=0.3)
+    queries = np.unique(np.concatenate([np.arange(64), np.arange(4000, 4064), np.arange(cfg.T - 64, cfg.T)]))
+    route_parity(cfg, queries=queries, label=f"beta {beta}")
+
+
 @pytest.mark.parametrize("case", PREFILL_EDGE, ids=[c[0] for c in PREFILL_EDGE])
 def test_route_layer_prefill_edge(case):
     name, over = case[0], case[1]
