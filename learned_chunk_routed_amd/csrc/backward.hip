@@ -939,29 +939,73 @@ __global__ __launch_bounds__(256) void sbwd_du_kernel(const float* __restrict__ 
 
 // dx[b, slot(q0+t), m] = sum_j dU[b,t,j] A[m][j]: 64 rows x 256 hidden columns per block
 template <typename T, int RP>
-__global__ __launch_bounds__(256) void sbwd_dx_kernel(const float* __restrict__ dU, const T* __restrict__ A, int Dh,
-                                                      int r, float* __restrict__ dx, int N, int q0, int nq) {
-  constexpr int TR = 64;
-  __shared__ float us[TR * RP];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RP <= 64 ? 4 : 2))) void sbwd_dx_kernel(
+    const float* __restrict__ dU, const T* __restrict__ A, int Dh, int r, float* __restrict__ dx, int N, int q0,
+    int nq) {
+  // a block: 64 rows x 256 columns; a thread: one column, 4 rows at a time, so that
+  // one 16-byte LDS read of dU feeds 4 FMAs; every output element still sums its r
+  // products in rank order
+  constexpr int TR = 64, CPT = 1;
+  __shared__ __align__(16) float us[TR * RP];
   const int tid = threadIdx.x, b = blockIdx.z;
-  const int t0 = blockIdx.x * TR, m = blockIdx.y * 256 + tid;
+  const int t0 = blockIdx.x * TR, mb = blockIdx.y * 256 * CPT + tid;
   for (int x = tid; x < TR * RP; x += 256) {
     const int tt = t0 + x / RP;
     us[x] = tt < nq ? dU[((size_t)b * nq + tt) * RP + x % RP] : 0.f;
   }
   __syncthreads();
-  if (m >= Dh) return;
-  float a[RP];
+  if (mb >= Dh) return;
+  float a[CPT][RP];
+  // the thread's row of A: 16-byte loads when whole, aligned rows fill the padding
+  constexpr int EV = 16 / sizeof(T);
+  const bool vec = r == RP && ((uintptr_t)A & 15) == 0;
 #pragma unroll
-  for (int j = 0; j < RP; ++j) a[j] = j < r ? Elem<T>::to_f(A[(size_t)m * r + j]) : 0.f;
+  for (int c = 0; c < CPT; ++c) {
+    const int m = mb + 256 * c;
+    if (vec && m < Dh) {
+      const T* ar = A + (size_t)m * RP;
+#pragma unroll
+      for (int j = 0; j < RP; j += EV) {
+        T e[EV];
+        *reinterpret_cast<uint4*>(e) = *reinterpret_cast<const uint4*>(ar + j);
+#pragma unroll
+        for (int i = 0; i < EV; ++i) a[c][j + i] = Elem<T>::to_f(e[i]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RP; ++j) a[c][j] = (m < Dh && j < r) ? Elem<T>::to_f(A[(size_t)m * r + j]) : 0.f;
+    }
+  }
   const size_t L = (size_t)N * kSlots;
-  for (int tl = 0; tl < TR; ++tl) {
-    const int t = t0 + tl;
-    if (t >= nq) break;
-    float acc = 0.f;
+  const int tn = min(TR, nq - t0);
+  for (int tl = 0; tl < tn; tl += 4) {   // rows tl .. tl + 3 < TR: past nq they are zero in LDS
+    float acc[4][CPT];
 #pragma unroll
-    for (int j = 0; j < RP; ++j) acc += us[tl * RP + j] * a[j];
-    dx[((size_t)b * L + slot_of_c(q0 + t)) * Dh + m] = acc;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[i][c] = 0.f;
+#pragma unroll
+    for (int j = 0; j < RP; j += 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(us + (tl + i) * RP + j);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          acc[i][c] += u[0] * a[c][j];
+          acc[i][c] += u[1] * a[c][j + 1];
+          acc[i][c] += u[2] * a[c][j + 2];
+          acc[i][c] += u[3] * a[c][j + 3];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (tl + i >= tn) break;
+      float* row = dx + ((size_t)b * L + slot_of_c(q0 + t0 + tl + i)) * Dh;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+        if (mb + 256 * c < Dh) row[mb + 256 * c] = acc[i][c];
+    }
   }
 }
 
