@@ -1064,11 +1064,19 @@ __global__ __launch_bounds__(256) void sbwd_da_kernel(const T* __restrict__ x, c
     }
     __syncthreads();
     if (m < Dh) {
-      for (int tl = 0; tl < 16 && rb + tl < r1; ++tl) {
-        const int row = rb + tl, b = row / nq, t = row % nq;
-        const float v = Elem<T>::to_f(x[((size_t)b * L + slot_of_c(q0 + t)) * Dh + m]);
+      // the tile's 16 x values in flight together; rows past r1 contribute nothing
+      const int nr = min(16, r1 - rb);
+      float xv[16];
 #pragma unroll
-        for (int j = 0; j < RP; ++j) acc[j] += us[tl * RP + j] * v;
+      for (int tl = 0; tl < 16; ++tl) {
+        const int row = rb + min(tl, nr - 1), b = row / nq, t = row % nq;
+        xv[tl] = Elem<T>::to_f(x[((size_t)b * L + slot_of_c(q0 + t)) * Dh + m]);
+      }
+#pragma unroll
+      for (int tl = 0; tl < 16; ++tl) {
+        if (tl >= nr) break;
+#pragma unroll
+        for (int j = 0; j < RP; ++j) acc[j] += us[tl * RP + j] * xv[tl];
       }
     }
   }
