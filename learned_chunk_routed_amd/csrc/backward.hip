@@ -1030,11 +1030,19 @@ __global__ __launch_bounds__(256) void sbwd_db_kernel(const float* __restrict__ 
       us[x] = row < r1 ? U[(size_t)row * RP + x % RP] : 0.f;
     }
     __syncthreads();
-    for (int tl = 0; tl < 16 && rb + tl < r1; ++tl) {
-      const int row = rb + tl, b = row / nq, t = row % nq;
-      const float v = dqt[(((size_t)b * Hq + h) * nq + t) * D + e];
+    // the tile's 16 dq~ values in flight together; rows past r1 contribute nothing
+    const int nr = min(16, r1 - rb);
+    float dv[16];
 #pragma unroll
-      for (int j = 0; j < RP; ++j) acc[j] += us[tl * RP + j] * v;
+    for (int tl = 0; tl < 16; ++tl) {
+      const int row = rb + min(tl, nr - 1), b = row / nq, t = row % nq;
+      dv[tl] = dqt[(((size_t)b * Hq + h) * nq + t) * D + e];
+    }
+#pragma unroll
+    for (int tl = 0; tl < 16; ++tl) {
+      if (tl >= nr) break;
+#pragma unroll
+      for (int j = 0; j < RP; ++j) acc[j] += us[tl * RP + j] * dv[tl];
     }
   }
   if (col < HD) {
