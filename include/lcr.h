@@ -26,8 +26,9 @@
  *    LCR_ERR_HIP means a launch was rejected by the HIP runtime; earlier
  *    kernels of the same call may already have been enqueued.
  *  - Limits: d in {64, 128}; 1 <= G <= 8; 0 <= K <= 64; radius >= 0.
- *  - The library keeps no state between calls and may be called from several
- *    host threads on different streams.
+ *  - The library keeps no state between calls (apart from the wait limit of
+ *    lcr_set_wait_limit) and may be called from several host threads on
+ *    different streams.
  */
 #ifndef LCR_H
 #define LCR_H
@@ -69,6 +70,21 @@ typedef enum {
   LCR_OP_ROUTED_ATTENTION_BACKWARD = 4,
   LCR_OP_ROUTE_SCORE_BACKWARD = 5
 } lcr_op;
+
+/*
+ * Failure-handling hook. The pooled kernels (bf16 routed attention of
+ * prefill-sized problems, the query side of its backward, and the split routed
+ * attention of wide windows) coordinate their waves through counters in LDS.
+ * Every wait on such a counter gives up after `polls` polls (default 2^22, a
+ * fraction of a second), so a logic error cannot hang the GPU. A wave whose
+ * wait gives up stops and writes NaN to every output row it owns (o and lse of
+ * the forward; dq and dzsel of the backward), so an incomplete result never
+ * passes for a valid one; the call still returns LCR_OK. Rows of waves that
+ * completed their walk are exact. polls < 1 restores the default. The setting
+ * is process-wide (the one piece of state the library keeps) and applies to
+ * calls enqueued after this returns. Returns the previous setting.
+ */
+int lcr_set_wait_limit(int polls);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int lcr_version(void);
@@ -117,8 +133,10 @@ int lcr_chunk_summary_range(const lcr_dims* dims, const void* q, const void* k, 
                             float* s, float* H, void* stream);
 
 /*
- * Mean summaries: the "Mean summary" ablation of "Prefilling-dLLM v2" (Table 6;
- * Section "Discussion": attention-weighted summaries replaced by mean pooling).
+ * Mean summaries: the "Mean summary" ablation of "Prefilling-dLLM v2" (Table 6)
+ * and of "The 172x Speedup Has an Evidence Budget" (section "The mechanism tests
+ * reveal what actually contributes"): attention-weighted summaries replaced by
+ * mean pooling.
  * The pooling weights are uniform, so
  *
  *   s[b,h,c] = (1/63) sum_j k[b,g(h),64c+j]   (the same for every head of a group)

@@ -19,6 +19,7 @@ from .ops import (  # noqa: F401
     route_layer,
     route_layer_backward,
     workspace_bytes,
+    set_wait_limit,
     make_dims,
     default_scale,
 )

@@ -31,8 +31,7 @@
 //    kernel merges them.
 // Sliding-window attention uses the same tile machinery with 16 consecutive
 // slots of one head per tile and a band mask.
-#include <stdlib.h>
-
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -452,10 +451,11 @@ __device__ __forceinline__ void dma_chunk(const bf16_t* kc, const bf16_t* vc, bf
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // Bounded wait until an LDS counter reaches target (wave-uniform). Returns false
-// after ~2^22 polls (a fraction of a second), so a logic error cannot hang the GPU.
-constexpr int kSpinLimit = 1 << 22;
-__device__ __forceinline__ bool spin_until_ge(int* ctr, int target) {
-  for (int it = 0; it < kSpinLimit; ++it) {
+// after `limit` polls (by default 2^22, a fraction of a second), so a logic error
+// cannot hang the GPU. A wave whose wait gives up stops its walk and writes NaN to
+// every output row it owns, so an incomplete result cannot pass for a valid one.
+__device__ __forceinline__ bool spin_until_ge(int* ctr, int target, int limit) {
+  for (int it = 0; it < limit; ++it) {
     if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return true;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -487,6 +487,7 @@ struct RoutedParams {
   float* part;
   int B, Hq, Hkv, N, K, R, q0, nq, nsplit;
   int nent, epb;  // decode-sized plan: entries per 2-query tile, entries per block
+  int spin;       // polls before a wait on an LDS counter gives up (>= 1)
   float sl2;      // scale * log2(e)
 };
 
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
       // (1) this wave's share of position pos + PD
       if (j + PD < end) {
         const int p2 = pos + PD, s2 = p2 % NBUF, use2 = p2 / NBUF;
-        if (use2 > 0 && !spin_until_ge(&ctl_done[s2], WAVES * use2)) {
+        if (use2 > 0 && !spin_until_ge(&ctl_done[s2], WAVES * use2, p.spin)) {
           failed = true;
           break;
         }
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
     }
     if (any) {
       if constexpr (SWZ) {
-        if (!spin_until_ge(&ctl_arr[slot_buf], WAVES * (pos / NBUF + 1))) {
+        if (!spin_until_ge(&ctl_arr[slot_buf], WAVES * (pos / NBUF + 1), p.spin)) {
           failed = true;
           break;
         }
@@ -748,10 +749,16 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
   }
   if constexpr (SWZ) wait_vm<0>();   // no load of this wave outlives the block
 
-  // ---- results
+  // ---- results (NaN rows when this wave's walk was cut short by a wait that gave up)
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     if (!rv[tt]) continue;
+    if (failed) {
+      mrow[tt] = __builtin_nanf("");
+      lrow[tt] = __builtin_nanf("");
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm) acc[tt][dm] = f32x4{mrow[tt], mrow[tt], mrow[tt], mrow[tt]};
+    }
     if (p.nsplit == 1) {
       const float inv = 1.f / lrow[tt];
       T* orow = reinterpret_cast<T*>(p.o) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq[tt])) * D;
@@ -1111,7 +1118,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
           if (lane == 0) lds_store_rel(&s_landed, hx);
           told = hx;
           int it = 0;
-          for (; it < kSpinLimit && known_free == 0u; ++it) {
+          for (; it < p.spin && known_free == 0u; ++it) {
             __builtin_amdgcn_s_sleep(1);
             known_free = (unsigned)__ballot(lane < NH && lds_load_rel(&s_rem[lane < NH ? lane : 0]) == 0);
           }
@@ -1206,7 +1213,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
     while (seen < need) {
       seen = lds_load_rel(&s_landed);
       if (seen >= need) break;
-      if (++it == kSpinLimit || lds_load_rel(&s_fail) != 0) return false;
+      if (++it >= p.spin || lds_load_rel(&s_fail) != 0) return false;
       __builtin_amdgcn_s_sleep(1);
     }
     compiler_fence();
@@ -1271,7 +1278,13 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   }
   if (failed && lane == 0) lds_store_rel(&s_fail, 1);
 
-  // ---- results
+  // ---- results (NaN rows when this wave's walk was cut short by a wait that gave up)
+  if (failed) {
+    mrow = __builtin_nanf("");
+    lrow = mrow;
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) acc[dm] = f32x4{mrow, mrow, mrow, mrow};
+  }
   if (rv) {
     const float inv = 1.f / lrow;
     bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D;
@@ -1313,6 +1326,7 @@ struct BwdQueryParams {
   float* cbias;
   float* cu;
   int B, Hq, Hkv, N, K, R, q0, nq;
+  int spin;       // polls before a wait on an LDS counter gives up (>= 1)
   float scale;
 };
 
@@ -1459,7 +1473,7 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
           if (lane == 0) lds_store_rel(&s_landed, hx);
           told = hx;
           int it = 0;
-          for (; it < kSpinLimit && known_free == 0u; ++it) {
+          for (; it < p.spin && known_free == 0u; ++it) {
             __builtin_amdgcn_s_sleep(1);
             known_free = (unsigned)__ballot(lane < NH && lds_load_rel(&s_rem[lane < NH ? lane : 0]) == 0);
           }
@@ -1578,7 +1592,7 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
     while (seen < need) {
       seen = lds_load_rel(&s_landed);
       if (seen >= need) break;
-      if (++it == kSpinLimit || lds_load_rel(&s_fail) != 0) return false;
+      if (++it >= p.spin || lds_load_rel(&s_fail) != 0) return false;
       __builtin_amdgcn_s_sleep(1);
     }
     compiler_fence();
@@ -1714,7 +1728,14 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
   }
   if (failed && lane == 0) lds_store_rel(&s_fail, 1);
 
-  // ---- results
+  // ---- results (NaN rows when this wave's walk was cut short by a wait that gave up)
+  if (failed) {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) dqa[dm] = f32x4{nan, nan, nan, nan};
+    if (rv && g16 == 0)
+      for (int kk = 0; kk < p.K; ++kk) p.dzsel[rqk + kk] = nan;
+  }
   if (rv) {
     float* dqr = p.dq + row;
 #pragma unroll
@@ -2311,6 +2332,12 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
 
 static size_t align256a(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Polls before a wait on an LDS counter gives up, read at every launch.
+static constexpr int kDefaultWaitLimit = 1 << 22;
+static std::atomic<int> g_wait_limit{kDefaultWaitLimit};
+int set_wait_limit(int polls) { return g_wait_limit.exchange(polls >= 1 ? polls : kDefaultWaitLimit); }
+static int wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+
 // LDS bytes of the K/V staging buffers (all planes, all buffers).
 static size_t kv_lds_bytes(int d, int dtype) {
   const int np = dtype == 0 ? 3 : 1;
@@ -2353,12 +2380,6 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   // 8 waves x 1 tile when the selections of 32 queries do not fit in LDS.
   pl.waves = 8;
   pl.tiles = 2;
-  if (const char* e = getenv("LCR_ROUTED_WAVES16")) {
-    if (e[0] == '1') {
-      pl.waves = 16;
-      pl.tiles = 1;
-    }
-  }
   pl.qblock = 2 * pl.waves * pl.tiles;
   pl.nsplit = 1;
   if (routed_lds(dm, K, pl.qblock, pl.waves) > routed_lds_limit()) {
@@ -2441,7 +2462,6 @@ static hipError_t launch_routed_d(const RouteDims& dm, const AttnPlan& pl, const
   constexpr int NB = sizeof(T) == 2 ? 3 : (D == 128 ? 1 : 2);
   constexpr int NB1 = sizeof(T) == 2 ? 2 : NB;
   if (pl.waves == 8 && pl.tiles == 2) return launch_routed_t<T, D, 8, 2, NB>(dm, pl, prm, st);
-  if (pl.waves == 16) return launch_routed_t<T, D, 16, 1, NB>(dm, pl, prm, st);
   if (pl.waves == 8) return launch_routed_t<T, D, 8, 1, NB>(dm, pl, prm, st);
   return launch_routed_t<T, D, 1, 1, NB1>(dm, pl, prm, st);
 }
@@ -2502,6 +2522,7 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, cons
   prm.nsplit = pl.nsplit;
   prm.nent = pl.nent;
   prm.epb = pl.epb;
+  prm.spin = wait_limit();
   prm.sl2 = scale * kLog2e;
   if (pl.kind == 2) return dm.d == 64 ? launch_prefill_d<64>(dm, pl, prm, st) : launch_prefill_d<128>(dm, pl, prm, st);
   if (pl.kind == 1) {
@@ -2558,6 +2579,7 @@ hipError_t launch_bwd_query_pool(const RouteDims& dm, const void* q, const void*
   prm.R = radius;
   prm.q0 = q0;
   prm.nq = nq;
+  prm.spin = wait_limit();
   prm.scale = scale;
   return dm.d == 128 ? launch_bwd_query_pool_d<128>(prm, st) : launch_bwd_query_pool_d<64>(prm, st);
 }

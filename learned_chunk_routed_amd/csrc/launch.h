@@ -60,6 +60,8 @@ struct AttnPlan {
   size_t ws;       // workspace bytes for the split partials
 };
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq);
+// polls before a wait on an LDS counter gives up (< 1: the default); returns the previous value
+int set_wait_limit(int polls);
 size_t routed_lds_limit();
 hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& plan, const void* q,
                                    const void* k, const void* v, const int32_t* idx,

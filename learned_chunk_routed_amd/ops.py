@@ -60,6 +60,13 @@ def workspace_bytes(op, dims: Dims, D=0, r=0, K=0, nq=0, radius=0) -> int:
     return int(_lib.load().lcr_workspace_bytes(op, dims, D, r, K, radius, nq))
 
 
+def set_wait_limit(polls: int) -> int:
+    """Polls before a wait on an LDS counter inside the pooled kernels gives up
+    (polls < 1 restores the default); a wave that gives up writes NaN rows.
+    Process-wide; returns the previous setting."""
+    return int(_lib.load().lcr_set_wait_limit(int(polls)))
+
+
 def _workspace(nbytes, device, ws=None):
     if nbytes == 0:
         return None

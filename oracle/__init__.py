@@ -20,7 +20,7 @@ here is pinned by closed forms, invariants, brute force or a library routine;
 none is "parity unpinned".
 """
 from .route import (  # noqa: F401
-    SLOTS, CONTENT, slot_of, chunk_of, mask_slot,
+    SLOTS, CONTENT, slot_of,
     softmax, entropy,
     chunk_summary, chunk_summary_from_mask,
     routing_query, window_bounds, candidate_mask,

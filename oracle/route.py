@@ -28,16 +28,6 @@ def slot_of(i):
     return (i // CONTENT) * SLOTS + (i % CONTENT)
 
 
-def chunk_of(i):
-    """Chunk holding content index i."""
-    return np.asarray(i, dtype=np.int64) // CONTENT
-
-
-def mask_slot(c):
-    """Slot of chunk c's routing mask (the last of its 64 slots)."""
-    return np.asarray(c, dtype=np.int64) * SLOTS + (SLOTS - 1)
-
-
 def group_of(h, G):
     """KV head used by query head h: contiguous GQA groups (Figure 3 caption: a GQA group)."""
     return h // G

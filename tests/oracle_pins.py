@@ -240,6 +240,38 @@ def pin_topk_brute_force():
                     assert list(got[:m]) == sorted(best) and np.all(got[m:] == -1), "top-K set"
 
 
+def pin_topk_margin_by_explicit_sort():
+    """The selection margin of every row against an explicit sort of that row's
+    candidate group scores: the K-th best minus the (K+1)-th best, +inf when the row
+    has at most K candidates. Equivalently, the lowest chosen score minus the highest
+    score left out, which ties the margin to the chosen set itself. (The GPU tests
+    use this margin to decide which rows must match bit for bit.)"""
+    cases = [(9, 3, 30, 0.4), (7, 4, 70, 0.0), (12, 1, 10, 0.9), (6, 5, 40, 0.2)]
+    n_inf = n_fin = 0
+    for seed, (N, K, R, beta) in enumerate(cases):
+        c = case(40 + seed, N=N, K=K, R=R, beta=beta)
+        queries = np.arange(0, c["T"], 5)
+        r = run_layer(c, queries)
+        for b in range(c["B"]):
+            for g in range(c["Hkv"]):
+                for t in range(len(queries)):
+                    cs = [cc for cc in range(N) if r["cand"][t, cc]]
+                    vals = sorted((float(r["zhat"][b, g, t, cc]) for cc in cs), reverse=True)
+                    got = float(r["margin"][b, g, t])
+                    if len(vals) <= K:
+                        assert got == math.inf, "margin must be +inf with at most K candidates"
+                        n_inf += 1
+                        continue
+                    n_fin += 1
+                    assert abs(got - (vals[K - 1] - vals[K])) <= 1e-12, "margin = K-th minus (K+1)-th score"
+                    chosen = [int(x) for x in r["idx"][b, g, t] if x >= 0]
+                    left = [cc for cc in cs if cc not in chosen]
+                    lo_in = min(float(r["zhat"][b, g, t, cc]) for cc in chosen)
+                    hi_out = max(float(r["zhat"][b, g, t, cc]) for cc in left)
+                    assert abs(got - (lo_in - hi_out)) <= 1e-12, "margin = lowest chosen minus highest left out"
+    assert n_inf > 0 and n_fin > 0, "the cases must cover both kinds of row"
+
+
 def pin_topk_ties_and_padding():
     c = case(12, N=7, K=4, R=70, beta=0.0)
     c["q"][:] = 0.0

@@ -270,3 +270,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_wait_limit_setting(lib):
+    """The failure-handling hook keeps one process-wide setting: it returns the previous
+    value, and a value below one restores the default (2^22 polls)."""
+    default = 1 << 22
+    assert lib.lcr_set_wait_limit(5) == default
+    assert lib.lcr_set_wait_limit(0) == 5
+    assert lib.lcr_set_wait_limit(-3) == default
+    assert lib.lcr_set_wait_limit(0) == default

@@ -4,7 +4,8 @@ The graph is replayed several times, with fresh tail queries and hidden states
 copied into the captured buffers and unrelated eager work between replays;
 every replay must equal the eager call on the same inputs bit for bit (the
 kernels are deterministic, and they clear nothing with memset, so a replay has
-nothing to redo).
+nothing to redo). The first and the last replay are also checked against the
+fp64 oracle on the inputs copied back from the device.
 """
 import numpy as np
 import pytest
@@ -12,7 +13,8 @@ import torch
 
 import learned_chunk_routed_amd as lcr
 from lcr_inputs import get_config, route_inputs
-from gpu_util import to_dev
+from oracle import route as O
+from gpu_util import to_dev, f64, check_selection, max_err, OUT_TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -69,3 +71,25 @@ def test_decode_step_graph_replays_match_eager():
         assert torch.equal(got[1], zsel), f"replay {rep}: zsel"
         assert torch.equal(got[2], out[:, :, slots]), f"replay {rep}: output"
         assert bool(torch.isfinite(got[2].float()).all()), f"replay {rep}: non-finite output"
+        if rep in (0, 3):
+            _replay_against_oracle(cfg, q, k, v, x, A, Bm, i_tail, got, rep)
+
+
+def _replay_against_oracle(cfg, q, k, v, x, A, Bm, i_tail, got, rep):
+    """The replayed step's selection and output against the oracle on the same bits."""
+    ref = O.route_layer(f64(q), f64(k), f64(v), f64(x), f64(A), f64(Bm), K=cfg.K, R=cfg.R, beta=cfg.beta,
+                        scale=cfg.scale, queries=i_tail)
+    idx_gpu = got[0].cpu().numpy().astype(np.int64)
+    same = check_selection(idx_gpu, ref, cfg.K, f"graph replay {rep}")
+    zref = O.gather_zsel(ref["z"], idx_gpu, cfg.G)
+    o_ref = ref["o"].copy()
+    diff_t = np.nonzero(~same.all(axis=(0, 1)))[0]
+    if len(diff_t):
+        qr = f64(q)[:, :, O.slot_of(i_tail[diff_t])]
+        o_ref[:, :, diff_t], _ = O.routed_attention(qr, f64(k), f64(v), idx_gpu[:, :, diff_t], zref[:, :, diff_t],
+                                                    cfg.R, cfg.scale, i_tail[diff_t])
+    o_err = max_err(f64(got[2]), o_ref)
+    fin = np.isfinite(zref)
+    z_err = max_err(f64(got[1])[fin], zref[fin])
+    print(f"    replay {rep}: idx_same={int(same.sum())}/{same.size} o_err={o_err:.2e} z_err={z_err:.2e}", flush=True)
+    assert o_err < OUT_TOL["bf16"] and z_err < 5e-5 * max(1.0, np.abs(zref[fin]).max())

@@ -79,6 +79,22 @@ def _topk_one_short(zhat, cand, K):
     return np.concatenate([idx, pad], axis=-1), margin
 
 
+def _margin_next_pair(zhat, cand, K):
+    idx, margin = _orig["select_topk"](zhat, cand, K)
+    _, m2 = _orig["select_topk"](zhat, cand, K + 1)
+    return idx, np.where(np.isfinite(margin), m2, margin)
+
+
+def _margin_scaled(zhat, cand, K):
+    idx, margin = _orig["select_topk"](zhat, cand, K)
+    return idx, margin * 1e6
+
+
+def _margin_zero_when_few(zhat, cand, K):
+    idx, margin = _orig["select_topk"](zhat, cand, K)
+    return idx, np.where(np.isfinite(margin), margin, 0.0)
+
+
 def _group_mean(z, G):
     B, Hq, n, N = z.shape
     return z.reshape(B, Hq // G, G, n, N).mean(axis=2)
@@ -159,6 +175,9 @@ MUTATIONS = {
     "chunk logit uses the group maximum": ("gather_zsel", _zsel_group_max),
     "ties go to the larger index": ("select_topk", _topk_larger_index_wins),
     "one chunk short": ("select_topk", _topk_one_short),
+    "margin taken one rank too deep": ("select_topk", _margin_next_pair),
+    "margin scaled": ("select_topk", _margin_scaled),
+    "margin zero instead of +inf with few candidates": ("select_topk", _margin_zero_when_few),
     "group mean instead of maximum": ("group_max", _group_mean),
     "group uses its first head only": ("group_max", _group_first_head),
     "pooling includes the mask slot": ("chunk_summary_from_mask", _summary_all_slots),
