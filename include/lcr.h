@@ -205,6 +205,27 @@ int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, con
                          void* stream);
 
 /*
+ * lcr_routed_attention for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, semantics and results as lcr_routed_attention,
+ * without ws/ws_bytes: where the plan needs workspace (decode-sized problems
+ * keep partial results), it uses a static device array of
+ * LCR_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs on
+ * until the process ends (its device address is looked up on the first call on
+ * each device; nothing is allocated or freed by the call). Every call on one
+ * GPU shares that array: calls that overlap in time on the same GPU (different
+ * streams, or threads) race and give wrong results; calls ordered on one
+ * stream are safe. The array needs no clearing (every partial a call reads is
+ * written by that call first). Errors: as lcr_routed_attention, and
+ * LCR_ERR_UNSUPPORTED when lcr_workspace_bytes(LCR_OP_ROUTED_ATTENTION, ...)
+ * exceeds LCR_NOALLOC_SCRATCH_BYTES.
+ */
+#define LCR_NOALLOC_SCRATCH_BYTES (8u << 20)
+int lcr_routed_attention_noalloc(const lcr_dims* dims, const void* q, const void* k, const void* v,
+                                 const int32_t* idx, const float* zsel, int K, int radius, float scale,
+                                 int q0, int nq, void* o, float* lse, void* stream);
+
+/*
  * Gradients of lcr_routed_attention with the chosen chunks held fixed ("The 172x
  * Speedup Has an Evidence Budget", section "How learned routing controls what
  * the model can read": chunk membership is not differentiable; the router is

@@ -12,6 +12,7 @@ LCR_OK, LCR_ERR_ARG, LCR_ERR_DTYPE, LCR_ERR_WORKSPACE, LCR_ERR_HIP, LCR_ERR_UNSU
 LCR_F32, LCR_BF16 = 0, 1
 OP_CHUNK_SUMMARY, OP_ROUTE_SCORE_TOPK, OP_ROUTED_ATTENTION, OP_SWA_ATTENTION = 0, 1, 2, 3
 OP_ROUTED_ATTENTION_BACKWARD, OP_ROUTE_SCORE_BACKWARD = 4, 5
+LCR_NOALLOC_SCRATCH_BYTES = 8 << 20   # static scratch of lcr_routed_attention_noalloc
 
 
 class Dims(ctypes.Structure):
@@ -33,6 +34,7 @@ SIGNATURES = {
     "lcr_route_score_topk": (_i, [_pd, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _f, _f, _i, _i, _i, _i,
                                   _vp, _vp, _vp, _sz, _vp]),
     "lcr_routed_attention": (_i, [_pd, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "lcr_routed_attention_noalloc": (_i, [_pd, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _i, _vp, _vp, _vp]),
     "lcr_routed_attention_backward": (_i, [_pd, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _i, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lcr_route_score_backward": (_i, [_pd, _vp, _vp, _vp, _vp, _i, _i, _vp, _f, _f, _i, _i, _i, _vp, _vp, _vp, _vp,

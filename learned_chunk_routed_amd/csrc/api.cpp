@@ -109,6 +109,24 @@ int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, con
                                             radius, scale, q0, nq, o, lse, ws, (hipStream_t)stream));
 }
 
+int lcr_routed_attention_noalloc(const lcr_dims* dims, const void* q, const void* k, const void* v,
+                                 const int32_t* idx, const float* zsel, int K, int radius, float scale, int q0,
+                                 int nq, void* o, float* lse, void* stream) {
+  const int st = check_routed_attention(dims, q, k, v, idx, zsel, K, radius, scale, q0, nq, o);
+  if (st != LCR_OK) return st;
+  if (nq == 0) return LCR_OK;
+  const RouteDims dm = to_route_dims(dims);
+  const AttnPlan plan = plan_routed_attention(dm, K, radius, nq);
+  if (plan.lds > routed_lds_limit()) return LCR_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (plan.ws > 0) {
+    if (plan.ws > routed_scratch_bytes()) return LCR_ERR_UNSUPPORTED;
+    if (routed_scratch(&ws) != hipSuccess) return LCR_ERR_HIP;
+  }
+  return hip_status(launch_routed_attention(dm, plan, q, k, v, K > 0 ? idx : nullptr, K > 0 ? zsel : nullptr, K,
+                                            radius, scale, q0, nq, o, lse, ws, (hipStream_t)stream));
+}
+
 int lcr_routed_attention_backward(const lcr_dims* dims, const void* q, const void* k, const void* v,
                                   const int32_t* idx, const float* zsel, int K, int radius, float scale, int q0,
                                   int nq, const void* o, const float* lse, const void* dO, float* dq, float* dk,

@@ -32,6 +32,7 @@
 // Sliding-window attention uses the same tile machinery with 16 consecutive
 // slots of one head per tile and a band mask.
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -2331,6 +2332,39 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
 // ---------------------------------------------------------------- host side
 
 static size_t align256a(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------- static scratch
+// For lcr_routed_attention_noalloc (callers that cannot allocate device memory):
+// the partial results of decode-sized plans go to this file-scope device array
+// instead of a caller workspace. Each GPU the library runs on holds its own copy
+// until the process ends. Host code must not pass the array's name to a kernel
+// (on the host it is only a stand-in): its device address is looked up once per
+// device with hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+size_t routed_scratch_bytes() { return kScratchBytes; }
+
+hipError_t routed_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {   // first call on this device, which is current
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return hipSuccess;
+}
 
 // Polls before a wait on an LDS counter gives up, read at every launch.
 static constexpr int kDefaultWaitLimit = 1 << 22;

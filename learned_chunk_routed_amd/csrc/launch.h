@@ -62,6 +62,11 @@ struct AttnPlan {
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq);
 // polls before a wait on an LDS counter gives up (< 1: the default); returns the previous value
 int set_wait_limit(int polls);
+// the static scratch of lcr_routed_attention_noalloc: its size, and its device
+// address on the current device (looked up on the first call per device)
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+size_t routed_scratch_bytes();
+hipError_t routed_scratch(void** out);
 size_t routed_lds_limit();
 hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& plan, const void* q,
                                    const void* k, const void* v, const int32_t* idx,

@@ -280,3 +280,19 @@ def test_wait_limit_setting(lib):
     assert lib.lcr_set_wait_limit(0) == 5
     assert lib.lcr_set_wait_limit(-3) == default
     assert lib.lcr_set_wait_limit(0) == default
+
+
+def test_noalloc_rejects_plans_beyond_the_scratch(lib):
+    """lcr_routed_attention_noalloc checks on the host that the plan's partials fit its
+    static scratch; a decode-sized plan of 1,000 queries (one partial per row, 14.8 MB)
+    does not, and is rejected before anything is enqueued."""
+    d = dims(N=2048)
+    K, R, nq = 32, 256, 1000
+    need = lib.lcr_workspace_bytes(_lib.OP_ROUTED_ATTENTION, d, 0, 0, K, R, nq)
+    assert need > _lib.LCR_NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(256)   # never dereferenced: the call is rejected on the host
+    rc = lib.lcr_routed_attention_noalloc(d, p, p, p, p, p, K, R, 0.1, 0, nq, p, None, None)
+    assert rc == _lib.LCR_ERR_UNSUPPORTED
+    assert lib.lcr_routed_attention_noalloc(d, p, p, p, p, p, K, R, 0.1, 0, 0, p, None, None) == _lib.LCR_OK
+    assert lib.lcr_routed_attention_noalloc(d, None, p, p, p, p, K, R, 0.1, 0, nq, p, None, None) == \
+        _lib.LCR_ERR_ARG
