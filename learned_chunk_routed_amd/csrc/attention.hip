@@ -793,7 +793,7 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
 // ---------------------------------------------------------------- routed attention, prefill (bf16)
 //
 // Same tiles and algebra as routed_attention_kernel, with the work of a block
-// split between one producer wave and kPfCons consumer waves so that no wave
+// split between one producer wave and kCons consumer waves so that no wave
 // waits for another one's progress except through a pool of chunk halves:
 //  - setup (all waves): the list of chunks the block's queries need (the window
 //    range first, then the rest ascending), per list position a mask of the
@@ -810,11 +810,8 @@ __global__ __launch_bounds__(WAVES * 64) void routed_attention_kernel(RoutedPara
 //    it still needs, and K is free again long before V. The chunk logit of a
 //    lane's next selected chunk is loaded from zsel one visit ahead, so LDS
 //    holds only the pool and the position tables.
-// A consumer stays under 128 VGPRs, so 16 waves fit a CU (four per SIMD to hide
-// the S -> softmax -> PV chain of each wave).
-constexpr int kPfCons = 15;             // consumer waves
-constexpr int kPfWaves = kPfCons + 1;   // + the producer
-constexpr int kPfQB = 2 * kPfCons;      // queries per block
+// Chunks in the block's window range take the masked softmax only where some
+// lane's window covers part of the chunk; every other visit takes the lean one.
 
 
 
@@ -843,14 +840,13 @@ __device__ __forceinline__ float tile_softmax(f32x4 sacc[4], int mode, int lo, i
   const float m_cand = mode == 1 ? max2(m_old, mb) : (mode == 2 ? max2(m_old, zc) : m_old);
   const float m_new = m_cand > m_old + 8.f ? m_cand : m_old;
   const float base = mode == 2 ? mb : (mode == 1 ? m_new : 0.f);
-  float e[16];
   float rs = 0.f;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      e[4 * mt + i] = fast_exp2(fmaf(sacc[mt][i], sl2, -base));
-      rs += e[4 * mt + i];
+      sacc[mt][i] = fast_exp2(fmaf(sacc[mt][i], sl2, -base));   // in place: no second set of registers
+      rs += sacc[mt][i];
     }
   rs = col_sum(rs);
   const float alpha = mode == 0 ? 1.f : fast_exp2(m_old - m_new);
@@ -871,7 +867,7 @@ __device__ __forceinline__ float tile_softmax(f32x4 sacc[4], int mode, int lo, i
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int mt = 2 * ks + (h >> 1), i0 = 2 * (h & 1);
-      wv[h] = pack2_bf16(e[4 * mt + i0] * scale, e[4 * mt + i0 + 1] * scale);
+      wv[h] = pack2_bf16(sacc[mt][i0] * scale, sacc[mt][i0 + 1] * scale);
     }
     pf[ks] = __builtin_bit_cast(s16x8, wv);
   }
@@ -893,6 +889,29 @@ __device__ __forceinline__ void s_tiles(const bf16_t* buf, const QFrag<D, 1>* q,
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t][mt] = mfma16(a, q[t].f[ks][0], acc[t][mt]);
     }
+  }
+}
+
+// The same for one tile, with the lane's K offsets derived in place from an asm
+// mbcnt (which the compiler cannot merge with another) instead of being kept live
+// across the chunk loop, where registers are short. Row 16 mt + l % 16 shares its
+// swizzle with row l % 16 (period 16 for d = 128, 8 row pairs for d = 64), so the
+// four m-tiles differ by immediate offsets.
+template <int D>
+__device__ __forceinline__ void s_tile_lean(const bf16_t* buf, const QFrag<D, 1>& q, f32x4 acc[4]) {
+  typedef TileLayout<D, true> TL;
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const int L16 = ln & 15, g16 = ln >> 4;
+  const bf16_t* rowp = buf + L16 * D;
+  const int sw = TL::swz_k(L16);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const bf16_t* pk = rowp + (((4 * ks + g16) ^ sw) << 3);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(load8(pk + 16 * mt * D), q.f[ks][0], acc[mt]);
   }
 }
 
@@ -976,10 +995,37 @@ __device__ __forceinline__ int lds_load_rel(int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <int D, int NH>
-__global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedParams p) {
+// Shape of the pooled prefill kernel: TPW 16-column tiles (2 queries x 8 head rows
+// each) per consumer wave. One tile: 15 consumers under 128 VGPRs (16 waves, four per
+// SIMD). Two tiles: 11 consumers under 168 VGPRs (12 waves, three per SIMD), 44
+// queries per block, so each chunk the block loads serves more queries.
+template <int TPW> struct PfCfg;
+template <> struct PfCfg<1> {
+  static constexpr int kProd = 1;
+  static constexpr int kCons = 15;
+  typedef unsigned Mask;
+};
+template <> struct PfCfg<2> {
+  static constexpr int kProd = 1;
+  static constexpr int kCons = 11;
+  typedef unsigned long long Mask;
+};
+template <int TPW> constexpr int pf_waves() { return PfCfg<TPW>::kCons + PfCfg<TPW>::kProd; }
+template <int TPW> constexpr int pf_qblock() { return 2 * TPW * PfCfg<TPW>::kCons; }
+
+template <int D, int NH, int TPW>
+__global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(RoutedParams p) {
   typedef TileLayout<D, true> TL;
+  typedef typename PfCfg<TPW>::Mask MaskT;
   static_assert(TL::KE == TL::VE, "K and V halves share one pool");
+  constexpr int kCons = PfCfg<TPW>::kCons;
+  constexpr int kProd = PfCfg<TPW>::kProd;   // producer waves: producer r loads positions j = r (mod kProd)
+  constexpr int kWaves = kCons + kProd;
+  constexpr int NHP = NH / kProd;             // pool entries of each producer
+  static_assert(NH % kProd == 0, "the pool splits evenly among the producers");
+  constexpr int QB = pf_qblock<TPW>();        // queries per block
+  constexpr int WB = 2 * TPW;                 // mask bits (queries) per consumer wave
+  static_assert(QB <= 8 * (int)sizeof(MaskT), "one mask bit per query of the block");
   constexpr int HE = TL::KE;                   // elements per half (the K or the V of a chunk)
   constexpr int NI = D / 8;                    // DMA instructions per half
   constexpr int HF = (63 / NI) < NH ? (63 / NI) : NH;   // halves in flight
@@ -988,103 +1034,92 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = p.Hq / p.Hkv;
   bf16_t* kvb = reinterpret_cast<bf16_t*>(smem);
-  int* pos_chunk = reinterpret_cast<int*>(smem + (size_t)NH * HE * sizeof(bf16_t));   // [N]
-  unsigned* pos_mask = reinterpret_cast<unsigned*>(pos_chunk + p.N);                  // [N]
-  short* pos_of = reinterpret_cast<short*>(pos_mask + p.N);                           // [N]
+  MaskT* pos_mask = reinterpret_cast<MaskT*>(smem + (size_t)NH * HE * sizeof(bf16_t));   // [N]
+  int* pos_chunk = reinterpret_cast<int*>(pos_mask + p.N);                              // [N]
+  short* pos_of = reinterpret_cast<short*>(pos_chunk + p.N);                             // [N]
   // after setup, the same bytes hold per position the pool entries of its K (byte 2j) and V (2j + 1)
   unsigned char* pos_half = reinterpret_cast<unsigned char*>(pos_of);
   __shared__ int s_n;
-  __shared__ int s_landed;           // halves landed: K of position j is half 2j, V half 2j + 1
+  // halves landed per producer: position j is producer j % kProd's (j / kProd)-th, its K the
+  // producer's half 2 (j / kProd), its V half 2 (j / kProd) + 1
+  __shared__ int s_landed[kProd];
   __shared__ int s_rem[NH];          // consumers still to finish the half held by a pool entry
   __shared__ int s_fail;
-  __shared__ int s_nlo[kPfQB];       // per query: selected chunks below the block's window range
-  __shared__ int s_nin[kPfQB];       // ... and inside it
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
-  const int nqb = (p.nq + kPfQB - 1) / kPfQB;
+  const int nqb = (p.nq + QB - 1) / QB;
   const int tile = xcd_tile(nqb * p.B * p.Hkv);   // (batch-head, query block), batch-head major
   if (tile < 0) return;
   const int bg = tile / nqb, b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const int tb0 = (tile - bg * nqb) * kPfQB;
+  const int tb0 = (tile - bg * nqb) * QB;
   const long long L = (long long)p.N * kSlots;
   const long long Tcont = (long long)p.N * kContent;
   const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (size_t)bg * L * D;
   const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (size_t)bg * L * D;
-  constexpr int NT = 64 * kPfWaves;
+  constexpr int NT = 64 * kWaves;
 
   // ---- setup: chunk list and per-position query masks
-  if (tid == 0) {
-    s_landed = 0;
-    s_fail = 0;
-  }
+  if (tid == 0) s_fail = 0;
+  if (tid < kProd) s_landed[tid] = 0;
   if (tid < NH) s_rem[tid] = 0;
-  if (tid < kPfQB) {
-    s_nlo[tid] = 0;
-    s_nin[tid] = 0;
-  }
   for (int c = tid; c < p.N; c += NT) pos_of[c] = 0;
   __syncthreads();
-  const int t_last = min(tb0 + kPfQB, p.nq) - 1;
+  const int t_last = min(tb0 + QB, p.nq) - 1;
   // the block's window range: chunks in the window of any of its queries
   const int cw0 = (int)(max(0LL, (long long)p.q0 + tb0 - p.R) / kContent);
   const int cw1 = (int)(min(Tcont - 1, (long long)p.q0 + t_last + p.R) / kContent);
   for (int c = cw0 + tid; c <= cw1; c += NT) pos_of[c] = 1;
-  for (int e = tid; e < kPfQB * p.K; e += NT) {
+  for (int e = tid; e < QB * p.K; e += NT) {
     const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
     const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
-    if (c >= 0 && c < p.N) {
-      pos_of[c] = 1;
-      if (c < cw0) atomicAdd(&s_nlo[qi], 1);
-      else if (c <= cw1) atomicAdd(&s_nin[qi], 1);
-    }
+    if (c >= 0 && c < p.N) pos_of[c] = 1;
   }
   __syncthreads();
   if (w == 0) {
-    // list order: the window range first (every block's heavy positions up front), then
-    // the other chunks ascending, so that concurrently running blocks walk the remote
-    // chunks in step and share them in L2
+    // list order: ascending, so that concurrently running blocks walk the remote chunks
+    // in step and share them in L2, and each query meets its selected chunks in the
+    // order of its zsel row
     int base = 0;
-    auto append = [&](int c, bool f) {
+    for (int c0 = 0; c0 < p.N; c0 += 64) {
+      const int c = c0 + lane;
+      const bool f = c < p.N && pos_of[c] != 0;
       const unsigned long long m = __ballot(f);
       const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
       if (f) {
         pos_chunk[pos] = c;
-        pos_mask[pos] = 0u;
+        pos_mask[pos] = MaskT(0);
         pos_of[c] = (short)pos;
       }
       base += __popcll(m);
-    };
-    for (int c0 = cw0; c0 <= cw1; c0 += 64) {
-      const int c = c0 + lane;
-      append(c, c <= cw1 && pos_of[c] != 0);
-    }
-    for (int c0 = 0; c0 < p.N; c0 += 64) {
-      const int c = c0 + lane;
-      append(c, c < p.N && (c < cw0 || c > cw1) && pos_of[c] != 0);
     }
     if (lane == 0) s_n = base;
   }
   __syncthreads();
   const int n = s_n;
-  for (int e = tid; e < kPfQB * p.K; e += NT) {
+  for (int e = tid; e < QB * p.K; e += NT) {
     const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
     const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
-    if (c >= 0 && c < p.N) atomicOr(&pos_mask[pos_of[c]], 1u << qi);
+    if (c >= 0 && c < p.N) atomicOr(&pos_mask[pos_of[c]], MaskT(1) << qi);
   }
-  for (int qi = w; qi < kPfQB; qi += kPfWaves) {
+  for (int qi = w; qi < QB; qi += kWaves) {
     const int t = tb0 + qi;
     if (t >= p.nq) continue;
     const long long i = (long long)p.q0 + t;
     const int c0 = (int)(max(0LL, i - p.R) / kContent), c1 = (int)(min(Tcont - 1, i + p.R) / kContent);
-    for (int c = c0 + lane; c <= c1; c += 64) atomicOr(&pos_mask[pos_of[c]], 1u << qi);
+    for (int c = c0 + lane; c <= c1; c += 64) atomicOr(&pos_mask[pos_of[c]], MaskT(1) << qi);
   }
   __syncthreads();
 
-  if (w == kPfCons) {
-    // ---------------- producer
+  if (w >= kCons) {
+    // ---------------- producer r = w - kCons: positions j = r, r + kProd, ... into its own
+    // NHP entries of the pool (several producers keep more loads in flight than one
+    // wave's vmcnt allows)
     // Its instructions go ahead of the consumers' on the shared SIMD: the whole block
     // runs at the pace of its loads, so their issue must not wait behind softmax work.
     __builtin_amdgcn_s_setprio(3);
+    const int r = __builtin_amdgcn_readfirstlane(w - kCons);   // wave-uniform: entry numbers stay scalar
+    const int e0 = r * NHP;
+    int* landed = &s_landed[r];
     int told = 0;   // landed halves already published (monotonic)
     bool ok = true;
     int voffk[4], voffv[4];
@@ -1095,33 +1130,39 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
     }
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)kvb);
-    // publish the halves below hh2 - HF + 1 once at most HF - 1 of this wave's loads are in flight
+    constexpr int HFP = HF < NHP ? HF : NHP;   // this producer's halves in flight
+    // publish the halves below hh2 - HFP + 1 once at most HFP - 1 of this wave's loads are in flight
     auto publish_landed = [&](int hh2) {
-      if (hh2 >= HF && hh2 - HF + 1 > told) {
-        wait_vm<(HF - 1) * NI>();
+      if (hh2 >= HFP && hh2 - HFP + 1 > told) {
+        wait_vm<(HFP - 1) * NI>();
         compiler_fence();
-        if (lane == 0) lds_store_rel(&s_landed, hh2 - HF + 1);
-        told = hh2 - HF + 1;
+        if (lane == 0) lds_store_rel(landed, hh2 - HFP + 1);
+        told = hh2 - HFP + 1;
       }
     };
-    // Any free entry takes the next half. Entries seen free stay known (only this wave
-    // fills them), so the counts are read again only when none is known free. Before
-    // waiting for one, everything issued is awaited and published, so that the
+    // Any free entry of its own takes the next half. Entries seen free stay known (only
+    // this wave fills them), so the counts are read again only when none is known free.
+    // Before waiting for one, everything issued is awaited and published, so that the
     // consumers that hold the pool can finish. Returns -1 when the wait gives up or
     // another wave has failed.
-    unsigned known_free = NH == 32 ? ~0u : (1u << NH) - 1u;
+    const unsigned mine_all = ((1u << NHP) - 1u) << e0;
+    unsigned known_free = mine_all;
+    auto free_entries = [&]() -> unsigned {
+      const bool own = lane >= e0 && lane < e0 + NHP;
+      return (unsigned)__ballot(own && lds_load_rel(&s_rem[own ? lane : e0]) == 0);
+    };
     auto acquire = [&](int hx) -> int {
       if (known_free == 0u) {
-        known_free = (unsigned)__ballot(lane < NH && lds_load_rel(&s_rem[lane < NH ? lane : 0]) == 0);
+        known_free = free_entries();
         if (known_free == 0u) {
           wait_vm<0>();
           compiler_fence();
-          if (lane == 0) lds_store_rel(&s_landed, hx);
+          if (lane == 0) lds_store_rel(landed, hx);
           told = hx;
           int it = 0;
           for (; it < p.spin && known_free == 0u; ++it) {
             __builtin_amdgcn_s_sleep(1);
-            known_free = (unsigned)__ballot(lane < NH && lds_load_rel(&s_rem[lane < NH ? lane : 0]) == 0);
+            known_free = free_entries();
           }
           if (known_free == 0u || lds_load_rel(&s_fail) != 0) return -1;
         }
@@ -1131,21 +1172,22 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
       return e;
     };
     // Chunks and consumer counts of 64 positions are read lane-parallel up front.
+    int hl = 0;   // this producer's halves issued so far
     for (int base = 0; base < n && ok; base += 64) {
       const int pj = base + lane < n ? base + lane : n - 1;
       const int pcl = pos_chunk[pj];
-      const unsigned pml = pos_mask[pj];
+      const MaskT pml = pos_mask[pj];
       int ul = 0;
 #pragma unroll
-      for (int cw = 0; cw < kPfCons; ++cw) ul += ((pml >> (2 * cw)) & 3u) != 0u ? 1 : 0;
+      for (int cw = 0; cw < kCons; ++cw) ul += ((pml >> (WB * cw)) & ((MaskT(1) << WB) - 1)) != 0 ? 1 : 0;
       const int cnt = min(64, n - base);
-      for (int jj = 0; jj < cnt; ++jj) {
+      for (int jj = (r - base % kProd + kProd) % kProd; jj < cnt; jj += kProd) {
         const int hk = 2 * (base + jj);
         const int users = __builtin_amdgcn_readlane(ul, jj);
         const size_t off = (size_t)__builtin_amdgcn_readlane(pcl, jj) * kSlots * D;
         // K, then V, each into an entry of its own: K is released once its users have
         // formed S, well before they are done with V
-        const int ek = acquire(hk);
+        const int ek = acquire(hl);
         if (ek < 0) {
           ok = false;
           break;
@@ -1155,9 +1197,10 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
           pos_half[hk] = (unsigned char)ek;
         }
         compiler_fence();
-        publish_landed(hk);
+        publish_landed(hl);
         dma_half_fast<D>(kg + off, lds0 + (uint32_t)(ek * HE * 2), voffk);
-        const int ev = acquire(hk + 1);
+        ++hl;
+        const int ev = acquire(hl);
         if (ev < 0) {
           ok = false;
           break;
@@ -1167,56 +1210,73 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
           pos_half[hk + 1] = (unsigned char)ev;
         }
         compiler_fence();
-        publish_landed(hk + 1);
+        publish_landed(hl);
         dma_half_fast<D>(vg + off, lds0 + (uint32_t)(ev * HE * 2), voffv);
+        ++hl;
       }
     }
     wait_vm<0>();
     compiler_fence();
     if (lane == 0) {
-      if (ok) lds_store_rel(&s_landed, 2 * n);
+      if (ok) lds_store_rel(landed, hl);
       else lds_store_rel(&s_fail, 1);
     }
     return;
   }
 
-  // ---------------- consumer w: queries 2w and 2w + 1 of the block, one 16-row tile
+  // ---------------- consumer w: queries WB w .. WB w + WB - 1 of the block; tile t holds
+  // queries WB w + 2 t and WB w + 2 t + 1 (lane column: query qq of the tile, head hh)
   const int qq = (lane & 15) >> 3, hh = lane & 7;
   const int h = g * G + hh;
-  const int qb = 2 * w + qq;                 // this lane's query in the block
-  const int tq = tb0 + qb;
-  const int iq = p.q0 + tq;                  // content indices fit in 32 bits (N < 32768 on this path)
-  const bool rv = tq < p.nq && hh < G;
   const int R32 = (int)min((long long)p.R, Tcont);   // a wider radius selects the same keys
-  QFrag<D, 1> qf;
-  load_qfrag<bf16_t, D, 1>(qf, rv ? reinterpret_cast<const bf16_t*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D
-                                  : nullptr, lane);
-  f32x4 acc[D / 16];
+  QFrag<D, 1> qf[TPW];
+  f32x4 acc[TPW][D / 16];
+  float mrow[TPW], lrow[TPW], znext[TPW];
+  int ptr[TPW];
+  bool rv[TPW];
+  // zsel row of this lane's query in tile 0; tile t's row is zoff0 + 2 K t (a lane whose
+  // tile-t query is past nq never advances, so only its first read needs the clamp below)
+  int zoff0 = 0;
+  const int iq0 = p.q0 + tb0 + WB * w + qq;    // tile t's query is iq0 + 2 t (content indices fit in 32 bits)
 #pragma unroll
-  for (int dm = 0; dm < D / 16; ++dm) acc[dm] = zero4();
-  float mrow = kNegBig, lrow = 0.f;
-  int ptr = 0;   // selected chunks of this lane's query visited so far
-  const int nlo = s_nlo[qb], nin = s_nin[qb];
-  // the chunk logits of this lane's row stay in HBM / L2: the one for the next selected
-  // chunk is loaded a visit ahead (rows past the tile's queries or heads read a valid row)
-  const float* zrow = p.zsel + (((size_t)b * p.Hq + (hh < G ? h : g * G)) * p.nq + (tq < p.nq ? tq : p.nq - 1)) * p.K;
-  // the v-th selected chunk visited: the list walks the window range, then the chunks
-  // below it, then those above, each ascending, while zsel is ascending
-  auto zsel_slot = [&](int v) {
-    const int ks = v < nin ? nlo + v : (v < nin + nlo ? v - nin : v);
-    return ks < p.K ? ks : p.K - 1;
-  };
-  float znext = p.K > 0 ? zrow[zsel_slot(0)] : 0.f;
-  // landed halves known to this wave: the count is read again only when it falls short
-  int seen = 0;
-  auto await = [&](int need) -> bool {
+  for (int t = 0; t < TPW; ++t) {
+    const int tq = iq0 + 2 * t - p.q0;
+    rv[t] = tq < p.nq && hh < G;
+    load_qfrag<bf16_t, D, 1>(qf[t], rv[t] ? reinterpret_cast<const bf16_t*>(p.q) +
+                                                (((size_t)b * p.Hq + h) * L + slot_of_i(iq0 + 2 * t)) * D
+                                          : nullptr, lane);
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) acc[t][dm] = zero4();
+    mrow[t] = kNegBig;
+    lrow[t] = 0.f;
+    ptr[t] = 0;
+    // the chunk logits of this lane's row stay in HBM / L2: the one for the next selected
+    // chunk (the list is ascending, as is each zsel row) is loaded a visit ahead; rows
+    // past the block's queries or heads read a valid row
+    const int zo = (int)((((size_t)b * p.Hq + (hh < G ? h : g * G)) * p.nq + (tq < p.nq ? tq : p.nq - 1)) * p.K);
+    if (t == 0) zoff0 = zo;
+    znext[t] = p.K > 0 ? p.zsel[zo] : 0.f;
+  }
+  // landed halves of each producer known to this wave: a count is read again only when it
+  // falls short. Half hv (0: K, 1: V) of position j is producer j % kProd's half
+  // 2 (j / kProd) + hv.
+  int seen[kProd];
+#pragma unroll
+  for (int r = 0; r < kProd; ++r) seen[r] = 0;
+  auto await = [&](int j, int hv) -> bool {
+    const int r = j % kProd, need = 2 * (j / kProd) + hv + 1;
     int it = 0;
-    while (seen < need) {
-      seen = lds_load_rel(&s_landed);
-      if (seen >= need) break;
+    int sr = 0;
+#pragma unroll
+    for (int x = 0; x < kProd; ++x) sr = x == r ? seen[x] : sr;
+    while (sr < need) {
+      sr = lds_load_rel(&s_landed[r]);
+      if (sr >= need) break;
       if (++it >= p.spin || lds_load_rel(&s_fail) != 0) return false;
       __builtin_amdgcn_s_sleep(1);
     }
+#pragma unroll
+    for (int x = 0; x < kProd; ++x) seen[x] = x == r ? sr : seen[x];
     compiler_fence();
     return true;
   };
@@ -1229,74 +1289,98 @@ __global__ __launch_bounds__(64 * kPfWaves) void routed_prefill_kernel(RoutedPar
   bool failed = false;
   for (int base = 0; base < n && !failed; base += 64) {
     const int pl = base + lane < n ? base + lane : n - 1;
-    const unsigned pm = base + lane < n ? pos_mask[pl] : 0u;
+    const unsigned wbl = base + lane < n ? (unsigned)((pos_mask[pl] >> (WB * w)) & ((MaskT(1) << WB) - 1)) : 0u;
     const int pc = pos_chunk[pl];
-    unsigned long long mine = __ballot(((pm >> (2 * w)) & 3u) != 0u);
+    unsigned long long mine = __ballot(wbl != 0u);
     while (mine != 0ull) {
       const int bit = __builtin_ctzll(mine);
       mine &= mine - 1ull;
       const int j = base + bit;
       const int c = __builtin_amdgcn_readlane(pc, bit);
-      const unsigned bits = (unsigned)__builtin_amdgcn_readlane((int)pm, bit) >> (2 * w);
-      // per lane: window keys, selected chunk, or nothing
-      const bool qa = ((bits >> qq) & 1u) != 0u;
-      const int rel = iq - c * kContent;   // query index relative to the chunk's first key
-      const bool win = rel + R32 >= 0 && rel - R32 <= kContent - 1;
-      const int mode = (!qa || !rv) ? 0 : (win ? 1 : 2);
-      const int lo = mode == 1 ? max(0, rel - R32) : 0;
-      const int hi = mode == 1 ? min(kContent - 1, rel + R32) : kContent - 1;
-      const float zc = znext * kLog2e;
-      if (qa && !win) {
-        ++ptr;
-        znext = zrow[zsel_slot(ptr)];   // lands while this chunk is processed
-      }
-      const bool anywin = __ballot(mode == 1) != 0ull;
-      if (!await(2 * j + 1)) {
+      const unsigned wb = (unsigned)__builtin_amdgcn_readlane((int)wbl, bit);   // this wave's queries on c
+      const bool inr = c >= cw0 && c <= cw1;     // inside the block's window range (uniform)
+      const int last = (TPW == 2 && (wb & 12u) != 0u) ? 1 : 0;   // last active tile (uniform)
+      if (!await(j, 0)) {
         failed = true;
         break;
       }
       const int ek = pos_half[2 * j];   // written by the producer before the landed count covered it
-      f32x4 sacc[1][4];
-      s_tiles<D, 1>(kvb + ek * HE, &qf, sacc, lane);
-      release(ek);
-      s16x8 pf[1][2];
-      const float alpha = anywin ? tile_softmax<true>(sacc[0], mode, lo, hi, zc, p.sl2, g16, mrow, lrow, pf[0])
-                                 : tile_softmax<false>(sacc[0], mode, lo, hi, zc, p.sl2, g16, mrow, lrow, pf[0]);
-      if (__ballot(alpha != 1.f) != 0ull) {
+      int ev = -1;
+      // tile by tile: S, softmax, then P V, so that only one tile's P is live; K is released
+      // after the last tile's S, V after its P V
 #pragma unroll
-        for (int dm = 0; dm < D / 16; ++dm)
+      for (int t = 0; t < TPW; ++t) {
+        const unsigned tb = (wb >> (2 * t)) & 3u;
+        if (tb == 0u) continue;                  // uniform: neither query of the tile uses c
+        // per lane: window keys (mode 1), selected chunk (2) or nothing (0); a window lane
+        // whose window covers only part of the chunk needs per-key bounds (partial)
+        const bool qa = ((tb >> qq) & 1u) != 0u;
+        bool win = false;
+        int lo = 0, hi = kContent - 1;
+        if (inr) {
+          const int rel = iq0 + 2 * t - c * kContent;   // query index relative to the chunk's first key
+          win = rel + R32 >= 0 && rel - R32 <= kContent - 1;
+          if (win && qa && rv[t]) {
+            lo = max(0, rel - R32);
+            hi = min(kContent - 1, rel + R32);
+          }
+        }
+        const int mode = (!qa || !rv[t]) ? 0 : (win ? 1 : 2);
+        const bool partial = inr && __ballot(lo > 0 || hi < kContent - 1) != 0ull;
+        const float zc = znext[t] * kLog2e;
+        if (qa && !win) {
+          ++ptr[t];
+          znext[t] = p.zsel[zoff0 + 2 * p.K * t + min(ptr[t], p.K - 1)];   // lands while this chunk is processed
+        }
+        f32x4 sacc[4];
+        s_tile_lean<D>(kvb + ek * HE, qf[t], sacc);
+        if (t == last) release(ek);
+        s16x8 pf[2];
+        const float alpha = partial ? tile_softmax<true>(sacc, mode, lo, hi, zc, p.sl2, g16, mrow[t], lrow[t], pf)
+                                    : tile_softmax<false>(sacc, mode, lo, hi, zc, p.sl2, g16, mrow[t], lrow[t], pf);
+        if (__ballot(alpha != 1.f) != 0ull) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[dm][i] *= alpha;
+          for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][dm][i] *= alpha;
+        }
+        if (ev < 0) {
+          if (!await(j, 1)) {
+            failed = true;
+            break;
+          }
+          ev = pos_half[2 * j + 1];
+        }
+        pv_tiles<D, 1>(kvb + ev * HE, &pf, &acc[t]);
+        if (t == last) release(ev);
       }
-      if (!await(2 * j + 2)) {
-        failed = true;
-        break;
-      }
-      const int ev = pos_half[2 * j + 1];
-      pv_tiles<D, 1>(kvb + ev * HE, pf, &acc);
-      release(ev);
+      if (failed) break;
     }
   }
   if (failed && lane == 0) lds_store_rel(&s_fail, 1);
 
   // ---- results (NaN rows when this wave's walk was cut short by a wait that gave up)
-  if (failed) {
-    mrow = __builtin_nanf("");
-    lrow = mrow;
 #pragma unroll
-    for (int dm = 0; dm < D / 16; ++dm) acc[dm] = f32x4{mrow, mrow, mrow, mrow};
-  }
-  if (rv) {
-    const float inv = 1.f / lrow;
-    bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D;
+  for (int t = 0; t < TPW; ++t) {
+    if (failed) {
+      mrow[t] = __builtin_nanf("");
+      lrow[t] = mrow[t];
 #pragma unroll
-    for (int dm = 0; dm < D / 16; ++dm) {
-      float v4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v4[i] = acc[dm][i] * inv;
-      store4<bf16_t>(orow + 16 * dm + 4 * g16, v4);
+      for (int dm = 0; dm < D / 16; ++dm) acc[t][dm] = f32x4{mrow[t], mrow[t], mrow[t], mrow[t]};
     }
-    if (p.lse != nullptr && g16 == 0) p.lse[((size_t)b * p.Hq + h) * p.nq + tq] = (mrow + __log2f(lrow)) * kLn2;
+    if (rv[t]) {
+      const float inv = 1.f / lrow[t];
+      bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq0 + 2 * t)) * D;
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm) {
+        float v4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = acc[t][dm][i] * inv;
+        store4<bf16_t>(orow + 16 * dm + 4 * g16, v4);
+      }
+      if (p.lse != nullptr && g16 == 0)
+        p.lse[((size_t)b * p.Hq + h) * p.nq + (iq0 + 2 * t - p.q0)] = (mrow[t] + __log2f(lrow[t])) * kLn2;
+    }
   }
 }
 
@@ -2401,10 +2485,14 @@ static size_t routed_lds(const RouteDims& dm, int K, int qblock, int waves) {
 
 // LDS of routed_prefill_kernel: the pool of nh K-or-V halves and the per-position
 // tables (chunk, query mask, position of each chunk).
-static size_t prefill_lds(const RouteDims& dm, int nh) {
-  const size_t b = (size_t)nh * 64 * dm.d * 2 + (size_t)dm.N * (4 + 4 + 2);
+static size_t prefill_lds(const RouteDims& dm, int nh, int tpw) {
+  const size_t mask = tpw == 1 ? sizeof(PfCfg<1>::Mask) : sizeof(PfCfg<2>::Mask);
+  const size_t b = (size_t)nh * 64 * dm.d * 2 + (size_t)dm.N * (mask + 4 + 2);
   return (b + 15) & ~(size_t)15;
 }
+
+// tiles per consumer wave of the pooled prefill kernel
+static constexpr int kPfTiles = 2;
 
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   AttnPlan pl;
@@ -2458,13 +2546,13 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   if (pl.kind == 0 && pl.nsplit == 1 && dm.dtype == 1 && dm.N < 32768) {
     // bf16 prefill: producer / consumer kernel with the largest pool of halves that fits
     for (int nh : {9, 8, 6, 4}) {
-      const size_t lds = prefill_lds(dm, nh);
+      const size_t lds = prefill_lds(dm, nh, kPfTiles);
       if (lds <= routed_lds_limit()) {
         pl.kind = 2;
         pl.nbuf = nh;
-        pl.waves = kPfWaves;
-        pl.tiles = 2;
-        pl.qblock = kPfQB;
+        pl.tiles = kPfTiles;
+        pl.waves = kPfTiles == 1 ? pf_waves<1>() : pf_waves<2>();
+        pl.qblock = kPfTiles == 1 ? pf_qblock<1>() : pf_qblock<2>();
         pl.lds = lds;
         break;
       }
@@ -2517,11 +2605,12 @@ static hipError_t launch_decode_t(const RouteDims& dm, const AttnPlan& pl, const
 
 template <int D, int NH>
 static hipError_t launch_prefill_t(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
-  auto kern = routed_prefill_kernel<D, NH>;
+  constexpr int TPW = kPfTiles;
+  auto kern = routed_prefill_kernel<D, NH, TPW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
   if (e != hipSuccess) return e;
-  const int tiles = (prm.nq + kPfQB - 1) / kPfQB * dm.B * dm.Hkv;
-  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * kPfWaves), pl.lds, st, prm);
+  const int tiles = (prm.nq + pf_qblock<TPW>() - 1) / pf_qblock<TPW>() * dm.B * dm.Hkv;
+  hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * pf_waves<TPW>()), pl.lds, st, prm);
   return hipGetLastError();
 }
 
