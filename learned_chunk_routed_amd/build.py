@@ -1,6 +1,6 @@
 """Build liblcr.so (HIP kernels for gfx950 + the C ABI) in-tree.
 
-Usage: python -m learned_chunk_routed_amd.build [-v]
+Usage: python -m learned_chunk_routed_amd.build [-v] [--sanitized]
 
 Every HIP translation unit is compiled with hipcc for gfx950 only, with
 packed-fp32 instructions disabled; the host-only validation unit is compiled
@@ -65,5 +65,52 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     return OUT
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same sources, for
+# the CPU tests of the C ABI (argument validation, planners, workspace sizes). Only the
+# host code is instrumented; the GPU code is built as usual and never runs under it.
+SAN_BUILD = os.path.join(BUILD, "sanitized")
+SAN_OUT = os.path.join(SAN_BUILD, "liblcr_sanitized.so")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer"]
+CLANGXX = os.environ.get("CLANGXX", "/opt/rocm/bin/amdclang++")
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime (it carries the UBSan handlers too) that a
+    process must preload to load the sanitized library."""
+    r = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, text=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return path
+
+
+def build_sanitized(verbose: bool = False, jobs: int = 4) -> str:
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    flags = [f for f in HIP_FLAGS if f != "-O3"] + ["-O1", "-g"] + SAN_HOST
+    jobs_list, objs = [], []
+    for src in HIP_SOURCES:
+        obj = os.path.join(SAN_BUILD, src + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        jobs_list.append([HIPCC] + flags + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(SAN_BUILD, src + ".o")
+        jobs_list.append([CLANGXX, "-O1", "-g", "-std=c++17", "-fPIC", "-fsanitize=address,undefined",
+                          "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"),
+                          "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs_list))
+    tmp = SAN_OUT + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-shared-libsan"] + SAN_HOST + ["-o", tmp] + objs,
+         verbose)
+    os.replace(tmp, SAN_OUT)
+    return SAN_OUT
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
