@@ -2119,6 +2119,194 @@ __global__ __launch_bounds__(64) void routed_decode_kernel(RoutedParams p) {
   }
 }
 
+// bf16 variant of routed_decode_kernel with the same entries, runs and partials:
+// a chunk's K fragments (the A operand of S^T = K Q^T, row-major in HBM like the
+// operand) go straight into registers and only its V passes through LDS (for the
+// transposing reads), so a block holds 2 x 16 KB of LDS instead of 2 x 32 KB. The
+// next chunk's V is loaded into the other LDS buffer when a chunk starts, its K
+// right after S has consumed the current K registers: both are in flight during the
+// softmax and P V. (Blocks of four waves with short runs merged in LDS, to keep
+// more chunks in flight per CU, measured slower: the gather of scattered 16 KB
+// chunks from a cache larger than the 256 MB MALL is bound by HBM, not by loads in
+// flight.)
+template <int D>
+__global__ __launch_bounds__(64) void routed_decode_kv_kernel(RoutedParams p) {
+  typedef TileLayout<D, true> TL;
+  constexpr int KS = D / 32;
+  constexpr int HE = TL::VE;                 // elements of one V half
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* vbufs = reinterpret_cast<bf16_t*>(smem);                                  // [2][64][D] swizzled V
+  const int G = p.Hq / p.Hkv;
+  float* zs = reinterpret_cast<float*>(smem + (size_t)2 * HE * sizeof(bf16_t));     // [2][G][K]
+  const int lane = threadIdx.x, g16 = lane >> 4, L16 = lane & 15;
+  const int bg = blockIdx.y, b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int tb0 = 2 * blockIdx.x;
+  const long long L = (long long)p.N * kSlots;
+  const long long Tcont = (long long)p.N * kContent;
+  const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (size_t)bg * L * D;
+  const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v) + (size_t)bg * L * D;
+
+  // selections of the two queries: lane k holds entry k
+  int s0 = -1, s1 = -1;
+  if (p.K > 0) {   // uniform; idx may be NULL when K = 0
+    const int kl = lane < p.K ? lane : p.K - 1, t1 = tb0 + 1 < p.nq ? tb0 + 1 : tb0;
+    s0 = p.idx[((size_t)bg * p.nq + tb0) * p.K + kl];        // in bounds for every lane: no branch
+    s1 = p.idx[((size_t)bg * p.nq + t1) * p.K + kl];
+    if (lane >= p.K || s0 >= p.N) s0 = -1;
+    if (lane >= p.K || tb0 + 1 >= p.nq || s1 >= p.N) s1 = -1;
+  }
+  const int t_last = min(tb0 + 2, p.nq) - 1;
+  const long long i_first = (long long)p.q0 + tb0, i_last = (long long)p.q0 + t_last;
+  const int cw0 = (int)(max(0LL, i_first - p.R) / kContent);
+  const int cw1 = (int)(min(Tcont - 1, i_last + p.R) / kContent);
+  const int e_end = min(p.nent, (int)blockIdx.z * p.epb + p.epb);
+  // chunk of entry e, or -1 (wave-uniform); a chunk in several places belongs to one entry
+  auto chunk_of = [&](int e) -> int {
+    int c;
+    if (e < p.K) {
+      c = __builtin_amdgcn_readlane(s0, e);
+      if (c >= cw0 && c <= cw1) c = -1;
+    } else if (e < 2 * p.K) {
+      c = __builtin_amdgcn_readlane(s1, e - p.K);
+      if (c >= 0 && ((c >= cw0 && c <= cw1) || __ballot(s0 == c) != 0ull)) c = -1;
+    } else {
+      c = cw0 + (e - 2 * p.K);
+      if (c > cw1) c = -1;
+    }
+    return c;
+  };
+  auto next_entry = [&](int e, int& c) -> int {
+    c = -1;
+    for (; e < e_end; ++e) {
+      c = chunk_of(e);
+      if (c >= 0) return e;
+    }
+    return e_end;
+  };
+
+  // this lane's row: query qq of the tile, head hh of the group
+  const int qq = (lane & 15) >> 3, hh = lane & 7;
+  const int h = g * G + hh;
+  const int t = tb0 + qq;
+  const bool rv = t < p.nq && hh < G;
+  const long long iq = (long long)p.q0 + t;
+  const size_t rows = (size_t)p.B * p.Hq * p.nq;
+  float* pp = p.part + ((size_t)blockIdx.z * rows + ((size_t)b * p.Hq + h) * p.nq + t) * (D + 4);
+  int c;
+  int e = next_entry((int)blockIdx.z * p.epb, c);
+  if (c < 0) {
+    if (rv && g16 == 0) {
+      pp[D] = kNegBig;
+      pp[D + 1] = 0.f;
+    }
+    return;
+  }
+  int voffv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) voffv[u] = dma_voff<D>(true, u, lane);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)vbufs);
+  // K fragments of chunk cc: lane holds key 16 mt + l % 16, d = 32 ks + 8 (l / 16) + {0..7}
+  s16x8 kf[4][KS];
+  auto load_k = [&](int cc) {
+    const bf16_t* kc = kg + ((size_t)cc * kSlots + L16) * D + 8 * g16;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = load8(kc + 16 * mt * D + 32 * ks);
+  };
+  dma_half_fast<D>(vg + (size_t)c * kSlots * D, lds0, voffv);
+  load_k(c);
+
+  // the two queries' chunk logits into LDS and the query fragments
+  if (p.K > 0) {   // uniform; zsel may be NULL when K = 0
+    constexpr int kZPer = 16;   // 2 queries x G <= 8 heads x K <= 64 values over 64 lanes
+    const int nz = 2 * G * p.K;
+    float zv[kZPer];
+#pragma unroll
+    for (int j = 0; j < kZPer; ++j) {
+      if (64 * j < nz) {   // uniform
+        const int x = lane + 64 * j < nz ? lane + 64 * j : nz - 1;
+        const int xq = x / (G * p.K), rem = x - xq * G * p.K, xh = rem / p.K, xk = rem - xh * p.K;
+        const int tt = tb0 + xq < p.nq ? tb0 + xq : tb0;
+        zv[j] = p.zsel[(((size_t)b * p.Hq + g * G + xh) * p.nq + tt) * p.K + xk];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kZPer; ++j)
+      if (lane + 64 * j < nz) zs[lane + 64 * j] = zv[j] * kLog2e;
+  }
+  QFrag<D, 1> qf;
+  load_qfrag<bf16_t, D, 1>(qf, rv ? reinterpret_cast<const bf16_t*>(p.q) + (((size_t)b * p.Hq + h) * L + slot_of_i(iq)) * D
+                                  : nullptr, lane);
+
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) acc[dm] = zero4();
+  float m = kNegBig, l = 0.f;
+  int cur = 0;
+  for (;;) {
+    int cn;
+    const int en = next_entry(e + 1, cn);
+    wait_vm<0>();   // chunk c's K (registers) and V (LDS buffer cur) have landed
+    wait_lgkm0();   // and every read of the other V buffer (the previous chunk's) has returned
+    compiler_fence();
+    if (cn >= 0) dma_half_fast<D>(vg + (size_t)cn * kSlots * D, lds0 + (uint32_t)((cur ^ 1) * HE * 2), voffv);
+    // per lane: window keys, selected-chunk keys or nothing
+    const long long cf = (long long)c * kContent, cl = cf + kContent - 1;
+    const bool win = cf <= iq + p.R && cl >= iq - p.R;
+    const unsigned long long m0 = __ballot(s0 == c), m1 = __ballot(s1 == c);   // full-wave ballots
+    const unsigned long long mq = qq ? m1 : m0;
+    const int ksel = mq != 0ull ? __builtin_ctzll(mq) : -1;
+    int mode = win ? 1 : (ksel >= 0 ? 2 : 0);
+    if (!rv) mode = 0;
+    int lo = 0, hi = kContent - 1;
+    if (mode == 1) {
+      lo = (int)max(0LL, iq - p.R - cf);
+      hi = (int)min((long long)kContent - 1, iq + p.R - cf);
+    }
+    const bool partial = __ballot(lo > 0 || hi < kContent - 1) != 0ull;
+    const float zc = mode == 2 ? zs[(qq * G + hh) * p.K + ksel] : 0.f;
+    f32x4 sacc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      sacc[mt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc[mt] = mfma16(kf[mt][ks], qf.f[ks][0], sacc[mt]);
+    }
+    if (cn >= 0) load_k(cn);   // the K registers are free once the MFMAs above have read them
+    s16x8 pf[2];
+    const float alpha = partial ? tile_softmax<true>(sacc, mode, lo, hi, zc, p.sl2, g16, m, l, pf)
+                                : tile_softmax<false>(sacc, mode, lo, hi, zc, p.sl2, g16, m, l, pf);
+    if (__ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[dm][i] *= alpha;
+    }
+    pv_tiles<D, 1>(vbufs + cur * HE, &pf, &acc);
+    if (cn < 0) break;
+    e = en;
+    c = cn;
+    cur ^= 1;
+  }
+  wait_vm<0>();
+  if (!rv) return;
+  if (l > 0.f) {
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) {
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = acc[dm][i];
+      store4<float>(pp + 16 * dm + 4 * g16, v4);
+    }
+  }
+  if (g16 == 0) {
+    pp[D] = m;
+    pp[D + 1] = l;
+  }
+}
+
 // ---------------------------------------------------------------- sliding-window attention
 //
 // swa_kernel serves float32 inputs (three bf16 planes staged through registers);
@@ -2494,6 +2682,10 @@ static size_t prefill_lds(const RouteDims& dm, int nh, int tpw) {
 // tiles per consumer wave of the pooled prefill kernel
 static constexpr int kPfTiles = 2;
 
+// single-wave blocks the decode-sized plan aims at (about two per CU: 1,024 and
+// 2,048 measured slower, the combine then reads more partials)
+static constexpr long long kDecodeBlocks = 512;
+
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   AttnPlan pl;
   pl.nent = 0;
@@ -2524,7 +2716,7 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
       // single-wave blocks per CU), at least two chunks per block
       pl.kind = 1;
       const long long tiles = (long long)((nq + 1) / 2) * dm.B * dm.Hkv;
-      long long runs = (512 + tiles - 1) / (tiles > 0 ? tiles : 1);
+      long long runs = (kDecodeBlocks + tiles - 1) / (tiles > 0 ? tiles : 1);
       if (runs > nent / 2) runs = nent / 2;
       if (runs < 1) runs = 1;
       pl.epb = (int)((nent + runs - 1) / runs);
@@ -2538,7 +2730,9 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
     }
   }
   if (pl.kind == 1) {
-    pl.lds = (size_t)(dm.dtype == 1 ? 2 : 1) * routed_buf_bytes(dm.d, dm.dtype) + (size_t)2 * (dm.Hq / dm.Hkv) * K * 4;
+    // bf16: two V halves (K goes to registers); float32: one staged K + V buffer of three planes
+    pl.lds = (dm.dtype == 1 ? (size_t)2 * 64 * dm.d * 2 : routed_buf_bytes(dm.d, dm.dtype)) +
+             (size_t)2 * (dm.Hq / dm.Hkv) * K * 4;
   } else {
     pl.lds = routed_lds(dm, K, pl.qblock, pl.waves);
   }
@@ -2590,7 +2784,7 @@ static hipError_t launch_routed_d(const RouteDims& dm, const AttnPlan& pl, const
 
 template <typename T, int D>
 static hipError_t launch_decode_t(const RouteDims& dm, const AttnPlan& pl, const RoutedParams& prm, hipStream_t st) {
-  auto kern = routed_decode_kernel<T, D>;
+  auto kern = std::is_same<T, bf16_t>::value ? routed_decode_kv_kernel<D> : routed_decode_kernel<T, D>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
   if (e != hipSuccess) return e;
   dim3 grid((prm.nq + 1) / 2, dm.B * dm.Hkv, pl.nsplit);
