@@ -915,6 +915,32 @@ __device__ __forceinline__ void s_tile_lean(const bf16_t* buf, const QFrag<D, 1>
   }
 }
 
+// S^T of NT tiles sharing every K fragment read, with the lane offsets formed in
+// place as in s_tile_lean.
+template <int D, int NT>
+__device__ __forceinline__ void s_tiles_lean(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4]) {
+  typedef TileLayout<D, true> TL;
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const int L16 = ln & 15, g16 = ln >> 4;
+  const bf16_t* rowp = buf + L16 * D;
+  const int sw = TL::swz_k(L16);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[t][mt] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const bf16_t* pk = rowp + (((4 * ks + g16) ^ sw) << 3);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const s16x8 a = load8(pk + 16 * mt * D);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][mt] = mfma16(a, q[t].f[ks][0], acc[t][mt]);
+    }
+  }
+}
+
 // O^T += V^T P^T for NT tiles sharing every V^T fragment read (vbuf: a V half).
 // The swizzle XORs an even key into the 16-byte block index, so the offset of
 // rows r0 + 32 ks + 16 u and columns col + 16 dm is the unswizzled offset of
@@ -2423,13 +2449,16 @@ __global__ __launch_bounds__(512) void swa_kernel(SwaParams p) {
 
 // Sliding-window attention, bf16 inputs. A block of G waves (one head each, the
 // heads of one KV group) covers 32 consecutive slots: two 16-row tiles per wave,
-// so every V^T fragment of O^T += V^T P^T read from LDS serves both tiles (S^T =
-// K Q^T is formed one tile at a time, which keeps the wave's registers in bounds). The 64-slot K/V tiles of the band come into a
-// RING-deep LDS ring with direct-to-LDS loads (swizzled layout), RING - 1 tiles
-// ahead, issued by the first DW waves; a raw s_barrier per tile, after each
-// issuing wave has seen its own loads of that tile land, makes the tile visible
-// and frees the slot of the previous one (no register staging, and no barrier
-// that would wait for the loads still in flight). Rows of a partial last tile
+// so every K fragment of S^T = K Q^T and every V^T fragment of O^T += V^T P^T
+// read from LDS serves both tiles. The 64-slot K/V tiles of the band come into a
+// RING-deep LDS ring with direct-to-LDS loads (swizzled layout), issued by the
+// first DW waves; a raw s_barrier per tile, after each issuing wave has seen its
+// own loads of that tile land, makes the tile visible and frees the slot of the
+// tile before the previous one (no register staging, and no barrier that would
+// wait for the loads still in flight). The loop is software-pipelined by one
+// tile: while the softmax of tile j runs on the VALU, the MFMAs form S of tile
+// j + 1, interleaved with it instruction by instruction where both query tiles
+// are fully inside the window; then P V of tile j. Rows of a partial last tile
 // are read from the sequence's last row and masked out.
 template <int D, int DW, int RING>
 __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
@@ -2438,8 +2467,8 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
   constexpr int NI = D / 8;                 // 1 KB instructions per half
   constexpr int RPI = 512 / D, BPR = D / 8;
   constexpr int PER = 2 * NI / DW;          // instructions per issuing wave per tile
-  constexpr int PD = RING - 1;              // tiles issued ahead
-  static_assert((2 * NI) % DW == 0 && PD * PER < 64, "in-flight loads must fit the vmcnt counter");
+  // at most RING - 2 tiles of loads are in flight per issuing wave
+  static_assert(RING >= 3 && (2 * NI) % DW == 0 && (RING - 2) * PER < 64, "in-flight loads must fit the vmcnt counter");
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* kvb = reinterpret_cast<bf16_t*>(smem);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g16 = lane >> 4;
@@ -2477,21 +2506,17 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
   wait_vm<0>();
   // Full tiles: groups of four 1 KB loads with a uniform base (SGPRs) and per-lane
   // offsets that repeat every group (the swizzle period); the rare partial last
-  // tile reads its missing rows from the sequence's last row, with the lane index
-  // formed in place so that its addresses are not kept live across the loop.
+  // tile reads its missing rows from the sequence's last row. The lane index is
+  // formed in place so that no address is kept live across the loop.
   static_assert(PER % 4 == 0, "whole groups of four loads per wave");
-  int voff[2][4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    voff[0][u] = dma_voff<D>(false, u, lane);
-    voff[1][u] = dma_voff<D>(true, u, lane);
-  }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)kvb);
   auto issue = [&](int j) {
     if (w >= DW) return;
     const int kb = kb0 + 64 * j;
     const uint32_t lbuf = lds0 + (uint32_t)((j % RING) * BUFE * 2);
+    int ln;   // the lane index formed in place: no per-lane offsets live across the loop
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     if (kb + 64 <= L) {
 #pragma unroll
       for (int gi = 0; gi < PER / 4; ++gi) {
@@ -2503,12 +2528,10 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lg + u * 1024),
-                       "v"(is_v ? voff[1][u] : voff[0][u]), "s"(sg)
+                       "v"(dma_voff<D>(is_v, u, ln)), "s"(sg)
                        : "memory", "m0");
       }
     } else {
-      int ln;
-      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
       const int rows_valid = L - kb;
       bf16_t* buf = kvb + (j % RING) * BUFE;
       for (int u = 0; u < PER; ++u) {
@@ -2522,56 +2545,42 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
       }
     }
   };
-#pragma unroll
-  for (int jj = 0; jj < PD; ++jj)
-    if (jj < ntile) issue(jj);
-
-  for (int j = 0; j < ntile; ++j) {
-    const int kb = kb0 + 64 * j;
-    // this wave's share of tile j has landed (later tiles stay in flight) ...
+  // Tile t is made visible by arrive(t): this wave's loads of it have landed
+  // (tiles up to t + RING - 3 being issued), every wave's LDS reads before the
+  // barrier have returned, and tile t + RING - 2 goes into the slot of tile t - 2,
+  // which no wave reads any more (in the pipelined run below a wave reads tile
+  // t - 1 after arrive(t), so the slot of t - 1 is not yet free).
+  auto arrive = [&](int t) {
     if (w < DW) {
-      const int ahead = min(PD - 1, ntile - 1 - j);
-      if constexpr (PD >= 3) {
-        if (ahead >= 2) wait_vm<(PD >= 3 ? 2 : 0) * PER>();
-        else if (ahead == 1) wait_vm<PER>();
-        else wait_vm<0>();
-      } else if constexpr (PD == 2) {
-        if (ahead >= 1) wait_vm<PER>();
-        else wait_vm<0>();
-      } else {
-        wait_vm<0>();
-      }
+      const int ahead = min(t + RING - 3, ntile - 1) - t;
+      static_assert(RING <= 4, "at most one tile in flight beside the one awaited");
+      if (ahead >= 1) wait_vm<(RING >= 4 ? PER : 0)>();
+      else wait_vm<0>();
     }
-    // ... and every wave's LDS reads of tile j - 1 have returned
     wait_lgkm0();
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    if (j + PD < ntile) issue(j + PD);   // into the slot of tile j - 1
+    if (t + RING - 2 < ntile) issue(t + RING - 2);
+  };
+  // one K/V tile at the band's edges: S, masked softmax and P V of each query
+  // tile that sees it
+  auto edge_step = [&](int j) {
+    const int kb = kb0 + 64 * j;
     const bf16_t* buf = kvb + (j % RING) * BUFE;
     bool act[2];
+    s16x8 pf[2][2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int ts = t0 + 16 * tt;
       act[tt] = ts < L && kb <= ts + 15 + R && kb + 63 >= ts - R;   // wave-uniform
-    }
-    s16x8 pf[2][2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
       if (!act[tt]) continue;
-      // S one tile at a time (its scores are consumed right away); P V below shares
-      // every V^T fragment read between the two tiles
       f32x4 sacc[1][4];
-      s_tiles<D, 1>(buf, &qf[tt], sacc, lane);
-      const int ts = t0 + 16 * tt;
+      s_tiles_lean<D, 1>(buf, &qf[tt], sacc);
       const int mode = trow[tt] < L ? 1 : 0;
       const int lo = max(0, trow[tt] - R - kb);
       const int hi = min(63, min(L - 1, trow[tt] + R) - kb);
-      // a tile inside the window of all 16 rows (and of the sequence) needs no mask
-      const bool inside = kb >= ts + 15 - R && kb + 63 <= ts + R && kb + 63 < L && ts + 15 < L;
-      const float alpha =
-          inside ? tile_softmax<false, false>(sacc[0], mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt])
-                 : tile_softmax<true, false>(sacc[0], mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
+      const float alpha = tile_softmax<true, false>(sacc[0], mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
       if (__ballot(alpha != 1.f) != 0ull) {
 #pragma unroll
         for (int dm = 0; dm < D / 16; ++dm)
@@ -2582,6 +2591,63 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
     if (act[0] && act[1]) pv_tiles<D, 2>(buf + TL::KE, pf, acc);
     else if (act[0]) pv_tiles<D, 1>(buf + TL::KE, &pf[0], &acc[0]);
     else if (act[1]) pv_tiles<D, 1>(buf + TL::KE, &pf[1], &acc[1]);
+  };
+  // tiles jlo .. jhi lie inside the window of all 32 rows (and of the sequence)
+  const int jlo = max(0, (t0 + 31 - R - kb0 + 63) >> 6);   // ceiling of a quotient, numerator >= -63
+  int jhi = min(t0 + R, L - 1) - 63 - kb0;
+  jhi = jhi < 0 ? -1 : min(ntile - 1, jhi >> 6);
+  if (t0 + 31 >= L) jhi = -1;
+
+  for (int jj = 0; jj < RING - 2 && jj < ntile; ++jj) issue(jj);
+  int j = 0;
+  for (; j < ntile && j < jlo; ++j) {
+    arrive(j);
+    edge_step(j);
+  }
+  if (j <= jhi) {
+    // Pipelined run: S of tile j + 1 (every K fragment read serving both query
+    // tiles) is formed ahead of the softmax of tile j, whose VALU work can then
+    // run beside those MFMAs; then P V of tile j.
+    f32x4 sc[2][4], sn[2][4];
+    arrive(j);
+    s_tiles_lean<D, 2>(kvb + (j % RING) * BUFE, qf, sc);
+    for (; j <= jhi; ++j) {
+      const bf16_t* buf = kvb + (j % RING) * BUFE;
+      s16x8 pf[2][2];
+      float alpha[2];
+      const bool nx = j < jhi;
+      if (nx) arrive(j + 1);
+      // (after the run's last tile the products are formed once more on that tile
+      // and dropped, which keeps them and the softmax in one scheduling region)
+      s_tiles_lean<D, 2>(kvb + ((nx ? j + 1 : j) % RING) * BUFE, qf, sn);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        alpha[tt] = tile_softmax<false, false>(sc[tt], 1, 0, 63, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
+      // one MFMA, then a few softmax VALU instructions, in turn
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        if (__ballot(alpha[tt] != 1.f) != 0ull) {
+#pragma unroll
+          for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha[tt];
+        }
+      }
+      pv_tiles<D, 2>(buf + TL::KE, pf, acc);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sc[tt][mt] = sn[tt][mt];
+    }
+  }
+  for (; j < ntile; ++j) {
+    arrive(j);
+    edge_step(j);
   }
 
 #pragma unroll
@@ -2920,7 +2986,7 @@ template <int D>
 static hipError_t launch_swa_bf16(const SwaParams& prm, int G, hipStream_t st) {
   if (G >= 4) return launch_swa_bf16_t<D, 4, 4>(prm, G, st);
   if (G >= 2) return launch_swa_bf16_t<D, 2, 4>(prm, G, st);
-  if constexpr (D == 128) return launch_swa_bf16_t<D, 1, 2>(prm, G, st);
+  if constexpr (D == 128) return launch_swa_bf16_t<D, 1, 3>(prm, G, st);
   else return launch_swa_bf16_t<D, 1, 4>(prm, G, st);
 }
 

@@ -983,21 +983,43 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) zz[nt][i] = (ahi[nt][i] + ax[nt][i]) * scale - beta * t.hv[i];
   };
-  // every chunk row tile of the head, the next tile's loads in flight; wave w starts
+  // every chunk row tile of the head, the loads of the next tile (the next two where
+  // two query tiles leave the registers for a third buffer) in flight; wave w starts
   // at tile w so that the waves' atomic updates of the group maximum rarely meet
   auto sweep = [&](bool ranks, auto&& emit) {
-    TileBuf ta, tb;
     f32x4 zz[NT];
     auto tile_at = [&](int it) { return (w + it) % NMT; };
-    load_tile(tile_at(0), ta, ranks);
-    for (int it = 0; it < NMT; it += 2) {
-      if (it + 1 < NMT) load_tile(tile_at(it + 1), tb, ranks);
-      tile_scores(ta, zz);
-      emit(tile_at(it), ta, zz);
-      if (it + 1 < NMT) {
-        if (it + 2 < NMT) load_tile(tile_at(it + 2), ta, ranks);
-        tile_scores(tb, zz);
-        emit(tile_at(it + 1), tb, zz);
+    if constexpr (NT <= 2) {
+      TileBuf ta, tb, tc;
+      load_tile(tile_at(0), ta, ranks);
+      if (1 < NMT) load_tile(tile_at(1), tb, ranks);
+      for (int it = 0; it < NMT; it += 3) {
+        if (it + 2 < NMT) load_tile(tile_at(it + 2), tc, ranks);
+        tile_scores(ta, zz);
+        emit(tile_at(it), ta, zz);
+        if (it + 1 < NMT) {
+          if (it + 3 < NMT) load_tile(tile_at(it + 3), ta, ranks);
+          tile_scores(tb, zz);
+          emit(tile_at(it + 1), tb, zz);
+        }
+        if (it + 2 < NMT) {
+          if (it + 4 < NMT) load_tile(tile_at(it + 4), tb, ranks);
+          tile_scores(tc, zz);
+          emit(tile_at(it + 2), tc, zz);
+        }
+      }
+    } else {
+      TileBuf ta, tb;
+      load_tile(tile_at(0), ta, ranks);
+      for (int it = 0; it < NMT; it += 2) {
+        if (it + 1 < NMT) load_tile(tile_at(it + 1), tb, ranks);
+        tile_scores(ta, zz);
+        emit(tile_at(it), ta, zz);
+        if (it + 1 < NMT) {
+          if (it + 2 < NMT) load_tile(tile_at(it + 2), ta, ranks);
+          tile_scores(tb, zz);
+          emit(tile_at(it + 1), tb, zz);
+        }
       }
     }
   };

@@ -371,6 +371,10 @@ SWA_CASES = [
     ("bf16 d64 ragged", dict(B=2, Hq=6, Hkv=2, L=333, d=64, R=100, dtype="bf16")),
     # a sequence shorter than one 64-slot tile
     ("bf16 short", dict(B=1, Hq=4, Hkv=2, L=40, d=128, R=10, dtype="bf16")),
+    # one head per group (a single wave loads and computes: three-tile ring at d = 128),
+    # radius wide enough for runs of tiles inside every row's window
+    ("bf16 one head per group", dict(B=1, Hq=2, Hkv=2, L=1500, d=128, R=600, dtype="bf16")),
+    ("bf16 d64 one head per group", dict(B=1, Hq=2, Hkv=2, L=900, d=64, R=300, dtype="bf16")),
 ]
 
 
