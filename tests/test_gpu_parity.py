@@ -254,6 +254,57 @@ def test_route_layer_prefill_edge(case):
     route_parity(cfg, queries=queries, q0=q0, nq=nq, label=f"prefill {name}")
 
 
+def test_topk_exact_ties_many_chunks():
+    """Exact ties in the group maximum at N = 600, where the fused top-K first narrows each
+    query's keys to at most 128 candidates: chunk 2i + 1 has the summary and entropy of
+    chunk 2i, so every score occurs twice. The chosen set must be a top K of the oracle's
+    group maxima; where twins straddle the threshold, the smaller chunk is chosen (the
+    oracle's tie rule); rows whose K-th and (K+1)-th scores differ by more than 1e-3 match
+    the oracle exactly."""
+    B, Hq, Hkv, N, d, r, D, K, R, beta = 1, 8, 2, 600, 128, 16, 96, 31, 200, 0.5
+    G, L, T = Hq // Hkv, N * 64, N * 63
+    print(f"[case] top-K ties N={N} K={K} Hq={Hq} Hkv={Hkv}", flush=True)
+    rng = np.random.default_rng(2024)
+
+    def bf16(shape, std=1.0):
+        return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(torch.bfloat16)
+    q, x = bf16((B, Hq, L, d)), bf16((B, L, D))
+    A, Bm = bf16((D, r), 0.02), bf16((r, Hq * d), 0.02)
+    s = rng.standard_normal((B, Hq, N // 2, d)).repeat(2, axis=2).astype(np.float32)
+    H = (rng.random((B, Hq, N // 2)) * 4.0).repeat(2, axis=2).astype(np.float32)
+    idx, zsel = lcr.route_score_topk(q.cuda(), x.cuda(), A.cuda(), Bm.cuda(), torch.from_numpy(s).cuda(),
+                                     torch.from_numpy(H).cuda(), Hkv=Hkv, K=K, radius=R, beta=beta)
+    torch.cuda.synchronize()
+    queries = np.unique(np.concatenate([np.arange(0, 64), np.arange(T // 2, T // 2 + 64), np.arange(T - 64, T)]))
+    f = lambda t: t.float().numpy().astype(np.float64)
+    slots = O.slot_of(queries)
+    qt = O.routing_query(f(q)[:, :, slots], f(x)[:, slots], f(A), f(Bm))
+    zhat = O.group_max(O.route_scores(qt, s.astype(np.float64), H.astype(np.float64), beta, 1.0 / np.sqrt(d)), G)
+    cand = O.candidate_mask(queries, R, N)
+    ref_idx, margin = O.select_topk(zhat, cand, K)
+    got = idx.cpu().numpy()[:, :, queries].astype(np.int64)
+    straddle = 0
+    for b in range(B):
+        for g in range(Hkv):
+            for j in range(len(queries)):
+                row = got[b, g, j]
+                assert np.all(np.diff(row) > 0) and row.min() >= 0, "ascending distinct chunk ids"
+                chosen = np.zeros(N, bool)
+                chosen[row] = True
+                assert cand[j][row].all(), "only candidates"
+                z = zhat[b, g, j]
+                left = cand[j] & ~chosen
+                assert z[chosen].min() >= z[left].max() - 1e-4, "a top K of the group maxima"
+                for c in range(0, N, 2):   # twins straddling the threshold: the smaller id
+                    if cand[j][c] and cand[j][c + 1] and chosen[c] != chosen[c + 1]:
+                        straddle += 1
+                        assert chosen[c], f"twin {c + 1} chosen over {c}"
+                if margin[b, g, j] > 1e-3:
+                    assert np.array_equal(row, ref_idx[b, g, j]), "selection differs from the oracle"
+    print(f"    rows={B * Hkv * len(queries)} twins straddling the threshold: {straddle}", flush=True)
+    assert straddle > 0
+
+
 def _routed_plan_ws(cfg, K, nq):
     dims = lcr.make_dims(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d,
                          torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)
