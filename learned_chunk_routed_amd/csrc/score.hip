@@ -766,6 +766,50 @@ __device__ __forceinline__ int wave_topk(const uint32_t* key, int K, int lane, E
   return wave_topk_select<P>(key, K, theta, take_all, lane, emit);
 }
 
+// The same selection, narrowed first: the K-th largest of the 64 lane maxima is at
+// most the K-th largest key, so the keys at or above it hold the whole top K (ties
+// at the threshold included). Up to kNarrow of them are compacted in element order
+// into two keys per lane through buf (this wave's 2 kNarrow words of LDS) and the
+// selection runs on those; with more, on all keys. emit(slot, e, key) is called
+// for every chosen element e = 64 j + l, slots in element order.
+constexpr int kNarrow = 128;
+
+template <int P, typename Emit>
+__device__ __forceinline__ int wave_topk_narrow(const uint32_t* key, int K, int lane, uint32_t* buf, Emit emit) {
+  uint32_t lm[1][1] = {{key[0]}};
+#pragma unroll
+  for (int j = 1; j < P; ++j) lm[0][0] = max(lm[0][0], key[j]);
+  uint32_t thl;
+  bool tal;
+  wave_topk_thresholds<1, 1>(lm, K, &thl, &tal);
+  const uint32_t lq = tal ? 1u : max(thl, 1u);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const bool in = key[j] >= lq;
+    const unsigned long long m = __ballot(in);
+    const int pos = base + __popcll(m & lt);
+    if (in && pos < kNarrow) {
+      buf[pos] = key[j];
+      buf[kNarrow + pos] = 64 * j + lane;
+    }
+    base += __popcll(m);
+  }
+  if (base > kNarrow) return wave_topk<P>(key, K, lane, [&](int slot, int j) { emit(slot, 64 * j + lane, key[j]); });
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  uint32_t ck[2];
+  int ci[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int pos = 64 * jj + lane;
+    ck[jj] = pos < base ? buf[pos] : 0u;
+    ci[jj] = (int)buf[kNarrow + pos];
+  }
+  return wave_topk<2>(ck, K, lane, [&](int slot, int jj) { emit(slot, ci[jj], ck[jj]); });
+}
+
 // ---------------------------------------------------------------------------- 4. fused scoring (bf16)
 //
 // route_score3_kernel: for QT = 16 NT consecutive queries of one KV group,
@@ -793,9 +837,8 @@ constexpr int kRsWaves = 8;
 __host__ __device__ inline size_t rs3_keys(int NT, int N) { return (size_t)16 * NT * (N + 1) * 4; }
 __host__ __device__ inline size_t rs3_off_z(int NT, int N) { return ((size_t)16 * NT * N + 15) & ~(size_t)15; }
 __host__ __device__ inline size_t rs3_stage(int NT, int K) { return (size_t)kRsWaves * 16 * NT * K * 4; }
-// beyond 256 chunks the top-K first narrows each query's keys to at most 128
-// candidates, compacted through a per-wave list of 128 keys and 128 chunk ids
-constexpr int kRsCand = 128;
+// beyond 256 chunks the top-K first narrows each query's keys to at most kNarrow
+// candidates, compacted through a per-wave list of kNarrow keys and chunk ids
 __host__ __device__ inline bool rs3_filter(int N) { return N > 256; }
 __host__ __device__ inline size_t rs3_off_f(int NT, int N, int K, bool stage) {
   return (rs3_off_z(NT, N) + (stage ? rs3_stage(NT, K) : 0) + 15) & ~(size_t)15;
@@ -803,7 +846,7 @@ __host__ __device__ inline size_t rs3_off_f(int NT, int N, int K, bool stage) {
 // offset of the chosen lists: past the keys, or past ranks + staging rows (+ the
 // candidate lists) if longer
 __host__ __device__ inline size_t rs3_off_c(int NT, int N, int K, bool stage) {
-  const size_t over = rs3_off_f(NT, N, K, stage) + (rs3_filter(N) ? (size_t)kRsWaves * kRsCand * 8 : 0);
+  const size_t over = rs3_off_f(NT, N, K, stage) + (rs3_filter(N) ? (size_t)kRsWaves * kNarrow * 8 : 0);
   return ((rs3_keys(NT, N) > over ? rs3_keys(NT, N) : over) + 15) & ~(size_t)15;
 }
 __host__ __device__ inline size_t rs3_lds(int NT, int N, int K, bool stage) {
@@ -1091,7 +1134,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
       uint32_t thl[QW];
       bool tal[QW];
       wave_topk_thresholds<1, QW>(lm, K, thl, tal);
-      uint32_t* cbuf = reinterpret_cast<uint32_t*>(smem + rs3_off_f(NT, N, K, STAGE)) + w * 2 * kRsCand;
+      uint32_t* cbuf = reinterpret_cast<uint32_t*>(smem + rs3_off_f(NT, N, K, STAGE)) + w * 2 * kNarrow;
       const unsigned long long lt = (1ull << lane) - 1ull;
       bool fits = true;
 #pragma unroll
@@ -1103,20 +1146,20 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
           const bool in = key[qq][j] >= lq;
           const unsigned long long m = __ballot(in);
           const int pos = base + __popcll(m & lt);
-          if (in && pos < kRsCand) {
+          if (in && pos < kNarrow) {
             cbuf[pos] = key[qq][j];
-            cbuf[kRsCand + pos] = 64 * j + lane;
+            cbuf[kNarrow + pos] = 64 * j + lane;
           }
           base += __popcll(m);
         }
-        fits = fits && base <= kRsCand;   // wave-uniform
+        fits = fits && base <= kNarrow;   // wave-uniform
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int pos = 64 * jj + lane;
           ckey[qq][jj] = pos < base ? cbuf[pos] : 0u;
-          cidx[qq][jj] = (int)cbuf[kRsCand + pos];
+          cidx[qq][jj] = (int)cbuf[kNarrow + pos];
         }
         __builtin_amdgcn_wave_barrier();   // the next query's writes come after these reads
       }
@@ -1413,25 +1456,14 @@ __global__ __launch_bounds__(256) void score_small_kernel(const bf16_t* __restri
   float* s_l = reinterpret_cast<float*>(smem);
   float* zm = s_l + (size_t)G * 32 * D;
 
-  // 1. rows c0 .. c0 + 31 (clamped to N - 1) of every head's summaries into LDS:
-  //    LDS piece p of row `row` holds source piece p ^ (row & 15)
-  {
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)smem);
-    const int prow = lane / PR, pp = lane - prow * PR;
-    for (int ins = w; ins < G * IPH; ins += 4) {
-      const int hh = ins / IPH, r0 = (ins - hh * IPH) * RPI;
-      const int row = r0 + prow;
-      const int c = min(c0 + row, N - 1);
-      const float* sh = s + ((size_t)b * Hq + g * G + hh) * N * D;
-      const int voff = (c * D + ((pp ^ (row & 15)) << 2)) * 4;
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
-                       lds0 + (uint32_t)((hh * 32 + r0) * D * 4)),
-                   "v"(voff), "s"(sh)
-                   : "memory", "m0");
-    }
-  }
-  // 2. meanwhile: this wave's heads (w, w + 4) as B operands, and their entropies
+  // 1. wave w moves rows c0 .. c0 + 31 (clamped to N - 1) of its own heads' summaries
+  //    (heads w and w + 4) into LDS, each after that head's B operands and entropies:
+  //    it scores its first head while the second one's rows are still in flight, and
+  //    no wave waits for another one's loads. LDS piece p of row `row` holds source
+  //    piece p ^ (row & 15).
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)smem);
+  const int prow = lane / PR, pp = lane - prow * PR;
   const int nhw = G > w ? (G - w + 3) / 4 : 0;   // 0, 1 or 2 heads
   s16x8 qb[2][2][KS][2];                          // [head slot][query tile][k-step][plane]
   float hv[2][2][4];                              // [head slot][chunk tile][i]
@@ -1453,9 +1485,20 @@ __global__ __launch_bounds__(256) void score_small_kernel(const bf16_t* __restri
         const int c = c0 + 16 * mt + 4 * g16 + i;
         hv[hs][mt][i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
       }
+    if (hs < nhw) {
+      const float* sh = s + ((size_t)b * Hq + h) * N * D;
+#pragma unroll
+      for (int ii = 0; ii < IPH; ++ii) {
+        const int r0 = ii * RPI, row = r0 + prow;
+        const int c = min(c0 + row, N - 1);
+        const int voff = (c * D + ((pp ^ (row & 15)) << 2)) * 4;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
+                         lds0 + (uint32_t)((hh * 32 + r0) * D * 4)),
+                     "v"(voff), "s"(sh)
+                     : "memory", "m0");
+      }
+    }
   }
-  wait_vm<0>();
-  __syncthreads();
 
   // 3. scores of this wave's heads; the wave's maximum over them
   float zmx[2][2][4];
@@ -1469,6 +1512,10 @@ __global__ __launch_bounds__(256) void score_small_kernel(const bf16_t* __restri
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
     if (hs >= nhw) break;
+    // this head's rows and operands have landed: all of this wave's loads but the
+    // second head's rows (the last IPH issued) for the first head, all for the second
+    if (hs == 0 && nhw == 2) wait_vm<IPH>();
+    else wait_vm<0>();
     const int hh = w + 4 * hs, h = g * G + hh;
     f32x4 ahi[2][2], ax[2][2];
 #pragma unroll
@@ -1561,6 +1608,7 @@ __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict
   __shared__ int ccount[4];
   __shared__ int chosen[64];
   __shared__ int s_count;
+  __shared__ uint32_t nbuf[4][2 * kNarrow];   // per wave: the narrowed candidates
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long long row = blockIdx.x;
   const int t = (int)(row % nq);
@@ -1587,10 +1635,13 @@ __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict
     const bool cand = (c < N) & ((63LL * c + 62 < i - R) | (63LL * c > i + R));
     key[j] = cand ? order_key(zv[j]) : 0u;
   }
-  const int nw = wave_topk<P>(key, K, lane, [&](int slot, int j) {
-    ckey[64 * w + slot] = key[j];
-    cidx[64 * w + slot] = cw + 64 * j + lane;
-  });
+  auto keep = [&](int slot, int e, uint32_t kv) {
+    ckey[64 * w + slot] = kv;
+    cidx[64 * w + slot] = cw + e;
+  };
+  int nw;
+  if constexpr (P >= 8) nw = wave_topk_narrow<P>(key, K, lane, nbuf[w], keep);
+  else nw = wave_topk<P>(key, K, lane, [&](int slot, int j) { keep(slot, 64 * j + lane, key[j]); });
   if (lane == 0) ccount[w] = nw;
   __syncthreads();
   // 2. wave 0: the final K from the survivors (element 64 e + l = entry l of wave e's list: chunk order)
