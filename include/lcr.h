@@ -27,8 +27,8 @@
  *    kernels of the same call may already have been enqueued.
  *  - Limits: d in {64, 128}; 1 <= G <= 8; 0 <= K <= 64; radius >= 0.
  *  - The library keeps no state between calls (apart from the wait limit of
- *    lcr_set_wait_limit) and may be called from several host threads on
- *    different streams.
+ *    lcr_set_wait_limit and the tile order of lcr_set_tile_order) and may be
+ *    called from several host threads on different streams.
  */
 #ifndef LCR_H
 #define LCR_H
@@ -85,6 +85,17 @@ typedef enum {
  * calls enqueued after this returns. Returns the previous setting.
  */
 int lcr_set_wait_limit(int polls);
+
+/*
+ * Test hook for order independence. The tiled kernels (the pooled routed
+ * attention of prefill-sized problems, the query side of its backward and the
+ * fused bf16 scoring) map their blocks onto (batch, KV group, query block)
+ * tiles in an XCD-aware order; reversed != 0 walks the same tiles in the
+ * opposite order. No block depends on another, so every output is bit for bit
+ * the same either way; tests compare the two. Process-wide, for calls enqueued
+ * after this returns; returns the previous setting (0 or 1). Default 0.
+ */
+int lcr_set_tile_order(int reversed);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int lcr_version(void);

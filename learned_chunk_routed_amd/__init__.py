@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     route_layer_backward,
     workspace_bytes,
     set_wait_limit,
+    set_tile_order,
     make_dims,
     default_scale,
 )

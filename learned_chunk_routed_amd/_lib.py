@@ -27,6 +27,7 @@ SIGNATURES = {
     "lcr_version": (_i, []),
     "lcr_status_string": (ctypes.c_char_p, [_i]),
     "lcr_set_wait_limit": (_i, [_i]),
+    "lcr_set_tile_order": (_i, [_i]),
     "lcr_workspace_bytes": (_sz, [_i, _pd, _i, _i, _i, _i, _i]),
     "lcr_chunk_summary": (_i, [_pd, _vp, _vp, _f, _vp, _vp, _vp]),
     "lcr_chunk_summary_range": (_i, [_pd, _vp, _vp, _f, _i, _i, _vp, _vp, _vp]),

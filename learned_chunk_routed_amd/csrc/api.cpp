@@ -41,6 +41,8 @@ const char* lcr_status_string(int status) {
 
 int lcr_set_wait_limit(int polls) { return set_wait_limit(polls); }
 
+int lcr_set_tile_order(int reversed) { return set_tile_order(reversed); }
+
 size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, int radius, int nq) {
   if (check_dims(dims) != LCR_OK || K < 0 || nq < 0 || radius < 0) return 0;
   const RouteDims dm = to_route_dims(dims);

@@ -489,6 +489,7 @@ struct RoutedParams {
   int B, Hq, Hkv, N, K, R, q0, nq, nsplit;
   int nent, epb;  // decode-sized plan: entries per 2-query tile, entries per block
   int spin;       // polls before a wait on an LDS counter gives up (>= 1)
+  int rev;        // tiles in reversed order (results do not depend on it)
   float sl2;      // scale * log2(e)
 };
 
@@ -1074,7 +1075,7 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
   const int nqb = (p.nq + QB - 1) / QB;
-  const int tile = xcd_tile(nqb * p.B * p.Hkv);   // (batch-head, query block), batch-head major
+  const int tile = xcd_tile(nqb * p.B * p.Hkv, p.rev);   // (batch-head, query block), batch-head major
   if (tile < 0) return;
   const int bg = tile / nqb, b = bg / p.Hkv, g = bg - b * p.Hkv;
   const int tb0 = (tile - bg * nqb) * QB;
@@ -1438,6 +1439,7 @@ struct BwdQueryParams {
   float* cu;
   int B, Hq, Hkv, N, K, R, q0, nq;
   int spin;       // polls before a wait on an LDS counter gives up (>= 1)
+  int rev;        // tiles in reversed order (results do not depend on it)
   float scale;
 };
 
@@ -1467,7 +1469,7 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
   const int nqb = (p.nq + kBqQB - 1) / kBqQB;
-  const int tile = xcd_tile(nqb * p.B * p.Hkv);   // (batch-head, query block), batch-head major
+  const int tile = xcd_tile(nqb * p.B * p.Hkv, p.rev);   // (batch-head, query block), batch-head major
   if (tile < 0) return;
   const int bg = tile / nqb, b = bg / p.Hkv, g = bg - b * p.Hkv;
   const int tb0 = (tile - bg * nqb) * kBqQB;
@@ -2710,6 +2712,10 @@ static std::atomic<int> g_wait_limit{kDefaultWaitLimit};
 int set_wait_limit(int polls) { return g_wait_limit.exchange(polls >= 1 ? polls : kDefaultWaitLimit); }
 static int wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
 
+static std::atomic<int> g_tile_order{0};
+int set_tile_order(int reversed) { return g_tile_order.exchange(reversed != 0 ? 1 : 0); }
+int tile_order() { return g_tile_order.load(std::memory_order_relaxed); }
+
 // LDS bytes of the K/V staging buffers (all planes, all buffers).
 static size_t kv_lds_bytes(int d, int dtype) {
   const int np = dtype == 0 ? 3 : 1;
@@ -2906,6 +2912,7 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, cons
   prm.nent = pl.nent;
   prm.epb = pl.epb;
   prm.spin = wait_limit();
+  prm.rev = tile_order();
   prm.sl2 = scale * kLog2e;
   if (pl.kind == 2) return dm.d == 64 ? launch_prefill_d<64>(dm, pl, prm, st) : launch_prefill_d<128>(dm, pl, prm, st);
   if (pl.kind == 1) {
@@ -2963,6 +2970,7 @@ hipError_t launch_bwd_query_pool(const RouteDims& dm, const void* q, const void*
   prm.q0 = q0;
   prm.nq = nq;
   prm.spin = wait_limit();
+  prm.rev = tile_order();
   prm.scale = scale;
   return dm.d == 128 ? launch_bwd_query_pool_d<128>(prm, st) : launch_bwd_query_pool_d<64>(prm, st);
 }

@@ -38,10 +38,12 @@ constexpr float kNegBig = -1.0e30f;
 constexpr int kXcds = 8;
 __host__ __device__ __forceinline__ int xcd_per(int total) { return (total + kXcds - 1) / kXcds; }
 __host__ __device__ __forceinline__ int xcd_grid(int total) { return xcd_per(total) * kXcds; }
-__device__ __forceinline__ int xcd_tile(int total) {   // tile of this block, or -1 (nothing to do)
+// reversed != 0 walks the tiles in the opposite order (same blocks, same XCD
+// ranges mirrored): results do not depend on it, which tests check.
+__device__ __forceinline__ int xcd_tile(int total, int reversed = 0) {   // tile of this block, or -1
   const int bid = blockIdx.x;
   const int l = (bid % kXcds) * xcd_per(total) + bid / kXcds;
-  return l < total ? l : -1;
+  return l < total ? (reversed ? total - 1 - l : l) : -1;
 }
 
 // ---------------------------------------------------------------- conversions

@@ -62,6 +62,8 @@ struct AttnPlan {
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq);
 // polls before a wait on an LDS counter gives up (< 1: the default); returns the previous value
 int set_wait_limit(int polls);
+int set_tile_order(int reversed);
+int tile_order();
 // the static scratch of lcr_routed_attention_noalloc: its size, and its device
 // address on the current device (looked up on the first call per device)
 constexpr size_t kScratchBytes = (size_t)8 << 20;

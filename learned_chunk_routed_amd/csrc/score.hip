@@ -894,13 +894,13 @@ template <int D, int RP, int NT, int P, bool STAGE>
 __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bt, const float* __restrict__ upart, int nsplit,
     const bf16_t* __restrict__ sp, const float* __restrict__ H, float beta, float scale, int32_t* __restrict__ idx,
-    float* __restrict__ zsel, int B, int Hq, int Hkv, int N, int q0, int nq, int K, int R) {
+    float* __restrict__ zsel, int B, int Hq, int Hkv, int N, int q0, int nq, int K, int R, int rev) {
   constexpr int QT = 16 * NT, KS = D / 32, RK = RP / 32;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, g16 = lane >> 4, L16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqb = (nq + QT - 1) / QT;
-  const int tile = xcd_tile(nqb * B * Hkv);   // (batch-group, query block), batch-group major
+  const int tile = xcd_tile(nqb * B * Hkv, rev);   // (batch-group, query block), batch-group major
   if (tile < 0) return;
   const int bg = tile / nqb, b = bg / Hkv, g = bg - b * Hkv;
   const int G = Hq / Hkv;
@@ -1841,7 +1841,7 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
     if (e != hipSuccess) return e;                                                                               \
     hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * kRsWaves), lds, st, (const bf16_t*)q, ws.bt,      \
                        ws.upart, nsplit, ws.splanes, H, beta, scale, idx, zsel, dm.B, dm.Hq, dm.Hkv, dm.N, q0, nq, \
-                       K, radius);                                                                               \
+                       K, radius, tile_order());                                                                               \
   } while (0)
   if (dm.N <= 256) LCR_RS(3, 4);
   else if (dm.N <= 512) LCR_RS(3, 8);

@@ -67,6 +67,12 @@ def set_wait_limit(polls: int) -> int:
     return int(_lib.load().lcr_set_wait_limit(int(polls)))
 
 
+def set_tile_order(reversed: bool) -> int:
+    """Walk the tiles of the tiled kernels in reversed order (a test hook: outputs are
+    bit for bit the same either way). Process-wide; returns the previous setting."""
+    return int(_lib.load().lcr_set_tile_order(1 if reversed else 0))
+
+
 def _workspace(nbytes, device, ws=None):
     if nbytes == 0:
         return None

@@ -282,6 +282,15 @@ def test_wait_limit_setting(lib):
     assert lib.lcr_set_wait_limit(0) == default
 
 
+def test_tile_order_setting(lib):
+    """The order-independence hook: any nonzero value means reversed, the previous
+    setting comes back, and the default is the XCD-aware order (0)."""
+    assert lib.lcr_set_tile_order(7) == 0
+    assert lib.lcr_set_tile_order(1) == 1
+    assert lib.lcr_set_tile_order(0) == 1
+    assert lib.lcr_set_tile_order(0) == 0
+
+
 def test_noalloc_rejects_plans_beyond_the_scratch(lib):
     """lcr_routed_attention_noalloc checks on the host that the plan's partials fit its
     static scratch; a decode-sized plan of 1,000 queries (one partial per row, 14.8 MB)

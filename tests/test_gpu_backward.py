@@ -210,6 +210,24 @@ def test_backward_reproducible_and_empty_range():
     assert dz.numel() == 0 and not dq.any() and not dk.any() and not dv.any()
 
 
+def test_backward_tile_order_independence():
+    """The pooled query side of the backward gives the same bits when its blocks walk the
+    (KV group, query block) tiles in reversed order."""
+    cfg = get_config("prefill_16k", N=40, Hq=8, Hkv=2, K=6, R=64)
+    print("[case] backward tile order independence", flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, 0, cfg.T)
+    idx, zsel = selection(cfg, dr, 0, cfg.T)
+    a = run_gpu(cfg, inp, dr["dO"], idx, zsel, 0, cfg.T)
+    lcr.set_tile_order(True)
+    try:
+        b = run_gpu(cfg, inp, dr["dO"], idx, zsel, 0, cfg.T)
+    finally:
+        lcr.set_tile_order(False)
+    for x, y, n in zip(a, b, ("dq", "dk", "dv", "dzsel")):
+        assert np.array_equal(x, y), f"{n} differs with the tiles in reversed order"
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "prefill_16k"])
 def test_chunk_summary_backward(name):
     """Pooling backward: mask-slot rows of dq written, content rows of dk accumulated

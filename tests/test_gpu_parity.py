@@ -347,6 +347,30 @@ def test_determinism_and_decode_split_matches_prefill():
     assert max_err(f64(lc), f64(a["lse"][:, :, q0:])) < LSE_TOL["bf16"]
 
 
+def test_tile_order_independence():
+    """The tiled kernels (fused scoring, pooled routed attention) give the same bits when
+    their blocks walk the tiles in reversed order: no block depends on another or on the
+    order in which the hardware dispatches them. Same layer as the determinism test
+    (N = 128, 8/2 heads: the fused scoring and the pooled prefill plan)."""
+    cfg = get_config("tiny_fp32", N=128, Hq=8, Hkv=2, d=128, r=32, D=256, K=8, R=128, dtype="bf16")
+    print("[case] tile order independence of the tiled prefill kernels", flush=True)
+    assert _routed_plan_ws(cfg, cfg.K, cfg.T) == 0, "the whole-range call must take the pooled prefill plan"
+    inp = route_inputs(cfg)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    run = lambda: lcr.route_layer(dev["q"], dev["k"], dev["v"], dev["x"], dev["A"], dev["Bm"], K=cfg.K,
+                                  radius=cfg.R, scale=cfg.scale, want_lse=True)
+    a = run()
+    prev = lcr.set_tile_order(True)
+    try:
+        assert prev == 0
+        b = run()
+        torch.cuda.synchronize()
+    finally:
+        lcr.set_tile_order(False)
+    for key in ["s", "H", "idx", "zsel", "o", "lse"]:
+        assert torch.equal(a[key], b[key]), key
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_route_layer_fp32_prefill_plan(d):
     """float32 inputs at a size whose routed attention takes the block-per-query-range
