@@ -837,16 +837,9 @@ constexpr int kRsWaves = 8;
 __host__ __device__ inline size_t rs3_keys(int NT, int N) { return (size_t)16 * NT * (N + 1) * 4; }
 __host__ __device__ inline size_t rs3_off_z(int NT, int N) { return ((size_t)16 * NT * N + 15) & ~(size_t)15; }
 __host__ __device__ inline size_t rs3_stage(int NT, int K) { return (size_t)kRsWaves * 16 * NT * K * 4; }
-// beyond 256 chunks the top-K first narrows each query's keys to at most kNarrow
-// candidates, compacted through a per-wave list of kNarrow keys and chunk ids
-__host__ __device__ inline bool rs3_filter(int N) { return N > 256; }
-__host__ __device__ inline size_t rs3_off_f(int NT, int N, int K, bool stage) {
-  return (rs3_off_z(NT, N) + (stage ? rs3_stage(NT, K) : 0) + 15) & ~(size_t)15;
-}
-// offset of the chosen lists: past the keys, or past ranks + staging rows (+ the
-// candidate lists) if longer
+// offset of the chosen lists: past the keys, or past ranks + staging rows if longer
 __host__ __device__ inline size_t rs3_off_c(int NT, int N, int K, bool stage) {
-  const size_t over = rs3_off_f(NT, N, K, stage) + (rs3_filter(N) ? (size_t)kRsWaves * kNarrow * 8 : 0);
+  const size_t over = rs3_off_z(NT, N) + (stage ? rs3_stage(NT, K) : 0);
   return ((rs3_keys(NT, N) > over ? rs3_keys(NT, N) : over) + 15) & ~(size_t)15;
 }
 __host__ __device__ inline size_t rs3_lds(int NT, int N, int K, bool stage) {
@@ -1113,69 +1106,13 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
     __syncthreads();
     uint32_t theta[QW];
     bool take_all[QW];
-    // Narrowing (many chunks): the K-th largest of the 64 lane maxima is at most the
-    // K-th largest key, so the keys at or above it hold the whole top K (ties at
-    // the threshold included). Where each query has at most 128 of them, they are
-    // compacted in chunk order into two keys per lane and the selection runs on
-    // those; otherwise on all keys.
-    constexpr bool kNarrow = P >= 8;
-    uint32_t ckey[QW][2];
-    int cidx[QW][2];
-    bool narrowed = false;
-    if constexpr (kNarrow) {
-      uint32_t lm[QW][1];
-#pragma unroll
-      for (int qq = 0; qq < QW; ++qq) {
-        uint32_t m = key[qq][0];
-#pragma unroll
-        for (int j = 1; j < P; ++j) m = max(m, key[qq][j]);
-        lm[qq][0] = m;
-      }
-      uint32_t thl[QW];
-      bool tal[QW];
-      wave_topk_thresholds<1, QW>(lm, K, thl, tal);
-      uint32_t* cbuf = reinterpret_cast<uint32_t*>(smem + rs3_off_f(NT, N, K, STAGE)) + w * 2 * kNarrow;
-      const unsigned long long lt = (1ull << lane) - 1ull;
-      bool fits = true;
-#pragma unroll
-      for (int qq = 0; qq < QW; ++qq) {
-        const uint32_t lq = tal[qq] ? 1u : max(thl[qq], 1u);
-        int base = 0;
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-          const bool in = key[qq][j] >= lq;
-          const unsigned long long m = __ballot(in);
-          const int pos = base + __popcll(m & lt);
-          if (in && pos < kNarrow) {
-            cbuf[pos] = key[qq][j];
-            cbuf[kNarrow + pos] = 64 * j + lane;
-          }
-          base += __popcll(m);
-        }
-        fits = fits && base <= kNarrow;   // wave-uniform
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int pos = 64 * jj + lane;
-          ckey[qq][jj] = pos < base ? cbuf[pos] : 0u;
-          cidx[qq][jj] = (int)cbuf[kNarrow + pos];
-        }
-        __builtin_amdgcn_wave_barrier();   // the next query's writes come after these reads
-      }
-      narrowed = fits;
-      if (narrowed) wave_topk_thresholds<2, QW>(ckey, K, theta, take_all);
-    }
-    if (!narrowed) wave_topk_thresholds<P, QW>(key, K, theta, take_all);
+    wave_topk_thresholds<P, QW>(key, K, theta, take_all);
 #pragma unroll
     for (int qq = 0; qq < QW; ++qq) {
       const int qi = w + kRsWaves * qq, t = t0 + qi;
       if (t >= nq) break;
-      const int cnt =
-          narrowed ? wave_topk_select<2>(ckey[qq], K, theta[qq], take_all[qq], lane,
-                                         [&](int slot, int jj) { chosen[w * 64 + slot] = cidx[qq][jj]; })
-                   : wave_topk_select<P>(key[qq], K, theta[qq], take_all[qq], lane,
-                                         [&](int slot, int j) { chosen[w * 64 + slot] = 64 * j + lane; });
+      const int cnt = wave_topk_select<P>(key[qq], K, theta[qq], take_all[qq], lane,
+                                          [&](int slot, int j) { chosen[w * 64 + slot] = 64 * j + lane; });
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       if (lane < K) {

@@ -255,12 +255,11 @@ def test_route_layer_prefill_edge(case):
 
 
 def test_topk_exact_ties_many_chunks():
-    """Exact ties in the group maximum at N = 600, where the fused top-K first narrows each
-    query's keys to at most 128 candidates: chunk 2i + 1 has the summary and entropy of
-    chunk 2i, so every score occurs twice. The chosen set must be a top K of the oracle's
-    group maxima; where twins straddle the threshold, the smaller chunk is chosen (the
-    oracle's tie rule); rows whose K-th and (K+1)-th scores differ by more than 1e-3 match
-    the oracle exactly."""
+    """Exact ties in the group maximum at N = 600 (the fused scoring with 16 keys per lane):
+    chunk 2i + 1 has the summary and entropy of chunk 2i, so every score occurs twice. The
+    chosen set must be a top K of the oracle's group maxima; where twins straddle the
+    threshold, the smaller chunk is chosen (the oracle's tie rule); rows whose K-th and
+    (K+1)-th scores differ by more than 1e-3 match the oracle exactly."""
     B, Hq, Hkv, N, d, r, D, K, R, beta = 1, 8, 2, 600, 128, 16, 96, 31, 200, 0.5
     G, L, T = Hq // Hkv, N * 64, N * 63
     print(f"[case] top-K ties N={N} K={K} Hq={Hq} Hkv={Hkv}", flush=True)
