@@ -834,8 +834,19 @@ __device__ __forceinline__ int wave_topk_narrow(const uint32_t* key, int K, int 
 // N = 1024 within the 160 KB of a CU.
 constexpr int kRsWaves = 8;
 
-__host__ __device__ inline size_t rs3_keys(int NT, int N) { return (size_t)16 * NT * (N + 1) * 4; }
-__host__ __device__ inline size_t rs3_off_z(int NT, int N) { return ((size_t)16 * NT * N + 15) & ~(size_t)15; }
+// Row strides chosen for the LDS banks (64 banks of 4 bytes): key rows of rs3_zs(N)
+// words, 3 modulo 64, so that the group-maximum atomics of a wave (16 query rows x 16
+// chunks per tile) meet at most two to a bank; rank rows of rs3_rn(N) bytes (all of a
+// row's 16-chunk tiles, a multiple of 16 bytes, 4 words modulo 64), so that a wave's
+// 4-byte rank reads of 16 rows x 4 chunk groups hit 64 distinct banks.
+__host__ __device__ inline int rs3_zs(int N) { return N + (((3 - N % 64) % 64) + 64) % 64; }
+__host__ __device__ inline int rs3_rn(int N) {
+  int r4 = (N + 15) / 16 * 4;
+  r4 += (((4 - r4 % 64) % 64) + 64) % 64;
+  return 4 * r4;
+}
+__host__ __device__ inline size_t rs3_keys(int NT, int N) { return (size_t)16 * NT * rs3_zs(N) * 4; }
+__host__ __device__ inline size_t rs3_off_z(int NT, int N) { return ((size_t)16 * NT * rs3_rn(N) + 15) & ~(size_t)15; }
 __host__ __device__ inline size_t rs3_stage(int NT, int K) { return (size_t)kRsWaves * 16 * NT * K * 4; }
 // offset of the chosen lists: past the keys, or past ranks + staging rows if longer
 __host__ __device__ inline size_t rs3_off_c(int NT, int N, int K, bool stage) {
@@ -899,9 +910,9 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
   const int G = Hq / Hkv;
   const int t0 = (tile - bg * nqb) * QT;
   const long long L = (long long)N * kSlots;
-  const int NMT = (N + 15) / 16, ZS = N + 1;
+  const int NMT = (N + 15) / 16, ZS = rs3_zs(N), RN = rs3_rn(N);
   uint32_t* zk = reinterpret_cast<uint32_t*>(smem);             // A, B: [QT][ZS] group-maximum keys
-  uint8_t* rank_t = smem;                                       // B, C: [QT][N] rank in zsel, 0xFF if not chosen
+  uint8_t* rank_t = smem;                                       // B, C: [QT][RN] rank in zsel, 0xFF if not chosen
   float* zst = reinterpret_cast<float*>(smem + rs3_off_z(NT, N));   // C (STAGE): per wave [QT][K] zsel rows
   int* chosen = reinterpret_cast<int*>(smem + rs3_off_c(NT, N, K, STAGE));
   for (int e = tid; e < QT * ZS; e += 64 * kRsWaves) zk[e] = 0u;
@@ -979,7 +990,6 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
     uint32_t rk[NT];
   };
   const bf16_t* sph = sp + (size_t)(b * Hq + h) * NMT * KS * 2 * 64 * 8;
-  const bool rk4 = (N & 3) == 0;
   auto load_tile = [&](int mt, TileBuf& t, bool ranks) {
     const bf16_t* base = sph + (size_t)mt * KS * 2 * 64 * 8;
 #pragma unroll
@@ -994,16 +1004,8 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
     if (ranks) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int cb = 16 * mt + 4 * g16;
-        const uint8_t* rr = rank_t + (16 * nt + L16) * N + cb;
-        if (rk4 && cb + 3 < N) {
-          t.rk[nt] = *reinterpret_cast<const uint32_t*>(rr);
-        } else {
-          uint32_t v = 0u;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v |= (cb + i < N ? (uint32_t)rr[i] : 0xFFu) << (8 * i);
-          t.rk[nt] = v;
-        }
+        // chunks past N read the row's 0xFF fill
+        t.rk[nt] = *reinterpret_cast<const uint32_t*>(rank_t + (16 * nt + L16) * RN + 16 * mt + 4 * g16);
       }
     }
   };
@@ -1100,7 +1102,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
       }
     }
     __syncthreads();   // every wave holds its keys: the table becomes ranks and staging rows
-    for (int e = tid; e < QT * N / 4; e += 64 * kRsWaves) reinterpret_cast<uint32_t*>(rank_t)[e] = 0xFFFFFFFFu;
+    for (int e = tid; e < QT * RN / 4; e += 64 * kRsWaves) reinterpret_cast<uint32_t*>(rank_t)[e] = 0xFFFFFFFFu;
     if constexpr (STAGE)
       for (int e = tid; e < kRsWaves * QT * K; e += 64 * kRsWaves) zst[e] = -INFINITY;   // unfilled slots
     __syncthreads();
@@ -1118,7 +1120,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
       if (lane < K) {
         const int c = lane < cnt ? chosen[w * 64 + lane] : -1;
         idx[((size_t)bg * nq + t) * K + lane] = c;
-        if (c >= 0) rank_t[qi * N + c] = (uint8_t)lane;
+        if (c >= 0) rank_t[qi * RN + c] = (uint8_t)lane;
         else if constexpr (!STAGE)
           for (int hh = 0; hh < G; ++hh) zsel[(((size_t)b * Hq + g * G + hh) * nq + t) * K + lane] = -INFINITY;
       }
