@@ -363,7 +363,7 @@ __global__ __launch_bounds__(64) void bwd_fill_kernel(BwdParams p) {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_key_kernel(BwdParams p) {
-  constexpr int LDR = D + 8;
+  constexpr int LDR = D + 16;   // staged row stride in elements (288 bytes at d = 128: rows 8 banks apart)
   constexpr int RS = kKeyRows;   // rows staged per step
   constexpr int TPR = 256 / RS;  // staging threads per row
   constexpr int PPT = D / 8 / TPR;   // 16-byte pieces per thread per staged tensor
