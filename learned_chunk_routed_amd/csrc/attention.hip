@@ -916,20 +916,17 @@ __device__ __forceinline__ void s_tile_lean(const bf16_t* buf, const QFrag<D, 1>
   }
 }
 
-// S^T of NT tiles sharing every K fragment read, with the lane offsets formed in
-// place as in s_tile_lean.
+// S^T of NT tiles sharing every K fragment read, added to the accumulators as they
+// come in (which may hold a mask: -inf where a key is out of a row's window), with
+// the lane offsets formed in place as in s_tile_lean.
 template <int D, int NT>
-__device__ __forceinline__ void s_tiles_lean(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4]) {
+__device__ __forceinline__ void s_tiles_lean_acc(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4]) {
   typedef TileLayout<D, true> TL;
   int ln;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
   const int L16 = ln & 15, g16 = ln >> 4;
   const bf16_t* rowp = buf + L16 * D;
   const int sw = TL::swz_k(L16);
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[t][mt] = zero4();
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
     const bf16_t* pk = rowp + (((4 * ks + g16) ^ sw) << 3);
@@ -940,6 +937,15 @@ __device__ __forceinline__ void s_tiles_lean(const bf16_t* buf, const QFrag<D, 1
       for (int t = 0; t < NT; ++t) acc[t][mt] = mfma16(a, q[t].f[ks][0], acc[t][mt]);
     }
   }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void s_tiles_lean(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[t][mt] = zero4();
+  s_tiles_lean_acc<D, NT>(buf, q, acc);
 }
 
 // O^T += V^T P^T for NT tiles sharing every V^T fragment read (vbuf: a V half).
@@ -2565,91 +2571,95 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
     compiler_fence();
     if (t + RING - 2 < ntile) issue(t + RING - 2);
   };
-  // one K/V tile at the band's edges: S, masked softmax and P V of each query
-  // tile that sees it
-  auto edge_step = [&](int j) {
-    const int kb = kb0 + 64 * j;
-    const bf16_t* buf = kvb + (j % RING) * BUFE;
-    bool act[2];
-    s16x8 pf[2][2];
+  // Tile jt lies inside the window of all 32 rows (and of the sequence): the run
+  // between the band's edges, whose products start from zero accumulators.
+  auto inside = [&](int jt) {
+    const int kb = kb0 + 64 * jt;
+    return kb >= t0 + 31 - R && kb + 63 <= t0 + R && kb + 63 < L && t0 + 31 < L;   // wave-uniform
+  };
+  // Accumulators of S^T for a band-edge tile jt before the products: 0, or -inf for
+  // each key outside a row's window or past the sequence (rows past the sequence mask
+  // all keys), so the softmax needs no bounds.
+  auto s_init = [&](int jt, f32x4 (&s)[2][4]) {
+    const int kb = kb0 + 64 * jt;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int ts = t0 + 16 * tt;
-      act[tt] = ts < L && kb <= ts + 15 + R && kb + 63 >= ts - R;   // wave-uniform
-      if (!act[tt]) continue;
-      f32x4 sacc[1][4];
-      s_tiles_lean<D, 1>(buf, &qf[tt], sacc);
-      const int mode = trow[tt] < L ? 1 : 0;
-      const int lo = max(0, trow[tt] - R - kb);
-      const int hi = min(63, min(L - 1, trow[tt] + R) - kb);
-      const float alpha = tile_softmax<true, false>(sacc[0], mode, lo, hi, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
-      if (__ballot(alpha != 1.f) != 0ull) {
-#pragma unroll
-        for (int dm = 0; dm < D / 16; ++dm)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha;
+      int lo = 1, hi = 0;
+      if (trow[tt] < L) {
+        lo = max(0, trow[tt] - R - kb);
+        hi = min(63, min(L - 1, trow[tt] + R) - kb);
       }
+      // key 16 mt + 4 g16 + i is kept when lo <= key <= hi
+      const int los = lo - 4 * g16, his = hi - 4 * g16;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[tt][mt][i] = (16 * mt + i >= los && 16 * mt + i <= his) ? 0.f : -INFINITY;
     }
-    if (act[0] && act[1]) pv_tiles<D, 2>(buf + TL::KE, pf, acc);
-    else if (act[0]) pv_tiles<D, 1>(buf + TL::KE, &pf[0], &acc[0]);
-    else if (act[1]) pv_tiles<D, 1>(buf + TL::KE, &pf[1], &acc[1]);
   };
-  // tiles jlo .. jhi lie inside the window of all 32 rows (and of the sequence)
-  const int jlo = max(0, (t0 + 31 - R - kb0 + 63) >> 6);   // ceiling of a quotient, numerator >= -63
-  int jhi = min(t0 + R, L - 1) - 63 - kb0;
-  jhi = jhi < 0 ? -1 : min(ntile - 1, jhi >> 6);
-  if (t0 + 31 >= L) jhi = -1;
 
   for (int jj = 0; jj < RING - 2 && jj < ntile; ++jj) issue(jj);
-  int j = 0;
-  for (; j < ntile && j < jlo; ++j) {
-    arrive(j);
-    edge_step(j);
+  // Pipelined walk over the band: S of tile j + 1 (every K fragment read serving both
+  // query tiles) is formed ahead of the softmax of tile j, whose VALU work runs beside
+  // those MFMAs; then P V of tile j for both query tiles (a query tile that does not
+  // reach a band-edge tile gets P = 0 there).
+  f32x4 sc[2][4], sn[2][4];
+  arrive(0);
+  if (inside(0)) {
+    s_tiles_lean<D, 2>(kvb, qf, sc);
+  } else {
+    s_init(0, sc);
+    s_tiles_lean_acc<D, 2>(kvb, qf, sc);
   }
-  if (j <= jhi) {
-    // Pipelined run: S of tile j + 1 (every K fragment read serving both query
-    // tiles) is formed ahead of the softmax of tile j, whose VALU work can then
-    // run beside those MFMAs; then P V of tile j.
-    f32x4 sc[2][4], sn[2][4];
-    arrive(j);
-    s_tiles_lean<D, 2>(kvb + (j % RING) * BUFE, qf, sc);
-    for (; j <= jhi; ++j) {
-      const bf16_t* buf = kvb + (j % RING) * BUFE;
-      s16x8 pf[2][2];
-      float alpha[2];
-      const bool nx = j < jhi;
-      if (nx) arrive(j + 1);
-      // (after the run's last tile the products are formed once more on that tile
-      // and dropped, which keeps them and the softmax in one scheduling region)
-      s_tiles_lean<D, 2>(kvb + ((nx ? j + 1 : j) % RING) * BUFE, qf, sn);
+  for (int j = 0; j < ntile; ++j) {
+    const bf16_t* buf = kvb + (j % RING) * BUFE;
+    s16x8 pf[2][2];
+    float alpha[2];
+    const bool nx = j + 1 < ntile;
+    if (nx) arrive(j + 1);
+    // (after the last tile the products are formed once more on that tile and
+    // dropped, which keeps them and the softmax in one scheduling region)
+    const int jn = nx ? j + 1 : j;
+    const bf16_t* bufn = kvb + (jn % RING) * BUFE;
+    // the products and the softmax in one region, one MFMA then a few softmax VALU
+    // instructions in turn; the region is written twice so that the run between
+    // the edges keeps zero-initialised products
+    if (inside(jn)) {
+      s_tiles_lean<D, 2>(bufn, qf, sn);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         alpha[tt] = tile_softmax<false, false>(sc[tt], 1, 0, 63, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
-      // one MFMA, then a few softmax VALU instructions, in turn
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        if (__ballot(alpha[tt] != 1.f) != 0ull) {
-#pragma unroll
-          for (int dm = 0; dm < D / 16; ++dm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha[tt];
-        }
-      }
-      pv_tiles<D, 2>(buf + TL::KE, pf, acc);
+    } else {
+      s_init(jn, sn);
+      s_tiles_lean_acc<D, 2>(bufn, qf, sn);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
+        alpha[tt] = tile_softmax<false, false>(sc[tt], 1, 0, 63, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) sc[tt][mt] = sn[tt][mt];
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
     }
-  }
-  for (; j < ntile; ++j) {
-    arrive(j);
-    edge_step(j);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if (__ballot(alpha[tt] != 1.f) != 0ull) {
+#pragma unroll
+        for (int dm = 0; dm < D / 16; ++dm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha[tt];
+      }
+    }
+    pv_tiles<D, 2>(buf + TL::KE, pf, acc);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) sc[tt][mt] = sn[tt][mt];
   }
 
 #pragma unroll
