@@ -251,17 +251,18 @@ int lcr_routed_attention_noalloc(const lcr_dims* dims, const void* q, const void
  *
  * Inputs exactly as passed to (and produced by) the forward call: q, k, v, idx,
  * zsel, K, radius, scale, q0, nq; o [B,Hq,L,d] and lse [B,Hq,nq] (both
- * required); dO [B,Hq,L,d] (rows slot(i) read). dtype must be LCR_BF16.
+ * required); dO [B,Hq,L,d] (rows slot(i) read); q, k, v, o, dO in dims->dtype.
  * Outputs, float32: dq [B,Hq,L,d] (only rows slot(i) of the queried i are
  * written); dk, dv [B,Hkv,L,d] (every row written: rows no queried row reads,
  * mask slots included, are zero); dzsel [B,Hq,nq,K] (may be NULL when K = 0).
  * Only the nq queried rows contribute. ws: lcr_workspace_bytes(
  * LCR_OP_ROUTED_ATTENTION_BACKWARD, dims, 0, 0, K, radius, nq) bytes, contents
- * need not be initialised. Arithmetic: bf16 products (probabilities and their
- * gradients rounded to bf16 for the products), float32 accumulation in a
- * fixed order: results are reproducible bit for bit.
- * Errors: as lcr_routed_attention; LCR_ERR_UNSUPPORTED for LCR_F32 inputs or
- * N > 32768.
+ * need not be initialised. Arithmetic: LCR_BF16 takes bf16 products
+ * (probabilities and their gradients rounded to bf16 for the products) with
+ * float32 accumulation; LCR_F32 takes float32 throughout on the vector ALUs (a
+ * plain path for parity-sized problems, not tuned for speed). Either way the
+ * order is fixed: results are reproducible bit for bit.
+ * Errors: as lcr_routed_attention; LCR_ERR_UNSUPPORTED for N > 32768.
  */
 int lcr_routed_attention_backward(const lcr_dims* dims, const void* q, const void* k, const void* v,
                                   const int32_t* idx, const float* zsel, int K, int radius, float scale,

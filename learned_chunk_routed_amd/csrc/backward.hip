@@ -549,6 +549,230 @@ __global__ __launch_bounds__(256, 2) void bwd_key_kernel(BwdParams p) {
 }
 
 
+// ---------------------------------------------------------------- float32 inputs
+// The same gradients for float32 q, k, v, o, dO, in plain float32 VALU arithmetic
+// (every product and sum in float32, a fixed order: reproducible bit for bit). The
+// float32 entry point serves parity-sized problems, so these kernels favour a plain
+// structure over speed; the inverse index is the bf16 path's.
+//  bwd32_query_kernel: one block per (batch, head, query row); a wave takes one key
+//    at a time (lanes own D/64 dimensions each, dot products by wave sums). Window
+//    keys: p = exp(scale q.k - lse), ds = p (dO.v - D). Selected chunk c (waves
+//    take chunk slots in turn): the chunk's logits and dO.v per key (lane j holds
+//    key j), its own log-sum-exp LSE_c, pi_j, U_c = sum pi_j dO.v_j, dz_c =
+//    P_c (U_c - D), ds_j = P_c pi_j (dO.v_j - U_c). dq = scale sum ds k (the four
+//    waves' partial sums added in wave order). Writes dq, dzsel and, for the key
+//    side, D, the chunk bias z_c - lse - LSE_c and U_c.
+//  bwd32_key_kernel: one block per (batch, KV group, chunk); lane l of wave w owns
+//    key 16 w + l / 4 and a quarter of the dimensions. Rows (query, head) are
+//    staged 16 at a time: the window's queries, then the chunk's inverse-index
+//    entries; per row p = exp(scale q.k + bias) (window: bias -lse, keys outside
+//    the row's window excluded; chunk: bias z_c - lse - LSE_c), ds = p (dO.v - sub)
+//    (sub: D or U_c); dk = scale sum ds q, dv = sum p dO.
+constexpr int kBwd32Rows = 16;
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd32_query_kernel(BwdParams p) {
+  constexpr int DPL = D / 64;   // dimensions per lane
+  __shared__ float part[4][D];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / p.G;
+  const size_t L = (size_t)p.N * kSlots;
+  const float* q = reinterpret_cast<const float*>(p.q);
+  const float* kk = reinterpret_cast<const float*>(p.k);
+  const float* vv = reinterpret_cast<const float*>(p.v);
+  const float* o = reinterpret_cast<const float*>(p.o);
+  const float* dO = reinterpret_cast<const float*>(p.dO);
+  const int i = p.q0 + t;
+  const size_t rq = ((size_t)b * p.Hq + h) * p.nq + t;   // (batch, head, row) of lse, dsum, zsel
+  const size_t qoff = (((size_t)b * p.Hq + h) * L + slot_of_c(i)) * D;
+  const float* kg = kk + ((size_t)b * p.Hkv + g) * L * D;
+  const float* vg = vv + ((size_t)b * p.Hkv + g) * L * D;
+  float qv[DPL], dv[DPL], acc[DPL];
+  float dsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const int dd = DPL * lane + e;
+    qv[e] = q[qoff + dd];
+    dv[e] = dO[qoff + dd];
+    dsum += dv[e] * o[qoff + dd];
+    acc[e] = 0.f;
+  }
+  dsum = wave_sum(dsum);
+  const float lse = p.lse[rq];
+  auto dots = [&](size_t koff, float& sq, float& sd) {
+    float a = 0.f, c = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      a += qv[e] * kg[koff + DPL * lane + e];
+      c += dv[e] * vg[koff + DPL * lane + e];
+    }
+    sq = wave_sum(a);
+    sd = wave_sum(c);
+  };
+  // window keys, wave w taking every fourth
+  const int T = p.N * kContent;
+  const int lo = max(0, i - p.R), hi = min(T - 1, i + p.R);
+  for (int u = lo + w; u <= hi; u += 4) {
+    const size_t koff = (size_t)slot_of_c(u) * D;
+    float sq, sd;
+    dots(koff, sq, sd);
+    const float ds = expf(p.scale * sq - lse) * (sd - dsum);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] += ds * kg[koff + DPL * lane + e];
+  }
+  // selected chunks, wave w taking slots w, w + 4, ...
+  for (int ks = w; ks < p.K; ks += 4) {
+    const int c = p.idx[(((size_t)b * p.Hkv + g) * p.nq + t) * p.K + ks];
+    if (c < 0) {
+      if (lane == 0) {
+        p.dzsel[rq * p.K + ks] = 0.f;
+        p.cbias[rq * p.K + ks] = -INFINITY;
+        p.cu[rq * p.K + ks] = 0.f;
+      }
+      continue;
+    }
+    float lj = -INFINITY, ej = 0.f;   // lane j: key j's logit and dO.v
+    for (int j = 0; j < kContent; ++j) {
+      float sq, sd;
+      dots((size_t)(c * kSlots + j) * D, sq, sd);
+      if (lane == j) {
+        lj = p.scale * sq;
+        ej = sd;
+      }
+    }
+    const float m = wave_max(lj);
+    const float lsec = m + logf(wave_sum(lane < kContent ? expf(lj - m) : 0.f));
+    const float pij = lane < kContent ? expf(lj - lsec) : 0.f;
+    const float U = wave_sum(pij * ej);
+    const float z = p.zsel[rq * p.K + ks];
+    const float Pc = expf(z - lse);
+    const float dsj = Pc * pij * (ej - U);
+    for (int j = 0; j < kContent; ++j) {
+      const float dj = __shfl(dsj, j);
+      const size_t koff = (size_t)(c * kSlots + j) * D;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += dj * kg[koff + DPL * lane + e];
+    }
+    if (lane == 0) {
+      p.dzsel[rq * p.K + ks] = Pc * (U - dsum);
+      p.cbias[rq * p.K + ks] = z - lse - lsec;
+      p.cu[rq * p.K + ks] = U;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) part[w][DPL * lane + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int dd = threadIdx.x;
+    reinterpret_cast<float*>(p.dq)[qoff + dd] = p.scale * (((part[0][dd] + part[1][dd]) + part[2][dd]) + part[3][dd]);
+  }
+  if (threadIdx.x == 0) p.dsum[rq] = dsum;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd32_key_kernel(BwdParams p) {
+  constexpr int DQ = D / 4;          // dimensions per lane
+  constexpr int RB = kBwd32Rows;     // rows staged per round
+  __shared__ float sq[RB][D], sdo[RB][D];
+  __shared__ float sbias[RB], ssub[RB];
+  __shared__ int squery[RB];         // content index of a window row, INT_MIN / 2 for chunk rows and padding
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = blockIdx.x % p.N, bg = blockIdx.x / p.N, b = bg / p.Hkv, g = bg % p.Hkv;
+  const size_t L = (size_t)p.N * kSlots;
+  const int key = 16 * w + lane / 4, d0 = DQ * (lane & 3);
+  const float* q = reinterpret_cast<const float*>(p.q);
+  const float* dO = reinterpret_cast<const float*>(p.dO);
+  const size_t krow = ((size_t)bg * L + (size_t)c * kSlots + key) * D;
+  float kf[DQ], vf[DQ], dka[DQ], dva[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    kf[e] = reinterpret_cast<const float*>(p.k)[krow + d0 + e];
+    vf[e] = reinterpret_cast<const float*>(p.v)[krow + d0 + e];
+    dka[e] = 0.f;
+    dva[e] = 0.f;
+  }
+  const int u_key = c * kContent + key;   // content index of this lane's key (key < 63)
+  const int iw_lo = max(p.q0, c * kContent - p.R);
+  const int iw_hi = min(p.q0 + p.nq - 1, c * kContent + kContent - 1 + p.R);
+  const int nwq = max(0, iw_hi - iw_lo + 1);
+  const int ncnt = p.nq > 0 ? p.cnt[(size_t)bg * p.N + c] : 0;
+  const size_t per = (size_t)p.nq * p.K;
+  const int* lst = p.list + (size_t)bg * per + (p.nq > 0 ? p.off[(size_t)bg * (p.N + 1) + c] : 0);
+  const int nrow = (nwq + ncnt) * p.G;   // window rows first, then the chunk's entries, G heads each
+  for (int r0 = 0; r0 < nrow; r0 += RB) {
+    __syncthreads();   // the previous round's readers are done
+    // stage the round's q and dO rows (padding rows as zeros) and their scalars
+    for (int x = tid; x < RB * D; x += 256) {
+      const int rr = x / D, dd = x % D, r = r0 + rr;
+      float qx = 0.f, dx = 0.f;
+      if (r < nrow) {
+        const int e = r / p.G, hh = r % p.G, hq = g * p.G + hh;
+        const int i = e < nwq ? iw_lo + e : p.q0 + lst[e - nwq] / p.K;
+        const size_t off = (((size_t)b * p.Hq + hq) * L + slot_of_c(i)) * D + dd;
+        qx = q[off];
+        dx = dO[off];
+      }
+      sq[rr][dd] = qx;
+      sdo[rr][dd] = dx;
+    }
+    if (tid < RB) {
+      const int r = r0 + tid;
+      float bias = -INFINITY, sub = 0.f;
+      int qi = INT_MIN / 2;
+      if (r < nrow) {
+        const int e = r / p.G, hh = r % p.G, hq = g * p.G + hh;
+        if (e < nwq) {
+          qi = iw_lo + e;
+          const size_t rq = ((size_t)b * p.Hq + hq) * p.nq + (qi - p.q0);
+          bias = -p.lse[rq];
+          sub = p.dsum[rq];
+        } else {
+          const int ent = lst[e - nwq];
+          const size_t rq = ((size_t)b * p.Hq + hq) * p.nq + ent / p.K;
+          bias = p.cbias[rq * p.K + ent % p.K];
+          sub = p.cu[rq * p.K + ent % p.K];
+        }
+      }
+      sbias[tid] = bias;
+      ssub[tid] = sub;
+      squery[tid] = qi;
+    }
+    __syncthreads();
+    const int nr = min(RB, nrow - r0);
+    for (int rr = 0; rr < nr; ++rr) {
+      float a = 0.f, dd = 0.f;
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        a += sq[rr][d0 + e] * kf[e];
+        dd += sdo[rr][d0 + e] * vf[e];
+      }
+      // the key's four lanes hold quarters of the dimensions
+      a += __shfl_xor(a, 1);
+      a += __shfl_xor(a, 2);
+      dd += __shfl_xor(dd, 1);
+      dd += __shfl_xor(dd, 2);
+      const int qi = squery[rr];
+      bool ok = key < kContent;
+      if (qi != INT_MIN / 2) ok = ok && abs(u_key - qi) <= p.R;
+      const float pr = ok ? expf(p.scale * a + sbias[rr]) : 0.f;
+      const float ds = pr * (dd - ssub[rr]);
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) {
+        dka[e] += ds * sq[rr][d0 + e];
+        dva[e] += pr * sdo[rr][d0 + e];
+      }
+    }
+  }
+  float* dkb = p.dk + krow;
+  float* dvb = p.dv + krow;
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) {
+    dkb[d0 + e] = p.scale * dka[e];
+    dvb[d0 + e] = dva[e];
+  }
+}
+
 // ---------------------------------------------------------------- 4. summary pooling backward
 // "Prefilling-dLLM v2", Figure 3 caption: alpha = softmax_j(scale q_m . k_j) over the
 // chunk's 63 content keys, s = sum_j alpha_j k_j; "The 172x Speedup...": entropy
@@ -1231,8 +1455,8 @@ hipError_t launch_route_score_backward(const RouteDims& dm, const void* q, const
                                                      dx, dA, dBm, ds, dH, w, st);
 }
 
-template <int D>
-static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t st) {
+// the inverse index (per chunk, the (query, slot) entries that selected it)
+static hipError_t launch_bwd_index(const BwdParams& prm, hipStream_t st) {
   const size_t bgn = (size_t)prm.B * prm.Hkv * prm.N;
   const int ntile = bwd_ntile(prm.nq);
   const size_t idx_lds = (size_t)prm.N * 4;
@@ -1253,6 +1477,14 @@ static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t st) {
     hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)std::min<size_t>((no + 255) / 256, 65535)), dim3(256), 0,
                        st, prm.off, no);
   }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t st) {
+  const size_t bgn = (size_t)prm.B * prm.Hkv * prm.N;
+  hipError_t e = launch_bwd_index(prm, st);
+  if (e != hipSuccess) return e;
   const int tiles = prm.B * prm.Hkv * ((prm.nq + 1) / 2);
   const size_t lds = routed_bwd_lds_bytes(D);
   e = hipFuncSetAttribute((const void*)bwd_query_kernel<D>,
@@ -1271,6 +1503,17 @@ static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t st) {
     }
   }
   hipLaunchKernelGGL(bwd_key_kernel<D>, dim3((unsigned)bgn), dim3(256), 0, st, prm);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd32_d(const BwdParams& prm, hipStream_t st) {
+  hipError_t e = launch_bwd_index(prm, st);
+  if (e != hipSuccess) return e;
+  if (prm.nq > 0) hipLaunchKernelGGL(bwd32_query_kernel<D>, dim3(prm.nq, prm.Hq, prm.B), dim3(256), 0, st, prm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd32_key_kernel<D>, dim3((unsigned)((size_t)prm.B * prm.Hkv * prm.N)), dim3(256), 0, st, prm);
   return hipGetLastError();
 }
 
@@ -1318,6 +1561,7 @@ hipError_t launch_routed_attention_backward(const RouteDims& dm, const void* q, 
   prm.q0 = q0;
   prm.nq = nq;
   prm.scale = scale;
+  if (dm.dtype == 0) return dm.d == 128 ? launch_bwd32_d<128>(prm, st) : launch_bwd32_d<64>(prm, st);
   return dm.d == 128 ? launch_bwd_d<128>(prm, st) : launch_bwd_d<64>(prm, st);
 }
 

@@ -91,7 +91,6 @@ int check_routed_attention_backward(const lcr_dims* d, const void* q, const void
                                     const float* dq, const float* dk, const float* dv, const float* dzsel) {
   int st = check_routed_attention(d, q, k, v, idx, zsel, K, radius, scale, q0, nq, o);
   if (st != LCR_OK) return st;
-  if (d->dtype != LCR_BF16) return LCR_ERR_UNSUPPORTED;
   if (!dk || !dv) return LCR_ERR_ARG;
   if (nq > 0) {
     if (!lse || !dO || !dq) return LCR_ERR_ARG;

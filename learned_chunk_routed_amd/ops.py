@@ -212,7 +212,7 @@ def routed_attention_backward(q, k, v, idx, zsel, o, lse, dO, *, radius, scale=N
     T = N * CONTENT
     nq = T - q0 if nq is None else nq
     K = idx.shape[-1]
-    _need(q.dtype == torch.bfloat16, "routed_attention_backward takes bfloat16 q, k, v, o, dO")
+    _need(q.dtype in (torch.bfloat16, torch.float32), "routed_attention_backward takes bfloat16 or float32 q, k, v, o, dO")
     _check(q, "q", dev)
     _check(k, "k", dev, q.dtype, (B, Hkv, N * SLOTS, d))
     _check(v, "v", dev, q.dtype, (B, Hkv, N * SLOTS, d))
@@ -310,7 +310,7 @@ def route_layer_backward(q, k, v, x, A, Bm, fwd, dO, *, radius, beta=0.0, scale=
     """Gradients of the whole route layer with the forward's selection held fixed.
 
     fwd is the dict route_layer returned (with want_lse=True: s, idx, zsel, o, lse);
-    dO [B,Hq,L,d] bf16 is the upstream gradient on o. Chains the attention, scoring
+    dO [B,Hq,L,d] (q's dtype) is the upstream gradient on o. Chains the attention, scoring
     and pooling backward calls; returns a dict with dq [B,Hq,L,d] (query rows from
     attention and scoring, mask rows from the pooling), dk, dv, dx, dA, dBm, and the
     intermediates dzsel, ds, dH (all float32)."""

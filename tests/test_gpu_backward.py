@@ -102,6 +102,43 @@ def test_backward_tiny(name):
         assert np.all(gz[~np.isfinite(zsel)] == 0), "padded selections get no gradient"
 
 
+@pytest.mark.parametrize("name", sorted(TINY))
+def test_backward_tiny_fp32(name):
+    """float32 inputs take the plain float32 backward (vector ALUs, fixed order): every
+    gradient within 1e-5 of the fp64 oracle (relative to its largest magnitude), two
+    calls equal bit for bit, untouched rows zero."""
+    kw = dict(TINY[name])
+    q0 = kw.pop("q0", 0)
+    nq = kw.pop("nq", None)
+    cfg = get_config("prefill_16k", dtype="fp32", **kw)
+    nq = cfg.T - q0 if nq is None else nq
+    print(f"[case] float32 backward {name}: B={cfg.B} N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} K={cfg.K} "
+          f"R={cfg.R} q0={q0} nq={nq}", flush=True)
+    inp = route_inputs(cfg)
+    dr = backward_draws(cfg, q0, nq)
+    idx, zsel = selection(cfg, dr, q0, nq)
+    gq, gk, gv, gz = run_gpu(cfg, inp, dr["dO"], idx, zsel, q0, nq)
+    again = run_gpu(cfg, inp, dr["dO"], idx, zsel, q0, nq)
+    for x, y, n in zip((gq, gk, gv, gz), again, ("dq", "dk", "dv", "dzsel")):
+        assert np.array_equal(x, y), f"{n} differs between two identical calls"
+    queries = np.arange(q0, q0 + nq)
+    sl = O.slot_of(queries)
+    q, k, v = as_f64(inp["q"]), as_f64(inp["k"]), as_f64(inp["v"])
+    dO = as_f64(dr["dO"])
+    rq, rk, rv, rz = OB.routed_attention_backward(q[:, :, sl], k, v, idx, zsel.astype(np.float64), cfg.R,
+                                                  cfg.scale, queries, dO[:, :, sl])
+    errs = dict(dq=rel_err(gq[:, :, sl], rq), dk=rel_err(gk, rk), dv=rel_err(gv, rv),
+                dzsel=rel_err(np.where(np.isfinite(zsel), gz, 0.0), rz))
+    print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e < 1e-5, f"{name}: {n} error {e:.3e}"
+    other = np.setdiff1d(np.arange(cfg.L), sl)
+    assert np.all(gq[:, :, other] == 0)
+    assert np.all(gk[:, :, SL - 1::SL] == 0) and np.all(gv[:, :, SL - 1::SL] == 0)
+    if cfg.K:
+        assert np.all(gz[~np.isfinite(zsel)] == 0), "padded selections get no gradient"
+
+
 def test_backward_layer_selection():
     """The selection and chunk logits of the oracle route layer itself (a real top-K)."""
     cfg = get_config("prefill_16k", N=10, Hq=8, Hkv=2, d=128, K=3, R=30, beta=0.2)
@@ -302,11 +339,14 @@ def test_route_score_backward(name):
     assert not gx[:, other].any(), "dx rows outside the queried set stay zero"
 
 
-def test_route_layer_backward_end_to_end():
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_route_layer_backward_end_to_end(dtype):
     """The three backward calls chained (attention, scoring, pooling) give the whole
-    layer's gradients with the oracle's selection held fixed."""
-    cfg = get_config("prefill_16k", N=10, Hq=8, Hkv=2, d=128, r=16, D=96, K=3, R=30, beta=0.3)
-    print("[case] route layer backward end to end", flush=True)
+    layer's gradients with the oracle's selection held fixed: within the bf16
+    tolerance for bf16 inputs, within 1e-5 for float32 inputs (every call then
+    computes in float32)."""
+    cfg = get_config("prefill_16k", N=10, Hq=8, Hkv=2, d=128, r=16, D=96, K=3, R=30, beta=0.3, dtype=dtype)
+    print(f"[case] route layer backward end to end, {dtype}", flush=True)
     inp = route_inputs(cfg)
     f = {n: as_f64(inp[n]) for n in ("q", "k", "v", "x", "A", "Bm")}
     queries = np.arange(cfg.T)
@@ -332,8 +372,9 @@ def test_route_layer_backward_end_to_end():
                 dx=rel_err(f64(sc["dx"]), want["dx"]), dA=rel_err(f64(sc["dA"]), want["dA"]),
                 dBm=rel_err(f64(sc["dBm"]), want["dBm"]))
     print("    " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    tol = BWD_TOL if dtype == "bf16" else 1e-5
     for n, e in errs.items():
-        assert e < BWD_TOL, f"{n} error {e:.3e}"
+        assert e < tol, f"{n} error {e:.3e}"
 
 
 @pytest.mark.timeout(300)
