@@ -511,6 +511,57 @@ def test_swa(case):
     assert o_err < OUT_TOL[c["dtype"]] and l_err < LSE_TOL[c["dtype"]]
 
 
+def _random_swa_cases(n=10, seed=4242):
+    """Seeded shapes across the SWA kernel's plans: 1 to 8 heads per group (one, two or four
+    loading waves), d 64 / 128, any length and radius (partial tiles, radii past the
+    sequence, radius 0), bf16 and float32."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for j in range(n):
+        G = int(rng.choice([1, 2, 3, 4, 7, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        L = int(rng.integers(1, 1600))
+        mode = int(rng.integers(0, 3))
+        R = 0 if mode == 0 else int(rng.integers(1, 200) if mode == 1 else rng.integers(L // 2 + 1, 2 * L + 2))
+        d = int(rng.choice([64, 128]))
+        dt = "fp32" if j % 4 == 3 else "bf16"
+        out.append((f"random {j}", dict(B=int(rng.integers(1, 3)), Hq=G * Hkv, Hkv=Hkv, L=L, d=d, R=R, dtype=dt)))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_swa_cases(), ids=lambda c: c[0])
+def test_swa_random_shapes(case):
+    test_swa(case)
+
+
+def _random_route_cases(n=8, seed=5151):
+    """Seeded whole-layer shapes: chunk counts from 2 to 48, GQA groups of 1 to 8 heads,
+    d 64 / 128, K 0 to 16, radii from 0 past the sequence, partial query ranges, an
+    entropy weight, bf16 and float32."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for j in range(n):
+        N = int(rng.integers(2, 49))
+        G = int(rng.choice([1, 2, 4, 7, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        T = N * 63
+        q0 = int(rng.integers(0, T // 2)) if j % 3 == 1 else 0
+        nq = int(rng.integers(1, T - q0 + 1)) if j % 3 == 1 else None
+        dt = "fp32" if j % 4 == 2 else "bf16"
+        over = dict(N=N, Hq=G * Hkv, Hkv=Hkv, d=int(rng.choice([64, 128])), r=16, D=96,
+                    K=int(rng.integers(0, 17)), R=[0, int(rng.integers(1, 300)), 4000][int(rng.integers(0, 3))],
+                    beta=float(rng.choice([0.0, 0.5])), dtype=dt)
+        out.append((f"random {j}", over, q0, nq))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_route_cases(), ids=lambda c: c[0])
+def test_route_layer_random_shapes(case):
+    name, over, q0, nq = case
+    cfg = get_config("tiny_fp32", **over)
+    route_parity(cfg, q0=q0, nq=nq, label=f"{name} {over} q0={q0} nq={nq}")
+
+
 @pytest.mark.timeout(600)
 def test_stack_64k_route_layer_sampled():
     """A route layer of the 64K stack (N = 1,024 chunks: scoring takes the general path, the
