@@ -875,6 +875,66 @@ __device__ __forceinline__ float tile_softmax(f32x4 sacc[4], int mode, int lo, i
   return alpha;
 }
 
+// The lean softmax of a remote visit on which only one query of the tile is active:
+// the lanes of half ACT (lane % 16 / 8 == ACT) hold its head columns, the other half
+// the idle query's. The lane pair (l, l ^ 8) of a 16-lane row shares the active
+// column's 16 scores of that row group: the active lane keeps those of m-tiles 0 and
+// 1, its partner takes those of m-tiles 2 and 3 through a DPP rotation by 8, so each
+// lane exponentiates 8 scores instead of 16. Per score the arithmetic is that of
+// tile_softmax in mode 2 (valid active lanes); the idle query keeps its state and
+// gets P = 0.
+template <int ACT>
+__device__ __forceinline__ float tile_softmax_half(f32x4 sacc[4], bool valid, float zc, float sl2, int g16, int lane,
+                                                   float& m, float& l, s16x8 pf[2]) {
+  constexpr int kIdle = ACT == 0 ? 0xC : 0x3;   // DPP bank mask of the idle half (4 lanes per bank)
+  constexpr int kAct = ACT == 0 ? 0x3 : 0xC;
+  constexpr int kRor8 = 0x128;                   // row_ror:8
+  const bool act = ((lane >> 3) & 1) == ACT;
+  if (g16 == 3) sacc[3][3] = -INFINITY;   // chunk slot 63: the routing mask, never a key
+  float x[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    x[r] = __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(sacc[r >> 2][r & 3]),
+                                                                 (int)__float_as_uint(sacc[2 + (r >> 2)][r & 3]),
+                                                                 kRor8, 0xF, kIdle, false));
+  float mx = max3(x[0], x[1], max3(x[2], x[3], max3(x[4], x[5], max2(x[6], x[7]))));
+  mx = max2(mx, __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(mx), kRor8, 0xF, 0xF, false)));
+  mx = col_max(mx);
+  const float mb = mx * sl2;
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    x[r] = fast_exp2(fmaf(x[r], sl2, -mb));
+    rs += x[r];
+  }
+  rs += __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(rs), kRor8, 0xF, 0xF, false));
+  rs = col_sum(rs);
+  const bool on = valid && act;
+  const float m_old = m;
+  const float m_cand = on ? max2(m_old, zc) : m_old;
+  const float m_new = m_cand > m_old + 8.f ? m_cand : m_old;
+  const float alpha = fast_exp2(m_old - m_new);
+  const float wz = fast_exp2(zc - m_new);
+  float scale = on ? wz * __builtin_amdgcn_rcpf(rs) : 0.f;
+  l = on ? l * alpha + wz : l;
+  m = m_new;
+  // the partner lanes scale the active column's scores with its factor
+  scale = __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(scale), (int)__float_as_uint(scale),
+                                                                kRor8, 0xF, kIdle, false));
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  u32x4 p0, p1;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t wv = pack2_bf16(x[2 * h] * scale, x[2 * h + 1] * scale);
+    // m-tiles 0, 1: the active lane's own words; 2, 3: its partner's, rotated back
+    p1[h] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, kRor8, 0xF, kAct, false);
+    p0[h] = act ? wv : 0u;
+  }
+  pf[0] = __builtin_bit_cast(s16x8, p0);
+  pf[1] = __builtin_bit_cast(s16x8, p1);
+  return alpha;
+}
+
 // S^T for NT tiles sharing every K fragment read.
 template <int D, int NT>
 __device__ __forceinline__ void s_tiles(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4], int lane) {
@@ -1369,8 +1429,14 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
         s_tile_lean<D>(kvb + ek * HE, qf[t], sacc);
         if (t == last) release(ek);
         s16x8 pf[2];
-        const float alpha = partial ? tile_softmax<true>(sacc, mode, lo, hi, zc, p.sl2, g16, mrow[t], lrow[t], pf)
-                                    : tile_softmax<false>(sacc, mode, lo, hi, zc, p.sl2, g16, mrow[t], lrow[t], pf);
+        float alpha;
+        if (!inr && tb != 3u) {   // uniform: a remote chunk that one query of the tile selected
+          alpha = tb == 1u ? tile_softmax_half<0>(sacc, rv[t], zc, p.sl2, g16, lane, mrow[t], lrow[t], pf)
+                           : tile_softmax_half<1>(sacc, rv[t], zc, p.sl2, g16, lane, mrow[t], lrow[t], pf);
+        } else {
+          alpha = partial ? tile_softmax<true>(sacc, mode, lo, hi, zc, p.sl2, g16, mrow[t], lrow[t], pf)
+                          : tile_softmax<false>(sacc, mode, lo, hi, zc, p.sl2, g16, mrow[t], lrow[t], pf);
+        }
         if (__ballot(alpha != 1.f) != 0ull) {
 #pragma unroll
           for (int dm = 0; dm < D / 16; ++dm)
