@@ -346,6 +346,56 @@ def test_determinism_and_decode_split_matches_prefill():
     assert max_err(f64(lc), f64(a["lse"][:, :, q0:])) < LSE_TOL["bf16"]
 
 
+def test_routed_attention_chunk_logit_extremes():
+    """The pooled prefill kernel on given selections whose chunk logits force every
+    branch of its online softmax, checked against the oracle: rows whose logits climb
+    by 12 at each selected chunk (a rescale at every remote visit), fall by 12, lie far
+    below the window (chunk weights near zero), or are ordinary; some rows select fewer
+    chunks than K (-1 / -inf padding). Most remote visits have one active query of the
+    tile, the path whose lane pairs share that query's scores. 28/4 heads, N = 128."""
+    cfg = get_config("tiny_fp32", N=128, Hq=28, Hkv=4, d=128, r=32, D=256, K=8, R=64, dtype="bf16")
+    print("[case] chunk logit extremes: N=128 Hq=28 Hkv=4 K=8 R=64 bf16", flush=True)
+    assert _routed_plan_ws(cfg, cfg.K, cfg.T) == 0, "the whole-range call must take the pooled prefill plan"
+    inp = route_inputs(cfg)
+    rng = np.random.default_rng(20261204)
+    B, Hq, Hkv, G, K, T = cfg.B, cfg.Hq, cfg.Hkv, cfg.G, cfg.K, cfg.T
+    idx = np.full((B, Hkv, T, K), -1, dtype=np.int32)
+    zsel = np.full((B, Hq, T, K), -np.inf, dtype=np.float32)
+    c = np.arange(cfg.N)
+    for t in range(T):
+        # remote chunks of query t: none of their content indices lies in its window
+        cand = c[(63 * c + 62 < t - cfg.R) | (63 * c > t + cfg.R)]
+        m = min(K, len(cand)) - (3 if t % 7 == 0 else 0)
+        kk = np.arange(m)
+        pattern = t % 4
+        for g in range(Hkv):
+            idx[0, g, t, :m] = np.sort(rng.choice(cand, size=m, replace=False))
+            for hh in range(G):
+                if pattern == 0:
+                    z = -20.0 + 12.0 * kk
+                elif pattern == 1:
+                    z = 40.0 - 12.0 * kk
+                elif pattern == 2:
+                    z = np.full(m, -60.0)
+                else:
+                    z = rng.normal(0.0, 2.0, size=m)
+                zsel[0, g * G + hh, t, :m] = z + 0.5 * hh
+    dev = {k: to_dev(v) for k, v in inp.items() if k in ("q", "k", "v")}
+    o, lse = lcr.routed_attention(dev["q"], dev["k"], dev["v"], torch.from_numpy(idx).cuda(),
+                                  torch.from_numpy(zsel).cuda(), radius=cfg.R, scale=cfg.scale, want_lse=True)
+    torch.cuda.synchronize()
+    queries = np.unique(np.concatenate([np.arange(0, 44), np.arange(4000, 4044), np.arange(T - 44, T),
+                                        rng.choice(T, size=40, replace=False)]))
+    f = _f(inp)
+    o_ref, l_ref = O.routed_attention(f["q"][:, :, O.slot_of(queries)], f["k"], f["v"], idx[:, :, queries].astype(np.int64),
+                                      zsel[:, :, queries].astype(np.float64), cfg.R, cfg.scale, queries)
+    o_err = max_err(f64(o)[:, :, O.slot_of(queries)], o_ref)
+    l_err = max_err(f64(lse)[:, :, queries], l_ref)
+    print(f"    rows={len(queries)} o_err={o_err:.2e} lse_err={l_err:.2e}", flush=True)
+    assert o_err < OUT_TOL["bf16"], f"output error {o_err:.3e}"
+    assert l_err < LSE_TOL["bf16"], f"lse error {l_err:.3e}"
+
+
 def test_tile_order_independence():
     """The tiled kernels (fused scoring, pooled routed attention) give the same bits when
     their blocks walk the tiles in reversed order: no block depends on another or on the
