@@ -953,32 +953,13 @@ __device__ __forceinline__ void s_tiles(const bf16_t* buf, const QFrag<D, 1>* q,
   }
 }
 
-// The same for one tile, with the lane's K offsets derived in place from an asm
-// mbcnt (which the compiler cannot merge with another) instead of being kept live
-// across the chunk loop, where registers are short. Row 16 mt + l % 16 shares its
-// swizzle with row l % 16 (period 16 for d = 128, 8 row pairs for d = 64), so the
-// four m-tiles differ by immediate offsets.
-template <int D>
-__device__ __forceinline__ void s_tile_lean(const bf16_t* buf, const QFrag<D, 1>& q, f32x4 acc[4]) {
-  typedef TileLayout<D, true> TL;
-  int ln;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-  const int L16 = ln & 15, g16 = ln >> 4;
-  const bf16_t* rowp = buf + L16 * D;
-  const int sw = TL::swz_k(L16);
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt] = zero4();
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    const bf16_t* pk = rowp + (((4 * ks + g16) ^ sw) << 3);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(load8(pk + 16 * mt * D), q.f[ks][0], acc[mt]);
-  }
-}
-
 // S^T of NT tiles sharing every K fragment read, added to the accumulators as they
-// come in (which may hold a mask: -inf where a key is out of a row's window), with
-// the lane offsets formed in place as in s_tile_lean.
+// come in (which may hold a mask: -inf where a key is out of a row's window). The
+// lane's K offsets are derived in place from an asm mbcnt (which the compiler cannot
+// merge with another) instead of being kept live across the tile loop, where
+// registers are short. Row 16 mt + l % 16 shares its swizzle with row l % 16 (period
+// 16 for d = 128, 8 row pairs for d = 64), so the four m-tiles differ by immediate
+// offsets.
 template <int D, int NT>
 __device__ __forceinline__ void s_tiles_lean_acc(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4]) {
   typedef TileLayout<D, true> TL;
@@ -1035,6 +1016,43 @@ __device__ __forceinline__ void pv_tiles(const bf16_t* vbuf, const s16x8 (*pf)[2
       const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int t = 0; t < NT; ++t) o[t][dm] = mfma16(a, pf[t][ks], o[t][dm]);
+    }
+  }
+}
+
+// S^T and O^T += V^T P^T for one tile with lane offsets that the caller formed once
+// (element offsets into a K or V half: koff = (l % 16) D and ksw = that row's K
+// swizzle; voff = the V^T fragment's row and column offset of pv_tiles). The V
+// swizzle key is still formed in place from an asm mbcnt: keeping it live across
+// the chunk loop as well costs more in spills than it saves.
+template <int D>
+__device__ __forceinline__ void s_tile_pre(const bf16_t* buf, const QFrag<D, 1>& q, f32x4 acc[4], int koff, int ksw,
+                                           int g16) {
+  const bf16_t* rowp = buf + koff;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const bf16_t* pk = rowp + (((4 * ks + g16) ^ ksw) << 3);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(load8(pk + 16 * mt * D), q.f[ks][0], acc[mt]);
+  }
+}
+template <int D>
+__device__ __forceinline__ void pv_tile_pre(const bf16_t* vbuf, const s16x8* pf, f32x4* o, int voff) {
+  typedef TileLayout<D, true> TL;
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const int vkey = 8 * TL::swz_v(ln >> 2);
+  const bf16_t* base = vbuf + voff;
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) {
+    const bf16_t* bd = base + (vkey ^ (16 * dm));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const s16x4 lo = ds_read_tr(bd + 32 * ks * D);
+      const s16x4 hi = ds_read_tr(bd + (32 * ks + 16) * D);
+      o[dm] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[dm]);
     }
   }
 }
@@ -1322,6 +1340,9 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
   const int qq = (lane & 15) >> 3, hh = lane & 7;
   const int h = g * G + hh;
   const int R32 = (int)min((long long)p.R, Tcont);   // a wider radius selects the same keys
+  // lane offsets of the K and V fragment reads, formed once
+  const int koff = (lane & 15) * D, ksw = TL::swz_k(lane & 15);
+  const int voff = (lane >> 2) * D + 4 * (lane & 3);
   QFrag<D, 1> qf[TPW];
   f32x4 acc[TPW][D / 16];
   float mrow[TPW], lrow[TPW], znext[TPW];
@@ -1426,7 +1447,7 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
           znext[t] = p.zsel[zoff0 + 2 * p.K * t + min(ptr[t], p.K - 1)];   // lands while this chunk is processed
         }
         f32x4 sacc[4];
-        s_tile_lean<D>(kvb + ek * HE, qf[t], sacc);
+        s_tile_pre<D>(kvb + ek * HE, qf[t], sacc, koff, ksw, g16);
         if (t == last) release(ek);
         s16x8 pf[2];
         float alpha;
@@ -1450,7 +1471,7 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
           }
           ev = pos_half[2 * j + 1];
         }
-        pv_tiles<D, 1>(kvb + ev * HE, &pf, &acc[t]);
+        pv_tile_pre<D>(kvb + ev * HE, pf, acc[t], voff);
         if (t == last) release(ev);
       }
       if (failed) break;
