@@ -346,15 +346,18 @@ def test_determinism_and_decode_split_matches_prefill():
     assert max_err(f64(lc), f64(a["lse"][:, :, q0:])) < LSE_TOL["bf16"]
 
 
-def test_routed_attention_chunk_logit_extremes():
+@pytest.mark.parametrize("heads", [(28, 4, 128), (16, 2, 64), (4, 2, 128)], ids=lambda h: f"{h[0]}/{h[1]} d{h[2]}")
+def test_routed_attention_chunk_logit_extremes(heads):
     """The pooled prefill kernel on given selections whose chunk logits force every
     branch of its online softmax, checked against the oracle: rows whose logits climb
     by 12 at each selected chunk (a rescale at every remote visit), fall by 12, lie far
     below the window (chunk weights near zero), or are ordinary; some rows select fewer
     chunks than K (-1 / -inf padding). Most remote visits have one active query of the
-    tile, the path whose lane pairs share that query's scores. 28/4 heads, N = 128."""
-    cfg = get_config("tiny_fp32", N=128, Hq=28, Hkv=4, d=128, r=32, D=256, K=8, R=64, dtype="bf16")
-    print("[case] chunk logit extremes: N=128 Hq=28 Hkv=4 K=8 R=64 bf16", flush=True)
+    tile, the path whose lane pairs share that query's scores. N = 128; GQA groups of 7,
+    8 and 2 heads (idle head lanes in the tile), d = 128 and 64."""
+    Hq, Hkv, d = heads
+    cfg = get_config("tiny_fp32", N=128, Hq=Hq, Hkv=Hkv, d=d, r=32, D=256, K=8, R=64, dtype="bf16")
+    print(f"[case] chunk logit extremes: N=128 Hq={Hq} Hkv={Hkv} d={d} K=8 R=64 bf16", flush=True)
     assert _routed_plan_ws(cfg, cfg.K, cfg.T) == 0, "the whole-range call must take the pooled prefill plan"
     inp = route_inputs(cfg)
     rng = np.random.default_rng(20261204)
