@@ -1057,20 +1057,8 @@ __device__ __forceinline__ void pv_tile_pre(const bf16_t* vbuf, const s16x8* pf,
   }
 }
 
-// One half (K or V) of a chunk: NI = D / 8 direct-to-LDS instructions of 1 KB.
-template <int D>
-__device__ __forceinline__ void dma_half(const bf16_t* src, bf16_t* dst, bool is_v, int lane) {
-  typedef TileLayout<D, true> TL;
-  constexpr int NI = D / 8, RPI = 512 / D, BPR = D / 8;
-#pragma unroll
-  for (int ii = 0; ii < NI; ++ii) {
-    const int pr = ii * RPI + lane / BPR, pb = lane % BPR;
-    const int sw = is_v ? TL::swz_v(pr) : TL::swz_k(pr);
-    dma16(src + pr * D + ((pb ^ sw) << 3), dst + ii * 512);
-  }
-}
-
-// The same half with the global address split into a uniform 64-bit base
+// One half (K or V) of a chunk, NI = D / 8 direct-to-LDS instructions of 1 KB,
+// with the global address split into a uniform 64-bit base
 // (SGPRs) and per-lane 32-bit offsets that depend only on the lane and on the
 // instruction's position in a group of four (the swizzle repeats every 16 rows,
 // one group spans 4 KB). voff[u] is precomputed once; per instruction only M0

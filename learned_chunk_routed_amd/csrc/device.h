@@ -158,11 +158,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 // Reduction over the four lanes {l%16 + 16*g}: they share one MFMA output column.
 // v_permlane16_swap / v_permlane32_swap exchange 16-lane rows (resp. 32-lane
 // halves) between two registers; with both operands equal, element 0 and 1 of
