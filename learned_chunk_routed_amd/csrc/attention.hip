@@ -1020,38 +1020,40 @@ __device__ __forceinline__ void pv_tiles(const bf16_t* vbuf, const s16x8 (*pf)[2
   }
 }
 
-// S^T and O^T += V^T P^T for one tile with lane offsets that the caller formed once
-// (element offsets into a K or V half: koff = (l % 16) D and ksw = that row's K
-// swizzle; voff = the V^T fragment's row and column offset of pv_tiles). The V
-// swizzle key is still formed in place from an asm mbcnt: keeping it live across
-// the chunk loop as well costs more in spills than it saves.
+// S^T and O^T += V^T P^T for one tile of the pooled prefill kernel, on LDS byte
+// addresses. A pool entry starts at a multiple of 16 KB (the pool is the first thing
+// in the block's LDS, which holds no static variables), so the row swizzle and the
+// fragment's k-step (S) or column block (P V) combine by one XOR of the 16-byte block
+// bits: klane = row (l % 16) in bytes + ((l / 16) ^ that row's K swizzle) * 16, and
+// vlane = the V^T fragment's byte offset of pv_tiles with its swizzle key; both are
+// formed once per wave. The m-tiles and k-halves are immediate offsets.
+typedef __attribute__((address_space(3))) const s16x8 lds_cs16x8;
+__device__ __forceinline__ s16x8 lds_load8_at(uint32_t a) { return *(lds_cs16x8*)(size_t)a; }
+__device__ __forceinline__ s16x4 lds_read_tr_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a);
+}
 template <int D>
-__device__ __forceinline__ void s_tile_pre(const bf16_t* buf, const QFrag<D, 1>& q, f32x4 acc[4], int koff, int ksw,
-                                           int g16) {
-  const bf16_t* rowp = buf + koff;
+__device__ __forceinline__ void s_tile_x(uint32_t ebase, const QFrag<D, 1>& q, f32x4 acc[4], uint32_t klane) {
+  const uint32_t a0 = ebase + klane;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) acc[mt] = zero4();
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    const bf16_t* pk = rowp + (((4 * ks + g16) ^ ksw) << 3);
+    const uint32_t ak = a0 ^ (uint32_t)(ks << 6);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(load8(pk + 16 * mt * D), q.f[ks][0], acc[mt]);
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(lds_load8_at(ak + 16 * mt * D * 2), q.f[ks][0], acc[mt]);
   }
 }
 template <int D>
-__device__ __forceinline__ void pv_tile_pre(const bf16_t* vbuf, const s16x8* pf, f32x4* o, int voff) {
-  typedef TileLayout<D, true> TL;
-  int ln;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-  const int vkey = 8 * TL::swz_v(ln >> 2);
-  const bf16_t* base = vbuf + voff;
+__device__ __forceinline__ void pv_tile_x(uint32_t ebase, const s16x8* pf, f32x4* o, uint32_t vlane) {
+  const uint32_t a0 = ebase + vlane;
 #pragma unroll
   for (int dm = 0; dm < D / 16; ++dm) {
-    const bf16_t* bd = base + (vkey ^ (16 * dm));
+    const uint32_t ad = a0 ^ (uint32_t)(dm << 5);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const s16x4 lo = ds_read_tr(bd + 32 * ks * D);
-      const s16x4 hi = ds_read_tr(bd + (32 * ks + 16) * D);
+      const s16x4 lo = lds_read_tr_at(ad + 32 * ks * D * 2);
+      const s16x4 hi = lds_read_tr_at(ad + (32 * ks + 16) * D * 2);
       o[dm] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[dm]);
     }
   }
@@ -1138,12 +1140,15 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
   short* pos_of = reinterpret_cast<short*>(pos_chunk + p.N);                             // [N]
   // after setup, the same bytes hold per position the pool entries of its K (byte 2j) and V (2j + 1)
   unsigned char* pos_half = reinterpret_cast<unsigned char*>(pos_of);
-  __shared__ int s_n;
+  // the block's counters follow the tables (no static LDS: the pool starts at LDS address 0)
+  int* tail = reinterpret_cast<int*>(smem + (((size_t)NH * HE * sizeof(bf16_t) +
+                                                (size_t)p.N * (sizeof(MaskT) + 4 + 2) + 15) & ~(size_t)15));
+  int& s_n = tail[0];
+  int& s_fail = tail[1];
   // halves landed per producer: position j is producer j % kProd's (j / kProd)-th, its K the
   // producer's half 2 (j / kProd), its V half 2 (j / kProd) + 1
-  __shared__ int s_landed[kProd];
-  __shared__ int s_rem[NH];          // consumers still to finish the half held by a pool entry
-  __shared__ int s_fail;
+  int* s_landed = tail + 2;
+  int* s_rem = tail + 2 + kProd;   // consumers still to finish the half held by a pool entry
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
   const int nqb = (p.nq + QB - 1) / QB;
@@ -1328,9 +1333,10 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
   const int qq = (lane & 15) >> 3, hh = lane & 7;
   const int h = g * G + hh;
   const int R32 = (int)min((long long)p.R, Tcont);   // a wider radius selects the same keys
-  // lane offsets of the K and V fragment reads, formed once
-  const int koff = (lane & 15) * D, ksw = TL::swz_k(lane & 15);
-  const int voff = (lane >> 2) * D + 4 * (lane & 3);
+  // lane byte offsets of the K and V fragment reads within a pool entry, formed once
+  const uint32_t klane = (uint32_t)((lane & 15) * D * 2 + ((g16 ^ TL::swz_k(lane & 15)) << 4));
+  const uint32_t vlane = (uint32_t)(((lane >> 2) * D + 4 * (lane & 3) + 8 * TL::swz_v(lane >> 2)) * 2);
+  const uint32_t kvb0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)kvb;
   QFrag<D, 1> qf[TPW];
   f32x4 acc[TPW][D / 16];
   float mrow[TPW], lrow[TPW], znext[TPW];
@@ -1435,7 +1441,7 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
           znext[t] = p.zsel[zoff0 + 2 * p.K * t + min(ptr[t], p.K - 1)];   // lands while this chunk is processed
         }
         f32x4 sacc[4];
-        s_tile_pre<D>(kvb + ek * HE, qf[t], sacc, koff, ksw, g16);
+        s_tile_x<D>(kvb0 + (uint32_t)(ek * HE * 2), qf[t], sacc, klane);
         if (t == last) release(ek);
         s16x8 pf[2];
         float alpha;
@@ -1459,7 +1465,7 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
           }
           ev = pos_half[2 * j + 1];
         }
-        pv_tile_pre<D>(kvb + ev * HE, pf, acc[t], voff);
+        pv_tile_x<D>(kvb0 + (uint32_t)(ev * HE * 2), pf, acc[t], vlane);
         if (t == last) release(ev);
       }
       if (failed) break;
@@ -2833,7 +2839,7 @@ static size_t routed_lds(const RouteDims& dm, int K, int qblock, int waves) {
 static size_t prefill_lds(const RouteDims& dm, int nh, int tpw) {
   const size_t mask = tpw == 1 ? sizeof(PfCfg<1>::Mask) : sizeof(PfCfg<2>::Mask);
   const size_t b = (size_t)nh * 64 * dm.d * 2 + (size_t)dm.N * (mask + 4 + 2);
-  return (b + 15) & ~(size_t)15;
+  return ((b + 15) & ~(size_t)15) + 4 * (2 + 1 + 32);   // + the block's counters
 }
 
 // tiles per consumer wave of the pooled prefill kernel
