@@ -953,42 +953,6 @@ __device__ __forceinline__ void s_tiles(const bf16_t* buf, const QFrag<D, 1>* q,
   }
 }
 
-// S^T of NT tiles sharing every K fragment read, added to the accumulators as they
-// come in (which may hold a mask: -inf where a key is out of a row's window). The
-// lane's K offsets are derived in place from an asm mbcnt (which the compiler cannot
-// merge with another) instead of being kept live across the tile loop, where
-// registers are short. Row 16 mt + l % 16 shares its swizzle with row l % 16 (period
-// 16 for d = 128, 8 row pairs for d = 64), so the four m-tiles differ by immediate
-// offsets.
-template <int D, int NT>
-__device__ __forceinline__ void s_tiles_lean_acc(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4]) {
-  typedef TileLayout<D, true> TL;
-  int ln;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-  const int L16 = ln & 15, g16 = ln >> 4;
-  const bf16_t* rowp = buf + L16 * D;
-  const int sw = TL::swz_k(L16);
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    const bf16_t* pk = rowp + (((4 * ks + g16) ^ sw) << 3);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const s16x8 a = load8(pk + 16 * mt * D);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t][mt] = mfma16(a, q[t].f[ks][0], acc[t][mt]);
-    }
-  }
-}
-
-template <int D, int NT>
-__device__ __forceinline__ void s_tiles_lean(const bf16_t* buf, const QFrag<D, 1>* q, f32x4 (*acc)[4]) {
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[t][mt] = zero4();
-  s_tiles_lean_acc<D, NT>(buf, q, acc);
-}
-
 // O^T += V^T P^T for NT tiles sharing every V^T fragment read (vbuf: a V half).
 // The swizzle XORs an even key into the 16-byte block index, so the offset of
 // rows r0 + 32 ks + 16 u and columns col + 16 dm is the unswizzled offset of
@@ -1020,13 +984,14 @@ __device__ __forceinline__ void pv_tiles(const bf16_t* vbuf, const s16x8 (*pf)[2
   }
 }
 
-// S^T and O^T += V^T P^T for one tile of the pooled prefill kernel, on LDS byte
-// addresses. A pool entry starts at a multiple of 16 KB (the pool is the first thing
-// in the block's LDS, which holds no static variables), so the row swizzle and the
-// fragment's k-step (S) or column block (P V) combine by one XOR of the 16-byte block
-// bits: klane = row (l % 16) in bytes + ((l / 16) ^ that row's K swizzle) * 16, and
-// vlane = the V^T fragment's byte offset of pv_tiles with its swizzle key; both are
-// formed once per wave. The m-tiles and k-halves are immediate offsets.
+// S^T and O^T += V^T P^T on LDS byte addresses, for the pooled prefill kernel (one
+// tile) and the SWA kernel (NT tiles sharing every fragment read). A K or V half
+// starts at a multiple of 8 KB (the pool or ring is the first thing in the block's
+// LDS, and neither kernel declares static LDS), so the row swizzle and the fragment's
+// k-step (S) or column block (P V) combine by one XOR of the 16-byte block bits:
+// klane = row (l % 16) in bytes + ((l / 16) ^ that row's K swizzle) * 16, and vlane =
+// the V^T fragment's byte offset of pv_tiles with its swizzle key; both are formed
+// once per wave. The m-tiles and k-halves are immediate offsets.
 typedef __attribute__((address_space(3))) const s16x8 lds_cs16x8;
 __device__ __forceinline__ s16x8 lds_load8_at(uint32_t a) { return *(lds_cs16x8*)(size_t)a; }
 __device__ __forceinline__ s16x4 lds_read_tr_at(uint32_t a) {
@@ -1055,6 +1020,45 @@ __device__ __forceinline__ void pv_tile_x(uint32_t ebase, const s16x8* pf, f32x4
       const s16x4 lo = lds_read_tr_at(ad + 32 * ks * D * 2);
       const s16x4 hi = lds_read_tr_at(ad + (32 * ks + 16) * D * 2);
       o[dm] = mfma16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[dm]);
+    }
+  }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void s_tiles_x_acc(uint32_t ebase, const QFrag<D, 1>* q, f32x4 (*acc)[4], uint32_t klane) {
+  const uint32_t a0 = ebase + klane;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const uint32_t ak = a0 ^ (uint32_t)(ks << 6);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const s16x8 a = lds_load8_at(ak + 16 * mt * D * 2);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][mt] = mfma16(a, q[t].f[ks][0], acc[t][mt]);
+    }
+  }
+}
+template <int D, int NT>
+__device__ __forceinline__ void s_tiles_x(uint32_t ebase, const QFrag<D, 1>* q, f32x4 (*acc)[4], uint32_t klane) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[t][mt] = zero4();
+  s_tiles_x_acc<D, NT>(ebase, q, acc, klane);
+}
+template <int D, int NT>
+__device__ __forceinline__ void pv_tiles_x(uint32_t ebase, const s16x8 (*pf)[2], f32x4 (*o)[D / 16], uint32_t vlane) {
+  const uint32_t a0 = ebase + vlane;
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) {
+    const uint32_t ad = a0 ^ (uint32_t)(dm << 5);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const s16x4 lo = lds_read_tr_at(ad + 32 * ks * D * 2);
+      const s16x4 hi = lds_read_tr_at(ad + (32 * ks + 16) * D * 2);
+      const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) o[t][dm] = mfma16(a, pf[t][ks], o[t][dm]);
     }
   }
 }
@@ -2584,6 +2588,8 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
     mrow[tt] = kNegBig;
     lrow[tt] = 0.f;
   }
+  const uint32_t klane = (uint32_t)((lane & 15) * D * 2 + ((g16 ^ TL::swz_k(lane & 15)) << 4));
+  const uint32_t vlane = (uint32_t)(((lane >> 2) * D + 4 * (lane & 3) + 8 * TL::swz_v(lane >> 2)) * 2);
   const int R = min(p.R, L);   // a wider radius covers the same slots
   const int lo_all = max(0, t0 - R);
   const int hi_all = min(L - 1, t0 + 31 + R);
@@ -2687,13 +2693,12 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
   f32x4 sc[2][4], sn[2][4];
   arrive(0);
   if (inside(0)) {
-    s_tiles_lean<D, 2>(kvb, qf, sc);
+    s_tiles_x<D, 2>(lds0, qf, sc, klane);
   } else {
     s_init(0, sc);
-    s_tiles_lean_acc<D, 2>(kvb, qf, sc);
+    s_tiles_x_acc<D, 2>(lds0, qf, sc, klane);
   }
   for (int j = 0; j < ntile; ++j) {
-    const bf16_t* buf = kvb + (j % RING) * BUFE;
     s16x8 pf[2][2];
     float alpha[2];
     const bool nx = j + 1 < ntile;
@@ -2701,12 +2706,11 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
     // (after the last tile the products are formed once more on that tile and
     // dropped, which keeps them and the softmax in one scheduling region)
     const int jn = nx ? j + 1 : j;
-    const bf16_t* bufn = kvb + (jn % RING) * BUFE;
     // the products and the softmax in one region, one MFMA then a few softmax VALU
     // instructions in turn; the region is written twice so that the run between
     // the edges keeps zero-initialised products
     if (inside(jn)) {
-      s_tiles_lean<D, 2>(bufn, qf, sn);
+      s_tiles_x<D, 2>(lds0 + (uint32_t)((jn % RING) * BUFE * 2), qf, sn, klane);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         alpha[tt] = tile_softmax<false, false>(sc[tt], 1, 0, 63, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
@@ -2717,7 +2721,7 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
       }
     } else {
       s_init(jn, sn);
-      s_tiles_lean_acc<D, 2>(bufn, qf, sn);
+      s_tiles_x_acc<D, 2>(lds0 + (uint32_t)((jn % RING) * BUFE * 2), qf, sn, klane);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         alpha[tt] = tile_softmax<false, false>(sc[tt], 1, 0, 63, 0.f, p.sl2, g16, mrow[tt], lrow[tt], pf[tt]);
@@ -2736,7 +2740,7 @@ __global__ __launch_bounds__(512) void swa_bf16_kernel(SwaParams p) {
           for (int i = 0; i < 4; ++i) acc[tt][dm][i] *= alpha[tt];
       }
     }
-    pv_tiles<D, 2>(buf + TL::KE, pf, acc);
+    pv_tiles_x<D, 2>(lds0 + (uint32_t)(((j % RING) * BUFE + TL::KE) * 2), pf, acc, vlane);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
