@@ -889,6 +889,9 @@ __device__ __forceinline__ float tile_softmax_half(f32x4 sacc[4], bool valid, fl
   constexpr int kIdle = ACT == 0 ? 0xC : 0x3;   // DPP bank mask of the idle half (4 lanes per bank)
   constexpr int kAct = ACT == 0 ? 0x3 : 0xC;
   constexpr int kRor8 = 0x128;                   // row_ror:8
+  // row_shl:8 (lane l reads l + 8) or row_shr:8 (l - 8): the active lane reads its partner,
+  // the idle lane reads past its row and gets 0 (bound_ctrl)
+  constexpr int kToAct = ACT == 0 ? 0x108 : 0x118;
   const bool act = ((lane >> 3) & 1) == ACT;
   if (g16 == 3) sacc[3][3] = -INFINITY;   // chunk slot 63: the routing mask, never a key
   float x[8];
@@ -907,7 +910,7 @@ __device__ __forceinline__ float tile_softmax_half(f32x4 sacc[4], bool valid, fl
     x[r] = fast_exp2(fmaf(x[r], sl2, -mb));
     rs += x[r];
   }
-  rs += __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(rs), kRor8, 0xF, 0xF, false));
+  rs += __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(rs), kRor8, 0xF, 0xF, true));
   rs = col_sum(rs);
   const bool on = valid && act;
   const float m_old = m;
@@ -927,7 +930,7 @@ __device__ __forceinline__ float tile_softmax_half(f32x4 sacc[4], bool valid, fl
   for (int h = 0; h < 4; ++h) {
     const uint32_t wv = pack2_bf16(x[2 * h] * scale, x[2 * h + 1] * scale);
     // m-tiles 0, 1: the active lane's own words; 2, 3: its partner's, rotated back
-    p1[h] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, kRor8, 0xF, kAct, false);
+    p1[h] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, kToAct, 0xF, 0xF, true);
     p0[h] = act ? wv : 0u;
   }
   pf[0] = __builtin_bit_cast(s16x8, p0);
