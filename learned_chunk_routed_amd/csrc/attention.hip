@@ -1910,9 +1910,7 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
         }
       s16x8 pf[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int jq = 0; jq < 8; ++jq) pf[ks][jq] = (short)f2bf(jq < 4 ? ds[2 * ks][jq] : ds[2 * ks + 1][jq - 4]);
+      for (int ks = 0; ks < 2; ++ks) pf[ks] = pack8_bf16(ds[2 * ks], ds[2 * ks + 1]);
       // dQ^T += K^T dS^T: K^T read transposed from the swizzled K half. Rows r0 + 32 ks + 16 u
       // share the swizzle of r0 (period 16), so each column block is one XOR per lane.
       {

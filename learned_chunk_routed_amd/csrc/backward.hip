@@ -239,9 +239,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_kernel(BwdParams p) {
     // dQ^T += K^T dS^T: B operand = dS^T (keys as k, permuted as the S^T output)
     s16x8 pf[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[ks][j] = (short)f2bf(j < 4 ? ds[2 * ks][j] : ds[2 * ks + 1][j - 4]);
+    for (int ks = 0; ks < 2; ++ks) pf[ks] = pack8_bf16(ds[2 * ks], ds[2 * ks + 1]);
 #pragma unroll
     for (int dm = 0; dm < D / 16; ++dm)
 #pragma unroll
@@ -518,12 +516,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_kernel(BwdParams p) {
       // steps (rows 32 kq + 4 g16 + j and 32 kq + 16 + 4 g16 + j, as the S output holds them)
 #pragma unroll
       for (int kq = 0; kq < RS / 32; ++kq) {
-        s16x8 pa, da;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pa[j] = (short)f2bf(j < 4 ? pv[2 * kq][j] : pv[2 * kq + 1][j - 4]);
-          da[j] = (short)f2bf(j < 4 ? dsv[2 * kq][j] : dsv[2 * kq + 1][j - 4]);
-        }
+        const s16x8 pa = pack8_bf16(pv[2 * kq], pv[2 * kq + 1]);
+        const s16x8 da = pack8_bf16(dsv[2 * kq], dsv[2 * kq + 1]);
 #pragma unroll
         for (int nt = 0; nt < D / 16; ++nt) {
           const s16x8 bo = lds_col_frag(dos, LDR, 32 * kq + 4 * g16, 32 * kq + 16 + 4 * g16, 16 * nt, lane);

@@ -105,6 +105,18 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(hf32x2{a, b}, hbf16x2));
 }
 
+// Two groups of four floats -> eight bf16 (a, then b; round to nearest even, two
+// values per instruction): an MFMA operand formed from two 16-row output tiles.
+__device__ __forceinline__ s16x8 pack8_bf16(const float* a, const float* b) {
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  u32x4 w;
+  w[0] = pack2_bf16(a[0], a[1]);
+  w[1] = pack2_bf16(a[2], a[3]);
+  w[2] = pack2_bf16(b[0], b[1]);
+  w[3] = pack2_bf16(b[2], b[3]);
+  return __builtin_bit_cast(s16x8, w);
+}
+
 // x = hi + lo as pack8_split, with the round-to-nearest-even conversions done by
 // v_cvt_pk_bf16_f32 (two values per instruction).
 __device__ __forceinline__ void pack8_split_hw(const float* v, s16x8& hi, s16x8& lo) {
