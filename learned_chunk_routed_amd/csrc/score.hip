@@ -506,22 +506,28 @@ __global__ __launch_bounds__(64 * kSmallW) void qtilde_small_kernel(const bf16_t
 
 // ---------------------------------------------------------------------------- 2. scores
 
-// Split a float into NS bf16 planes (2: 16 significant bits, 3: 24 bits).
+// Split a float into NS bf16 planes (2: 16 significant bits, 3: 24 bits): each plane
+// is the round-to-nearest-even bf16 of what the planes before it leave, converted two
+// values per instruction (v_cvt_pk_bf16_f32).
 template <int NS>
 __device__ __forceinline__ void split_ns(const float* v, s16x8* out) {
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  u32x4 w[NS];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const bf16_t h = f2bf(v[j]);
-    const float r = v[j] - bf2f(h);
-    out[0][j] = (short)h;
-    if constexpr (NS == 2) {
-      out[1][j] = (short)f2bf(r);
-    } else {
-      const bf16_t m = f2bf(r);
-      out[1][j] = (short)m;
-      out[2][j] = (short)f2bf(r - bf2f(m));
+  for (int j = 0; j < 4; ++j) {
+    float a = v[2 * j], b = v[2 * j + 1];
+#pragma unroll
+    for (int pl = 0; pl < NS; ++pl) {
+      const uint32_t pw = pack2_bf16(a, b);
+      w[pl][j] = pw;
+      if (pl + 1 < NS) {
+        a -= __uint_as_float(pw << 16);
+        b -= __uint_as_float(pw & 0xFFFF0000u);
+      }
     }
   }
+#pragma unroll
+  for (int pl = 0; pl < NS; ++pl) out[pl] = __builtin_bit_cast(s16x8, w[pl]);
 }
 
 // NS = 2 for bf16 inputs (hi.hi + hi.lo + lo.hi), 3 for float32 inputs (six plane pairs).
