@@ -1104,7 +1104,7 @@ __device__ __forceinline__ void load8_split(const T* p, int n, s16x8& hi, s16x8&
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = j < n ? Elem<T>::to_f(p[j]) : 0.f;
-  pack8_split(v, hi, lo);
+  pack8_split_hw(v, hi, lo);
 }
 
 // dU[b,t,j] = sum_h sum_e dq~[b,h,t,e] Bm[j][h*D + e] on MFMA: one wave per 16 rows x RP

@@ -88,15 +88,6 @@ __device__ __forceinline__ s16x8 pack8(const float* v) {
   for (int j = 0; j < 8; ++j) r[j] = (short)f2bf(v[j]);
   return r;
 }
-__device__ __forceinline__ void pack8_split(const float* v, s16x8& hi, s16x8& lo) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bf16_t h, l;
-    split_bf16(v[j], h, l);
-    hi[j] = (short)h;
-    lo[j] = (short)l;
-  }
-}
 
 // Two floats -> packed bf16x2 (v_cvt_pk_bf16_f32, round to nearest even).
 typedef __bf16 hbf16x2 __attribute__((ext_vector_type(2)));
@@ -117,8 +108,9 @@ __device__ __forceinline__ s16x8 pack8_bf16(const float* a, const float* b) {
   return __builtin_bit_cast(s16x8, w);
 }
 
-// x = hi + lo as pack8_split, with the round-to-nearest-even conversions done by
-// v_cvt_pk_bf16_f32 (two values per instruction).
+// Eight floats x -> hi = bf16(x) and lo = bf16(x - hi), 16 significant bits in total,
+// with the round-to-nearest-even conversions done by v_cvt_pk_bf16_f32 (two values per
+// instruction).
 __device__ __forceinline__ void pack8_split_hw(const float* v, s16x8& hi, s16x8& lo) {
   typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
   u32x4 h, l;

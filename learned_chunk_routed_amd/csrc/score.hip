@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void u_kernel(const T* __restrict__ x, const T
         for (int j = 0; j < 8; ++j) xv[j] = 0.f;
       }
       s16x8 xh, xl;
-      if (kSplit) pack8_split(xv, xh, xl);
+      if (kSplit) pack8_split_hw(xv, xh, xl);
       else xh = pack8(xv);
 #pragma unroll
       for (int nt = 0; nt < RP / 16; ++nt) {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void q_kernel(const T* __restrict__ q, const T
         }
       }
     }
-    pack8_split(uv, uh[ks], ul[ks]);
+    pack8_split_hw(uv, uh[ks], ul[ks]);
   }
   __syncthreads();
 #pragma unroll
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(64 * kSmallW) void qtilde_small_kernel(const bf16_t
     float uv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) uv[j] = u_s[(16 * mt + L16) * US + 32 * ks + 8 * g16 + j];
-    pack8_split(uv, uh[ks], ul[ks]);
+    pack8_split_hw(uv, uh[ks], ul[ks]);
   }
 #pragma unroll
   for (int nn = 0; nn < D / 64; ++nn) {
@@ -1359,7 +1359,7 @@ __global__ __launch_bounds__(256) void qtilde_dec_kernel(const bf16_t* __restric
     float uv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) uv[j] = u_s[(16 * mt + L16) * US + 32 * ks + 8 * g16 + j];
-    pack8_split(uv, uh[ks], ul[ks]);
+    pack8_split_hw(uv, uh[ks], ul[ks]);
   }
 #pragma unroll
   for (int nn = 0; nn < NTW; ++nn) {
