@@ -935,13 +935,10 @@ __global__ __launch_bounds__(256) void sbwd_dqt_dense_kernel(const int32_t* __re
       const int cl = x / (D / 4), e = 4 * (x % (D / 4)), c = c0 + cl;
       f32x4 v = zero4();
       if (c < N) v = *reinterpret_cast<const f32x4*>(s + ((size_t)bh * N + c) * D + e);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16_t hi, lo;
-        split_bf16(v[j], hi, lo);
-        sp[0][cl * SS + e + j] = hi;
-        sp[1][cl * SS + e + j] = lo;
-      }
+      uint2 hi, lo;
+      split4_bf16(v, hi, lo);
+      *reinterpret_cast<uint2*>(&sp[0][cl * SS + e]) = hi;   // 8-byte aligned: SS and e are multiples of 4
+      *reinterpret_cast<uint2*>(&sp[1][cl * SS + e]) = lo;
     }
     __syncthreads();
     for (int x = tid; x < kDqR * K; x += 256) {
@@ -1026,13 +1023,10 @@ __global__ __launch_bounds__(256) void sbwd_ds_dense_kernel(const int32_t* __res
       const int tl = x / (D / 4), e = 4 * (x % (D / 4)), row = t0 + tl;
       f32x4 v = zero4();
       if (row < tend) v = *reinterpret_cast<const f32x4*>(qt + ((size_t)bh * nq + row) * D + e);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16_t hi, lo;
-        split_bf16(v[j], hi, lo);
-        qp[0][tl * QS + e + j] = hi;
-        qp[1][tl * QS + e + j] = lo;
-      }
+      uint2 hi, lo;
+      split4_bf16(v, hi, lo);
+      *reinterpret_cast<uint2*>(&qp[0][tl * QS + e]) = hi;   // 8-byte aligned: QS and e are multiples of 4
+      *reinterpret_cast<uint2*>(&qp[1][tl * QS + e]) = lo;
     }
     __syncthreads();
     for (int x = tid; x < kDsC * kDsT; x += 256) {

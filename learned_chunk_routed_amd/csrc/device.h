@@ -96,6 +96,15 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(hf32x2{a, b}, hbf16x2));
 }
 
+// Four floats x -> hi = bf16(x) and lo = bf16(x - hi) as two 8-byte groups (element
+// 0 in the low half of the first word), conversions two values per instruction.
+__device__ __forceinline__ void split4_bf16(const f32x4& v, uint2& hi, uint2& lo) {
+  const uint32_t h01 = pack2_bf16(v[0], v[1]), h23 = pack2_bf16(v[2], v[3]);
+  hi = make_uint2(h01, h23);
+  lo = make_uint2(pack2_bf16(v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xFFFF0000u)),
+                  pack2_bf16(v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xFFFF0000u)));
+}
+
 // Two groups of four floats -> eight bf16 (a, then b; round to nearest even, two
 // values per instruction): an MFMA operand formed from two 16-row output tiles.
 __device__ __forceinline__ s16x8 pack8_bf16(const float* a, const float* b) {
