@@ -1779,7 +1779,7 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
     p.dsum[rq] = dsum;
     for (int kk = 0; kk < p.K; ++kk) p.dzsel[rqk + kk] = 0.f;
   }
-  const float sc = p.scale;
+  const float sl2 = p.scale * kLog2e;   // the only live copy of the scale: dQ is scaled by sl2 * ln 2
   f32x4 dqa[D / 16];
 #pragma unroll
   for (int dm = 0; dm < D / 16; ++dm) dqa[dm] = zero4();
@@ -1828,7 +1828,7 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
       const bool win = rel + R32 >= 0 && rel - R32 <= kContent - 1;
       const int mode = (!qa || !rv) ? 0 : (win ? 1 : 2);
       const int lo = mode == 1 ? max(0, rel - R32) : 0;
-      const int hi = mode == 1 ? min(kContent - 1, rel + R32) : kContent - 1;
+      const int hi = mode == 1 ? min(kContent - 1, rel + R32) : (mode == 2 ? kContent - 1 : -1);
       int slot = 0;
       float z = 0.f;
       if (qa && !win) {
@@ -1863,12 +1863,13 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
       }
       release(ev);
       // intra-chunk softmax statistics of every column (used where the chunk is selected)
+      // in base-2 units: every exponent below is one FMA and one exp2
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (16 * mt + 4 * g16 + e < kContent) mx = fmaxf(mx, sc * sacc[0][mt][e]);
+          if (16 * mt + 4 * g16 + e < kContent) mx = fmaxf(mx, sl2 * sacc[0][mt][e]);
       mx = col_max(mx);
       float l = 0.f, tu = 0.f;
 #pragma unroll
@@ -1876,19 +1877,24 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int jj = 16 * mt + 4 * g16 + e;
-          const float ex = jj < kContent ? __expf(sc * sacc[0][mt][e] - mx) : 0.f;
+          const float ex = jj < kContent ? fast_exp2(fmaf(sacc[0][mt][e], sl2, -mx)) : 0.f;
           l += ex;
           tu += ex * pacc[mt][e];
         }
       l = col_sum(l);
       tu = col_sum(tu);
-      const float il = 1.f / l, U = tu * il;
-      float Pc = 0.f;
+      const float U = tu / l;
+      // The weight of a key is exp2(s sl2 - b): b = lse log2 e inside the window; for a
+      // selected chunk b = mx + log2 l - (z - lse) log2 e = -cbias log2 e folds the chunk
+      // weight exp(z - lse) and the intra-chunk normalisation into the exponent.
+      float b = lse * kLog2e, sub = dsum;
       if (mode == 2) {
-        Pc = __expf(z - lse);
+        const float lc = mx + fast_log2(l);
+        b = lc - (z - lse) * kLog2e;
+        sub = U;
         if (g16 == 0) {
-          p.dzsel[rqk + slot] = Pc * (U - dsum);
-          p.cbias[rqk + slot] = z - lse - (mx + __logf(l));
+          p.dzsel[rqk + slot] = __expf(z - lse) * (U - dsum);
+          p.cbias[rqk + slot] = (z - lse) - lc * kLn2;
           p.cu[rqk + slot] = U;
         }
       }
@@ -1898,15 +1904,7 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int jj = 16 * mt + 4 * g16 + e;
-          float v = 0.f;
-          if (mode == 1) {
-            const float pw = (jj >= lo && jj <= hi) ? __expf(sc * sacc[0][mt][e] - lse) : 0.f;
-            v = pw * (pacc[mt][e] - dsum);
-          } else if (mode == 2) {
-            const float ex = jj < kContent ? __expf(sc * sacc[0][mt][e] - mx) : 0.f;   // recomputed: saves registers
-            v = Pc * ex * il * (pacc[mt][e] - U);
-          }
-          ds[mt][e] = v;
+          ds[mt][e] = (jj >= lo && jj <= hi) ? fast_exp2(fmaf(sacc[0][mt][e], sl2, -b)) * (pacc[mt][e] - sub) : 0.f;
         }
       s16x8 pf[2];
 #pragma unroll
@@ -1944,7 +1942,7 @@ __global__ __launch_bounds__(64 * kBqWaves) void bwd_query_pool_kernel(BwdQueryP
   if (rv) {
     float* dqr = p.dq + row;
 #pragma unroll
-    for (int dm = 0; dm < D / 16; ++dm) *reinterpret_cast<f32x4*>(dqr + 16 * dm + 4 * g16) = dqa[dm] * sc;
+    for (int dm = 0; dm < D / 16; ++dm) *reinterpret_cast<f32x4*>(dqr + 16 * dm + 4 * g16) = dqa[dm] * (sl2 * kLn2);
   }
 }
 

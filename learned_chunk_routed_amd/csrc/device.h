@@ -201,6 +201,7 @@ __device__ __forceinline__ float col_max(float v) { return xor32_max(xor16_max(v
 __device__ __forceinline__ float col_sum(float v) { return xor32_sum(xor16_sum(v)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }   // normal x only
 
 // ---------------------------------------------------------------- wait counters
 
