@@ -48,7 +48,7 @@ size_t lcr_workspace_bytes(int op, const lcr_dims* dims, int D, int r, int K, in
   const RouteDims dm = to_route_dims(dims);
   switch (op) {
     case LCR_OP_ROUTE_SCORE_TOPK:
-      return (K > 0 && nq > 0 && D > 0 && r > 0 && r <= 128) ? score_ws_bytes(dm, D, r, nq) : 0;
+      return (K > 0 && nq > 0 && D > 0 && r > 0 && r <= 128) ? score_ws_bytes(dm, D, r, nq, K) : 0;
     case LCR_OP_ROUTED_ATTENTION:
       return nq > 0 ? plan_routed_attention(dm, K, radius, nq).ws : 0;
     case LCR_OP_ROUTED_ATTENTION_BACKWARD:
@@ -91,10 +91,10 @@ int lcr_route_score_topk(const lcr_dims* dims, const void* q, const void* x, con
   if (st != LCR_OK) return st;
   if (K == 0 || nq == 0) return LCR_OK;
   const RouteDims dm = to_route_dims(dims);
-  const size_t need = score_ws_bytes(dm, D, r, nq);
+  const size_t need = score_ws_bytes(dm, D, r, nq, K);
   if (ws == nullptr || ws_bytes < need) return LCR_ERR_WORKSPACE;
   return hip_status(launch_route_score_topk(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx,
-                                            zsel, score_ws_carve(ws, dm, D, r, nq), (hipStream_t)stream));
+                                            zsel, score_ws_carve(ws, dm, D, r, nq, K), (hipStream_t)stream));
 }
 
 int lcr_routed_attention(const lcr_dims* dims, const void* q, const void* k, const void* v, const int32_t* idx,

@@ -32,8 +32,8 @@ struct ScoreWs {
   bf16_t* at;      // [rank padded, D padded to 32] A transposed (bf16 prefill path)
   bf16_t* bt;      // [Hq*d, rank padded] B transposed (bf16 prefill path)
 };
-size_t score_ws_bytes(const RouteDims& dm, int D, int r, int nq);
-ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int D, int r, int nq);
+size_t score_ws_bytes(const RouteDims& dm, int D, int r, int nq, int K);
+ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int D, int r, int nq, int K);
 hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const void* x, const void* A,
                                    const void* Bm, int D, int r, const float* s, const float* H,
                                    float beta, float scale, int K, int radius, int q0, int nq,

@@ -839,6 +839,7 @@ __device__ __forceinline__ int wave_topk_narrow(const uint32_t* key, int K, int 
 // LDS is the key table plus the chosen lists, which admits 32 queries per block at
 // N = 1024 within the 160 KB of a CU.
 constexpr int kRsWaves = 8;
+constexpr int kMaxGroup = 8;   // query heads per KV group of the fused scoring kernels
 
 // Row strides chosen for the LDS banks (64 banks of 4 bytes): key rows of rs3_zs(N)
 // words, 3 modulo 64, so that the group-maximum atomics of a wave (16 query rows x 16
@@ -900,6 +901,79 @@ __global__ __launch_bounds__(256) void split_frag_kernel(const float* __restrict
   *reinterpret_cast<s16x8*>(dst + 64 * 8) = lo;
 }
 
+// q~ = q + u B_h of head h for the 16 NT queries t0 .. t0 + 16 NT - 1 (u summed from
+// its nsplit partials; rows past nq are zero), split into bf16 hi + lo as the B
+// operand of the scoring product: lane l holds query 16 nt + l % 16 and
+// d = 32 ks + 8 (l / 16) + {0..7}, the layout of the q~^T output fragment. The product
+// u B_h runs on MFMA with u split into hi + lo and B exact (B comes transposed, so its
+// fragments are plain loads).
+template <int D, int RP, int NT>
+__device__ __forceinline__ void rs_qtilde(const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bt,
+                                          const float* __restrict__ upart, int nsplit, int B, int b, int h, int Hq,
+                                          long long L, int q0, int t0, int nq, int lane, s16x8 (&qh)[NT][D / 32],
+                                          s16x8 (&ql)[NT][D / 32]) {
+  constexpr int KS = D / 32, RK = RP / 32;
+  const int g16 = lane >> 4, L16 = lane & 15;
+  s16x8 bt[KS][2][RK];   // B_h^T: d rows 16 (2 ks + half) + L16, ranks 32 rk + 8 g16 + {0..7}
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int rk = 0; rk < RK; ++rk)
+        bt[ks][half][rk] = load8(Bt + ((size_t)h * D + 16 * (2 * ks + half) + L16) * RP + 32 * rk + 8 * g16);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int tq = t0 + 16 * nt + L16;
+    const int tc = tq < nq ? tq : nq - 1;
+    const bf16_t* qrow = q + ((size_t)b * Hq + h) * L * D + (size_t)slot_of((long long)q0 + tc) * D;
+    s16x4 q4[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        q4[ks][half] = *reinterpret_cast<const s16x4*>(qrow + 16 * (2 * ks + half) + 4 * g16);
+    s16x8 uh[RK], ul[RK];
+#pragma unroll
+    for (int rk = 0; rk < RK; ++rk) {
+      float uv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) uv[j] = 0.f;
+      for (int sp2 = 0; sp2 < nsplit; ++sp2) {
+        const float* up = upart + (((size_t)sp2 * B + b) * nq + tc) * RP + 32 * rk + 8 * g16;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uv[j] += a0[j];
+          uv[4 + j] += a1[j];
+        }
+      }
+      if (tq >= nq) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) uv[j] = 0.f;
+      }
+      pack8_split_hw(uv, uh[rk], ul[rk]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float qv[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int rk = 0; rk < RK; ++rk) {
+          acc = mfma16(bt[ks][half][rk], ul[rk], acc);
+          acc = mfma16(bt[ks][half][rk], uh[rk], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[4 * half + i] = acc[i] + bf2f((bf16_t)q4[ks][half][i]);
+      }
+      pack8_split_hw(qv, qh[nt][ks], ql[nt][ks]);
+    }
+  }
+}
+
 template <int D, int RP, int NT, int P, bool STAGE>
 __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bt, const float* __restrict__ upart, int nsplit,
@@ -928,66 +1002,7 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
 
   // ---- 0. q~ of head h as the scoring B operand, in registers
   s16x8 qh[NT][KS], ql[NT][KS];
-  if (hw) {
-    s16x8 bt[KS][2][RK];   // B_h^T: d rows 16 (2 ks + half) + L16, ranks 32 rk + 8 g16 + {0..7}
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int rk = 0; rk < RK; ++rk)
-          bt[ks][half][rk] = load8(Bt + ((size_t)h * D + 16 * (2 * ks + half) + L16) * RP + 32 * rk + 8 * g16);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int tq = t0 + 16 * nt + L16;
-      const int tc = tq < nq ? tq : nq - 1;
-      const bf16_t* qrow = q + ((size_t)b * Hq + h) * L * D + (size_t)slot_of((long long)q0 + tc) * D;
-      s16x4 q4[KS][2];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-          q4[ks][half] = *reinterpret_cast<const s16x4*>(qrow + 16 * (2 * ks + half) + 4 * g16);
-      s16x8 uh[RK], ul[RK];
-#pragma unroll
-      for (int rk = 0; rk < RK; ++rk) {
-        float uv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) uv[j] = 0.f;
-        for (int sp2 = 0; sp2 < nsplit; ++sp2) {
-          const float* up = upart + (((size_t)sp2 * B + b) * nq + tc) * RP + 32 * rk + 8 * g16;
-          const f32x4 a0 = *reinterpret_cast<const f32x4*>(up);
-          const f32x4 a1 = *reinterpret_cast<const f32x4*>(up + 4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            uv[j] += a0[j];
-            uv[4 + j] += a1[j];
-          }
-        }
-        if (tq >= nq) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) uv[j] = 0.f;
-        }
-        pack8_split_hw(uv, uh[rk], ul[rk]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        float qv[8];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int rk = 0; rk < RK; ++rk) {
-            acc = mfma16(bt[ks][half][rk], ul[rk], acc);
-            acc = mfma16(bt[ks][half][rk], uh[rk], acc);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) qv[4 * half + i] = acc[i] + bf2f((bf16_t)q4[ks][half][i]);
-        }
-        pack8_split_hw(qv, qh[nt][ks], ql[nt][ks]);
-      }
-    }
-  }
+  if (hw) rs_qtilde<D, RP, NT>(q, Bt, upart, nsplit, B, b, h, Hq, L, q0, t0, nq, lane, qh, ql);
   __syncthreads();   // keys initialised
 
   struct TileBuf {
@@ -1162,6 +1177,301 @@ __global__ __launch_bounds__(64 * kRsWaves) void route_score3_kernel(
       } else {
         for (int e = lane; e < len; e += 64) zrow[e] = zw[e];
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- 4b. one-sweep scoring
+//
+// route_score_stream_kernel: the block, the q~ registers and the split products of
+// route_score3_kernel, with the selection taken during the one sweep over the
+// summaries, so that no product is formed twice. The chunk row tiles are walked in
+// batches of TB tiles (CB = 16 TB chunks):
+//  A. wave w < G forms the scores of head w for the batch's chunks (each wave starts
+//     at another tile of the batch) and stores them as order-preserving keys in the
+//     batch table, one row per (head, query);
+//  B. after a block barrier, every wave takes QT / 8 of the queries: one lane per
+//     chunk of the batch forms the group maximum over the heads' keys, drops chunks
+//     that are not candidates (past N or in the query's window range) and keeps the
+//     ones whose key is strictly above the key of the query's K-th place (the chunks
+//     arrive in ascending order, so a tie belongs to the earlier chunk). These are
+//     merged into the query's list (in LDS, best first: key descending, chunk
+//     ascending among equal keys) by ranks: an entering chunk goes behind every
+//     entry with a key at least as large and every entering chunk ahead of it in
+//     that order; an entry moves back by the entering chunks with larger keys; the
+//     places past K leave. Each entry owns a row of per-head keys: the rows of the
+//     leaving entries pass to the entering chunks and are filled from the batch
+//     table. A second barrier frees the table for the next batch.
+// After the last batch the list of a query is its top K: written as idx in ascending
+// chunk order, with the per-head scores (keys mapped back to floats bit for bit) as
+// zsel; unfilled places are -1 and -inf. The selection is the same as the one of
+// route_score3_kernel (the order of chunks with equal keys decides ties in both); the
+// LDS does not grow with N: the batch table is G x QT x (CB + 4) words, the lists
+// QT x K x (3 + G) words and 64 words per wave hand rows over.
+__host__ __device__ inline size_t ss_lds(int NT, int G, int TB, int K) {
+  const size_t QT = (size_t)16 * NT;
+  return (size_t)G * QT * (16 * TB + 4) * 4 + QT * K * (3 + (size_t)G) * 4 + (size_t)kRsWaves * 64 * 4 + QT * 4;
+}
+
+// The order-preserving key of a float back to the float (the inverse of order_key on
+// every value that order_key does not clamp).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// LDS block barrier that leaves vector-memory loads in flight: every wave's LDS
+// accesses before it have completed; the tile loads of the next batch keep running.
+__device__ __forceinline__ void lds_block_barrier() {
+  wait_lgkm0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Minimum of a wave's values, in every lane: rotations within each 16-lane row
+// (DPP row_ror 8, 4, 2, 1), then the row pairs l ^ 16 and l ^ 32 (permlane swaps).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min((uint32_t)r[0], (uint32_t)r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+// Selections with at most this many elements past the K best drop them one at a time;
+// more take the bisection of wave_topk_thresholds.
+constexpr int kDropRounds = 16;
+
+template <int D, int RP, int NT, int TB>
+__global__ __launch_bounds__(64 * kRsWaves) void route_score_stream_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ Bt, const float* __restrict__ upart, int nsplit,
+    const bf16_t* __restrict__ sp, const float* __restrict__ H, float beta, float scale, int32_t* __restrict__ idx,
+    float* __restrict__ zsel, int B, int Hq, int Hkv, int N, int q0, int nq, int K, int R, int rev) {
+  constexpr int QT = 16 * NT, KS = D / 32, CB = 16 * TB, CBS = CB + 4;
+  constexpr int NBUF = NT <= 2 ? 3 : 2;   // tile buffers in the ring (registers allow three for two query tiles)
+  constexpr int QW = QT / kRsWaves;       // queries per wave in the selection
+  static_assert(TB % NBUF == 0, "a batch is a whole number of rounds of the tile ring");
+  static_assert(CB <= 64 && QT % kRsWaves == 0, "one lane per chunk of a batch");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, g16 = lane >> 4, L16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nqb = (nq + QT - 1) / QT;
+  const int tile = xcd_tile(nqb * B * Hkv, rev);   // (batch-group, query block), batch-group major
+  if (tile < 0) return;
+  const int bg = tile / nqb, b = bg / Hkv, g = bg - b * Hkv;
+  const int G = Hq / Hkv;
+  const int t0 = (tile - bg * nqb) * QT;
+  const long long L = (long long)N * kSlots;
+  const int NMT = (N + 15) / 16;
+  const int nbatch = (NMT + TB - 1) / TB;
+  uint32_t* st = reinterpret_cast<uint32_t*>(smem);          // [G][QT][CBS] keys of the batch per head
+  uint32_t* lk = st + (size_t)G * QT * CBS;                  // [QT][K] list keys, best first (0: empty)
+  int* lc = reinterpret_cast<int*>(lk + QT * K);             // [QT][K] their chunks (-1: empty)
+  int* ls = lc + QT * K;                                     // [QT][K] their rows of lh
+  uint32_t* lh = reinterpret_cast<uint32_t*>(ls + QT * K);   // [QT][K][G] per-head keys of a row's entry
+  for (int e = tid; e < QT * K; e += 64 * kRsWaves) {
+    lk[e] = 0u;
+    lc[e] = -1;
+    ls[e] = e % K;
+  }
+  for (int e = tid; e < QT; e += 64 * kRsWaves) ls[QT * K + QT * K * G + kRsWaves * 64 + e] = 0;   // lth
+
+  const bool hw = w < G;   // this wave owns head w (wave-uniform)
+  const int h = g * G + (hw ? w : 0);
+  s16x8 qh[NT][KS], ql[NT][KS];
+  if (hw) rs_qtilde<D, RP, NT>(q, Bt, upart, nsplit, B, b, h, Hq, L, q0, t0, nq, lane, qh, ql);
+  __syncthreads();   // lists initialised
+
+  struct TileBuf {
+    s16x8 sf[KS][2];
+    float hv[4];
+  };
+  const bf16_t* sph = sp + (size_t)(b * Hq + h) * NMT * KS * 2 * 64 * 8;
+  // tile of step it: batch it / TB, rotated by w within the batch
+  auto tile_at = [&](int it) {
+    const int b0 = it - it % TB, bs = min(TB, NMT - b0);
+    return b0 + (it - b0 + w) % bs;
+  };
+  auto load_tile = [&](int it, TileBuf& t) {
+    const int mt = tile_at(it);
+    const bf16_t* base = sph + (size_t)mt * KS * 2 * 64 * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) t.sf[ks][pl] = load8(base + ((ks * 2 + pl) * 64 + lane) * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * mt + 4 * g16 + i;
+      t.hv[i] = H[((size_t)b * Hq + h) * N + (c < N ? c : N - 1)];
+    }
+  };
+  // scores of the step's tile, as keys into the batch table (row (w, query), column
+  // chunk - first chunk of the batch)
+  auto score_tile = [&](int it, const TileBuf& t) {
+    f32x4 ahi[NT], ax[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      ahi[nt] = zero4();
+      ax[nt] = zero4();
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        ax[nt] = mfma16(t.sf[ks][0], ql[nt][ks], ax[nt]);
+        ax[nt] = mfma16(t.sf[ks][1], qh[nt][ks], ax[nt]);
+        ahi[nt] = mfma16(t.sf[ks][0], qh[nt][ks], ahi[nt]);
+      }
+    const int col = 16 * (tile_at(it) - (it - it % TB)) + 4 * g16;
+    typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      u32x4 kv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kv[i] = order_key((ahi[nt][i] + ax[nt][i]) * scale - beta * t.hv[i]);
+      *reinterpret_cast<u32x4*>(st + ((size_t)w * QT + 16 * nt + L16) * CBS + col) = kv;
+    }
+  };
+  // B: the batch's candidates into the lists of this wave's queries. A list holds its
+  // entries in ascending chunk order in places 0 .. K - 1 (key 0: an empty place), with
+  // lth the K-th largest key of a full list (0 otherwise). Lane p holds place p of the
+  // list, lane l chunk c0 + l of the batch: the top K of the two, in element order, is
+  // the new list.
+  int* wscr = ls + QT * K + QT * K * G + w * 64;   // this wave's row hand-over slots
+  uint32_t* lth = reinterpret_cast<uint32_t*>(wscr + (kRsWaves - w) * 64);   // [QT]
+  auto select_batch = [&](int bi) {
+    const int c0 = CB * bi;
+    const int c = c0 + lane;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll 1
+    for (int qq = 0; qq < QW; ++qq) {
+      const int qi = w + kRsWaves * qq, t = t0 + qi;
+      if (t >= nq) break;   // wave-uniform
+      const long long i = (long long)q0 + t;
+      uint32_t hk[kMaxGroup];   // every head's key at once (rows past G repeat the last head)
+#pragma unroll
+      for (int hh = 0; hh < kMaxGroup; ++hh)
+        hk[hh] = st[((size_t)min(hh, G - 1) * QT + qi) * CBS + (lane < CB ? lane : 0)];
+      uint32_t kb = hk[0];
+#pragma unroll
+      for (int hh = 1; hh < kMaxGroup; ++hh) kb = max(kb, hk[hh]);
+      const bool cand = lane < CB && c < N && ((63LL * c + 62 < i - R) | (63LL * c > i + R));
+      // only a key above the K-th of the list can enter (a tie belongs to the earlier chunk)
+      uint32_t key[2];
+      key[1] = cand && kb > lth[qi] ? kb : 0u;
+      if (__ballot(key[1] != 0u) == 0ull) continue;
+      key[0] = lane < K ? lk[qi * K + lane] : 0u;
+      const int pc = lane < K ? lc[qi * K + lane] : -1;
+      const int ps = lane < K ? ls[qi * K + lane] : 0;
+      uint32_t theta;
+      bool take_all;
+      int slot0 = -1, slot1 = -1;   // new places of this lane's list entry and batch chunk
+      int cnt;
+      const int n0 = __popcll(__ballot(key[0] != 0u));
+      const int drop = n0 + __popcll(__ballot(key[1] != 0u)) - K;   // elements past the K best
+      if (drop > kDropRounds) {
+        wave_topk_thresholds<2, 1>(reinterpret_cast<const uint32_t(*)[2]>(key), K, &theta, &take_all);
+        cnt = wave_topk_select<2>(key, K, theta, take_all, lane, [&](int slot, int j) {
+          if (j == 0) slot0 = slot;
+          else slot1 = slot;
+        });
+      } else {
+        // few past the K best: drop the smallest key drop times, among equal keys the
+        // last element (batch after list, higher lanes later), then keep the rest in order
+        for (int r = 0; r < drop; ++r) {
+          const uint32_t mn =
+              wave_min_u32(min(key[0] != 0u ? key[0] : ~0u, key[1] != 0u ? key[1] : ~0u));
+          const unsigned long long b1 = __ballot(key[1] == mn);
+          if (b1 != 0ull) {
+            if (lane == 63 - __builtin_clzll(b1)) key[1] = 0u;
+          } else {
+            const unsigned long long b0 = __ballot(key[0] == mn);
+            if (lane == 63 - __builtin_clzll(b0)) key[0] = 0u;
+          }
+        }
+        const unsigned long long m0 = __ballot(key[0] != 0u), m1 = __ballot(key[1] != 0u);
+        if (key[0] != 0u) slot0 = __popcll(m0 & lt);
+        if (key[1] != 0u) slot1 = __popcll(m0) + __popcll(m1 & lt);
+        cnt = __popcll(m0) + __popcll(m1);
+        take_all = cnt < K;
+        theta = take_all ? 0u : wave_min_u32(min(key[0] != 0u ? key[0] : ~0u, key[1] != 0u ? key[1] : ~0u));
+      }
+      // rows of lh: those of the list places not kept pass to the entering chunks, then
+      // to the places left empty, both in lane order
+      const bool freed = lane < K && slot0 < 0, enter = slot1 >= 0;
+      const unsigned long long fm = __ballot(freed), em = __ballot(enter);
+      const int nenter = __popcll(em);
+      if (freed) wscr[__popcll(fm & lt)] = ps;
+      __builtin_amdgcn_wave_barrier();
+      int row = 0;
+      if (enter) row = wscr[__popcll(em & lt)];
+      const bool empty = lane >= cnt && lane < K;
+      int erow = 0;
+      if (empty) erow = wscr[nenter + lane - cnt];
+      __builtin_amdgcn_wave_barrier();
+      if (slot0 >= 0) {
+        lk[qi * K + slot0] = key[0];
+        lc[qi * K + slot0] = pc;
+        ls[qi * K + slot0] = ps;
+      }
+      if (enter) {
+        lk[qi * K + slot1] = key[1];
+        lc[qi * K + slot1] = c;
+        ls[qi * K + slot1] = row;
+#pragma unroll
+        for (int hh = 0; hh < kMaxGroup; ++hh)
+          if (hh < G) lh[((size_t)qi * K + row) * G + hh] = hk[hh];
+      }
+      if (empty) {
+        lk[qi * K + lane] = 0u;
+        lc[qi * K + lane] = -1;
+        ls[qi * K + lane] = erow;
+      }
+      if (lane == 0) lth[qi] = take_all ? 0u : theta;
+    }
+  };
+  auto end_batch = [&](int bi) {
+    lds_block_barrier();   // the batch's keys are in the table
+    select_batch(bi);
+    lds_block_barrier();   // the table is free for the next batch
+  };
+
+  if (K > 0) {
+    if (hw) {
+      TileBuf tb[NBUF];
+#pragma unroll
+      for (int u = 0; u < NBUF - 1; ++u)
+        if (u < NMT) load_tile(u, tb[u]);
+      for (int bi = 0; bi < nbatch; ++bi) {
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          const int it = bi * TB + u;
+          if (it < NMT) {   // wave-uniform
+            if (it + NBUF - 1 < NMT) load_tile(it + NBUF - 1, tb[(u + NBUF - 1) % NBUF]);
+            score_tile(it, tb[u % NBUF]);
+          }
+        }
+        end_batch(bi);
+      }
+    } else {
+      for (int bi = 0; bi < nbatch; ++bi) end_batch(bi);
+    }
+  }
+
+  // the lists out (already in ascending chunk order, empty places last)
+  for (int qq = 0; qq < QW; ++qq) {
+    const int qi = w + kRsWaves * qq, t = t0 + qi;
+    if (t >= nq || K == 0) break;
+    if (lane < K) {
+      const bool valid = lk[qi * K + lane] != 0u;
+      const int ps = ls[qi * K + lane];
+      idx[((size_t)bg * nq + t) * K + lane] = valid ? lc[qi * K + lane] : -1;
+      for (int hh = 0; hh < G; ++hh)
+        zsel[(((size_t)b * Hq + g * G + hh) * nq + t) * K + lane] =
+            valid ? key_to_float(lh[((size_t)qi * K + ps) * G + hh]) : -INFINITY;
     }
   }
 }
@@ -1626,9 +1936,24 @@ static int u_splits(const RouteDims& dm, int Dh, int nq) {
   return (nslices + per - 1) / per;
 }
 
-// bf16 prefill-sized problems take the fused scoring kernel (no q~, z or zhat in memory).
-static bool fused_score_ok(const RouteDims& dm, int r, int nq) {
-  return dm.dtype == 1 && dm.N <= 1024 && r <= 64 && nq > kSmallQ && dm.Hq / dm.Hkv <= 8;
+// The one-sweep scoring kernel's LDS (48 queries per block) fits with batches of 64
+// chunks, else of 32 (0: neither).
+constexpr size_t kScoreLdsMax = 160 * 1024;
+static int stream_batch_tiles(const RouteDims& dm, int K) {
+  const int G = dm.Hq / dm.Hkv;
+  if (K < 1 || K > 64 || G > kMaxGroup) return 0;
+  if (ss_lds(3, G, 4, K) <= kScoreLdsMax) return 4;
+  if (ss_lds(3, G, 2, K) <= kScoreLdsMax) return 2;
+  return 0;
+}
+constexpr int kStreamMaxN = 16384;   // chunks (about 1M slots)
+
+// bf16 prefill-sized problems take a fused scoring kernel (no q~, z or zhat in memory):
+// the two-sweep kernel up to 1,024 chunks (its key table grows with N), the one-sweep
+// kernel beyond.
+static bool fused_score_ok(const RouteDims& dm, int r, int nq, int K) {
+  if (!(dm.dtype == 1 && r <= 64 && nq > kSmallQ && dm.Hq / dm.Hkv <= kMaxGroup)) return false;
+  return dm.N <= 1024 || (dm.N <= kStreamMaxN && stream_batch_tiles(dm, K) > 0);
 }
 
 // bf16 decode-sized problems (at most 32 queries) take the kernels of section 5.
@@ -1642,19 +1967,19 @@ static size_t bt_bytes(const RouteDims& dm, int r) { return (size_t)dm.Hq * dm.d
 // summaries as fragment-major bf16 hi/lo planes, rows padded to whole 16-chunk tiles
 static size_t frag_bytes(const RouteDims& dm) { return (size_t)dm.B * dm.Hq * ((dm.N + 15) / 16 * 16) * 2 * dm.d * 2; }
 
-size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq) {
+size_t score_ws_bytes(const RouteDims& dm, int Dh, int r, int nq, int K) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
   if (small_score_ok(dm, r, nq))
     return align256((size_t)u_small_splits(Dh) * dm.B * nq * rank_pad(r) * 4) +
            align256((size_t)dm.B * dm.Hq * kDecQ * 2 * dm.d * 2) + align256(rows_g * dm.N * 4) +
            align256(rows_h * dm.N * 4);
   const size_t upart = (size_t)u_splits(dm, Dh, nq) * dm.B * nq * rank_pad(r) * 4;
-  if (fused_score_ok(dm, r, nq))
+  if (fused_score_ok(dm, r, nq, K))
     return align256(upart) + align256(frag_bytes(dm)) + align256(at_bytes(Dh, r)) + align256(bt_bytes(dm, r));
   return align256(rows_h * dm.d * 4) + align256(rows_g * dm.N * 4) + align256(rows_h * dm.N * 4) + align256(upart);
 }
 
-ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
+ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq, int K) {
   const size_t rows_h = (size_t)dm.B * dm.Hq * nq, rows_g = (size_t)dm.B * dm.Hkv * nq;
   char* p = (char*)ws;
   ScoreWs out;
@@ -1673,7 +1998,7 @@ ScoreWs score_ws_carve(void* ws, const RouteDims& dm, int Dh, int r, int nq) {
     out.z = (float*)p;
     return out;
   }
-  if (fused_score_ok(dm, r, nq)) {
+  if (fused_score_ok(dm, r, nq, K)) {
     out.qt = nullptr;
     out.zhat = nullptr;
     out.z = nullptr;
@@ -1771,9 +2096,28 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
                      (const bf16_t*)Bm, r, HD, ws.bt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 48 queries per block up to N = 512 (the q~ of the wave's head for them stays in
-  // registers as three 16-query tiles), 32 beyond, where 48 rows of keys would pass
-  // the 160 KB of LDS
+  // Past 1,024 chunks one sweep, the selection taken during it: 48 queries per block,
+  // batches of 64 chunks (32 where those do not fit). Up to 1,024 the two-sweep kernel
+  // below is faster (it selects once per query, from all keys; the one-sweep kernel
+  // merges once per batch).
+  if (dm.N > 1024) {
+    const int tiles3 = (nq + 47) / 48 * dm.B * dm.Hkv;
+    const int tb = stream_batch_tiles(dm, K);
+    if (tb == 0) return hipErrorInvalidValue;   // excluded by fused_score_ok
+    {
+      const size_t lds = ss_lds(3, dm.Hq / dm.Hkv, tb, K);
+      auto kern = tb == 4 ? route_score_stream_kernel<D, RP, 3, 4> : route_score_stream_kernel<D, RP, 3, 2>;
+      e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles3)), dim3(64 * kRsWaves), lds, st, (const bf16_t*)q, ws.bt,
+                         ws.upart, nsplit, ws.splanes, H, beta, scale, idx, zsel, dm.B, dm.Hq, dm.Hkv, dm.N, q0, nq,
+                         K, radius, tile_order());
+      return hipGetLastError();
+    }
+  }
+  // Two sweeps: 48 queries per block up to N = 512 (the q~ of the wave's head for them
+  // stays in registers as three 16-query tiles), 32 beyond, where 48 rows of keys would
+  // pass the 160 KB of LDS.
   const int NT = dm.N <= 512 ? 3 : 2;
   // zsel staged in LDS when the rows fit
   const bool stage = rs3_lds(NT, dm.N, K, true) <= (size_t)(160 * 1024 - 512);
@@ -1879,7 +2223,7 @@ hipError_t launch_route_score_topk(const RouteDims& dm, const void* q, const voi
     return r <= 32 ? launch_small_score<128, 32>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st)
                    : launch_small_score<128, 64>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st);
   }
-  if (fused_score_ok(dm, r, nq)) {
+  if (fused_score_ok(dm, r, nq, K)) {
     if (dm.d == 64) return r <= 32 ? launch_fused_score<64, 32>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st)
                                    : launch_fused_score<64, 64>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st);
     return r <= 32 ? launch_fused_score<128, 32>(dm, q, x, A, Bm, D, r, s, H, beta, scale, K, radius, q0, nq, idx, zsel, ws, st)

@@ -254,13 +254,15 @@ def test_route_layer_prefill_edge(case):
     route_parity(cfg, queries=queries, q0=q0, nq=nq, label=f"prefill {name}")
 
 
-def test_topk_exact_ties_many_chunks():
-    """Exact ties in the group maximum at N = 600 (the fused scoring with 16 keys per lane):
+@pytest.mark.parametrize("N", [600, 1200])
+def test_topk_exact_ties_many_chunks(N):
+    """Exact ties in the group maximum at N = 600 (the two-sweep fused scoring, 16 keys per
+    lane) and N = 1,200 (the one-sweep fused scoring, 19 batches, the last one partial):
     chunk 2i + 1 has the summary and entropy of chunk 2i, so every score occurs twice. The
     chosen set must be a top K of the oracle's group maxima; where twins straddle the
     threshold, the smaller chunk is chosen (the oracle's tie rule); rows whose K-th and
     (K+1)-th scores differ by more than 1e-3 match the oracle exactly."""
-    B, Hq, Hkv, N, d, r, D, K, R, beta = 1, 8, 2, 600, 128, 16, 96, 31, 200, 0.5
+    B, Hq, Hkv, d, r, D, K, R, beta = 1, 8, 2, 128, 16, 96, 31, 200, 0.5
     G, L, T = Hq // Hkv, N * 64, N * 63
     print(f"[case] top-K ties N={N} K={K} Hq={Hq} Hkv={Hkv}", flush=True)
     rng = np.random.default_rng(2024)
@@ -615,19 +617,16 @@ def test_route_layer_random_shapes(case):
     route_parity(cfg, q0=q0, nq=nq, label=f"{name} {over} q0={q0} nq={nq}")
 
 
-@pytest.mark.timeout(600)
-def test_stack_64k_route_layer_sampled():
-    """A route layer of the 64K stack (N = 1,024 chunks: scoring takes the general path, the
-    routed kernel its chunk pool with 1,024 positions), inputs drawn on the device; the
-    oracle gets the same bits copied back (mask-query rows, sampled query and x rows, K, V)."""
+def _device_route_layer_sampled(cfg, layer, label, n_blocks=4, seed=11):
+    """A route layer with inputs drawn on the device; the oracle gets the same bits copied
+    back (mask-query rows, sampled query and x rows, K, V) and checks sampled queries."""
     from lcr_inputs import stack_layer_torch
-    cfg = get_config("stack_64k")
-    print(f"[case] stack_64k route layer 3: N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} K={cfg.K} R={cfg.R}", flush=True)
-    t = stack_layer_torch(cfg, 3, "cuda", route=True)
+    print(f"[case] {label}: N={cfg.N} Hq={cfg.Hq} Hkv={cfg.Hkv} K={cfg.K} R={cfg.R}", flush=True)
+    t = stack_layer_torch(cfg, layer, "cuda", route=True)
     res = lcr.route_layer(t["q"], t["k"], t["v"], t["x"], t["A"], t["Bm"], K=cfg.K, radius=cfg.R, beta=cfg.beta,
                           scale=cfg.scale, want_lse=True)
     torch.cuda.synchronize()
-    queries = sample_query_blocks(cfg.T, n_blocks=4, block=32, seed=11)
+    queries = sample_query_blocks(cfg.T, n_blocks=n_blocks, block=32, seed=seed)
     slots = torch.from_numpy(O.slot_of(queries)).cuda()
     q_rows = f64(t["q"][:, :, slots])
     q_mask = f64(t["q"].view(cfg.B, cfg.Hq, cfg.N, 64, cfg.d)[:, :, :, 63])
@@ -637,7 +636,7 @@ def test_stack_64k_route_layer_sampled():
                              queries=queries)
     tq = queries
     idx_gpu = res["idx"][:, :, torch.from_numpy(tq).cuda()].cpu().numpy().astype(np.int64)
-    same = check_selection(idx_gpu, ref, cfg.K, "stack_64k")
+    same = check_selection(idx_gpu, ref, cfg.K, label)
     # every sampled row is checked: rows whose selection differs from the oracle's (ungated
     # near-ties) get the oracle's attention recomputed with the GPU's chunks and its scores
     zref = O.gather_zsel(ref["z"], idx_gpu, cfg.G)
@@ -657,3 +656,17 @@ def test_stack_64k_route_layer_sampled():
           f"lse_err={l_err:.2e} z_err={z_err:.2e}", flush=True)
     assert o_err < OUT_TOL["bf16"] and l_err < LSE_TOL["bf16"]
     assert z_err < Z_TOL["bf16"] * max(1.0, np.abs(zref[fin]).max())
+
+
+@pytest.mark.timeout(600)
+def test_stack_64k_route_layer_sampled():
+    """A route layer of the 64K stack (N = 1,024 chunks: the two-sweep fused scoring at its
+    largest N, the routed kernel's chunk pool with 1,024 positions)."""
+    _device_route_layer_sampled(get_config("stack_64k"), 3, "stack_64k route layer 3")
+
+
+@pytest.mark.timeout(600)
+def test_prefill_128k_route_layer_sampled():
+    """A 128K prefill route layer (N = 2,048 chunks, 129,024 queries): the one-sweep fused
+    scoring (selection merged batch by batch) and a smaller chunk pool in the routed kernel."""
+    _device_route_layer_sampled(get_config("stack_64k", N=2048), 5, "prefill 128K route layer", seed=12)
