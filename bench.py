@@ -20,13 +20,15 @@ Printed JSON line (one, rank 0):
                slot attends to every slot: the sliding window with R >= L);
                dense_64k and dense_128k the same at 65,536 and 131,072 slots
   prefill_32k_entropy  ms per 32K route layer with the entropy term (batch 2, beta 0.5)
+  prefill_128k ms per 128K prefill route layer (2,048 chunks), with the scoring call and the
+               routed attention timed on their own
   stack_64k    ms per 28-layer attention forward at 64K (7 route layers, 21 SWA layers)
   backward_16k ms of the route layer's backward on the 16K-prefill workload:
                attention (dq, dk, dv, dzsel, with its MFMA roofline), scoring
                (dq, dx, dA, dBm, ds, dH) and pooling (dq mask rows, dk)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--no-decode] [--no-swa] [--only {prefill,decode,swa,dense,backward,entropy,stack,copy}]
+       [--no-decode] [--no-swa] [--only {prefill,decode,swa,dense,backward,entropy,prefill128k,stack,copy}]
 (--only copy runs a plain 1 GiB device copy, used to calibrate byte counters.)
 """
 import argparse
@@ -463,6 +465,51 @@ def bench_entropy(args, torch, lcr):
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def bench_prefill_128k(args, torch, lcr):
+    """A 128K prefill route layer: N = 2,048 chunks (131,072 slots, 129,024 content queries),
+    28/4 heads, d = 128, rank 64 from hidden 3584, K = 32, window radius 256, beta = 0, inputs
+    drawn on the device. Whole layers timed with HIP events (1 warmup, 3 timed), then the
+    scoring call and the routed attention timed on their own."""
+    from lcr_inputs import get_config, stack_layer_torch
+    cfg = get_config("stack_64k", N=2048)
+    log("[bench] prefill_128k: generating inputs on the device")
+    d = stack_layer_torch(cfg, 0, "cuda", route=True)
+    step, idx, b = _route_layer_runner(cfg, d, torch, lcr)
+    step()
+    torch.cuda.synchronize()
+    n = 3
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for _ in range(n):
+        step()
+    e[1].record()
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / n
+
+    def timed(fn):
+        out = []
+        for _ in range(n):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            out.append(ev[0].elapsed_time(ev[1]))
+        return float(np.mean(out))
+    score_ms = timed(lambda: lcr.route_score_topk(d["q"], d["x"], d["A"], d["Bm"], b["s"], b["H"], Hkv=cfg.Hkv,
+                                                  K=cfg.K, radius=cfg.R, beta=cfg.beta, scale=cfg.scale,
+                                                  idx=b["idx"], zsel=b["zsel"], ws=b["ws_s"]))
+    attn_ms = timed(lambda: lcr.routed_attention(d["q"], d["k"], d["v"], b["idx"], b["zsel"], radius=cfg.R,
+                                                 scale=cfg.scale, out=b["out"], ws=b["ws_a"]))
+    local, chunks = prefill_flops(cfg, int((idx >= 0).sum().item()))
+    tf = (local + chunks) / (attn_ms * 1e-3) / 1e12
+    del d, b
+    return {"ms_per_layer": round(ms, 3), "queries_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+            "route_score_topk_ms": round(score_ms, 3), "routed_attention_ms": round(attn_ms, 3),
+            "roofline": {"bound": "mfma", "kernel": "routed_prefill_kernel", "achieved": round(tf, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def bench_stack(args, torch, lcr):
     """The 28-layer attention forward at 64K: route layers at l % 4 == 3 (7 of them), bidirectional
     SWA with radius 1280 over all 65,536 slots in the other 21, each layer with its own inputs
@@ -587,7 +634,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-swa", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "swa", "dense", "backward", "entropy", "stack", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "swa", "dense", "backward", "entropy", "prefill128k",
+                                       "stack", "copy"],
                     default=None)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -613,6 +661,9 @@ def main():
         return
     if args.only == "entropy":
         print(json.dumps({"prefill_32k_entropy": bench_entropy(args, torch, lcr)}), flush=True)
+        return
+    if args.only == "prefill128k":
+        print(json.dumps({"prefill_128k": bench_prefill_128k(args, torch, lcr)}), flush=True)
         return
     if args.only == "stack":
         print(json.dumps({"stack_64k": bench_stack(args, torch, lcr)}), flush=True)
@@ -661,6 +712,7 @@ def main():
     if args.only is None:
         line["backward_16k"] = bench_backward(args, torch, lcr)
         line["prefill_32k_entropy"] = bench_entropy(args, torch, lcr)
+        line["prefill_128k"] = bench_prefill_128k(args, torch, lcr)
         line["stack_64k"] = bench_stack(args, torch, lcr)
     if args.only is None and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
