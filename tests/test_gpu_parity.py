@@ -226,6 +226,13 @@ PREFILL_EDGE = [
     # past 512 chunks the fused scoring takes 32-query blocks with 16 keys per lane
     ("700 chunks, entropy term", dict(N=700, K=32, beta=0.5)),
     ("1024 chunks, head dim 64", dict(N=1024, d=64, K=32)),
+    # past 1,024 chunks the one-sweep scoring: batches of 64 chunks, or of 32 for groups of 8 heads
+    ("1100 chunks, entropy term", dict(N=1100, K=32, beta=0.5)),
+    ("1100 chunks, eight-head groups", dict(N=1100, Hq=16, Hkv=2, K=32)),
+    ("1100 chunks, head dim 64, K=17, ragged query range", dict(N=1100, d=64, K=17), 20000, 3001),
+    ("1100 chunks, K=1", dict(N=1100, K=1)),
+    # K = 64 with groups of 8 heads does not fit the one-sweep kernel: the general path
+    ("1100 chunks, eight-head groups, K=64", dict(N=1100, Hq=16, Hkv=2, K=64, R=30)),
 ]
 
 
