@@ -490,6 +490,7 @@ struct RoutedParams {
   int nent, epb;  // decode-sized plan: entries per 2-query tile, entries per block
   int spin;       // polls before a wait on an LDS counter gives up (>= 1)
   int rev;        // tiles in reversed order (results do not depend on it)
+  int qb;         // pooled prefill kernel: queries per block (at most its compile-time count)
   float sl2;      // scale * log2(e)
 };
 
@@ -1158,11 +1159,13 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
   int* s_rem = tail + 2 + kProd;   // consumers still to finish the half held by a pool entry
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4;
-  const int nqb = (p.nq + QB - 1) / QB;
+  const int qb = p.qb;                         // this launch's queries per block (<= QB)
+  const int nqb = (p.nq + qb - 1) / qb;
   const int tile = xcd_tile(nqb * p.B * p.Hkv, p.rev);   // (batch-head, query block), batch-head major
   if (tile < 0) return;
   const int bg = tile / nqb, b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const int tb0 = (tile - bg * nqb) * QB;
+  const int tb0 = (tile - bg * nqb) * qb;
+  const int qend = min(tb0 + qb, p.nq);        // the block's queries are tb0 .. qend - 1
   const long long L = (long long)p.N * kSlots;
   const long long Tcont = (long long)p.N * kContent;
   const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k) + (size_t)bg * L * D;
@@ -1175,14 +1178,14 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
   if (tid < NH) s_rem[tid] = 0;
   for (int c = tid; c < p.N; c += NT) pos_of[c] = 0;
   __syncthreads();
-  const int t_last = min(tb0 + QB, p.nq) - 1;
+  const int t_last = qend - 1;
   // the block's window range: chunks in the window of any of its queries
   const int cw0 = (int)(max(0LL, (long long)p.q0 + tb0 - p.R) / kContent);
   const int cw1 = (int)(min(Tcont - 1, (long long)p.q0 + t_last + p.R) / kContent);
   for (int c = cw0 + tid; c <= cw1; c += NT) pos_of[c] = 1;
   for (int e = tid; e < QB * p.K; e += NT) {
     const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
-    const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
+    const int c = (t < qend) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
     if (c >= 0 && c < p.N) pos_of[c] = 1;
   }
   __syncthreads();
@@ -1209,12 +1212,12 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
   const int n = s_n;
   for (int e = tid; e < QB * p.K; e += NT) {
     const int qi = e / p.K, kk = e - qi * p.K, t = tb0 + qi;
-    const int c = (t < p.nq) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
+    const int c = (t < qend) ? p.idx[((size_t)bg * p.nq + t) * p.K + kk] : -1;
     if (c >= 0 && c < p.N) atomicOr(&pos_mask[pos_of[c]], MaskT(1) << qi);
   }
   for (int qi = w; qi < QB; qi += kWaves) {
     const int t = tb0 + qi;
-    if (t >= p.nq) continue;
+    if (t >= qend) continue;
     const long long i = (long long)p.q0 + t;
     const int c0 = (int)(max(0LL, i - p.R) / kContent), c1 = (int)(min(Tcont - 1, i + p.R) / kContent);
     for (int c = c0 + lane; c <= c1; c += 64) atomicOr(&pos_mask[pos_of[c]], MaskT(1) << qi);
@@ -1356,7 +1359,7 @@ __global__ __launch_bounds__(64 * pf_waves<TPW>()) void routed_prefill_kernel(Ro
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int tq = iq0 + 2 * t - p.q0;
-    rv[t] = tq < p.nq && hh < G;
+    rv[t] = tq < qend && hh < G;
     load_qfrag<bf16_t, D, 1>(qf[t], rv[t] ? reinterpret_cast<const bf16_t*>(p.q) +
                                                 (((size_t)b * p.Hq + h) * L + slot_of_i(iq0 + 2 * t)) * D
                                           : nullptr, lane);
@@ -2852,6 +2855,30 @@ static constexpr int kPfTiles = 2;
 // 2,048 measured slower, the combine then reads more partials)
 static constexpr long long kDecodeBlocks = 512;
 
+// Queries per block of the pooled prefill kernel (at most qmax, one block per CU at a
+// time). A launch of a few rounds of blocks leaves most CUs idle while its last,
+// partial round runs; where the full-size blocks take at most kBalanceRounds rounds,
+// the count that minimises rounds x queries per block is taken instead (the block
+// time scales with its queries), ties to the larger count. On 256 CUs the 16K prefill
+// (4 x 16,128 queries) goes from 1,468 blocks of 44 (5.7 rounds, six block times)
+// to 1,536 blocks of 42 (six rounds of 42/44 of a block time).
+constexpr int kCus = 256;            // compute units of an MI355X
+constexpr int kBalanceRounds = 8;
+static int balanced_qblock(long long nq, long long groups, int qmax) {
+  auto rounds = [&](int qb) { return ((nq + qb - 1) / qb * groups + kCus - 1) / kCus; };
+  if (nq <= 0 || rounds(qmax) > kBalanceRounds) return qmax;
+  int best = qmax;
+  long long best_cost = rounds(qmax) * qmax;
+  for (int qb = qmax - 1; qb >= (qmax + 1) / 2; --qb) {
+    const long long cost = rounds(qb) * qb;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = qb;
+    }
+  }
+  return best;
+}
+
 AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
   AttnPlan pl;
   pl.nent = 0;
@@ -2912,7 +2939,7 @@ AttnPlan plan_routed_attention(const RouteDims& dm, int K, int radius, int nq) {
         pl.nbuf = nh;
         pl.tiles = kPfTiles;
         pl.waves = kPfTiles == 1 ? pf_waves<1>() : pf_waves<2>();
-        pl.qblock = kPfTiles == 1 ? pf_qblock<1>() : pf_qblock<2>();
+        pl.qblock = balanced_qblock(nq, (long long)dm.B * dm.Hkv, kPfTiles == 1 ? pf_qblock<1>() : pf_qblock<2>());
         pl.lds = lds;
         break;
       }
@@ -2969,7 +2996,7 @@ static hipError_t launch_prefill_t(const RouteDims& dm, const AttnPlan& pl, cons
   auto kern = routed_prefill_kernel<D, NH, TPW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
   if (e != hipSuccess) return e;
-  const int tiles = (prm.nq + pf_qblock<TPW>() - 1) / pf_qblock<TPW>() * dm.B * dm.Hkv;
+  const int tiles = (prm.nq + prm.qb - 1) / prm.qb * dm.B * dm.Hkv;
   hipLaunchKernelGGL(kern, dim3(xcd_grid(tiles)), dim3(64 * pf_waves<TPW>()), pl.lds, st, prm);
   return hipGetLastError();
 }
@@ -3007,6 +3034,7 @@ hipError_t launch_routed_attention(const RouteDims& dm, const AttnPlan& pl, cons
   prm.epb = pl.epb;
   prm.spin = wait_limit();
   prm.rev = tile_order();
+  prm.qb = pl.qblock;
   prm.sl2 = scale * kLog2e;
   if (pl.kind == 2) return dm.d == 64 ? launch_prefill_d<64>(dm, pl, prm, st) : launch_prefill_d<128>(dm, pl, prm, st);
   if (pl.kind == 1) {
