@@ -1243,7 +1243,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 
 // Selections with at most this many elements past the K best drop them one at a time;
 // more take the bisection of wave_topk_thresholds.
-constexpr int kDropRounds = 16;
+constexpr int kDropRounds = 8;
 
 template <int D, int RP, int NT, int TB>
 __global__ __launch_bounds__(64 * kRsWaves) void route_score_stream_kernel(
