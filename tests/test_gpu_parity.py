@@ -232,6 +232,8 @@ PREFILL_EDGE = [
     ("1100 chunks, head dim 64, K=17, ragged query range", dict(N=1100, d=64, K=17), 20000, 3001),
     ("1100 chunks, K=1", dict(N=1100, K=1)),
     ("1100 chunks, batch 2", dict(N=1100, B=2, K=8, beta=0.25)),
+    # float32 past 1,024 chunks: per-head scores through memory, the block-tiled routed kernel
+    ("1100 chunks, float32", dict(N=1100, Hq=2, Hkv=1, d=64, K=8, dtype="fp32")),
     # K = 64 with groups of 8 heads does not fit the one-sweep kernel: the general path
     ("1100 chunks, eight-head groups, K=64", dict(N=1100, Hq=16, Hkv=2, K=64, R=30)),
 ]
