@@ -241,13 +241,28 @@ __global__ __launch_bounds__(256) void q_kernel(const T* __restrict__ q, const T
   }
 }
 
-// 1d. u_stream_kernel (bf16, prefill-sized): u = x A for 64 queries per block with
-//     the hidden dimension split over the 4 waves. x fragments stream from HBM
-//     straight into MFMA registers, and A comes transposed (rows = rank, padded with
-//     zeros to whole 32-wide k-steps), so both operands are plain 16-byte loads with
-//     kUsPD k-steps in flight per wave; the wave partials are summed through LDS and
-//     one partial set is written (no split of the hidden dimension in memory).
-constexpr int kUsPD = 4;   // k-steps of loads in flight per wave
+// LDS block barrier that leaves vector-memory loads in flight: every wave's LDS
+// accesses before it have completed; loads issued earlier keep running (__syncthreads
+// would wait for them too).
+__device__ __forceinline__ void lds_block_barrier() {
+  wait_lgkm0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 1d. u_stream_kernel (bf16, prefill-sized): u = x A for 64 queries per block, 8
+//     waves. x passes through LDS 256 columns (one stage) at a time: consecutive
+//     threads load consecutive 16-byte pieces of one row, so every row is read as
+//     512-byte runs (HBM serves scattered 64-byte pieces of thousands of rows at a
+//     third of its bandwidth), with kUsPD stages of loads in flight in registers.
+//     Wave w multiplies k-step w of each stage for all 64 rows against A transposed
+//     (rows = rank, zero-padded to whole stages; plain 16-byte loads from L2, in
+//     flight with the stage's x). The wave partials are summed through LDS and one
+//     partial set is written (no split of the hidden dimension in memory).
+constexpr int kUsPD = 2;               // stages of loads in flight per thread
+constexpr int kUsCols = 256;           // x columns per stage (8 k-steps, one per wave)
+constexpr int kUsRow = kUsCols + 8;    // LDS row stride of a staged x tile (elements)
 
 template <int RP>
 __global__ __launch_bounds__(256) void transpose_a_kernel(const bf16_t* __restrict__ A, int Dh, int r, int Dhp,
@@ -270,62 +285,77 @@ __global__ __launch_bounds__(256) void transpose_b_kernel(const bf16_t* __restri
 }
 
 template <int RP>
-__global__ __launch_bounds__(256) void u_stream_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ At,
+__global__ __launch_bounds__(512) void u_stream_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ At,
                                                        int Dh, int Dhp, float* __restrict__ upart, int N, int q0,
                                                        int nq) {
   constexpr int NTR = RP / 16;
   constexpr int US = RP + 4;
-  extern __shared__ __align__(16) unsigned char smem[];   // wave partials [4][64][US] f32
-  float* red = reinterpret_cast<float*>(smem);
+  constexpr int PPT = 64 * kUsCols / 8 / 512;   // 16-byte pieces of a stage per thread (4)
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* xs = reinterpret_cast<bf16_t*>(smem);       // [2][64][kUsRow] staged x
+  float* red = reinterpret_cast<float*>(smem);        // after the walk: wave partials [8][64][US]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g16 = lane >> 4, L16 = lane & 15;
   const int b = blockIdx.y, t0 = blockIdx.x * 64;
   const long long L = (long long)N * kSlots;
-  const int nks = Dhp / 32, kw = (nks + 3) / 4;
-  const int ks0 = min(w * kw, nks), n = min(nks, ks0 + kw) - ks0;   // this wave's k-steps
-  const bf16_t* xr[4];
+  const int nst = (Dhp + kUsCols - 1) / kUsCols;     // stages (the last one may be partial)
+  // this thread's pieces: rows (tid >> 5) + 16 j, 8-column group tid & 31 of every stage;
+  // rows past nq read the block's first row (never stored)
+  const int c8 = 8 * (tid & 31);
+  const bf16_t* xr[PPT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int t = t0 + 16 * mt + L16;
-    xr[mt] = x + ((size_t)b * L + slot_of((long long)q0 + (t < nq ? t : 0))) * Dh;
+  for (int j = 0; j < PPT; ++j) {
+    const int t = t0 + (tid >> 5) + 16 * j;
+    xr[j] = x + ((size_t)b * L + slot_of((long long)q0 + (t < nq ? t : t0))) * Dh;
   }
   f32x4 acc[4][NTR];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NTR; ++nt) acc[mt][nt] = zero4();
-  s16x8 xf[kUsPD][4], af[kUsPD][NTR];
-  // k-step ks into register slot p; past the wave's range a valid step is loaded and not used.
-  // No value is masked (that would make every load wait at once): rows past nq read row
-  // q0's data and are never stored, and pieces past Dh (Dh % 8 == 0: a piece is wholly in
-  // or out) read the row's first piece, which meets the zero padding of the transposed A.
-  auto load = [&](int ks, int p) {
-    ks = min(ks, nks - 1);
-    const int kg = 32 * ks + 8 * g16;
-    const int kx = kg < Dh ? kg : 0;
+  s16x8 xv[kUsPD][PPT], av[kUsPD][NTR];
+  // stage st into register slot p. Pieces past Dh read the row's first piece, which meets
+  // the zero padding of the transposed A; k-steps past Dhp read A's first k-step and are
+  // not multiplied. Nothing is masked, so no load waits for another.
+  auto load = [&](int st, int p) {
+    st = min(st, nst - 1);
+    const int col = kUsCols * st + c8;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) xf[p][mt] = load8(xr[mt] + kx);
+    for (int j = 0; j < PPT; ++j) xv[p][j] = load8(xr[j] + (col < Dh ? col : 0));
+    const int kg = kUsCols * st + 32 * w + 8 * g16;
 #pragma unroll
-    for (int nt = 0; nt < NTR; ++nt) af[p][nt] = load8(At + (size_t)(16 * nt + L16) * Dhp + kg);
+    for (int nt = 0; nt < NTR; ++nt) av[p][nt] = load8(At + (size_t)(16 * nt + L16) * Dhp + (kg < Dhp ? kg : 8 * g16));
   };
-  auto mul = [&](int p) {
+  // stage st (its x in slot p) through LDS buffer st & 1, then this wave's k-step of it
+  auto step = [&](int st, int p) {
+    bf16_t* xb = xs + (size_t)(st & 1) * 64 * kUsRow;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int j = 0; j < PPT; ++j)
+      *reinterpret_cast<s16x8*>(xb + ((tid >> 5) + 16 * j) * kUsRow + c8) = xv[p][j];
+    lds_block_barrier();   // the stage is in LDS; every wave is done with the buffer's previous stage
+    s16x8 af[NTR];
 #pragma unroll
-      for (int nt = 0; nt < NTR; ++nt) acc[mt][nt] = mfma16(xf[p][mt], af[p][nt], acc[mt][nt]);
-  };
+    for (int nt = 0; nt < NTR; ++nt) af[nt] = av[p][nt];
+    load(st + kUsPD, p);   // the slot is free: the next stage but kUsPD - 1 goes in flight
+    if (kUsCols * st + 32 * w < Dhp) {   // wave-uniform: this wave's k-step exists
 #pragma unroll
-  for (int p = 0; p < kUsPD; ++p) load(ks0 + p, p);
-  int it = 0;
-  for (; it + kUsPD <= n; it += kUsPD) {
+      for (int mt = 0; mt < 4; ++mt) {
+        const s16x8 xf = *reinterpret_cast<const s16x8*>(xb + (16 * mt + L16) * kUsRow + 32 * w + 8 * g16);
 #pragma unroll
-    for (int p = 0; p < kUsPD; ++p) {
-      mul(p);
-      load(ks0 + it + p + kUsPD, p);
+        for (int nt = 0; nt < NTR; ++nt) acc[mt][nt] = mfma16(xf, af[nt], acc[mt][nt]);
+      }
     }
+  };
+#pragma unroll
+  for (int p = 0; p < kUsPD; ++p) load(p, p);
+  int st = 0;
+  for (; st + kUsPD <= nst; st += kUsPD) {
+#pragma unroll
+    for (int p = 0; p < kUsPD; ++p) step(st + p, p);
   }
 #pragma unroll
   for (int p = 0; p < kUsPD; ++p)
-    if (it + p < n) mul(p);
+    if (st + p < nst) step(st + p, p);
+  __syncthreads();   // every wave is done with the staged x: the partials overlay it
   // D layout: lane holds u[query 16 mt + 4 g16 + i][rank 16 nt + L16]
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -334,14 +364,20 @@ __global__ __launch_bounds__(256) void u_stream_kernel(const bf16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[(w * 64 + 16 * mt + 4 * g16 + i) * US + 16 * nt + L16] = acc[mt][nt][i];
   __syncthreads();
-  for (int e = tid; e < 64 * RP; e += 256) {
+  for (int e = tid; e < 64 * RP; e += 512) {
     const int t = e / RP, nn = e - t * RP;
-    if (t0 + t < nq)
-      upart[((size_t)b * nq + t0 + t) * RP + nn] =
-          ((red[t * US + nn] + red[(64 + t) * US + nn]) + red[(128 + t) * US + nn]) + red[(192 + t) * US + nn];
+    if (t0 + t < nq) {
+      float a = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) a += red[(ww * 64 + t) * US + nn];
+      upart[((size_t)b * nq + t0 + t) * RP + nn] = a;
+    }
   }
 }
-static size_t u_stream_lds(int RP) { return (size_t)4 * 64 * (RP + 4) * 4; }
+static size_t u_stream_lds(int RP) {
+  const size_t xs = (size_t)2 * 64 * kUsRow * 2, part = (size_t)8 * 64 * (RP + 4) * 4;
+  return xs > part ? xs : part;
+}
 
 // 1c. qtilde_small_kernel (bf16, at most 32 queries, as in a decode step): one
 //     block per head computes u = x A for all the queries itself, then
@@ -1219,15 +1255,6 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// LDS block barrier that leaves vector-memory loads in flight: every wave's LDS
-// accesses before it have completed; the tile loads of the next batch keep running.
-__device__ __forceinline__ void lds_block_barrier() {
-  wait_lgkm0();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Minimum of a wave's values, in every lane: rotations within each 16-lane row
 // (DPP row_ror 8, 4, 2, 1), then the row pairs l ^ 16 and l ^ 32 (permlane swaps).
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -2074,7 +2101,7 @@ static hipError_t launch_fused_score(const RouteDims& dm, const void* q, const v
     auto uk = u_stream_kernel<RP>;
     e = hipFuncSetAttribute((const void*)uk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)u_stream_lds(RP));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(uk, dim3((nq + 63) / 64, dm.B), dim3(256), u_stream_lds(RP), st, (const bf16_t*)x, ws.at, Dh,
+    hipLaunchKernelGGL(uk, dim3((nq + 63) / 64, dm.B), dim3(512), u_stream_lds(RP), st, (const bf16_t*)x, ws.at, Dh,
                        Dhp, ws.upart, dm.N, q0, nq);
   } else {
     nsplit = u_splits(dm, Dh, nq);
