@@ -7,8 +7,8 @@
 //
 // One block of four waves per (batch, KV head, chunk of the requested range c0 ..):
 // the chunk's keys are read
-// from HBM once into LDS with 16-byte loads (float32, padded rows so that lane j
-// reading row j is bank-conflict free) and serve the G mask queries of the group,
+// from HBM once into LDS with 16-byte loads (float32 rows 4 banks apart, so that lane j
+// reading row j with 16-byte LDS reads is bank-conflict free) and serve the G mask queries of the group,
 // wave w taking heads w, w + 4, ... Lane j < 63 owns content key j for the logits
 // (four independent partial sums over d); for the weighted sum lanes own output
 // columns. Work is tiny next to the routed attention (4*63*d flops per head and
@@ -34,8 +34,8 @@ __global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(const T* 
   const int G = Hq / Hkv;
   const size_t L = (size_t)N * kSlots;
   constexpr int VE = 16 / sizeof(T);   // elements per 16-byte load
-  __shared__ float ks[kContent][D + 1];
-  __shared__ float qs[kSumWaves][D];
+  __shared__ __align__(16) float ks[kContent][D + 4];   // rows 16-byte aligned, 4 banks apart
+  __shared__ __align__(16) float qs[kSumWaves][D];
   __shared__ float al[kSumWaves][64];
 
   const T* kc = k + (((size_t)b * Hkv + g) * L + (size_t)c * kSlots) * D;
@@ -62,9 +62,12 @@ __global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(const T* 
     if (!MEAN && lane < kContent) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-      for (int e = 0; e < D; e += 4)
+      for (int e = 0; e < D; e += 4) {
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[w][e]);
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(&ks[lane][e]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] = fmaf(qs[w][e + u], ks[lane][e + u], acc[u]);
+        for (int u = 0; u < 4; ++u) acc[u] = fmaf(qv[u], kv[u], acc[u]);
+      }
       logit = scale * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
     }
     const float m = wave_max(logit);
