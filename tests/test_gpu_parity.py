@@ -223,6 +223,8 @@ PREFILL_EDGE = [
     ("K=64", dict(K=64, R=30)),
     ("radius zero", dict(R=0)),
     ("wide window", dict(R=3000)),
+    # batch 2 over few rounds of blocks: the pooled kernel takes fewer than 44 queries per block
+    ("batch 2", dict(B=2, beta=0.5)),
     # past 512 chunks the fused scoring takes 32-query blocks with 16 keys per lane
     ("700 chunks, entropy term", dict(N=700, K=32, beta=0.5)),
     ("1024 chunks, head dim 64", dict(N=1024, d=64, K=32)),
